@@ -1,0 +1,339 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+* hand-worked examples in tests/golden/worked_examples.json;
+* brute force on tiny inputs (tests/bruteforce.py: substring enumeration, continuation trie,
+  Python-ordered suffixes);
+* closed forms (periodic rows, all-distinct rows, a corpus holding the tail once);
+* a cross-path invariant: corpus matching against the one-document corpus [ctx, -1] equals
+  self matching for lengths >= 2, computed by two independent oracle routines.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from tests import bruteforce as bf
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
+
+
+def knobs(k, D=24, nb=1, M=128, mode=0, factor=1_000_000, prob=100_000, offset=0):
+    return dict(k=k, max_tree_depth=D, num_backoff=nb, max_occurrences=M, mode=mode,
+                spec_factor_ppm=factor, spec_offset_ppm=offset, min_token_prob_ppm=prob,
+                min_self_match=1, min_corpus_match=2)
+
+
+# ------------------------------------------------------------------ hand-worked golden cases
+@pytest.mark.parametrize("case", GOLD["local"], ids=lambda c: c["name"])
+def test_golden_local(orc, case):
+    ctx, t = orc.context(case["row"], case["n"], case["sampled"])
+    assert t == len(case["sampled"])
+    mb = orc.match_back(ctx, case["D"])
+    assert mb.tolist() == case["mb"]
+    for i, (l, sup, sites) in enumerate(zip(case["ladder"], case["support"], case["sites"])):
+        assert orc.kth_largest(mb, i + 1) == l
+        assert orc.count_at_least(mb, l) == sup
+        assert orc.first_sites(mb, l, 128).tolist() == sites
+    row = np.array(case["row"], np.int32)[None]
+    samp = np.array(case["sampled"], np.int32)[None]
+    n = np.array([case["n"]], np.int32)
+    for key, exp in case.items():
+        if key.startswith("expand_l"):
+            l = int(key.split("_")[1][1:])
+            k = int(key.split("_k")[1])
+            sites = case["sites"][case["ladder"].index(l)]
+            toks, counts, snum = orc.expand(ctx, sites, k)
+            assert toks.tolist() == exp["tokens"] and counts.tolist() == exp["counts"]
+            assert snum == exp["snum"]
+        if key.startswith("longest_fill_k"):
+            p = orc.make_params(int(key.split("_k")[1]), max_tree_depth=case["D"])
+            d, nv = orc.propose(p, n, row, samp)
+            assert d[0].tolist() == exp["draft"] and nv[0] == exp["num_valid"]
+        if key.startswith("scored_"):
+            parts = key.split("_")
+            nb = int(parts[1][2:]) if parts[1].startswith("nb") else 1
+            kk = int([x for x in parts if x.startswith("k")][0][1:])
+            factor = int([x for x in parts if x.startswith("factor")][0][6:]) * 1_000_000
+            prob = int([x for x in parts if x.startswith("prob")][0][4:])
+            p = orc.make_params(kk, max_tree_depth=case["D"], num_backoff=nb, mode=1,
+                                spec_factor_ppm=factor, min_token_prob_ppm=prob)
+            d, nv, info = orc.propose(p, n, row, samp, with_info=True)
+            assert d[0].tolist() == exp["draft"] and nv[0] == exp["num_valid"]
+            if "snum" in exp:
+                assert info[0].snum == exp["snum"] and info[0].c0 == exp["c0"]
+
+
+@pytest.mark.parametrize("case", GOLD["global"], ids=lambda c: c["name"])
+def test_golden_global(orc, case):
+    C = np.array(case["text"], np.int32)
+    lc = orc.LiveCorpus(10**6)
+    lc.ingest(case["docs"])
+    assert lc.text().tolist() == case["text"]
+    ctx, _ = orc.context(case["row"], case["n"], case["sampled"])
+    m = orc.corpus_match(C, ctx, case["D"])
+    assert m.tolist() == case["corpus_m"]
+    for i, (l, sup, sites) in enumerate(zip(case["ladder"], case["support"], case["sites"])):
+        assert orc.kth_largest(m, i + 1) == l
+        assert orc.count_at_least(m, l) == sup
+        assert orc.first_sites(m, l, 128).tolist() == sites
+    toks, counts, snum = orc.expand(C, case["sites"][0], 8)
+    assert toks.tolist() == case["expand"]["tokens"]
+    assert counts.tolist() == case["expand"]["counts"] and snum == case["expand"]["snum"]
+    p = orc.make_params(4, max_tree_depth=case["D"])
+    d, nv = orc.propose(p, np.array([case["n"]]), np.array([case["row"]]),
+                        np.array([case["sampled"]]), corpus=C)
+    assert d[0].tolist() == case["longest_fill_k4"]["draft"]
+    assert nv[0] == case["longest_fill_k4"]["num_valid"]
+
+
+@pytest.mark.parametrize("case", GOLD["suffix_array"], ids=lambda c: str(c["text"]))
+def test_golden_suffix_array(orc, case):
+    assert orc.suffix_array(case["text"]).tolist() == case["sa"]
+
+
+# ------------------------------------------------------------------ brute force, tiny inputs
+def _rand_ctx(rng, V, L):
+    return rng.integers(0, V, size=L).astype(np.int32)
+
+
+def test_match_back_and_ladder_bruteforce(orc):
+    rng = np.random.default_rng(11)
+    for it in range(400):
+        V = int(rng.choice([2, 3, 4, 16]))
+        L = int(rng.integers(1, 48))
+        D = int(rng.choice([1, 2, 3, 5, 8, 24]))
+        ctx = _rand_ctx(rng, V, L)
+        mb = orc.match_back(ctx, D)
+        assert mb.tolist() == bf.local_mb(ctx.tolist(), D), (it, ctx, D)
+        for t in range(1, 6):
+            l = bf.ladder(lambda x: len(bf.local_occ_ends(ctx.tolist(), x)), min(D, L - 1), t)
+            assert orc.kth_largest(mb, t) == l, (it, t)
+            if l >= 1:
+                ends = bf.local_occ_ends(ctx.tolist(), l)
+                assert orc.count_at_least(mb, l) == len(ends)
+                M = int(rng.integers(1, 6))
+                assert orc.first_sites(mb, l, M).tolist() == [j + 1 for j in ends][:M]
+
+
+def _rand_corpus(rng, V, ndocs, lo, hi):
+    docs = [rng.integers(0, V, size=int(rng.integers(lo, hi + 1))).astype(np.int32)
+            for _ in range(ndocs)]
+    lc = __import__("oracle").LiveCorpus(10**9)
+    lc.ingest(docs)
+    return lc.text()
+
+
+def test_corpus_match_bruteforce(orc):
+    rng = np.random.default_rng(12)
+    for it in range(300):
+        V = int(rng.choice([2, 3, 5]))
+        C = _rand_corpus(rng, V, int(rng.integers(0, 6)), 0, 12)
+        L = int(rng.integers(1, 10))
+        D = int(rng.choice([2, 3, 4, 6, 24]))
+        ctx = _rand_ctx(rng, V, L)
+        if it % 3 == 0:  # a -1 inside the context never matches a document separator
+            ctx = rng.integers(-1, V, size=L).astype(np.int32)
+        m = orc.corpus_match(C, ctx, D)
+        for t in range(1, 5):
+            l = bf.ladder(lambda x: len(bf.corpus_occ_starts(C.tolist(), ctx.tolist(), x)),
+                          min(D, L), t)
+            assert orc.kth_largest(m, t) == l, (it, C, ctx, D, t)
+            if l >= 1:
+                starts = bf.corpus_occ_starts(C.tolist(), ctx.tolist(), l)
+                assert orc.count_at_least(m, l) == len(starts)
+                assert orc.first_sites(m, l, 3).tolist() == sorted(i + l for i in starts)[:3]
+
+
+def test_expand_matches_trie(orc):
+    rng = np.random.default_rng(13)
+    for it in range(400):
+        V = int(rng.choice([2, 3, 4]))
+        X = rng.integers(-1, V, size=int(rng.integers(1, 40))).astype(np.int32)
+        nsites = int(rng.integers(1, 8))
+        sites = np.sort(rng.choice(len(X), size=min(nsites, len(X)), replace=False))
+        cap = int(rng.integers(0, 10))
+        scored = bool(rng.integers(0, 2))
+        prob = int(rng.choice([0, 100_000, 300_000, 500_000, 1_000_000]))
+        toks, counts, snum = orc.expand(X, sites, cap, scored, prob)
+        bt, bc, bs = bf.trie_expand(X.tolist(), sites.tolist(), cap, scored, prob)
+        assert toks.tolist() == bt and counts.tolist() == bc and snum == bs, (it, X, sites)
+
+
+def test_cross_path_one_document_corpus(orc):
+    """Corpus matching against [ctx, -1] and self matching share no code in the oracle but
+    must find the same occurrences for every length >= 2."""
+    rng = np.random.default_rng(14)
+    for it in range(300):
+        V = int(rng.choice([2, 3, 4]))
+        L = int(rng.integers(2, 40))
+        D = int(rng.choice([2, 3, 6, 24]))
+        ctx = _rand_ctx(rng, V, L)
+        C = np.concatenate([ctx, [-1]]).astype(np.int32)
+        mb = orc.match_back(ctx, D)
+        m = orc.corpus_match(C, ctx, D)
+        # corpus end e = local end j; the local cap is min(D, j+1), the corpus one min(D, L)
+        # and e+1, which agree on every end j <= L-2.
+        assert np.array_equal(np.minimum(m[: L - 1], D), mb), (it, ctx)
+        for t in range(1, 4):
+            lt, gt = orc.kth_largest(mb, t), orc.kth_largest(m, t)
+            if lt >= 2 or gt >= 2:
+                assert lt == gt
+                assert (orc.first_sites(mb, lt, 5).tolist()
+                        == orc.first_sites(m, gt, 5).tolist())
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_propose_bruteforce(orc, mode):
+    rng = np.random.default_rng(15 + mode)
+    for it in range(150):
+        V = int(rng.choice([2, 3, 4, 6]))
+        B = 3
+        S = int(rng.integers(1, 30))
+        T = int(rng.integers(0, 3))
+        k = int(rng.integers(1, 7))
+        nb = 1 if mode == 0 else int(rng.integers(1, 5))
+        M = int(rng.choice([1, 2, 3, 128]))
+        D = int(rng.choice([2, 3, 5, 24]))
+        kn = knobs(k, D=D, nb=nb, M=M, mode=mode,
+                   factor=int(rng.choice([500_000, 1_000_000, 2_000_000])),
+                   prob=int(rng.choice([0, 100_000, 400_000])),
+                   offset=int(rng.choice([0, 1_000_000])))
+        tok = rng.integers(0, V, size=(B, S)).astype(np.int32)
+        n = rng.integers(-2, S + 3, size=B).astype(np.int32)
+        samp = rng.integers(-1, V, size=(B, T)).astype(np.int32)
+        C = _rand_corpus(rng, V, int(rng.integers(0, 5)), 0, 10) if rng.integers(0, 2) else None
+        d, nv = orc.propose(orc.params_from(kn), n, tok, samp, corpus=C)
+        for b in range(B):
+            ed, en = bf.propose_row(kn, tok[b].tolist(), n[b], samp[b].tolist(),
+                                    None if C is None else C.tolist())
+            assert d[b].tolist() == ed and nv[b] == en, (it, b, kn, tok[b], n[b], samp[b], C)
+
+
+def test_suffix_array_bruteforce(orc):
+    rng = np.random.default_rng(16)
+    for it in range(200):
+        V = int(rng.choice([1, 2, 3, 5]))
+        n = int(rng.integers(0, 200))
+        text = rng.integers(-1, V, size=n).astype(np.int32)
+        assert orc.suffix_array(text).tolist() == bf.suffix_array(text.tolist())
+
+
+# ------------------------------------------------------------------ closed forms
+@pytest.mark.parametrize("p,r,D", [(3, 5, 24), (4, 6, 5), (5, 3, 24), (2, 20, 7), (7, 4, 3)])
+def test_periodic_row_closed_form(orc, p, r, D):
+    """Row (0..p-1)^r: an earlier copy of the tail ends every p tokens.  l1 = min(D, L-p); the
+    sites with that length are ends j = L-1-m*p (m >= 1, j >= l1-1); from site L-m*p the
+    continuation is 0,1,2,... for m*p tokens, so c_d = c0 - floor(d/p) and token d = d mod p."""
+    ctx = np.tile(np.arange(p, dtype=np.int32), r)
+    L = len(ctx)
+    l1 = min(D, L - p)
+    mb = orc.match_back(ctx, D)
+    assert orc.kth_largest(mb, 1) == l1
+    ms = [m for m in range(1, r) if L - 1 - m * p >= l1 - 1]
+    assert orc.count_at_least(mb, l1) == len(ms)
+    sites = orc.first_sites(mb, l1, 128)
+    assert sites.tolist() == sorted(L - m * p for m in ms)
+    k = 3 * p + 2
+    toks, counts, snum = orc.expand(ctx, sites, k)
+    c0 = len(ms)
+    nexp = min(k, c0 * p)
+    assert toks.tolist() == [d % p for d in range(nexp)]
+    assert counts.tolist() == [c0 - d // p for d in range(nexp)]
+    assert snum == sum(c0 - d // p for d in range(nexp))
+    # whole call, longest-match mode: the draft continues the period, the rest is the fill
+    row = ctx[:-1][None]
+    d, nv = orc.propose(orc.make_params(k, max_tree_depth=D), np.array([L - 1]), row,
+                        ctx[-1:][None])
+    assert nv[0] == nexp and d[0, :nexp].tolist() == [x % p for x in range(nexp)]
+    assert (d[0, nexp:] == ctx[-1]).all()
+    # scored mode: cap = floor(factor * l1); stop when c_d / c0 < 0.5
+    pr = orc.make_params(k, max_tree_depth=D, mode=1, spec_factor_ppm=1_000_000,
+                         min_token_prob_ppm=500_000)
+    d, nv, info = orc.propose(pr, np.array([L - 1]), row, ctx[-1:][None], with_info=True)
+    n2 = 0
+    while n2 < min(k, l1, c0 * p) and (c0 - n2 // p) * 2 >= c0:
+        n2 += 1
+    assert nv[0] == n2 and info[0].snum == sum(c0 - x // p for x in range(n2))
+    assert (d[0, n2:] == -1).all()
+
+
+def test_all_distinct_row(orc):
+    for L in (1, 2, 17, 300):
+        ctx = np.arange(L, dtype=np.int32) + 5
+        for mode in (0, 1):
+            d, nv = orc.propose(orc.make_params(6, mode=mode, num_backoff=1 + 2 * mode),
+                                np.array([L - 1]), ctx[:-1][None] if L > 1 else
+                                np.zeros((1, 1), np.int32), ctx[-1:][None])
+            assert nv[0] == 0
+            assert (d[0] == (ctx[-1] if mode == 0 else -1)).all()
+
+
+def test_unique_corpus_occurrence(orc):
+    """A corpus that holds the tail exactly once: the draft is that document's continuation,
+    every chain probability is 1 (c_d = 1) and the draft stops at the document's end."""
+    rng = np.random.default_rng(17)
+    for it in range(50):
+        tail = rng.choice(np.arange(100, 200), size=int(rng.integers(2, 8)),
+                          replace=False).astype(np.int32)
+        cont = rng.integers(300, 400, size=int(rng.integers(1, 12))).astype(np.int32)
+        docs = [rng.integers(500, 600, size=10).astype(np.int32),
+                np.concatenate([rng.integers(700, 800, size=3), tail, cont]).astype(np.int32)]
+        lc = orc.LiveCorpus(10**6)
+        lc.ingest(docs)
+        C = lc.text()
+        row = np.concatenate([rng.integers(900, 1000, size=5), tail[:-1]]).astype(np.int32)
+        k = 8
+        for mode in (0, 1):
+            p = orc.make_params(k, mode=mode, num_backoff=1 + mode, spec_factor_ppm=10**8,
+                                min_token_prob_ppm=10**6)
+            d, nv, info = orc.propose(p, np.array([len(row)]), row[None], tail[-1:][None],
+                                      corpus=C, with_info=True)
+            n = min(k, len(cont))
+            assert nv[0] == n and d[0, :n].tolist() == cont[:n].tolist()
+            assert info[0].snum == n and info[0].c0 == 1
+            assert info[0].chosen_len == len(tail)
+
+
+# ------------------------------------------------------------------ state update, corpus model
+def test_update_state(orc):
+    rng = np.random.default_rng(18)
+    for it in range(100):
+        B, S, T = 4, int(rng.integers(1, 12)), int(rng.integers(0, 4))
+        tok = rng.integers(0, 9, size=(B, S)).astype(np.int32)
+        n = rng.integers(-2, S + 2, size=B).astype(np.int32)
+        samp = rng.integers(-1, 9, size=(B, T)).astype(np.int32)
+        new, nn = orc.update_state(tok, n, samp)
+        for b in range(B):
+            nb_ = max(0, min(int(n[b]), S))
+            t = 0
+            while t < T and samp[b, t] >= 0:
+                t += 1
+            w = min(t, S - nb_)
+            assert nn[b] == nb_ + w
+            assert new[b, nb_:nb_ + w].tolist() == samp[b, :w].tolist()
+            assert new[b, :nb_].tolist() == tok[b, :nb_].tolist()
+            assert new[b, nb_ + w:].tolist() == tok[b, nb_ + w:].tolist()
+
+
+def test_live_corpus_eviction(orc):
+    rng = np.random.default_rng(19)
+    for it in range(100):
+        cap = int(rng.integers(0, 60))
+        lc = orc.LiveCorpus(cap)
+        hist = []
+        for step in range(int(rng.integers(1, 6))):
+            docs = [rng.integers(0, 9, size=int(rng.integers(0, 15))).astype(np.int32)
+                    for _ in range(int(rng.integers(0, 4)))]
+            lc.ingest(docs)
+            hist += [d.tolist() for d in docs]
+            # the live set is the longest run of most recent documents that fits
+            tot, live = 0, []
+            for d in reversed(hist):
+                if tot + len(d) + 1 > cap:
+                    break
+                tot += len(d) + 1
+                live.insert(0, d)
+            exp = [x for d in live for x in d + [-1]]
+            assert lc.text().tolist() == exp
+            assert len(exp) <= cap
