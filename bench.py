@@ -1,0 +1,174 @@
+"""Benchmark of the drafter step on one MI355X.
+
+A step is one sfx_propose over one batch: every request's self match, corpus probes, vote and
+selection.  Default workload: B=256 requests, S=16384 resident tokens (valid lengths
+U[4096,16384]), V=151936, k=16, scored mode, and a 1M-token template corpus indexed on the
+device.  Inputs are synthetic (seeded generators in workloads/) and already resident in HBM when
+the timed region starts; the token buffers rotate over enough copies to exceed the 256 MB
+Infinity Cache, so each step streams its rows from HBM.
+
+Prints one JSON line (metric, value, roofline, cpu_baseline, ...).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(n, samp, B, T, k):
+    """Words the method must touch per call: each request's context (its row prefix and the
+    sampled ids appended to it), its length, and the [k] draft plus valid count written back.
+    Corpus words are not counted (a conservative floor)."""
+    t = (samp >= 0).cumprod(axis=1).sum(axis=1)
+    L = np.minimum(np.maximum(n, 0), 1 << 30) + t
+    return int(4 * L.sum() + 4 * B * (1 + T) + 4 * B * (k + 1)), int(L.sum())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--distinct-sets", type=int, default=4)
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=64)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the drafter path has no multi-GPU mode in this "
+              "build (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import suffix_match_drafter_amd as sfx
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.config]
+    log(f"[bench] workload {w.name}: B={w.B} S={w.S} V={w.V} k={w.k} mode={w.mode}")
+
+    # ---------------------------------------------------------------- inputs
+    t0 = time.time()
+    sets = [W.make_batch(args.config, set_index=i) for i in range(args.distinct_sets)]
+    docs = W.corpus_docs(args.config)
+    log(f"[bench] generated {len(sets)} input sets and {len(docs)} corpus docs "
+        f"in {time.time() - t0:.1f}s")
+    cfg = sfx.Config(max_batch=w.B, max_seq=w.S, max_sampled=w.T,
+                     corpus_capacity=(1 << 20) if w.corpus else 0, **w.knobs())
+    d = sfx.Drafter(cfg)
+    rebuild_s = None
+    corpus_n = 0
+    if w.corpus:
+        d.ingest_docs(docs)
+        torch.cuda.synchronize()
+        t1 = time.time()
+        d.rebuild()
+        torch.cuda.synchronize()
+        rebuild_s = time.time() - t1
+        corpus_n = int(d.corpus_snapshot().numel())
+        log(f"[bench] corpus {corpus_n} tokens indexed in {rebuild_s * 1e3:.1f} ms")
+    bufs = []
+    for c in range(args.copies):
+        for (n, tok, samp) in sets:
+            bufs.append((torch.from_numpy(n).to(dev), torch.from_numpy(tok).to(dev),
+                         torch.from_numpy(samp).to(dev)))
+    nbuf = len(bufs)
+    resident_mb = sum(b[1].numel() * 4 for b in bufs) / 1e6
+    alg = [algorithmic_bytes(n, samp, w.B, w.T, w.k) for (n, tok, samp) in sets]
+    alg_bytes = float(np.mean([a[0] for a in alg]))
+    ctx_tokens = float(np.mean([a[1] for a in alg]))
+    draft = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+    nv = torch.empty((w.B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    # ---------------------------------------------------------------- timed region
+    for i in range(args.warmup):
+        b = bufs[i % nbuf]
+        d.propose(b[0], b[1], b[2], draft, nv, stream)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        b = bufs[i % nbuf]
+        d.propose(b[0], b[1], b[2], draft, nv, stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    calls_s = 1e3 / ms
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] {args.steps} steps over {nbuf} rotating buffers ({resident_mb:.0f} MB): "
+        f"{ms * 1e3:.2f} us/step, {calls_s:.0f} calls/s, {achieved:.0f} GB/s algorithmic")
+
+    # ---------------------------------------------------------------- oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+
+        cores = len(os.sched_getaffinity(0))
+        n, tok, samp = sets[0]
+        R = min(args.cpu_rows, w.B)
+        corpus = W.join_docs(docs) if w.corpus else None
+        p = O.params_from(w.knobs())
+        t2 = time.time()
+        O.propose(p, n[:R], tok[:R], samp[:R], corpus=corpus, num_threads=cores)
+        dt = time.time() - t2
+        cpu = {"value": round(R / w.B / dt, 3), "unit": "propose calls/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"first {R} of {w.B} rows of input set 0 (one call scaled by {w.B}/{R}),"
+                         f" {dt:.1f}s wall, OpenMP over rows, {O.BUILD_FLAGS}"}
+        log(f"[bench] oracle: {R} rows in {dt:.2f}s on {cores} cores")
+
+    out = {
+        "metric": "propose calls/s at B=256,S=16K,1M-token corpus; % of HBM roofline",
+        "value": round(calls_s, 1),
+        "unit": "propose calls/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "T": w.T, "V": w.V, "k": w.k,
+                   "max_tree_depth": w.max_tree_depth, "num_backoff": w.num_backoff,
+                   "max_occurrences": w.max_occurrences,
+                   "mode": "scored" if w.mode == 1 else "longest_fill",
+                   "corpus_tokens": corpus_n, "rotating_buffers": nbuf,
+                   "resident_input_MB": round(resident_mb, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "extra": {"tokens_scanned_per_s": round(ctx_tokens * calls_s, 1),
+                  "algorithmic_bytes_per_call": int(alg_bytes),
+                  "index_rebuild_ms": None if rebuild_s is None else round(rebuild_s * 1e3, 2),
+                  "index_rebuild_tokens_per_s":
+                      None if not rebuild_s else round(corpus_n / rebuild_s, 1)},
+    }
+    print(json.dumps(out), flush=True)
+    d.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,170 @@
+/*
+ * sfx.h -- C-ABI of libsfx, the MI355X (gfx950) suffix-match drafter.
+ *
+ * The drafter proposes, for every request of a decode batch, a draft of up to k next tokens by
+ * matching the request's last tokens against (a) its own prompt+output and (b) a shared corpus
+ * of finished responses, then expanding the best match by depth-wise frequency vote.
+ *
+ * Passages this interface follows (cited by page title and section):
+ *   - vLLM issue "[RFC]: Suffix decoding on GPU (suffix_gpu)", Design: the proposer contract
+ *     propose(k, num_tokens_no_spec, token_ids, sampled, counts) -> (drafts [B,k],
+ *     valid counts [B]); finished requests are ingested into a cross-request index.
+ *   - PyPI page "suffix-gpu 0.1.1", Highlights and Quickstart: device tensors in and out, no
+ *     per-step host synchronisation, static shapes; int32 state token_ids [B,S],
+ *     num_tokens_no_spec [B], sampled [B,T] (-1 padded); draft [B,k] (-1 padded) and
+ *     num_valid [B]; harvest_finished(row_indices, lengths, token_ids) and poll().
+ *   - same page, How it works steps 1-4: local match_back ladder, global suffix-array match,
+ *     fused vote + score, corpus ring + delta with a side-stream suffix-array rebuild that is
+ *     swapped without moving buffers.
+ *   - vLLM docs "Suffix Decoding", Model Runner V2: longest suffix up to max_tree_depth,
+ *     corpus probed by the last 2 and last 4 tokens, longer match wins, fill with the last
+ *     sampled token, corpus budget with oldest-first eviction.
+ *   - gitcode blog "vLLM Suffix Decoding 投机解码实战", section 4: knob ranges
+ *     (max_tree_depth >= 1, max_spec_factor >= 0, min_token_prob in [0,1]).
+ *
+ * Conventions (all entry points):
+ *   - Every array argument is a DEVICE pointer owned by the caller unless stated otherwise; the
+ *     library never frees it and never keeps it past the call.  Arrays are dense row-major.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is enqueued on
+ *     it; entry points on the propose path neither synchronise the host nor allocate.
+ *   - Return value: SFX_OK (0) or a negative SFX_E* code; on error nothing was enqueued and
+ *     sfx_last_error() returns a thread-local message.  Values the host cannot see without a
+ *     synchronisation (lengths stored in device memory) are clamped on the device instead of
+ *     being rejected.
+ *   - A context is used from one host thread at a time and its work is ordered by the streams
+ *     given; two calls that overlap on different streams without ordering race.
+ */
+#ifndef SFX_H
+#define SFX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SFX_OK = 0,
+  SFX_EINVAL = -1,     /* bad argument or configuration */
+  SFX_ENOMEM = -2,     /* device allocation failed (only sfx_create allocates) */
+  SFX_ECAPACITY = -3,  /* shape above what the context was created for */
+  SFX_EHIP = -4,       /* a HIP runtime call failed */
+  SFX_ESTATE = -5      /* call not valid in the context's current state */
+};
+
+enum {
+  SFX_MODE_LONGEST_FILL = 0, /* vLLM docs, Model Runner V2: longer match wins, fill with the
+                                last sampled token, no stop rule (requires num_backoff == 1) */
+  SFX_MODE_SCORED = 1        /* suffix-gpu page, How it works step 3: adaptive stop rule and
+                                score; best score wins; -1 padding */
+};
+
+typedef struct sfx_config {
+  int32_t k;                /* draft width, 1..32 */
+  int32_t max_tree_depth;   /* D: longest suffix matched, 1..64 (>= 2 when a corpus is used) */
+  int32_t num_backoff;      /* nb: ladder candidates per source, 1..8 */
+  int32_t max_occurrences;  /* M: earliest continuation sites kept per candidate, 1..128 */
+  int32_t mode;             /* SFX_MODE_* */
+  int32_t min_self_match;   /* shortest self match that makes a candidate, >= 1 */
+  int32_t min_corpus_match; /* shortest corpus match that makes a candidate, 2..max_tree_depth */
+  int32_t max_batch;        /* largest B accepted by sfx_propose */
+  int32_t max_seq;          /* largest S accepted by sfx_propose (row capacity) */
+  int32_t max_sampled;      /* largest T accepted by sfx_propose, 0..16 */
+  int64_t spec_factor_ppm;  /* max_spec_factor * 1e6, >= 0 (SCORED) */
+  int64_t spec_offset_ppm;  /* max_spec_offset * 1e6, >= 0 (SCORED) */
+  int64_t min_token_prob_ppm; /* min_token_prob * 1e6, 0..1e6 (SCORED) */
+  int64_t corpus_capacity;  /* ring size in tokens, separators included; 0 = no corpus;
+                               at most 2^30 */
+} sfx_config;
+
+typedef struct sfx_ctx sfx_ctx;
+
+/* Validates *cfg and allocates every device buffer the context will ever use (rows scratch,
+ * corpus ring, double-buffered corpus index, control block) on the current HIP device.
+ * Returns SFX_EINVAL for a configuration outside the ranges above, SFX_ENOMEM when device
+ * memory runs out.  *out receives the context. */
+int sfx_create(const sfx_config* cfg, sfx_ctx** out);
+
+/* Waits for the context's own side-stream work, then frees everything it allocated. */
+void sfx_destroy(sfx_ctx* ctx);
+
+/* Thread-local text of the last error (never NULL). */
+const char* sfx_last_error(void);
+
+/* One drafter step for B requests (RFC page, Design; suffix-gpu page, How it works 1-3).
+ *   num_tokens_no_spec [B]   row prefix length n_b; clamped to [0,S] on the device
+ *   token_ids          [B,S] resident rows; only token_ids[b, 0:n_b] is read
+ *   sampled            [B,T] last verifier output, -1 padded; the leading non-negative
+ *                            entries are appended (virtually) to the row prefix
+ *   draft              [B,k] out: proposed ids; the rest of the row is the last sampled token
+ *                            (LONGEST_FILL) or -1 (SCORED); all -1 when a row has no sampled id
+ *   num_valid          [B]   out: number of proposed ids
+ * Token ids must be >= 0.  Requires B <= max_batch, S <= max_seq, T <= max_sampled
+ * (else SFX_ECAPACITY).  Reads the corpus index that is live when the kernel runs. */
+int sfx_propose(sfx_ctx* ctx, int32_t B, int32_t S, int32_t T, const int32_t* num_tokens_no_spec,
+                const int32_t* token_ids, const int32_t* sampled, int32_t* draft,
+                int32_t* num_valid, void* stream);
+
+/* State update (suffix-gpu page, Quickstart: propose_with_update).  Writes the leading
+ * non-negative sampled ids of row b after its clamped prefix, as many as fit in S, and stores
+ * the new length in num_tokens_out[b].  token_ids is modified in place.  Needs no context. */
+int sfx_update_state(int32_t B, int32_t S, int32_t T, int32_t* token_ids,
+                     const int32_t* num_tokens_no_spec, const int32_t* sampled,
+                     int32_t* num_tokens_out, void* stream);
+
+/* Ingest finished rows into the corpus (suffix-gpu page, Quickstart: harvest_finished; How it
+ * works step 4).  Document r is token_ids[row_indices[r], 0:clamp(lengths[r], 0, S)], appended
+ * in r order and followed by one -1 separator; afterwards the oldest documents are evicted
+ * while the live total exceeds corpus_capacity.  token_ids is [num_rows, S]; a row index
+ * outside [0, num_rows) makes an empty document.  New documents become visible to
+ * sfx_propose at once (through the delta scan until the next rebuild is swapped in).
+ * SFX_ESTATE when the context has no corpus. */
+int sfx_harvest_finished(sfx_ctx* ctx, int32_t R, const int32_t* row_indices,
+                         const int32_t* lengths, const int32_t* token_ids, int32_t num_rows,
+                         int32_t S, void* stream);
+
+/* Ingest packed documents: document d is tokens[doc_offsets[d] : doc_offsets[d+1]] (offsets
+ * int64, non-decreasing, device memory); otherwise as sfx_harvest_finished. */
+int sfx_ingest(sfx_ctx* ctx, int32_t num_docs, const int64_t* doc_offsets, const int32_t* tokens,
+               void* stream);
+
+/* Rebuild the corpus index over the live corpus and make it live, in stream order on `stream`
+ * (snapshot copy, suffix array by prefix doubling, n-gram interval tables).  The host thread
+ * waits for the stream while it drives the doubling rounds. */
+int sfx_rebuild(sfx_ctx* ctx, void* stream);
+
+/* Same rebuild, off the critical path: the snapshot is copied in order on `stream`, the
+ * suffix array and tables are built into the idle buffer by the library's worker thread on the
+ * context's own side stream, and sfx_poll swaps them in.  SFX_ESTATE if a rebuild is already
+ * in flight. */
+int sfx_rebuild_async(sfx_ctx* ctx, void* stream);
+
+/* Non-blocking: if an asynchronous rebuild has finished, enqueue on `stream` the swap that makes
+ * it live (buffers never move, so captured work keeps its pointers) and set *swapped = 1;
+ * otherwise *swapped = 0.  `swapped` is a host pointer. */
+int sfx_poll(sfx_ctx* ctx, int32_t* swapped, void* stream);
+
+/* Block until an in-flight asynchronous rebuild has finished, then swap it in on `stream`.
+ * No-op when none is in flight. */
+int sfx_wait_rebuild(sfx_ctx* ctx, void* stream);
+
+/* Copy the live corpus text (documents in ingest order, each followed by -1) into text_out
+ * (device, capacity `cap` ints) and its length into *n_out (host pointer).  Synchronises the
+ * stream.  SFX_ECAPACITY if cap is too small. */
+int sfx_corpus_snapshot(sfx_ctx* ctx, int32_t* text_out, int64_t cap, int64_t* n_out,
+                        void* stream);
+
+/* Suffix array (suffix-gpu page, Highlights and References: Manber & Myers prefix doubling):
+ * sa[r] = start of the r-th smallest suffix of text[0:n], tokens compared as signed int32, a
+ * proper prefix before the longer suffix.  text and sa are device arrays; workspace is a
+ * device buffer of at least sfx_suffix_array_workspace_bytes(n) bytes.  The host waits for
+ * `stream` once per doubling round.  n at most 2^30. */
+size_t sfx_suffix_array_workspace_bytes(int64_t n);
+int sfx_build_suffix_array(const int32_t* text, int64_t n, int32_t* sa, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,259 @@
+"""suffix_match_drafter_amd -- MI355X (gfx950) suffix-match drafter.
+
+Thin ctypes binding over ``libsfx.so`` (C-ABI in ``include/sfx.h``).  This module only
+marshals arguments: every step of the drafter runs in the library's HIP kernels.  PyTorch is
+used for device memory and streams.  There is no CPU fallback: if the library is missing the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsfx.so")
+
+MODE_LONGEST_FILL = 0
+MODE_SCORED = 1
+
+OK, EINVAL, ENOMEM, ECAPACITY, EHIP, ESTATE = 0, -1, -2, -3, -4, -5
+_NAMES = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", ECAPACITY: "ECAPACITY", EHIP: "EHIP",
+          ESTATE: "ESTATE"}
+
+# every entry point declared in include/sfx.h
+EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_update_state",
+           "sfx_harvest_finished", "sfx_ingest", "sfx_rebuild", "sfx_rebuild_async", "sfx_poll",
+           "sfx_wait_rebuild", "sfx_corpus_snapshot", "sfx_suffix_array_workspace_bytes",
+           "sfx_build_suffix_array")
+
+
+class SfxError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_int32),
+        ("max_tree_depth", ctypes.c_int32),
+        ("num_backoff", ctypes.c_int32),
+        ("max_occurrences", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
+        ("min_self_match", ctypes.c_int32),
+        ("min_corpus_match", ctypes.c_int32),
+        ("max_batch", ctypes.c_int32),
+        ("max_seq", ctypes.c_int32),
+        ("max_sampled", ctypes.c_int32),
+        ("spec_factor_ppm", ctypes.c_int64),
+        ("spec_offset_ppm", ctypes.c_int64),
+        ("min_token_prob_ppm", ctypes.c_int64),
+        ("corpus_capacity", ctypes.c_int64),
+    ]
+
+
+@dataclasses.dataclass
+class Config:
+    k: int
+    max_tree_depth: int = 24
+    num_backoff: int = 1
+    max_occurrences: int = 128
+    mode: int = MODE_LONGEST_FILL
+    min_self_match: int = 1
+    min_corpus_match: int = 2
+    max_batch: int = 256
+    max_seq: int = 16384
+    max_sampled: int = 1
+    spec_factor_ppm: int = 1_000_000
+    spec_offset_ppm: int = 0
+    min_token_prob_ppm: int = 100_000
+    corpus_capacity: int = 0
+
+    def _c(self) -> _Config:
+        return _Config(*[getattr(self, f[0]) for f in _Config._fields_])
+
+
+_V = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libsfx.so (torch is imported first so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m suffix_match_drafter_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(path)
+    sig = {
+        "sfx_create": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_V)]),
+        "sfx_destroy": (None, [_V]),
+        "sfx_last_error": (ctypes.c_char_p, []),
+        "sfx_propose": (ctypes.c_int, [_V, _I32, _I32, _I32, _V, _V, _V, _V, _V, _V]),
+        "sfx_update_state": (ctypes.c_int, [_I32, _I32, _I32, _V, _V, _V, _V, _V]),
+        "sfx_harvest_finished": (ctypes.c_int, [_V, _I32, _V, _V, _V, _I32, _I32, _V]),
+        "sfx_ingest": (ctypes.c_int, [_V, _I32, _V, _V, _V]),
+        "sfx_rebuild": (ctypes.c_int, [_V, _V]),
+        "sfx_rebuild_async": (ctypes.c_int, [_V, _V]),
+        "sfx_poll": (ctypes.c_int, [_V, ctypes.POINTER(_I32), _V]),
+        "sfx_wait_rebuild": (ctypes.c_int, [_V, _V]),
+        "sfx_corpus_snapshot": (ctypes.c_int, [_V, _V, _I64, ctypes.POINTER(_I64), _V]),
+        "sfx_suffix_array_workspace_bytes": (ctypes.c_size_t, [_I64]),
+        "sfx_build_suffix_array": (ctypes.c_int, [_V, _I64, _V, _V, ctypes.c_size_t, _V]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(rc):
+    if rc != OK:
+        raise SfxError(rc, load().sfx_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _V(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _i32(t: torch.Tensor, name: str, ndim: int) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_cuda:
+        raise TypeError(f"{name} must be an int32 CUDA/HIP tensor")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-D tensor")
+    return t
+
+
+def _ptr(t):
+    return _V(t.data_ptr()) if t is not None and t.numel() else _V(0)
+
+
+class Drafter:
+    """One drafter context: configuration, corpus ring and double-buffered corpus index."""
+
+    def __init__(self, cfg: Config):
+        L = load()
+        self.cfg = cfg
+        h = _V()
+        _check(L.sfx_create(ctypes.byref(cfg._c()), ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            load().sfx_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def propose(self, num_tokens, token_ids, sampled, draft=None, num_valid=None, stream=None):
+        tok = _i32(token_ids, "token_ids", 2)
+        B, S = tok.shape
+        samp = _i32(sampled, "sampled", 2)
+        nt = _i32(num_tokens, "num_tokens_no_spec", 1)
+        if samp.shape[0] != B or nt.shape[0] != B:
+            raise ValueError("batch sizes differ")
+        if draft is None:
+            draft = torch.empty((B, self.cfg.k), dtype=torch.int32, device=tok.device)
+        if num_valid is None:
+            num_valid = torch.empty((B,), dtype=torch.int32, device=tok.device)
+        _i32(draft, "draft", 2)
+        _i32(num_valid, "num_valid", 1)
+        if draft.shape != (B, self.cfg.k) or num_valid.shape != (B,):
+            raise ValueError("draft must be [B,k] and num_valid [B]")
+        _check(load().sfx_propose(self._h, B, S, samp.shape[1], _ptr(nt), _ptr(tok), _ptr(samp),
+                                  _ptr(draft), _ptr(num_valid), _stream(stream)))
+        return draft, num_valid
+
+    def propose_with_update(self, num_tokens, token_ids, sampled, stream=None):
+        draft, nv = self.propose(num_tokens, token_ids, sampled, stream=stream)
+        new_n = update_state(token_ids, num_tokens, sampled, stream=stream)
+        return draft, nv, new_n
+
+    def harvest_finished(self, row_indices, lengths, token_ids, stream=None):
+        rows = _i32(row_indices, "row_indices", 1)
+        lens = _i32(lengths, "lengths", 1)
+        tok = _i32(token_ids, "token_ids", 2)
+        if rows.shape != lens.shape:
+            raise ValueError("row_indices and lengths differ in size")
+        _check(load().sfx_harvest_finished(self._h, rows.shape[0], _ptr(rows), _ptr(lens),
+                                           _ptr(tok), tok.shape[0], tok.shape[1],
+                                           _stream(stream)))
+
+    def ingest(self, doc_offsets, tokens, stream=None):
+        offs = doc_offsets
+        if offs.dtype != torch.int64 or not offs.is_cuda or offs.dim() != 1:
+            raise TypeError("doc_offsets must be a 1-D int64 CUDA/HIP tensor")
+        tok = _i32(tokens, "tokens", 1)
+        _check(load().sfx_ingest(self._h, offs.shape[0] - 1, _ptr(offs), _ptr(tok),
+                                 _stream(stream)))
+
+    def ingest_docs(self, docs, stream=None):
+        """Convenience: ingest a list of 1-D int sequences (host) as packed documents."""
+        import numpy as np
+
+        lens = [len(d) for d in docs]
+        offs = np.zeros(len(docs) + 1, np.int64)
+        offs[1:] = np.cumsum(lens)
+        flat = np.concatenate([np.asarray(d, np.int32) for d in docs]) if docs else \
+            np.zeros(0, np.int32)
+        dev = torch.device("cuda")
+        self.ingest(torch.from_numpy(offs).to(dev), torch.from_numpy(flat).to(dev), stream)
+
+    def rebuild(self, stream=None):
+        _check(load().sfx_rebuild(self._h, _stream(stream)))
+
+    def rebuild_async(self, stream=None):
+        _check(load().sfx_rebuild_async(self._h, _stream(stream)))
+
+    def poll(self, stream=None) -> bool:
+        sw = _I32(0)
+        _check(load().sfx_poll(self._h, ctypes.byref(sw), _stream(stream)))
+        return bool(sw.value)
+
+    def wait_rebuild(self, stream=None):
+        _check(load().sfx_wait_rebuild(self._h, _stream(stream)))
+
+    def corpus_snapshot(self, stream=None) -> torch.Tensor:
+        cap = max(int(self.cfg.corpus_capacity), 1)
+        out = torch.empty(cap, dtype=torch.int32, device="cuda")
+        n = _I64(0)
+        _check(load().sfx_corpus_snapshot(self._h, _ptr(out), cap, ctypes.byref(n),
+                                          _stream(stream)))
+        return out[: n.value]
+
+
+def update_state(token_ids, num_tokens, sampled, num_tokens_out=None, stream=None):
+    tok = _i32(token_ids, "token_ids", 2)
+    samp = _i32(sampled, "sampled", 2)
+    nt = _i32(num_tokens, "num_tokens_no_spec", 1)
+    B, S = tok.shape
+    if num_tokens_out is None:
+        num_tokens_out = torch.empty((B,), dtype=torch.int32, device=tok.device)
+    _check(load().sfx_update_state(B, S, samp.shape[1], _ptr(tok), _ptr(nt), _ptr(samp),
+                                   _ptr(num_tokens_out), _stream(stream)))
+    return num_tokens_out
+
+
+def build_suffix_array(text: torch.Tensor, stream=None) -> torch.Tensor:
+    t = _i32(text, "text", 1)
+    n = t.shape[0]
+    sa = torch.empty(n, dtype=torch.int32, device=t.device)
+    L = load()
+    wsb = L.sfx_suffix_array_workspace_bytes(n)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=t.device)
+    _check(L.sfx_build_suffix_array(_ptr(t), n, _ptr(sa), _ptr(ws), wsb, _stream(stream)))
+    return sa

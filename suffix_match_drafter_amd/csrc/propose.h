@@ -1,0 +1,30 @@
+// propose.h -- launch interface of the drafter-step kernels (internal to libsfx).
+#pragma once
+
+#include "sfx_internal.h"
+
+namespace sfx {
+
+struct ProposeArgs {
+  int32_t B, S, T;
+  const int32_t* ntns;
+  const int32_t* tok;
+  const int32_t* samp;
+  int32_t* draft;
+  int32_t* nvalid;
+  int32_t k, D, nb, M, mode, min_self, min_corpus;
+  int64_t factor_ppm, offset_ppm, prob_ppm;
+  const Ctl* ctl;  // nullptr when the context has no corpus
+  IndexBuf idx[2];
+  const int32_t* ring;
+  int64_t ring_cap;
+};
+
+size_t propose_dynamic_lds(int S, int T);
+// Allows `dyn` bytes of dynamic LDS on every propose kernel instantiation.
+hipError_t propose_prepare(size_t dyn);
+hipError_t launch_propose(const ProposeArgs& a, hipStream_t st);
+hipError_t launch_update_state(int B, int S, int T, int32_t* tok, const int32_t* ntns,
+                               const int32_t* samp, int32_t* nout, hipStream_t st);
+
+}  // namespace sfx

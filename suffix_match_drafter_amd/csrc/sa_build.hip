@@ -1,0 +1,533 @@
+// sa_build.hip -- suffix array by prefix doubling over a stable LSD radix sort, and the n-gram
+// probe tables derived from it.
+//
+// suffix-gpu page, Highlights and References: the cross-request memory is a suffix array built
+// by Manber & Myers prefix doubling.  Round h sorts every suffix start i by the pair
+// (rank_h[i], rank_h[i+h]) -- rank 0 standing for "past the end", so a proper prefix sorts
+// first -- and re-ranks each suffix by the index of the first member of its group.  Rounds stop
+// when all ranks differ.  Tokens compare as signed int32, so the -1 document separator sorts
+// before every token.
+//
+// The sort is an LSD radix sort with 8-bit digits: per-tile digit histograms, one exclusive
+// scan in digit-major order, then a stable scatter in which each wavefront ranks equal digits
+// with eight ballots.  Keys of a round pack both ranks into 2*bits(n) bits so only the needed
+// digits are sorted.
+#include "sa_build.h"
+
+#include <algorithm>
+
+namespace sfx {
+
+namespace {
+
+constexpr int RS_T = 256;              // threads per radix tile
+constexpr int RS_I = 16;               // items per thread
+constexpr int RS_TILE = RS_T * RS_I;   // 4096 keys per tile
+constexpr int SC_T = 1024;             // scan block
+constexpr int SC_I = 4;
+constexpr int SC_TILE = SC_T * SC_I;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------ generic int32 scans
+// Three phases: per-tile reduction, scan of tile totals, per-tile apply.  Op: 0 sum, 1 max.
+template <int OP>
+__device__ __forceinline__ int sc_op(int a, int b) { return OP == 0 ? a + b : (a > b ? a : b); }
+
+template <int OP>
+__device__ int block_scan_incl(int v, int* wbuf) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x = sc_op<OP>(x, y);
+  }
+  if (lane == 63) wbuf[wid] = x;
+  __syncthreads();
+  if (wid == 0) {
+    int s = lane < SC_T / 64 ? wbuf[lane] : (OP == 0 ? 0 : INT32_MIN);
+#pragma unroll
+    for (int o = 1; o < SC_T / 64; o <<= 1) {
+      int y = __shfl_up(s, o, 64);
+      if (lane >= o) s = sc_op<OP>(s, y);
+    }
+    if (lane < SC_T / 64) wbuf[lane] = s;
+  }
+  __syncthreads();
+  if (wid) x = sc_op<OP>(x, wbuf[wid - 1]);
+  __syncthreads();
+  return x;
+}
+
+template <int OP>
+__global__ __launch_bounds__(SC_T) void scan_reduce_kernel(const int32_t* in, int64_t m,
+                                                           int32_t* tile_tot) {
+  __shared__ int wbuf[SC_T / 64];
+  const int64_t base = (int64_t)blockIdx.x * SC_TILE + (int64_t)threadIdx.x * SC_I;
+  int acc = OP == 0 ? 0 : INT32_MIN;
+  for (int u = 0; u < SC_I; ++u)
+    if (base + u < m) acc = sc_op<OP>(acc, in[base + u]);
+  int r = block_scan_incl<OP>(acc, wbuf);
+  if (threadIdx.x == SC_T - 1) tile_tot[blockIdx.x] = r;
+}
+
+// Exclusive scan of the tile totals in one block (loops over chunks of SC_T).
+template <int OP>
+__global__ __launch_bounds__(SC_T) void scan_tiles_kernel(int32_t* tile_tot, int64_t ntiles) {
+  __shared__ int wbuf[SC_T / 64];
+  __shared__ int incl_buf[SC_T];
+  __shared__ int carry;
+  constexpr int ID = OP == 0 ? 0 : INT32_MIN;
+  if (threadIdx.x == 0) carry = ID;
+  __syncthreads();
+  for (int64_t c = 0; c < ntiles; c += SC_T) {
+    const int64_t i = c + threadIdx.x;
+    const int v = i < ntiles ? tile_tot[i] : ID;
+    const int incl = block_scan_incl<OP>(v, wbuf);
+    const int cin = carry;
+    incl_buf[threadIdx.x] = incl;
+    __syncthreads();
+    const int excl = threadIdx.x ? sc_op<OP>(cin, incl_buf[threadIdx.x - 1]) : cin;
+    if (i < ntiles) tile_tot[i] = excl;
+    __syncthreads();
+    if (threadIdx.x == SC_T - 1) carry = sc_op<OP>(cin, incl);
+    __syncthreads();
+  }
+}
+
+// Inclusive (INCL=1) or exclusive scan of `in` into `out` with the tile prefixes.
+template <int OP, int INCL>
+__global__ __launch_bounds__(SC_T) void scan_apply_kernel(const int32_t* in, int32_t* out,
+                                                          int64_t m, const int32_t* tile_pre) {
+  __shared__ int wbuf[SC_T / 64];
+  __shared__ int incl_buf[SC_T];
+  constexpr int ID = OP == 0 ? 0 : INT32_MIN;
+  const int64_t base = (int64_t)blockIdx.x * SC_TILE + (int64_t)threadIdx.x * SC_I;
+  int v[SC_I];
+  int acc = ID;
+#pragma unroll
+  for (int u = 0; u < SC_I; ++u) {
+    v[u] = base + u < m ? in[base + u] : ID;
+    acc = sc_op<OP>(acc, v[u]);
+  }
+  const int incl = block_scan_incl<OP>(acc, wbuf);
+  incl_buf[threadIdx.x] = incl;
+  __syncthreads();
+  int run = threadIdx.x ? incl_buf[threadIdx.x - 1] : ID;
+  run = sc_op<OP>(run, tile_pre[blockIdx.x]);
+#pragma unroll
+  for (int u = 0; u < SC_I; ++u) {
+    const int nxt = sc_op<OP>(run, v[u]);
+    if (base + u < m) out[base + u] = INCL ? nxt : run;
+    run = nxt;
+  }
+}
+
+template <int OP, int INCL>
+hipError_t scan_i32(const int32_t* in, int32_t* out, int64_t m, int32_t* tmp, hipStream_t st) {
+  if (m <= 0) return hipSuccess;
+  const int64_t nt = cdiv(m, SC_TILE);
+  hipLaunchKernelGGL((scan_reduce_kernel<OP>), dim3(nt), dim3(SC_T), 0, st, in, m, tmp);
+  hipLaunchKernelGGL((scan_tiles_kernel<OP>), dim3(1), dim3(SC_T), 0, st, tmp, nt);
+  hipLaunchKernelGGL((scan_apply_kernel<OP, INCL>), dim3(nt), dim3(SC_T), 0, st, in, out, m, tmp);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ stable LSD radix sort
+template <typename K>
+__global__ __launch_bounds__(RS_T) void rs_hist_kernel(const K* keys, int64_t n, int shift,
+                                                       int32_t* hist, int64_t ntiles) {
+  __shared__ int h[256];
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * RS_TILE;
+#pragma unroll 4
+  for (int i = 0; i < RS_I; ++i) {
+    const int64_t e = base + (int64_t)i * RS_T + threadIdx.x;
+    if (e < n) atomicAdd(&h[(int)((keys[e] >> shift) & 255)], 1);
+  }
+  __syncthreads();
+  hist[(int64_t)threadIdx.x * ntiles + blockIdx.x] = h[threadIdx.x];
+}
+
+template <typename K>
+__global__ __launch_bounds__(RS_T) void rs_scatter_kernel(const K* kin, const int32_t* vin,
+                                                          K* kout, int32_t* vout, int64_t n,
+                                                          int shift, const int32_t* offs,
+                                                          int64_t ntiles) {
+  __shared__ int run[256];
+  __shared__ int gbase[256];
+  __shared__ int wcnt[RS_T / 64][256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  run[tid] = 0;
+  gbase[tid] = offs[(int64_t)tid * ntiles + blockIdx.x];
+#pragma unroll
+  for (int x = 0; x < RS_T / 64; ++x) wcnt[x][tid] = 0;
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t base = (int64_t)blockIdx.x * RS_TILE;
+  for (int r = 0; r < RS_I; ++r) {
+    const int64_t e = base + (int64_t)r * RS_T + tid;
+    const bool valid = e < n;
+    const K key = valid ? kin[e] : K(0);
+    const int32_t val = valid ? vin[e] : 0;
+    const int d = (int)((key >> shift) & 255);
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const uint64_t bb = __ballot(valid && ((d >> bit) & 1));
+      m &= ((d >> bit) & 1) ? bb : ~bb;
+    }
+    const int wrank = __popcll(m & below);
+    if (valid && wrank == 0) wcnt[w][d] = __popcll(m);
+    __syncthreads();
+    int pre = 0;
+    if (valid) {
+      pre = run[d];
+      for (int x = 0; x < w; ++x) pre += wcnt[x][d];
+    }
+    __syncthreads();
+    {
+      int s = 0;
+#pragma unroll
+      for (int x = 0; x < RS_T / 64; ++x) {
+        s += wcnt[x][tid];
+        wcnt[x][tid] = 0;
+      }
+      run[tid] += s;
+    }
+    if (valid) {
+      const int64_t pos = (int64_t)gbase[d] + pre + wrank;
+      kout[pos] = key;
+      vout[pos] = val;
+    }
+    __syncthreads();
+  }
+}
+
+// Sorts (k[0..n), v[0..n)) by the key bits [0, bits) stably; the result ends in buffer
+// `*which` (0: k0/v0, 1: k1/v1).
+template <typename K>
+hipError_t radix_sort(K* k0, int32_t* v0, K* k1, int32_t* v1, int64_t n, int bits,
+                      int32_t* hist, int32_t* tmp, int* which, hipStream_t st) {
+  *which = 0;
+  if (n <= 1) return hipSuccess;
+  const int64_t nt = cdiv(n, RS_TILE);
+  K* ka = k0;
+  int32_t* va = v0;
+  K* kb = k1;
+  int32_t* vb = v1;
+  for (int shift = 0; shift < bits; shift += 8) {
+    hipLaunchKernelGGL((rs_hist_kernel<K>), dim3(nt), dim3(RS_T), 0, st, ka, n, shift, hist, nt);
+    hipError_t e = scan_i32<0, 0>(hist, hist, 256 * nt, tmp, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((rs_scatter_kernel<K>), dim3(nt), dim3(RS_T), 0, st, ka, va, kb, vb, n,
+                       shift, hist, nt);
+    std::swap(ka, kb);
+    std::swap(va, vb);
+    *which ^= 1;
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ prefix doubling kernels
+__global__ void minmax_kernel(const int32_t* text, int64_t n, int32_t* mm) {
+  int lo = INT32_MAX, hi = INT32_MIN;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int v = text[i];
+    lo = v < lo ? v : lo;
+    hi = v > hi ? v : hi;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const int a = __shfl_xor(lo, o, 64), b = __shfl_xor(hi, o, 64);
+    lo = a < lo ? a : lo;
+    hi = b > hi ? b : hi;
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicMin(&mm[0], lo);
+    atomicMax(&mm[1], hi);
+  }
+}
+
+__global__ void init_keys_kernel(const int32_t* text, int64_t n, int32_t tmin, uint64_t* k,
+                                 int32_t* v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  k[i] = (uint64_t)(uint32_t)((int64_t)text[i] - tmin);
+  v[i] = (int32_t)i;
+}
+
+// head[j] = j+1 if key[j] differs from key[j-1] (or j == 0), else 0
+__global__ void heads_kernel(const uint64_t* k, int64_t n, int32_t* head) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  head[j] = (j == 0 || k[j] != k[j - 1]) ? (int32_t)(j + 1) : 0;
+}
+
+// rank[v[j]] = group head index + 1 (from the inclusive max scan); count the groups
+__global__ void rank_kernel(const int32_t* v, const int32_t* headmax, const int32_t* head,
+                            int64_t n, int32_t* rank, uint32_t* ngroups) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int is_head = 0;
+  if (j < n) {
+    rank[v[j]] = headmax[j];
+    is_head = head[j] != 0;
+  }
+  const uint64_t bal = __ballot(is_head);
+  if ((threadIdx.x & 63) == 0 && bal) atomicAdd(ngroups, (uint32_t)__popcll(bal));
+}
+
+__global__ void pair_keys_kernel(const int32_t* v, const int32_t* rank, int64_t n, int64_t h,
+                                 int bits, uint64_t* k) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  const int64_t i = v[j];
+  const uint64_t r1 = (uint32_t)rank[i];
+  const uint64_t r2 = i + h < n ? (uint32_t)rank[i + h] : 0u;
+  k[j] = (r1 << bits) | r2;
+}
+
+__global__ void copy_i32_kernel(const int32_t* a, int32_t* b, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) b[i] = a[i];
+}
+
+inline int bits_for(uint64_t maxv) {
+  int b = 0;
+  while (b < 64 && (maxv >> b) != 0) ++b;
+  return b < 1 ? 1 : b;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ workspace
+size_t sa_workspace_bytes(int64_t n) {
+  const int64_t nn = n < 1 ? 1 : n;
+  const int64_t nt = cdiv(nn, RS_TILE);
+  size_t b = 0;
+  b += 2 * sizeof(uint64_t) * (size_t)nn;        // k0, k1
+  b += 2 * sizeof(int32_t) * (size_t)nn;         // v0, v1
+  b += 3 * sizeof(int32_t) * (size_t)nn;         // rank, head, aux
+  b += sizeof(int32_t) * (size_t)(256 * nt + 64);  // hist
+  b += sizeof(int32_t) * (size_t)(cdiv(256 * nt + nn, SC_TILE) + 64);  // scan tiles
+  b += 256;                                      // counters
+  b += 16 * 256;                                 // alignment slack
+  return b;
+}
+
+SaWork sa_carve(void* ws, int64_t n) {
+  const int64_t nn = n < 1 ? 1 : n;
+  const int64_t nt = cdiv(nn, RS_TILE);
+  uintptr_t p = ((uintptr_t)ws + 255) & ~(uintptr_t)255;
+  auto take = [&](size_t bytes) {
+    void* r = (void*)p;
+    p = (p + bytes + 255) & ~(uintptr_t)255;
+    return r;
+  };
+  SaWork w;
+  w.k0 = (uint64_t*)take(sizeof(uint64_t) * nn);
+  w.k1 = (uint64_t*)take(sizeof(uint64_t) * nn);
+  w.v0 = (int32_t*)take(sizeof(int32_t) * nn);
+  w.v1 = (int32_t*)take(sizeof(int32_t) * nn);
+  w.rank = (int32_t*)take(sizeof(int32_t) * nn);
+  w.head = (int32_t*)take(sizeof(int32_t) * nn);
+  w.aux = (int32_t*)take(sizeof(int32_t) * nn);
+  w.hist = (int32_t*)take(sizeof(int32_t) * (256 * nt + 64));
+  w.tiles = (int32_t*)take(sizeof(int32_t) * (cdiv(256 * nt + nn, SC_TILE) + 64));
+  w.counters = (uint32_t*)take(256);
+  w.n = nn;
+  return w;
+}
+
+hipError_t sa_build(const int32_t* text, int64_t n, int32_t* sa, const SaWork& w, hipStream_t st,
+                    int* rounds_out) {
+  if (rounds_out) *rounds_out = 0;
+  if (n <= 0) return hipSuccess;
+  const int TB = 256;
+  const int64_t gb = cdiv(n, TB);
+  // token range -> bits of the first sort
+  int32_t mm_init[2] = {INT32_MAX, INT32_MIN};
+  hipError_t e = hipMemcpyAsync(w.counters, mm_init, sizeof(mm_init), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(minmax_kernel, dim3((unsigned)std::min<int64_t>(gb, 4096)), dim3(TB), 0, st,
+                     text, n, (int32_t*)w.counters);
+  int32_t mm[2];
+  if ((e = hipMemcpyAsync(mm, w.counters, sizeof(mm), hipMemcpyDeviceToHost, st)) != hipSuccess)
+    return e;
+  if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+  hipLaunchKernelGGL(init_keys_kernel, dim3(gb), dim3(TB), 0, st, text, n, mm[0], w.k0, w.v0);
+  int which = 0;
+  e = radix_sort<uint64_t>(w.k0, w.v0, w.k1, w.v1, n,
+                           bits_for((uint64_t)((int64_t)mm[1] - mm[0])), w.hist, w.tiles, &which,
+                           st);
+  if (e != hipSuccess) return e;
+  uint64_t* kc = which ? w.k1 : w.k0;
+  int32_t* vc = which ? w.v1 : w.v0;
+  uint64_t* ko = which ? w.k0 : w.k1;
+  int32_t* vo = which ? w.v0 : w.v1;
+  const int rbits = bits_for((uint64_t)n);
+  int rounds = 0;
+  for (int64_t h = 0;; h = h ? 2 * h : 1) {
+    if (h > 0) {
+      hipLaunchKernelGGL(pair_keys_kernel, dim3(gb), dim3(TB), 0, st, vc, w.rank, n, h, rbits, kc);
+      e = radix_sort<uint64_t>(kc, vc, ko, vo, n, 2 * rbits, w.hist, w.tiles, &which, st);
+      if (e != hipSuccess) return e;
+      if (which) {
+        std::swap(kc, ko);
+        std::swap(vc, vo);
+      }
+    }
+    ++rounds;
+    hipLaunchKernelGGL(heads_kernel, dim3(gb), dim3(TB), 0, st, kc, n, w.head);
+    if ((e = scan_i32<1, 1>(w.head, w.aux, n, w.tiles, st)) != hipSuccess) return e;
+    if ((e = hipMemsetAsync(w.counters + 8, 0, sizeof(uint32_t), st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(rank_kernel, dim3(gb), dim3(TB), 0, st, vc, w.aux, w.head, n, w.rank,
+                       w.counters + 8);
+    uint32_t groups = 0;
+    if ((e = hipMemcpyAsync(&groups, w.counters + 8, sizeof(groups), hipMemcpyDeviceToHost, st)) !=
+        hipSuccess)
+      return e;
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+    if ((int64_t)groups == n || h >= n) break;
+  }
+  hipLaunchKernelGGL(copy_i32_kernel, dim3(gb), dim3(TB), 0, st, vc, sa, n);
+  if (rounds_out) *rounds_out = rounds;
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ n-gram probe tables
+namespace {
+
+// For SA position j: does suffix sa[j] start an n-gram occurrence that is followed by a token?
+__device__ __forceinline__ bool ngram_ok(const int32_t* text, int64_t n, int64_t i, int ng) {
+  if (i + ng >= n) return false;
+  for (int x = 0; x <= ng; ++x)
+    if (text[i + x] < 0) return false;
+  return true;
+}
+
+__global__ void ng_flags_kernel(const int32_t* text, const int32_t* sa, int64_t n, int ng,
+                                int32_t* valid, int32_t* head) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  const int64_t i = sa[j];
+  const bool ok = ngram_ok(text, n, i, ng);
+  bool hd = false;
+  if (ok) {
+    hd = true;
+    if (j > 0) {
+      const int64_t p = sa[j - 1];
+      if (ngram_ok(text, n, p, ng)) {
+        bool same = true;
+        for (int x = 0; x < ng; ++x) same = same && text[p + x] == text[i + x];
+        hd = !same;
+      }
+    }
+  }
+  valid[j] = ok ? 1 : 0;
+  head[j] = hd ? 1 : 0;
+}
+
+// At each group head: record the group's offset in the position list by group id.
+__global__ void ng_heads_kernel(const int32_t* head, const int32_t* gid_incl,
+                                const int32_t* cvalid_excl, int64_t n, int32_t* goff) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  if (head[j]) goff[gid_incl[j] - 1] = cvalid_excl[j];
+}
+
+__global__ void ng_total_kernel(const int32_t* valid, const int32_t* cvalid_excl,
+                                const int32_t* gid_incl, int64_t n, int32_t* goff,
+                                int32_t* ngroups) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  const int32_t G = gid_incl[n - 1];
+  goff[G] = cvalid_excl[n - 1] + valid[n - 1];
+  *ngroups = G;
+}
+
+// Group key of every position (by suffix-array scatter) and the hash insert of each group.
+__global__ void ng_groups_kernel(const int32_t* text, const int32_t* sa, int64_t n, int ng,
+                                 const int32_t* valid, const int32_t* head,
+                                 const int32_t* gid_incl, const int32_t* goff,
+                                 const int32_t* ngroups, uint32_t* gkey, NgramSlot* ht,
+                                 uint32_t mask) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  const int64_t i = sa[j];
+  const uint32_t none = (uint32_t)(*ngroups);
+  gkey[i] = valid[j] ? (uint32_t)(gid_incl[j] - 1) : none;
+  if (!head[j]) return;
+  const int32_t g = gid_incl[j] - 1;
+  int key[4] = {-1, -1, -1, -1};
+  for (int x = 0; x < ng; ++x) key[x] = text[i + x];
+  uint32_t h = ngram_hash(key, ng) & mask;
+  for (;;) {
+    const int prev = atomicCAS(&ht[h].owner, 0, g + 1);
+    if (prev == 0) break;
+    h = (h + 1) & mask;
+  }
+  for (int x = 0; x < 4; ++x) ht[h].key[x] = key[x];
+  ht[h].off = goff[g];
+  ht[h].cnt = goff[g + 1] - goff[g];
+}
+
+__global__ void iota_kernel(int32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = (int32_t)i;
+}
+
+}  // namespace
+
+hipError_t ngram_tables_build(const int32_t* text, const int32_t* sa, int64_t n, int32_t* pl[kNG],
+                              NgramSlot* ht[kNG], uint32_t ht_slots, const SaWork& w,
+                              hipStream_t st) {
+  if (n <= 0) {
+    // an empty snapshot still gets empty tables, so every probe ends at an empty slot
+    for (int g = 0; g < kNG; ++g) {
+      hipError_t e = hipMemsetAsync(ht[g], 0, sizeof(NgramSlot) * (size_t)ht_slots, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const int TB = 256;
+  const int64_t gb = cdiv(n, TB);
+  const uint32_t mask = ht_slots - 1;
+  // workspace reuse: valid/head/gid/cvalid in the int32 arrays, group offsets in k1 (before
+  // the sort needs it), group keys of positions in k0 (as uint32)
+  int32_t* valid = w.head;
+  int32_t* head = w.rank;
+  int32_t* gid = w.aux;
+  int32_t* cval = w.v1;
+  int32_t* goff = (int32_t*)w.k1;
+  uint32_t* gkey0 = (uint32_t*)w.k0;
+  uint32_t* gkey1 = (uint32_t*)w.k1;
+  int32_t* ngroups = (int32_t*)(w.counters + 16);
+  const int kbits = bits_for((uint64_t)n);
+  hipError_t e;
+  for (int g = 0; g < kNG; ++g) {
+    const int ng = g + 2;
+    hipLaunchKernelGGL(ng_flags_kernel, dim3(gb), dim3(TB), 0, st, text, sa, n, ng, valid, head);
+    if ((e = scan_i32<0, 1>(head, gid, n, w.tiles, st)) != hipSuccess) return e;
+    if ((e = scan_i32<0, 0>(valid, cval, n, w.tiles, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(ng_heads_kernel, dim3(gb), dim3(TB), 0, st, head, gid, cval, n, goff);
+    hipLaunchKernelGGL(ng_total_kernel, dim3(1), dim3(64), 0, st, valid, cval, gid, n, goff,
+                       ngroups);
+    if ((e = hipMemsetAsync(ht[g], 0, sizeof(NgramSlot) * (size_t)ht_slots, st)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(ng_groups_kernel, dim3(gb), dim3(TB), 0, st, text, sa, n, ng, valid, head,
+                       gid, goff, ngroups, gkey0, ht[g], mask);
+    // positions in increasing order, stably sorted by group id: each group's occurrences
+    // end up in position order
+    hipLaunchKernelGGL(iota_kernel, dim3(gb), dim3(TB), 0, st, w.v0, n);
+    int which = 0;
+    e = radix_sort<uint32_t>(gkey0, w.v0, gkey1, pl[g], n, kbits, w.hist, w.tiles, &which, st);
+    if (e != hipSuccess) return e;
+    if (!which) hipLaunchKernelGGL(copy_i32_kernel, dim3(gb), dim3(TB), 0, st, w.v0, pl[g], n);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sfx

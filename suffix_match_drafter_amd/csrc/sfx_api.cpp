@@ -1,0 +1,485 @@
+// sfx_api.cpp -- host side of libsfx: the C-ABI declared in include/sfx.h.
+//
+// Host code only validates, allocates at creation, and enqueues kernels.  The propose and ingest
+// paths never read device memory from the host.  The index rebuild is driven by the host
+// (one stream wait per doubling round), either inline on the caller's stream (sfx_rebuild) or
+// on a library-owned worker thread and side stream (sfx_rebuild_async + sfx_poll).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+
+#include "../../include/sfx.h"
+#include "corpus.h"
+#include "propose.h"
+#include "sa_build.h"
+
+using namespace sfx;
+
+namespace {
+
+thread_local std::string g_err = "no error";
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SFX_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_OR_RETURN(expr, what)                  \
+  do {                                             \
+    hipError_t e_ = (expr);                        \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+constexpr int kIngestChunk = 65536;  // documents per ingest launch
+
+uint32_t next_pow2_u32(uint64_t v) {
+  uint64_t p = 1;
+  while (p < v) p <<= 1;
+  return p > 0x80000000ull ? 0x80000000u : (uint32_t)p;
+}
+
+}  // namespace
+
+struct sfx_ctx {
+  sfx_config cfg{};
+  int device = 0;
+  // corpus (absent when corpus_capacity == 0)
+  Ctl* ctl = nullptr;
+  int32_t* ring = nullptr;
+  int64_t cap = 0;
+  int64_t* doc_start = nullptr;
+  int64_t dcap = 0;
+  int64_t* doc_off = nullptr;
+  int64_t* range_dev = nullptr;  // [2] snapshot range read back by the rebuild driver
+  IndexBuf idx[2]{};
+  uint32_t ht_slots = 0;
+  void* sa_ws = nullptr;
+  size_t sa_ws_bytes = 0;
+  SaWork saw{};
+  hipStream_t side = nullptr;
+  hipEvent_t ev_snap = nullptr;
+  hipEvent_t ev_done = nullptr;
+  int active_host = -1;  // host mirror of the live buffer
+  // asynchronous rebuild
+  std::thread worker;
+  std::atomic<int> async_state{0};  // 0 idle, 1 running, 2 finished
+  int async_buf = -1;
+  uint32_t async_mask = 0;
+  int async_err = SFX_OK;
+  std::string async_msg;
+};
+
+namespace {
+
+int validate(const sfx_config* c) {
+  if (!c) return fail(SFX_EINVAL, "config is NULL");
+  if (c->k < 1 || c->k > kMaxK) return fail(SFX_EINVAL, "k=%d outside [1,%d]", c->k, kMaxK);
+  if (c->max_tree_depth < 1 || c->max_tree_depth > kMaxD)
+    return fail(SFX_EINVAL, "max_tree_depth=%d outside [1,%d]", c->max_tree_depth, kMaxD);
+  if (c->num_backoff < 1 || c->num_backoff > kMaxNB)
+    return fail(SFX_EINVAL, "num_backoff=%d outside [1,%d]", c->num_backoff, kMaxNB);
+  if (c->max_occurrences < 1 || c->max_occurrences > kMaxM)
+    return fail(SFX_EINVAL, "max_occurrences=%d outside [1,%d]", c->max_occurrences, kMaxM);
+  if (c->mode != SFX_MODE_LONGEST_FILL && c->mode != SFX_MODE_SCORED)
+    return fail(SFX_EINVAL, "mode=%d unknown", c->mode);
+  if (c->mode == SFX_MODE_LONGEST_FILL && c->num_backoff != 1)
+    return fail(SFX_EINVAL, "LONGEST_FILL mode takes num_backoff == 1 (got %d)", c->num_backoff);
+  if (c->min_self_match < 1) return fail(SFX_EINVAL, "min_self_match must be >= 1");
+  if (c->max_batch < 0) return fail(SFX_EINVAL, "max_batch must be >= 0");
+  if (c->max_seq < 0 || c->max_seq > 65536)
+    return fail(SFX_EINVAL, "max_seq=%d outside [0,65536]", c->max_seq);
+  if (c->max_sampled < 0 || c->max_sampled > kMaxT)
+    return fail(SFX_EINVAL, "max_sampled=%d outside [0,%d]", c->max_sampled, kMaxT);
+  if (c->spec_factor_ppm < 0) return fail(SFX_EINVAL, "max_spec_factor must be >= 0");
+  if (c->spec_offset_ppm < 0) return fail(SFX_EINVAL, "max_spec_offset must be >= 0");
+  if (c->spec_factor_ppm > (int64_t)1e15 || c->spec_offset_ppm > (int64_t)1e15)
+    return fail(SFX_EINVAL, "spec factor/offset too large");
+  if (c->min_token_prob_ppm < 0 || c->min_token_prob_ppm > 1000000)
+    return fail(SFX_EINVAL, "min_token_prob must be in [0,1]");
+  if (c->corpus_capacity < 0 || c->corpus_capacity > (int64_t(1) << 30))
+    return fail(SFX_EINVAL, "corpus_capacity outside [0, 2^30]");
+  if (c->corpus_capacity > 0) {
+    if (c->max_tree_depth < 2)
+      return fail(SFX_EINVAL, "a corpus needs max_tree_depth >= 2 (last-2 probe)");
+    if (c->min_corpus_match < 2 || c->min_corpus_match > c->max_tree_depth)
+      return fail(SFX_EINVAL, "min_corpus_match=%d outside [2, max_tree_depth]",
+                  c->min_corpus_match);
+  }
+  return SFX_OK;
+}
+
+void free_ctx(sfx_ctx* c) {
+  auto f = [](void* p) {
+    if (p) (void)hipFree(p);
+  };
+  f(c->ctl);
+  f(c->ring);
+  f(c->doc_start);
+  f(c->doc_off);
+  f(c->range_dev);
+  for (auto& b : c->idx) {
+    f(b.text);
+    f(b.sa);
+    for (int g = 0; g < kNG; ++g) {
+      f(b.pl[g]);
+      f(b.ht[g]);
+    }
+  }
+  f(c->sa_ws);
+  if (c->side) (void)hipStreamDestroy(c->side);
+  if (c->ev_snap) (void)hipEventDestroy(c->ev_snap);
+  if (c->ev_done) (void)hipEventDestroy(c->ev_done);
+  delete c;
+}
+
+// Table size for n snapshot tokens: a power of two at least twice any possible group count.
+uint32_t slots_for(const sfx_ctx* c, int64_t n) {
+  uint32_t s = next_pow2_u32((uint64_t)(n < 1 ? 1 : n) * 2);
+  return s > c->ht_slots ? c->ht_slots : s;
+}
+
+// Suffix array and probe tables of buffer `buf`, whose snapshot range was recorded on `st`.
+int build_index(sfx_ctx* c, int buf, hipStream_t st, uint32_t* mask_out) {
+  int64_t range[2] = {0, 0};
+  HIP_OR_RETURN(hipMemcpyAsync(range, c->range_dev, sizeof range, hipMemcpyDeviceToHost, st),
+                "snapshot range read");
+  HIP_OR_RETURN(hipStreamSynchronize(st), "snapshot wait");
+  const int64_t n = range[1] - range[0];
+  if (n < 0 || n > c->cap) return fail(SFX_EHIP, "corrupt snapshot range");
+  IndexBuf& b = c->idx[buf];
+  HIP_OR_RETURN(sa_build(b.text, n, b.sa, c->saw, st, nullptr), "suffix array build");
+  const uint32_t slots = slots_for(c, n);
+  HIP_OR_RETURN(ngram_tables_build(b.text, b.sa, n, b.pl, b.ht, slots, c->saw, st),
+                "probe table build");
+  *mask_out = slots - 1;
+  return SFX_OK;
+}
+
+int check_ctx(sfx_ctx* c) {
+  if (!c) return fail(SFX_EINVAL, "context is NULL");
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess && dev != c->device)
+    return fail(SFX_EINVAL, "context was created on device %d, current device is %d", c->device,
+                dev);
+  return SFX_OK;
+}
+
+void finish_async(sfx_ctx* c) {
+  if (c->worker.joinable()) c->worker.join();
+}
+
+int swap_in(sfx_ctx* c, hipStream_t st) {
+  HIP_OR_RETURN(hipStreamWaitEvent(st, c->ev_done, 0), "wait for rebuild");
+  HIP_OR_RETURN(launch_swap(c->ctl, c->async_buf, c->async_mask, st), "swap launch");
+  c->active_host = c->async_buf;
+  c->async_state.store(0);
+  return SFX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sfx_last_error(void) { return g_err.c_str(); }
+
+int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
+  if (!out) return fail(SFX_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = validate(cfg);
+  if (rc) return rc;
+  sfx_ctx* c = new sfx_ctx();
+  c->cfg = *cfg;
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    delete c;
+    return fail(SFX_EHIP, "no HIP device");
+  }
+  hipError_t e = propose_prepare(propose_dynamic_lds(cfg->max_seq, cfg->max_sampled));
+  if (e != hipSuccess) {
+    free_ctx(c);
+    return hip_fail(e, "propose kernel attributes");
+  }
+  if (cfg->corpus_capacity > 0) {
+    c->cap = cfg->corpus_capacity;
+    c->dcap = c->cap + 1;
+    c->ht_slots = next_pow2_u32((uint64_t)c->cap * 2);
+    auto al = [&](void** p, size_t bytes) { return hipMalloc(p, bytes) == hipSuccess; };
+    bool ok = al((void**)&c->ctl, sizeof(Ctl)) && al((void**)&c->ring, 4 * c->cap) &&
+              al((void**)&c->doc_start, 8 * c->dcap) &&
+              al((void**)&c->doc_off, 8 * (kIngestChunk + 1)) &&
+              al((void**)&c->range_dev, 32);
+    for (int bi = 0; bi < 2 && ok; ++bi) {
+      IndexBuf& b = c->idx[bi];
+      ok = al((void**)&b.text, 4 * c->cap) && al((void**)&b.sa, 4 * c->cap);
+      for (int g = 0; g < kNG && ok; ++g)
+        ok = al((void**)&b.pl[g], 4 * c->cap) &&
+             al((void**)&b.ht[g], sizeof(NgramSlot) * (size_t)c->ht_slots);
+    }
+    c->sa_ws_bytes = sa_workspace_bytes(c->cap);
+    ok = ok && al(&c->sa_ws, c->sa_ws_bytes);
+    if (!ok) {
+      free_ctx(c);
+      return fail(SFX_ENOMEM, "device allocation failed for a corpus of %lld tokens",
+                  (long long)cfg->corpus_capacity);
+    }
+    c->saw = sa_carve(c->sa_ws, c->cap);
+    if (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&c->ev_snap, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c->ev_done, hipEventDisableTiming) != hipSuccess) {
+      free_ctx(c);
+      return fail(SFX_EHIP, "stream/event creation failed");
+    }
+    if ((e = launch_ctl_init(c->ctl, c->side)) != hipSuccess ||
+        (e = hipStreamSynchronize(c->side)) != hipSuccess) {
+      free_ctx(c);
+      return hip_fail(e, "control block init");
+    }
+  }
+  *out = c;
+  return SFX_OK;
+}
+
+void sfx_destroy(sfx_ctx* c) {
+  if (!c) return;
+  finish_async(c);
+  if (c->side) (void)hipStreamSynchronize(c->side);
+  free_ctx(c);
+}
+
+int sfx_propose(sfx_ctx* c, int32_t B, int32_t S, int32_t T, const int32_t* ntns,
+                const int32_t* tok, const int32_t* samp, int32_t* draft, int32_t* nvalid,
+                void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  const sfx_config& g = c->cfg;
+  if (B < 0 || S < 0 || T < 0) return fail(SFX_EINVAL, "negative shape B=%d S=%d T=%d", B, S, T);
+  if (B > g.max_batch || S > g.max_seq || T > g.max_sampled)
+    return fail(SFX_ECAPACITY, "shape B=%d S=%d T=%d above max_batch=%d max_seq=%d max_sampled=%d",
+                B, S, T, g.max_batch, g.max_seq, g.max_sampled);
+  if (B == 0) return SFX_OK;
+  if (!ntns || !draft || !nvalid || (S > 0 && !tok) || (T > 0 && !samp))
+    return fail(SFX_EINVAL, "NULL array argument");
+  ProposeArgs a{};
+  a.B = B;
+  a.S = S;
+  a.T = T;
+  a.ntns = ntns;
+  a.tok = tok;
+  a.samp = samp;
+  a.draft = draft;
+  a.nvalid = nvalid;
+  a.k = g.k;
+  a.D = g.max_tree_depth;
+  a.nb = g.num_backoff;
+  a.M = g.max_occurrences;
+  a.mode = g.mode;
+  a.min_self = g.min_self_match;
+  a.min_corpus = g.min_corpus_match;
+  a.factor_ppm = g.spec_factor_ppm;
+  a.offset_ppm = g.spec_offset_ppm;
+  a.prob_ppm = g.min_token_prob_ppm;
+  a.ctl = c->ctl;
+  a.idx[0] = c->idx[0];
+  a.idx[1] = c->idx[1];
+  a.ring = c->ring;
+  a.ring_cap = c->cap > 0 ? c->cap : 1;
+  HIP_OR_RETURN(launch_propose(a, (hipStream_t)stream), "propose launch");
+  return SFX_OK;
+}
+
+int sfx_update_state(int32_t B, int32_t S, int32_t T, int32_t* tok, const int32_t* ntns,
+                     const int32_t* samp, int32_t* nout, void* stream) {
+  if (B < 0 || S < 0 || T < 0) return fail(SFX_EINVAL, "negative shape");
+  if (B == 0) return SFX_OK;
+  if (!ntns || !nout || (S > 0 && !tok) || (T > 0 && !samp))
+    return fail(SFX_EINVAL, "NULL array argument");
+  HIP_OR_RETURN(launch_update_state(B, S, T, tok, ntns, samp, nout, (hipStream_t)stream),
+                "update_state launch");
+  return SFX_OK;
+}
+
+static int ingest_common(sfx_ctx* c, IngestArgs a, int hint, hipStream_t st) {
+  a.ctl = c->ctl;
+  a.ring = c->ring;
+  a.cap = c->cap;
+  a.doc_start = c->doc_start;
+  a.dcap = c->dcap;
+  a.doc_off = c->doc_off;
+  const int R = a.R;
+  for (int r0 = 0; r0 < R; r0 += kIngestChunk) {
+    IngestArgs ch = a;
+    ch.R = R - r0 < kIngestChunk ? R - r0 : kIngestChunk;
+    if (ch.doc_offsets) ch.doc_offsets += r0;
+    else {
+      ch.row_indices += r0;
+      ch.lengths += r0;
+    }
+    HIP_OR_RETURN(launch_ingest(ch, hint, st), "ingest launch");
+  }
+  return SFX_OK;
+}
+
+int sfx_harvest_finished(sfx_ctx* c, int32_t R, const int32_t* rows, const int32_t* lengths,
+                         const int32_t* tok, int32_t num_rows, int32_t S, void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!c->ctl) return fail(SFX_ESTATE, "context has no corpus (corpus_capacity == 0)");
+  if (R < 0 || S < 0 || num_rows < 0) return fail(SFX_EINVAL, "negative shape");
+  if (R == 0) return SFX_OK;
+  if (!rows || !lengths || (S > 0 && num_rows > 0 && !tok))
+    return fail(SFX_EINVAL, "NULL array argument");
+  IngestArgs a{};
+  a.R = R;
+  a.row_indices = rows;
+  a.lengths = lengths;
+  a.num_rows = num_rows;
+  a.S = S;
+  a.tokens = tok;
+  return ingest_common(c, a, S, (hipStream_t)stream);
+}
+
+int sfx_ingest(sfx_ctx* c, int32_t num_docs, const int64_t* offs, const int32_t* tokens,
+               void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!c->ctl) return fail(SFX_ESTATE, "context has no corpus (corpus_capacity == 0)");
+  if (num_docs < 0) return fail(SFX_EINVAL, "negative num_docs");
+  if (num_docs == 0) return SFX_OK;
+  if (!offs || !tokens) return fail(SFX_EINVAL, "NULL array argument");
+  IngestArgs a{};
+  a.R = num_docs;
+  a.doc_offsets = offs;
+  a.tokens = tokens;
+  return ingest_common(c, a, 1 << 16, (hipStream_t)stream);
+}
+
+static int pick_buffer(sfx_ctx* c) { return c->active_host == 0 ? 1 : 0; }
+
+int sfx_rebuild(sfx_ctx* c, void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!c->ctl) return fail(SFX_ESTATE, "context has no corpus (corpus_capacity == 0)");
+  if (c->async_state.load() != 0) return fail(SFX_ESTATE, "an asynchronous rebuild is in flight");
+  hipStream_t st = (hipStream_t)stream;
+  const int buf = pick_buffer(c);
+  HIP_OR_RETURN(launch_snapshot(c->ctl, c->ring, c->cap, c->idx[buf].text, buf, c->range_dev, st),
+                "snapshot launch");
+  uint32_t mask = 0;
+  if ((rc = build_index(c, buf, st, &mask)) != SFX_OK) return rc;
+  HIP_OR_RETURN(launch_swap(c->ctl, buf, mask, st), "swap launch");
+  c->active_host = buf;
+  return SFX_OK;
+}
+
+int sfx_rebuild_async(sfx_ctx* c, void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!c->ctl) return fail(SFX_ESTATE, "context has no corpus (corpus_capacity == 0)");
+  if (c->async_state.load() != 0) return fail(SFX_ESTATE, "an asynchronous rebuild is in flight");
+  finish_async(c);
+  hipStream_t st = (hipStream_t)stream;
+  const int buf = pick_buffer(c);
+  HIP_OR_RETURN(launch_snapshot(c->ctl, c->ring, c->cap, c->idx[buf].text, buf, c->range_dev, st),
+                "snapshot launch");
+  HIP_OR_RETURN(hipEventRecord(c->ev_snap, st), "snapshot event");
+  c->async_buf = buf;
+  c->async_err = SFX_OK;
+  c->async_state.store(1);
+  c->worker = std::thread([c, buf]() {
+    (void)hipSetDevice(c->device);
+    int r = SFX_OK;
+    uint32_t mask = 0;
+    if (hipStreamWaitEvent(c->side, c->ev_snap, 0) != hipSuccess) r = fail(SFX_EHIP, "wait");
+    if (r == SFX_OK) r = build_index(c, buf, c->side, &mask);
+    if (r == SFX_OK && hipEventRecord(c->ev_done, c->side) != hipSuccess)
+      r = fail(SFX_EHIP, "rebuild event");
+    if (r == SFX_OK && hipStreamSynchronize(c->side) != hipSuccess)
+      r = fail(SFX_EHIP, "rebuild wait");
+    c->async_mask = mask;
+    c->async_err = r;
+    if (r != SFX_OK) c->async_msg = g_err;
+    c->async_state.store(2);
+  });
+  return SFX_OK;
+}
+
+int sfx_poll(sfx_ctx* c, int32_t* swapped, void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (swapped) *swapped = 0;
+  if (!c->ctl || c->async_state.load() != 2) return SFX_OK;
+  finish_async(c);
+  if (c->async_err != SFX_OK) {
+    c->async_state.store(0);
+    return fail(c->async_err, "asynchronous rebuild failed: %s", c->async_msg.c_str());
+  }
+  if ((rc = swap_in(c, (hipStream_t)stream)) != SFX_OK) return rc;
+  if (swapped) *swapped = 1;
+  return SFX_OK;
+}
+
+int sfx_wait_rebuild(sfx_ctx* c, void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!c->ctl || c->async_state.load() == 0) return SFX_OK;
+  finish_async(c);
+  if (c->async_err != SFX_OK) {
+    c->async_state.store(0);
+    return fail(c->async_err, "asynchronous rebuild failed: %s", c->async_msg.c_str());
+  }
+  return swap_in(c, (hipStream_t)stream);
+}
+
+int sfx_corpus_snapshot(sfx_ctx* c, int32_t* text_out, int64_t cap, int64_t* n_out,
+                        void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!n_out) return fail(SFX_EINVAL, "n_out is NULL");
+  *n_out = 0;
+  if (!c->ctl) return SFX_OK;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_OR_RETURN(launch_live_range(c->ctl, c->range_dev + 2, st), "range launch");
+  int64_t range[2];
+  HIP_OR_RETURN(hipMemcpyAsync(range, c->range_dev + 2, sizeof range, hipMemcpyDeviceToHost, st),
+                "range read");
+  HIP_OR_RETURN(hipStreamSynchronize(st), "range wait");
+  const int64_t n = range[1] - range[0];
+  *n_out = n;
+  if (n > cap) return fail(SFX_ECAPACITY, "live corpus has %lld tokens, buffer %lld",
+                           (long long)n, (long long)cap);
+  if (n > 0 && !text_out) return fail(SFX_EINVAL, "text_out is NULL");
+  HIP_OR_RETURN(launch_ring_copy(c->ctl, c->ring, c->cap, text_out, cap, st), "copy launch");
+  HIP_OR_RETURN(hipStreamSynchronize(st), "copy wait");
+  return SFX_OK;
+}
+
+size_t sfx_suffix_array_workspace_bytes(int64_t n) { return sa_workspace_bytes(n); }
+
+int sfx_build_suffix_array(const int32_t* text, int64_t n, int32_t* sa, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (n < 0 || n > (int64_t(1) << 30)) return fail(SFX_EINVAL, "n=%lld outside [0,2^30]",
+                                                   (long long)n);
+  if (n == 0) return SFX_OK;
+  if (!text || !sa || !ws) return fail(SFX_EINVAL, "NULL array argument");
+  if (ws_bytes < sa_workspace_bytes(n))
+    return fail(SFX_ECAPACITY, "workspace of %zu bytes, %zu needed", ws_bytes,
+                sa_workspace_bytes(n));
+  SaWork w = sa_carve(ws, n);
+  HIP_OR_RETURN(sa_build(text, n, sa, w, (hipStream_t)stream, nullptr), "suffix array build");
+  return SFX_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,247 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle, bit-exact.
+
+Drafts, valid counts, suffix arrays, updated rows and live corpora must be identical element by
+element on the same seeded inputs.  Sizes span several tiles with ragged tails; the workload
+configurations run at full size."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = min(16, len(os.sched_getaffinity(0)))
+
+
+@pytest.fixture(scope="module")
+def S():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import suffix_match_drafter_amd as sfx
+
+    sfx.load()
+    return sfx
+
+
+def dev(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_gpu(S, knobs, n, tok, samp, corpus_docs=None, capacity=0, drafter=None):
+    import torch
+
+    B, Sq = tok.shape
+    T = samp.shape[1]
+    d = drafter
+    if d is None:
+        cfg = S.Config(max_batch=max(B, 1), max_seq=max(Sq, 1), max_sampled=max(T, 1),
+                       corpus_capacity=capacity, **knobs)
+        d = S.Drafter(cfg)
+        if corpus_docs is not None:
+            d.ingest_docs(corpus_docs)
+            d.rebuild()
+    draft, nv = d.propose(dev(n), dev(tok), dev(samp))
+    torch.cuda.synchronize()
+    return draft.cpu().numpy(), nv.cpu().numpy(), d
+
+
+def assert_same(got, exp, what=""):
+    gd, gn = got
+    ed, en = exp
+    bad = np.nonzero((gd != ed).any(axis=1) | (gn != en))[0]
+    assert bad.size == 0, (f"{what}: {bad.size} rows differ, first {bad[:5].tolist()}; "
+                           f"row {bad[0]}: gpu {gd[bad[0]].tolist()}/{gn[bad[0]]} "
+                           f"oracle {ed[bad[0]].tolist()}/{en[bad[0]]}")
+
+
+def knobs_of(w):
+    return w.knobs()
+
+
+# ------------------------------------------------------------------ fuzz and edge cases
+@pytest.mark.parametrize("mode", [0, 1])
+def test_fuzz_small(S, mode):
+    rng = np.random.default_rng(100 + mode)
+    for it in range(40):
+        V = int(rng.choice([2, 3, 5, 50]))
+        B = int(rng.integers(1, 9))
+        Sq = int(rng.integers(1, 300))
+        T = int(rng.integers(0, 4))
+        nb = 1 if mode == 0 else int(rng.integers(1, 9))
+        kn = dict(k=int(rng.integers(1, 33)), max_tree_depth=int(rng.choice([1, 2, 3, 7, 24, 64])),
+                  num_backoff=nb, max_occurrences=int(rng.choice([1, 2, 5, 64, 128])), mode=mode,
+                  spec_factor_ppm=int(rng.choice([0, 500_000, 2_000_000])),
+                  spec_offset_ppm=int(rng.choice([0, 1_000_000])),
+                  min_token_prob_ppm=int(rng.choice([0, 100_000, 500_000, 1_000_000])),
+                  min_self_match=int(rng.choice([1, 1, 2])))
+        tok = rng.integers(0, V, size=(B, Sq)).astype(np.int32)
+        n = rng.integers(-3, Sq + 4, size=B).astype(np.int32)
+        samp = rng.integers(-1, V, size=(B, T)).astype(np.int32)
+        exp = O.propose(O.params_from(kn), n, tok, samp)
+        got = run_gpu(S, kn, n, tok, samp)[:2]
+        assert_same(got, exp, f"fuzz it={it} kn={kn} B={B} S={Sq} T={T}")
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_fuzz_with_corpus(S, mode):
+    rng = np.random.default_rng(200 + mode)
+    for it in range(25):
+        V = int(rng.choice([2, 3, 6, 40]))
+        B = int(rng.integers(1, 7))
+        Sq = int(rng.integers(2, 200))
+        nb = 1 if mode == 0 else int(rng.integers(1, 9))
+        D = int(rng.choice([2, 3, 4, 5, 6, 9, 24]))
+        kn = dict(k=int(rng.integers(1, 17)), max_tree_depth=D, num_backoff=nb,
+                  max_occurrences=int(rng.choice([1, 3, 128])), mode=mode,
+                  spec_factor_ppm=int(rng.choice([1_000_000, 2_000_000])),
+                  min_token_prob_ppm=int(rng.choice([0, 100_000, 400_000])),
+                  min_corpus_match=int(rng.integers(2, D + 1)))
+        docs = [rng.integers(0, V, size=int(rng.integers(0, 60))).astype(np.int32)
+                for _ in range(int(rng.integers(1, 40)))]
+        lc = O.LiveCorpus(10**7)
+        lc.ingest(docs)
+        tok = rng.integers(0, V, size=(B, Sq)).astype(np.int32)
+        n = rng.integers(0, Sq + 1, size=B).astype(np.int32)
+        samp = rng.integers(0, V, size=(B, 1)).astype(np.int32)
+        exp = O.propose(O.params_from(kn), n, tok, samp, corpus=lc.text())
+        got = run_gpu(S, kn, n, tok, samp, corpus_docs=docs, capacity=1 << 14)[:2]
+        assert_same(got, exp, f"corpus fuzz it={it} kn={kn}")
+
+
+def test_degenerate_rows(S):
+    """Empty rows, rows with no sampled token, a single repeated token (every position
+    matches), n above S, S not a multiple of 4, T=0."""
+    B, Sq = 6, 301
+    tok = np.full((B, Sq), 7, np.int32)
+    n = np.array([0, 1, 301, 400, -5, 150], np.int32)
+    samp = np.array([[7, -1], [-1, 3], [7, 7], [2, -1], [7, -1], [7, 7]], np.int32)
+    for mode in (0, 1):
+        kn = dict(k=32, max_tree_depth=64, num_backoff=1 + 7 * mode, max_occurrences=128,
+                  mode=mode, spec_factor_ppm=10**7, min_token_prob_ppm=0)
+        exp = O.propose(O.params_from(kn), n, tok, samp)
+        assert_same(run_gpu(S, kn, n, tok, samp)[:2], exp, f"degenerate mode {mode}")
+    kn = dict(k=4, max_tree_depth=24, num_backoff=1, max_occurrences=128, mode=0)
+    e0 = O.propose(O.params_from(kn), n, tok, samp[:, :0])
+    assert_same(run_gpu(S, kn, n, tok, samp[:, :0])[:2], e0, "T=0")
+
+
+# ------------------------------------------------------------------ workload configurations
+@pytest.mark.parametrize("cid", [1, 2])
+def test_config_self_match(S, cid):
+    w = W.WORKLOADS[cid]
+    n, tok, samp = W.make_batch(cid)
+    exp = O.propose(O.params_from(w.knobs()), n, tok, samp, num_threads=NTHREADS)
+    got = run_gpu(S, w.knobs(), n, tok, samp)[:2]
+    assert_same(got, exp, f"config {cid}")
+    assert (got[1] <= w.k).all()
+    assert (got[0] != W.POISON).all()
+
+
+@pytest.mark.parametrize("cid", [3, 4])
+def test_config_corpus(S, cid):
+    import torch
+
+    w = W.WORKLOADS[cid]
+    docs = W.corpus_docs(cid)
+    text = W.join_docs(docs)
+    n, tok, samp = W.make_batch(cid)
+    cap = 1 << 20
+    got_d, got_n, d = run_gpu(S, w.knobs(), n, tok, samp, corpus_docs=docs, capacity=cap)
+    snap = d.corpus_snapshot().cpu().numpy()
+    assert np.array_equal(snap, text)
+    exp = O.propose(O.params_from(w.knobs()), n, tok, samp, corpus=text, num_threads=NTHREADS)
+    assert_same((got_d, got_n), exp, f"config {cid}")
+    # a second call on the same context is identical (no state leaks between calls)
+    d2, n2 = d.propose(dev(n), dev(tok), dev(samp))
+    torch.cuda.synchronize()
+    assert np.array_equal(d2.cpu().numpy(), got_d) and np.array_equal(n2.cpu().numpy(), got_n)
+    d.close()
+
+
+# ------------------------------------------------------------------ suffix arrays
+@pytest.mark.parametrize("n,V", [(1, 5), (2, 1), (17, 2), (1000, 3), (4097, 2), (70001, 50),
+                                 (250000, 7)])
+def test_suffix_array_random(S, n, V):
+    rng = np.random.default_rng(n)
+    text = rng.integers(-1, V, size=n).astype(np.int32)
+    sa = S.build_suffix_array(dev(text)).cpu().numpy()
+    assert np.array_equal(sa, O.suffix_array(text))
+
+
+def test_suffix_array_repetitive(S):
+    # long repeats force many doubling rounds
+    base = np.arange(37, dtype=np.int32)
+    text = np.concatenate([np.tile(base, 60), [-1], np.tile(base[:5], 300), [-1]]).astype(np.int32)
+    sa = S.build_suffix_array(dev(text)).cpu().numpy()
+    assert np.array_equal(sa, O.suffix_array(text))
+
+
+def test_suffix_array_template_corpus(S):
+    text = W.join_docs(W.corpus_docs(4))
+    sa = S.build_suffix_array(dev(text)).cpu().numpy()
+    assert np.array_equal(sa, O.suffix_array(text))
+
+
+# ------------------------------------------------------------------ state update
+def test_update_state(S):
+    import torch
+
+    rng = np.random.default_rng(5)
+    B, Sq, T = 37, 129, 3
+    tok = rng.integers(0, 100, size=(B, Sq)).astype(np.int32)
+    n = rng.integers(-2, Sq + 3, size=B).astype(np.int32)
+    samp = rng.integers(-1, 100, size=(B, T)).astype(np.int32)
+    exp_tok, exp_n = O.update_state(tok, n, samp)
+    t = dev(tok)
+    got_n = S.update_state(t, dev(n), dev(samp))
+    torch.cuda.synchronize()
+    assert np.array_equal(t.cpu().numpy(), exp_tok)
+    assert np.array_equal(got_n.cpu().numpy(), exp_n)
+
+
+# ------------------------------------------------------------------ ingest, eviction, rebuild
+def test_ring_eviction_and_delta(S):
+    """Documents appended past the capacity evict the oldest; drafts are defined on the live
+    corpus whether a document is indexed (rebuilt) or still in the delta."""
+    import torch
+
+    rng = np.random.default_rng(9)
+    V = 6
+    kn = dict(k=6, max_tree_depth=8, num_backoff=3, max_occurrences=7, mode=1,
+              spec_factor_ppm=3_000_000, min_token_prob_ppm=100_000)
+    cap = 3000
+    cfg = S.Config(max_batch=16, max_seq=256, max_sampled=1, corpus_capacity=cap, **kn)
+    d = S.Drafter(cfg)
+    live = O.LiveCorpus(cap)
+    B, Sq = 16, 256
+    for step in range(12):
+        R = int(rng.integers(1, 9))
+        rows = rng.integers(0, V, size=(R, 200)).astype(np.int32)
+        lens = rng.integers(-5, 230, size=R).astype(np.int32)
+        idx = rng.permutation(R).astype(np.int32)
+        d.harvest_finished(dev(idx), dev(lens), dev(rows))
+        live.ingest(O.harvest_docs(rows, idx, lens))
+        if step % 3 == 1:
+            d.wait_rebuild()
+            d.rebuild()
+        if step % 4 == 2:
+            d.rebuild_async()
+            if step % 8 == 2:
+                d.wait_rebuild()
+        assert np.array_equal(d.corpus_snapshot().cpu().numpy(), live.text()), step
+        tok = rng.integers(0, V, size=(B, Sq)).astype(np.int32)
+        n = rng.integers(0, Sq + 1, size=B).astype(np.int32)
+        samp = rng.integers(0, V, size=(B, 1)).astype(np.int32)
+        exp = O.propose(O.params_from(kn), n, tok, samp, corpus=live.text())
+        got = run_gpu(S, kn, n, tok, samp, drafter=d)[:2]
+        assert_same(got, exp, f"ring step {step}")
+        d.poll()
+    d.wait_rebuild()
+    torch.cuda.synchronize()
+    d.close()
