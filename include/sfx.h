@@ -69,7 +69,7 @@ typedef struct sfx_config {
   int32_t min_self_match;   /* shortest self match that makes a candidate, >= 1 */
   int32_t min_corpus_match; /* shortest corpus match that makes a candidate, 2..max_tree_depth */
   int32_t max_batch;        /* largest B accepted by sfx_propose */
-  int32_t max_seq;          /* largest S accepted by sfx_propose (row capacity) */
+  int32_t max_seq;          /* largest S accepted by sfx_propose (row capacity), 0..32768 */
   int32_t max_sampled;      /* largest T accepted by sfx_propose, 0..16 */
   int64_t spec_factor_ppm;  /* max_spec_factor * 1e6, >= 0 (SCORED) */
   int64_t spec_offset_ppm;  /* max_spec_offset * 1e6, >= 0 (SCORED) */

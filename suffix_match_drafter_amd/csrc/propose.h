@@ -21,6 +21,9 @@ struct ProposeArgs {
 };
 
 size_t propose_dynamic_lds(int S, int T);
+// Static LDS of the propose kernel (the per-request bookkeeping).
+size_t propose_static_lds();
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one gfx950 workgroup
 // Allows `dyn` bytes of dynamic LDS on every propose kernel instantiation.
 hipError_t propose_prepare(size_t dyn);
 hipError_t launch_propose(const ProposeArgs& a, hipStream_t st);

@@ -1,16 +1,21 @@
 // propose.hip -- the drafter step on gfx950: one workgroup (16 wavefronts) per request.
 //
 // Steps, in the order of the suffix-gpu page, How it works:
-//   1. local match: a backward match length against the tail for every earlier position,
-//      kept as bytes in LDS with a length histogram -> num_backoff ladder lengths (t-th largest
-//      value) and, per ladder length, the earliest max_occurrences continuation sites;
-//   2. global match (vLLM docs, Model Runner V2: probe by the last 2 and last 4 tokens, extend
-//      to the longest match): 2-, 3- and 4-gram probes into hash tables over the suffix-array
-//      groups of the live snapshot, backward extension of the 4-gram occurrences, plus a
-//      brute-force scan of the not-yet-indexed delta documents;
-//   3. expansion: one wavefront per candidate votes depth by depth over its sites with an LDS
-//      hash of token counts; stop rule and score use integer cross-multiplication; selection
-//      and the [k] output row are written by thread 0.
+//   1. local match (step 1): the request's context is staged in LDS with every 16-byte load in
+//      flight at once; each wavefront owns a contiguous chunk of end positions (lanes on
+//      consecutive positions, so LDS reads are conflict-free) and computes the backward match
+//      length against the tail of every position, into a per-wavefront length histogram.  The
+//      histograms give the ladder (t-th largest length) and, per wavefront, the exact offsets
+//      of its earliest continuation sites, so one ordered pass writes the sites of every level;
+//   2. global match (step 2; vLLM docs, Model Runner V2: probe by the last 2 and last 4 tokens,
+//      extend to the longest match): 2-, 3- and 4-gram probes into hash tables over the
+//      suffix-array groups of the live snapshot and backward extension of the 4-gram
+//      occurrences.  Without a delta, a dedicated wavefront does all of it -- probes, ladder and
+//      sites -- while the other fifteen stage the context.  With a delta (documents appended
+//      since the snapshot) the whole workgroup scans the delta by brute force and merges;
+//   3. expansion (step 3): one wavefront per candidate votes depth by depth over its sites
+//      (ballots when few sites are alive, an LDS hash otherwise); stop rule and score use
+//      integer cross-multiplication; selection and the [k] output row follow.
 #include "propose.h"
 
 namespace sfx {
@@ -19,7 +24,10 @@ namespace {
 
 constexpr int NT = 1024;
 constexpr int NW = NT / 64;
+constexpr int GW = NW - 1;          // the corpus wavefront of the fast path
 constexpr int kVoteSlots = 256;
+constexpr int kStageUnroll = 8;     // 16-byte loads in flight per thread while staging
+constexpr int kSmallVote = 24;      // alive sites at or below this vote with ballots
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -27,19 +35,56 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+// DPP controls (GFX9 encoding): cross-lane moves inside the VALU, no LDS round trip.
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside a row of 16
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside a half row of 8
+constexpr int kDppRowBcast15 = 0x142; // lane 15 of each row to the next row
+constexpr int kDppRowBcast31 = 0x143; // lane 31 to rows 2 and 3
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_incl_add(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
   return v;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, 64);
-    v = w > v ? w : v;
-  }
-  return v;
+__device__ __forceinline__ int wave_sum(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_add(v), 63);
+}
+
+// Maximum / minimum over the 64 lanes (every lane takes part).
+__device__ __forceinline__ int wave_max(int v) {
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppQuadXor1, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppQuadXor2, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppHalfMirror, 0xF, 0xF, false));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppMirror, 0xF, 0xF, false));
+  const int a0 = __builtin_amdgcn_readlane(v, 0), a1 = __builtin_amdgcn_readlane(v, 16);
+  const int a2 = __builtin_amdgcn_readlane(v, 32), a3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a0, a1), max(a2, a3));
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+  v = min(v, __builtin_amdgcn_mov_dpp(v, kDppQuadXor1, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_mov_dpp(v, kDppQuadXor2, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_mov_dpp(v, kDppHalfMirror, 0xF, 0xF, false));
+  v = min(v, __builtin_amdgcn_mov_dpp(v, kDppMirror, 0xF, 0xF, false));
+  const int a0 = __builtin_amdgcn_readlane(v, 0), a1 = __builtin_amdgcn_readlane(v, 16);
+  const int a2 = __builtin_amdgcn_readlane(v, 32), a3 = __builtin_amdgcn_readlane(v, 48);
+  return min(min(a0, a1), min(a2, a3));
+}
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
 // Exclusive prefix sum of one int per thread over the workgroup; *total gets the sum.
@@ -73,7 +118,7 @@ __device__ __forceinline__ int ctx_at(const int32_t* row, const int32_t* smp, in
   return x < n ? row[x] : smp[x - n];
 }
 
-// Count one vote for `tok` in the wavefront's LDS table; returns the slot used.
+// Count one vote for `tok` in a wavefront's LDS table; returns the slot used.
 __device__ __forceinline__ int vote_insert(int* hk, int* hc, int tok) {
   uint32_t h = ((uint32_t)tok * 0x9E3779B1u) >> 24;
   for (;;) {
@@ -87,12 +132,10 @@ __device__ __forceinline__ int vote_insert(int* hk, int* hc, int tok) {
 }
 
 struct Smem {
-  int n, t, L, Lcap;
-  int has_index, active;
-  long long snap_start, snap_n, tail_w, delta_lo, delta_hi;
-  uint32_t ht_mask;
   int tail[kMaxD];
-  int hist[kMaxD + 1];
+  int gtail[kMaxD];
+  int whist[NW][kMaxD + 1];
+  int wsuf[NW][kMaxD + 2];
   int ghist[kMaxD + 1];
   int dhist[kMaxD + 1];
   int g_off[kNG], g_live[kNG];
@@ -102,10 +145,21 @@ struct Smem {
   int cand_out[2 * kMaxNB][kMaxK];
   int lsites[kMaxNB][kMaxM];
   long long gsites[kMaxNB][kMaxM];
-  const int32_t* plp[kNG];  // position lists of the live buffer, indexable by n-gram size
+  int wpre[kMaxNB][NW];
+  int clist[NW][256];  // per-wavefront positions of two-token matches to extend
+  const int32_t* plp[kNG];
   int wsum[NW + 1];
-  int vkey[NW][kVoteSlots];
-  int vcnt[NW][kVoteSlots];
+  int sel[2];
+};
+
+// Shape of one request and the corpus state it sees.  Every thread derives it from the same
+// uniform loads, so no thread waits for another before the staging starts.
+struct Req {
+  int n, t, L, J, Lcap, C;
+  int act;
+  bool has, fast;
+  long long snap_start, snap_n, tail_w, delta_lo, delta_hi;
+  uint32_t ht_mask;
 };
 
 __device__ __forceinline__ int spec_cap(const ProposeArgs& a, int l) {
@@ -127,10 +181,10 @@ struct View {
   const NgramSlot* ht2;
   uint32_t mask;
 };
-__device__ __forceinline__ View view_of(const ProposeArgs& a, int act) {
+__device__ __forceinline__ View view_of(const ProposeArgs& a, int act, uint32_t mask) {
   const bool z = act == 0;
   View v;
-  v.mask = 0;
+  v.mask = mask;
   v.text = z ? a.idx[0].text : a.idx[1].text;
   v.pl0 = z ? a.idx[0].pl[0] : a.idx[1].pl[0];
   v.pl1 = z ? a.idx[0].pl[1] : a.idx[1].pl[1];
@@ -140,6 +194,7 @@ __device__ __forceinline__ View view_of(const ProposeArgs& a, int act) {
   v.ht2 = z ? a.idx[0].ht[2] : a.idx[1].ht[2];
   return v;
 }
+
 // Probe of the (G+2)-gram that ends the context: its group in the position list, minus the
 // prefix of occurrences in documents evicted since the snapshot.
 template <int G>
@@ -186,6 +241,18 @@ __device__ void probe_ngram(const View& ib, const int* tail, int Lcap, long long
   *live_out = live;
 }
 
+// Backward extension of a 4-gram occurrence starting at snapshot position i: the match length
+// (>= 4) against the tail, at most `cap`.
+__device__ __forceinline__ int extend4(const int32_t* text, const int* tail, int i, int cap) {
+  int m = 4;
+  while (m < cap && i - 1 - (m - 4) >= 0) {
+    const int c = text[i - 1 - (m - 4)];
+    if (c < 0 || c != tail[m]) break;
+    ++m;
+  }
+  return m;
+}
+
 // Corpus token at logical position q: snapshot text below snap_end, ring slot above.
 __device__ __forceinline__ int corpus_at(const ProposeArgs& a, const int32_t* text,
                                          long long snap_start, long long snap_n, long long q) {
@@ -194,158 +261,371 @@ __device__ __forceinline__ int corpus_at(const ProposeArgs& a, const int32_t* te
   return a.ring[q % a.ring_cap];
 }
 
+// The corpus wavefront of the fast path (live snapshot, no delta): tail from global memory,
+// probes, extension of the live 4-gram occurrences, global ladder and earliest sites.
+__device__ void corpus_wave_fast(const ProposeArgs& a, const Req& r, Smem& sm,
+                                 const int32_t* row, const int32_t* smp, int lane) {
+  const int n = r.n, L = r.L, Lcap = r.Lcap, nb = a.nb, M = a.M;
+  if (lane < Lcap) sm.gtail[lane] = ctx_at(row, smp, n, L - 1 - lane);
+  if (lane <= kMaxD) sm.ghist[lane] = 0;
+  wave_sync();
+  const View ib = view_of(a, r.act, r.ht_mask);
+  const long long snap_start = r.snap_start;
+  const long long dead_below = r.tail_w - snap_start;
+  if (lane == 0) probe_ngram<0>(ib, sm.gtail, Lcap, dead_below, &sm.g_off[0], &sm.g_live[0]);
+  if (lane == 1) probe_ngram<1>(ib, sm.gtail, Lcap, dead_below, &sm.g_off[1], &sm.g_live[1]);
+  if (lane == 2) probe_ngram<2>(ib, sm.gtail, Lcap, dead_below, &sm.g_off[2], &sm.g_live[2]);
+  wave_sync();
+  const int live4 = sm.g_live[2];
+  const int32_t* pl4 = ib.pl2 + sm.g_off[2];
+  if (Lcap >= 5 && live4 > 0) {
+    for (int x = lane; x < live4; x += 64) {
+      const int m = extend4(ib.text, sm.gtail, pl4[x], Lcap);
+      if (m >= 5) atomicAdd(&sm.ghist[m], 1);
+    }
+  }
+  wave_sync();
+  if (lane == 0) {
+    int gcum = 0, ti = 0;
+    for (int l = Lcap; l >= 2 && ti < nb; --l) {
+      gcum += sm.ghist[l];
+      const int cnt = l <= 4 ? sm.g_live[l - 2] : gcum;
+      while (ti < nb && cnt >= ti + 1) {
+        sm.cand_len[nb + ti] = l;
+        sm.cand_sup[nb + ti] = cnt;
+        ++ti;
+      }
+    }
+    for (; ti < nb; ++ti) {
+      sm.cand_len[nb + ti] = 0;
+      sm.cand_sup[nb + ti] = 0;
+    }
+    const int minc = a.min_corpus > 2 ? a.min_corpus : 2;
+    for (int i = 0; i < nb; ++i) {
+      const int ci = nb + i;
+      sm.cand_valid[ci] = sm.cand_len[ci] >= minc;
+      sm.cand_c0[ci] = sm.cand_sup[ci] < M ? sm.cand_sup[ci] : M;
+      sm.cand_src[ci] =
+          (i > 0 && sm.cand_len[ci] == sm.cand_len[ci - 1]) ? sm.cand_src[ci - 1] : ci;
+    }
+  }
+  wave_sync();
+  const uint64_t below = lanes_below(lane);
+  for (int ti = 0; ti < nb; ++ti) {
+    const int ci = nb + ti;
+    if (!sm.cand_valid[ci] || sm.cand_src[ci] != ci) continue;
+    const int l = sm.cand_len[ci];
+    long long* gs = sm.gsites[ti];
+    if (l <= 4) {
+      const int g = l - 2;
+      const int32_t* pl = (g == 0 ? ib.pl0 : (g == 1 ? ib.pl1 : ib.pl2)) + sm.g_off[g];
+      const int ns = sm.g_live[g] < M ? sm.g_live[g] : M;
+      for (int x = lane; x < ns; x += 64) gs[x] = (long long)pl[x] + l + snap_start;
+    } else {
+      int run = 0;
+      for (int base = 0; base < live4 && run < M; base += 64) {
+        const int x = base + lane;
+        const int i = x < live4 ? pl4[x] : 0;
+        const bool q = x < live4 && extend4(ib.text, sm.gtail, i, l) >= l;
+        const uint64_t bal = __ballot(q);
+        const int rk = run + __popcll(bal & below);
+        if (q && rk < M) gs[rk] = (long long)i + 4 + snap_start;
+        run += __popcll(bal);
+      }
+    }
+  }
+}
+
+// Stage the context (row prefix and leading sampled ids) in LDS with `nst` threads.
+template <bool VEC>
+__device__ __forceinline__ void stage_context(int* ctxs, const int32_t* row, const int32_t* smp,
+                                              int n, int t, int stid, int nst) {
+  if (VEC) {
+    for (int base = 0; base < n; base += nst * 4 * kStageUnroll) {
+      int4 q[kStageUnroll];
+#pragma unroll
+      for (int u = 0; u < kStageUnroll; ++u) {
+        const int i4 = base + (u * nst + stid) * 4;
+        q[u] = i4 + 3 < n ? *reinterpret_cast<const int4*>(row + i4) : make_int4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kStageUnroll; ++u) {
+        const int i4 = base + (u * nst + stid) * 4;
+        if (i4 + 3 < n) {
+          *reinterpret_cast<int4*>(ctxs + i4) = q[u];
+        } else if (i4 < n) {
+          for (int x = i4; x < n; ++x) ctxs[x] = row[x];
+        }
+      }
+    }
+  } else {
+    for (int x = stid; x < n; x += nst) ctxs[x] = row[x];
+  }
+  for (int x = stid; x < t; x += nst) ctxs[n + x] = smp[x];
+}
+
+// Ints of dynamic LDS before the length bytes: the context, at least the vote tables.
+__host__ __device__ inline int propose_row_ints(int S, int T) {
+  int ints = (S + T + 4 + 3) & ~3;
+  const int vote = NW * 2 * kVoteSlots;
+  return ints < vote ? vote : ints;
+}
+
 template <int KMAX, bool VEC>
 __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
-  extern __shared__ uint8_t mbs[];
+  extern __shared__ int4 ctx4[];
+  int* ctxs = reinterpret_cast<int*>(ctx4);
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = blockIdx.x;
   const int32_t* row = a.tok + (int64_t)b * a.S;
   const int32_t* smp = a.samp + (int64_t)b * a.T;
   const int D = a.D, nb = a.nb, M = a.M;
+  const uint64_t below = lanes_below(lane);
 
-  if (tid == 0) {
+  Req r;
+  {
     int n = a.ntns[b];
     n = n < 0 ? 0 : (n > a.S ? a.S : n);
     int t = 0;
     while (t < a.T && smp[t] >= 0) ++t;
-    sm.n = n;
-    sm.t = t;
-    sm.L = n + t;
-    sm.Lcap = D < n + t ? D : n + t;
-    int has = 0, act = -1;
-    if (a.ctl) {
-      act = a.ctl->active;
-      has = 1;
-      sm.tail_w = a.ctl->tail;
-      long long head = a.ctl->head;
-      if (act >= 0) {
-        sm.ht_mask = a.ctl->ht_mask[act];
-        sm.snap_start = a.ctl->snap_start[act];
-        sm.snap_n = a.ctl->snap_end[act] - sm.snap_start;
-        long long lo = a.ctl->snap_end[act];
-        sm.delta_lo = lo > sm.tail_w ? lo : sm.tail_w;
+    r.n = n;
+    r.t = t;
+    r.L = n + t;
+    r.J = r.L > 0 ? r.L - 1 : 0;
+    r.Lcap = D < r.L ? D : r.L;
+    r.has = a.ctl != nullptr;
+    r.act = -1;
+    r.fast = false;
+    r.snap_start = r.snap_n = r.tail_w = r.delta_lo = r.delta_hi = 0;
+    r.ht_mask = 0;
+    bool delta = false;
+    if (r.has) {
+      const Ctl* c = a.ctl;
+      r.act = c->active;
+      r.tail_w = c->tail;
+      r.delta_hi = c->head;
+      if (r.act >= 0) {
+        r.ht_mask = r.act == 0 ? c->ht_mask[0] : c->ht_mask[1];
+        r.snap_start = r.act == 0 ? c->snap_start[0] : c->snap_start[1];
+        const long long se = r.act == 0 ? c->snap_end[0] : c->snap_end[1];
+        r.snap_n = se - r.snap_start;
+        r.delta_lo = se > r.tail_w ? se : r.tail_w;
       } else {
-        sm.snap_start = 0;
-        sm.snap_n = 0;
-        sm.delta_lo = sm.tail_w;
+        r.delta_lo = r.tail_w;
       }
-      sm.delta_hi = head;
+      delta = r.delta_hi - r.delta_lo > 1;
+      r.fast = r.act >= 0 && r.snap_n > 0 && !delta && r.Lcap >= 2;
     }
-    sm.has_index = has;
-    sm.active = act;
+    const int nww = r.fast ? NW - 1 : NW;
+    r.C = (((r.J + nww - 1) / nww) + 255) / 256 * 256;
   }
-  if (tid <= kMaxD) {
-    sm.hist[tid] = 0;
-    sm.ghist[tid] = 0;
-    sm.dhist[tid] = 0;
-  }
-  __syncthreads();
-  const int n = sm.n, t = sm.t, L = sm.L, Lcap = sm.Lcap;
+  const int n = r.n, t = r.t, L = r.L, Lcap = r.Lcap, J = r.J, C = r.C;
   int32_t* drow = a.draft + (int64_t)b * a.k;
   if (t == 0) {
     for (int i = tid; i < a.k; i += NT) drow[i] = -1;
     if (tid == 0) a.nvalid[b] = 0;
     return;
   }
-  for (int i = tid; i < Lcap; i += NT) sm.tail[i] = ctx_at(row, smp, n, L - 1 - i);
+  const bool fast = r.fast;
+  for (int i = tid; i < NW * (kMaxD + 1); i += NT) (&sm.whist[0][0])[i] = 0;
+  if (!fast && tid < 2 * kMaxNB) sm.cand_valid[tid] = 0;
+
+  // ---------------------------------------------------------------- stage || corpus wave
+  if (fast && wid == GW) {
+    corpus_wave_fast(a, r, sm, row, smp, lane);
+  } else {
+    stage_context<VEC>(ctxs, row, smp, n, t, tid, fast ? NT - 64 : NT);
+  }
   __syncthreads();
 
   // ---------------------------------------------------------------- 1. local match lengths
-  const int J = L - 1;  // candidate ends j = 0..L-2
-  {
-    const int t0 = sm.tail[0];
-    int ones = 0;
-    for (int j0 = tid * 4; j0 < J; j0 += NT * 4) {
-      int v[4];
-      if (VEC && j0 + 3 < n) {
-        int4 q = *reinterpret_cast<const int4*>(row + j0);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-      } else {
+  // Wavefront w < NWW owns end positions [w*C, w*C + C); lane l reads 4 of them per round
+  // (one 16-byte LDS read), screens the last two tail tokens in registers and extends the rare
+  // two-token matches with a wavefront-uniform loop.  Lengths are kept as bytes in LDS.
+  const int NWW = fast ? NW - 1 : NW;
+  const bool worker = wid < NWW;
+  const int cbeg = worker ? (wid * C < J ? wid * C : J) : J;
+  const int cend = worker ? (cbeg + C < J ? cbeg + C : J) : J;
+  uint8_t* mbs = reinterpret_cast<uint8_t*>(ctxs + propose_row_ints(a.S, a.T));
+  if (tid < Lcap) sm.tail[tid] = ctxs[L - 1 - tid];
+  if (worker) {
+    const int t0 = ctxs[L - 1];
+    const int t1 = L >= 2 ? ctxs[L - 2] : -1;
+    const bool two = D >= 2;
+    // tail tokens at offsets off0 .. off0+3 for this lane's share of an extension
+    const int off0 = 2 + 4 * (lane & 15);
+    int tq[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = j0 + u < J ? ctx_at(row, smp, n, j0 + u) : 0;
+    for (int x = 0; x < 4; ++x) tq[x] = off0 + x < L ? ctxs[L - 1 - off0 - x] : -1;
+    int ones = 0;
+    for (int r0 = cbeg; r0 < cend; r0 += 256) {
+      const int j0 = r0 + 4 * lane;
+      int v0 = -1, v1 = -1, v2 = -1, v3 = -1, pv = -1;
+      if (j0 < cend) {
+        const int4 q = ctx4[j0 >> 2];
+        v0 = q.x; v1 = q.y; v2 = q.z; v3 = q.w;
+        pv = j0 > 0 ? ctxs[j0 - 1] : -1;
       }
+      int m[4];
+      m[0] = (j0 < cend && v0 == t0) ? ((two && j0 >= 1 && pv == t1) ? 2 : 1) : 0;
+      m[1] = (j0 + 1 < cend && v1 == t0) ? ((two && v0 == t1) ? 2 : 1) : 0;
+      m[2] = (j0 + 2 < cend && v2 == t0) ? ((two && v1 == t1) ? 2 : 1) : 0;
+      m[3] = (j0 + 3 < cend && v3 == t0) ? ((two && v2 == t1) ? 2 : 1) : 0;
+      if (j0 < cend)
+        *reinterpret_cast<uint32_t*>(mbs + j0) =
+            (uint32_t)m[0] | ((uint32_t)m[1] << 8) | ((uint32_t)m[2] << 16) | ((uint32_t)m[3] << 24);
+      // two-token matches that may go further are compacted and extended below; the others
+      // are final
+      uint32_t cf = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int jj = j0 + u;
-        if (jj < J) {
-          int m = 0;
-          if (v[u] == t0) {
-            m = 1;
-            const int lim = D < jj + 1 ? D : jj + 1;
-            while (m < lim && ctx_at(row, smp, n, jj - m) == sm.tail[m]) ++m;
+        const int lim = D < j0 + u + 1 ? D : j0 + u + 1;
+        if (m[u] == 2 && lim > 2) cf |= 1u << u;
+        else if (m[u] == 1) ++ones;
+        else if (m[u] == 2) atomicAdd(&sm.whist[wid][2], 1);
+      }
+      const int cc = __popc(cf);
+      const int cincl = wave_incl_add(cc);
+      const int ctot = __builtin_amdgcn_readlane(cincl, 63);
+      if (ctot) {
+        int slot = cincl - cc;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (cf & (1u << u)) sm.clist[wid][slot++] = j0 + u;
+        wave_sync();
+        // sixteen lanes per candidate, four tail offsets per lane: the first mismatching
+        // offset over the row of sixteen is the match length
+        for (int p = 0; p < ctot; p += 4) {
+          const int ci = p + (lane >> 4);
+          const bool ok = ci < ctot;
+          const int j = ok ? sm.clist[wid][ci] : 0;
+          const int lim = D < j + 1 ? D : j + 1;
+          int fm = lim;
+#pragma unroll
+          for (int x = 3; x >= 0; --x) {
+            const int o = off0 + x;
+            if (ok && o < lim && ctxs[j - o] != tq[x]) fm = o;
           }
-          mbs[jj] = (uint8_t)m;
-          if (m == 1) ++ones;
-          else if (m > 1) atomicAdd(&sm.hist[m], 1);
+          fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppQuadXor1, 0xF, 0xF, false));
+          fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppQuadXor2, 0xF, 0xF, false));
+          fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppHalfMirror, 0xF, 0xF, false));
+          fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppMirror, 0xF, 0xF, false));
+          if (ok && (lane & 15) == 0) {
+            mbs[j] = (uint8_t)fm;
+            atomicAdd(&sm.whist[wid][fm], 1);
+          }
         }
+        wave_sync();
       }
     }
     ones = wave_sum(ones);
-    if (lane == 0 && ones) atomicAdd(&sm.hist[1], ones);
+    if (lane == 0) atomicAdd(&sm.whist[wid][1], ones);
+    wave_sync();
+    // this wavefront's suffix sums: wsuf[w][v] = its positions with length >= v
+    const int h = lane <= D ? sm.whist[wid][lane] : 0;
+    const int incl = wave_incl_add(h);
+    sm.wsuf[wid][lane] = __builtin_amdgcn_readlane(incl, 63) - incl + h;
   }
   __syncthreads();
-
-  // local ladder: l_t = t-th largest match length
-  if (tid == 0) {
-    int cum = 0, ti = 0;
+  // ladder (wavefront 0): count_ge(v) in lane v; l_t = largest v with count_ge(v) >= t
+  if (wid == 0) {
+    int cg = 0;
+    for (int w = 0; w < NWW; ++w) cg += sm.wsuf[w][lane];
     const int maxl = D < J ? D : J;
-    for (int l = maxl; l >= 1 && ti < nb; --l) {
-      cum += sm.hist[l];
-      while (ti < nb && cum >= ti + 1) {
-        sm.cand_len[ti] = l;
-        sm.cand_sup[ti] = cum;
-        ++ti;
-      }
-    }
-    for (; ti < nb; ++ti) {
-      sm.cand_len[ti] = 0;
-      sm.cand_sup[ti] = 0;
-    }
     const int mins = a.min_self > 1 ? a.min_self : 1;
-    for (int i = 0; i < nb; ++i) {
-      sm.cand_valid[i] = sm.cand_len[i] >= mins;
-      sm.cand_c0[i] = sm.cand_sup[i] < M ? sm.cand_sup[i] : M;
-      sm.cand_src[i] = (i > 0 && sm.cand_len[i] == sm.cand_len[i - 1]) ? sm.cand_src[i - 1] : i;
+    for (int ti = 0; ti < nb; ++ti) {
+      const uint64_t ok = __ballot(lane >= 1 && lane <= maxl && cg >= ti + 1);
+      const int l = ok ? 63 - __builtin_clzll(ok) : 0;
+      const int sup = l ? __builtin_amdgcn_readlane(cg, l) : 0;
+      if (lane == 0) {
+        sm.cand_len[ti] = l;
+        sm.cand_sup[ti] = sup;
+        sm.cand_valid[ti] = l >= mins;
+        sm.cand_c0[ti] = sup < M ? sup : M;
+        sm.cand_src[ti] = (ti > 0 && l == sm.cand_len[ti - 1]) ? sm.cand_src[ti - 1] : ti;
+      }
+      // exclusive per-wavefront offsets of this level's sites
+      const int c = (l >= 1 && lane < NWW) ? sm.wsuf[lane][l] : 0;
+      const int x = wave_incl_add(c);
+      if (lane < NW) sm.wpre[ti][lane] = x - c;
+      wave_sync();
     }
   }
   __syncthreads();
 
-  // earliest sites per distinct ladder length: ordered compaction over the LDS lengths
-  {
-    const int seg = (J + NT - 1) / NT;
-    const int lo = tid * seg < J ? tid * seg : J;
-    const int hi = lo + seg < J ? lo + seg : J;
-    for (int ti = 0; ti < nb; ++ti) {
-      if (!sm.cand_valid[ti] || sm.cand_src[ti] != ti) continue;  // uniform
-      const int l = sm.cand_len[ti];
-      int c = 0;
-      for (int j = lo; j < hi; ++j) c += mbs[j] >= l;
-      int total;
-      int r = block_exclusive_scan(c, sm.wsum, &total);
-      if (c && r < M) {
-        for (int j = lo; j < hi && r < M; ++j)
-          if (mbs[j] >= l) sm.lsites[ti][r++] = j + 1;
+  // earliest sites of every distinct local level: 16 length bytes per lane, SWAR compares,
+  // wavefront prefix sums for the order
+  if (worker) {
+    int lv[kMaxNB], pre[kMaxNB], run[kMaxNB];
+    bool act[kMaxNB];
+    bool any = false;
+#pragma unroll
+    for (int ti = 0; ti < kMaxNB; ++ti) {
+      act[ti] = ti < nb && sm.cand_valid[ti] && sm.cand_src[ti] == ti && sm.wpre[ti][wid] < M;
+      lv[ti] = act[ti] ? sm.cand_len[ti] : 0;
+      pre[ti] = act[ti] ? sm.wpre[ti][wid] : 0;
+      run[ti] = 0;
+      any = any || act[ti];
+    }
+    for (int r0 = cbeg; any && r0 < cend; r0 += 1024) {
+      const int jb = r0 + 16 * lane;
+      uint4 q = make_uint4(0, 0, 0, 0);
+      uint32_t keep = 0;
+      if (jb < cend) {
+        q = *reinterpret_cast<const uint4*>(mbs + jb);
+        const int nbytes = cend - jb;
+        keep = nbytes >= 16 ? 0xFFFFu : ((1u << nbytes) - 1u);
+      }
+      any = false;
+#pragma unroll
+      for (int ti = 0; ti < kMaxNB; ++ti) {
+        if (act[ti]) {
+          const uint32_t sub = (uint32_t)lv[ti] * 0x01010101u;
+          uint32_t flags = 0;
+          const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const uint32_t ge = ((wd[x] | 0x80808080u) - sub) & 0x80808080u;
+            const uint32_t nib = ((ge >> 7) & 1u) | ((ge >> 14) & 2u) | ((ge >> 21) & 4u) |
+                                 ((ge >> 28) & 8u);
+            flags |= nib << (4 * x);
+          }
+          flags &= keep;
+          const int c = __popc(flags);
+          const int incl = wave_incl_add(c);
+          const int tot = __builtin_amdgcn_readlane(incl, 63);
+          int rk = pre[ti] + run[ti] + incl - c;
+          while (flags && rk < M) {
+            const int bpos = __builtin_ctz(flags);
+            sm.lsites[ti][rk++] = jb + bpos + 1;
+            flags &= flags - 1;
+          }
+          run[ti] += tot;
+          act[ti] = pre[ti] + run[ti] < M;
+          any = any || act[ti];
+        }
       }
     }
   }
 
-  // ---------------------------------------------------------------- 2. global match
-  for (int i = tid; i < nb; i += NT) sm.cand_valid[nb + i] = 0;
-  __syncthreads();
-  if (sm.has_index && Lcap >= 2) {
-    const int act = sm.active;
-    const long long snap_start = sm.snap_start;
-    const long long dead_below = sm.tail_w - snap_start;  // snapshot coords of live start
-    View ib = view_of(a, act >= 0 ? act : 0);
-    ib.mask = sm.ht_mask;
+  // ---------------------------------------------------------------- 2. global (general path)
+  if (r.has && !fast && Lcap >= 2) {
+    if (tid <= kMaxD) {
+      sm.ghist[tid] = 0;
+      sm.dhist[tid] = 0;
+    }
+    __syncthreads();
+    const int act = r.act;
+    const long long snap_start = r.snap_start;
+    const long long dead_below = r.tail_w - snap_start;
+    const View ib = view_of(a, act >= 0 ? act : 0, r.ht_mask);
     if (tid == 0) {
       sm.plp[0] = ib.pl0;
       sm.plp[1] = ib.pl1;
       sm.plp[2] = ib.pl2;
     }
-    // probes: thread g looks up the (g+2)-gram ending at the last token
-    if (act >= 0 && sm.snap_n > 0) {
+    if (act >= 0 && r.snap_n > 0) {
       if (tid == 0) probe_ngram<0>(ib, sm.tail, Lcap, dead_below, &sm.g_off[0], &sm.g_live[0]);
       if (tid == 1) probe_ngram<1>(ib, sm.tail, Lcap, dead_below, &sm.g_off[1], &sm.g_live[1]);
       if (tid == 2) probe_ngram<2>(ib, sm.tail, Lcap, dead_below, &sm.g_off[2], &sm.g_live[2]);
@@ -354,33 +634,25 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       sm.g_live[tid] = 0;
     }
     __syncthreads();
-    // backward extension of the live 4-gram occurrences
     const int live4 = sm.g_live[2];
     if (act >= 0 && Lcap >= 5 && live4 > 0) {
       const int32_t* pl4 = ib.pl2 + sm.g_off[2];
-      const int32_t* text = ib.text;
       for (int x = tid; x < live4; x += NT) {
-        const int i = pl4[x];
-        int m = 4;
-        while (m < Lcap && i - 1 - (m - 4) >= 0) {
-          int c = text[i - 1 - (m - 4)];
-          if (c < 0 || c != sm.tail[m]) break;
-          ++m;
-        }
+        const int m = extend4(ib.text, sm.tail, pl4[x], Lcap);
         if (m >= 5) atomicAdd(&sm.ghist[m], 1);
       }
     }
     // delta: documents appended since the live snapshot, scanned by brute force
-    const long long dlo = sm.delta_lo, dhi = sm.delta_hi;
+    const long long dlo = r.delta_lo, dhi = r.delta_hi;
     if (dhi - dlo > 1) {
-      const int t0 = sm.tail[0];
+      const int tt0 = sm.tail[0];
       for (long long e = dlo + tid; e + 1 < dhi; e += NT) {
         const int c = a.ring[e % a.ring_cap];
-        if (c != t0) continue;
+        if (c != tt0) continue;
         if (a.ring[(e + 1) % a.ring_cap] < 0) continue;
         int m = 1;
         while (m < Lcap && e - m >= dlo) {
-          int x = a.ring[(e - m) % a.ring_cap];
+          const int x = a.ring[(e - m) % a.ring_cap];
           if (x < 0 || x != sm.tail[m]) break;
           ++m;
         }
@@ -388,7 +660,6 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       }
     }
     __syncthreads();
-    // global ladder: count_ge(l) = snapshot support + delta support
     if (tid == 0) {
       int dcum = 0, gcum = 0, ti = 0;
       for (int l = Lcap; l >= 2 && ti < nb; --l) {
@@ -412,8 +683,8 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
         const int ci = nb + i;
         sm.cand_valid[ci] = sm.cand_len[ci] >= minc;
         sm.cand_c0[ci] = sm.cand_sup[ci] < M ? sm.cand_sup[ci] : M;
-        sm.cand_src[ci] = (i > 0 && sm.cand_len[ci] == sm.cand_len[ci - 1]) ? sm.cand_src[ci - 1]
-                                                                             : ci;
+        sm.cand_src[ci] =
+            (i > 0 && sm.cand_len[ci] == sm.cand_len[ci - 1]) ? sm.cand_src[ci - 1] : ci;
       }
     }
     __syncthreads();
@@ -433,33 +704,17 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
           for (int x = tid; x < nsnap; x += NT) gs[x] = (long long)pl[x] + l + snap_start;
         } else {
           const int32_t* pl4 = ib.pl2 + sm.g_off[2];
-          const int32_t* text = ib.text;
           const int seg = (live4 + NT - 1) / NT;
           const int lo = tid * seg < live4 ? tid * seg : live4;
           const int hi = lo + seg < live4 ? lo + seg : live4;
           int c = 0;
-          for (int x = lo; x < hi; ++x) {
-            const int i = pl4[x];
-            int m = 4;
-            while (m < l && i - 1 - (m - 4) >= 0) {
-              int cc = text[i - 1 - (m - 4)];
-              if (cc < 0 || cc != sm.tail[m]) break;
-              ++m;
-            }
-            c += m >= l;
-          }
+          for (int x = lo; x < hi; ++x) c += extend4(ib.text, sm.tail, pl4[x], l) >= l;
           int total;
-          int r = block_exclusive_scan(c, sm.wsum, &total);
-          if (c && r < M) {
-            for (int x = lo; x < hi && r < M; ++x) {
+          int rk = block_exclusive_scan(c, sm.wsum, &total);
+          if (c && rk < M) {
+            for (int x = lo; x < hi && rk < M; ++x) {
               const int i = pl4[x];
-              int m = 4;
-              while (m < l && i - 1 - (m - 4) >= 0) {
-                int cc = text[i - 1 - (m - 4)];
-                if (cc < 0 || cc != sm.tail[m]) break;
-                ++m;
-              }
-              if (m >= l) gs[r++] = (long long)i + 4 + snap_start;
+              if (extend4(ib.text, sm.tail, i, l) >= l) gs[rk++] = (long long)i + 4 + snap_start;
             }
           }
           nsnap = total < M ? total : M;
@@ -477,25 +732,25 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
           if (a.ring[(e + 1) % a.ring_cap] < 0) continue;
           int m = 0;
           while (m < l && e - m >= dlo) {
-            int x = a.ring[(e - m) % a.ring_cap];
+            const int x = a.ring[(e - m) % a.ring_cap];
             if (x < 0 || x != sm.tail[m]) break;
             ++m;
           }
           c += m >= l;
         }
         int total;
-        int r = block_exclusive_scan(c, sm.wsum, &total) + nsnap;
-        if (c && r < M) {
-          for (long long e = lo; e < hi && r < M; ++e) {
+        int rk = block_exclusive_scan(c, sm.wsum, &total) + nsnap;
+        if (c && rk < M) {
+          for (long long e = lo; e < hi && rk < M; ++e) {
             if (e + 1 >= dhi) break;
             if (a.ring[(e + 1) % a.ring_cap] < 0) continue;
             int m = 0;
             while (m < l && e - m >= dlo) {
-              int x = a.ring[(e - m) % a.ring_cap];
+              const int x = a.ring[(e - m) % a.ring_cap];
               if (x < 0 || x != sm.tail[m]) break;
               ++m;
             }
-            if (m >= l) gs[r++] = e + 1;
+            if (m >= l) gs[rk++] = e + 1;
           }
         }
       }
@@ -505,27 +760,28 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   __syncthreads();
 
   // ---------------------------------------------------------------- 3. expansion and vote
-  if (wid < 2 * nb && sm.cand_valid[wid]) {
+  const bool voter = wid < 2 * nb && sm.cand_valid[wid] && sm.cand_src[wid] == wid;
+  int w0[KMAX], w1[KMAX];
+  int c0 = 0, cap = 0;
+  if (voter) {
     const int ci = wid;
     const int src = sm.cand_src[ci];
-    const bool local = ci < nb;
-    const int c0 = sm.cand_c0[ci];
-    const int cap = spec_cap(a, sm.cand_len[ci]);
+    c0 = sm.cand_c0[ci];
+    cap = spec_cap(a, sm.cand_len[ci]);
     const int s0 = lane, s1 = lane + 64;
-    int w0[KMAX], w1[KMAX];
-    if (local) {
+    if (ci < nb) {
       const int* ls = sm.lsites[src];
       const int p0 = s0 < c0 ? ls[s0] : 0, p1 = s1 < c0 ? ls[s1] : 0;
 #pragma unroll
       for (int d = 0; d < KMAX; ++d) {
-        w0[d] = (s0 < c0 && d < cap && p0 + d < L) ? ctx_at(row, smp, n, p0 + d) : -1;
-        w1[d] = (s1 < c0 && d < cap && p1 + d < L) ? ctx_at(row, smp, n, p1 + d) : -1;
+        w0[d] = (s0 < c0 && d < cap && p0 + d < L) ? ctxs[p0 + d] : -1;
+        w1[d] = (s1 < c0 && d < cap && p1 + d < L) ? ctxs[p1 + d] : -1;
       }
     } else {
       const long long* gs = sm.gsites[src - nb];
-      const int act = sm.active;
+      const int act = r.act;
       const int32_t* text = act == 0 ? a.idx[0].text : (act == 1 ? a.idx[1].text : nullptr);
-      const long long ss = sm.snap_start, sn = sm.snap_n;
+      const long long ss = r.snap_start, sn = r.snap_n;
       const long long q0 = s0 < c0 ? gs[s0] : 0, q1 = s1 < c0 ? gs[s1] : 0;
       bool live0 = s0 < c0, live1 = s1 < c0;
 #pragma unroll
@@ -539,51 +795,75 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
         w1[d] = x1;
       }
     }
-    int* hk = sm.vkey[wid];
-    int* hc = sm.vcnt[wid];
-    bool al0 = s0 < c0, al1 = s1 < c0;
+  }
+  __syncthreads();  // the context in LDS is dead from here on: it holds the vote tables
+  if (voter) {
+    const int ci = wid;
+    int* hk = ctxs + wid * (2 * kVoteSlots);
+    int* hc = hk + kVoteSlots;
+    bool al0 = lane < c0, al1 = lane + 64 < c0;
     int nout = 0;
     long long snum = 0;
-    for (int d = 0; d < cap; ++d) {
-      // the window arrays act as shift registers: slot 0 is always the current depth
-      const int cur0 = w0[0], cur1 = w1[0];
+    bool done = false;
 #pragma unroll
-      for (int x = 0; x + 1 < KMAX; ++x) {
-        w0[x] = w0[x + 1];
-        w1[x] = w1[x + 1];
+    for (int d = 0; d < KMAX; ++d) {
+      if (!done && d < cap) {
+        const int tk0 = al0 ? w0[d] : -1, tk1 = al1 ? w1[d] : -1;
+        const uint64_t v0 = __ballot(tk0 >= 0), v1 = __ballot(tk1 >= 0);
+        const int nalive = __popcll(v0) + __popcll(v1);
+        int c = 0, w = -1;
+        if (nalive == 0) {
+          done = true;
+        } else if (nalive == 1) {
+          c = 1;
+          w = v0 ? __builtin_amdgcn_readlane(tk0, __builtin_ctzll(v0))
+                 : __builtin_amdgcn_readlane(tk1, __builtin_ctzll(v1));
+        } else if (nalive <= kSmallVote) {
+          // few alive sites: one ballot pair per distinct token
+          uint64_t key = 0, r0 = v0, r1 = v1;
+          while (r0 | r1) {
+            const int tok = r0 ? __builtin_amdgcn_readlane(tk0, __builtin_ctzll(r0))
+                               : __builtin_amdgcn_readlane(tk1, __builtin_ctzll(r1));
+            const uint64_t e0 = __ballot(tk0 == tok), e1 = __ballot(tk1 == tok);
+            const uint64_t cnt = (uint64_t)(__popcll(e0) + __popcll(e1));
+            const uint64_t k = (cnt << 32) | (uint32_t)(0x7FFFFFFF - tok);
+            key = k > key ? k : key;
+            r0 &= ~e0;
+            r1 &= ~e1;
+          }
+          c = (int)(key >> 32);
+          w = 0x7FFFFFFF - (int)(uint32_t)(key & 0xFFFFFFFFu);
+        } else {
+          // many alive sites: counts in an LDS hash, then max count and smallest token
+          for (int x = lane; x < kVoteSlots; x += 64) {
+            hk[x] = -1;
+            hc[x] = 0;
+          }
+          wave_sync();
+          int sl0 = -1, sl1 = -1;
+          if (tk0 >= 0) sl0 = vote_insert(hk, hc, tk0);
+          if (tk1 >= 0) sl1 = vote_insert(hk, hc, tk1);
+          wave_sync();
+          const int cnt0 = sl0 >= 0 ? hc[sl0] : 0, cnt1 = sl1 >= 0 ? hc[sl1] : 0;
+          c = wave_max(cnt0 > cnt1 ? cnt0 : cnt1);
+          int tmin = 0x7FFFFFFF;
+          if (sl0 >= 0 && cnt0 == c) tmin = tk0;
+          if (sl1 >= 0 && cnt1 == c && tk1 < tmin) tmin = tk1;
+          w = wave_min(tmin);
+          wave_sync();
+        }
+        if (!done) {
+          if (a.mode == 1 && (long long)c * 1000000 < a.prob_ppm * (long long)c0) {
+            done = true;
+          } else {
+            if (lane == 0) sm.cand_out[ci][nout] = w;
+            ++nout;
+            snum += c;
+            al0 = tk0 == w;
+            al1 = tk1 == w;
+          }
+        }
       }
-      w0[KMAX - 1] = -1;
-      w1[KMAX - 1] = -1;
-      for (int x = lane; x < kVoteSlots; x += 64) {
-        hk[x] = -1;
-        hc[x] = 0;
-      }
-      wave_sync();
-      const int tk0 = al0 ? cur0 : -1, tk1 = al1 ? cur1 : -1;
-      int sl0 = -1, sl1 = -1;
-      if (tk0 >= 0) sl0 = vote_insert(hk, hc, tk0);
-      if (tk1 >= 0) sl1 = vote_insert(hk, hc, tk1);
-      wave_sync();
-      uint64_t key = 0;
-      if (sl0 >= 0) {
-        uint64_t k0 = ((uint64_t)(uint32_t)hc[sl0] << 32) | (uint32_t)(0x7FFFFFFF - tk0);
-        key = k0 > key ? k0 : key;
-      }
-      if (sl1 >= 0) {
-        uint64_t k1 = ((uint64_t)(uint32_t)hc[sl1] << 32) | (uint32_t)(0x7FFFFFFF - tk1);
-        key = k1 > key ? k1 : key;
-      }
-      key = wave_max_u64(key);
-      if (key == 0) break;
-      const int c = (int)(key >> 32);
-      const int w = 0x7FFFFFFF - (int)(uint32_t)(key & 0xFFFFFFFFu);
-      if (a.mode == 1 && (long long)c * 1000000 < a.prob_ppm * (long long)c0) break;
-      if (lane == 0) sm.cand_out[ci][nout] = w;
-      ++nout;
-      snum += c;
-      al0 = tk0 == w;
-      al1 = tk1 == w;
-      wave_sync();
     }
     if (lane == 0) {
       sm.cand_n[ci] = nout;
@@ -592,29 +872,43 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   }
   __syncthreads();
 
-  // selection and output row
-  if (tid == 0) {
-    int win = -1;
-    if (a.mode == 0) {
-      const int lv = sm.cand_valid[0], gv = sm.cand_valid[nb];
-      if (lv && (!gv || sm.cand_len[0] >= sm.cand_len[nb])) win = 0;
-      else if (gv) win = nb;
-    } else {
-      for (int i = 0; i < 2 * nb; ++i) {
-        if (!sm.cand_valid[i]) continue;
-        if (win < 0 ||
-            sm.cand_snum[i] * (long long)sm.cand_c0[win] > sm.cand_snum[win] * (long long)sm.cand_c0[i])
-          win = i;
+  // selection and output row, by wavefront 0 from registers (a candidate with the same length
+  // as an earlier one of its source shares that one's sites and vote)
+  if (wid != 0) return;
+  const bool cv = lane < 2 * nb && sm.cand_valid[lane];
+  const int csrc = cv ? sm.cand_src[lane] : 0;
+  const long long csn = cv ? sm.cand_snum[csrc] : 0;
+  const int cc0 = cv ? sm.cand_c0[lane] : 1;
+  const int clen = cv ? sm.cand_len[lane] : 0;
+  const int cn = cv ? sm.cand_n[csrc] : 0;
+  const uint64_t vmask = __ballot(cv);
+  int win = -1;
+  if (a.mode == 0) {
+    const bool lv = (vmask >> 0) & 1, gv = (vmask >> nb) & 1;
+    const int l0 = __builtin_amdgcn_readlane(clen, 0), g0 = __builtin_amdgcn_readlane(clen, nb);
+    if (lv && (!gv || l0 >= g0)) win = 0;
+    else if (gv) win = nb;
+  } else {
+    long long bsn = 0;
+    int bc0 = 1;
+    for (int i = 0; i < 2 * nb; ++i) {
+      if (!((vmask >> i) & 1)) continue;
+      const long long sn = (long long)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                            (int)((uint64_t)csn >> 32), i) << 32) |
+                                       (uint32_t)__builtin_amdgcn_readlane((int)csn, i));
+      const int c0i = __builtin_amdgcn_readlane(cc0, i);
+      if (win < 0 || sn * (long long)bc0 > bsn * (long long)c0i) {
+        win = i;
+        bsn = sn;
+        bc0 = c0i;
       }
     }
-    sm.wsum[0] = win;
-    sm.wsum[1] = win >= 0 ? sm.cand_n[win] : 0;
   }
-  __syncthreads();
-  const int win = sm.wsum[0], nv = sm.wsum[1];
+  const int ws = win >= 0 ? __builtin_amdgcn_readlane(csrc, win) : -1;
+  const int nv = win >= 0 ? __builtin_amdgcn_readlane(cn, win) : 0;
   const int fill = a.mode == 0 ? sm.tail[0] : -1;
-  for (int i = tid; i < a.k; i += NT) drow[i] = i < nv ? sm.cand_out[win][i] : fill;
-  if (tid == 0) a.nvalid[b] = nv;
+  for (int i = lane; i < a.k; i += 64) drow[i] = i < nv ? sm.cand_out[ws][i] : fill;
+  if (lane == 0) a.nvalid[b] = nv;
 }
 
 __global__ void update_state_kernel(int B, int S, int T, int32_t* tok, const int32_t* ntns,
@@ -642,7 +936,13 @@ hipError_t launch_k(const ProposeArgs& a, bool vec, size_t dyn, hipStream_t st) 
 
 }  // namespace
 
-size_t propose_dynamic_lds(int S, int T) { return ((size_t)S + T + 16) & ~(size_t)15; }
+// Dynamic LDS: the context (S + T ints, also the vote tables once the context is dead), then
+// one match-length byte per end position.
+size_t propose_dynamic_lds(int S, int T) {
+  return (size_t)propose_row_ints(S, T) * sizeof(int) + (((size_t)S + T + 16 + 15) & ~(size_t)15);
+}
+
+size_t propose_static_lds() { return sizeof(Smem); }
 
 hipError_t propose_prepare(size_t dyn) {
   const void* fns[] = {

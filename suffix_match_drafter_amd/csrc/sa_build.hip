@@ -232,7 +232,9 @@ hipError_t radix_sort(K* k0, int32_t* v0, K* k1, int32_t* v1, int64_t n, int bit
 }
 
 // ------------------------------------------------------------------ prefix doubling kernels
-__global__ void minmax_kernel(const int32_t* text, int64_t n, int32_t* mm) {
+__global__ __launch_bounds__(256) void minmax_kernel(const int32_t* text, int64_t n,
+                                                     int32_t* mm) {
+  __shared__ int slo[4], shi[4];
   int lo = INT32_MAX, hi = INT32_MIN;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -247,6 +249,15 @@ __global__ void minmax_kernel(const int32_t* text, int64_t n, int32_t* mm) {
     hi = b > hi ? b : hi;
   }
   if ((threadIdx.x & 63) == 0) {
+    slo[threadIdx.x >> 6] = lo;
+    shi[threadIdx.x >> 6] = hi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) {
+      lo = slo[w] < lo ? slo[w] : lo;
+      hi = shi[w] > hi ? shi[w] : hi;
+    }
     atomicMin(&mm[0], lo);
     atomicMax(&mm[1], hi);
   }
@@ -260,24 +271,22 @@ __global__ void init_keys_kernel(const int32_t* text, int64_t n, int32_t tmin, u
   v[i] = (int32_t)i;
 }
 
-// head[j] = j+1 if key[j] differs from key[j-1] (or j == 0), else 0
-__global__ void heads_kernel(const uint64_t* k, int64_t n, int32_t* head) {
+// head[j] = j+1 if key[j] differs from key[j-1] (or j == 0), else 0; any equal neighbour
+// raises *dup (a plain store of the same value from any number of wavefronts).
+__global__ void heads_kernel(const uint64_t* k, int64_t n, int32_t* head, uint32_t* dup) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= n) return;
-  head[j] = (j == 0 || k[j] != k[j - 1]) ? (int32_t)(j + 1) : 0;
+  bool same = false;
+  if (j < n) {
+    same = j > 0 && k[j] == k[j - 1];
+    head[j] = same ? 0 : (int32_t)(j + 1);
+  }
+  if (__ballot(same) && (threadIdx.x & 63) == 0) *dup = 1u;
 }
 
-// rank[v[j]] = group head index + 1 (from the inclusive max scan); count the groups
-__global__ void rank_kernel(const int32_t* v, const int32_t* headmax, const int32_t* head,
-                            int64_t n, int32_t* rank, uint32_t* ngroups) {
+// rank[v[j]] = index + 1 of the first member of j's group (inclusive max scan of heads)
+__global__ void rank_kernel(const int32_t* v, const int32_t* headmax, int64_t n, int32_t* rank) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int is_head = 0;
-  if (j < n) {
-    rank[v[j]] = headmax[j];
-    is_head = head[j] != 0;
-  }
-  const uint64_t bal = __ballot(is_head);
-  if ((threadIdx.x & 63) == 0 && bal) atomicAdd(ngroups, (uint32_t)__popcll(bal));
+  if (j < n) rank[v[j]] = headmax[j];
 }
 
 __global__ void pair_keys_kernel(const int32_t* v, const int32_t* rank, int64_t n, int64_t h,
@@ -352,7 +361,7 @@ hipError_t sa_build(const int32_t* text, int64_t n, int32_t* sa, const SaWork& w
   int32_t mm_init[2] = {INT32_MAX, INT32_MIN};
   hipError_t e = hipMemcpyAsync(w.counters, mm_init, sizeof(mm_init), hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(minmax_kernel, dim3((unsigned)std::min<int64_t>(gb, 4096)), dim3(TB), 0, st,
+  hipLaunchKernelGGL(minmax_kernel, dim3((unsigned)std::min<int64_t>(gb, 256)), dim3(TB), 0, st,
                      text, n, (int32_t*)w.counters);
   int32_t mm[2];
   if ((e = hipMemcpyAsync(mm, w.counters, sizeof(mm), hipMemcpyDeviceToHost, st)) != hipSuccess)
@@ -381,17 +390,16 @@ hipError_t sa_build(const int32_t* text, int64_t n, int32_t* sa, const SaWork& w
       }
     }
     ++rounds;
-    hipLaunchKernelGGL(heads_kernel, dim3(gb), dim3(TB), 0, st, kc, n, w.head);
-    if ((e = scan_i32<1, 1>(w.head, w.aux, n, w.tiles, st)) != hipSuccess) return e;
     if ((e = hipMemsetAsync(w.counters + 8, 0, sizeof(uint32_t), st)) != hipSuccess) return e;
-    hipLaunchKernelGGL(rank_kernel, dim3(gb), dim3(TB), 0, st, vc, w.aux, w.head, n, w.rank,
-                       w.counters + 8);
-    uint32_t groups = 0;
-    if ((e = hipMemcpyAsync(&groups, w.counters + 8, sizeof(groups), hipMemcpyDeviceToHost, st)) !=
+    hipLaunchKernelGGL(heads_kernel, dim3(gb), dim3(TB), 0, st, kc, n, w.head, w.counters + 8);
+    if ((e = scan_i32<1, 1>(w.head, w.aux, n, w.tiles, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(rank_kernel, dim3(gb), dim3(TB), 0, st, vc, w.aux, n, w.rank);
+    uint32_t dup = 0;
+    if ((e = hipMemcpyAsync(&dup, w.counters + 8, sizeof(dup), hipMemcpyDeviceToHost, st)) !=
         hipSuccess)
       return e;
     if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
-    if ((int64_t)groups == n || h >= n) break;
+    if (!dup || h >= n) break;
   }
   hipLaunchKernelGGL(copy_i32_kernel, dim3(gb), dim3(TB), 0, st, vc, sa, n);
   if (rounds_out) *rounds_out = rounds;

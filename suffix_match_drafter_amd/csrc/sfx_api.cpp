@@ -100,8 +100,8 @@ int validate(const sfx_config* c) {
     return fail(SFX_EINVAL, "LONGEST_FILL mode takes num_backoff == 1 (got %d)", c->num_backoff);
   if (c->min_self_match < 1) return fail(SFX_EINVAL, "min_self_match must be >= 1");
   if (c->max_batch < 0) return fail(SFX_EINVAL, "max_batch must be >= 0");
-  if (c->max_seq < 0 || c->max_seq > 65536)
-    return fail(SFX_EINVAL, "max_seq=%d outside [0,65536]", c->max_seq);
+  if (c->max_seq < 0 || c->max_seq > kMaxSeq)
+    return fail(SFX_EINVAL, "max_seq=%d outside [0,%d]", c->max_seq, kMaxSeq);
   if (c->max_sampled < 0 || c->max_sampled > kMaxT)
     return fail(SFX_EINVAL, "max_sampled=%d outside [0,%d]", c->max_sampled, kMaxT);
   if (c->spec_factor_ppm < 0) return fail(SFX_EINVAL, "max_spec_factor must be >= 0");
@@ -207,7 +207,14 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
     delete c;
     return fail(SFX_EHIP, "no HIP device");
   }
-  hipError_t e = propose_prepare(propose_dynamic_lds(cfg->max_seq, cfg->max_sampled));
+  const size_t lds = propose_dynamic_lds(cfg->max_seq, cfg->max_sampled);
+  if (lds + propose_static_lds() > kLdsBytes) {
+    delete c;
+    return fail(SFX_EINVAL, "max_seq=%d with max_sampled=%d needs %zu bytes of LDS per request, "
+                "more than the %zu a workgroup has", cfg->max_seq, cfg->max_sampled,
+                lds + propose_static_lds(), kLdsBytes);
+  }
+  hipError_t e = propose_prepare(lds);
   if (e != hipSuccess) {
     free_ctx(c);
     return hip_fail(e, "propose kernel attributes");

@@ -14,6 +14,7 @@ constexpr int kMaxD = 64;    // max_tree_depth limit (tail staged in LDS, length
 constexpr int kMaxNB = 8;    // num_backoff limit
 constexpr int kMaxM = 128;   // max_occurrences limit (two sites per lane of one wavefront)
 constexpr int kMaxT = 16;    // sampled width limit
+constexpr int kMaxSeq = 32768;  // row capacity limit: a whole context is staged in LDS
 constexpr int kNG = 3;       // probe tables for 2-, 3- and 4-grams
 constexpr int kEmptyTok = -1;
 

@@ -46,7 +46,7 @@ def _cfg(sfx, **kw):
     dict(k=0), dict(k=33), dict(max_tree_depth=0), dict(max_tree_depth=65),
     dict(num_backoff=0), dict(num_backoff=9), dict(num_backoff=2, mode=0),
     dict(max_occurrences=0), dict(max_occurrences=129), dict(mode=2), dict(min_self_match=0),
-    dict(max_seq=70000), dict(max_sampled=17), dict(max_batch=-1),
+    dict(max_seq=70000), dict(max_seq=32769), dict(max_sampled=17), dict(max_batch=-1),
     dict(mode=1, num_backoff=2, spec_factor_ppm=-1), dict(mode=1, min_token_prob_ppm=1_000_001),
     dict(mode=1, min_token_prob_ppm=-5), dict(corpus_capacity=-1),
     dict(corpus_capacity=(1 << 30) + 1), dict(corpus_capacity=100, max_tree_depth=1),
