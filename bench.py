@@ -12,8 +12,10 @@ Prints one JSON line (metric, value, roofline, cpu_baseline, ...).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -23,6 +25,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+KERNEL_SOURCES = ("suffix_match_drafter_amd/csrc/propose.hip",
+                  "suffix_match_drafter_amd/csrc/propose.h",
+                  "suffix_match_drafter_amd/csrc/sfx_internal.h")
 
 
 def log(*a):
@@ -38,6 +43,44 @@ def algorithmic_bytes(n, samp, B, T, k):
     return int(4 * L.sum() + 4 * B * (1 + T) + 4 * B * (k + 1)), int(L.sum())
 
 
+def kernel_source_hash():
+    """sha256 over the propose kernel's sources: a traffic figure taken from hardware counters
+    holds only for the kernel it was taken on."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per propose launch from the committed counter summary for this workload
+    (FETCH_SIZE + WRITE_SIZE per dispatch, scaled by a plain copy of known size), or None when
+    there is none or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"propose_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_val or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def copy_calibration(torch, dev, mib, reps):
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE and WRITE_SIZE
+    counters (run outside the timed region, only when asked for)."""
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} copies of {mib} MiB")
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -48,6 +91,9 @@ def main():
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run a plain copy of this many MiB before the timed region (counter "
+                         "calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -99,6 +145,8 @@ def main():
     draft = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
     nv = torch.empty((w.B,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration_mib > 0:
+        copy_calibration(torch, dev, args.copy_calibration_mib, 5)
 
     # ---------------------------------------------------------------- timed region
     for i in range(args.warmup):
@@ -162,7 +210,8 @@ def main():
                    "corpus_tokens": corpus_n, "rotating_buffers": nbuf,
                    "resident_input_MB": round(resident_mb, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name)},
         "cpu_baseline": cpu,
         "extra": {"tokens_scanned_per_s": round(ctx_tokens * calls_s, 1),
                   "algorithmic_bytes_per_call": int(alg_bytes),

@@ -73,6 +73,16 @@ __device__ __forceinline__ int wave_max(int v) {
   return max(max(a0, a1), max(a2, a3));
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor2, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppHalfMirror, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppMirror, 0xF, 0xF, false));
+  const uint32_t a0 = __builtin_amdgcn_readlane((int)v, 0), a1 = __builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t a2 = __builtin_amdgcn_readlane((int)v, 32), a3 = __builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a0, a1), max(a2, a3));
+}
+
 __device__ __forceinline__ int wave_min(int v) {
   v = min(v, __builtin_amdgcn_mov_dpp(v, kDppQuadXor1, 0xF, 0xF, false));
   v = min(v, __builtin_amdgcn_mov_dpp(v, kDppQuadXor2, 0xF, 0xF, false));
@@ -88,7 +98,7 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) {
 }
 
 // Exclusive prefix sum of one int per thread over the workgroup; *total gets the sum.
-__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -147,6 +157,8 @@ struct Smem {
   long long gsites[kMaxNB][kMaxM];
   int wpre[kMaxNB][NW];
   int clist[NW][256];  // per-wavefront positions of two-token matches to extend
+  int gpl[kNG][kMaxM];  // heads of the live 2-, 3- and 4-gram groups
+  int gm4[kMaxM];       // extension lengths of the first 4-gram occurrences
   const int32_t* plp[kNG];
   int wsum[NW + 1];
   int sel[2];
@@ -198,7 +210,7 @@ __device__ __forceinline__ View view_of(const ProposeArgs& a, int act, uint32_t 
 // Probe of the (G+2)-gram that ends the context: its group in the position list, minus the
 // prefix of occurrences in documents evicted since the snapshot.
 template <int G>
-__device__ void probe_ngram(const View& ib, const int* tail, int Lcap, long long dead_below,
+__device__ void probe_ngram(const View ib, const int* tail, int Lcap, long long dead_below,
                             int* off_out, int* live_out) {
   constexpr int ng = G + 2;
   int off = 0, live = 0;
@@ -261,72 +273,196 @@ __device__ __forceinline__ int corpus_at(const ProposeArgs& a, const int32_t* te
   return a.ring[q % a.ring_cap];
 }
 
-// The corpus wavefront of the fast path (live snapshot, no delta): tail from global memory,
-// probes, extension of the live 4-gram occurrences, global ladder and earliest sites.
-__device__ void corpus_wave_fast(const ProposeArgs& a, const Req& r, Smem& sm,
-                                 const int32_t* row, const int32_t* smp, int lane) {
-  const int n = r.n, L = r.L, Lcap = r.Lcap, nb = a.nb, M = a.M;
+// Depth-wise vote of one candidate held by one wavefront: lane l owns sites l and l+64, whose
+// continuation windows are w0 / w1 (-1 past the end of a continuation).  Writes the tokens to
+// out[] (lane 0) and returns the count and the sum of per-depth counts.  cmin is the smallest
+// count the stop rule keeps (0 when there is no stop rule).
+template <int KMAX>
+__device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[KMAX], int c0,
+                                         int cap, int cmin, int* hk, int* hc, int lane, int* out,
+                                         int* n_out, long long* snum_out) {
+  bool al0 = lane < c0, al1 = lane + 64 < c0;
+  int nout = 0;
+  long long snum = 0;
+  bool done = false;
+#pragma unroll
+  for (int d = 0; d < KMAX; ++d) {
+    if (!done && d < cap) {
+      const int tk0 = al0 ? w0[d] : -1, tk1 = al1 ? w1[d] : -1;
+      const uint64_t v0 = __ballot(tk0 >= 0), v1 = __ballot(tk1 >= 0);
+      int c = 0, w = -1;
+      if ((v0 | v1) == 0) {
+        done = true;
+      } else {
+        // the first alive site is the reference; when every alive site agrees with it the
+        // token wins with all their votes
+        const int fl = v0 ? __builtin_ctzll(v0) : __builtin_ctzll(v1);
+        const int first = v0 ? __builtin_amdgcn_readlane(tk0, fl) : __builtin_amdgcn_readlane(tk1, fl);
+        const uint64_t f0 = __ballot(tk0 == first), f1 = __ballot(tk1 == first);
+        const int nalive = __popcll(v0) + __popcll(v1);
+        if (f0 == v0 && f1 == v1) {
+          c = nalive;
+          w = first;
+        } else if (nalive <= kSmallVote) {
+          // few alive sites: one ballot pair per distinct token
+          uint64_t key = ((uint64_t)(__popcll(f0) + __popcll(f1)) << 32) |
+                         (uint32_t)(0x7FFFFFFF - first);
+          uint64_t r0 = v0 & ~f0, rr1 = v1 & ~f1;
+          while (r0 | rr1) {
+            const int tok = r0 ? __builtin_amdgcn_readlane(tk0, __builtin_ctzll(r0))
+                               : __builtin_amdgcn_readlane(tk1, __builtin_ctzll(rr1));
+            const uint64_t e0 = __ballot(tk0 == tok), e1 = __ballot(tk1 == tok);
+            const uint64_t k = ((uint64_t)(__popcll(e0) + __popcll(e1)) << 32) |
+                               (uint32_t)(0x7FFFFFFF - tok);
+            key = k > key ? k : key;
+            r0 &= ~e0;
+            rr1 &= ~e1;
+          }
+          c = (int)(key >> 32);
+          w = 0x7FFFFFFF - (int)(uint32_t)(key & 0xFFFFFFFFu);
+        } else {
+          // many alive sites: counts in an LDS hash, then max count and smallest token
+          for (int x = lane; x < kVoteSlots; x += 64) {
+            hk[x] = -1;
+            hc[x] = 0;
+          }
+          wave_sync();
+          int sl0 = -1, sl1 = -1;
+          if (tk0 >= 0) sl0 = vote_insert(hk, hc, tk0);
+          if (tk1 >= 0) sl1 = vote_insert(hk, hc, tk1);
+          wave_sync();
+          const int cnt0 = sl0 >= 0 ? hc[sl0] : 0, cnt1 = sl1 >= 0 ? hc[sl1] : 0;
+          if (__ballot(tk0 >= (1 << 24) || tk1 >= (1 << 24)) == 0) {
+            // tokens below 2^24: count and token packed in one key, one reduction
+            const uint32_t k0 = sl0 >= 0 ? ((uint32_t)cnt0 << 24) | (uint32_t)(0xFFFFFF - tk0) : 0u;
+            const uint32_t k1 = sl1 >= 0 ? ((uint32_t)cnt1 << 24) | (uint32_t)(0xFFFFFF - tk1) : 0u;
+            const uint32_t key = wave_max_u32(k0 > k1 ? k0 : k1);
+            c = (int)(key >> 24);
+            w = 0xFFFFFF - (int)(key & 0xFFFFFFu);
+          } else {
+            c = wave_max(cnt0 > cnt1 ? cnt0 : cnt1);
+            int tmin = 0x7FFFFFFF;
+            if (sl0 >= 0 && cnt0 == c) tmin = tk0;
+            if (sl1 >= 0 && cnt1 == c && tk1 < tmin) tmin = tk1;
+            w = wave_min(tmin);
+          }
+          wave_sync();
+        }
+        if (c < cmin) {
+          done = true;
+        } else {
+          if (lane == 0) out[nout] = w;
+          ++nout;
+          snum += c;
+          al0 = tk0 == w;
+          al1 = tk1 == w;
+        }
+      }
+    }
+  }
+  *n_out = nout;
+  *snum_out = snum;
+}
+
+// Smallest count c with c / c0 >= min_token_prob (exact: c * 1e6 >= prob_ppm * c0).
+__device__ __forceinline__ int stop_threshold(const ProposeArgs& a, int c0) {
+  if (a.mode != 1) return 0;
+  return (int)((a.prob_ppm * (long long)c0 + 999999) / 1000000);
+}
+
+// The corpus wavefront of the fast path (live snapshot, no delta), first part, run while the
+// other wavefronts stage the context: tail from global memory, the three n-gram probes, the
+// heads of the three position-ordered groups into LDS, and the backward extension of the live
+// 4-gram occurrences into a length histogram (lengths of the first kMaxM kept in LDS).
+__device__ __forceinline__ void corpus_wave_probe(const ProposeArgs& a, const Req& r, Smem& sm,
+                                                  const int32_t* row, const int32_t* smp,
+                                                  int lane) {
+  const int n = r.n, L = r.L, Lcap = r.Lcap, M = a.M;
   if (lane < Lcap) sm.gtail[lane] = ctx_at(row, smp, n, L - 1 - lane);
   if (lane <= kMaxD) sm.ghist[lane] = 0;
   wave_sync();
   const View ib = view_of(a, r.act, r.ht_mask);
-  const long long snap_start = r.snap_start;
-  const long long dead_below = r.tail_w - snap_start;
+  const long long dead_below = r.tail_w - r.snap_start;
   if (lane == 0) probe_ngram<0>(ib, sm.gtail, Lcap, dead_below, &sm.g_off[0], &sm.g_live[0]);
   if (lane == 1) probe_ngram<1>(ib, sm.gtail, Lcap, dead_below, &sm.g_off[1], &sm.g_live[1]);
   if (lane == 2) probe_ngram<2>(ib, sm.gtail, Lcap, dead_below, &sm.g_off[2], &sm.g_live[2]);
   wave_sync();
+#pragma unroll
+  for (int g = 0; g < kNG; ++g) {
+    const int32_t* pl = (g == 0 ? ib.pl0 : (g == 1 ? ib.pl1 : ib.pl2)) + sm.g_off[g];
+    const int ns = sm.g_live[g] < M ? sm.g_live[g] : M;
+    for (int x = lane; x < ns; x += 64) sm.gpl[g][x] = pl[x];
+  }
   const int live4 = sm.g_live[2];
-  const int32_t* pl4 = ib.pl2 + sm.g_off[2];
   if (Lcap >= 5 && live4 > 0) {
+    const int32_t* pl4 = ib.pl2 + sm.g_off[2];
     for (int x = lane; x < live4; x += 64) {
-      const int m = extend4(ib.text, sm.gtail, pl4[x], Lcap);
+      const int i = pl4[x];
+      const int m = extend4(ib.text, sm.gtail, i, Lcap);
+      if (x < kMaxM) {
+        sm.gm4[x] = m;
+        sm.gpl[2][x] = i;
+      }
       if (m >= 5) atomicAdd(&sm.ghist[m], 1);
     }
   }
+}
+
+// Second part, run while the other wavefronts compute the match lengths of the context: the
+// corpus ladder (lane l holds the support of length l) and the earliest sites of each level.
+__device__ __forceinline__ void corpus_wave_sites(const ProposeArgs& a, const Req& r, Smem& sm,
+                                                  int lane) {
+  const int Lcap = r.Lcap, nb = a.nb, M = a.M;
+  const long long snap_start = r.snap_start;
   wave_sync();
-  if (lane == 0) {
-    int gcum = 0, ti = 0;
-    for (int l = Lcap; l >= 2 && ti < nb; --l) {
-      gcum += sm.ghist[l];
-      const int cnt = l <= 4 ? sm.g_live[l - 2] : gcum;
-      while (ti < nb && cnt >= ti + 1) {
-        sm.cand_len[nb + ti] = l;
-        sm.cand_sup[nb + ti] = cnt;
-        ++ti;
-      }
-    }
-    for (; ti < nb; ++ti) {
-      sm.cand_len[nb + ti] = 0;
-      sm.cand_sup[nb + ti] = 0;
-    }
-    const int minc = a.min_corpus > 2 ? a.min_corpus : 2;
-    for (int i = 0; i < nb; ++i) {
-      const int ci = nb + i;
-      sm.cand_valid[ci] = sm.cand_len[ci] >= minc;
-      sm.cand_c0[ci] = sm.cand_sup[ci] < M ? sm.cand_sup[ci] : M;
-      sm.cand_src[ci] =
-          (i > 0 && sm.cand_len[ci] == sm.cand_len[ci - 1]) ? sm.cand_src[ci - 1] : ci;
-    }
-  }
-  wave_sync();
-  const uint64_t below = lanes_below(lane);
+  // support of length l: the live (l)-gram group for l <= 4, else extensions reaching l
+  const int gh = (lane >= 5 && lane <= Lcap) ? sm.ghist[lane] : 0;
+  const int gin = wave_incl_add(gh);
+  const int gsuf = __builtin_amdgcn_readlane(gin, 63) - gin + gh;
+  const int sup_l = lane >= 2 && lane <= 4 ? sm.g_live[lane - 2] : gsuf;
+  const int minc = a.min_corpus > 2 ? a.min_corpus : 2;
+  int prev_l = -1, prev_src = -1;
   for (int ti = 0; ti < nb; ++ti) {
+    const uint64_t ok = __ballot(lane >= 2 && lane <= Lcap && sup_l >= ti + 1);
+    const int l = ok ? 63 - __builtin_clzll(ok) : 0;
+    const int sup = l ? __builtin_amdgcn_readlane(sup_l, l) : 0;
     const int ci = nb + ti;
-    if (!sm.cand_valid[ci] || sm.cand_src[ci] != ci) continue;
-    const int l = sm.cand_len[ci];
+    const int src = (ti > 0 && l == prev_l) ? prev_src : ci;
+    prev_l = l;
+    prev_src = src;
+    if (lane == 0) {
+      sm.cand_len[ci] = l;
+      sm.cand_sup[ci] = sup;
+      sm.cand_valid[ci] = l >= minc;
+      sm.cand_c0[ci] = sup < M ? sup : M;
+      sm.cand_src[ci] = src;
+    }
+    if (l < minc || src != ci) continue;
     long long* gs = sm.gsites[ti];
     if (l <= 4) {
       const int g = l - 2;
-      const int32_t* pl = (g == 0 ? ib.pl0 : (g == 1 ? ib.pl1 : ib.pl2)) + sm.g_off[g];
-      const int ns = sm.g_live[g] < M ? sm.g_live[g] : M;
-      for (int x = lane; x < ns; x += 64) gs[x] = (long long)pl[x] + l + snap_start;
+      const int ns = sup < M ? sup : M;
+      for (int x = lane; x < ns; x += 64) gs[x] = (long long)sm.gpl[g][x] + l + snap_start;
     } else {
+      // the first M live 4-gram occurrences (position order) whose extension reaches l
+      const int live4 = sm.g_live[2];
+      const uint64_t below = lanes_below(lane);
+      const View ib = view_of(a, r.act, r.ht_mask);
+      const int32_t* pl4 = ib.pl2 + sm.g_off[2];
       int run = 0;
       for (int base = 0; base < live4 && run < M; base += 64) {
         const int x = base + lane;
-        const int i = x < live4 ? pl4[x] : 0;
-        const bool q = x < live4 && extend4(ib.text, sm.gtail, i, l) >= l;
+        bool q = false;
+        int i = 0;
+        if (x < live4) {
+          if (x < kMaxM) {
+            i = sm.gpl[2][x];
+            q = sm.gm4[x] >= l;
+          } else {
+            i = pl4[x];
+            q = extend4(ib.text, sm.gtail, i, l) >= l;
+          }
+        }
         const uint64_t bal = __ballot(q);
         const int rk = run + __popcll(bal & below);
         if (q && rk < M) gs[rk] = (long long)i + 4 + snap_start;
@@ -401,14 +537,14 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     r.ht_mask = 0;
     bool delta = false;
     if (r.has) {
-      const Ctl* c = a.ctl;
-      r.act = c->active;
-      r.tail_w = c->tail;
-      r.delta_hi = c->head;
+      const Ctl c = *a.ctl;  // one round of loads for the whole control block
+      r.act = c.active;
+      r.tail_w = c.tail;
+      r.delta_hi = c.head;
       if (r.act >= 0) {
-        r.ht_mask = r.act == 0 ? c->ht_mask[0] : c->ht_mask[1];
-        r.snap_start = r.act == 0 ? c->snap_start[0] : c->snap_start[1];
-        const long long se = r.act == 0 ? c->snap_end[0] : c->snap_end[1];
+        r.ht_mask = r.act == 0 ? c.ht_mask[0] : c.ht_mask[1];
+        r.snap_start = r.act == 0 ? c.snap_start[0] : c.snap_start[1];
+        const long long se = r.act == 0 ? c.snap_end[0] : c.snap_end[1];
         r.snap_n = se - r.snap_start;
         r.delta_lo = se > r.tail_w ? se : r.tail_w;
       } else {
@@ -433,7 +569,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
 
   // ---------------------------------------------------------------- stage || corpus wave
   if (fast && wid == GW) {
-    corpus_wave_fast(a, r, sm, row, smp, lane);
+    corpus_wave_probe(a, r, sm, row, smp, lane);
   } else {
     stage_context<VEC>(ctxs, row, smp, n, t, tid, fast ? NT - 64 : NT);
   }
@@ -449,6 +585,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   const int cend = worker ? (cbeg + C < J ? cbeg + C : J) : J;
   uint8_t* mbs = reinterpret_cast<uint8_t*>(ctxs + propose_row_ints(a.S, a.T));
   if (tid < Lcap) sm.tail[tid] = ctxs[L - 1 - tid];
+  if (fast && wid == GW) corpus_wave_sites(a, r, sm, lane);
   if (worker) {
     const int t0 = ctxs[L - 1];
     const int t1 = L >= 2 ? ctxs[L - 2] : -1;
@@ -528,45 +665,47 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     sm.wsuf[wid][lane] = __builtin_amdgcn_readlane(incl, 63) - incl + h;
   }
   __syncthreads();
-  // ladder (wavefront 0): count_ge(v) in lane v; l_t = largest v with count_ge(v) >= t
-  if (wid == 0) {
+  // ladder and this wavefront's site offsets: every worker wavefront derives them from the
+  // per-wavefront suffix sums (lane v of cg = positions with length >= v); wavefront 0 also
+  // records the candidates.  Then the earliest sites of every distinct local level: 16 length
+  // bytes per lane, SWAR compares, wavefront prefix sums for the order.
+  if (worker) {
     int cg = 0;
     for (int w = 0; w < NWW; ++w) cg += sm.wsuf[w][lane];
     const int maxl = D < J ? D : J;
     const int mins = a.min_self > 1 ? a.min_self : 1;
-    for (int ti = 0; ti < nb; ++ti) {
-      const uint64_t ok = __ballot(lane >= 1 && lane <= maxl && cg >= ti + 1);
-      const int l = ok ? 63 - __builtin_clzll(ok) : 0;
-      const int sup = l ? __builtin_amdgcn_readlane(cg, l) : 0;
-      if (lane == 0) {
-        sm.cand_len[ti] = l;
-        sm.cand_sup[ti] = sup;
-        sm.cand_valid[ti] = l >= mins;
-        sm.cand_c0[ti] = sup < M ? sup : M;
-        sm.cand_src[ti] = (ti > 0 && l == sm.cand_len[ti - 1]) ? sm.cand_src[ti - 1] : ti;
-      }
-      // exclusive per-wavefront offsets of this level's sites
-      const int c = (l >= 1 && lane < NWW) ? sm.wsuf[lane][l] : 0;
-      const int x = wave_incl_add(c);
-      if (lane < NW) sm.wpre[ti][lane] = x - c;
-      wave_sync();
-    }
-  }
-  __syncthreads();
-
-  // earliest sites of every distinct local level: 16 length bytes per lane, SWAR compares,
-  // wavefront prefix sums for the order
-  if (worker) {
     int lv[kMaxNB], pre[kMaxNB], run[kMaxNB];
     bool act[kMaxNB];
     bool any = false;
+    int prev_l = -1, prev_src = -1;
 #pragma unroll
     for (int ti = 0; ti < kMaxNB; ++ti) {
-      act[ti] = ti < nb && sm.cand_valid[ti] && sm.cand_src[ti] == ti && sm.wpre[ti][wid] < M;
-      lv[ti] = act[ti] ? sm.cand_len[ti] : 0;
-      pre[ti] = act[ti] ? sm.wpre[ti][wid] : 0;
+      act[ti] = false;
+      lv[ti] = 0;
+      pre[ti] = 0;
       run[ti] = 0;
-      any = any || act[ti];
+      if (ti < nb) {
+        const uint64_t ok = __ballot(lane >= 1 && lane <= maxl && cg >= ti + 1);
+        const int l = ok ? 63 - __builtin_clzll(ok) : 0;
+        const int sup = l ? __builtin_amdgcn_readlane(cg, l) : 0;
+        const int src = (ti > 0 && l == prev_l) ? prev_src : ti;
+        prev_l = l;
+        prev_src = src;
+        if (wid == 0 && lane == 0) {
+          sm.cand_len[ti] = l;
+          sm.cand_sup[ti] = sup;
+          sm.cand_valid[ti] = l >= mins;
+          sm.cand_c0[ti] = sup < M ? sup : M;
+          sm.cand_src[ti] = src;
+        }
+        const int c = (l >= 1 && lane < NWW) ? sm.wsuf[lane][l] : 0;
+        const int x = wave_incl_add(c);
+        const int mypre = __builtin_amdgcn_readlane(x - c, wid);
+        act[ti] = l >= mins && src == ti && mypre < M;
+        lv[ti] = l;
+        pre[ti] = mypre;
+        any = any || act[ti];
+      }
     }
     for (int r0 = cbeg; any && r0 < cend; r0 += 1024) {
       const int jb = r0 + 16 * lane;
@@ -798,76 +937,14 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   }
   __syncthreads();  // the context in LDS is dead from here on: it holds the vote tables
   if (voter) {
-    const int ci = wid;
-    int* hk = ctxs + wid * (2 * kVoteSlots);
-    int* hc = hk + kVoteSlots;
-    bool al0 = lane < c0, al1 = lane + 64 < c0;
     int nout = 0;
     long long snum = 0;
-    bool done = false;
-#pragma unroll
-    for (int d = 0; d < KMAX; ++d) {
-      if (!done && d < cap) {
-        const int tk0 = al0 ? w0[d] : -1, tk1 = al1 ? w1[d] : -1;
-        const uint64_t v0 = __ballot(tk0 >= 0), v1 = __ballot(tk1 >= 0);
-        const int nalive = __popcll(v0) + __popcll(v1);
-        int c = 0, w = -1;
-        if (nalive == 0) {
-          done = true;
-        } else if (nalive == 1) {
-          c = 1;
-          w = v0 ? __builtin_amdgcn_readlane(tk0, __builtin_ctzll(v0))
-                 : __builtin_amdgcn_readlane(tk1, __builtin_ctzll(v1));
-        } else if (nalive <= kSmallVote) {
-          // few alive sites: one ballot pair per distinct token
-          uint64_t key = 0, r0 = v0, r1 = v1;
-          while (r0 | r1) {
-            const int tok = r0 ? __builtin_amdgcn_readlane(tk0, __builtin_ctzll(r0))
-                               : __builtin_amdgcn_readlane(tk1, __builtin_ctzll(r1));
-            const uint64_t e0 = __ballot(tk0 == tok), e1 = __ballot(tk1 == tok);
-            const uint64_t cnt = (uint64_t)(__popcll(e0) + __popcll(e1));
-            const uint64_t k = (cnt << 32) | (uint32_t)(0x7FFFFFFF - tok);
-            key = k > key ? k : key;
-            r0 &= ~e0;
-            r1 &= ~e1;
-          }
-          c = (int)(key >> 32);
-          w = 0x7FFFFFFF - (int)(uint32_t)(key & 0xFFFFFFFFu);
-        } else {
-          // many alive sites: counts in an LDS hash, then max count and smallest token
-          for (int x = lane; x < kVoteSlots; x += 64) {
-            hk[x] = -1;
-            hc[x] = 0;
-          }
-          wave_sync();
-          int sl0 = -1, sl1 = -1;
-          if (tk0 >= 0) sl0 = vote_insert(hk, hc, tk0);
-          if (tk1 >= 0) sl1 = vote_insert(hk, hc, tk1);
-          wave_sync();
-          const int cnt0 = sl0 >= 0 ? hc[sl0] : 0, cnt1 = sl1 >= 0 ? hc[sl1] : 0;
-          c = wave_max(cnt0 > cnt1 ? cnt0 : cnt1);
-          int tmin = 0x7FFFFFFF;
-          if (sl0 >= 0 && cnt0 == c) tmin = tk0;
-          if (sl1 >= 0 && cnt1 == c && tk1 < tmin) tmin = tk1;
-          w = wave_min(tmin);
-          wave_sync();
-        }
-        if (!done) {
-          if (a.mode == 1 && (long long)c * 1000000 < a.prob_ppm * (long long)c0) {
-            done = true;
-          } else {
-            if (lane == 0) sm.cand_out[ci][nout] = w;
-            ++nout;
-            snum += c;
-            al0 = tk0 == w;
-            al1 = tk1 == w;
-          }
-        }
-      }
-    }
+    int* hk = ctxs + wid * (2 * kVoteSlots);
+    vote_run<KMAX>(w0, w1, c0, cap, stop_threshold(a, c0), hk, hk + kVoteSlots, lane,
+                   sm.cand_out[wid], &nout, &snum);
     if (lane == 0) {
-      sm.cand_n[ci] = nout;
-      sm.cand_snum[ci] = snum;
+      sm.cand_n[wid] = nout;
+      sm.cand_snum[wid] = snum;
     }
   }
   __syncthreads();
