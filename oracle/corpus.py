@@ -4,7 +4,7 @@ SuffixGPU page, How it works step 4: finished sequences are appended as new docu
 oldest documents are evicted when the ring is full; vLLM docs "Suffix Decoding", Model Runner
 V2: the corpus keeps finished responses up to a token budget, oldest first out.
 
-Readings taken (listed in the design doc):
+Readings taken:
   * each document occupies len + 1 tokens: its tokens and one -1 separator after it;
   * after documents are appended, the oldest are dropped while the total exceeds the capacity,
     so the live set is always the longest run of most recent documents that fits (a document

@@ -9,7 +9,7 @@
  * The drafter is a heuristic, so this file runs its steps in the order the pages give them
  * (SuffixGPU page, "How it works": local matching, global matching, expansion & selection), in
  * the simplest loops that express each definition.  Where the pages leave a detail open the
- * reading taken is stated at the function and listed in the design doc.
+ * reading taken is stated at the function.
  */
 #define _GNU_SOURCE
 #include "oracle.h"
