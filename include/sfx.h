@@ -60,6 +60,13 @@ enum {
                                 score; best score wins; -1 padding */
 };
 
+enum {
+  SFX_FLAG_STREAM_CONTEXT = 1 /* sfx_propose reads each context from device memory instead of
+                                 staging it in the workgroup's LDS (same results).  Without it a
+                                 row is staged when it fits (max_seq up to about 19K tokens) and
+                                 streamed otherwise. */
+};
+
 typedef struct sfx_config {
   int32_t k;                /* draft width, 1..32 */
   int32_t max_tree_depth;   /* D: longest suffix matched, 1..64 (>= 2 when a corpus is used) */
@@ -76,6 +83,8 @@ typedef struct sfx_config {
   int64_t min_token_prob_ppm; /* min_token_prob * 1e6, 0..1e6 (SCORED) */
   int64_t corpus_capacity;  /* ring size in tokens, separators included; 0 = no corpus;
                                at most 2^30 */
+  int32_t flags;            /* SFX_FLAG_* (0 = defaults) */
+  int32_t reserved;         /* must be 0 */
 } sfx_config;
 
 typedef struct sfx_ctx sfx_ctx;

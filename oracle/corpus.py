@@ -38,6 +38,7 @@ class LiveCorpus:
         self.capacity = int(capacity)
         self.docs: deque[np.ndarray] = deque()
         self.total = 0
+        self.dropped = 0
 
     def ingest(self, docs) -> None:
         for d in docs:
@@ -47,6 +48,11 @@ class LiveCorpus:
         while self.docs and self.total > self.capacity:
             old = self.docs.popleft()
             self.total -= len(old) + 1
+            self.dropped += 1
+
+    def evicted(self) -> int:
+        """Number of documents dropped so far."""
+        return self.dropped
 
     def text(self) -> np.ndarray:
         if not self.docs:

@@ -30,6 +30,9 @@ EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_up
            "sfx_build_suffix_array")
 
 
+FLAG_STREAM_CONTEXT = 1  # read contexts from device memory instead of staging them in LDS
+
+
 class SfxError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__(f"{_NAMES.get(code, code)}: {msg}")
@@ -52,6 +55,8 @@ class _Config(ctypes.Structure):
         ("spec_offset_ppm", ctypes.c_int64),
         ("min_token_prob_ppm", ctypes.c_int64),
         ("corpus_capacity", ctypes.c_int64),
+        ("flags", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -71,6 +76,8 @@ class Config:
     spec_offset_ppm: int = 0
     min_token_prob_ppm: int = 100_000
     corpus_capacity: int = 0
+    flags: int = 0
+    reserved: int = 0
 
     def _c(self) -> _Config:
         return _Config(*[getattr(self, f[0]) for f in _Config._fields_])

@@ -18,14 +18,19 @@ struct ProposeArgs {
   IndexBuf idx[2];
   const int32_t* ring;
   int64_t ring_cap;
+  int32_t stream_ctx;  // read the context from HBM instead of staging it in LDS
 };
 
-size_t propose_dynamic_lds(int S, int T);
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one gfx950 workgroup
+// Dynamic LDS of one request: the staged context (when staged) and the hit lists.
+size_t propose_dynamic_lds(bool staged, int S, int T);
 // Static LDS of the propose kernel (the per-request bookkeeping).
 size_t propose_static_lds();
-constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one gfx950 workgroup
-// Allows `dyn` bytes of dynamic LDS on every propose kernel instantiation.
-hipError_t propose_prepare(size_t dyn);
+// Whether a call with row capacity S stages the context in LDS: it does unless asked not to or
+// the staged layout does not fit one workgroup's LDS.
+bool propose_staged(int S, int T, bool stream_ctx);
+// Allows the largest dynamic LDS on every propose kernel instantiation.
+hipError_t propose_prepare();
 hipError_t launch_propose(const ProposeArgs& a, hipStream_t st);
 hipError_t launch_update_state(int B, int S, int T, int32_t* tok, const int32_t* ntns,
                                const int32_t* samp, int32_t* nout, hipStream_t st);

@@ -26,7 +26,6 @@ constexpr int NT = 1024;
 constexpr int NW = NT / 64;
 constexpr int GW = NW - 1;          // the corpus wavefront of the fast path
 constexpr int kVoteSlots = 256;
-constexpr int kStageUnroll = 8;     // 16-byte loads in flight per thread while staging
 constexpr int kSmallVote = 24;      // alive sites at or below this vote with ballots
 
 __device__ __forceinline__ void wave_sync() {
@@ -56,10 +55,6 @@ __device__ __forceinline__ int wave_incl_add(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);
   v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);
   return v;
-}
-
-__device__ __forceinline__ int wave_sum(int v) {
-  return __builtin_amdgcn_readlane(wave_incl_add(v), 63);
 }
 
 // Maximum / minimum over the 64 lanes (every lane takes part).
@@ -155,8 +150,6 @@ struct Smem {
   int cand_out[2 * kMaxNB][kMaxK];
   int lsites[kMaxNB][kMaxM];
   long long gsites[kMaxNB][kMaxM];
-  int wpre[kMaxNB][NW];
-  int clist[NW][256];  // per-wavefront positions of two-token matches to extend
   int gpl[kNG][kMaxM];  // heads of the live 2-, 3- and 4-gram groups
   int gm4[kMaxM];       // extension lengths of the first 4-gram occurrences
   const int32_t* plp[kNG];
@@ -472,52 +465,133 @@ __device__ __forceinline__ void corpus_wave_sites(const ProposeArgs& a, const Re
   }
 }
 
-// Stage the context (row prefix and leading sampled ids) in LDS with `nst` threads.
-template <bool VEC>
-__device__ __forceinline__ void stage_context(int* ctxs, const int32_t* row, const int32_t* smp,
-                                              int n, int t, int stid, int nst) {
-  if (VEC) {
-    for (int base = 0; base < n; base += nst * 4 * kStageUnroll) {
-      int4 q[kStageUnroll];
+// Dynamic LDS of one request.  Staged: [context ints | hit positions (u16) | hit lengths (u8)];
+// streaming (the context stays in HBM): [hit positions | hit lengths].  The vote tables of the
+// expansion alias the start of the region once the context and the hit lists are dead.
+constexpr int kVoteBytes = NW * 2 * kVoteSlots * 4;
+__host__ __device__ inline int ctx_ints(int S, int T) { return (S + T + 4 + 3) & ~3; }
+// Hit-list entries: wavefront w owns [w*C, w*C + C) with C = ceil(J / waves) rounded up to 64,
+// J <= S + T - 1, so S + T + 64 * NW entries always suffice.
+__host__ __device__ inline int hit_cap(int S, int T) { return (S + T + 64 * NW + 15) & ~15; }
+__host__ __device__ inline size_t hpos_offset(bool staged, int S, int T) {
+  return staged ? (size_t)4 * ctx_ints(S, T) : 0;
+}
+__host__ __device__ inline size_t hmb_offset(bool staged, int S, int T) {
+  return hpos_offset(staged, S, T) + (size_t)2 * hit_cap(S, T);
+}
+__host__ __device__ inline size_t dyn_bytes(bool staged, int S, int T) {
+  const size_t b = (hmb_offset(staged, S, T) + hit_cap(S, T) + 15) & ~(size_t)15;
+  return b < (size_t)kVoteBytes ? (size_t)kVoteBytes : b;
+}
+
+constexpr int kScreenLoads = 32;  // dword loads in flight per lane while screening (2048 positions)
+
+__device__ __forceinline__ int lanes_before(uint64_t bal) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
+// Local step 1 for one wavefront's chunk [cbeg, cend) of end positions: load the row part with
+// every load of a lane in flight (lane-strided dwords, so each load instruction is one coalesced
+// 256-byte run), stage it in LDS when STAGED, and list the positions whose token equals the last
+// context token t0, in position order, at hpos[0..).  Returns the number of hits.
+template <bool STAGED>
+__device__ __forceinline__ int stage_screen(int* ctxs, uint16_t* hpos, const int32_t* row,
+                                            const int32_t* smp, int n, int cbeg, int cend, int t0,
+                                            int lane) {
+  int nhit = 0;
+  const int rend = cend < n ? cend : n;
+  for (int g0 = cbeg; g0 < rend; g0 += 64 * kScreenLoads) {
+    int v[kScreenLoads];
 #pragma unroll
-      for (int u = 0; u < kStageUnroll; ++u) {
-        const int i4 = base + (u * nst + stid) * 4;
-        q[u] = i4 + 3 < n ? *reinterpret_cast<const int4*>(row + i4) : make_int4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < kScreenLoads; ++i) {
+      const int x = g0 + 64 * i + lane;
+      v[i] = x < rend ? row[x] : -1;
+    }
 #pragma unroll
-      for (int u = 0; u < kStageUnroll; ++u) {
-        const int i4 = base + (u * nst + stid) * 4;
-        if (i4 + 3 < n) {
-          *reinterpret_cast<int4*>(ctxs + i4) = q[u];
-        } else if (i4 < n) {
-          for (int x = i4; x < n; ++x) ctxs[x] = row[x];
-        }
+    for (int i = 0; i < kScreenLoads; ++i) {
+      const int x = g0 + 64 * i + lane;
+      if (STAGED && x < rend) ctxs[x] = v[i];
+      const bool h = x < rend && v[i] == t0;
+      const uint64_t bal = __ballot(h);
+      if (h) hpos[nhit + lanes_before(bal)] = (uint16_t)x;
+      nhit += __popcll(bal);
+    }
+  }
+  // end positions among the sampled ids (at most T - 1 of them, after every row position)
+  if (cend > n) {
+    const int x = (cbeg > n ? cbeg : n) + lane;
+    const bool h = x < cend && smp[x - n] == t0;
+    const uint64_t bal = __ballot(h);
+    if (h) hpos[nhit + lanes_before(bal)] = (uint16_t)x;
+    nhit += __popcll(bal);
+  }
+  return nhit;
+}
+
+// Local step 2: the backward match length of every listed hit (its last token already matches).
+// Eight lanes per hit, each comparing OPL consecutive tail offsets; the smallest mismatching
+// offset over the eight (or the cap min(D, j+1)) is the length.  Lengths go to hmb[] and the
+// wavefront's histogram.
+template <bool STAGED, int OPL>
+__device__ __forceinline__ void extend_hits(const int* ctxs, const uint16_t* hpos, uint8_t* hmb,
+                                            int nhit, const int* tail, int D, int* whist,
+                                            const int32_t* row, const int32_t* smp, int n,
+                                            int lane) {
+  const int g = lane >> 3, r = lane & 7;
+  int tq[OPL];
+#pragma unroll
+  for (int x = 0; x < OPL; ++x) {
+    const int o = 1 + r * OPL + x;
+    tq[x] = o < D ? tail[o] : -1;
+  }
+  for (int e0 = 0; e0 < nhit; e0 += 16) {
+    int j[2], lim[2], c[2][OPL];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = e0 + 8 * h + g;
+      j[h] = e < nhit ? hpos[e] : 0;
+      lim[h] = e < nhit ? (D < j[h] + 1 ? D : j[h] + 1) : 0;
+#pragma unroll
+      for (int x = 0; x < OPL; ++x) {
+        const int o = 1 + r * OPL + x;
+        const int at = o < lim[h] ? j[h] - o : 0;
+        c[h][x] = STAGED ? ctxs[at] : ctx_at(row, smp, n, at);
       }
     }
-  } else {
-    for (int x = stid; x < n; x += nst) ctxs[x] = row[x];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int fm = lim[h];
+#pragma unroll
+      for (int x = OPL - 1; x >= 0; --x) {
+        const int o = 1 + r * OPL + x;
+        if (o < lim[h] && c[h][x] != tq[x]) fm = o;
+      }
+      fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppQuadXor1, 0xF, 0xF, false));
+      fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppQuadXor2, 0xF, 0xF, false));
+      fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppHalfMirror, 0xF, 0xF, false));
+      const int e = e0 + 8 * h + g;
+      if (r == 0 && e < nhit) {
+        hmb[e] = (uint8_t)fm;
+        atomicAdd(&whist[fm], 1);
+      }
+    }
   }
-  for (int x = stid; x < t; x += nst) ctxs[n + x] = smp[x];
 }
 
-// Ints of dynamic LDS before the length bytes: the context, at least the vote tables.
-__host__ __device__ inline int propose_row_ints(int S, int T) {
-  int ints = (S + T + 4 + 3) & ~3;
-  const int vote = NW * 2 * kVoteSlots;
-  return ints < vote ? vote : ints;
-}
-
-template <int KMAX, bool VEC>
+template <int KMAX, bool STAGED>
 __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
-  extern __shared__ int4 ctx4[];
-  int* ctxs = reinterpret_cast<int*>(ctx4);
+  extern __shared__ int4 dyn4[];
+  unsigned char* dyn = reinterpret_cast<unsigned char*>(dyn4);
+  int* ctxs = reinterpret_cast<int*>(dyn);  // the context (STAGED only)
+  uint16_t* hpos_all = reinterpret_cast<uint16_t*>(dyn + hpos_offset(STAGED, a.S, a.T));
+  uint8_t* hmb_all = dyn + hmb_offset(STAGED, a.S, a.T);
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = blockIdx.x;
   const int32_t* row = a.tok + (int64_t)b * a.S;
   const int32_t* smp = a.samp + (int64_t)b * a.T;
   const int D = a.D, nb = a.nb, M = a.M;
-  const uint64_t below = lanes_below(lane);
 
   Req r;
   {
@@ -554,7 +628,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       r.fast = r.act >= 0 && r.snap_n > 0 && !delta && r.Lcap >= 2;
     }
     const int nww = r.fast ? NW - 1 : NW;
-    r.C = (((r.J + nww - 1) / nww) + 255) / 256 * 256;
+    r.C = ((r.J + nww - 1) / nww + 63) / 64 * 64;
   }
   const int n = r.n, t = r.t, L = r.L, Lcap = r.Lcap, J = r.J, C = r.C;
   int32_t* drow = a.draft + (int64_t)b * a.k;
@@ -566,98 +640,34 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   const bool fast = r.fast;
   for (int i = tid; i < NW * (kMaxD + 1); i += NT) (&sm.whist[0][0])[i] = 0;
   if (!fast && tid < 2 * kMaxNB) sm.cand_valid[tid] = 0;
+  if (tid < Lcap) sm.tail[tid] = ctx_at(row, smp, n, L - 1 - tid);
+  if (STAGED && tid < t) ctxs[n + tid] = smp[tid];
 
-  // ---------------------------------------------------------------- stage || corpus wave
-  if (fast && wid == GW) {
-    corpus_wave_probe(a, r, sm, row, smp, lane);
-  } else {
-    stage_context<VEC>(ctxs, row, smp, n, t, tid, fast ? NT - 64 : NT);
-  }
-  __syncthreads();
-
-  // ---------------------------------------------------------------- 1. local match lengths
-  // Wavefront w < NWW owns end positions [w*C, w*C + C); lane l reads 4 of them per round
-  // (one 16-byte LDS read), screens the last two tail tokens in registers and extends the rare
-  // two-token matches with a wavefront-uniform loop.  Lengths are kept as bytes in LDS.
+  // ---------------------------------------------------------------- 1. local match
+  // Wavefront w < NWW owns end positions [w*C, w*C + C): it stages them (STAGED) and lists the
+  // ones whose token equals the last context token, while the corpus wavefront of the fast path
+  // probes the corpus.
   const int NWW = fast ? NW - 1 : NW;
   const bool worker = wid < NWW;
   const int cbeg = worker ? (wid * C < J ? wid * C : J) : J;
   const int cend = worker ? (cbeg + C < J ? cbeg + C : J) : J;
-  uint8_t* mbs = reinterpret_cast<uint8_t*>(ctxs + propose_row_ints(a.S, a.T));
-  if (tid < Lcap) sm.tail[tid] = ctxs[L - 1 - tid];
+  uint16_t* hpos = hpos_all + wid * C;
+  uint8_t* hmb = hmb_all + wid * C;
+  int nhit = 0;
+  if (fast && wid == GW) {
+    corpus_wave_probe(a, r, sm, row, smp, lane);
+  } else if (worker) {
+    nhit = stage_screen<STAGED>(ctxs, hpos, row, smp, n, cbeg, cend, smp[t - 1], lane);
+  }
+  __syncthreads();
+
+  // match lengths of the hits (the corpus wavefront derives its ladder and sites meanwhile)
   if (fast && wid == GW) corpus_wave_sites(a, r, sm, lane);
   if (worker) {
-    const int t0 = ctxs[L - 1];
-    const int t1 = L >= 2 ? ctxs[L - 2] : -1;
-    const bool two = D >= 2;
-    // tail tokens at offsets off0 .. off0+3 for this lane's share of an extension
-    const int off0 = 2 + 4 * (lane & 15);
-    int tq[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) tq[x] = off0 + x < L ? ctxs[L - 1 - off0 - x] : -1;
-    int ones = 0;
-    for (int r0 = cbeg; r0 < cend; r0 += 256) {
-      const int j0 = r0 + 4 * lane;
-      int v0 = -1, v1 = -1, v2 = -1, v3 = -1, pv = -1;
-      if (j0 < cend) {
-        const int4 q = ctx4[j0 >> 2];
-        v0 = q.x; v1 = q.y; v2 = q.z; v3 = q.w;
-        pv = j0 > 0 ? ctxs[j0 - 1] : -1;
-      }
-      int m[4];
-      m[0] = (j0 < cend && v0 == t0) ? ((two && j0 >= 1 && pv == t1) ? 2 : 1) : 0;
-      m[1] = (j0 + 1 < cend && v1 == t0) ? ((two && v0 == t1) ? 2 : 1) : 0;
-      m[2] = (j0 + 2 < cend && v2 == t0) ? ((two && v1 == t1) ? 2 : 1) : 0;
-      m[3] = (j0 + 3 < cend && v3 == t0) ? ((two && v2 == t1) ? 2 : 1) : 0;
-      if (j0 < cend)
-        *reinterpret_cast<uint32_t*>(mbs + j0) =
-            (uint32_t)m[0] | ((uint32_t)m[1] << 8) | ((uint32_t)m[2] << 16) | ((uint32_t)m[3] << 24);
-      // two-token matches that may go further are compacted and extended below; the others
-      // are final
-      uint32_t cf = 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int lim = D < j0 + u + 1 ? D : j0 + u + 1;
-        if (m[u] == 2 && lim > 2) cf |= 1u << u;
-        else if (m[u] == 1) ++ones;
-        else if (m[u] == 2) atomicAdd(&sm.whist[wid][2], 1);
-      }
-      const int cc = __popc(cf);
-      const int cincl = wave_incl_add(cc);
-      const int ctot = __builtin_amdgcn_readlane(cincl, 63);
-      if (ctot) {
-        int slot = cincl - cc;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (cf & (1u << u)) sm.clist[wid][slot++] = j0 + u;
-        wave_sync();
-        // sixteen lanes per candidate, four tail offsets per lane: the first mismatching
-        // offset over the row of sixteen is the match length
-        for (int p = 0; p < ctot; p += 4) {
-          const int ci = p + (lane >> 4);
-          const bool ok = ci < ctot;
-          const int j = ok ? sm.clist[wid][ci] : 0;
-          const int lim = D < j + 1 ? D : j + 1;
-          int fm = lim;
-#pragma unroll
-          for (int x = 3; x >= 0; --x) {
-            const int o = off0 + x;
-            if (ok && o < lim && ctxs[j - o] != tq[x]) fm = o;
-          }
-          fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppQuadXor1, 0xF, 0xF, false));
-          fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppQuadXor2, 0xF, 0xF, false));
-          fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppHalfMirror, 0xF, 0xF, false));
-          fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppMirror, 0xF, 0xF, false));
-          if (ok && (lane & 15) == 0) {
-            mbs[j] = (uint8_t)fm;
-            atomicAdd(&sm.whist[wid][fm], 1);
-          }
-        }
-        wave_sync();
-      }
-    }
-    ones = wave_sum(ones);
-    if (lane == 0) atomicAdd(&sm.whist[wid][1], ones);
+    if (D <= 25)
+      extend_hits<STAGED, 3>(ctxs, hpos, hmb, nhit, sm.tail, D, sm.whist[wid], row, smp, n, lane);
+    else
+      extend_hits<STAGED, 8>(ctxs, hpos, hmb, nhit, sm.tail, D, sm.whist[wid], row, smp, n, lane);
     wave_sync();
     // this wavefront's suffix sums: wsuf[w][v] = its positions with length >= v
     const int h = lane <= D ? sm.whist[wid][lane] : 0;
@@ -667,8 +677,8 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   __syncthreads();
   // ladder and this wavefront's site offsets: every worker wavefront derives them from the
   // per-wavefront suffix sums (lane v of cg = positions with length >= v); wavefront 0 also
-  // records the candidates.  Then the earliest sites of every distinct local level: 16 length
-  // bytes per lane, SWAR compares, wavefront prefix sums for the order.
+  // records the candidates.  Then the earliest sites of every distinct local level, in one
+  // ordered pass over the wavefront's hit list.
   if (worker) {
     int cg = 0;
     for (int w = 0; w < NWW; ++w) cg += sm.wsuf[w][lane];
@@ -707,40 +717,19 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
         any = any || act[ti];
       }
     }
-    for (int r0 = cbeg; any && r0 < cend; r0 += 1024) {
-      const int jb = r0 + 16 * lane;
-      uint4 q = make_uint4(0, 0, 0, 0);
-      uint32_t keep = 0;
-      if (jb < cend) {
-        q = *reinterpret_cast<const uint4*>(mbs + jb);
-        const int nbytes = cend - jb;
-        keep = nbytes >= 16 ? 0xFFFFu : ((1u << nbytes) - 1u);
-      }
+    for (int e0 = 0; any && e0 < nhit; e0 += 64) {
+      const int e = e0 + lane;
+      const int j = e < nhit ? hpos[e] : 0;
+      const int m = e < nhit ? hmb[e] : 0;
       any = false;
 #pragma unroll
       for (int ti = 0; ti < kMaxNB; ++ti) {
         if (act[ti]) {
-          const uint32_t sub = (uint32_t)lv[ti] * 0x01010101u;
-          uint32_t flags = 0;
-          const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const uint32_t ge = ((wd[x] | 0x80808080u) - sub) & 0x80808080u;
-            const uint32_t nib = ((ge >> 7) & 1u) | ((ge >> 14) & 2u) | ((ge >> 21) & 4u) |
-                                 ((ge >> 28) & 8u);
-            flags |= nib << (4 * x);
-          }
-          flags &= keep;
-          const int c = __popc(flags);
-          const int incl = wave_incl_add(c);
-          const int tot = __builtin_amdgcn_readlane(incl, 63);
-          int rk = pre[ti] + run[ti] + incl - c;
-          while (flags && rk < M) {
-            const int bpos = __builtin_ctz(flags);
-            sm.lsites[ti][rk++] = jb + bpos + 1;
-            flags &= flags - 1;
-          }
-          run[ti] += tot;
+          const bool q = m >= lv[ti];
+          const uint64_t bal = __ballot(q);
+          const int rk = pre[ti] + run[ti] + lanes_before(bal);
+          if (q && rk < M) sm.lsites[ti][rk] = j + 1;
+          run[ti] += __popcll(bal);
           act[ti] = pre[ti] + run[ti] < M;
           any = any || act[ti];
         }
@@ -913,8 +902,14 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       const int p0 = s0 < c0 ? ls[s0] : 0, p1 = s1 < c0 ? ls[s1] : 0;
 #pragma unroll
       for (int d = 0; d < KMAX; ++d) {
-        w0[d] = (s0 < c0 && d < cap && p0 + d < L) ? ctxs[p0 + d] : -1;
-        w1[d] = (s1 < c0 && d < cap && p1 + d < L) ? ctxs[p1 + d] : -1;
+        const bool q0 = s0 < c0 && d < cap && p0 + d < L, q1 = s1 < c0 && d < cap && p1 + d < L;
+        if (STAGED) {
+          w0[d] = q0 ? ctxs[p0 + d] : -1;
+          w1[d] = q1 ? ctxs[p1 + d] : -1;
+        } else {
+          w0[d] = q0 ? ctx_at(row, smp, n, p0 + d) : -1;
+          w1[d] = q1 ? ctx_at(row, smp, n, p1 + d) : -1;
+        }
       }
     } else {
       const long long* gs = sm.gsites[src - nb];
@@ -935,11 +930,11 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       }
     }
   }
-  __syncthreads();  // the context in LDS is dead from here on: it holds the vote tables
+  __syncthreads();  // the context and the hit lists are dead from here on: vote tables
   if (voter) {
     int nout = 0;
     long long snum = 0;
-    int* hk = ctxs + wid * (2 * kVoteSlots);
+    int* hk = reinterpret_cast<int*>(dyn) + wid * (2 * kVoteSlots);
     vote_run<KMAX>(w0, w1, c0, cap, stop_threshold(a, c0), hk, hk + kVoteSlots, lane,
                    sm.cand_out[wid], &nout, &snum);
     if (lane == 0) {
@@ -1003,8 +998,8 @@ __global__ void update_state_kernel(int B, int S, int T, int32_t* tok, const int
 }
 
 template <int KMAX>
-hipError_t launch_k(const ProposeArgs& a, bool vec, size_t dyn, hipStream_t st) {
-  if (vec)
+hipError_t launch_k(const ProposeArgs& a, bool staged, size_t dyn, hipStream_t st) {
+  if (staged)
     hipLaunchKernelGGL((propose_kernel<KMAX, true>), dim3(a.B), dim3(NT), dyn, st, a);
   else
     hipLaunchKernelGGL((propose_kernel<KMAX, false>), dim3(a.B), dim3(NT), dyn, st, a);
@@ -1013,33 +1008,48 @@ hipError_t launch_k(const ProposeArgs& a, bool vec, size_t dyn, hipStream_t st) 
 
 }  // namespace
 
-// Dynamic LDS: the context (S + T ints, also the vote tables once the context is dead), then
-// one match-length byte per end position.
-size_t propose_dynamic_lds(int S, int T) {
-  return (size_t)propose_row_ints(S, T) * sizeof(int) + (((size_t)S + T + 16 + 15) & ~(size_t)15);
+size_t propose_dynamic_lds(bool staged, int S, int T) { return dyn_bytes(staged, S, T); }
+
+namespace {
+size_t g_static_lds = 0;  // largest static LDS over the propose instantiations (queried)
 }
 
-size_t propose_static_lds() { return sizeof(Smem); }
+size_t propose_static_lds() { return g_static_lds ? g_static_lds : sizeof(Smem); }
 
-hipError_t propose_prepare(size_t dyn) {
+bool propose_staged(int S, int T, bool stream_ctx) {
+  return !stream_ctx && dyn_bytes(true, S, T) + propose_static_lds() <= kLdsBytes;
+}
+
+hipError_t propose_prepare() {
   const void* fns[] = {
       (const void*)propose_kernel<8, true>,  (const void*)propose_kernel<8, false>,
       (const void*)propose_kernel<16, true>, (const void*)propose_kernel<16, false>,
       (const void*)propose_kernel<32, true>, (const void*)propose_kernel<32, false>};
+  size_t st = sizeof(Smem);
   for (const void* f : fns) {
-    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    hipFuncAttributes fa;
+    hipError_t e = hipFuncGetAttributes(&fa, f);
+    if (e != hipSuccess) return e;
+    if (fa.sharedSizeBytes > st) st = fa.sharedSizeBytes;
+  }
+  if (st >= kLdsBytes) return hipErrorInvalidValue;
+  for (const void* f : fns) {
+    hipError_t e =
+        hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsBytes - st));
     if (e != hipSuccess) return e;
   }
+  g_static_lds = st;
   return hipSuccess;
 }
 
 hipError_t launch_propose(const ProposeArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
-  const bool vec = (a.S % 4 == 0) && ((uintptr_t)a.tok % 16 == 0);
-  const size_t dyn = propose_dynamic_lds(a.S, a.T);
-  if (a.k <= 8) return launch_k<8>(a, vec, dyn, st);
-  if (a.k <= 16) return launch_k<16>(a, vec, dyn, st);
-  return launch_k<32>(a, vec, dyn, st);
+  const bool staged = propose_staged(a.S, a.T, a.stream_ctx != 0);
+  const size_t dyn = dyn_bytes(staged, a.S, a.T);
+  if (dyn + propose_static_lds() > kLdsBytes) return hipErrorInvalidValue;
+  if (a.k <= 8) return launch_k<8>(a, staged, dyn, st);
+  if (a.k <= 16) return launch_k<16>(a, staged, dyn, st);
+  return launch_k<32>(a, staged, dyn, st);
 }
 
 hipError_t launch_update_state(int B, int S, int T, int32_t* tok, const int32_t* ntns,

@@ -119,6 +119,8 @@ int validate(const sfx_config* c) {
       return fail(SFX_EINVAL, "min_corpus_match=%d outside [2, max_tree_depth]",
                   c->min_corpus_match);
   }
+  if (c->flags & ~SFX_FLAG_STREAM_CONTEXT) return fail(SFX_EINVAL, "unknown flags 0x%x", c->flags);
+  if (c->reserved != 0) return fail(SFX_EINVAL, "reserved must be 0");
   return SFX_OK;
 }
 
@@ -207,17 +209,21 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
     delete c;
     return fail(SFX_EHIP, "no HIP device");
   }
-  const size_t lds = propose_dynamic_lds(cfg->max_seq, cfg->max_sampled);
-  if (lds + propose_static_lds() > kLdsBytes) {
-    delete c;
-    return fail(SFX_EINVAL, "max_seq=%d with max_sampled=%d needs %zu bytes of LDS per request, "
-                "more than the %zu a workgroup has", cfg->max_seq, cfg->max_sampled,
-                lds + propose_static_lds(), kLdsBytes);
-  }
-  hipError_t e = propose_prepare(lds);
+  hipError_t e = propose_prepare();
   if (e != hipSuccess) {
-    free_ctx(c);
+    delete c;
     return hip_fail(e, "propose kernel attributes");
+  }
+  {
+    const bool staged =
+        propose_staged(cfg->max_seq, cfg->max_sampled, (cfg->flags & SFX_FLAG_STREAM_CONTEXT) != 0);
+    const size_t lds = propose_dynamic_lds(staged, cfg->max_seq, cfg->max_sampled);
+    if (lds + propose_static_lds() > kLdsBytes) {
+      delete c;
+      return fail(SFX_EINVAL, "max_seq=%d with max_sampled=%d needs %zu bytes of LDS per request, "
+                  "more than the %zu a workgroup has", cfg->max_seq, cfg->max_sampled,
+                  lds + propose_static_lds(), kLdsBytes);
+    }
   }
   if (cfg->corpus_capacity > 0) {
     c->cap = cfg->corpus_capacity;
@@ -303,6 +309,7 @@ int sfx_propose(sfx_ctx* c, int32_t B, int32_t S, int32_t T, const int32_t* ntns
   a.idx[1] = c->idx[1];
   a.ring = c->ring;
   a.ring_cap = c->cap > 0 ? c->cap : 1;
+  a.stream_ctx = (g.flags & SFX_FLAG_STREAM_CONTEXT) != 0;
   HIP_OR_RETURN(launch_propose(a, (hipStream_t)stream), "propose launch");
   return SFX_OK;
 }

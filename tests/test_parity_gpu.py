@@ -33,7 +33,7 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def run_gpu(S, knobs, n, tok, samp, corpus_docs=None, capacity=0, drafter=None):
+def run_gpu(S, knobs, n, tok, samp, corpus_docs=None, capacity=0, drafter=None, flags=0):
     import torch
 
     B, Sq = tok.shape
@@ -41,7 +41,7 @@ def run_gpu(S, knobs, n, tok, samp, corpus_docs=None, capacity=0, drafter=None):
     d = drafter
     if d is None:
         cfg = S.Config(max_batch=max(B, 1), max_seq=max(Sq, 1), max_sampled=max(T, 1),
-                       corpus_capacity=capacity, **knobs)
+                       corpus_capacity=capacity, flags=flags, **knobs)
         d = S.Drafter(cfg)
         if corpus_docs is not None:
             d.ingest_docs(corpus_docs)
@@ -64,9 +64,15 @@ def knobs_of(w):
     return w.knobs()
 
 
+# Both context paths: staged in LDS (flags 0, rows up to about 19K tokens) and read from device
+# memory (flags 1, FLAG_STREAM_CONTEXT, the path of longer rows).
+FLAGS = [0, 1]
+
+
 # ------------------------------------------------------------------ fuzz and edge cases
+@pytest.mark.parametrize("flags", FLAGS)
 @pytest.mark.parametrize("mode", [0, 1])
-def test_fuzz_small(S, mode):
+def test_fuzz_small(S, mode, flags):
     rng = np.random.default_rng(100 + mode)
     for it in range(40):
         V = int(rng.choice([2, 3, 5, 50]))
@@ -84,12 +90,13 @@ def test_fuzz_small(S, mode):
         n = rng.integers(-3, Sq + 4, size=B).astype(np.int32)
         samp = rng.integers(-1, V, size=(B, T)).astype(np.int32)
         exp = O.propose(O.params_from(kn), n, tok, samp)
-        got = run_gpu(S, kn, n, tok, samp)[:2]
-        assert_same(got, exp, f"fuzz it={it} kn={kn} B={B} S={Sq} T={T}")
+        got = run_gpu(S, kn, n, tok, samp, flags=flags)[:2]
+        assert_same(got, exp, f"fuzz it={it} kn={kn} B={B} S={Sq} T={T} flags={flags}")
 
 
+@pytest.mark.parametrize("flags", FLAGS)
 @pytest.mark.parametrize("mode", [0, 1])
-def test_fuzz_with_corpus(S, mode):
+def test_fuzz_with_corpus(S, mode, flags):
     rng = np.random.default_rng(200 + mode)
     for it in range(25):
         V = int(rng.choice([2, 3, 6, 40]))
@@ -110,11 +117,12 @@ def test_fuzz_with_corpus(S, mode):
         n = rng.integers(0, Sq + 1, size=B).astype(np.int32)
         samp = rng.integers(0, V, size=(B, 1)).astype(np.int32)
         exp = O.propose(O.params_from(kn), n, tok, samp, corpus=lc.text())
-        got = run_gpu(S, kn, n, tok, samp, corpus_docs=docs, capacity=1 << 14)[:2]
-        assert_same(got, exp, f"corpus fuzz it={it} kn={kn}")
+        got = run_gpu(S, kn, n, tok, samp, corpus_docs=docs, capacity=1 << 14, flags=flags)[:2]
+        assert_same(got, exp, f"corpus fuzz it={it} kn={kn} flags={flags}")
 
 
-def test_degenerate_rows(S):
+@pytest.mark.parametrize("flags", FLAGS)
+def test_degenerate_rows(S, flags):
     """Empty rows, rows with no sampled token, a single repeated token (every position
     matches), n above S, S not a multiple of 4, T=0."""
     B, Sq = 6, 301
@@ -125,26 +133,52 @@ def test_degenerate_rows(S):
         kn = dict(k=32, max_tree_depth=64, num_backoff=1 + 7 * mode, max_occurrences=128,
                   mode=mode, spec_factor_ppm=10**7, min_token_prob_ppm=0)
         exp = O.propose(O.params_from(kn), n, tok, samp)
-        assert_same(run_gpu(S, kn, n, tok, samp)[:2], exp, f"degenerate mode {mode}")
+        assert_same(run_gpu(S, kn, n, tok, samp, flags=flags)[:2], exp, f"degenerate mode {mode}")
     kn = dict(k=4, max_tree_depth=24, num_backoff=1, max_occurrences=128, mode=0)
     e0 = O.propose(O.params_from(kn), n, tok, samp[:, :0])
-    assert_same(run_gpu(S, kn, n, tok, samp[:, :0])[:2], e0, "T=0")
+    assert_same(run_gpu(S, kn, n, tok, samp[:, :0], flags=flags)[:2], e0, "T=0")
+
+
+def test_long_repeated_rows(S):
+    """Rows of one repeated token at full length (every end position is a hit), a long row that
+    starts with a repeated run, and rows of period 2, in both context paths and at the largest
+    row capacity."""
+    B, Sq = 4, 32768
+    tok = np.full((B, Sq), 5, np.int32)
+    tok[1, 20000:] = np.arange(Sq - 20000) % 97 + 10
+    tok[2, :] = np.arange(Sq) % 2
+    tok[3, :] = np.arange(Sq) % 3
+    n = np.array([Sq, Sq, Sq - 1, 20001], np.int32)
+    samp = np.array([[5], [5], [1], [2]], np.int32)
+    for mode in (0, 1):
+        kn = dict(k=32, max_tree_depth=64, num_backoff=1 + 7 * mode, max_occurrences=128,
+                  mode=mode, spec_factor_ppm=10**7, min_token_prob_ppm=0)
+        exp = O.propose(O.params_from(kn), n, tok, samp, num_threads=NTHREADS)
+        # a 32768-token row only runs on the streaming path; 16384 fits either
+        assert_same(run_gpu(S, kn, n, tok, samp)[:2], exp, f"long rows mode {mode}")
+        h = Sq // 2
+        n2 = np.minimum(n, h)
+        exp2 = O.propose(O.params_from(kn), n2, tok[:, :h], samp, num_threads=NTHREADS)
+        for flags in FLAGS:
+            assert_same(run_gpu(S, kn, n2, np.ascontiguousarray(tok[:, :h]), samp,
+                                flags=flags)[:2], exp2, f"half rows mode {mode} flags {flags}")
 
 
 # ------------------------------------------------------------------ workload configurations
+@pytest.mark.parametrize("flags", FLAGS)
 @pytest.mark.parametrize("cid", [1, 2])
-def test_config_self_match(S, cid):
+def test_config_self_match(S, cid, flags):
     w = W.WORKLOADS[cid]
     n, tok, samp = W.make_batch(cid)
     exp = O.propose(O.params_from(w.knobs()), n, tok, samp, num_threads=NTHREADS)
-    got = run_gpu(S, w.knobs(), n, tok, samp)[:2]
-    assert_same(got, exp, f"config {cid}")
+    got = run_gpu(S, w.knobs(), n, tok, samp, flags=flags)[:2]
+    assert_same(got, exp, f"config {cid} flags {flags}")
     assert (got[1] <= w.k).all()
     assert (got[0] != W.POISON).all()
 
 
-@pytest.mark.parametrize("cid", [3, 4])
-def test_config_corpus(S, cid):
+@pytest.mark.parametrize("cid,flags", [(3, 0), (4, 0), (4, 1)])
+def test_config_corpus(S, cid, flags):
     import torch
 
     w = W.WORKLOADS[cid]
@@ -152,7 +186,8 @@ def test_config_corpus(S, cid):
     text = W.join_docs(docs)
     n, tok, samp = W.make_batch(cid)
     cap = 1 << 20
-    got_d, got_n, d = run_gpu(S, w.knobs(), n, tok, samp, corpus_docs=docs, capacity=cap)
+    got_d, got_n, d = run_gpu(S, w.knobs(), n, tok, samp, corpus_docs=docs, capacity=cap,
+                              flags=flags)
     snap = d.corpus_snapshot().cpu().numpy()
     assert np.array_equal(snap, text)
     exp = O.propose(O.params_from(w.knobs()), n, tok, samp, corpus=text, num_threads=NTHREADS)
@@ -162,6 +197,49 @@ def test_config_corpus(S, cid):
     torch.cuda.synchronize()
     assert np.array_equal(d2.cpu().numpy(), got_d) and np.array_equal(n2.cpu().numpy(), got_n)
     d.close()
+
+
+def test_config_ingest_under_load(S):
+    """Workload 5: a 2^22-token ring seeded with the template corpus; every step harvests 256
+    finished rows and starts an asynchronous rebuild while B=512 requests of up to 32768 tokens
+    propose.  At several steps (with a rebuild in flight, so part of the corpus is only in the
+    delta, and after the ring has started to evict) every row must equal the oracle on the live
+    corpus, whatever rebuild is live at that moment."""
+    import torch
+
+    w = W.WORKLOADS[5]
+    cfg = S.Config(max_batch=w.B, max_seq=w.S, max_sampled=w.T,
+                   corpus_capacity=w.ring_capacity, **w.knobs())
+    d = S.Drafter(cfg)
+    seed = W.corpus_docs(5)
+    d.ingest_docs(seed)
+    d.rebuild()
+    lc = O.LiveCorpus(w.ring_capacity)
+    lc.ingest(seed)
+    n, tok, samp = W.make_batch(5)
+    dn, dt, ds = dev(n), dev(tok), dev(samp)
+    p = O.params_from(w.knobs())
+    checks = 0
+    for step in range(12):
+        itok, rows, lens = W.ingest_batch(5, step)
+        d.harvest_finished(dev(rows), dev(lens), dev(itok))
+        lc.ingest([itok[r, :lens[r]] for r in rows])
+        if step % 2 == 0:
+            d.wait_rebuild()
+            d.rebuild_async()
+        if step in (0, 5, 11):
+            got_d, got_n = d.propose(dn, dt, ds)
+            torch.cuda.synchronize()
+            exp = O.propose(p, n, tok, samp, corpus=lc.text(), num_threads=NTHREADS)
+            assert_same((got_d.cpu().numpy(), got_n.cpu().numpy()), exp, f"step {step}")
+            assert (got_n.cpu().numpy() <= w.k).all()
+            checks += 1
+    d.wait_rebuild()
+    snap = d.corpus_snapshot().cpu().numpy()
+    assert np.array_equal(snap, lc.text())
+    assert lc.evicted() > 0, "the ring should have started evicting"
+    d.close()
+    assert checks == 3
 
 
 # ------------------------------------------------------------------ suffix arrays
