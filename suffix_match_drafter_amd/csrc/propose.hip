@@ -119,6 +119,20 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
   return base + x - v;
 }
 
+// Barrier over the worker wavefronts only, so that the corpus wavefront of the fast path keeps
+// working through the local phases: an LDS arrival count.  Every worker wavefront passes each
+// such barrier exactly once, so the count reaches k * (workers) at the k-th one; the spin is
+// bounded as a guard.
+__device__ __forceinline__ void worker_barrier(int* ctr, int target, int lane) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  for (int spin = 0; spin < (1 << 24); ++spin) {
+    if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 __device__ __forceinline__ int ctx_at(const int32_t* row, const int32_t* smp, int n, int x) {
   return x < n ? row[x] : smp[x - n];
 }
@@ -154,6 +168,7 @@ struct Smem {
   int gm4[kMaxM];       // extension lengths of the first 4-gram occurrences
   const int32_t* plp[kNG];
   int wsum[NW + 1];
+  int wbar;  // arrivals at the worker-only barriers
   int sel[2];
 };
 
@@ -247,13 +262,27 @@ __device__ void probe_ngram(const View ib, const int* tail, int Lcap, long long 
 }
 
 // Backward extension of a 4-gram occurrence starting at snapshot position i: the match length
-// (>= 4) against the tail, at most `cap`.
+// (>= 4) against the tail, at most `cap`.  The preceding tokens are fetched eight at a time, all
+// eight loads in flight, so a match of length l costs about (l - 4) / 8 + 1 round trips.
 __device__ __forceinline__ int extend4(const int32_t* text, const int* tail, int i, int cap) {
   int m = 4;
-  while (m < cap && i - 1 - (m - 4) >= 0) {
-    const int c = text[i - 1 - (m - 4)];
-    if (c < 0 || c != tail[m]) break;
-    ++m;
+  for (int base = 0; base < cap - 4; base += 8) {
+    int c[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int o = base + q;
+      c[q] = (o < cap - 4 && i - 1 - o >= 0) ? text[i - 1 - o] : -2;
+    }
+    bool stop = false;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (!stop) {
+        const int ti = 4 + base + q < kMaxD ? 4 + base + q : kMaxD - 1;
+        if (c[q] >= 0 && c[q] == tail[ti]) ++m;
+        else stop = true;
+      }
+    }
+    if (stop) break;
   }
   return m;
 }
@@ -465,117 +494,171 @@ __device__ __forceinline__ void corpus_wave_sites(const ProposeArgs& a, const Re
   }
 }
 
-// Dynamic LDS of one request.  Staged: [context ints | hit positions (u16) | hit lengths (u8)];
-// streaming (the context stays in HBM): [hit positions | hit lengths].  The vote tables of the
-// expansion alias the start of the region once the context and the hit lists are dead.
+// Dynamic LDS of one request.  Staged: [context ints | hit positions (u16) | hit lengths (u8) |
+// hit bit words]; streaming (the context stays in HBM): the same without the context.  The vote
+// tables of the expansion alias the start of the region once those are dead.
 constexpr int kVoteBytes = NW * 2 * kVoteSlots * 4;
-__host__ __device__ inline int ctx_ints(int S, int T) { return (S + T + 4 + 3) & ~3; }
+// context ints, then 64 spare slots that absorb the staging stores of lanes past the row end
+__host__ __device__ inline int ctx_ints(int S, int T) { return ((S + T + 4 + 3) & ~3) + 64; }
+__host__ __device__ inline int ctx_spare(int S, int T) { return ctx_ints(S, T) - 64; }
 // Hit-list entries: wavefront w owns [w*C, w*C + C) with C = ceil(J / waves) rounded up to 64,
 // J <= S + T - 1, so S + T + 64 * NW entries always suffice.
-__host__ __device__ inline int hit_cap(int S, int T) { return (S + T + 64 * NW + 15) & ~15; }
+__host__ __device__ inline int hit_cap(int S, int T) { return (S + T + 64 * NW + 63) & ~63; }
 __host__ __device__ inline size_t hpos_offset(bool staged, int S, int T) {
   return staged ? (size_t)4 * ctx_ints(S, T) : 0;
 }
 __host__ __device__ inline size_t hmb_offset(bool staged, int S, int T) {
   return hpos_offset(staged, S, T) + (size_t)2 * hit_cap(S, T);
 }
+// one 64-bit word of hit bits per 64 end positions
+__host__ __device__ inline size_t bits_offset(bool staged, int S, int T) {
+  return (hmb_offset(staged, S, T) + hit_cap(S, T) + 15) & ~(size_t)15;
+}
 __host__ __device__ inline size_t dyn_bytes(bool staged, int S, int T) {
-  const size_t b = (hmb_offset(staged, S, T) + hit_cap(S, T) + 15) & ~(size_t)15;
+  const size_t b = bits_offset(staged, S, T) + (size_t)8 * (hit_cap(S, T) / 64);
   return b < (size_t)kVoteBytes ? (size_t)kVoteBytes : b;
 }
 
-constexpr int kScreenLoads = 32;  // dword loads in flight per lane while screening (2048 positions)
+constexpr int kScreenLoads = 32;  // 64-position words per screening group (2048 positions)
+constexpr uint32_t kBufferWord3 = 0x00020000;  // raw buffer resource, gfx9 format bits
 
 __device__ __forceinline__ int lanes_before(uint64_t bal) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 }
 
-// Local step 1 for one wavefront's chunk [cbeg, cend) of end positions: load the row part with
-// every load of a lane in flight (lane-strided dwords, so each load instruction is one coalesced
-// 256-byte run), stage it in LDS when STAGED, and list the positions whose token equals the last
-// context token t0, in position order, at hpos[0..).  Returns the number of hits.
-template <bool STAGED>
-__device__ __forceinline__ int stage_screen(int* ctxs, uint16_t* hpos, const int32_t* row,
-                                            const int32_t* smp, int n, int cbeg, int cend, int t0,
-                                            int lane) {
-  int nhit = 0;
-  const int rend = cend < n ? cend : n;
-  for (int g0 = cbeg; g0 < rend; g0 += 64 * kScreenLoads) {
-    int v[kScreenLoads];
-#pragma unroll
-    for (int i = 0; i < kScreenLoads; ++i) {
-      const int x = g0 + 64 * i + lane;
-      v[i] = x < rend ? row[x] : -1;
-    }
-#pragma unroll
-    for (int i = 0; i < kScreenLoads; ++i) {
-      const int x = g0 + 64 * i + lane;
-      if (STAGED && x < rend) ctxs[x] = v[i];
-      const bool h = x < rend && v[i] == t0;
-      const uint64_t bal = __ballot(h);
-      if (h) hpos[nhit + lanes_before(bal)] = (uint16_t)x;
-      nhit += __popcll(bal);
-    }
-  }
-  // end positions among the sampled ids (at most T - 1 of them, after every row position)
-  if (cend > n) {
-    const int x = (cbeg > n ? cbeg : n) + lane;
-    const bool h = x < cend && smp[x - n] == t0;
-    const uint64_t bal = __ballot(h);
-    if (h) hpos[nhit + lanes_before(bal)] = (uint16_t)x;
-    nhit += __popcll(bal);
-  }
-  return nhit;
+// Lane l of acc := v (l and v wavefront-uniform).  gfx9 reads at most one SGPR per VALU
+// instruction besides M0, so the lane select goes through M0; nothing else in this kernel uses
+// M0 (no LDS DMA, no relative indexing, no messages), so setting it here disturbs nothing.
+__device__ __forceinline__ uint32_t put_lane(uint32_t acc, uint32_t v, int l) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %2\n\tv_writelane_b32 %0, %1, m0" : "+v"(acc) : "s"(v), "s"(l) : "m0");
+#pragma clang diagnostic pop
+  return acc;
 }
 
-// Local step 2: the backward match length of every listed hit (its last token already matches).
-// Eight lanes per hit, each comparing OPL consecutive tail offsets; the smallest mismatching
-// offset over the eight (or the cap min(D, j+1)) is the length.  Lengths go to hmb[] and the
-// wavefront's histogram.
-template <bool STAGED, int OPL>
+// Local step 1 for one wavefront's chunk [cbeg, cend) of end positions.  The row part is read
+// with bounds-checked buffer loads (every load of a lane in flight; lanes on consecutive
+// positions, so each load instruction is one coalesced 256-byte run) and staged in LDS when
+// STAGED.  For every 64 positions one ballot is kept as a bit word: the end positions whose
+// token is the last context token t0 (match length >= 1).  Word i covers positions
+// cbeg + 64 i ...; the end positions among the sampled ids (at most T - 1, after every row
+// position) go to *s1, based at max(cbeg, n).  Returns the number of row words.
+template <bool STAGED>
+__device__ __forceinline__ int stage_screen(int* ctxs, int spare, uint64_t* b1w,
+                                            const int32_t* row, const int32_t* smp, int n,
+                                            int cbeg, int cend, int t0, int lane, uint64_t* s1) {
+  const int rend = __builtin_amdgcn_readfirstlane(cend < n ? cend : n);
+  // t0 arrives by a scalar load, which shares a counter with the LDS stores below: settle it
+  // once here so that no store in the loop has to drain that counter
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  int nw = 0;
+  if (rend > cbeg) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, rend * 4, kBufferWord3);
+    for (int g0 = cbeg; g0 < rend; g0 += 64 * kScreenLoads) {
+      int v[kScreenLoads];
+      const int vo = (g0 + lane) * 4;
+#pragma unroll
+      for (int i = 0; i < kScreenLoads; ++i)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo + 256 * i, 0, 0);
+      const int ne = (rend - g0 + 63) >> 6 < kScreenLoads ? (rend - g0 + 63) >> 6 : kScreenLoads;
+      uint32_t a1 = 0;
+#pragma unroll
+      for (int i = 0; i < kScreenLoads; ++i) {
+        if (i < ne) {
+          const int rem = rend - g0 - 64 * i;  // >= 1
+          const uint64_t inmask = rem >= 64 ? ~0ull : ((1ull << rem) - 1ull);
+          const int x = g0 + 64 * i + lane;
+          if (STAGED) {
+            if (rem >= 64) ctxs[x] = v[i];
+            else ctxs[x < rend ? x : spare + lane] = v[i];
+          }
+          const uint64_t w1 = __ballot(v[i] == t0) & inmask;
+          a1 = put_lane(a1, (uint32_t)w1, 2 * i);
+          a1 = put_lane(a1, (uint32_t)(w1 >> 32), 2 * i + 1);
+        }
+      }
+      if (lane < 2 * ne) reinterpret_cast<uint32_t*>(b1w + nw)[lane] = a1;
+      nw += ne;
+    }
+  }
+  *s1 = 0;
+  if (cend > n) {
+    const int x = (cbeg > n ? cbeg : n) + lane;
+    const bool in = x < cend;
+    const int v = in ? smp[x - n] : -1;
+    *s1 = __ballot(in && v == t0);
+  }
+  return nw;
+}
+
+// Positions of the set bits of nw words (word i based at base0 + 64 i) followed by one extra
+// word `extra` based at xbase, in order, into out[]; returns their number.  Every lane of the
+// wavefront takes part.
+__device__ __forceinline__ int bits_to_list(const uint64_t* w, int nw, uint64_t extra, int xbase,
+                                            int base0, uint16_t* out, int lane) {
+  int cnt = 0;
+  for (int w0 = 0; w0 <= nw; w0 += 64) {
+    const int wi = w0 + lane;
+    uint64_t wd = wi < nw ? w[wi] : (wi == nw ? extra : 0ull);
+    const int base = wi < nw ? base0 + 64 * wi : xbase;
+    const int c = __popcll(wd);
+    const int incl = wave_incl_add(c);
+    int at = cnt + incl - c;
+    while (wd) {
+      out[at++] = (uint16_t)(base + __builtin_ctzll(wd));
+      wd &= wd - 1;
+    }
+    cnt += __builtin_amdgcn_readlane(incl, 63);
+  }
+  return cnt;
+}
+
+// Local step 2: the backward match length of every listed hit (its last token already matches,
+// so the length is at least 1), one hit per lane: the previous token decides whether the match
+// goes on; if it does, the tail is compared four offsets per round.  Lengths go to hmb[] and
+// the wavefront's histogram.
+template <bool STAGED>
 __device__ __forceinline__ void extend_hits(const int* ctxs, const uint16_t* hpos, uint8_t* hmb,
                                             int nhit, const int* tail, int D, int* whist,
                                             const int32_t* row, const int32_t* smp, int n,
                                             int lane) {
-  const int g = lane >> 3, r = lane & 7;
-  int tq[OPL];
+  const int t1 = D >= 2 ? tail[1] : -1;
+  for (int e0 = 0; e0 < nhit; e0 += 64) {
+    const int e = e0 + lane;
+    const bool ok = e < nhit;
+    const int j = ok ? hpos[e] : 0;
+    const int lim = D < j + 1 ? D : j + 1;
+    int m = 1;
+    if (ok && lim >= 2) {
+      const int c1 = STAGED ? ctxs[j - 1] : ctx_at(row, smp, n, j - 1);
+      if (c1 == t1) {
+        m = 2;
+        for (int o0 = 2; o0 < lim; o0 += 4) {
+          int c[4];
 #pragma unroll
-  for (int x = 0; x < OPL; ++x) {
-    const int o = 1 + r * OPL + x;
-    tq[x] = o < D ? tail[o] : -1;
-  }
-  for (int e0 = 0; e0 < nhit; e0 += 16) {
-    int j[2], lim[2], c[2][OPL];
+          for (int q = 0; q < 4; ++q) {
+            const int at = o0 + q < lim ? j - o0 - q : 0;
+            c[q] = STAGED ? ctxs[at] : ctx_at(row, smp, n, at);
+          }
+          bool stop = false;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int e = e0 + 8 * h + g;
-      j[h] = e < nhit ? hpos[e] : 0;
-      lim[h] = e < nhit ? (D < j[h] + 1 ? D : j[h] + 1) : 0;
-#pragma unroll
-      for (int x = 0; x < OPL; ++x) {
-        const int o = 1 + r * OPL + x;
-        const int at = o < lim[h] ? j[h] - o : 0;
-        c[h][x] = STAGED ? ctxs[at] : ctx_at(row, smp, n, at);
+          for (int q = 0; q < 4; ++q) {
+            if (!stop) {
+              if (o0 + q < lim && c[q] == tail[o0 + q]) ++m;
+              else stop = true;
+            }
+          }
+          if (stop) break;
+        }
       }
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      int fm = lim[h];
-#pragma unroll
-      for (int x = OPL - 1; x >= 0; --x) {
-        const int o = 1 + r * OPL + x;
-        if (o < lim[h] && c[h][x] != tq[x]) fm = o;
-      }
-      fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppQuadXor1, 0xF, 0xF, false));
-      fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppQuadXor2, 0xF, 0xF, false));
-      fm = min(fm, __builtin_amdgcn_mov_dpp(fm, kDppHalfMirror, 0xF, 0xF, false));
-      const int e = e0 + 8 * h + g;
-      if (r == 0 && e < nhit) {
-        hmb[e] = (uint8_t)fm;
-        atomicAdd(&whist[fm], 1);
-      }
-    }
+    if (ok) hmb[e] = (uint8_t)m;
+    const uint64_t one = __ballot(ok && m == 1);
+    if (ok && m > 1) atomicAdd(&whist[m], 1);
+    if (lane == 0 && one) atomicAdd(&whist[1], __popcll(one));
   }
 }
 
@@ -586,8 +669,10 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   int* ctxs = reinterpret_cast<int*>(dyn);  // the context (STAGED only)
   uint16_t* hpos_all = reinterpret_cast<uint16_t*>(dyn + hpos_offset(STAGED, a.S, a.T));
   uint8_t* hmb_all = dyn + hmb_offset(STAGED, a.S, a.T);
+  uint64_t* bits_all = reinterpret_cast<uint64_t*>(dyn + bits_offset(STAGED, a.S, a.T));
   __shared__ Smem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform (SGPR)
   const int b = blockIdx.x;
   const int32_t* row = a.tok + (int64_t)b * a.S;
   const int32_t* smp = a.samp + (int64_t)b * a.T;
@@ -640,46 +725,53 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   const bool fast = r.fast;
   for (int i = tid; i < NW * (kMaxD + 1); i += NT) (&sm.whist[0][0])[i] = 0;
   if (!fast && tid < 2 * kMaxNB) sm.cand_valid[tid] = 0;
+  if (tid == 0) sm.wbar = 0;
+  __syncthreads();
+  // the tail (read from the extension on) and the sampled ids of the staged context
   if (tid < Lcap) sm.tail[tid] = ctx_at(row, smp, n, L - 1 - tid);
   if (STAGED && tid < t) ctxs[n + tid] = smp[tid];
 
   // ---------------------------------------------------------------- 1. local match
-  // Wavefront w < NWW owns end positions [w*C, w*C + C): it stages them (STAGED) and lists the
-  // ones whose token equals the last context token, while the corpus wavefront of the fast path
-  // probes the corpus.
+  // Wavefront w < NWW owns end positions [w*C, w*C + C): it stages them (STAGED) and marks the
+  // ones whose token equals the last context token.  In the fast path the corpus wavefront
+  // probes the corpus and derives its ladder and sites meanwhile, through every local phase
+  // (the workers synchronise among themselves only).
   const int NWW = fast ? NW - 1 : NW;
   const bool worker = wid < NWW;
   const int cbeg = worker ? (wid * C < J ? wid * C : J) : J;
   const int cend = worker ? (cbeg + C < J ? cbeg + C : J) : J;
-  uint16_t* hpos = hpos_all + wid * C;
-  uint8_t* hmb = hmb_all + wid * C;
-  int nhit = 0;
   if (fast && wid == GW) {
     corpus_wave_probe(a, r, sm, row, smp, lane);
-  } else if (worker) {
-    nhit = stage_screen<STAGED>(ctxs, hpos, row, smp, n, cbeg, cend, smp[t - 1], lane);
-  }
-  __syncthreads();
+    corpus_wave_sites(a, r, sm, lane);
+  } else {
+    uint16_t* hpos = hpos_all + wid * C;
+    uint8_t* hmb = hmb_all + wid * C;
+    uint64_t* b1w = bits_all + wid * (C >> 6);
+    uint64_t s1 = 0;
+    const int sbase = cbeg > n ? cbeg : n;
+    const int nw = stage_screen<STAGED>(ctxs, ctx_spare(a.S, a.T), b1w, row, smp, n, cbeg, cend,
+                                        smp[t - 1], lane, &s1);
+    if (fast) worker_barrier(&sm.wbar, NWW, lane);
+    else __syncthreads();
 
-  // match lengths of the hits (the corpus wavefront derives its ladder and sites meanwhile)
-  if (fast && wid == GW) corpus_wave_sites(a, r, sm, lane);
-  if (worker) {
-    if (D <= 25)
-      extend_hits<STAGED, 3>(ctxs, hpos, hmb, nhit, sm.tail, D, sm.whist[wid], row, smp, n, lane);
-    else
-      extend_hits<STAGED, 8>(ctxs, hpos, hmb, nhit, sm.tail, D, sm.whist[wid], row, smp, n, lane);
+    // match lengths of the hits, listed in order
+    const int nhit = bits_to_list(b1w, nw, s1, sbase, cbeg, hpos, lane);
     wave_sync();
-    // this wavefront's suffix sums: wsuf[w][v] = its positions with length >= v
-    const int h = lane <= D ? sm.whist[wid][lane] : 0;
-    const int incl = wave_incl_add(h);
-    sm.wsuf[wid][lane] = __builtin_amdgcn_readlane(incl, 63) - incl + h;
-  }
-  __syncthreads();
-  // ladder and this wavefront's site offsets: every worker wavefront derives them from the
-  // per-wavefront suffix sums (lane v of cg = positions with length >= v); wavefront 0 also
-  // records the candidates.  Then the earliest sites of every distinct local level, in one
-  // ordered pass over the wavefront's hit list.
-  if (worker) {
+    extend_hits<STAGED>(ctxs, hpos, hmb, nhit, sm.tail, D, sm.whist[wid], row, smp, n, lane);
+    wave_sync();
+    {
+      // this wavefront's suffix sums: wsuf[w][v] = its positions with length >= v
+      const int h = lane <= D ? sm.whist[wid][lane] : 0;
+      const int incl = wave_incl_add(h);
+      sm.wsuf[wid][lane] = __builtin_amdgcn_readlane(incl, 63) - incl + h;
+    }
+    if (fast) worker_barrier(&sm.wbar, 2 * NWW, lane);
+    else __syncthreads();
+
+    // ladder and this wavefront's site offsets: every worker wavefront derives them from the
+    // per-wavefront suffix sums (lane v of cg = positions with length >= v); wavefront 0 also
+    // records the candidates.  Then the earliest sites of every distinct local level, in one
+    // ordered pass over the hit list.
     int cg = 0;
     for (int w = 0; w < NWW; ++w) cg += sm.wsuf[w][lane];
     const int maxl = D < J ? D : J;
