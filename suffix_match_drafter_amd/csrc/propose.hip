@@ -297,7 +297,7 @@ __device__ __forceinline__ int corpus_at(const ProposeArgs& a, const int32_t* te
 
 // Depth-wise vote of one candidate held by one wavefront: lane l owns sites l and l+64, whose
 // continuation windows are w0 / w1 (-1 past the end of a continuation).  Writes the tokens to
-// out[] (lane 0) and returns the count and the sum of per-depth counts.  cmin is the smallest
+// out[] and returns the count and the sum of per-depth counts.  cmin is the smallest
 // count the stop rule keeps (0 when there is no stop rule).
 template <int KMAX>
 __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[KMAX], int c0,
@@ -307,6 +307,7 @@ __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[
   int nout = 0;
   long long snum = 0;
   bool done = false;
+  int tokv = -1;  // lane i collects the i-th voted token
 #pragma unroll
   for (int d = 0; d < KMAX; ++d) {
     if (!done && d < cap) {
@@ -373,7 +374,7 @@ __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[
         if (c < cmin) {
           done = true;
         } else {
-          if (lane == 0) out[nout] = w;
+          tokv = lane == nout ? w : tokv;
           ++nout;
           snum += c;
           al0 = tk0 == w;
@@ -382,6 +383,7 @@ __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[
       }
     }
   }
+  if (lane < nout) out[lane] = tokv;
   *n_out = nout;
   *snum_out = snum;
 }
