@@ -323,15 +323,21 @@ __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[
         const int first = v0 ? __builtin_amdgcn_readlane(tk0, fl) : __builtin_amdgcn_readlane(tk1, fl);
         const uint64_t f0 = __ballot(tk0 == first), f1 = __ballot(tk1 == first);
         const int nalive = __popcll(v0) + __popcll(v1);
-        if (f0 == v0 && f1 == v1) {
+        const int cf = __popcll(f0) + __popcll(f1);
+        if (cf == nalive) {
           c = nalive;
           w = first;
+        } else if (2 * cf > nalive) {
+          // a strict majority: no other token can reach its count
+          c = cf;
+          w = first;
         } else if (nalive <= kSmallVote) {
-          // few alive sites: one ballot pair per distinct token
-          uint64_t key = ((uint64_t)(__popcll(f0) + __popcll(f1)) << 32) |
-                         (uint32_t)(0x7FFFFFFF - first);
+          // few alive sites: one ballot pair per distinct token, until the best count exceeds
+          // every vote not yet counted
+          uint64_t key = ((uint64_t)cf << 32) | (uint32_t)(0x7FFFFFFF - first);
           uint64_t r0 = v0 & ~f0, rr1 = v1 & ~f1;
-          while (r0 | rr1) {
+          int rest = nalive - cf;
+          while ((r0 | rr1) && (int)(key >> 32) <= rest) {
             const int tok = r0 ? __builtin_amdgcn_readlane(tk0, __builtin_ctzll(r0))
                                : __builtin_amdgcn_readlane(tk1, __builtin_ctzll(rr1));
             const uint64_t e0 = __ballot(tk0 == tok), e1 = __ballot(tk1 == tok);
@@ -340,6 +346,7 @@ __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[
             key = k > key ? k : key;
             r0 &= ~e0;
             rr1 &= ~e1;
+            rest -= __popcll(e0) + __popcll(e1);
           }
           c = (int)(key >> 32);
           w = 0x7FFFFFFF - (int)(uint32_t)(key & 0xFFFFFFFFu);
