@@ -16,6 +16,8 @@
 //   3. expansion (step 3): one wavefront per candidate votes depth by depth over its sites
 //      (ballots when few sites are alive, an LDS hash otherwise); stop rule and score use
 //      integer cross-multiplication; selection and the [k] output row follow.
+#include <type_traits>
+
 #include "propose.h"
 
 namespace sfx {
@@ -536,15 +538,25 @@ __device__ __forceinline__ int lanes_before(uint64_t bal) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 }
 
-// Lane l of acc := v (l and v wavefront-uniform).  gfx9 reads at most one SGPR per VALU
-// instruction besides M0, so the lane select goes through M0; nothing else in this kernel uses
-// M0 (no LDS DMA, no relative indexing, no messages), so setting it here disturbs nothing.
-__device__ __forceinline__ uint32_t put_lane(uint32_t acc, uint32_t v, int l) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %2\n\tv_writelane_b32 %0, %1, m0" : "+v"(acc) : "s"(v), "s"(l) : "m0");
-#pragma clang diagnostic pop
+// Lanes L and L+1 of acc := the low and high halves of a 64-bit ballot; L is an immediate.
+// The ballot is an SGPR pair written by a VALU compare just before, and the compiler does not
+// look inside inline assembly for hazards, so five wait states come first.
+template <int L>
+__device__ __forceinline__ uint32_t put_ballot(uint32_t acc, uint64_t v) {
+  asm volatile("s_nop 4\n\tv_writelane_b32 %0, %1, %3\n\tv_writelane_b32 %0, %2, %4"
+               : "+v"(acc)
+               : "s"((uint32_t)v), "s"((uint32_t)(v >> 32)), "i"(L), "i"(L + 1));
   return acc;
+}
+
+// f(integral_constant<int, I>) for I = I0 .. N-1, unrolled at compile time (so that lane and
+// register indices are immediates).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
 // Local step 1 for one wavefront's chunk [cbeg, cend) of end positions.  The row part is read
@@ -573,22 +585,24 @@ __device__ __forceinline__ int stage_screen(int* ctxs, int spare, uint64_t* b1w,
       for (int i = 0; i < kScreenLoads; ++i)
         v[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo + 256 * i, 0, 0);
       const int ne = (rend - g0 + 63) >> 6 < kScreenLoads ? (rend - g0 + 63) >> 6 : kScreenLoads;
+      const int nfull = (rend - g0) >> 6;  // elements whose 64 positions all lie below rend
       uint32_t a1 = 0;
-#pragma unroll
-      for (int i = 0; i < kScreenLoads; ++i) {
+      static_for<0, kScreenLoads>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
         if (i < ne) {
-          const int rem = rend - g0 - 64 * i;  // >= 1
-          const uint64_t inmask = rem >= 64 ? ~0ull : ((1ull << rem) - 1ull);
           const int x = g0 + 64 * i + lane;
-          if (STAGED) {
-            if (rem >= 64) ctxs[x] = v[i];
-            else ctxs[x < rend ? x : spare + lane] = v[i];
+          uint64_t w1;
+          if (i < nfull) {
+            if (STAGED) ctxs[x] = v[i];
+            w1 = __ballot(v[i] == t0);
+          } else {
+            const int rem = rend - g0 - 64 * i;  // 1..63
+            if (STAGED) ctxs[x < rend ? x : spare + lane] = v[i];
+            w1 = __ballot(v[i] == t0) & ((1ull << rem) - 1ull);
           }
-          const uint64_t w1 = __ballot(v[i] == t0) & inmask;
-          a1 = put_lane(a1, (uint32_t)w1, 2 * i);
-          a1 = put_lane(a1, (uint32_t)(w1 >> 32), 2 * i + 1);
+          a1 = put_ballot<(2 * i) & 62>(a1, w1);
         }
-      }
+      });
       if (lane < 2 * ne) reinterpret_cast<uint32_t*>(b1w + nw)[lane] = a1;
       nw += ne;
     }
