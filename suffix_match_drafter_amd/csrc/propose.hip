@@ -643,12 +643,17 @@ __device__ __forceinline__ int bits_to_list(const uint64_t* w, int nw, uint64_t 
 // so the length is at least 1), one hit per lane: the previous token decides whether the match
 // goes on; if it does, the tail is compared four offsets per round.  Lengths go to hmb[] and
 // the wavefront's histogram.
+constexpr int kTailRegs = 24;  // tail offsets 2 .. 25 held in registers during the extension
 template <bool STAGED>
 __device__ __forceinline__ void extend_hits(const int* ctxs, const uint16_t* hpos, uint8_t* hmb,
                                             int nhit, const int* tail, int D, int* whist,
                                             const int32_t* row, const int32_t* smp, int n,
                                             int lane) {
   const int t1 = D >= 2 ? tail[1] : -1;
+  const bool short_d = D <= 2 + kTailRegs;
+  int tq[kTailRegs];
+#pragma unroll
+  for (int x = 0; x < kTailRegs; ++x) tq[x] = (short_d && 2 + x < D) ? tail[2 + x] : -1;
   for (int e0 = 0; e0 < nhit; e0 += 64) {
     const int e = e0 + lane;
     const bool ok = e < nhit;
@@ -657,7 +662,27 @@ __device__ __forceinline__ void extend_hits(const int* ctxs, const uint16_t* hpo
     int m = 1;
     if (ok && lim >= 2) {
       const int c1 = STAGED ? ctxs[j - 1] : ctx_at(row, smp, n, j - 1);
-      if (c1 == t1) {
+      if (c1 == t1 && short_d) {
+        // offsets 2 .. 25 in six rounds of four, compared with tail values held in registers
+        m = 2;
+        bool go = true;
+#pragma unroll
+        for (int r = 0; r < kTailRegs / 4; ++r) {
+          if (go && 2 + 4 * r < lim) {
+            int c[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int o = 2 + 4 * r + q;
+              c[q] = STAGED ? ctxs[o < lim ? j - o : 0] : ctx_at(row, smp, n, o < lim ? j - o : 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              go = go && 2 + 4 * r + q < lim && c[q] == tq[4 * r + q];
+              m += go ? 1 : 0;
+            }
+          }
+        }
+      } else if (c1 == t1) {
         m = 2;
         for (int o0 = 2; o0 < lim; o0 += 4) {
           int c[4];
