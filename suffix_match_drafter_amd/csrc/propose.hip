@@ -310,19 +310,28 @@ __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[
   long long snum = 0;
   bool done = false;
   int tokv = -1;  // lane i collects the i-th voted token
+  bool site0 = true;  // site 0 (lane 0, first half) is still on the voted path
 #pragma unroll
   for (int d = 0; d < KMAX; ++d) {
     if (!done && d < cap) {
       const int tk0 = al0 ? w0[d] : -1, tk1 = al1 ? w1[d] : -1;
       const uint64_t v0 = __ballot(tk0 >= 0), v1 = __ballot(tk1 >= 0);
+      // site 0's token at this depth does not depend on the votes so far
+      const int s0tok = __builtin_amdgcn_readfirstlane(w0[d]);
       int c = 0, w = -1;
       if ((v0 | v1) == 0) {
         done = true;
       } else {
-        // the first alive site is the reference; when every alive site agrees with it the
-        // token wins with all their votes
-        const int fl = v0 ? __builtin_ctzll(v0) : __builtin_ctzll(v1);
-        const int first = v0 ? __builtin_amdgcn_readlane(tk0, fl) : __builtin_amdgcn_readlane(tk1, fl);
+        // the reference is an alive site's token: site 0's while it stays on the voted path,
+        // else the first alive site's; when every alive site agrees with it the token wins
+        // with all their votes
+        int first;
+        if (site0 && s0tok >= 0) {
+          first = s0tok;
+        } else {
+          const int fl = v0 ? __builtin_ctzll(v0) : __builtin_ctzll(v1);
+          first = v0 ? __builtin_amdgcn_readlane(tk0, fl) : __builtin_amdgcn_readlane(tk1, fl);
+        }
         const uint64_t f0 = __ballot(tk0 == first), f1 = __ballot(tk1 == first);
         const int nalive = __popcll(v0) + __popcll(v1);
         const int cf = __popcll(f0) + __popcll(f1);
@@ -386,6 +395,7 @@ __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[
           tokv = lane == nout ? w : tokv;
           ++nout;
           snum += c;
+          site0 = site0 && s0tok == w;
           al0 = tk0 == w;
           al1 = tk1 == w;
         }
