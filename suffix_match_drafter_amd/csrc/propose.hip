@@ -1,20 +1,23 @@
 // propose.hip -- the drafter step on gfx950: one workgroup (16 wavefronts) per request.
 //
 // Steps, in the order of the suffix-gpu page, How it works:
-//   1. local match (step 1): the request's context is staged in LDS with every 16-byte load in
-//      flight at once; each wavefront owns a contiguous chunk of end positions (lanes on
-//      consecutive positions, so LDS reads are conflict-free) and computes the backward match
-//      length against the tail of every position, into a per-wavefront length histogram.  The
-//      histograms give the ladder (t-th largest length) and, per wavefront, the exact offsets
-//      of its earliest continuation sites, so one ordered pass writes the sites of every level;
+//   1. local match (step 1): each worker wavefront owns a contiguous chunk of end positions; it
+//      streams the chunk with coalesced bounds-checked loads (staging it in LDS when the row
+//      fits there) and keeps one ballot word per 64 positions marking the positions whose
+//      token is the last context token.  The marked positions are listed in order and their
+//      backward match lengths against the tail computed, into a per-wavefront histogram.  The
+//      histograms give the ladder (t-th largest length) and, per wavefront, the offsets of its
+//      earliest continuation sites, so one ordered pass writes the sites of every level;
 //   2. global match (step 2; vLLM docs, Model Runner V2: probe by the last 2 and last 4 tokens,
 //      extend to the longest match): 2-, 3- and 4-gram probes into hash tables over the
 //      suffix-array groups of the live snapshot and backward extension of the 4-gram
 //      occurrences.  Without a delta, a dedicated wavefront does all of it -- probes, ladder and
-//      sites -- while the other fifteen stage the context.  With a delta (documents appended
-//      since the snapshot) the whole workgroup scans the delta by brute force and merges;
+//      sites -- while the other fifteen work through the local match, which synchronise among
+//      themselves only.  With a delta (documents appended since the snapshot) the whole
+//      workgroup scans the delta by brute force and merges;
 //   3. expansion (step 3): one wavefront per candidate votes depth by depth over its sites
-//      (ballots when few sites are alive, an LDS hash otherwise); stop rule and score use
+//      (one ballot pair when every alive site agrees or one token holds a majority, ballots
+//      per token when few sites are alive, an LDS hash otherwise); stop rule and score use
 //      integer cross-multiplication; selection and the [k] output row follow.
 #include <type_traits>
 
@@ -171,7 +174,6 @@ struct Smem {
   const int32_t* plp[kNG];
   int wsum[NW + 1];
   int wbar;  // arrivals at the worker-only barriers
-  int sel[2];
 };
 
 // Shape of one request and the corpus state it sees.  Every thread derives it from the same
