@@ -291,13 +291,18 @@ __device__ __forceinline__ int extend4(const int32_t* text, const int* tail, int
   return m;
 }
 
-// Corpus token at logical position q: snapshot text below snap_end, ring slot above.
+// Corpus token at logical position q: snapshot text below snap_end, else ring slot `slot`
+// (q mod ring capacity, which the caller steps along instead of dividing each time).
 __device__ __forceinline__ int corpus_at(const ProposeArgs& a, const int32_t* text,
-                                         long long snap_start, long long snap_n, long long q) {
+                                         long long snap_start, long long snap_n, long long q,
+                                         int slot) {
   long long s = q - snap_start;
   if (s >= 0 && s < snap_n) return text[s];
-  return a.ring[q % a.ring_cap];
+  return a.ring[slot];
 }
+
+__device__ __forceinline__ int ring_next(int r, int cap) { return r + 1 == cap ? 0 : r + 1; }
+__device__ __forceinline__ int ring_prev(int r, int cap) { return r == 0 ? cap - 1 : r - 1; }
 
 // Depth-wise vote of one candidate held by one wavefront: lane l owns sites l and l+64, whose
 // continuation windows are w0 / w1 (-1 past the end of a continuation).  Writes the tokens to
@@ -925,18 +930,25 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     // delta: documents appended since the live snapshot, scanned by brute force
     const long long dlo = r.delta_lo, dhi = r.delta_hi;
     if (dhi - dlo > 1) {
+      // ring slots are stepped, not divided: one division per thread
       const int tt0 = sm.tail[0];
+      const int cap = (int)a.ring_cap;
+      const int stride = (int)(NT % a.ring_cap);
+      int re = (int)((dlo + tid) % a.ring_cap);
       for (long long e = dlo + tid; e + 1 < dhi; e += NT) {
-        const int c = a.ring[e % a.ring_cap];
-        if (c != tt0) continue;
-        if (a.ring[(e + 1) % a.ring_cap] < 0) continue;
-        int m = 1;
-        while (m < Lcap && e - m >= dlo) {
-          const int x = a.ring[(e - m) % a.ring_cap];
-          if (x < 0 || x != sm.tail[m]) break;
-          ++m;
+        const int c = a.ring[re];
+        if (c == tt0 && a.ring[ring_next(re, cap)] >= 0) {
+          int m = 1, rb = re;
+          while (m < Lcap && e - m >= dlo) {
+            rb = ring_prev(rb, cap);
+            const int x = a.ring[rb];
+            if (x < 0 || x != sm.tail[m]) break;
+            ++m;
+          }
+          if (m >= 2) atomicAdd(&sm.dhist[m], 1);
         }
-        if (m >= 2) atomicAdd(&sm.dhist[m], 1);
+        re += stride;
+        if (re >= cap) re -= cap;
       }
     }
     __syncthreads();
@@ -1006,29 +1018,34 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
         const long long seg = (span + NT - 1) / NT;
         const long long lo = dlo + (long long)tid * seg < dhi ? dlo + (long long)tid * seg : dhi;
         const long long hi = lo + seg < dhi ? lo + seg : dhi;
-        int c = 0;
-        for (long long e = lo; e < hi; ++e) {
+        const int cap = (int)a.ring_cap;
+        const int rlo = (int)(lo % a.ring_cap);
+        int c = 0, re = rlo;
+        for (long long e = lo; e < hi; ++e, re = ring_next(re, cap)) {
           if (e + 1 >= dhi) break;
-          if (a.ring[(e + 1) % a.ring_cap] < 0) continue;
-          int m = 0;
+          if (a.ring[ring_next(re, cap)] < 0) continue;
+          int m = 0, rb = re;
           while (m < l && e - m >= dlo) {
-            const int x = a.ring[(e - m) % a.ring_cap];
+            const int x = a.ring[rb];
             if (x < 0 || x != sm.tail[m]) break;
             ++m;
+            rb = ring_prev(rb, cap);
           }
           c += m >= l;
         }
         int total;
         int rk = block_exclusive_scan(c, sm.wsum, &total) + nsnap;
         if (c && rk < M) {
-          for (long long e = lo; e < hi && rk < M; ++e) {
+          re = rlo;
+          for (long long e = lo; e < hi && rk < M; ++e, re = ring_next(re, cap)) {
             if (e + 1 >= dhi) break;
-            if (a.ring[(e + 1) % a.ring_cap] < 0) continue;
-            int m = 0;
+            if (a.ring[ring_next(re, cap)] < 0) continue;
+            int m = 0, rb = re;
             while (m < l && e - m >= dlo) {
-              const int x = a.ring[(e - m) % a.ring_cap];
+              const int x = a.ring[rb];
               if (x < 0 || x != sm.tail[m]) break;
               ++m;
+              rb = ring_prev(rb, cap);
             }
             if (m >= l) gs[rk++] = e + 1;
           }
@@ -1070,11 +1087,15 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       const long long ss = r.snap_start, sn = r.snap_n;
       const long long q0 = s0 < c0 ? gs[s0] : 0, q1 = s1 < c0 ? gs[s1] : 0;
       bool live0 = s0 < c0, live1 = s1 < c0;
+      const int rcap = (int)a.ring_cap;
+      int r0 = (int)(q0 % a.ring_cap), r1 = (int)(q1 % a.ring_cap);
 #pragma unroll
       for (int d = 0; d < KMAX; ++d) {
         int x0 = -1, x1 = -1;
-        if (live0 && d < cap) x0 = corpus_at(a, text, ss, sn, q0 + d);
-        if (live1 && d < cap) x1 = corpus_at(a, text, ss, sn, q1 + d);
+        if (live0 && d < cap) x0 = corpus_at(a, text, ss, sn, q0 + d, r0);
+        if (live1 && d < cap) x1 = corpus_at(a, text, ss, sn, q1 + d, r1);
+        r0 = ring_next(r0, rcap);
+        r1 = ring_next(r1, rcap);
         live0 = live0 && x0 >= 0;
         live1 = live1 && x1 >= 0;
         w0[d] = x0;
