@@ -304,6 +304,88 @@ __device__ __forceinline__ int corpus_at(const ProposeArgs& a, const int32_t* te
 __device__ __forceinline__ int ring_next(int r, int cap) { return r + 1 == cap ? 0 : r + 1; }
 __device__ __forceinline__ int ring_prev(int r, int cap) { return r == 0 ? cap - 1 : r - 1; }
 
+constexpr int kDeltaLoads = 8;  // 64-position chunks per round of the delta scan
+
+template <int U>
+__device__ __forceinline__ uint64_t pick_mask(const uint64_t (&h)[U], int u) {
+  uint64_t x = h[0];
+#pragma unroll
+  for (int i = 1; i < U; ++i) x = u == i ? h[i] : x;
+  return x;
+}
+
+// One wavefront scans the delta end positions [x0, x1), x1 < delta end (so every position has a
+// next token inside the delta), in position order.  Lanes read consecutive ring slots.  A
+// position is an occurrence of the tail's last two tokens when its own token is tail[0] and the
+// one before it (not before dlo) is tail[1]: two compares per chunk, whose ballots are combined
+// with a one-bit shift, select them.  Only those lanes extend backwards, and an occurrence
+// followed by a separator is dropped.  For every chunk that holds a candidate, f(x, m) gets each
+// lane's position and match length (0 where none); f returns false to stop the scan.
+template <typename F>
+__device__ __forceinline__ void delta_scan_wave(const ProposeArgs& a, long long dlo, long long x0,
+                                                long long x1, int Lcap, const int* tail,
+                                                int lane, F&& f) {
+  const int t0 = tail[0], t1 = tail[1];
+  if (t1 < 0 || x0 >= x1) return;  // a negative tail token matches no corpus token
+  const int cap = (int)a.ring_cap;
+  long long x = x0;
+  int r = (int)(x0 % a.ring_cap);
+  while (x < x1) {
+    // a run of ring slots without wrap-around: positions x .. x+len-1 in slots r .. r+len-1
+    const long long room = (long long)(cap - r);
+    const int len = (int)(x1 - x < room ? x1 - x : room);
+    uint64_t carry = 0;  // position x - 1 holds tail[1]
+    if (x - 1 >= dlo) carry = a.ring[ring_prev(r, cap)] == t1 ? 1ull : 0ull;
+    const int32_t* p = a.ring + r;
+    for (int o = 0; o < len; o += 64 * kDeltaLoads) {
+      int v[kDeltaLoads];
+      if (o + 64 * kDeltaLoads <= len) {
+#pragma unroll
+        for (int u = 0; u < kDeltaLoads; ++u) v[u] = p[o + 64 * u + lane];
+      } else {
+#pragma unroll
+        for (int u = 0; u < kDeltaLoads; ++u) {
+          const int i = o + 64 * u + lane;
+          v[u] = i < len ? p[i] : -1;
+        }
+      }
+      uint64_t hit[kDeltaLoads];
+      uint64_t any = 0;
+#pragma unroll
+      for (int u = 0; u < kDeltaLoads; ++u) {
+        const uint64_t b0 = __ballot(v[u] == t0), b1 = __ballot(v[u] == t1);
+        hit[u] = b0 & ((b1 << 1) | carry);
+        carry = b1 >> 63;
+        any |= hit[u];
+      }
+      if (!any) continue;
+      for (int u = 0; u < kDeltaLoads; ++u) {
+        const uint64_t hm = pick_mask(hit, u);
+        if (!hm) continue;
+        const int i = o + 64 * u + lane;  // this lane's offset in the run
+        const long long xp = x + i;
+        int m = 0;
+        if ((hm >> lane) & 1) {
+          const int s = r + i;
+          if (a.ring[ring_next(s, cap)] >= 0) {
+            m = 2;
+            int rb = ring_prev(s, cap);
+            while (m < Lcap && xp - m >= dlo) {
+              rb = ring_prev(rb, cap);
+              const int c = a.ring[rb];
+              if (c < 0 || c != tail[m]) break;
+              ++m;
+            }
+          }
+        }
+        if (!f(xp, m)) return;
+      }
+    }
+    x += len;
+    r = 0;  // a run ends at x1 or at the last slot
+  }
+}
+
 // Depth-wise vote of one candidate held by one wavefront: lane l owns sites l and l+64, whose
 // continuation windows are w0 / w1 (-1 past the end of a continuation).  Writes the tokens to
 // out[] and returns the count and the sum of per-depth counts.  cmin is the smallest
@@ -429,7 +511,7 @@ __device__ __forceinline__ void corpus_wave_probe(const ProposeArgs& a, const Re
                                                   int lane) {
   const int n = r.n, L = r.L, Lcap = r.Lcap, M = a.M;
   if (lane < Lcap) sm.gtail[lane] = ctx_at(row, smp, n, L - 1 - lane);
-  if (lane <= kMaxD) sm.ghist[lane] = 0;
+  for (int i = lane; i <= kMaxD; i += 64) sm.ghist[i] = 0;
   wave_sync();
   const View ib = view_of(a, r.act, r.ht_mask);
   const long long dead_below = r.tail_w - r.snap_start;
@@ -459,23 +541,25 @@ __device__ __forceinline__ void corpus_wave_probe(const ProposeArgs& a, const Re
 }
 
 // Second part, run while the other wavefronts compute the match lengths of the context: the
-// corpus ladder (lane l holds the support of length l) and the earliest sites of each level.
+// corpus ladder (lane l - 1 holds the support of length l) and the earliest sites of each level.
 __device__ __forceinline__ void corpus_wave_sites(const ProposeArgs& a, const Req& r, Smem& sm,
                                                   int lane) {
   const int Lcap = r.Lcap, nb = a.nb, M = a.M;
   const long long snap_start = r.snap_start;
   wave_sync();
-  // support of length l: the live (l)-gram group for l <= 4, else extensions reaching l
-  const int gh = (lane >= 5 && lane <= Lcap) ? sm.ghist[lane] : 0;
+  // support of length v = lane + 1 (lengths up to 64 on 64 lanes): the live v-gram group for
+  // v <= 4, else the extensions reaching v
+  const int v = lane + 1;
+  const int gh = (v >= 5 && v <= Lcap) ? sm.ghist[v] : 0;
   const int gin = wave_incl_add(gh);
   const int gsuf = __builtin_amdgcn_readlane(gin, 63) - gin + gh;
-  const int sup_l = lane >= 2 && lane <= 4 ? sm.g_live[lane - 2] : gsuf;
+  const int sup_l = v >= 2 && v <= 4 ? sm.g_live[v - 2] : gsuf;
   const int minc = a.min_corpus > 2 ? a.min_corpus : 2;
   int prev_l = -1, prev_src = -1;
   for (int ti = 0; ti < nb; ++ti) {
-    const uint64_t ok = __ballot(lane >= 2 && lane <= Lcap && sup_l >= ti + 1);
-    const int l = ok ? 63 - __builtin_clzll(ok) : 0;
-    const int sup = l ? __builtin_amdgcn_readlane(sup_l, l) : 0;
+    const uint64_t ok = __ballot(v >= 2 && v <= Lcap && sup_l >= ti + 1);
+    const int l = ok ? 64 - __builtin_clzll(ok) : 0;
+    const int sup = l ? __builtin_amdgcn_readlane(sup_l, l - 1) : 0;
     const int ci = nb + ti;
     const int src = (ti > 0 && l == prev_l) ? prev_src : ci;
     prev_l = l;
@@ -825,20 +909,21 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     extend_hits<STAGED>(ctxs, hpos, hmb, nhit, sm.tail, D, sm.whist[wid], row, smp, n, lane);
     wave_sync();
     {
-      // this wavefront's suffix sums: wsuf[w][v] = its positions with length >= v
-      const int h = lane <= D ? sm.whist[wid][lane] : 0;
+      // this wavefront's suffix sums: wsuf[w][v] = its positions with length >= v, for
+      // v = lane + 1 (lengths 1 .. 64 on 64 lanes)
+      const int h = lane + 1 <= D ? sm.whist[wid][lane + 1] : 0;
       const int incl = wave_incl_add(h);
-      sm.wsuf[wid][lane] = __builtin_amdgcn_readlane(incl, 63) - incl + h;
+      sm.wsuf[wid][lane + 1] = __builtin_amdgcn_readlane(incl, 63) - incl + h;
     }
     if (fast) worker_barrier(&sm.wbar, 2 * NWW, lane);
     else __syncthreads();
 
     // ladder and this wavefront's site offsets: every worker wavefront derives them from the
-    // per-wavefront suffix sums (lane v of cg = positions with length >= v); wavefront 0 also
+    // per-wavefront suffix sums (lane v - 1 of cg = positions with length >= v); wavefront 0 also
     // records the candidates.  Then the earliest sites of every distinct local level, in one
     // ordered pass over the hit list.
     int cg = 0;
-    for (int w = 0; w < NWW; ++w) cg += sm.wsuf[w][lane];
+    for (int w = 0; w < NWW; ++w) cg += sm.wsuf[w][lane + 1];
     const int maxl = D < J ? D : J;
     const int mins = a.min_self > 1 ? a.min_self : 1;
     int lv[kMaxNB], pre[kMaxNB], run[kMaxNB];
@@ -852,9 +937,9 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       pre[ti] = 0;
       run[ti] = 0;
       if (ti < nb) {
-        const uint64_t ok = __ballot(lane >= 1 && lane <= maxl && cg >= ti + 1);
-        const int l = ok ? 63 - __builtin_clzll(ok) : 0;
-        const int sup = l ? __builtin_amdgcn_readlane(cg, l) : 0;
+        const uint64_t ok = __ballot(lane + 1 <= maxl && cg >= ti + 1);
+        const int l = ok ? 64 - __builtin_clzll(ok) : 0;
+        const int sup = l ? __builtin_amdgcn_readlane(cg, l - 1) : 0;
         const int src = (ti > 0 && l == prev_l) ? prev_src : ti;
         prev_l = l;
         prev_src = src;
@@ -900,6 +985,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       sm.ghist[tid] = 0;
       sm.dhist[tid] = 0;
     }
+    for (int i = tid; i < NW * (kMaxD + 1); i += NT) (&sm.whist[0][0])[i] = 0;
     __syncthreads();
     const int act = r.act;
     const long long snap_start = r.snap_start;
@@ -927,35 +1013,48 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
         if (m >= 5) atomicAdd(&sm.ghist[m], 1);
       }
     }
-    // delta: documents appended since the live snapshot, scanned by brute force
+    // delta: documents appended since the live snapshot, scanned by brute force.  Wavefront w
+    // owns the end positions [sb, se) and keeps its occurrences of length >= 2 in LDS, in
+    // position order (offset from sb << 6 | length - 2; the context hit lists are dead by now),
+    // at most H of them, plus a length histogram.
     const long long dlo = r.delta_lo, dhi = r.delta_hi;
-    if (dhi - dlo > 1) {
-      // ring slots are stepped, not divided: one division per thread
-      const int tt0 = sm.tail[0];
-      const int cap = (int)a.ring_cap;
-      const int stride = (int)(NT % a.ring_cap);
-      int re = (int)((dlo + tid) % a.ring_cap);
-      for (long long e = dlo + tid; e + 1 < dhi; e += NT) {
-        const int c = a.ring[re];
-        if (c == tt0 && a.ring[ring_next(re, cap)] >= 0) {
-          int m = 1, rb = re;
-          while (m < Lcap && e - m >= dlo) {
-            rb = ring_prev(rb, cap);
-            const int x = a.ring[rb];
-            if (x < 0 || x != sm.tail[m]) break;
-            ++m;
-          }
-          if (m >= 2) atomicAdd(&sm.dhist[m], 1);
+    const bool has_delta = dhi - dlo > 1;
+    const long long dseg = has_delta ? ((dhi - 1 - dlo + NW - 1) / NW + 63) / 64 * 64 : 0;
+    const long long sb = dlo + (long long)wid * dseg;
+    const long long se = has_delta ? (sb + dseg < dhi - 1 ? sb + dseg : dhi - 1) : sb;
+    const int H = (int)((dyn_bytes(STAGED, a.S, a.T) - hpos_offset(STAGED, a.S, a.T)) / (4 * NW));
+    uint32_t* recs = reinterpret_cast<uint32_t*>(dyn + hpos_offset(STAGED, a.S, a.T)) + wid * H;
+    int nrec = 0;
+    if (has_delta) {
+      int* wh = sm.whist[wid];
+      delta_scan_wave(a, dlo, sb, se, Lcap, sm.tail, lane, [&](long long x, int m) {
+        const bool q = m >= 2;
+        const uint64_t bal = __ballot(q);
+        if (bal) {
+          const int rk = nrec + lanes_before(bal);
+          if (q && rk < H) recs[rk] = ((uint32_t)(x - sb) << 6) | (uint32_t)(m - 2);
+          if (q) atomicAdd(&wh[m], 1);
+          nrec += __popcll(bal);
         }
-        re += stride;
-        if (re >= cap) re -= cap;
-      }
+        return true;
+      });
+      wave_sync();
+      // this wavefront's suffix sums: wsuf[w][v] = its occurrences of length >= v, v = lane + 1
+      const int h = lane + 1 <= Lcap ? wh[lane + 1] : 0;
+      const int incl = wave_incl_add(h);
+      sm.wsuf[wid][lane + 1] = __builtin_amdgcn_readlane(incl, 63) - incl + h;
     }
     __syncthreads();
+    if (has_delta && wid == 0) {
+      int sum = 0;
+      for (int w = 0; w < NW; ++w) sum += sm.wsuf[w][lane + 1];
+      sm.dhist[lane + 1] = sum;  // delta occurrences of length >= lane + 1
+      wave_sync();
+    }
     if (tid == 0) {
-      int dcum = 0, gcum = 0, ti = 0;
+      int gcum = 0, ti = 0;
       for (int l = Lcap; l >= 2 && ti < nb; --l) {
-        dcum += sm.dhist[l];
+        const int dcum = sm.dhist[l];
         gcum += sm.ghist[l];
         int snap = l <= 4 ? sm.g_live[l - 2] : gcum;
         if (act < 0) snap = 0;
@@ -1012,43 +1111,33 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
           nsnap = total < M ? total : M;
         }
       }
-      // delta occurrences follow every snapshot occurrence in logical order
-      if (nsnap < M && dhi - dlo > 1) {
-        const long long span = dhi - dlo;
-        const long long seg = (span + NT - 1) / NT;
-        const long long lo = dlo + (long long)tid * seg < dhi ? dlo + (long long)tid * seg : dhi;
-        const long long hi = lo + seg < dhi ? lo + seg : dhi;
-        const int cap = (int)a.ring_cap;
-        const int rlo = (int)(lo % a.ring_cap);
-        int c = 0, re = rlo;
-        for (long long e = lo; e < hi; ++e, re = ring_next(re, cap)) {
-          if (e + 1 >= dhi) break;
-          if (a.ring[ring_next(re, cap)] < 0) continue;
-          int m = 0, rb = re;
-          while (m < l && e - m >= dlo) {
-            const int x = a.ring[rb];
-            if (x < 0 || x != sm.tail[m]) break;
-            ++m;
-            rb = ring_prev(rb, cap);
-          }
-          c += m >= l;
+      // delta occurrences follow every snapshot occurrence in logical order, and this
+      // wavefront's follow those of the wavefronts before it: from its records, then, if it
+      // found more than it kept, from a rescan past the last one kept
+      if (nsnap < M && has_delta) {
+        const int c = lane < NW ? sm.wsuf[lane][l] : 0;
+        const int incl = wave_incl_add(c);
+        int off = nsnap + __builtin_amdgcn_readlane(incl - c, wid);
+        const int kept = nrec < H ? nrec : H;
+        for (int base = 0; base < kept && off < M; base += 64) {
+          const int e = base + lane;
+          const uint32_t rc = e < kept ? recs[e] : 0u;
+          const bool q = e < kept && (int)(rc & 63u) + 2 >= l;
+          const uint64_t bal = __ballot(q);
+          const int rk = off + lanes_before(bal);
+          if (q && rk < M) gs[rk] = sb + (long long)(rc >> 6) + 1;
+          off += __popcll(bal);
         }
-        int total;
-        int rk = block_exclusive_scan(c, sm.wsum, &total) + nsnap;
-        if (c && rk < M) {
-          re = rlo;
-          for (long long e = lo; e < hi && rk < M; ++e, re = ring_next(re, cap)) {
-            if (e + 1 >= dhi) break;
-            if (a.ring[ring_next(re, cap)] < 0) continue;
-            int m = 0, rb = re;
-            while (m < l && e - m >= dlo) {
-              const int x = a.ring[rb];
-              if (x < 0 || x != sm.tail[m]) break;
-              ++m;
-              rb = ring_prev(rb, cap);
-            }
-            if (m >= l) gs[rk++] = e + 1;
-          }
+        if (nrec > H && off < M) {
+          const long long from = sb + (long long)(recs[H - 1] >> 6) + 1;
+          delta_scan_wave(a, dlo, from, se, Lcap, sm.tail, lane, [&](long long x, int m) {
+            const bool q = m >= l;
+            const uint64_t bal = __ballot(q);
+            const int rk = off + lanes_before(bal);
+            if (q && rk < M) gs[rk] = x + 1;
+            off += __popcll(bal);
+            return off < M;
+          });
         }
       }
       __syncthreads();

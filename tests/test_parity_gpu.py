@@ -139,6 +139,109 @@ def test_degenerate_rows(S, flags):
     assert_same(run_gpu(S, kn, n, tok, samp[:, :0], flags=flags)[:2], e0, "T=0")
 
 
+@pytest.mark.parametrize("flags", FLAGS)
+def test_full_depth_match(S, flags):
+    """max_tree_depth at its limit (64): an early copy of the last 63 context tokens (preceded by
+    another token) continues with Y, a later copy of all 64 continues with X.  The longest match
+    is the 64-token one, so the draft starts with X; a ladder that stops at 63 would take the
+    earlier site and draft Y.  Locally, in the corpus snapshot, split between snapshot and delta,
+    and in the delta alone."""
+    import torch
+
+    rng = np.random.default_rng(64)
+    V, n = 5000, 400
+    row = rng.integers(0, V, size=n).astype(np.int32)
+    samp = np.array([[int(rng.integers(0, V))]], np.int32)
+    tail = np.concatenate([row, samp[0]])[-64:]
+    X, Y = 4242, 4243
+    other = (int(tail[0]) + 1) % V
+    loc = row.copy()
+    loc[19] = other
+    loc[20:83] = tail[1:]
+    loc[83] = Y
+    loc[150:214] = tail
+    loc[214] = X
+    doc_a = np.concatenate([rng.integers(0, V, 30), [other], tail[1:], [Y],
+                            rng.integers(0, V, 20)]).astype(np.int32)
+    doc_b = np.concatenate([rng.integers(0, V, 30), tail, [X],
+                            rng.integers(0, V, 20)]).astype(np.int32)
+    text = W.join_docs([doc_a, doc_b])
+    nn = np.array([n], np.int32)
+    for mode, nb in ((0, 1), (1, 4)):
+        kn = dict(k=8, max_tree_depth=64, num_backoff=nb, max_occurrences=128, mode=mode,
+                  spec_factor_ppm=10**7, min_token_prob_ppm=0)
+        p = O.params_from(kn)
+        exp = O.propose(p, nn, loc[None], samp)
+        assert exp[0][0, 0] == X
+        assert_same(run_gpu(S, kn, nn, loc[None], samp, flags=flags)[:2], exp,
+                    f"local mode {mode}")
+        exp = O.propose(p, nn, row[None], samp, corpus=text)
+        assert exp[0][0, 0] == X
+        got = run_gpu(S, kn, nn, row[None], samp, corpus_docs=[doc_a, doc_b],
+                      capacity=1 << 12, flags=flags)
+        assert_same(got[:2], exp, f"corpus snapshot mode {mode}")
+        got[2].close()
+        cfg = S.Config(max_batch=1, max_seq=n, max_sampled=1, corpus_capacity=1 << 12,
+                       flags=flags, **kn)
+        for split in (True, False):
+            d = S.Drafter(cfg)
+            if split:
+                d.ingest_docs([doc_a])
+                d.rebuild()
+                d.ingest_docs([doc_b])
+            else:
+                d.ingest_docs([doc_a, doc_b])
+            dd, dn = d.propose(dev(nn), dev(row[None]), dev(samp))
+            torch.cuda.synchronize()
+            assert_same((dd.cpu().numpy(), dn.cpu().numpy()), exp,
+                        f"corpus delta split={split} mode {mode}")
+            d.close()
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+@pytest.mark.parametrize("wrap", [False, True])
+def test_delta_many_short_matches(S, flags, wrap):
+    """A delta with 20000 occurrences of exactly the last two context tokens, then three of the
+    last 24: far more short occurrences than any wavefront of the scan keeps, so the long
+    candidate's sites lie past every kept record and must be found again.  With wrap the delta
+    runs across the end of the ring and the oldest documents are evicted."""
+    import torch
+
+    rng = np.random.default_rng(77)
+    V, n = 1000, 200
+    row = rng.integers(0, V, size=(2, n)).astype(np.int32)
+    samp = rng.integers(0, V, size=(2, 1)).astype(np.int32)
+    ctx = np.concatenate([row[0], samp[0]])
+    tail = ctx[::-1][:24]
+    z = next(v for v in range(V) if v not in (tail[0], tail[1], tail[2]))
+    short = np.tile(np.array([tail[1], tail[0], z], np.int32), 20000)
+    longs = [np.concatenate([rng.integers(0, V, 50), ctx[-24:], [1000 + i],
+                             rng.integers(0, V, 50)]).astype(np.int32) for i in range(3)]
+    seed = [rng.integers(0, V, 3000).astype(np.int32) for _ in range(10)]
+    cap = 1 << 16 if wrap else 1 << 18
+    nn = np.full(2, n, np.int32)
+    for mode, nb in ((0, 1), (1, 4)):
+        kn = dict(k=8, max_tree_depth=24, num_backoff=nb, max_occurrences=128, mode=mode,
+                  spec_factor_ppm=2_000_000, min_token_prob_ppm=100_000)
+        cfg = S.Config(max_batch=2, max_seq=n, max_sampled=1, corpus_capacity=cap,
+                       flags=flags, **kn)
+        d = S.Drafter(cfg)
+        lc = O.LiveCorpus(cap)
+        d.ingest_docs(seed)
+        lc.ingest(seed)
+        d.rebuild()
+        d.ingest_docs([short] + longs)
+        lc.ingest([short] + longs)
+        assert (lc.evicted() > 0) == wrap
+        exp = O.propose(O.params_from(kn), nn, row, samp, corpus=lc.text())
+        if mode == 0:  # the longest match wins; SCORED prefers the unanimous short one
+            assert exp[0][0, 0] in (1000, 1001, 1002)
+        dd, dn = d.propose(dev(nn), dev(row), dev(samp))
+        torch.cuda.synchronize()
+        assert_same((dd.cpu().numpy(), dn.cpu().numpy()), exp, f"mode {mode}")
+        d.close()
+
+
 def test_long_repeated_rows(S):
     """Rows of one repeated token at full length (every end position is a hit), a long row that
     starts with a repeated run, and rows of period 2, in both context paths and at the largest
