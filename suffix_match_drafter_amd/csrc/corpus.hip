@@ -103,6 +103,17 @@ __global__ __launch_bounds__(PT) void ingest_plan_kernel(IngestArgs a) {
     if (dh + r >= ndt) a.doc_start[(dh + r) % a.dcap] = base + a.doc_off[r];
 }
 
+// Ring slots of a grid-stride walk: one division per thread, then steps of stride % cap.
+struct SlotWalk {
+  int64_t slot, step, cap;
+  __device__ SlotWalk(int64_t pos, int64_t stride, int64_t m)
+      : slot(pos % m), step(stride % m), cap(m) {}
+  __device__ void next() {
+    slot += step;
+    if (slot >= cap) slot -= cap;
+  }
+};
+
 // Copy the surviving tokens of document blockIdx.x (and its -1 separator) into the ring.
 __global__ __launch_bounds__(256) void ingest_scatter_kernel(IngestArgs a) {
   const int r = blockIdx.x;
@@ -110,12 +121,11 @@ __global__ __launch_bounds__(256) void ingest_scatter_kernel(IngestArgs a) {
   const int32_t* src = doc_src(a, r);
   const int64_t start = a.ctl->ingest_base + a.doc_off[r];
   const int64_t live_from = a.ctl->tail;
-  for (int64_t x = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; x <= len;
-       x += (int64_t)gridDim.y * blockDim.x) {
-    const int64_t pos = start + x;
-    if (pos < live_from) continue;
-    a.ring[pos % a.cap] = x < len ? src[x] : -1;
-  }
+  const int64_t x0 = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.y * blockDim.x;
+  SlotWalk w(start + x0, stride, a.cap);
+  for (int64_t x = x0; x <= len; x += stride, w.next())
+    if (start + x >= live_from) a.ring[w.slot] = x < len ? src[x] : -1;
 }
 
 // Linear copy of the live corpus [tail, head) into a snapshot text; records its range.
@@ -123,9 +133,10 @@ __global__ void snapshot_kernel(Ctl* ctl, const int32_t* ring, int64_t cap, int3
                                 int buf, int64_t* range_out) {
   const int64_t tail = ctl->tail, head = ctl->head;
   const int64_t n = head - tail;
-  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n;
-       x += (int64_t)gridDim.x * blockDim.x)
-    text[x] = ring[(tail + x) % cap];
+  const int64_t x0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  SlotWalk w(tail + x0, stride, cap);
+  for (int64_t x = x0; x < n; x += stride, w.next()) text[x] = ring[w.slot];
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     ctl->pending_start = tail;
     ctl->pending_end = head;
@@ -166,9 +177,10 @@ __global__ void live_range_kernel(const Ctl* ctl, int64_t* out) {
 __global__ void ring_copy_kernel(const Ctl* ctl, const int32_t* ring, int64_t cap, int32_t* out,
                                  int64_t out_cap) {
   const int64_t tail = ctl->tail, n = ctl->head - tail;
-  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n && x < out_cap;
-       x += (int64_t)gridDim.x * blockDim.x)
-    out[x] = ring[(tail + x) % cap];
+  const int64_t x0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  SlotWalk w(tail + x0, stride, cap);
+  for (int64_t x = x0; x < n && x < out_cap; x += stride, w.next()) out[x] = ring[w.slot];
 }
 
 }  // namespace

@@ -17,18 +17,19 @@ struct ProposeArgs {
   const Ctl* ctl;  // nullptr when the context has no corpus
   IndexBuf idx[2];
   const int32_t* ring;
-  int64_t ring_cap;
+  int64_t ring_cap;    // ring slots: slot = position % ring_cap
   int32_t stream_ctx;  // read the context from HBM instead of staging it in LDS
 };
 
 constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one gfx950 workgroup
-// Dynamic LDS of one request: the staged context (when staged) and the hit lists.
-size_t propose_dynamic_lds(bool staged, int S, int T);
+// Dynamic LDS of one request: the staged context (when staged), the hit lists and, with a
+// corpus, the delta scan's occurrence records.
+size_t propose_dynamic_lds(bool staged, int S, int T, bool corpus);
 // Static LDS of the propose kernel (the per-request bookkeeping).
 size_t propose_static_lds();
 // Whether a call with row capacity S stages the context in LDS: it does unless asked not to or
 // the staged layout does not fit one workgroup's LDS.
-bool propose_staged(int S, int T, bool stream_ctx);
+bool propose_staged(int S, int T, bool stream_ctx, bool corpus);
 // Allows the largest dynamic LDS on every propose kernel instantiation.
 hipError_t propose_prepare();
 hipError_t launch_propose(const ProposeArgs& a, hipStream_t st);

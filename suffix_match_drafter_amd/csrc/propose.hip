@@ -626,9 +626,17 @@ __host__ __device__ inline size_t hmb_offset(bool staged, int S, int T) {
 __host__ __device__ inline size_t bits_offset(bool staged, int S, int T) {
   return (hmb_offset(staged, S, T) + hit_cap(S, T) + 15) & ~(size_t)15;
 }
-__host__ __device__ inline size_t dyn_bytes(bool staged, int S, int T) {
-  const size_t b = bits_offset(staged, S, T) + (size_t)8 * (hit_cap(S, T) / 64);
-  return b < (size_t)kVoteBytes ? (size_t)kVoteBytes : b;
+// With a corpus, the region from hpos_offset on also holds the delta scan's occurrence records
+// (after the local phase), at least kDeltaMinRecs per wavefront.
+constexpr int kDeltaMinRecs = 256;
+__host__ __device__ inline size_t dyn_bytes(bool staged, int S, int T, bool corpus) {
+  size_t b = bits_offset(staged, S, T) + (size_t)8 * (hit_cap(S, T) / 64);
+  if (b < (size_t)kVoteBytes) b = kVoteBytes;
+  if (corpus) {
+    const size_t need = hpos_offset(staged, S, T) + (size_t)4 * NW * kDeltaMinRecs;
+    if (b < need) b = need;
+  }
+  return b;
 }
 
 constexpr int kScreenLoads = 32;  // 64-position words per screening group (2048 positions)
@@ -1022,8 +1030,9 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     const long long dseg = has_delta ? ((dhi - 1 - dlo + NW - 1) / NW + 63) / 64 * 64 : 0;
     const long long sb = dlo + (long long)wid * dseg;
     const long long se = has_delta ? (sb + dseg < dhi - 1 ? sb + dseg : dhi - 1) : sb;
-    const int H = (int)((dyn_bytes(STAGED, a.S, a.T) - hpos_offset(STAGED, a.S, a.T)) / (4 * NW));
-    uint32_t* recs = reinterpret_cast<uint32_t*>(dyn + hpos_offset(STAGED, a.S, a.T)) + wid * H;
+    const size_t dbase = hpos_offset(STAGED, a.S, a.T);
+    const int H = (int)((dyn_bytes(STAGED, a.S, a.T, true) - dbase) / (4 * NW));
+    uint32_t* recs = reinterpret_cast<uint32_t*>(dyn + dbase) + wid * H;
     int nrec = 0;
     if (has_delta) {
       int* wh = sm.whist[wid];
@@ -1270,7 +1279,9 @@ hipError_t launch_k(const ProposeArgs& a, bool staged, size_t dyn, hipStream_t s
 
 }  // namespace
 
-size_t propose_dynamic_lds(bool staged, int S, int T) { return dyn_bytes(staged, S, T); }
+size_t propose_dynamic_lds(bool staged, int S, int T, bool corpus) {
+  return dyn_bytes(staged, S, T, corpus);
+}
 
 namespace {
 size_t g_static_lds = 0;  // largest static LDS over the propose instantiations (queried)
@@ -1278,8 +1289,8 @@ size_t g_static_lds = 0;  // largest static LDS over the propose instantiations 
 
 size_t propose_static_lds() { return g_static_lds ? g_static_lds : sizeof(Smem); }
 
-bool propose_staged(int S, int T, bool stream_ctx) {
-  return !stream_ctx && dyn_bytes(true, S, T) + propose_static_lds() <= kLdsBytes;
+bool propose_staged(int S, int T, bool stream_ctx, bool corpus) {
+  return !stream_ctx && dyn_bytes(true, S, T, corpus) + propose_static_lds() <= kLdsBytes;
 }
 
 hipError_t propose_prepare() {
@@ -1306,8 +1317,9 @@ hipError_t propose_prepare() {
 
 hipError_t launch_propose(const ProposeArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
-  const bool staged = propose_staged(a.S, a.T, a.stream_ctx != 0);
-  const size_t dyn = dyn_bytes(staged, a.S, a.T);
+  const bool corpus = a.ctl != nullptr;
+  const bool staged = propose_staged(a.S, a.T, a.stream_ctx != 0, corpus);
+  const size_t dyn = dyn_bytes(staged, a.S, a.T, corpus);
   if (dyn + propose_static_lds() > kLdsBytes) return hipErrorInvalidValue;
   if (a.k <= 8) return launch_k<8>(a, staged, dyn, st);
   if (a.k <= 16) return launch_k<16>(a, staged, dyn, st);

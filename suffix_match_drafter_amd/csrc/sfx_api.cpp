@@ -215,9 +215,10 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
     return hip_fail(e, "propose kernel attributes");
   }
   {
-    const bool staged =
-        propose_staged(cfg->max_seq, cfg->max_sampled, (cfg->flags & SFX_FLAG_STREAM_CONTEXT) != 0);
-    const size_t lds = propose_dynamic_lds(staged, cfg->max_seq, cfg->max_sampled);
+    const bool corpus = cfg->corpus_capacity > 0;
+    const bool staged = propose_staged(cfg->max_seq, cfg->max_sampled,
+                                       (cfg->flags & SFX_FLAG_STREAM_CONTEXT) != 0, corpus);
+    const size_t lds = propose_dynamic_lds(staged, cfg->max_seq, cfg->max_sampled, corpus);
     if (lds + propose_static_lds() > kLdsBytes) {
       delete c;
       return fail(SFX_EINVAL, "max_seq=%d with max_sampled=%d needs %zu bytes of LDS per request, "
