@@ -81,6 +81,81 @@ def copy_calibration(torch, dev, mib, reps):
     del src, dst
 
 
+def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
+    """The ingest-and-rebuild workload: a ring of 2^22 tokens seeded with the template corpus;
+    every step harvests 256 finished rows of U[512,2048] tokens; propose runs at B=512, S=32768,
+    k=32.  After warm_steps (ring full and evicting), per step: the harvest (HIP events on the
+    calling stream), propose with that step's documents still in the delta, propose while the
+    asynchronous rebuild of the whole ring runs on the side stream, the rebuild's wall time, and
+    propose once it is live (no delta).  Outside the headline timed region."""
+    w = W.WORKLOADS[5]
+    t0 = time.time()
+    n, tok, samp = W.make_batch(5)
+    dn, dt, ds = (torch.from_numpy(x).to(dev) for x in (n, tok, samp))
+    batches = []
+    for st in range(warm_steps + steps):
+        itok, rows, lens = W.ingest_batch(5, st)
+        batches.append((torch.from_numpy(rows).to(dev), torch.from_numpy(lens).to(dev),
+                        torch.from_numpy(itok).to(dev), int(lens.sum())))
+    log(f"[bench] ingest workload inputs in {time.time() - t0:.1f}s")
+    cfg = sfx.Config(max_batch=w.B, max_seq=w.S, max_sampled=w.T,
+                     corpus_capacity=w.ring_capacity, **w.knobs())
+    d = sfx.Drafter(cfg)
+    d.ingest_docs(W.corpus_docs(5))
+    d.rebuild()
+    stream = torch.cuda.current_stream()
+    draft = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+    nv = torch.empty((w.B,), dtype=torch.int32, device=dev)
+    for st in range(warm_steps):
+        rows, lens, itok, _ = batches[st]
+        d.harvest_finished(rows, lens, itok, stream)
+        d.rebuild(stream)
+    torch.cuda.synchronize()
+
+    def timed(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def prop():
+        d.propose(dn, dt, ds, draft, nv, stream)
+
+    ing_ms, ing_tok, p_delta, p_during, p_live, reb_ms, step_ms = [], 0, [], [], [], [], []
+    for st in range(warm_steps, warm_steps + steps):
+        rows, lens, itok, ntok = batches[st]
+        ts = time.time()
+        ing_ms.append(timed(lambda: d.harvest_finished(rows, lens, itok, stream), 1))
+        ing_tok += ntok
+        p_delta.append(timed(prop, calls))
+        tr = time.time()
+        d.rebuild_async(stream)
+        p_during.append(timed(prop, calls))
+        d.wait_rebuild(stream)
+        torch.cuda.synchronize()
+        reb_ms.append((time.time() - tr) * 1e3)
+        step_ms.append((time.time() - ts) * 1e3)
+        p_live.append(timed(prop, calls))
+    d.close()
+    out = {
+        "workload": f"ingest-B{w.B}-S{w.S}-ring{w.ring_capacity}",
+        "steps": steps, "warm_steps": warm_steps,
+        "harvest_ms": round(float(np.mean(ing_ms)), 3),
+        "harvest_tokens_per_s": round(ing_tok / (sum(ing_ms) * 1e-3), 1),
+        "propose_us_with_delta": round(float(np.mean(p_delta)) * 1e3, 1),
+        "propose_us_during_rebuild": round(float(np.mean(p_during)) * 1e3, 1),
+        "propose_us_no_delta": round(float(np.mean(p_live)) * 1e3, 1),
+        "rebuild_ms": round(float(np.mean(reb_ms)), 2),
+        "rebuild_tokens_per_s": round(w.ring_capacity / (float(np.mean(reb_ms)) * 1e-3), 1),
+        "step_ms": round(float(np.mean(step_ms)), 2),
+    }
+    log(f"[bench] ingest workload: {out}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +166,10 @@ def main():
     ap.add_argument("--copies", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-ingest-load", action="store_true",
+                    help="skip the ingest-and-rebuild measurement after the timed region")
+    ap.add_argument("--ingest-load-only", action="store_true",
+                    help="run only the ingest-and-rebuild measurement (for profiling)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run a plain copy of this many MiB before the timed region (counter "
                          "calibration)")
@@ -109,6 +188,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.ingest_load_only:
+        print(json.dumps({"ingest_under_load": ingest_under_load(torch, sfx, W, dev)}), flush=True)
+        return
     w = W.WORKLOADS[args.config]
     log(f"[bench] workload {w.name}: B={w.B} S={w.S} V={w.V} k={w.k} mode={w.mode}")
 
@@ -167,6 +249,9 @@ def main():
     log(f"[bench] {args.steps} steps over {nbuf} rotating buffers ({resident_mb:.0f} MB): "
         f"{ms * 1e3:.2f} us/step, {calls_s:.0f} calls/s, {achieved:.0f} GB/s algorithmic")
 
+    # ---------------------------------------------------------------- outside the timed region
+    load = None if args.no_ingest_load else ingest_under_load(torch, sfx, W, dev)
+
     # ---------------------------------------------------------------- oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -217,7 +302,8 @@ def main():
                   "algorithmic_bytes_per_call": int(alg_bytes),
                   "index_rebuild_ms": None if rebuild_s is None else round(rebuild_s * 1e3, 2),
                   "index_rebuild_tokens_per_s":
-                      None if not rebuild_s else round(corpus_n / rebuild_s, 1)},
+                      None if not rebuild_s else round(corpus_n / rebuild_s, 1),
+                  "ingest_under_load": load},
     }
     print(json.dumps(out), flush=True)
     d.close()
