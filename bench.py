@@ -87,7 +87,8 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
     k=32.  After warm_steps (ring full and evicting), per step: the harvest (HIP events on the
     calling stream), propose with that step's documents still in the delta, propose while the
     asynchronous rebuild of the whole ring runs on the side stream, the rebuild's wall time, and
-    propose once it is live (no delta).  Outside the headline timed region."""
+    propose once it is live (no delta).  Then the whole corpus is saved to a host file and
+    loaded into a fresh context (wall time of each).  Outside the headline timed region."""
     w = W.WORKLOADS[5]
     t0 = time.time()
     n, tok, samp = W.make_batch(5)
@@ -139,6 +140,22 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
         reb_ms.append((time.time() - tr) * 1e3)
         step_ms.append((time.time() - ts) * 1e3)
         p_live.append(timed(prop, calls))
+    # save and restore of the whole corpus (host file; a fresh context of the same capacity)
+    import tempfile
+
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "corpus.sfx")
+        torch.cuda.synchronize()
+        t1 = time.time()
+        d.save(path, stream)
+        save_ms = (time.time() - t1) * 1e3
+        file_mb = os.path.getsize(path) / 1e6
+        d2 = sfx.Drafter(cfg)
+        torch.cuda.synchronize()
+        t1 = time.time()
+        d2.load(path, stream)
+        load_ms = (time.time() - t1) * 1e3
+        d2.close()
     d.close()
     out = {
         "workload": f"ingest-B{w.B}-S{w.S}-ring{w.ring_capacity}",
@@ -151,6 +168,9 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
         "rebuild_ms": round(float(np.mean(reb_ms)), 2),
         "rebuild_tokens_per_s": round(w.ring_capacity / (float(np.mean(reb_ms)) * 1e-3), 1),
         "step_ms": round(float(np.mean(step_ms)), 2),
+        "save_ms": round(save_ms, 1),
+        "load_ms": round(load_ms, 1),
+        "corpus_file_MB": round(file_mb, 1),
     }
     log(f"[bench] ingest workload: {out}")
     return out

@@ -50,7 +50,8 @@ enum {
   SFX_ENOMEM = -2,     /* device allocation failed (only sfx_create allocates) */
   SFX_ECAPACITY = -3,  /* shape above what the context was created for */
   SFX_EHIP = -4,       /* a HIP runtime call failed */
-  SFX_ESTATE = -5      /* call not valid in the context's current state */
+  SFX_ESTATE = -5,     /* call not valid in the context's current state */
+  SFX_EIO = -6         /* a corpus file could not be written or read, or is not valid */
 };
 
 enum {
@@ -163,6 +164,40 @@ int sfx_wait_rebuild(sfx_ctx* ctx, void* stream);
  * stream.  SFX_ECAPACITY if cap is too small. */
 int sfx_corpus_snapshot(sfx_ctx* ctx, int32_t* text_out, int64_t cap, int64_t* n_out,
                         void* stream);
+
+/* Persist the corpus (suffix-gpu page, TODO: the cross-request global memory -- corpus ring,
+ * suffix array and delta -- is saved to disk and restored across sessions, so the accumulated
+ * statistics survive a restart instead of being rebuilt).  Writes the host file `path`: the
+ * live documents (indexed and delta alike, in ingest order), their start positions, the ring
+ * counters, and the live index as its snapshot text and suffix array.  The n-gram tables are
+ * not written: sfx_load derives them from the suffix array.  Synchronises `stream` and copies
+ * through host memory.  An asynchronous rebuild still in flight keeps running and is not saved;
+ * what it covers is in the saved delta.  SFX_ESTATE without a corpus, SFX_EIO when the file
+ * cannot be written.
+ *
+ * File layout, little-endian:
+ *   bytes  0..7   magic "SFXCORP1"
+ *   bytes  8..71  int64 capacity, head, tail, doc_head, doc_tail, snap_start, snap_end,
+ *                 then uint64 checksum.  Live tokens are logical positions [tail, head); live
+ *                 documents are numbers [doc_tail, doc_head); the index covers logical
+ *                 positions [snap_start, snap_end) (empty when no index is live).
+ *   then          int32 tokens[head - tail]                (each document ends with -1)
+ *                 int64 doc_start[doc_head - doc_tail]      (logical start of each document)
+ *                 int32 index_text[snap_end - snap_start]
+ *                 int32 suffix_array[snap_end - snap_start]
+ *   checksum      FNV-1a over the payload's 32-bit words: h = 14695981039346656037, then for
+ *                 every word w: h = (h xor w) * 1099511628211 (mod 2^64). */
+int sfx_save(sfx_ctx* ctx, const char* path, void* stream);
+
+/* Restore a file written by sfx_save into a context created with the same corpus_capacity,
+ * replacing its whole corpus state; the n-gram tables are built from the saved suffix array on
+ * `stream`, and the restored index is live when the call returns.  Every counter, the document
+ * structure and the suffix array (a permutation) are checked on the host before anything is
+ * copied.  SFX_EIO for a file that cannot be read, is truncated, has trailing bytes, a wrong
+ * magic or checksum, or inconsistent contents (the context is then unchanged); SFX_EINVAL for a
+ * capacity mismatch; SFX_ESTATE without a corpus or with an asynchronous rebuild in flight.
+ * Synchronises `stream`. */
+int sfx_load(sfx_ctx* ctx, const char* path, void* stream);
 
 /* Suffix array (suffix-gpu page, Highlights and References: Manber & Myers prefix doubling):
  * sa[r] = start of the r-th smallest suffix of text[0:n], tokens compared as signed int32, a

@@ -19,15 +19,15 @@ LIB_PATH = os.path.join(_HERE, "libsfx.so")
 MODE_LONGEST_FILL = 0
 MODE_SCORED = 1
 
-OK, EINVAL, ENOMEM, ECAPACITY, EHIP, ESTATE = 0, -1, -2, -3, -4, -5
+OK, EINVAL, ENOMEM, ECAPACITY, EHIP, ESTATE, EIO = 0, -1, -2, -3, -4, -5, -6
 _NAMES = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", ECAPACITY: "ECAPACITY", EHIP: "EHIP",
-          ESTATE: "ESTATE"}
+          ESTATE: "ESTATE", EIO: "EIO"}
 
 # every entry point declared in include/sfx.h
 EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_update_state",
            "sfx_harvest_finished", "sfx_ingest", "sfx_rebuild", "sfx_rebuild_async", "sfx_poll",
-           "sfx_wait_rebuild", "sfx_corpus_snapshot", "sfx_suffix_array_workspace_bytes",
-           "sfx_build_suffix_array")
+           "sfx_wait_rebuild", "sfx_corpus_snapshot", "sfx_save", "sfx_load",
+           "sfx_suffix_array_workspace_bytes", "sfx_build_suffix_array")
 
 
 FLAG_STREAM_CONTEXT = 1  # read contexts from device memory instead of staging them in LDS
@@ -111,6 +111,8 @@ def load(path: str = LIB_PATH):
         "sfx_poll": (ctypes.c_int, [_V, ctypes.POINTER(_I32), _V]),
         "sfx_wait_rebuild": (ctypes.c_int, [_V, _V]),
         "sfx_corpus_snapshot": (ctypes.c_int, [_V, _V, _I64, ctypes.POINTER(_I64), _V]),
+        "sfx_save": (ctypes.c_int, [_V, ctypes.c_char_p, _V]),
+        "sfx_load": (ctypes.c_int, [_V, ctypes.c_char_p, _V]),
         "sfx_suffix_array_workspace_bytes": (ctypes.c_size_t, [_I64]),
         "sfx_build_suffix_array": (ctypes.c_int, [_V, _I64, _V, _V, ctypes.c_size_t, _V]),
     }
@@ -233,6 +235,14 @@ class Drafter:
 
     def wait_rebuild(self, stream=None):
         _check(load().sfx_wait_rebuild(self._h, _stream(stream)))
+
+    def save(self, path, stream=None):
+        """Write the corpus (live documents, counters, live index) to the host file `path`."""
+        _check(load().sfx_save(self._h, os.fsencode(path), _stream(stream)))
+
+    def load(self, path, stream=None):
+        """Replace the corpus with the one saved in `path` (same corpus_capacity)."""
+        _check(load().sfx_load(self._h, os.fsencode(path), _stream(stream)))
 
     def corpus_snapshot(self, stream=None) -> torch.Tensor:
         cap = max(int(self.cfg.corpus_capacity), 1)
