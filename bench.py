@@ -88,7 +88,8 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
     calling stream), propose with that step's documents still in the delta, propose while the
     asynchronous rebuild of the whole ring runs on the side stream, the rebuild's wall time, and
     propose once it is live (no delta).  Then the whole corpus is saved to a host file and
-    loaded into a fresh context (wall time of each).  Outside the headline timed region."""
+    loaded into a fresh context (wall time of each), and in-flight ingest is timed on it.
+    Outside the headline timed region."""
     w = W.WORKLOADS[5]
     t0 = time.time()
     n, tok, samp = W.make_batch(5)
@@ -155,7 +156,18 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
         t1 = time.time()
         d2.load(path, stream)
         load_ms = (time.time() - t1) * 1e3
-        d2.close()
+    # in-flight ingest on the restored context: B rows of responses growing by k + 1 tokens per
+    # step, chunks of at least 64 tokens (one 66-token chunk per row every second step)
+    rows = torch.arange(w.B, dtype=torch.int32, device=dev)
+    resp = torch.from_numpy(np.concatenate(
+        [batches[i % len(batches)][2].cpu().numpy() for i in range(2)])).to(dev)[: w.B]
+    lens = torch.zeros(w.B, dtype=torch.int32, device=dev)
+    fl_ms = []
+    for st in range(16):
+        lens += w.k + 1
+        fl_ms.append(timed(lambda: d2.ingest_inflight(rows, lens, resp, min_chunk=64,
+                                                      stream=stream), 1))
+    d2.close()
     d.close()
     out = {
         "workload": f"ingest-B{w.B}-S{w.S}-ring{w.ring_capacity}",
@@ -171,6 +183,8 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
         "save_ms": round(save_ms, 1),
         "load_ms": round(load_ms, 1),
         "corpus_file_MB": round(file_mb, 1),
+        "inflight_ingest_ms": round(float(np.mean(fl_ms)), 3),
+        "inflight_tokens_per_s": round(8 * w.B * 66 / (sum(fl_ms) * 1e-3), 1),
     }
     log(f"[bench] ingest workload: {out}")
     return out

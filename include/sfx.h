@@ -134,6 +134,25 @@ int sfx_harvest_finished(sfx_ctx* ctx, int32_t R, const int32_t* row_indices,
                          const int32_t* lengths, const int32_t* token_ids, int32_t num_rows,
                          int32_t S, void* stream);
 
+/* In-flight ingest (RFC page "[RFC]: Suffix decoding on GPU (suffix_gpu)", Design: in-flight
+ * responses are ingested off the critical path, finished requests are final-flushed before
+ * their batch rows are reused; the suffix_gpu_ingest_chunk knob).  The context keeps an ingest
+ * cursor for every batch row in [0, max_batch), 0 at creation.  For entry r, with
+ * row = row_indices[r] and n = clamp(lengths[r], 0, S): the chunk token_ids[row, cursor:n] is
+ * appended as one document (followed by -1) when it holds at least max(min_chunk, 1) tokens, or
+ * when final_flags[r] != 0 and it is not empty; the cursor then moves to n.  After a final
+ * flush the cursor is 0, so the row can start a new request.  n below the cursor (a row reused
+ * without a flush) restarts the row at 0.  Chunks are separate documents: matches and
+ * continuations do not cross from one chunk to the next.  Entries append in r order; an entry
+ * that appends nothing adds no document; a row listed again in the same call, or outside
+ * [0, min(num_rows, max_batch)), is ignored.  final_flags may be NULL (no flush).  Documents and
+ * eviction otherwise as sfx_harvest_finished; all decisions are taken on the device, so the
+ * call neither synchronises nor allocates.  R at most 65536 (else SFX_ECAPACITY). */
+int sfx_ingest_inflight(sfx_ctx* ctx, int32_t R, const int32_t* row_indices,
+                        const int32_t* lengths, const int32_t* final_flags,
+                        const int32_t* token_ids, int32_t num_rows, int32_t S, int32_t min_chunk,
+                        void* stream);
+
 /* Ingest packed documents: document d is tokens[doc_offsets[d] : doc_offsets[d+1]] (offsets
  * int64, non-decreasing, device memory); otherwise as sfx_harvest_finished. */
 int sfx_ingest(sfx_ctx* ctx, int32_t num_docs, const int64_t* doc_offsets, const int32_t* tokens,

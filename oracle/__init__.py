@@ -13,7 +13,7 @@ import subprocess
 
 import numpy as np
 
-from .corpus import LiveCorpus, harvest_docs  # noqa: F401
+from .corpus import InflightIngest, LiveCorpus, harvest_docs  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")

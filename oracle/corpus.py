@@ -62,3 +62,47 @@ class LiveCorpus:
             parts.append(d)
             parts.append(np.array([-1], np.int32))
         return np.concatenate(parts).astype(np.int32)
+
+
+class InflightIngest:
+    """Per-row ingest cursors of in-flight responses (RFC page "[RFC]: Suffix decoding on GPU
+    (suffix_gpu)", Design: in-flight responses are ingested off the critical path and finished
+    requests are final-flushed before their batch rows are reused; the ingest-chunk knob).
+
+    Reading taken (the page gives no document semantics for partial responses): an ingest call
+    appends, for every listed row, the tokens past the row's cursor as one separate document once
+    at least max(min_chunk, 1) of them have accumulated, or on a final flush whenever any are
+    left.  The cursor then moves to the row's length, or back to 0 after a final flush.  A length
+    below the cursor means the row was reused without a flush, and the row restarts at 0.  A row
+    listed twice in one call counts once, at its first entry; rows outside
+    [0, min(num_rows, max_rows)) are ignored.  docs() returns the call's documents in entry order,
+    to be given to LiveCorpus.ingest."""
+
+    def __init__(self, max_rows: int):
+        self.max_rows = int(max_rows)
+        self.cursor = [0] * self.max_rows
+
+    def docs(self, token_ids, row_indices, lengths, final=None, min_chunk=1):
+        tok = np.asarray(token_ids, dtype=np.int32)
+        num_rows, S = tok.shape
+        limit = min(num_rows, self.max_rows)
+        need = max(int(min_chunk), 1)
+        seen = set()
+        out = []
+        for r, (row, ln) in enumerate(zip(np.asarray(row_indices).tolist(),
+                                          np.asarray(lengths).tolist())):
+            row = int(row)
+            if row < 0 or row >= limit or row in seen:
+                continue
+            seen.add(row)
+            n = max(0, min(int(ln), S))
+            c = self.cursor[row]
+            if n < c:
+                c = 0
+            fin = final is not None and int(final[r]) != 0
+            chunk = n - c
+            take = chunk >= need or (fin and chunk > 0)
+            if take:
+                out.append(tok[row, c:n].copy())
+            self.cursor[row] = 0 if fin else (n if take else c)
+        return out

@@ -25,8 +25,8 @@ _NAMES = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", ECAPACITY: "ECAPACITY", EHIP: "EHI
 
 # every entry point declared in include/sfx.h
 EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_update_state",
-           "sfx_harvest_finished", "sfx_ingest", "sfx_rebuild", "sfx_rebuild_async", "sfx_poll",
-           "sfx_wait_rebuild", "sfx_corpus_snapshot", "sfx_save", "sfx_load",
+           "sfx_harvest_finished", "sfx_ingest_inflight", "sfx_ingest", "sfx_rebuild",
+           "sfx_rebuild_async", "sfx_poll", "sfx_wait_rebuild", "sfx_corpus_snapshot", "sfx_save", "sfx_load",
            "sfx_suffix_array_workspace_bytes", "sfx_build_suffix_array")
 
 
@@ -106,6 +106,7 @@ def load(path: str = LIB_PATH):
         "sfx_update_state": (ctypes.c_int, [_I32, _I32, _I32, _V, _V, _V, _V, _V]),
         "sfx_harvest_finished": (ctypes.c_int, [_V, _I32, _V, _V, _V, _I32, _I32, _V]),
         "sfx_ingest": (ctypes.c_int, [_V, _I32, _V, _V, _V]),
+        "sfx_ingest_inflight": (ctypes.c_int, [_V, _I32, _V, _V, _V, _V, _I32, _I32, _I32, _V]),
         "sfx_rebuild": (ctypes.c_int, [_V, _V]),
         "sfx_rebuild_async": (ctypes.c_int, [_V, _V]),
         "sfx_poll": (ctypes.c_int, [_V, ctypes.POINTER(_I32), _V]),
@@ -201,6 +202,24 @@ class Drafter:
         _check(load().sfx_harvest_finished(self._h, rows.shape[0], _ptr(rows), _ptr(lens),
                                            _ptr(tok), tok.shape[0], tok.shape[1],
                                            _stream(stream)))
+
+    def ingest_inflight(self, row_indices, lengths, token_ids, final=None, min_chunk=1,
+                        stream=None):
+        """Append each listed row's tokens past its ingest cursor as one document once at least
+        min_chunk have accumulated; rows with final != 0 flush what is left and restart."""
+        rows = _i32(row_indices, "row_indices", 1)
+        lens = _i32(lengths, "lengths", 1)
+        tok = _i32(token_ids, "token_ids", 2)
+        if rows.shape != lens.shape:
+            raise ValueError("row_indices and lengths differ in size")
+        fin = None
+        if final is not None:
+            fin = _i32(final, "final", 1)
+            if fin.shape != rows.shape:
+                raise ValueError("final and row_indices differ in size")
+        _check(load().sfx_ingest_inflight(self._h, rows.shape[0], _ptr(rows), _ptr(lens),
+                                          _ptr(fin), _ptr(tok), tok.shape[0], tok.shape[1],
+                                          int(min_chunk), _stream(stream)))
 
     def ingest(self, doc_offsets, tokens, stream=None):
         offs = doc_offsets

@@ -14,11 +14,13 @@ namespace {
 
 constexpr int PT = 1024;  // plan kernel threads
 
+// Length of entry r's document, or -1 when the entry appends no document at all.
 __device__ __forceinline__ int64_t doc_len(const IngestArgs& a, int r) {
   if (a.doc_offsets) {
     const int64_t l = a.doc_offsets[r + 1] - a.doc_offsets[r];
     return l < 0 ? 0 : l;
   }
+  if (a.seg_len) return a.seg_len[r];
   const int row = a.row_indices[r];
   if (row < 0 || row >= a.num_rows) return 0;
   int l = a.lengths[r];
@@ -28,11 +30,15 @@ __device__ __forceinline__ int64_t doc_len(const IngestArgs& a, int r) {
 __device__ __forceinline__ const int32_t* doc_src(const IngestArgs& a, int r) {
   if (a.doc_offsets) return a.tokens + a.doc_offsets[r];
   const int row = a.row_indices[r];
-  return a.tokens + (int64_t)(row < 0 ? 0 : row) * a.S;
+  const int32_t* base = a.tokens + (int64_t)(row < 0 ? 0 : row) * a.S;
+  return a.seg_start ? base + a.seg_start[r] : base;
 }
 
 // Offsets of the new documents (each takes len + 1 ring tokens), new head, and the eviction
 // that keeps the longest run of most recent documents fitting in the capacity.
+// Each entry's value packs its ring tokens above bit 20 and its document count (0 or 1) below, so
+// one scan gives both the offsets and the document numbers (at most 2^16 entries per launch).
+constexpr int kDocBits = 20;
 __global__ __launch_bounds__(PT) void ingest_plan_kernel(IngestArgs a) {
   __shared__ int64_t wsum[PT / 64];
   __shared__ int64_t carry;
@@ -42,7 +48,8 @@ __global__ __launch_bounds__(PT) void ingest_plan_kernel(IngestArgs a) {
   __syncthreads();
   for (int c = 0; c < a.R; c += PT) {
     const int r = c + tid;
-    const int64_t v = r < a.R ? doc_len(a, r) + 1 : 0;
+    const int64_t l = r < a.R ? doc_len(a, r) : -1;
+    const int64_t v = l >= 0 ? ((l + 1) << kDocBits) | 1 : 0;
     int64_t x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -53,15 +60,21 @@ __global__ __launch_bounds__(PT) void ingest_plan_kernel(IngestArgs a) {
     __syncthreads();
     int64_t pre = carry;
     for (int w = 0; w < wid; ++w) pre += wsum[w];
-    if (r < a.R) a.doc_off[r] = pre + x - v;
+    if (r < a.R) {
+      const int64_t before = pre + x - v;
+      a.doc_off[r] = before >> kDocBits;
+      a.doc_idx[r] = (int32_t)(before & ((1 << kDocBits) - 1));
+    }
     __syncthreads();
     if (tid == PT - 1) carry = pre + x;
     __syncthreads();
   }
   Ctl* ctl = a.ctl;
   if (tid == 0) {
-    const int64_t total = carry;
+    const int64_t total = carry >> kDocBits;
+    const int32_t ndocs = (int32_t)(carry & ((1 << kDocBits) - 1));
     a.doc_off[a.R] = total;
+    a.doc_idx[a.R] = ndocs;
     const int64_t base = ctl->head;
     const int64_t new_head = base + total;
     const int64_t thr = new_head - a.cap;
@@ -85,7 +98,7 @@ __global__ __launch_bounds__(PT) void ingest_plan_kernel(IngestArgs a) {
           else rh = mid;
         }
         new_tail = rl < a.R ? base + a.doc_off[rl] : new_head;
-        new_doc_tail = dh + rl;
+        new_doc_tail = dh + a.doc_idx[rl];
       }
     }
     s_base = base;
@@ -93,14 +106,58 @@ __global__ __launch_bounds__(PT) void ingest_plan_kernel(IngestArgs a) {
     ctl->ingest_base = base;
     ctl->head = new_head;
     ctl->tail = new_tail;
-    ctl->doc_head = dh + a.R;
+    ctl->doc_head = dh + ndocs;
     ctl->doc_tail = new_doc_tail;
     carry = dh;
   }
   __syncthreads();
   const int64_t dh = carry, base = s_base, ndt = s_doc_tail;
-  for (int r = tid; r < a.R; r += PT)
-    if (dh + r >= ndt) a.doc_start[(dh + r) % a.dcap] = base + a.doc_off[r];
+  for (int r = tid; r < a.R; r += PT) {
+    const int64_t d = dh + a.doc_idx[r];
+    if (doc_len(a, r) >= 0 && d >= ndt) a.doc_start[d % a.dcap] = base + a.doc_off[r];
+  }
+}
+
+// In-flight ingest, per entry r: a row listed again later in the same call is claimed by its
+// first entry only (claim = the smallest r); the claimed entry's chunk is the row's tokens past
+// its cursor, appended once it holds min_chunk tokens or, with final_flags[r], whenever it is not
+// empty.  The cursor then moves to the row's length, or back to 0 after a final flush.  A length
+// below the cursor means the row was reused without a flush: its cursor restarts at 0.
+__global__ void inflight_claim_kernel(InflightArgs a) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= a.R) return;
+  const int row = a.row_indices[r];
+  if (row >= 0 && row < a.num_rows && row < a.max_rows) atomicMin(&a.claim[row], r);
+}
+
+__global__ void inflight_prepare_kernel(InflightArgs a) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= a.R) return;
+  const int row = a.row_indices[r];
+  int start = 0, len = -1;
+  if (row >= 0 && row < a.num_rows && row < a.max_rows && a.claim[row] == r) {
+    int n = a.lengths[r];
+    n = n < 0 ? 0 : (n > a.S ? a.S : n);
+    int c = a.cursor[row];
+    if (n < c) c = 0;
+    const bool fin = a.final_flags && a.final_flags[r] != 0;
+    const int chunk = n - c;
+    const int need = a.min_chunk > 1 ? a.min_chunk : 1;
+    const bool take = chunk >= need || (fin && chunk > 0);
+    if (take) {
+      start = c;
+      len = chunk;
+    }
+    a.cursor[row] = fin ? 0 : (take ? n : c);
+    a.claim[row] = 0x7fffffff;
+  }
+  a.seg_start[r] = start;
+  a.seg_len[r] = len;
+}
+
+__global__ void claims_init_kernel(int32_t* claim, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) claim[i] = 0x7fffffff;
 }
 
 // Ring slots of a grid-stride walk: one division per thread, then steps of stride % cap.
@@ -118,6 +175,7 @@ struct SlotWalk {
 __global__ __launch_bounds__(256) void ingest_scatter_kernel(IngestArgs a) {
   const int r = blockIdx.x;
   const int64_t len = doc_len(a, r);
+  if (len < 0) return;  // no document
   const int32_t* src = doc_src(a, r);
   const int64_t start = a.ctl->ingest_base + a.doc_off[r];
   const int64_t live_from = a.ctl->tail;
@@ -191,6 +249,20 @@ hipError_t launch_ingest(const IngestArgs& a, int max_doc_len_hint, hipStream_t 
   int gy = (int)((max_doc_len_hint + 1 + 1023) / 1024);
   gy = gy < 1 ? 1 : (gy > 64 ? 64 : gy);
   hipLaunchKernelGGL(ingest_scatter_kernel, dim3(a.R, gy), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_inflight_prepare(const InflightArgs& a, hipStream_t st) {
+  if (a.R <= 0) return hipSuccess;
+  const int blocks = (a.R + 255) / 256;
+  hipLaunchKernelGGL(inflight_claim_kernel, dim3(blocks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(inflight_prepare_kernel, dim3(blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_claims_init(int32_t* claim, int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(claims_init_kernel, dim3((n + 255) / 256), dim3(256), 0, st, claim, n);
   return hipGetLastError();
 }
 

@@ -65,6 +65,9 @@ struct sfx_ctx {
   int64_t* doc_start = nullptr;
   int64_t dcap = 0;
   int64_t* doc_off = nullptr;
+  int32_t* doc_idx = nullptr;
+  int32_t* inflight = nullptr;   // [2 * max_batch] cursor and claim of every batch row, then
+                                 // [2 * kIngestChunk] segment starts and lengths
   int64_t* range_dev = nullptr;  // [2] snapshot range read back by the rebuild driver
   IndexBuf idx[2]{};
   uint32_t ht_slots = 0;
@@ -133,6 +136,8 @@ void free_ctx(sfx_ctx* c) {
   f(c->ring);
   f(c->doc_start);
   f(c->doc_off);
+  f(c->doc_idx);
+  f(c->inflight);
   f(c->range_dev);
   for (auto& b : c->idx) {
     f(b.text);
@@ -317,6 +322,8 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
     bool ok = al((void**)&c->ctl, sizeof(Ctl)) && al((void**)&c->ring, 4 * c->cap) &&
               al((void**)&c->doc_start, 8 * c->dcap) &&
               al((void**)&c->doc_off, 8 * (kIngestChunk + 1)) &&
+              al((void**)&c->doc_idx, 4 * (kIngestChunk + 1)) &&
+              al((void**)&c->inflight, 4 * (2 * (size_t)cfg->max_batch + 2 * kIngestChunk)) &&
               al((void**)&c->range_dev, 32);
     for (int bi = 0; bi < 2 && ok; ++bi) {
       IndexBuf& b = c->idx[bi];
@@ -340,6 +347,10 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
       return fail(SFX_EHIP, "stream/event creation failed");
     }
     if ((e = launch_ctl_init(c->ctl, c->side)) != hipSuccess ||
+        (e = hipMemsetAsync(c->inflight, 0, 4 * (size_t)cfg->max_batch, c->side)) !=
+            hipSuccess ||
+        (e = launch_claims_init(c->inflight + cfg->max_batch, cfg->max_batch, c->side)) !=
+            hipSuccess ||
         (e = hipStreamSynchronize(c->side)) != hipSuccess) {
       free_ctx(c);
       return hip_fail(e, "control block init");
@@ -416,6 +427,7 @@ static int ingest_common(sfx_ctx* c, IngestArgs a, int hint, hipStream_t st) {
   a.doc_start = c->doc_start;
   a.dcap = c->dcap;
   a.doc_off = c->doc_off;
+  a.doc_idx = c->doc_idx;
   const int R = a.R;
   for (int r0 = 0; r0 < R; r0 += kIngestChunk) {
     IngestArgs ch = a;
@@ -462,6 +474,47 @@ int sfx_ingest(sfx_ctx* c, int32_t num_docs, const int64_t* offs, const int32_t*
   a.doc_offsets = offs;
   a.tokens = tokens;
   return ingest_common(c, a, 1 << 16, (hipStream_t)stream);
+}
+
+int sfx_ingest_inflight(sfx_ctx* c, int32_t R, const int32_t* rows, const int32_t* lengths,
+                        const int32_t* final_flags, const int32_t* tok, int32_t num_rows,
+                        int32_t S, int32_t min_chunk, void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!c->ctl) return fail(SFX_ESTATE, "context has no corpus (corpus_capacity == 0)");
+  if (R < 0 || S < 0 || num_rows < 0 || min_chunk < 0)
+    return fail(SFX_EINVAL, "negative shape or min_chunk");
+  if (R == 0) return SFX_OK;
+  if (R > kIngestChunk)
+    return fail(SFX_ECAPACITY, "R=%d above %d entries per in-flight ingest", R, kIngestChunk);
+  if (!rows || !lengths || (S > 0 && num_rows > 0 && !tok))
+    return fail(SFX_EINVAL, "NULL array argument");
+  hipStream_t st = (hipStream_t)stream;
+  const int mb = c->cfg.max_batch;
+  InflightArgs f{};
+  f.R = R;
+  f.row_indices = rows;
+  f.lengths = lengths;
+  f.final_flags = final_flags;
+  f.num_rows = num_rows;
+  f.S = S;
+  f.min_chunk = min_chunk;
+  f.max_rows = mb;
+  f.cursor = c->inflight;
+  f.claim = c->inflight + mb;
+  f.seg_start = c->inflight + 2 * (size_t)mb;
+  f.seg_len = f.seg_start + kIngestChunk;
+  HIP_OR_RETURN(launch_inflight_prepare(f, st), "in-flight prepare launch");
+  IngestArgs a{};
+  a.R = R;
+  a.row_indices = rows;
+  a.lengths = lengths;
+  a.num_rows = num_rows;
+  a.S = S;
+  a.tokens = tok;
+  a.seg_start = f.seg_start;
+  a.seg_len = f.seg_len;
+  return ingest_common(c, a, S, st);
 }
 
 static int pick_buffer(sfx_ctx* c) { return c->active_host == 0 ? 1 : 0; }

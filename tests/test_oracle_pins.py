@@ -337,3 +337,70 @@ def test_live_corpus_eviction(orc):
             exp = [x for d in live for x in d + [-1]]
             assert lc.text().tolist() == exp
             assert len(exp) <= cap
+
+
+def test_inflight_ingest_hand_example(orc):
+    """In-flight ingest (RFC page, Design: in-flight responses ingested, finished ones
+    final-flushed), worked by hand from the rule: chunks past the cursor of at least min_chunk
+    tokens, a final flush takes any remainder and resets the cursor, a shorter length restarts
+    the row, a repeated row counts at its first entry, unknown rows are ignored."""
+    tok = np.array([[10, 11, 12, 13, 14, 15], [20, 21, 22, 23, 24, 25],
+                    [30, 31, 32, 33, 34, 35]], np.int32)
+    m = orc.InflightIngest(max_rows=3)
+    calls = [  # (rows, lengths, final, min_chunk) -> documents
+        (([0], [1], None, 2), []),
+        (([0], [3], None, 2), [[10, 11, 12]]),
+        (([0], [4], None, 2), []),
+        (([0], [5], [1], 2), [[13, 14]]),
+        (([0], [2], None, 2), [[10, 11]]),
+        (([0], [1], None, 2), []),             # shorter than the cursor: restart, 1 < 2
+        (([1, 1, 2], [3, 5, 2], None, 1), [[20, 21, 22], [30, 31]]),
+        (([1], [6], None, 4), []),             # 3 tokens past the cursor, below min_chunk
+        (([1, 4, -1, 2], [6, 6, 6, 2], [1, 1, 1, 1], 4), [[23, 24, 25]]),  # row 2: nothing left
+        (([2], [3], [1], 9), [[30, 31, 32]]),  # row 2's cursor was reset by the empty flush
+        (([0, 1], [6, 2], None, 2), [[10, 11, 12, 13, 14, 15], [20, 21]]),
+    ]
+    for i, ((rows, lens, fin, mc), exp) in enumerate(calls):
+        got = m.docs(tok, rows, lens, final=fin, min_chunk=mc)
+        assert [d.tolist() for d in got] == exp, f"call {i}"
+    assert m.cursor == [6, 2, 0]
+
+
+def test_inflight_ingest_invariants(orc):
+    """Random decode traces: with min_chunk 1 and a flush at every request's end, each request's
+    chunks concatenate to its whole response; with any min_chunk only a final flush may append
+    fewer than min_chunk tokens."""
+    rng = np.random.default_rng(23)
+    for it in range(60):
+        B, S = int(rng.integers(1, 6)), 64
+        mc = int(rng.integers(0, 6))
+        m = orc.InflightIngest(max_rows=B)
+        tok = np.zeros((B, S), np.int32)
+        n = np.zeros(B, np.int64)
+        got = {b: [] for b in range(B)}   # chunks of the current request of each row
+        done = []                         # (response, chunks) of finished requests
+        for step in range(30):
+            fin = np.zeros(B, np.int32)
+            for b in range(B):
+                grow = int(rng.integers(0, 5))
+                tok[b, n[b]:n[b] + grow] = rng.integers(0, 1000, size=min(grow, S - n[b]))
+                n[b] = min(S, n[b] + grow)
+                fin[b] = int(rng.random() < 0.15 or n[b] == S)
+            order = rng.permutation(B)
+            docs = m.docs(tok, order, n[order], final=fin[order], min_chunk=mc)
+            k = 0
+            for b in order:  # attribute the documents back to rows (entry order)
+                before = sum(len(c) for c in got[b])
+                if k < len(docs) and before < n[b] and \
+                        docs[k].tolist() == tok[b, before:before + len(docs[k])].tolist() and \
+                        (len(docs[k]) >= max(mc, 1) or fin[b]):
+                    got[b].append(docs[k])
+                    k += 1
+                if fin[b]:
+                    done.append((tok[b, :n[b]].copy(), got[b]))
+                    got[b], n[b] = [], 0
+            assert k == len(docs)
+        for resp, chunks in done:
+            cat = np.concatenate(chunks) if chunks else np.zeros(0, np.int32)
+            assert cat.tolist() == resp.tolist()
+            assert all(len(c) >= max(mc, 1) for c in chunks[:-1])
