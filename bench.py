@@ -284,6 +284,21 @@ def main():
         f"{ms * 1e3:.2f} us/step, {calls_s:.0f} calls/s, {achieved:.0f} GB/s algorithmic")
 
     # ---------------------------------------------------------------- outside the timed region
+    # acceptance estimate [B, k] and verifier feedback, each right after a propose
+    est = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+    acc = torch.full((w.B,), w.k // 2, dtype=torch.int32, device=dev)
+    est_ms, fb_ms = [], []
+    for i in range(20):
+        b = bufs[i % nbuf]
+        d.propose(b[0], b[1], b[2], draft, nv, stream)
+        for fn, lst in ((lambda: d.accept_estimate(w.B, est, stream), est_ms),
+                        (lambda: d.accept_feedback(acc, stream), fb_ms)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            lst.append(e0.elapsed_time(e1))
     load = None if args.no_ingest_load else ingest_under_load(torch, sfx, W, dev)
 
     # ---------------------------------------------------------------- oracle baseline
@@ -337,6 +352,8 @@ def main():
                   "index_rebuild_ms": None if rebuild_s is None else round(rebuild_s * 1e3, 2),
                   "index_rebuild_tokens_per_s":
                       None if not rebuild_s else round(corpus_n / rebuild_s, 1),
+                  "accept_estimate_us": round(float(np.mean(est_ms)) * 1e3, 2),
+                  "accept_feedback_us": round(float(np.mean(fb_ms)) * 1e3, 2),
                   "ingest_under_load": load},
     }
     print(json.dumps(out), flush=True)

@@ -184,6 +184,32 @@ int sfx_wait_rebuild(sfx_ctx* ctx, void* stream);
 int sfx_corpus_snapshot(sfx_ctx* ctx, int32_t* text_out, int64_t cap, int64_t* n_out,
                         void* stream);
 
+/* Per-slot acceptance estimate (vLLM docs "Suffix Decoding", Use adaptive verification at
+ * higher concurrency: the speculator reports a per-slot acceptance estimate learned online by
+ * draft source, match length and position, and the scheduler verifies only the slots worth
+ * their cost).  Every sfx_propose records, per row b < B, its winning candidate: source (0 the
+ * request's own context, 1 the corpus), match length, and num_valid (no winner: nothing).
+ * The context keeps a table of counts per (source, length 0..64, slot 0..31): proposed and
+ * accepted.
+ *
+ * sfx_accept_estimate: est_ppm [B, k] (device, int32) receives, for every slot d < num_valid of
+ *   row b's last propose, floor(10^6 * (accepted + 1) / (proposed + 2)) of its cell (Laplace's
+ *   rule: 500000 for an unseen cell), and 0 for the other slots.
+ * sfx_accept_feedback: num_accepted [B] (device) is the number of draft tokens the verifier
+ *   accepted for each row of the last propose (a prefix of the draft; clamped to
+ *   [0, num_valid]).  Every drafted slot d of the row adds one proposal to its cell, and one
+ *   acceptance when d < num_accepted.  The row's record is consumed, so feedback counts each
+ *   propose once.
+ * sfx_accept_reset: clears the table and the records.
+ * sfx_accept_counts: copies the table to `counts` (device, 2*65*32*2 uint64, index
+ *   ((source * 65 + length) * 32 + slot) * 2 + {0 proposed, 1 accepted}).
+ * All four enqueue on `stream` and neither synchronise nor allocate.  B at most max_batch
+ * (else SFX_ECAPACITY). */
+int sfx_accept_estimate(sfx_ctx* ctx, int32_t B, int32_t* est_ppm, void* stream);
+int sfx_accept_feedback(sfx_ctx* ctx, int32_t B, const int32_t* num_accepted, void* stream);
+int sfx_accept_reset(sfx_ctx* ctx, void* stream);
+int sfx_accept_counts(sfx_ctx* ctx, uint64_t* counts, void* stream);
+
 /* Persist the corpus (suffix-gpu page, TODO: the cross-request global memory -- corpus ring,
  * suffix array and delta -- is saved to disk and restored across sessions, so the accumulated
  * statistics survive a restart instead of being rebuilt).  Writes the host file `path`: the

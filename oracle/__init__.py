@@ -13,6 +13,7 @@ import subprocess
 
 import numpy as np
 
+from .accept import AcceptModel, picks_from_info  # noqa: F401
 from .corpus import InflightIngest, LiveCorpus, harvest_docs  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -26,7 +26,8 @@ _NAMES = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", ECAPACITY: "ECAPACITY", EHIP: "EHI
 # every entry point declared in include/sfx.h
 EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_update_state",
            "sfx_harvest_finished", "sfx_ingest_inflight", "sfx_ingest", "sfx_rebuild",
-           "sfx_rebuild_async", "sfx_poll", "sfx_wait_rebuild", "sfx_corpus_snapshot", "sfx_save", "sfx_load",
+           "sfx_rebuild_async", "sfx_poll", "sfx_wait_rebuild", "sfx_accept_estimate",
+           "sfx_accept_feedback", "sfx_accept_reset", "sfx_accept_counts", "sfx_corpus_snapshot", "sfx_save", "sfx_load",
            "sfx_suffix_array_workspace_bytes", "sfx_build_suffix_array")
 
 
@@ -112,6 +113,10 @@ def load(path: str = LIB_PATH):
         "sfx_poll": (ctypes.c_int, [_V, ctypes.POINTER(_I32), _V]),
         "sfx_wait_rebuild": (ctypes.c_int, [_V, _V]),
         "sfx_corpus_snapshot": (ctypes.c_int, [_V, _V, _I64, ctypes.POINTER(_I64), _V]),
+        "sfx_accept_estimate": (ctypes.c_int, [_V, _I32, _V, _V]),
+        "sfx_accept_feedback": (ctypes.c_int, [_V, _I32, _V, _V]),
+        "sfx_accept_reset": (ctypes.c_int, [_V, _V]),
+        "sfx_accept_counts": (ctypes.c_int, [_V, _V, _V]),
         "sfx_save": (ctypes.c_int, [_V, ctypes.c_char_p, _V]),
         "sfx_load": (ctypes.c_int, [_V, ctypes.c_char_p, _V]),
         "sfx_suffix_array_workspace_bytes": (ctypes.c_size_t, [_I64]),
@@ -254,6 +259,27 @@ class Drafter:
 
     def wait_rebuild(self, stream=None):
         _check(load().sfx_wait_rebuild(self._h, _stream(stream)))
+
+    def accept_estimate(self, B, est_ppm=None, stream=None):
+        """[B, k] int32 per-slot acceptance estimates (ppm) of the last propose's drafts."""
+        if est_ppm is None:
+            est_ppm = torch.empty((B, self.cfg.k), dtype=torch.int32, device="cuda")
+        _check(load().sfx_accept_estimate(self._h, B, _ptr(est_ppm), _stream(stream)))
+        return est_ppm
+
+    def accept_feedback(self, num_accepted, stream=None):
+        """Count the verifier's accepted tokens [B] against the last propose's drafts."""
+        na = _i32(num_accepted, "num_accepted", 1)
+        _check(load().sfx_accept_feedback(self._h, na.shape[0], _ptr(na), _stream(stream)))
+
+    def accept_reset(self, stream=None):
+        _check(load().sfx_accept_reset(self._h, _stream(stream)))
+
+    def accept_counts(self, stream=None) -> torch.Tensor:
+        """The counts table as int64 [2, 65, 32, 2] (proposed, accepted)."""
+        out = torch.empty((2, 65, 32, 2), dtype=torch.int64, device="cuda")
+        _check(load().sfx_accept_counts(self._h, _ptr(out), _stream(stream)))
+        return out
 
     def save(self, path, stream=None):
         """Write the corpus (live documents, counters, live index) to the host file `path`."""

@@ -19,6 +19,7 @@ struct ProposeArgs {
   const int32_t* ring;
   int64_t ring_cap;    // ring slots: slot = position % ring_cap
   int32_t stream_ctx;  // read the context from HBM instead of staging it in LDS
+  int32_t* pick;       // [B] out: the winner as num_valid << 16 | source << 8 | length, or -1
 };
 
 constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one gfx950 workgroup

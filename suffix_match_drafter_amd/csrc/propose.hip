@@ -876,7 +876,10 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   int32_t* drow = a.draft + (int64_t)b * a.k;
   if (t == 0) {
     for (int i = tid; i < a.k; i += NT) drow[i] = -1;
-    if (tid == 0) a.nvalid[b] = 0;
+    if (tid == 0) {
+      a.nvalid[b] = 0;
+      a.pick[b] = -1;
+    }
     return;
   }
   const bool fast = r.fast;
@@ -1250,8 +1253,12 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   const int ws = win >= 0 ? __builtin_amdgcn_readlane(csrc, win) : -1;
   const int nv = win >= 0 ? __builtin_amdgcn_readlane(cn, win) : 0;
   const int fill = a.mode == 0 ? sm.tail[0] : -1;
+  const int wlen = win >= 0 ? __builtin_amdgcn_readlane(clen, win) : 0;
   for (int i = lane; i < a.k; i += 64) drow[i] = i < nv ? sm.cand_out[ws][i] : fill;
-  if (lane == 0) a.nvalid[b] = nv;
+  if (lane == 0) {
+    a.nvalid[b] = nv;
+    a.pick[b] = win >= 0 ? (nv << 16) | ((win >= nb ? 1 : 0) << 8) | wlen : -1;
+  }
 }
 
 __global__ void update_state_kernel(int B, int S, int T, int32_t* tok, const int32_t* ntns,

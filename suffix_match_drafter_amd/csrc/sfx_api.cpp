@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "../../include/sfx.h"
+#include "accept.h"
 #include "corpus.h"
 #include "propose.h"
 #include "sa_build.h"
@@ -58,6 +59,8 @@ uint32_t next_pow2_u32(uint64_t v) {
 struct sfx_ctx {
   sfx_config cfg{};
   int device = 0;
+  int32_t* pick = nullptr;                 // [max_batch] winner of each row's last propose
+  unsigned long long* accept = nullptr;    // acceptance counts (accept.h layout)
   // corpus (absent when corpus_capacity == 0)
   Ctl* ctl = nullptr;
   int32_t* ring = nullptr;
@@ -132,6 +135,8 @@ void free_ctx(sfx_ctx* c) {
   auto f = [](void* p) {
     if (p) (void)hipFree(p);
   };
+  f(c->pick);
+  f(c->accept);
   f(c->ctl);
   f(c->ring);
   f(c->doc_start);
@@ -314,6 +319,19 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
                   lds + propose_static_lds(), kLdsBytes);
     }
   }
+  {
+    const int rows = cfg->max_batch > 0 ? cfg->max_batch : 1;
+    if (hipMalloc((void**)&c->pick, 4 * (size_t)rows) != hipSuccess ||
+        hipMalloc((void**)&c->accept, sizeof(unsigned long long) * kAcceptEntries) != hipSuccess) {
+      free_ctx(c);
+      return fail(SFX_ENOMEM, "device allocation failed for the acceptance table");
+    }
+    if ((e = launch_accept_reset(c->accept, c->pick, rows, nullptr)) != hipSuccess ||
+        (e = hipStreamSynchronize(nullptr)) != hipSuccess) {
+      free_ctx(c);
+      return hip_fail(e, "acceptance table init");
+    }
+  }
   if (cfg->corpus_capacity > 0) {
     c->cap = cfg->corpus_capacity;
     c->dcap = c->cap + 1;
@@ -405,6 +423,7 @@ int sfx_propose(sfx_ctx* c, int32_t B, int32_t S, int32_t T, const int32_t* ntns
   a.ring = c->ring;
   a.ring_cap = c->cap > 0 ? c->cap : 1;
   a.stream_ctx = (g.flags & SFX_FLAG_STREAM_CONTEXT) != 0;
+  a.pick = c->pick;
   HIP_OR_RETURN(launch_propose(a, (hipStream_t)stream), "propose launch");
   return SFX_OK;
 }
@@ -614,6 +633,51 @@ int sfx_corpus_snapshot(sfx_ctx* c, int32_t* text_out, int64_t cap, int64_t* n_o
   if (n > 0 && !text_out) return fail(SFX_EINVAL, "text_out is NULL");
   HIP_OR_RETURN(launch_ring_copy(c->ctl, c->ring, c->cap, text_out, cap, st), "copy launch");
   HIP_OR_RETURN(hipStreamSynchronize(st), "copy wait");
+  return SFX_OK;
+}
+
+int sfx_accept_estimate(sfx_ctx* c, int32_t B, int32_t* est_ppm, void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (B < 0) return fail(SFX_EINVAL, "negative B");
+  if (B > c->cfg.max_batch) return fail(SFX_ECAPACITY, "B=%d above max_batch=%d", B,
+                                        c->cfg.max_batch);
+  if (B == 0) return SFX_OK;
+  if (!est_ppm) return fail(SFX_EINVAL, "NULL array argument");
+  HIP_OR_RETURN(launch_accept_estimate(B, c->cfg.k, c->pick, c->accept, est_ppm,
+                                       (hipStream_t)stream), "estimate launch");
+  return SFX_OK;
+}
+
+int sfx_accept_feedback(sfx_ctx* c, int32_t B, const int32_t* num_accepted, void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (B < 0) return fail(SFX_EINVAL, "negative B");
+  if (B > c->cfg.max_batch) return fail(SFX_ECAPACITY, "B=%d above max_batch=%d", B,
+                                        c->cfg.max_batch);
+  if (B == 0) return SFX_OK;
+  if (!num_accepted) return fail(SFX_EINVAL, "NULL array argument");
+  HIP_OR_RETURN(launch_accept_feedback(B, c->pick, num_accepted, c->accept, (hipStream_t)stream),
+                "feedback launch");
+  return SFX_OK;
+}
+
+int sfx_accept_reset(sfx_ctx* c, void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  const int rows = c->cfg.max_batch > 0 ? c->cfg.max_batch : 1;
+  HIP_OR_RETURN(launch_accept_reset(c->accept, c->pick, rows, (hipStream_t)stream),
+                "reset launch");
+  return SFX_OK;
+}
+
+int sfx_accept_counts(sfx_ctx* c, uint64_t* counts, void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!counts) return fail(SFX_EINVAL, "NULL array argument");
+  HIP_OR_RETURN(hipMemcpyAsync(counts, c->accept, sizeof(unsigned long long) * kAcceptEntries,
+                               hipMemcpyDeviceToDevice, (hipStream_t)stream),
+                "counts copy");
   return SFX_OK;
 }
 

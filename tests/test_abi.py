@@ -73,6 +73,10 @@ def test_null_arguments_rejected(sfx):
     assert L.sfx_build_suffix_array(None, 0, None, None, 0, None) == sfx.OK
     assert L.sfx_save(None, b"/nonexistent", None) == sfx.EINVAL
     assert L.sfx_ingest_inflight(None, 1, None, None, None, None, 1, 1, 1, None) == sfx.EINVAL
+    assert L.sfx_accept_estimate(None, 1, None, None) == sfx.EINVAL
+    assert L.sfx_accept_feedback(None, 1, None, None) == sfx.EINVAL
+    assert L.sfx_accept_reset(None, None) == sfx.EINVAL
+    assert L.sfx_accept_counts(None, None, None) == sfx.EINVAL
     assert L.sfx_load(None, b"/nonexistent", None) == sfx.EINVAL
     # an empty update is a no-op that touches nothing
     assert L.sfx_update_state(0, 4, 1, None, None, None, None, None) == sfx.OK

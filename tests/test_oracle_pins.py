@@ -404,3 +404,25 @@ def test_inflight_ingest_invariants(orc):
             cat = np.concatenate(chunks) if chunks else np.zeros(0, np.int32)
             assert cat.tolist() == resp.tolist()
             assert all(len(c) >= max(mc, 1) for c in chunks[:-1])
+
+
+def test_accept_model_hand_values(orc):
+    """Acceptance estimate (vLLM docs, adaptive verification): values worked by hand from
+    Laplace's rule, (accepted + 1) / (proposed + 2) in ppm, with prefix acceptance."""
+    m = orc.AcceptModel()
+    m.record([(1, 5, 3), None, (0, 5, 2)])
+    assert m.estimate(3, 4).tolist() == [[500000, 500000, 500000, 0], [0] * 4,
+                                         [500000, 500000, 0, 0]]
+    m.feedback([2, 7, 0])   # row 0 accepts slots 0 and 1 of 3; row 1 has no draft; row 2 none
+    assert m.counts[1, 5, :3].tolist() == [[1, 1], [1, 1], [1, 0]]
+    assert m.counts[0, 5, :2].tolist() == [[1, 0], [1, 0]]
+    m.feedback([3, 3, 3])   # consumed: nothing more is counted
+    assert int(m.counts.sum()) == 3 + 2 + 2
+    m.record([(1, 5, 3)])
+    # slot 0: 2/3 -> 666666; slot 2: 1/3 -> 333333
+    assert m.estimate(1, 3).tolist() == [[666666, 666666, 333333]]
+    for _ in range(8):      # eight more fully accepted drafts: (9 + 1) / (9 + 2)
+        m.record([(1, 5, 1)])
+        m.feedback([1])
+    m.record([(1, 5, 1)])
+    assert m.estimate(1, 2).tolist() == [[10 * 1000000 // 11, 0]]
