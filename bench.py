@@ -81,6 +81,65 @@ def copy_calibration(torch, dev, mib, reps):
     del src, dst
 
 
+def event_ms(torch, stream, fn, reps):
+    """Mean milliseconds of fn() over reps back-to-back calls, HIP events on `stream`."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def graph_calls_per_s(torch, d, bufs, draft, nv, per_graph=32, replays=60):
+    """The same rotating calls captured once in a HIP graph (per_graph propose launches over
+    successive buffers) and replayed: per-call launch overhead removed."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(per_graph):
+            b = bufs[i % len(bufs)]
+            d.propose(b[0], b[1], b[2], draft, nv, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cur = torch.cuda.current_stream()
+        for i in range(per_graph):
+            b = bufs[i % len(bufs)]
+            d.propose(b[0], b[1], b[2], draft, nv, cur)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    ms = event_ms(torch, stream, g.replay, replays)
+    return per_graph / (ms * 1e-3)
+
+
+def other_workloads(torch, sfx, W, dev, calls=200):
+    """Workloads 1-3 (self match, self match + template corpus) in calls/s, one resident input
+    set each."""
+    out = {}
+    stream = torch.cuda.current_stream()
+    for cid in (1, 2, 3):
+        w = W.WORKLOADS[cid]
+        n, tok, samp = W.make_batch(cid)
+        dn, dt, ds = (torch.from_numpy(x).to(dev) for x in (n, tok, samp))
+        d = sfx.Drafter(sfx.Config(max_batch=w.B, max_seq=w.S, max_sampled=w.T,
+                                   corpus_capacity=(1 << 20) if w.corpus else 0, **w.knobs()))
+        if w.corpus:
+            d.ingest_docs(W.corpus_docs(cid))
+            d.rebuild()
+        draft = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+        nv = torch.empty((w.B,), dtype=torch.int32, device=dev)
+        fn = lambda: d.propose(dn, dt, ds, draft, nv, stream)  # noqa: E731
+        event_ms(torch, stream, fn, 20)
+        out[w.name] = round(1e3 / event_ms(torch, stream, fn, calls), 1)
+        d.close()
+    return out
+
+
 def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
     """The ingest-and-rebuild workload: a ring of 2^22 tokens seeded with the template corpus;
     every step harvests 256 finished rows of U[512,2048] tokens; propose runs at B=512, S=32768,
@@ -299,6 +358,12 @@ def main():
             e1.record(stream)
             e1.synchronize()
             lst.append(e0.elapsed_time(e1))
+    graph_cps = graph_calls_per_s(torch, d, bufs, draft, nv)
+    single = 1e3 / event_ms(torch, stream, lambda: d.propose(bufs[0][0], bufs[0][1], bufs[0][2],
+                                                             draft, nv, stream), 500)
+    others = other_workloads(torch, sfx, W, dev)
+    log(f"[bench] graph-captured {graph_cps:.0f} calls/s; one resident buffer {single:.0f} "
+        f"calls/s; {others}")
     load = None if args.no_ingest_load else ingest_under_load(torch, sfx, W, dev)
 
     # ---------------------------------------------------------------- oracle baseline
@@ -352,6 +417,9 @@ def main():
                   "index_rebuild_ms": None if rebuild_s is None else round(rebuild_s * 1e3, 2),
                   "index_rebuild_tokens_per_s":
                       None if not rebuild_s else round(corpus_n / rebuild_s, 1),
+                  "graph_captured_calls_per_s": round(graph_cps, 1),
+                  "single_buffer_calls_per_s": round(single, 1),
+                  "workloads_calls_per_s": others,
                   "accept_estimate_us": round(float(np.mean(est_ms)) * 1e3, 2),
                   "accept_feedback_us": round(float(np.mean(fb_ms)) * 1e3, 2),
                   "ingest_under_load": load},
