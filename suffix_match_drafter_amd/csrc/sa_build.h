@@ -14,6 +14,7 @@ struct SaWork {
   int32_t* rank;
   int32_t* head;
   int32_t* aux;
+  int32_t* act;  // positions (in suffix-array order) of the suffixes still sharing a rank
   int32_t* hist;
   int32_t* tiles;
   uint32_t* counters;

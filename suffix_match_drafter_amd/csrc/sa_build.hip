@@ -11,7 +11,10 @@
 // The sort is an LSD radix sort with 8-bit digits: per-tile digit histograms, one exclusive
 // scan in digit-major order, then a stable scatter in which each wavefront ranks equal digits
 // with eight ballots.  Keys of a round pack both ranks into 2*bits(n) bits so only the needed
-// digits are sorted.
+// digits are sorted.  A suffix whose rank is already unique keeps its place in every later
+// round, so after the first sort each round sorts only the suffixes of groups of two or more:
+// they are compacted in suffix-array order, sorted by (group rank, rank at i + h), and written
+// back into the same positions, which their groups still occupy.
 #include "sa_build.h"
 
 #include <algorithm>
@@ -299,6 +302,50 @@ __global__ void pair_keys_kernel(const int32_t* v, const int32_t* rank, int64_t 
   k[j] = (r1 << bits) | r2;
 }
 
+// cnt[j] = 1 when position j's group has two or more members (heads: nonzero at group starts).
+__global__ void active_flags_kernel(const int32_t* head, int64_t n, int32_t* cnt) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  const bool single = head[j] != 0 && (j + 1 == n || head[j + 1] != 0);
+  cnt[j] = single ? 0 : 1;
+}
+
+// incl[j]: active positions in [0, j].  The t-th active position gets its suffix i, the key
+// (rank[i] << bits) | rank[i + h] (0 past the end), and its position.
+__global__ void gather_active_kernel(const int32_t* incl, const int32_t* sa, const int32_t* rank,
+                                     int64_t n, int64_t h, int bits, int32_t* act, uint64_t* k,
+                                     int32_t* v) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  const int c = incl[j];
+  if (c == (j ? incl[j - 1] : 0)) return;  // not active
+  const int t = c - 1;
+  const int64_t i = sa[j];
+  const uint64_t r1 = (uint32_t)rank[i];
+  const uint64_t r2 = i + h < n ? (uint32_t)rank[i + h] : 0u;
+  k[t] = (r1 << bits) | r2;
+  v[t] = (int32_t)i;
+  act[t] = (int32_t)j;
+}
+
+// The sorted active suffixes back into their positions; a new group starts wherever the key
+// changes, and hv[t] = position + 1 at a start (else 0) for the max scan that ranks them.
+__global__ void scatter_back_kernel(const int32_t* act, const uint64_t* k, const int32_t* v,
+                                    int64_t m, int32_t* sa, int32_t* head, int32_t* hv) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= m) return;
+  const int32_t p = act[t];
+  sa[p] = v[t];
+  const bool start = t == 0 || k[t] != k[t - 1];
+  head[p] = start ? p + 1 : 0;
+  hv[t] = start ? p + 1 : 0;
+}
+
+__global__ void rerank_kernel(const int32_t* v, const int32_t* hmax, int64_t m, int32_t* rank) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < m) rank[v[t]] = hmax[t];
+}
+
 __global__ void copy_i32_kernel(const int32_t* a, int32_t* b, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) b[i] = a[i];
@@ -319,7 +366,7 @@ size_t sa_workspace_bytes(int64_t n) {
   size_t b = 0;
   b += 2 * sizeof(uint64_t) * (size_t)nn;        // k0, k1
   b += 2 * sizeof(int32_t) * (size_t)nn;         // v0, v1
-  b += 3 * sizeof(int32_t) * (size_t)nn;         // rank, head, aux
+  b += 4 * sizeof(int32_t) * (size_t)nn;         // rank, head, aux, act
   b += sizeof(int32_t) * (size_t)(256 * nt + 64);  // hist
   b += sizeof(int32_t) * (size_t)(cdiv(256 * nt + nn, SC_TILE) + 64);  // scan tiles
   b += 256;                                      // counters
@@ -344,6 +391,7 @@ SaWork sa_carve(void* ws, int64_t n) {
   w.rank = (int32_t*)take(sizeof(int32_t) * nn);
   w.head = (int32_t*)take(sizeof(int32_t) * nn);
   w.aux = (int32_t*)take(sizeof(int32_t) * nn);
+  w.act = (int32_t*)take(sizeof(int32_t) * nn);
   w.hist = (int32_t*)take(sizeof(int32_t) * (256 * nt + 64));
   w.tiles = (int32_t*)take(sizeof(int32_t) * (cdiv(256 * nt + nn, SC_TILE) + 64));
   w.counters = (uint32_t*)take(256);
@@ -375,33 +423,36 @@ hipError_t sa_build(const int32_t* text, int64_t n, int32_t* sa, const SaWork& w
   if (e != hipSuccess) return e;
   uint64_t* kc = which ? w.k1 : w.k0;
   int32_t* vc = which ? w.v1 : w.v0;
-  uint64_t* ko = which ? w.k0 : w.k1;
-  int32_t* vo = which ? w.v0 : w.v1;
+  // round 0 ranks: groups of equal first tokens
+  hipLaunchKernelGGL(copy_i32_kernel, dim3(gb), dim3(TB), 0, st, vc, sa, n);
+  hipLaunchKernelGGL(heads_kernel, dim3(gb), dim3(TB), 0, st, kc, n, w.head, w.counters + 8);
+  if ((e = scan_i32<1, 1>(w.head, w.aux, n, w.tiles, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL(rank_kernel, dim3(gb), dim3(TB), 0, st, vc, w.aux, n, w.rank);
   const int rbits = bits_for((uint64_t)n);
-  int rounds = 0;
-  for (int64_t h = 0;; h = h ? 2 * h : 1) {
-    if (h > 0) {
-      hipLaunchKernelGGL(pair_keys_kernel, dim3(gb), dim3(TB), 0, st, vc, w.rank, n, h, rbits, kc);
-      e = radix_sort<uint64_t>(kc, vc, ko, vo, n, 2 * rbits, w.hist, w.tiles, &which, st);
-      if (e != hipSuccess) return e;
-      if (which) {
-        std::swap(kc, ko);
-        std::swap(vc, vo);
-      }
-    }
-    ++rounds;
-    if ((e = hipMemsetAsync(w.counters + 8, 0, sizeof(uint32_t), st)) != hipSuccess) return e;
-    hipLaunchKernelGGL(heads_kernel, dim3(gb), dim3(TB), 0, st, kc, n, w.head, w.counters + 8);
-    if ((e = scan_i32<1, 1>(w.head, w.aux, n, w.tiles, st)) != hipSuccess) return e;
-    hipLaunchKernelGGL(rank_kernel, dim3(gb), dim3(TB), 0, st, vc, w.aux, n, w.rank);
-    uint32_t dup = 0;
-    if ((e = hipMemcpyAsync(&dup, w.counters + 8, sizeof(dup), hipMemcpyDeviceToHost, st)) !=
+  int rounds = 1;
+  for (int64_t h = 1;; h *= 2) {
+    // the suffixes still sharing a rank, and how many
+    hipLaunchKernelGGL(active_flags_kernel, dim3(gb), dim3(TB), 0, st, w.head, n, w.aux);
+    if ((e = scan_i32<0, 1>(w.aux, w.aux, n, w.tiles, st)) != hipSuccess) return e;
+    int32_t m = 0;
+    if ((e = hipMemcpyAsync(&m, w.aux + (n - 1), sizeof(m), hipMemcpyDeviceToHost, st)) !=
         hipSuccess)
       return e;
     if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
-    if (!dup || h >= n) break;
+    if (m == 0 || h >= n) break;
+    hipLaunchKernelGGL(gather_active_kernel, dim3(gb), dim3(TB), 0, st, w.aux, sa, w.rank, n, h,
+                       rbits, w.act, w.k0, w.v0);
+    e = radix_sort<uint64_t>(w.k0, w.v0, w.k1, w.v1, m, 2 * rbits, w.hist, w.tiles, &which, st);
+    if (e != hipSuccess) return e;
+    const uint64_t* ks = which ? w.k1 : w.k0;
+    const int32_t* vs = which ? w.v1 : w.v0;
+    const int64_t gm = cdiv(m, TB);
+    hipLaunchKernelGGL(scatter_back_kernel, dim3(gm), dim3(TB), 0, st, w.act, ks, vs, m, sa,
+                       w.head, w.aux);
+    if ((e = scan_i32<1, 1>(w.aux, w.aux, m, w.tiles, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(rerank_kernel, dim3(gm), dim3(TB), 0, st, vs, w.aux, m, w.rank);
+    ++rounds;
   }
-  hipLaunchKernelGGL(copy_i32_kernel, dim3(gb), dim3(TB), 0, st, vc, sa, n);
   if (rounds_out) *rounds_out = rounds;
   return hipGetLastError();
 }
