@@ -292,16 +292,6 @@ __global__ void rank_kernel(const int32_t* v, const int32_t* headmax, int64_t n,
   if (j < n) rank[v[j]] = headmax[j];
 }
 
-__global__ void pair_keys_kernel(const int32_t* v, const int32_t* rank, int64_t n, int64_t h,
-                                 int bits, uint64_t* k) {
-  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= n) return;
-  const int64_t i = v[j];
-  const uint64_t r1 = (uint32_t)rank[i];
-  const uint64_t r2 = i + h < n ? (uint32_t)rank[i + h] : 0u;
-  k[j] = (r1 << bits) | r2;
-}
-
 // cnt[j] = 1 when position j's group has two or more members (heads: nonzero at group starts).
 __global__ void active_flags_kernel(const int32_t* head, int64_t n, int32_t* cnt) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -460,34 +450,42 @@ hipError_t sa_build(const int32_t* text, int64_t n, int32_t* sa, const SaWork& w
 // ------------------------------------------------------------------ n-gram probe tables
 namespace {
 
-// For SA position j: does suffix sa[j] start an n-gram occurrence that is followed by a token?
-__device__ __forceinline__ bool ngram_ok(const int32_t* text, int64_t n, int64_t i, int ng) {
-  if (i + ng >= n) return false;
-  for (int x = 0; x <= ng; ++x)
-    if (text[i + x] < 0) return false;
-  return true;
-}
-
-__global__ void ng_flags_kernel(const int32_t* text, const int32_t* sa, int64_t n, int ng,
-                                int32_t* valid, int32_t* head) {
+// The flags of all three n-gram lengths from one gather of each suffix's first kNG + 2 tokens
+// (and its suffix-array predecessor's): bit g of flags[j] = the (g+2)-gram at sa[j] continues,
+// bit 8 + g = it also starts a group (its predecessor's differs or does not continue).
+__global__ void ng_flags_kernel(const int32_t* text, const int32_t* sa, int64_t n,
+                                int32_t* flags) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= n) return;
+  constexpr int W = kNG + 2;  // tokens that decide the longest n-gram and its continuation
   const int64_t i = sa[j];
-  const bool ok = ngram_ok(text, n, i, ng);
-  bool hd = false;
-  if (ok) {
-    hd = true;
-    if (j > 0) {
-      const int64_t p = sa[j - 1];
-      if (ngram_ok(text, n, p, ng)) {
-        bool same = true;
-        for (int x = 0; x < ng; ++x) same = same && text[p + x] == text[i + x];
-        hd = !same;
-      }
-    }
+  int t[W], q[W];
+#pragma unroll
+  for (int x = 0; x < W; ++x) t[x] = i + x < n ? text[i + x] : -1;
+  const int64_t p = j > 0 ? sa[j - 1] : -1;
+#pragma unroll
+  for (int x = 0; x < W; ++x) q[x] = p >= 0 && p + x < n ? text[p + x] : -1;
+  int f = 0;
+  bool okt = t[0] >= 0 && t[1] >= 0, okq = q[0] >= 0 && q[1] >= 0, same = t[0] == q[0];
+#pragma unroll
+  for (int g = 0; g < kNG; ++g) {
+    const int ng = g + 2;
+    okt = okt && t[ng] >= 0;      // tokens 0..ng real: the n-gram and its next token
+    okq = okq && q[ng] >= 0;
+    same = same && t[ng - 1] == q[ng - 1];
+    if (okt) f |= 1 << g;
+    if (okt && !(okq && same)) f |= 1 << (8 + g);
   }
-  valid[j] = ok ? 1 : 0;
-  head[j] = hd ? 1 : 0;
+  flags[j] = f;
+}
+
+__global__ void ng_unpack_kernel(const int32_t* flags, int64_t n, int g, int32_t* valid,
+                                 int32_t* head) {
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  const int f = flags[j];
+  valid[j] = (f >> g) & 1;
+  head[j] = (f >> (8 + g)) & 1;
 }
 
 // At each group head: record the group's offset in the position list by group id.
@@ -566,9 +564,10 @@ hipError_t ngram_tables_build(const int32_t* text, const int32_t* sa, int64_t n,
   int32_t* ngroups = (int32_t*)(w.counters + 16);
   const int kbits = bits_for((uint64_t)n);
   hipError_t e;
+  hipLaunchKernelGGL(ng_flags_kernel, dim3(gb), dim3(TB), 0, st, text, sa, n, w.act);
   for (int g = 0; g < kNG; ++g) {
     const int ng = g + 2;
-    hipLaunchKernelGGL(ng_flags_kernel, dim3(gb), dim3(TB), 0, st, text, sa, n, ng, valid, head);
+    hipLaunchKernelGGL(ng_unpack_kernel, dim3(gb), dim3(TB), 0, st, w.act, n, g, valid, head);
     if ((e = scan_i32<0, 1>(head, gid, n, w.tiles, st)) != hipSuccess) return e;
     if ((e = scan_i32<0, 0>(valid, cval, n, w.tiles, st)) != hipSuccess) return e;
     hipLaunchKernelGGL(ng_heads_kernel, dim3(gb), dim3(TB), 0, st, head, gid, cval, n, goff);
