@@ -240,8 +240,10 @@ int sfx_save(sfx_ctx* ctx, const char* path, void* stream);
  * structure and the suffix array (a permutation) are checked on the host before anything is
  * copied.  SFX_EIO for a file that cannot be read, is truncated, has trailing bytes, a wrong
  * magic or checksum, or inconsistent contents (the context is then unchanged); SFX_EINVAL for a
- * capacity mismatch; SFX_ESTATE without a corpus or with an asynchronous rebuild in flight.
- * Synchronises `stream`. */
+ * capacity mismatch; SFX_ESTATE without a corpus or with an asynchronous rebuild in flight or
+ * finished but not yet swapped in (sfx_wait_rebuild first).  The in-flight ingest cursors and
+ * the acceptance counts belong to the serving batch, not to the corpus: they are neither
+ * saved nor replaced.  Synchronises `stream`. */
 int sfx_load(sfx_ctx* ctx, const char* path, void* stream);
 
 /* Suffix array (suffix-gpu page, Highlights and References: Manber & Myers prefix doubling):
