@@ -380,6 +380,7 @@ def main():
 
     # ---------------------------------------------------------------- oracle baseline
     cpu = None
+    cpu_extra = None
     if not args.no_cpu_baseline:
         import oracle as O
 
@@ -400,6 +401,21 @@ def main():
                          f"{len(sets)} input sets, {dt:.1f}s wall, OpenMP over rows, "
                          f"{O.BUILD_FLAGS}"}
         log(f"[bench] oracle: {calls} calls in {dt:.1f}s on {cores} cores")
+        # one core, on the first 32 rows of one input set (scaled to whole calls), and the
+        # oracle's suffix array (single-threaded comparison sort) of the same corpus
+        n, tok, samp = sets[0]
+        t3 = time.time()
+        O.propose(p, n[:32], tok[:32], samp[:32], corpus=corpus, num_threads=1)
+        one_core = (32 / w.B) / (time.time() - t3)
+        cpu_sa = None
+        if corpus is not None:
+            t3 = time.time()
+            O.suffix_array(corpus)
+            cpu_sa = len(corpus) / (time.time() - t3)
+        cpu_extra = {"oracle_calls_per_s_1core": round(one_core, 4),
+                     "oracle_1core_sample": f"rows 0-31 of one input set, scaled to B={w.B}",
+                     "oracle_suffix_array_tokens_per_s":
+                         None if cpu_sa is None else round(cpu_sa, 1)}
 
     out = {
         "metric": "propose calls/s at B=256,S=16K,1M-token corpus; % of HBM roofline",
@@ -434,7 +450,8 @@ def main():
                   "workloads_calls_per_s": others,
                   "accept_estimate_us": round(float(np.mean(est_ms)) * 1e3, 2),
                   "accept_feedback_us": round(float(np.mean(fb_ms)) * 1e3, 2),
-                  "ingest_under_load": load},
+                  "ingest_under_load": load,
+                  "cpu_oracle_more": cpu_extra},
     }
     print(json.dumps(out), flush=True)
     d.close()
