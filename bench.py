@@ -155,7 +155,8 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
     n, tok, samp = W.make_batch(5)
     dn, dt, ds = (torch.from_numpy(x).to(dev) for x in (n, tok, samp))
     batches = []
-    for st in range(warm_steps + steps):
+    sync_reps = 5  # synchronous rebuilds, each after a harvest of new documents
+    for st in range(warm_steps + steps + sync_reps):
         itok, rows, lens = W.ingest_batch(5, st)
         batches.append((torch.from_numpy(rows).to(dev), torch.from_numpy(lens).to(dev),
                         torch.from_numpy(itok).to(dev), int(lens.sum())))
@@ -203,8 +204,8 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
         step_ms.append((time.time() - ts) * 1e3)
         p_live.append(timed(prop, calls))
     # the rebuild alone: synchronous, nothing else on the GPU, after one more harvest each
-    for st in range(5):
-        rows, lens, itok, _ = batches[(warm_steps + st) % len(batches)]
+    for st in range(sync_reps):
+        rows, lens, itok, _ = batches[warm_steps + steps + st]
         d.harvest_finished(rows, lens, itok, stream)
         torch.cuda.synchronize()
         tr = time.time()
