@@ -116,6 +116,17 @@ int sfx_propose(sfx_ctx* ctx, int32_t B, int32_t S, int32_t T, const int32_t* nu
                 const int32_t* token_ids, const int32_t* sampled, int32_t* draft,
                 int32_t* num_valid, void* stream);
 
+/* The masked form (suffix-gpu page, Quickstart: propose(num_tokens_no_spec, token_ids,
+ * combined_mask), for callers that keep token_ids up to date themselves).  Row b's context is
+ * token_ids[b, 0:clamp(n_b, 0, S)] alone; mask [B] (device int32) selects the rows to draft:
+ * a row with mask[b] == 0, or an empty row, gets no draft (num_valid 0, all -1).  Otherwise as
+ * sfx_propose, with the context's last token in the role of the last sampled id (LONGEST_FILL
+ * fills with it).  Needs max_sampled >= 1 (else SFX_ECAPACITY); uses context-owned scratch,
+ * so it neither synchronises nor allocates. */
+int sfx_propose_masked(sfx_ctx* ctx, int32_t B, int32_t S, const int32_t* num_tokens_no_spec,
+                       const int32_t* token_ids, const int32_t* mask, int32_t* draft,
+                       int32_t* num_valid, void* stream);
+
 /* State update (suffix-gpu page, Quickstart: propose_with_update).  Writes the leading
  * non-negative sampled ids of row b after its clamped prefix, as many as fit in S, and stores
  * the new length in num_tokens_out[b].  token_ids is modified in place.  Needs no context. */

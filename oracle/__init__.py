@@ -227,6 +227,26 @@ def propose(params: Params, num_tokens, token_ids, sampled, corpus=None, num_thr
     return draft, nv
 
 
+def propose_masked(params: Params, num_tokens, token_ids, mask, corpus=None, num_threads=1):
+    """The masked form (PyPI page "suffix-gpu 0.1.1", Quickstart: propose(num_tokens_no_spec,
+    token_ids, combined_mask)): row b's context is token_ids[b, 0:clamp(n_b, 0, S)] alone, and
+    rows with mask 0 get no draft.  Reading taken: otherwise the drafter step as usual, the
+    context's last token taking the role of the last sampled id (fill, C-14)."""
+    tok = _i32(token_ids)
+    B, S = tok.shape
+    n = np.clip(np.asarray(num_tokens, np.int64), 0, S)
+    m = np.asarray(mask)
+    prefix = np.zeros(B, np.int32)
+    last = np.full((B, 1), -1, np.int32)
+    for b in range(B):
+        if m[b] != 0 and n[b] > 0:
+            prefix[b] = n[b] - 1
+            last[b, 0] = tok[b, n[b] - 1]
+        else:
+            prefix[b] = n[b]
+    return propose(params, prefix, tok, last, corpus=corpus, num_threads=num_threads)
+
+
 def update_state(token_ids, num_tokens, sampled):
     tok = _i32(token_ids).copy()
     samp = _i32(sampled)

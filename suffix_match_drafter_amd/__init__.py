@@ -24,11 +24,12 @@ _NAMES = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", ECAPACITY: "ECAPACITY", EHIP: "EHI
           ESTATE: "ESTATE", EIO: "EIO"}
 
 # every entry point declared in include/sfx.h
-EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_update_state",
-           "sfx_harvest_finished", "sfx_ingest_inflight", "sfx_ingest", "sfx_rebuild",
-           "sfx_rebuild_async", "sfx_poll", "sfx_wait_rebuild", "sfx_accept_estimate",
-           "sfx_accept_feedback", "sfx_accept_reset", "sfx_accept_counts", "sfx_corpus_snapshot", "sfx_save", "sfx_load",
-           "sfx_suffix_array_workspace_bytes", "sfx_build_suffix_array")
+EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_propose_masked",
+           "sfx_update_state", "sfx_harvest_finished", "sfx_ingest_inflight", "sfx_ingest",
+           "sfx_rebuild", "sfx_rebuild_async", "sfx_poll", "sfx_wait_rebuild",
+           "sfx_accept_estimate", "sfx_accept_feedback", "sfx_accept_reset", "sfx_accept_counts",
+           "sfx_corpus_snapshot", "sfx_save", "sfx_load", "sfx_suffix_array_workspace_bytes",
+           "sfx_build_suffix_array")
 
 
 FLAG_STREAM_CONTEXT = 1  # read contexts from device memory instead of staging them in LDS
@@ -104,6 +105,7 @@ def load(path: str = LIB_PATH):
         "sfx_destroy": (None, [_V]),
         "sfx_last_error": (ctypes.c_char_p, []),
         "sfx_propose": (ctypes.c_int, [_V, _I32, _I32, _I32, _V, _V, _V, _V, _V, _V]),
+        "sfx_propose_masked": (ctypes.c_int, [_V, _I32, _I32, _V, _V, _V, _V, _V, _V]),
         "sfx_update_state": (ctypes.c_int, [_I32, _I32, _I32, _V, _V, _V, _V, _V]),
         "sfx_harvest_finished": (ctypes.c_int, [_V, _I32, _V, _V, _V, _I32, _I32, _V]),
         "sfx_ingest": (ctypes.c_int, [_V, _I32, _V, _V, _V]),
@@ -191,6 +193,23 @@ class Drafter:
             raise ValueError("draft must be [B,k] and num_valid [B]")
         _check(load().sfx_propose(self._h, B, S, samp.shape[1], _ptr(nt), _ptr(tok), _ptr(samp),
                                   _ptr(draft), _ptr(num_valid), _stream(stream)))
+        return draft, num_valid
+
+    def propose_masked(self, num_tokens, token_ids, mask, draft=None, num_valid=None,
+                       stream=None):
+        """The masked form: contexts are the rows themselves; rows with mask 0 get no draft."""
+        tok = _i32(token_ids, "token_ids", 2)
+        B, S = tok.shape
+        nt = _i32(num_tokens, "num_tokens_no_spec", 1)
+        m = _i32(mask, "mask", 1)
+        if nt.shape[0] != B or m.shape[0] != B:
+            raise ValueError("num_tokens_no_spec, mask and token_ids disagree on B")
+        if draft is None:
+            draft = torch.empty((B, self.cfg.k), dtype=torch.int32, device=tok.device)
+        if num_valid is None:
+            num_valid = torch.empty((B,), dtype=torch.int32, device=tok.device)
+        _check(load().sfx_propose_masked(self._h, B, S, _ptr(nt), _ptr(tok), _ptr(m),
+                                         _ptr(draft), _ptr(num_valid), _stream(stream)))
         return draft, num_valid
 
     def propose_with_update(self, num_tokens, token_ids, sampled, stream=None):

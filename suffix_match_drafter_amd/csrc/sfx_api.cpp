@@ -17,6 +17,7 @@
 #include "../../include/sfx.h"
 #include "accept.h"
 #include "corpus.h"
+#include "masked.h"
 #include "propose.h"
 #include "sa_build.h"
 
@@ -60,6 +61,7 @@ struct sfx_ctx {
   sfx_config cfg{};
   int device = 0;
   int32_t* pick = nullptr;                 // [max_batch] winner of each row's last propose
+  int32_t* masked = nullptr;               // [2 * max_batch] prefix lengths, sampled ids
   unsigned long long* accept = nullptr;    // acceptance counts (accept.h layout)
   // corpus (absent when corpus_capacity == 0)
   Ctl* ctl = nullptr;
@@ -136,6 +138,7 @@ void free_ctx(sfx_ctx* c) {
     if (p) (void)hipFree(p);
   };
   f(c->pick);
+  f(c->masked);
   f(c->accept);
   f(c->ctl);
   f(c->ring);
@@ -322,6 +325,7 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
   {
     const int rows = cfg->max_batch > 0 ? cfg->max_batch : 1;
     if (hipMalloc((void**)&c->pick, 4 * (size_t)rows) != hipSuccess ||
+        hipMalloc((void**)&c->masked, 8 * (size_t)rows) != hipSuccess ||
         hipMalloc((void**)&c->accept, sizeof(unsigned long long) * kAcceptEntries) != hipSuccess) {
       free_ctx(c);
       return fail(SFX_ENOMEM, "device allocation failed for the acceptance table");
@@ -426,6 +430,26 @@ int sfx_propose(sfx_ctx* c, int32_t B, int32_t S, int32_t T, const int32_t* ntns
   a.pick = c->pick;
   HIP_OR_RETURN(launch_propose(a, (hipStream_t)stream), "propose launch");
   return SFX_OK;
+}
+
+int sfx_propose_masked(sfx_ctx* c, int32_t B, int32_t S, const int32_t* ntns,
+                       const int32_t* tok, const int32_t* mask, int32_t* draft,
+                       int32_t* nvalid, void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  const sfx_config& g = c->cfg;
+  if (B < 0 || S < 0) return fail(SFX_EINVAL, "negative shape B=%d S=%d", B, S);
+  if (B > g.max_batch || S > g.max_seq || g.max_sampled < 1)
+    return fail(SFX_ECAPACITY, "shape B=%d S=%d above max_batch=%d max_seq=%d (or max_sampled 0)",
+                B, S, g.max_batch, g.max_seq);
+  if (B == 0) return SFX_OK;
+  if (!ntns || !mask || !draft || !nvalid || (S > 0 && !tok))
+    return fail(SFX_EINVAL, "NULL array argument");
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* n2 = c->masked;
+  int32_t* s2 = c->masked + g.max_batch;
+  HIP_OR_RETURN(launch_masked_prep(B, S, ntns, tok, mask, n2, s2, st), "masked prep launch");
+  return sfx_propose(c, B, S, 1, n2, tok, s2, draft, nvalid, stream);
 }
 
 int sfx_update_state(int32_t B, int32_t S, int32_t T, int32_t* tok, const int32_t* ntns,

@@ -426,3 +426,33 @@ def test_accept_model_hand_values(orc):
         m.feedback([1])
     m.record([(1, 5, 1)])
     assert m.estimate(1, 2).tolist() == [[10 * 1000000 // 11, 0]]
+
+
+def test_masked_form_matches_updated_state(orc):
+    """The masked form (PyPI page, Quickstart: propose(num_tokens_no_spec, token_ids,
+    combined_mask)) after the state update equals the ordinary step on the state before it: the
+    update writes the sampled id at n, and the masked call reads it back as the context's last
+    token.  Rows with mask 0, and empty rows, get no draft."""
+    rng = np.random.default_rng(29)
+    for mode, nb in ((0, 1), (1, 3)):
+        kn = dict(k=6, max_tree_depth=8, num_backoff=nb, max_occurrences=16, mode=mode,
+                  spec_factor_ppm=3_000_000, min_token_prob_ppm=100_000)
+        p = orc.params_from(kn)
+        B, S, V = 12, 80, 4
+        tok = rng.integers(0, V, size=(B, S)).astype(np.int32)
+        n = rng.integers(0, S, size=B).astype(np.int32)
+        samp = rng.integers(0, V, size=(B, 1)).astype(np.int32)
+        corpus = orc.LiveCorpus(1000)
+        corpus.ingest([rng.integers(0, V, size=30).astype(np.int32) for _ in range(5)])
+        exp_d, exp_n = orc.propose(p, n, tok, samp, corpus=corpus.text())
+        tok2, n2 = orc.update_state(tok, n, samp)
+        mask = np.ones(B, np.int32)
+        got_d, got_n = orc.propose_masked(p, n2, tok2, mask, corpus=corpus.text())
+        assert np.array_equal(got_d, exp_d) and np.array_equal(got_n, exp_n)
+        mask[::3] = 0
+        got_d, got_n = orc.propose_masked(p, n2, tok2, mask, corpus=corpus.text())
+        assert (got_d[::3] == -1).all() and (got_n[::3] == 0).all()
+        keep = mask != 0
+        assert np.array_equal(got_d[keep], exp_d[keep]) and np.array_equal(got_n[keep], exp_n[keep])
+        empty = orc.propose_masked(p, np.zeros(B, np.int32), tok2, np.ones(B, np.int32))
+        assert (empty[0] == -1).all() and (empty[1] == 0).all()

@@ -426,3 +426,46 @@ def test_ring_eviction_and_delta(S):
     d.wait_rebuild()
     torch.cuda.synchronize()
     d.close()
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+def test_masked_form(S, flags):
+    """sfx_propose_masked (PyPI page, Quickstart: propose(num_tokens_no_spec, token_ids,
+    combined_mask)) against the oracle's masked form, with a corpus, random masks and empty
+    rows; and, on the GPU alone, the masked call after update_state equals the ordinary call
+    on the state before it."""
+    import torch
+
+    rng = np.random.default_rng(57)
+    V, B, Sq = 6, 40, 300
+    docs = [rng.integers(0, V, size=int(rng.integers(1, 90))).astype(np.int32)
+            for _ in range(30)]
+    text = W.join_docs(docs)
+    for mode, nb in ((0, 1), (1, 4)):
+        kn = dict(k=10, max_tree_depth=12, num_backoff=nb, max_occurrences=64, mode=mode,
+                  spec_factor_ppm=2_000_000, min_token_prob_ppm=100_000)
+        p = O.params_from(kn)
+        cfg = S.Config(max_batch=B, max_seq=Sq, max_sampled=1, corpus_capacity=1 << 14,
+                       flags=flags, **kn)
+        d = S.Drafter(cfg)
+        d.ingest_docs(docs)
+        d.rebuild()
+        tok = rng.integers(0, V, size=(B, Sq)).astype(np.int32)
+        n = rng.integers(-2, Sq + 3, size=B).astype(np.int32)
+        n[:3] = 0
+        mask = (rng.random(B) < 0.7).astype(np.int32)
+        gd, gn = d.propose_masked(dev(n), dev(tok), dev(mask))
+        torch.cuda.synchronize()
+        exp = O.propose_masked(p, n, tok, mask, corpus=text)
+        assert_same((gd.cpu().numpy(), gn.cpu().numpy()), exp, f"masked mode {mode}")
+        # after the state update, the masked call equals the ordinary one before it
+        n0 = rng.integers(0, Sq, size=B).astype(np.int32)
+        samp = rng.integers(0, V, size=(B, 1)).astype(np.int32)
+        td = dev(tok)
+        od, on = d.propose(dev(n0), td, dev(samp))
+        n1 = S.update_state(td, dev(n0), dev(samp))
+        md, mn = d.propose_masked(n1, td, dev(np.ones(B, np.int32)))
+        torch.cuda.synchronize()
+        assert np.array_equal(od.cpu().numpy(), md.cpu().numpy())
+        assert np.array_equal(on.cpu().numpy(), mn.cpu().numpy())
+        d.close()
