@@ -127,6 +127,18 @@ int sfx_propose_masked(sfx_ctx* ctx, int32_t B, int32_t S, const int32_t* num_to
                        const int32_t* token_ids, const int32_t* mask, int32_t* draft,
                        int32_t* num_valid, void* stream);
 
+/* The counted form (RFC page, Design: the ngram_gpu contract propose(k, num_tokens_no_spec,
+ * token_ids, sampled, counts) -> (drafts [B,k], valid counts [B])).  counts [B] (device int32)
+ * is the number of valid entries of sampled[b], clamped to [0, T], in place of the -1 padding:
+ * the context appends sampled[b, 0:counts[b]] up to its first negative entry.  k is this
+ * call's draft width, 1 .. the configured k (else SFX_EINVAL / SFX_ECAPACITY): draft is [B, k]
+ * and the SCORED cap is taken against it.  Otherwise as sfx_propose; uses context-owned
+ * scratch, so it neither synchronises nor allocates. */
+int sfx_propose_counts(sfx_ctx* ctx, int32_t k, int32_t B, int32_t S, int32_t T,
+                       const int32_t* num_tokens_no_spec, const int32_t* token_ids,
+                       const int32_t* sampled, const int32_t* counts, int32_t* draft,
+                       int32_t* num_valid, void* stream);
+
 /* State update (suffix-gpu page, Quickstart: propose_with_update).  Writes the leading
  * non-negative sampled ids of row b after its clamped prefix, as many as fit in S, and stores
  * the new length in num_tokens_out[b].  token_ids is modified in place.  Needs no context. */

@@ -247,6 +247,23 @@ def propose_masked(params: Params, num_tokens, token_ids, mask, corpus=None, num
     return propose(params, prefix, tok, last, corpus=corpus, num_threads=num_threads)
 
 
+def propose_counts(params: Params, k, num_tokens, token_ids, sampled, counts, corpus=None,
+                   num_threads=1):
+    """The counted form (RFC page "[RFC]: Suffix decoding on GPU (suffix_gpu)", Design: the
+    ngram_gpu contract propose(k, num_tokens_no_spec, token_ids, sampled, counts)).  Reading
+    taken: counts[b], clamped to [0, T], is the number of valid entries of sampled[b] in place of
+    the -1 padding, and k is the call's draft width (the spec cap of SCORED mode is taken
+    against it)."""
+    samp = _i32(sampled)
+    B, T = samp.shape
+    c = np.clip(np.asarray(counts, np.int64), 0, T)
+    cut = np.where(np.arange(T)[None, :] < c[:, None], samp, -1).astype(np.int32)
+    pk = Params()
+    ctypes.memmove(ctypes.byref(pk), ctypes.byref(params), ctypes.sizeof(Params))
+    pk.k = int(k)
+    return propose(pk, num_tokens, token_ids, cut, corpus=corpus, num_threads=num_threads)
+
+
 def update_state(token_ids, num_tokens, sampled):
     tok = _i32(token_ids).copy()
     samp = _i32(sampled)

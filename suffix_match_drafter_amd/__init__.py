@@ -25,6 +25,7 @@ _NAMES = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", ECAPACITY: "ECAPACITY", EHIP: "EHI
 
 # every entry point declared in include/sfx.h
 EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_propose_masked",
+           "sfx_propose_counts",
            "sfx_update_state", "sfx_harvest_finished", "sfx_ingest_inflight", "sfx_ingest",
            "sfx_rebuild", "sfx_rebuild_async", "sfx_poll", "sfx_wait_rebuild",
            "sfx_accept_estimate", "sfx_accept_feedback", "sfx_accept_reset", "sfx_accept_counts",
@@ -106,6 +107,8 @@ def load(path: str = LIB_PATH):
         "sfx_last_error": (ctypes.c_char_p, []),
         "sfx_propose": (ctypes.c_int, [_V, _I32, _I32, _I32, _V, _V, _V, _V, _V, _V]),
         "sfx_propose_masked": (ctypes.c_int, [_V, _I32, _I32, _V, _V, _V, _V, _V, _V]),
+        "sfx_propose_counts": (ctypes.c_int, [_V, _I32, _I32, _I32, _I32, _V, _V, _V, _V, _V,
+                                              _V, _V]),
         "sfx_update_state": (ctypes.c_int, [_I32, _I32, _I32, _V, _V, _V, _V, _V]),
         "sfx_harvest_finished": (ctypes.c_int, [_V, _I32, _V, _V, _V, _I32, _I32, _V]),
         "sfx_ingest": (ctypes.c_int, [_V, _I32, _V, _V, _V]),
@@ -210,6 +213,25 @@ class Drafter:
             num_valid = torch.empty((B,), dtype=torch.int32, device=tok.device)
         _check(load().sfx_propose_masked(self._h, B, S, _ptr(nt), _ptr(tok), _ptr(m),
                                          _ptr(draft), _ptr(num_valid), _stream(stream)))
+        return draft, num_valid
+
+    def propose_counts(self, k, num_tokens, token_ids, sampled, counts, draft=None,
+                       num_valid=None, stream=None):
+        """The counted form: counts[b] valid entries of sampled[b]; drafts of width k."""
+        tok = _i32(token_ids, "token_ids", 2)
+        B, S = tok.shape
+        samp = _i32(sampled, "sampled", 2)
+        nt = _i32(num_tokens, "num_tokens_no_spec", 1)
+        cnt = _i32(counts, "counts", 1)
+        if samp.shape[0] != B or nt.shape[0] != B or cnt.shape[0] != B:
+            raise ValueError("num_tokens_no_spec, token_ids, sampled and counts disagree on B")
+        if draft is None:
+            draft = torch.empty((B, k), dtype=torch.int32, device=tok.device)
+        if num_valid is None:
+            num_valid = torch.empty((B,), dtype=torch.int32, device=tok.device)
+        _check(load().sfx_propose_counts(self._h, int(k), B, S, samp.shape[1], _ptr(nt),
+                                         _ptr(tok), _ptr(samp), _ptr(cnt), _ptr(draft),
+                                         _ptr(num_valid), _stream(stream)))
         return draft, num_valid
 
     def propose_with_update(self, num_tokens, token_ids, sampled, stream=None):

@@ -1,4 +1,5 @@
-// masked.h -- launch interface of the masked form's preparation kernel (internal to libsfx).
+// call_forms.h -- launch interface of the preparation kernels of the other call forms of the
+// drafter step (internal to libsfx).
 #pragma once
 
 #include "sfx_internal.h"
@@ -10,5 +11,9 @@ namespace sfx {
 hipError_t launch_masked_prep(int B, int S, const int32_t* ntns, const int32_t* tok,
                               const int32_t* mask, int32_t* n_out, int32_t* s_out,
                               hipStream_t st);
+
+// The counted form: sampled ids cut at counts[b] (clamped to [0, T]) and -1 padded.
+hipError_t launch_counts_prep(int B, int T, const int32_t* sampled, const int32_t* counts,
+                              int32_t* s_out, hipStream_t st);
 
 }  // namespace sfx

@@ -17,7 +17,7 @@
 #include "../../include/sfx.h"
 #include "accept.h"
 #include "corpus.h"
-#include "masked.h"
+#include "call_forms.h"
 #include "propose.h"
 #include "sa_build.h"
 
@@ -62,6 +62,7 @@ struct sfx_ctx {
   int device = 0;
   int32_t* pick = nullptr;                 // [max_batch] winner of each row's last propose
   int32_t* masked = nullptr;               // [2 * max_batch] prefix lengths, sampled ids
+  int32_t* counted = nullptr;              // [max_batch * max_sampled] cut sampled ids
   unsigned long long* accept = nullptr;    // acceptance counts (accept.h layout)
   // corpus (absent when corpus_capacity == 0)
   Ctl* ctl = nullptr;
@@ -139,6 +140,7 @@ void free_ctx(sfx_ctx* c) {
   };
   f(c->pick);
   f(c->masked);
+  f(c->counted);
   f(c->accept);
   f(c->ctl);
   f(c->ring);
@@ -326,6 +328,9 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
     const int rows = cfg->max_batch > 0 ? cfg->max_batch : 1;
     if (hipMalloc((void**)&c->pick, 4 * (size_t)rows) != hipSuccess ||
         hipMalloc((void**)&c->masked, 8 * (size_t)rows) != hipSuccess ||
+        hipMalloc((void**)&c->counted,
+                  4 * (size_t)rows * (cfg->max_sampled > 0 ? cfg->max_sampled : 1)) !=
+            hipSuccess ||
         hipMalloc((void**)&c->accept, sizeof(unsigned long long) * kAcceptEntries) != hipSuccess) {
       free_ctx(c);
       return fail(SFX_ENOMEM, "device allocation failed for the acceptance table");
@@ -389,11 +394,12 @@ void sfx_destroy(sfx_ctx* c) {
   free_ctx(c);
 }
 
-int sfx_propose(sfx_ctx* c, int32_t B, int32_t S, int32_t T, const int32_t* ntns,
-                const int32_t* tok, const int32_t* samp, int32_t* draft, int32_t* nvalid,
-                void* stream) {
-  int rc = check_ctx(c);
-  if (rc) return rc;
+}  // extern "C"
+
+// The drafter step with draft width k (at most the configured one), after argument checks.
+static int propose_k(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
+                     const int32_t* ntns, const int32_t* tok, const int32_t* samp,
+                     int32_t* draft, int32_t* nvalid, void* stream) {
   const sfx_config& g = c->cfg;
   if (B < 0 || S < 0 || T < 0) return fail(SFX_EINVAL, "negative shape B=%d S=%d T=%d", B, S, T);
   if (B > g.max_batch || S > g.max_seq || T > g.max_sampled)
@@ -411,7 +417,7 @@ int sfx_propose(sfx_ctx* c, int32_t B, int32_t S, int32_t T, const int32_t* ntns
   a.samp = samp;
   a.draft = draft;
   a.nvalid = nvalid;
-  a.k = g.k;
+  a.k = k;
   a.D = g.max_tree_depth;
   a.nb = g.num_backoff;
   a.M = g.max_occurrences;
@@ -432,6 +438,16 @@ int sfx_propose(sfx_ctx* c, int32_t B, int32_t S, int32_t T, const int32_t* ntns
   return SFX_OK;
 }
 
+extern "C" {
+
+int sfx_propose(sfx_ctx* c, int32_t B, int32_t S, int32_t T, const int32_t* ntns,
+                const int32_t* tok, const int32_t* samp, int32_t* draft, int32_t* nvalid,
+                void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  return propose_k(c, c->cfg.k, B, S, T, ntns, tok, samp, draft, nvalid, stream);
+}
+
 int sfx_propose_masked(sfx_ctx* c, int32_t B, int32_t S, const int32_t* ntns,
                        const int32_t* tok, const int32_t* mask, int32_t* draft,
                        int32_t* nvalid, void* stream) {
@@ -449,7 +465,25 @@ int sfx_propose_masked(sfx_ctx* c, int32_t B, int32_t S, const int32_t* ntns,
   int32_t* n2 = c->masked;
   int32_t* s2 = c->masked + g.max_batch;
   HIP_OR_RETURN(launch_masked_prep(B, S, ntns, tok, mask, n2, s2, st), "masked prep launch");
-  return sfx_propose(c, B, S, 1, n2, tok, s2, draft, nvalid, stream);
+  return propose_k(c, g.k, B, S, 1, n2, tok, s2, draft, nvalid, stream);
+}
+
+int sfx_propose_counts(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
+                       const int32_t* ntns, const int32_t* tok, const int32_t* sampled,
+                       const int32_t* counts, int32_t* draft, int32_t* nvalid, void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (k < 1) return fail(SFX_EINVAL, "k=%d below 1", k);
+  if (k > c->cfg.k) return fail(SFX_ECAPACITY, "k=%d above the configured k=%d", k, c->cfg.k);
+  if (B < 0 || T < 0) return fail(SFX_EINVAL, "negative shape B=%d T=%d", B, T);
+  if (B > c->cfg.max_batch || T > c->cfg.max_sampled)
+    return fail(SFX_ECAPACITY, "shape B=%d T=%d above max_batch=%d max_sampled=%d", B, T,
+                c->cfg.max_batch, c->cfg.max_sampled);
+  if (B == 0) return SFX_OK;
+  if (!counts || (T > 0 && !sampled)) return fail(SFX_EINVAL, "NULL array argument");
+  HIP_OR_RETURN(launch_counts_prep(B, T, sampled, counts, c->counted, (hipStream_t)stream),
+                "counts prep launch");
+  return propose_k(c, k, B, S, T, ntns, tok, c->counted, draft, nvalid, stream);
 }
 
 int sfx_update_state(int32_t B, int32_t S, int32_t T, int32_t* tok, const int32_t* ntns,

@@ -75,6 +75,8 @@ def test_null_arguments_rejected(sfx):
     assert L.sfx_ingest_inflight(None, 1, None, None, None, None, 1, 1, 1, None) == sfx.EINVAL
     assert L.sfx_accept_estimate(None, 1, None, None) == sfx.EINVAL
     assert L.sfx_propose_masked(None, 1, 4, None, None, None, None, None, None) == sfx.EINVAL
+    assert L.sfx_propose_counts(None, 1, 1, 4, 1, None, None, None, None, None, None,
+                                None) == sfx.EINVAL
     assert L.sfx_accept_feedback(None, 1, None, None) == sfx.EINVAL
     assert L.sfx_accept_reset(None, None) == sfx.EINVAL
     assert L.sfx_accept_counts(None, None, None) == sfx.EINVAL

@@ -456,3 +456,34 @@ def test_masked_form_matches_updated_state(orc):
         assert np.array_equal(got_d[keep], exp_d[keep]) and np.array_equal(got_n[keep], exp_n[keep])
         empty = orc.propose_masked(p, np.zeros(B, np.int32), tok2, np.ones(B, np.int32))
         assert (empty[0] == -1).all() and (empty[1] == 0).all()
+
+
+def test_counted_form(orc):
+    """The counted form (RFC page, Design: propose(k, num_tokens_no_spec, token_ids, sampled,
+    counts)): counts equal to the padding's own count reproduce the ordinary step; entries past
+    counts are ignored; in LONGEST_FILL mode (no score, no cap but k) a narrower k gives the
+    first k tokens of the wider draft."""
+    rng = np.random.default_rng(31)
+    B, S, T, V = 10, 60, 3, 4
+    tok = rng.integers(0, V, size=(B, S)).astype(np.int32)
+    n = rng.integers(0, S + 1, size=B).astype(np.int32)
+    samp = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    lead = rng.integers(0, T + 1, size=B)
+    for b in range(B):
+        samp[b, lead[b]:] = -1
+    for mode, nb in ((0, 1), (1, 3)):
+        kn = dict(k=8, max_tree_depth=8, num_backoff=nb, max_occurrences=16, mode=mode,
+                  spec_factor_ppm=3_000_000, min_token_prob_ppm=100_000)
+        p = orc.params_from(kn)
+        exp = orc.propose(p, n, tok, samp)
+        got = orc.propose_counts(p, 8, n, tok, samp, lead)
+        assert np.array_equal(got[0], exp[0]) and np.array_equal(got[1], exp[1])
+        junk = samp.copy()
+        junk[junk < 0] = 3  # entries past counts are never read
+        got = orc.propose_counts(p, 8, n, tok, junk, lead)
+        assert np.array_equal(got[0], exp[0]) and np.array_equal(got[1], exp[1])
+        if mode == 0:
+            for k in (1, 3, 5):
+                d, nv = orc.propose_counts(p, k, n, tok, samp, lead)
+                assert np.array_equal(d, exp[0][:, :k])
+                assert np.array_equal(nv, np.minimum(exp[1], k))

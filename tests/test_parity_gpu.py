@@ -469,3 +469,41 @@ def test_masked_form(S, flags):
         assert np.array_equal(od.cpu().numpy(), md.cpu().numpy())
         assert np.array_equal(on.cpu().numpy(), mn.cpu().numpy())
         d.close()
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+def test_counted_form(S, flags):
+    """sfx_propose_counts (RFC page, Design: propose(k, num_tokens_no_spec, token_ids, sampled,
+    counts)) against the oracle's counted form: counts below, at and above the valid entries,
+    negative counts, non-negative junk past the count, and every call width k up to the
+    configured one, in both modes, with a corpus."""
+    import torch
+
+    rng = np.random.default_rng(61)
+    V, B, Sq, T = 6, 36, 200, 3
+    docs = [rng.integers(0, V, size=int(rng.integers(1, 70))).astype(np.int32)
+            for _ in range(25)]
+    text = W.join_docs(docs)
+    for mode, nb in ((0, 1), (1, 4)):
+        kn = dict(k=12, max_tree_depth=10, num_backoff=nb, max_occurrences=64, mode=mode,
+                  spec_factor_ppm=1_500_000, min_token_prob_ppm=100_000)
+        p = O.params_from(kn)
+        cfg = S.Config(max_batch=B, max_seq=Sq, max_sampled=T, corpus_capacity=1 << 14,
+                       flags=flags, **kn)
+        d = S.Drafter(cfg)
+        d.ingest_docs(docs)
+        d.rebuild()
+        tok = rng.integers(0, V, size=(B, Sq)).astype(np.int32)
+        n = rng.integers(0, Sq + 1, size=B).astype(np.int32)
+        samp = rng.integers(0, V, size=(B, T)).astype(np.int32)
+        samp[rng.random((B, T)) < 0.15] = -1
+        counts = rng.integers(-1, T + 2, size=B).astype(np.int32)
+        for k in (1, 5, 12):
+            gd, gn = d.propose_counts(k, dev(n), dev(tok), dev(samp), dev(counts))
+            torch.cuda.synchronize()
+            exp = O.propose_counts(p, k, n, tok, samp, counts, corpus=text)
+            assert_same((gd.cpu().numpy(), gn.cpu().numpy()), exp, f"counted k={k} mode {mode}")
+        with pytest.raises(S.SfxError) as ei:
+            d.propose_counts(13, dev(n), dev(tok), dev(samp), dev(counts))
+        assert ei.value.code == S.ECAPACITY
+        d.close()
