@@ -62,10 +62,25 @@ enum {
 };
 
 enum {
-  SFX_FLAG_STREAM_CONTEXT = 1 /* sfx_propose reads each context from device memory instead of
-                                 staging it in the workgroup's LDS (same results).  Without it a
-                                 row is staged when it fits (max_seq up to about 19K tokens) and
-                                 streamed otherwise. */
+  SFX_FLAG_STREAM_CONTEXT = 1, /* sfx_propose reads each context from device memory instead of
+                                  staging it in the workgroup's LDS (same results).  Without it
+                                  a row is staged when it fits (max_seq up to about 19K tokens)
+                                  and streamed otherwise. */
+  SFX_FLAG_CHECK_INPUTS = 2    /* the propose and ingest calls also launch a check of their
+                                  device-resident inputs that sets SFX_ERR_* bits in the
+                                  context's error word (sfx_debug_errors); results do not
+                                  change */
+};
+
+/* Bits of the sticky device error word.  Each names an input that the device clamps or ignores
+ * because the host cannot see it without a synchronisation; the calls' results follow the
+ * documented clamping either way. */
+enum {
+  SFX_ERR_LENGTH = 1,            /* a length outside [0, S] (num_tokens_no_spec, lengths,
+                                    counts outside [0, T]) or a decreasing document offset */
+  SFX_ERR_NEGATIVE_TOKEN = 2,    /* a negative id inside a row prefix or a document */
+  SFX_ERR_SAMPLED_AFTER_PAD = 4, /* a non-negative sampled id after a negative one (ignored) */
+  SFX_ERR_ROW_INDEX = 8          /* an ingest row index outside the rows (ignored) */
 };
 
 typedef struct sfx_config {
@@ -268,6 +283,12 @@ int sfx_save(sfx_ctx* ctx, const char* path, void* stream);
  * the acceptance counts belong to the serving batch, not to the corpus: they are neither
  * saved nor replaced.  Synchronises `stream`. */
 int sfx_load(sfx_ctx* ctx, const char* path, void* stream);
+
+/* The optional debug call for the clamping convention of the device-resident inputs: waits for
+ * `stream`, stores the context's sticky error word (SFX_ERR_* bits raised since the last read)
+ * in *bits_out (host memory) and clears it.  The word is only written by calls of a context
+ * created with SFX_FLAG_CHECK_INPUTS; otherwise it reads 0.  Synchronises `stream`. */
+int sfx_debug_errors(sfx_ctx* ctx, uint32_t* bits_out, void* stream);
 
 /* Suffix array (suffix-gpu page, Highlights and References: Manber & Myers prefix doubling):
  * sa[r] = start of the r-th smallest suffix of text[0:n], tokens compared as signed int32, a

@@ -29,11 +29,15 @@ EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_pr
            "sfx_update_state", "sfx_harvest_finished", "sfx_ingest_inflight", "sfx_ingest",
            "sfx_rebuild", "sfx_rebuild_async", "sfx_poll", "sfx_wait_rebuild",
            "sfx_accept_estimate", "sfx_accept_feedback", "sfx_accept_reset", "sfx_accept_counts",
-           "sfx_corpus_snapshot", "sfx_save", "sfx_load", "sfx_suffix_array_workspace_bytes",
-           "sfx_build_suffix_array")
+           "sfx_corpus_snapshot", "sfx_save", "sfx_load", "sfx_debug_errors",
+           "sfx_suffix_array_workspace_bytes", "sfx_build_suffix_array")
 
 
 FLAG_STREAM_CONTEXT = 1  # read contexts from device memory instead of staging them in LDS
+FLAG_CHECK_INPUTS = 2    # check device-resident inputs into the sticky error word
+
+# bits of the sticky error word (include/sfx.h)
+ERR_LENGTH, ERR_NEGATIVE_TOKEN, ERR_SAMPLED_AFTER_PAD, ERR_ROW_INDEX = 1, 2, 4, 8
 
 
 class SfxError(RuntimeError):
@@ -124,6 +128,7 @@ def load(path: str = LIB_PATH):
         "sfx_accept_counts": (ctypes.c_int, [_V, _V, _V]),
         "sfx_save": (ctypes.c_int, [_V, ctypes.c_char_p, _V]),
         "sfx_load": (ctypes.c_int, [_V, ctypes.c_char_p, _V]),
+        "sfx_debug_errors": (ctypes.c_int, [_V, ctypes.POINTER(ctypes.c_uint32), _V]),
         "sfx_suffix_array_workspace_bytes": (ctypes.c_size_t, [_I64]),
         "sfx_build_suffix_array": (ctypes.c_int, [_V, _I64, _V, _V, ctypes.c_size_t, _V]),
     }
@@ -329,6 +334,12 @@ class Drafter:
     def load(self, path, stream=None):
         """Replace the corpus with the one saved in `path` (same corpus_capacity)."""
         _check(load().sfx_load(self._h, os.fsencode(path), _stream(stream)))
+
+    def debug_errors(self, stream=None) -> int:
+        """Read and clear the sticky ERR_* bits raised since the last read (synchronises)."""
+        v = ctypes.c_uint32(0)
+        _check(load().sfx_debug_errors(self._h, ctypes.byref(v), _stream(stream)))
+        return v.value
 
     def corpus_snapshot(self, stream=None) -> torch.Tensor:
         cap = max(int(self.cfg.corpus_capacity), 1)

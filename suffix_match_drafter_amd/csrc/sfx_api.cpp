@@ -18,6 +18,7 @@
 #include "accept.h"
 #include "corpus.h"
 #include "call_forms.h"
+#include "checks.h"
 #include "propose.h"
 #include "sa_build.h"
 
@@ -64,6 +65,7 @@ struct sfx_ctx {
   int32_t* masked = nullptr;               // [2 * max_batch] prefix lengths, sampled ids
   int32_t* counted = nullptr;              // [max_batch * max_sampled] cut sampled ids
   unsigned long long* accept = nullptr;    // acceptance counts (accept.h layout)
+  uint32_t* err = nullptr;                 // sticky SFX_ERR_* word (SFX_FLAG_CHECK_INPUTS)
   // corpus (absent when corpus_capacity == 0)
   Ctl* ctl = nullptr;
   int32_t* ring = nullptr;
@@ -129,7 +131,8 @@ int validate(const sfx_config* c) {
       return fail(SFX_EINVAL, "min_corpus_match=%d outside [2, max_tree_depth]",
                   c->min_corpus_match);
   }
-  if (c->flags & ~SFX_FLAG_STREAM_CONTEXT) return fail(SFX_EINVAL, "unknown flags 0x%x", c->flags);
+  if (c->flags & ~(SFX_FLAG_STREAM_CONTEXT | SFX_FLAG_CHECK_INPUTS))
+    return fail(SFX_EINVAL, "unknown flags 0x%x", c->flags);
   if (c->reserved != 0) return fail(SFX_EINVAL, "reserved must be 0");
   return SFX_OK;
 }
@@ -142,6 +145,7 @@ void free_ctx(sfx_ctx* c) {
   f(c->masked);
   f(c->counted);
   f(c->accept);
+  f(c->err);
   f(c->ctl);
   f(c->ring);
   f(c->doc_start);
@@ -195,6 +199,8 @@ int check_ctx(sfx_ctx* c) {
                 dev);
   return SFX_OK;
 }
+
+bool checking(const sfx_ctx* c) { return (c->cfg.flags & SFX_FLAG_CHECK_INPUTS) != 0; }
 
 void finish_async(sfx_ctx* c) {
   if (c->worker.joinable()) c->worker.join();
@@ -331,11 +337,13 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
         hipMalloc((void**)&c->counted,
                   4 * (size_t)rows * (cfg->max_sampled > 0 ? cfg->max_sampled : 1)) !=
             hipSuccess ||
-        hipMalloc((void**)&c->accept, sizeof(unsigned long long) * kAcceptEntries) != hipSuccess) {
+        hipMalloc((void**)&c->accept, sizeof(unsigned long long) * kAcceptEntries) != hipSuccess ||
+        hipMalloc((void**)&c->err, sizeof(uint32_t)) != hipSuccess) {
       free_ctx(c);
       return fail(SFX_ENOMEM, "device allocation failed for the acceptance table");
     }
     if ((e = launch_accept_reset(c->accept, c->pick, rows, nullptr)) != hipSuccess ||
+        (e = launch_clear_word(c->err, nullptr)) != hipSuccess ||
         (e = hipStreamSynchronize(nullptr)) != hipSuccess) {
       free_ctx(c);
       return hip_fail(e, "acceptance table init");
@@ -445,7 +453,11 @@ int sfx_propose(sfx_ctx* c, int32_t B, int32_t S, int32_t T, const int32_t* ntns
                 void* stream) {
   int rc = check_ctx(c);
   if (rc) return rc;
-  return propose_k(c, c->cfg.k, B, S, T, ntns, tok, samp, draft, nvalid, stream);
+  rc = propose_k(c, c->cfg.k, B, S, T, ntns, tok, samp, draft, nvalid, stream);
+  if (rc || !checking(c)) return rc;
+  HIP_OR_RETURN(launch_check_propose(B, S, T, ntns, tok, samp, nullptr, c->err,
+                                     (hipStream_t)stream), "input check launch");
+  return SFX_OK;
 }
 
 int sfx_propose_masked(sfx_ctx* c, int32_t B, int32_t S, const int32_t* ntns,
@@ -465,7 +477,11 @@ int sfx_propose_masked(sfx_ctx* c, int32_t B, int32_t S, const int32_t* ntns,
   int32_t* n2 = c->masked;
   int32_t* s2 = c->masked + g.max_batch;
   HIP_OR_RETURN(launch_masked_prep(B, S, ntns, tok, mask, n2, s2, st), "masked prep launch");
-  return propose_k(c, g.k, B, S, 1, n2, tok, s2, draft, nvalid, stream);
+  rc = propose_k(c, g.k, B, S, 1, n2, tok, s2, draft, nvalid, stream);
+  if (rc || !checking(c)) return rc;
+  HIP_OR_RETURN(launch_check_propose(B, S, 0, ntns, tok, nullptr, nullptr, c->err, st),
+                "input check launch");
+  return SFX_OK;
 }
 
 int sfx_propose_counts(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
@@ -483,7 +499,11 @@ int sfx_propose_counts(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
   if (!counts || (T > 0 && !sampled)) return fail(SFX_EINVAL, "NULL array argument");
   HIP_OR_RETURN(launch_counts_prep(B, T, sampled, counts, c->counted, (hipStream_t)stream),
                 "counts prep launch");
-  return propose_k(c, k, B, S, T, ntns, tok, c->counted, draft, nvalid, stream);
+  rc = propose_k(c, k, B, S, T, ntns, tok, c->counted, draft, nvalid, stream);
+  if (rc || !checking(c)) return rc;
+  HIP_OR_RETURN(launch_check_propose(B, S, T, ntns, tok, sampled, counts, c->err,
+                                     (hipStream_t)stream), "input check launch");
+  return SFX_OK;
 }
 
 int sfx_update_state(int32_t B, int32_t S, int32_t T, int32_t* tok, const int32_t* ntns,
@@ -535,6 +555,9 @@ int sfx_harvest_finished(sfx_ctx* c, int32_t R, const int32_t* rows, const int32
   a.num_rows = num_rows;
   a.S = S;
   a.tokens = tok;
+  if (checking(c))
+    HIP_OR_RETURN(launch_check_ingest(R, rows, lengths, num_rows, S, nullptr, tok, c->err,
+                                      (hipStream_t)stream), "input check launch");
   return ingest_common(c, a, S, (hipStream_t)stream);
 }
 
@@ -550,6 +573,9 @@ int sfx_ingest(sfx_ctx* c, int32_t num_docs, const int64_t* offs, const int32_t*
   a.R = num_docs;
   a.doc_offsets = offs;
   a.tokens = tokens;
+  if (checking(c))
+    HIP_OR_RETURN(launch_check_ingest(num_docs, nullptr, nullptr, 0, 0, offs, tokens, c->err,
+                                      (hipStream_t)stream), "input check launch");
   return ingest_common(c, a, 1 << 16, (hipStream_t)stream);
 }
 
@@ -568,6 +594,9 @@ int sfx_ingest_inflight(sfx_ctx* c, int32_t R, const int32_t* rows, const int32_
     return fail(SFX_EINVAL, "NULL array argument");
   hipStream_t st = (hipStream_t)stream;
   const int mb = c->cfg.max_batch;
+  if (checking(c))
+    HIP_OR_RETURN(launch_check_ingest(R, rows, lengths, num_rows < mb ? num_rows : mb, S, nullptr,
+                                      tok, c->err, st), "input check launch");
   InflightArgs f{};
   f.R = R;
   f.row_indices = rows;
@@ -890,6 +919,20 @@ int sfx_build_suffix_array(const int32_t* text, int64_t n, int32_t* sa, void* ws
                 sa_workspace_bytes(n));
   SaWork w = sa_carve(ws, n);
   HIP_OR_RETURN(sa_build(text, n, sa, w, (hipStream_t)stream, nullptr), "suffix array build");
+  return SFX_OK;
+}
+
+int sfx_debug_errors(sfx_ctx* c, uint32_t* bits_out, void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!bits_out) return fail(SFX_EINVAL, "bits_out is NULL");
+  hipStream_t st = (hipStream_t)stream;
+  uint32_t v = 0;
+  HIP_OR_RETURN(hipMemcpyAsync(&v, c->err, sizeof v, hipMemcpyDeviceToHost, st),
+                "error word read");
+  HIP_OR_RETURN(launch_clear_word(c->err, st), "error word clear");
+  HIP_OR_RETURN(hipStreamSynchronize(st), "error word sync");
+  *bits_out = v;
   return SFX_OK;
 }
 

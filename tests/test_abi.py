@@ -51,7 +51,7 @@ def _cfg(sfx, **kw):
     dict(mode=1, min_token_prob_ppm=-5), dict(corpus_capacity=-1),
     dict(corpus_capacity=(1 << 30) + 1), dict(corpus_capacity=100, max_tree_depth=1),
     dict(corpus_capacity=100, min_corpus_match=1), dict(corpus_capacity=100, min_corpus_match=25),
-    dict(flags=2), dict(reserved=1),
+    dict(flags=4), dict(flags=8), dict(reserved=1),
 ])
 def test_create_rejects_bad_config(sfx, bad):
     L = sfx.load()
@@ -81,6 +81,7 @@ def test_null_arguments_rejected(sfx):
     assert L.sfx_accept_reset(None, None) == sfx.EINVAL
     assert L.sfx_accept_counts(None, None, None) == sfx.EINVAL
     assert L.sfx_load(None, b"/nonexistent", None) == sfx.EINVAL
+    assert L.sfx_debug_errors(None, None, None) == sfx.EINVAL
     # an empty update is a no-op that touches nothing
     assert L.sfx_update_state(0, 4, 1, None, None, None, None, None) == sfx.OK
 
