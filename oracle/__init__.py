@@ -23,6 +23,8 @@ _lib = None
 MODE_LONGEST_FILL = 0
 MODE_SCORED = 1
 MAX_NB = 8
+# bit of a drafter config's `flags` that asks for the tree-depth cap (read by params_from)
+TREE_DEPTH_CAP_FLAG = 4
 
 
 def build(force: bool = True) -> str:
@@ -47,7 +49,7 @@ class Params(ctypes.Structure):
         ("mode", ctypes.c_int32),
         ("min_self_match", ctypes.c_int32),
         ("min_corpus_match", ctypes.c_int32),
-        ("pad_", ctypes.c_int32),
+        ("tree_depth_cap", ctypes.c_int32),
         ("spec_factor_ppm", ctypes.c_int64),
         ("spec_offset_ppm", ctypes.c_int64),
         ("min_token_prob_ppm", ctypes.c_int64),
@@ -124,9 +126,10 @@ def _i32(a) -> np.ndarray:
 
 def make_params(k, max_tree_depth=24, num_backoff=1, max_occurrences=128, mode=MODE_LONGEST_FILL,
                 min_self_match=1, min_corpus_match=2, spec_factor_ppm=1_000_000,
-                spec_offset_ppm=0, min_token_prob_ppm=100_000) -> Params:
+                spec_offset_ppm=0, min_token_prob_ppm=100_000, tree_depth_cap=0) -> Params:
     return Params(k, max_tree_depth, num_backoff, max_occurrences, mode, min_self_match,
-                  min_corpus_match, 0, spec_factor_ppm, spec_offset_ppm, min_token_prob_ppm)
+                  min_corpus_match, int(bool(tree_depth_cap)), spec_factor_ppm, spec_offset_ppm,
+                  min_token_prob_ppm)
 
 
 def params_from(cfg) -> Params:
@@ -137,7 +140,8 @@ def params_from(cfg) -> Params:
                        g("max_occurrences", 128), g("mode", MODE_LONGEST_FILL),
                        g("min_self_match", 1), g("min_corpus_match", 2),
                        g("spec_factor_ppm", 1_000_000), g("spec_offset_ppm", 0),
-                       g("min_token_prob_ppm", 100_000))
+                       g("min_token_prob_ppm", 100_000),
+                       g("tree_depth_cap", 0) or (int(g("flags", 0) or 0) & TREE_DEPTH_CAP_FLAG))
 
 
 # --------------------------------------------------------------------------- building blocks

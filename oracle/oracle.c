@@ -111,12 +111,22 @@ int32_t orc_first_sites(const int32_t* vals, int64_t n, int32_t l, int32_t M, in
 /* Adaptive speculation cap.  SuffixGPU page, Quickstart: cap = factor * match_len + offset;
  * gitcode blog section 4: max_spec_tokens = max_spec_factor * prefix_match_length.  The factor
  * and offset are exact rationals in millionths, so the cap is a floor of an integer ratio,
- * never more than k.  The Model Runner V2 selection does not use it (the draft may be k long). */
+ * never more than k.  The Model Runner V2 selection does not use it (the draft may be k long).
+ * With tree_depth_cap (either mode), the gitcode blog's parameter table in section 4 is read
+ * literally: max_tree_depth bounds the match length plus the draft length, so the cap is also
+ * at most D - l (and not below 0). */
 int32_t orc_spec_cap(const orc_params* p, int32_t l) {
-  if (p->mode != ORC_MODE_SCORED) return p->k;
-  int64_t c = (p->spec_factor_ppm * (int64_t)l + p->spec_offset_ppm) / 1000000;
-  if (c < 0) c = 0;
-  return c < p->k ? (int32_t)c : p->k;
+  int32_t cap = p->k;
+  if (p->mode == ORC_MODE_SCORED) {
+    int64_t c = (p->spec_factor_ppm * (int64_t)l + p->spec_offset_ppm) / 1000000;
+    if (c < 0) c = 0;
+    if (c < cap) cap = (int32_t)c;
+  }
+  if (p->tree_depth_cap) {
+    const int32_t room = p->max_tree_depth - l;
+    if (room < cap) cap = room < 0 ? 0 : room;
+  }
+  return cap;
 }
 
 /* Depth-wise vote.  SuffixGPU page, How it works step 3 and Highlights: continuations are

@@ -32,7 +32,7 @@ typedef struct {
   int32_t mode;              /* ORC_MODE_* */
   int32_t min_self_match;    /* shortest valid self match (>= 1) */
   int32_t min_corpus_match;  /* shortest valid corpus match (>= 2: last-2 probe) */
-  int32_t pad_;
+  int32_t tree_depth_cap;    /* nonzero: match length plus draft length at most D */
   int64_t spec_factor_ppm;   /* max_spec_factor * 1e6 */
   int64_t spec_offset_ppm;   /* max_spec_offset * 1e6 */
   int64_t min_token_prob_ppm;/* min_token_prob * 1e6 */

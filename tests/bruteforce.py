@@ -99,10 +99,14 @@ def propose_row(knobs, row, n, sampled, C=None):
     fill = ctx[-1] if mode == 0 else -1
 
     def cap_of(l):
-        if mode == 0:
-            return k
-        return max(0, min(k, (knobs["spec_factor_ppm"] * l + knobs.get("spec_offset_ppm", 0))
-                          // 10**6))
+        cap = k
+        if mode == 1:
+            cap = max(0, min(k, (knobs["spec_factor_ppm"] * l + knobs.get("spec_offset_ppm", 0))
+                             // 10**6))
+        if knobs.get("tree_depth_cap"):
+            # the tree's depth (match length plus drafted tokens) stays within max_tree_depth
+            cap = min(cap, max(0, D - l))
+        return cap
 
     cands = []
     for ti in range(1, nb + 1):

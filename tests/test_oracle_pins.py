@@ -18,10 +18,10 @@ from tests import bruteforce as bf
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
 
 
-def knobs(k, D=24, nb=1, M=128, mode=0, factor=1_000_000, prob=100_000, offset=0):
+def knobs(k, D=24, nb=1, M=128, mode=0, factor=1_000_000, prob=100_000, offset=0, tree=0):
     return dict(k=k, max_tree_depth=D, num_backoff=nb, max_occurrences=M, mode=mode,
                 spec_factor_ppm=factor, spec_offset_ppm=offset, min_token_prob_ppm=prob,
-                min_self_match=1, min_corpus_match=2)
+                min_self_match=1, min_corpus_match=2, tree_depth_cap=tree)
 
 
 # ------------------------------------------------------------------ hand-worked golden cases
@@ -198,7 +198,7 @@ def test_propose_bruteforce(orc, mode):
         kn = knobs(k, D=D, nb=nb, M=M, mode=mode,
                    factor=int(rng.choice([500_000, 1_000_000, 2_000_000])),
                    prob=int(rng.choice([0, 100_000, 400_000])),
-                   offset=int(rng.choice([0, 1_000_000])))
+                   offset=int(rng.choice([0, 1_000_000])), tree=int(rng.integers(0, 2)))
         tok = rng.integers(0, V, size=(B, S)).astype(np.int32)
         n = rng.integers(-2, S + 3, size=B).astype(np.int32)
         samp = rng.integers(-1, V, size=(B, T)).astype(np.int32)
@@ -487,3 +487,47 @@ def test_counted_form(orc):
                 d, nv = orc.propose_counts(p, k, n, tok, samp, lead)
                 assert np.array_equal(d, exp[0][:, :k])
                 assert np.array_equal(nv, np.minimum(exp[1], k))
+
+
+def test_tree_depth_cap(orc):
+    """Tree-depth cap (gitcode blog, section 4, parameter table: max_tree_depth bounds the match
+    length plus the draft length).  Hand case: the tail "1 2 3" matches at the row start (length
+    3, D = 6), whose continuation 4 5 6 7 8 1 2 3 would fill k = 8 slots; with the cap only
+    D - 3 = 3 tokens remain.  On random rows in LONGEST_FILL mode the winner does not depend on
+    the cap (it is chosen by length), so the capped draft is the uncapped one cut to D - l tokens
+    and filled; in both modes no draft exceeds D - l for its winner's length l."""
+    row = np.array([[1, 2, 3, 4, 5, 6, 7, 8, 1, 2]], np.int32)
+    samp = np.array([[3]], np.int32)
+    n = np.array([10], np.int32)
+    base = knobs(8, D=6)
+    d, nv = orc.propose(orc.params_from(base), n, row, samp)
+    assert d[0].tolist() == [4, 5, 6, 7, 8, 1, 2, 3] and nv[0] == 8
+    d, nv = orc.propose(orc.params_from(dict(base, tree_depth_cap=1)), n, row, samp)
+    assert d[0].tolist() == [4, 5, 6, 3, 3, 3, 3, 3] and nv[0] == 3
+    # the flag bit of a config reaches the same parameter
+    assert orc.params_from(dict(base, flags=orc.TREE_DEPTH_CAP_FLAG)).tree_depth_cap == 1
+
+    rng = np.random.default_rng(33)
+    B, S, V = 16, 80, 3
+    for mode, nb in ((0, 1), (1, 3)):
+        for D in (2, 5, 9, 24):
+            kn = knobs(10, D=D, nb=nb, M=16, mode=mode, factor=4_000_000)
+            tok = rng.integers(0, V, size=(B, S)).astype(np.int32)
+            n = rng.integers(0, S + 1, size=B).astype(np.int32)
+            samp = rng.integers(0, V, size=(B, 1)).astype(np.int32)
+            C = _rand_corpus(rng, V, 6, 0, 30)
+            free = orc.propose(orc.params_from(kn), n, tok, samp, corpus=C, with_info=True)
+            capd = orc.propose(orc.params_from(dict(kn, tree_depth_cap=1)), n, tok, samp,
+                               corpus=C, with_info=True)
+            for b in range(B):
+                r = capd[2][b]
+                if r.chosen >= 0:
+                    assert capd[1][b] <= max(0, D - r.chosen_len)
+                if mode == 0:
+                    l = free[2][b].chosen_len
+                    keep = min(int(free[1][b]), max(0, D - l)) if free[2][b].chosen >= 0 else 0
+                    assert capd[1][b] == keep
+                    fill = capd[0][b][-1] if keep < 10 else None
+                    assert capd[0][b][:keep].tolist() == free[0][b][:keep].tolist()
+                    if fill is not None:
+                        assert (capd[0][b][keep:] == samp[b, 0]).all()
