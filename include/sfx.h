@@ -66,10 +66,15 @@ enum {
                                   staging it in the workgroup's LDS (same results).  Without it
                                   a row is staged when it fits (max_seq up to about 19K tokens)
                                   and streamed otherwise. */
-  SFX_FLAG_CHECK_INPUTS = 2    /* the propose and ingest calls also launch a check of their
+  SFX_FLAG_CHECK_INPUTS = 2,   /* the propose and ingest calls also launch a check of their
                                   device-resident inputs that sets SFX_ERR_* bits in the
                                   context's error word (sfx_debug_errors); results do not
                                   change */
+  SFX_FLAG_TREE_DEPTH_CAP = 4  /* gitcode blog section 4, parameter table: max_tree_depth bounds
+                                  the match length plus the draft length, so a candidate of
+                                  match length l drafts at most max(0, max_tree_depth - l)
+                                  tokens (both modes; off by default, where only the match
+                                  length is bounded) */
 };
 
 /* Bits of the sticky device error word.  Each names an input that the device clamps or ignores

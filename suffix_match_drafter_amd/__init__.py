@@ -35,6 +35,7 @@ EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_pr
 
 FLAG_STREAM_CONTEXT = 1  # read contexts from device memory instead of staging them in LDS
 FLAG_CHECK_INPUTS = 2    # check device-resident inputs into the sticky error word
+FLAG_TREE_DEPTH_CAP = 4  # match length plus draft length at most max_tree_depth
 
 # bits of the sticky error word (include/sfx.h)
 ERR_LENGTH, ERR_NEGATIVE_TOKEN, ERR_SAMPLED_AFTER_PAD, ERR_ROW_INDEX = 1, 2, 4, 8

@@ -13,7 +13,10 @@ struct ProposeArgs {
   int32_t* draft;
   int32_t* nvalid;
   int32_t k, D, nb, M, mode, min_self, min_corpus;
-  int64_t factor_ppm, offset_ppm, prob_ppm;
+  // per-call tables filled on the host: the draft cap of a candidate of match length l,
+  // and the smallest vote count that keeps a chain of c0 sites going (stop rule)
+  uint8_t cap_of_len[kMaxD + 1];
+  uint8_t min_count[kMaxM + 1];
   const Ctl* ctl;  // nullptr when the context has no corpus
   IndexBuf idx[2];
   const int32_t* ring;

@@ -186,13 +186,6 @@ struct Req {
   uint32_t ht_mask;
 };
 
-__device__ __forceinline__ int spec_cap(const ProposeArgs& a, int l) {
-  if (a.mode != 1) return a.k;
-  long long c = (a.factor_ppm * (long long)l + a.offset_ppm) / 1000000;
-  if (c < 0) c = 0;
-  return c < a.k ? (int)c : a.k;
-}
-
 // Flat view of one index buffer.  Separate scalar fields (no arrays) and constant-index
 // selects keep the kernel arguments out of scratch memory.
 struct View {
@@ -496,11 +489,6 @@ __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[
   *snum_out = snum;
 }
 
-// Smallest count c with c / c0 >= min_token_prob (exact: c * 1e6 >= prob_ppm * c0).
-__device__ __forceinline__ int stop_threshold(const ProposeArgs& a, int c0) {
-  if (a.mode != 1) return 0;
-  return (int)((a.prob_ppm * (long long)c0 + 999999) / 1000000);
-}
 
 // The corpus wavefront of the fast path (live snapshot, no delta), first part, run while the
 // other wavefronts stage the context: tail from global memory, the three n-gram probes, the
@@ -1165,7 +1153,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     const int ci = wid;
     const int src = sm.cand_src[ci];
     c0 = sm.cand_c0[ci];
-    cap = spec_cap(a, sm.cand_len[ci]);
+    cap = a.cap_of_len[sm.cand_len[ci]];
     const int s0 = lane, s1 = lane + 64;
     if (ci < nb) {
       const int* ls = sm.lsites[src];
@@ -1209,7 +1197,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     int nout = 0;
     long long snum = 0;
     int* hk = reinterpret_cast<int*>(dyn) + wid * (2 * kVoteSlots);
-    vote_run<KMAX>(w0, w1, c0, cap, stop_threshold(a, c0), hk, hk + kVoteSlots, lane,
+    vote_run<KMAX>(w0, w1, c0, cap, a.min_count[c0], hk, hk + kVoteSlots, lane,
                    sm.cand_out[wid], &nout, &snum);
     if (lane == 0) {
       sm.cand_n[wid] = nout;

@@ -131,7 +131,7 @@ int validate(const sfx_config* c) {
       return fail(SFX_EINVAL, "min_corpus_match=%d outside [2, max_tree_depth]",
                   c->min_corpus_match);
   }
-  if (c->flags & ~(SFX_FLAG_STREAM_CONTEXT | SFX_FLAG_CHECK_INPUTS))
+  if (c->flags & ~(SFX_FLAG_STREAM_CONTEXT | SFX_FLAG_CHECK_INPUTS | SFX_FLAG_TREE_DEPTH_CAP))
     return fail(SFX_EINVAL, "unknown flags 0x%x", c->flags);
   if (c->reserved != 0) return fail(SFX_EINVAL, "reserved must be 0");
   return SFX_OK;
@@ -404,6 +404,31 @@ void sfx_destroy(sfx_ctx* c) {
 
 }  // extern "C"
 
+// The per-length draft cap and the per-c0 stop count of the drafter step (suffix-gpu page, How it
+// works step 3 and Quickstart; gitcode blog section 4): in SCORED mode a candidate of match
+// length l drafts at most floor((factor * l + offset) / 1e6) tokens, and the chain stops at a
+// vote count c with c * 1e6 < min_token_prob * c0.  Both are exact integer ratios, taken here
+// once per call.  With SFX_FLAG_TREE_DEPTH_CAP the match length plus the draft length stays
+// within max_tree_depth.
+static void fill_tables(const sfx_config& g, int32_t k, ProposeArgs* a) {
+  const bool scored = g.mode == SFX_MODE_SCORED;
+  for (int l = 0; l <= kMaxD; ++l) {
+    int64_t cap = k;
+    if (scored) {
+      const int64_t c = (g.spec_factor_ppm * l + g.spec_offset_ppm) / 1000000;
+      if (c < cap) cap = c < 0 ? 0 : c;
+    }
+    if (g.flags & SFX_FLAG_TREE_DEPTH_CAP) {
+      const int64_t room = (int64_t)g.max_tree_depth - l;
+      if (room < cap) cap = room < 0 ? 0 : room;
+    }
+    a->cap_of_len[l] = (uint8_t)cap;
+  }
+  for (int c0 = 0; c0 <= kMaxM; ++c0)
+    a->min_count[c0] =
+        scored ? (uint8_t)((g.min_token_prob_ppm * c0 + 999999) / 1000000) : (uint8_t)0;
+}
+
 // The drafter step with draft width k (at most the configured one), after argument checks.
 static int propose_k(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
                      const int32_t* ntns, const int32_t* tok, const int32_t* samp,
@@ -432,9 +457,7 @@ static int propose_k(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
   a.mode = g.mode;
   a.min_self = g.min_self_match;
   a.min_corpus = g.min_corpus_match;
-  a.factor_ppm = g.spec_factor_ppm;
-  a.offset_ppm = g.spec_offset_ppm;
-  a.prob_ppm = g.min_token_prob_ppm;
+  fill_tables(g, k, &a);
   a.ctl = c->ctl;
   a.idx[0] = c->idx[0];
   a.idx[1] = c->idx[1];

@@ -51,7 +51,7 @@ def _cfg(sfx, **kw):
     dict(mode=1, min_token_prob_ppm=-5), dict(corpus_capacity=-1),
     dict(corpus_capacity=(1 << 30) + 1), dict(corpus_capacity=100, max_tree_depth=1),
     dict(corpus_capacity=100, min_corpus_match=1), dict(corpus_capacity=100, min_corpus_match=25),
-    dict(flags=4), dict(flags=8), dict(reserved=1),
+    dict(flags=8), dict(flags=16), dict(reserved=1),
 ])
 def test_create_rejects_bad_config(sfx, bad):
     L = sfx.load()

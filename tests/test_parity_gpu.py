@@ -122,6 +122,46 @@ def test_fuzz_with_corpus(S, mode, flags):
 
 
 @pytest.mark.parametrize("flags", FLAGS)
+@pytest.mark.parametrize("mode", [0, 1])
+def test_tree_depth_cap(S, mode, flags):
+    """SFX_FLAG_TREE_DEPTH_CAP (gitcode blog, section 4: match length plus draft length at most
+    max_tree_depth) on random rows with a corpus, and in the counted form with a narrower k:
+    drafts equal the oracle's with the same cap."""
+    import torch
+
+    rng = np.random.default_rng(400 + mode)
+    for it in range(12):
+        V = int(rng.choice([2, 3, 6]))
+        B, Sq = int(rng.integers(1, 9)), int(rng.integers(2, 160))
+        nb = 1 if mode == 0 else int(rng.integers(1, 6))
+        D = int(rng.choice([2, 4, 7, 12, 24]))
+        kn = dict(k=int(rng.integers(1, 33)), max_tree_depth=D, num_backoff=nb,
+                  max_occurrences=int(rng.choice([2, 16, 128])), mode=mode,
+                  spec_factor_ppm=int(rng.choice([1_000_000, 4_000_000])),
+                  min_token_prob_ppm=int(rng.choice([0, 100_000])))
+        f = flags | S.FLAG_TREE_DEPTH_CAP
+        docs = [rng.integers(0, V, size=int(rng.integers(0, 50))).astype(np.int32)
+                for _ in range(int(rng.integers(1, 30)))]
+        lc = O.LiveCorpus(10**7)
+        lc.ingest(docs)
+        tok = rng.integers(0, V, size=(B, Sq)).astype(np.int32)
+        n = rng.integers(0, Sq + 1, size=B).astype(np.int32)
+        samp = rng.integers(0, V, size=(B, 1)).astype(np.int32)
+        p = O.params_from(dict(kn, flags=f))
+        assert p.tree_depth_cap == 1
+        exp = O.propose(p, n, tok, samp, corpus=lc.text())
+        got = run_gpu(S, kn, n, tok, samp, corpus_docs=docs, capacity=1 << 14, flags=f)
+        assert_same(got[:2], exp, f"tree cap it={it} kn={kn} flags={f}")
+        k2 = int(rng.integers(1, kn["k"] + 1))
+        cnt = np.ones(B, np.int32)
+        dd, dn = got[2].propose_counts(k2, dev(n), dev(tok), dev(samp), dev(cnt))
+        torch.cuda.synchronize()
+        exp2 = O.propose_counts(p, k2, n, tok, samp, cnt, corpus=lc.text())
+        assert_same((dd.cpu().numpy(), dn.cpu().numpy()), exp2, f"tree cap counts it={it} k={k2}")
+        got[2].close()
+
+
+@pytest.mark.parametrize("flags", FLAGS)
 def test_degenerate_rows(S, flags):
     """Empty rows, rows with no sampled token, a single repeated token (every position
     matches), n above S, S not a multiple of 4, T=0."""
