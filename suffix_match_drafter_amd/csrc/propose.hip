@@ -165,7 +165,7 @@ struct Smem {
   int g_off[kNG], g_live[kNG];
   int cand_len[2 * kMaxNB], cand_sup[2 * kMaxNB], cand_c0[2 * kMaxNB], cand_valid[2 * kMaxNB];
   int cand_src[2 * kMaxNB], cand_n[2 * kMaxNB];
-  long long cand_snum[2 * kMaxNB];
+  int cand_snum[2 * kMaxNB];  // at most k * M = 4096
   int cand_out[2 * kMaxNB][kMaxK];
   int lsites[kMaxNB][kMaxM];
   long long gsites[kMaxNB][kMaxM];
@@ -284,14 +284,14 @@ __device__ __forceinline__ int extend4(const int32_t* text, const int* tail, int
   return m;
 }
 
-// Corpus token at logical position q: snapshot text below snap_end, else ring slot `slot`
-// (q mod ring capacity, which the caller steps along instead of dividing each time).
-__device__ __forceinline__ int corpus_at(const ProposeArgs& a, const int32_t* text,
-                                         long long snap_start, long long snap_n, long long q,
-                                         int slot) {
-  long long s = q - snap_start;
-  if (s >= 0 && s < snap_n) return text[s];
-  return a.ring[slot];
+// Address of the corpus token at logical position q: snapshot text below snap_end, else ring slot
+// `slot` (q mod ring capacity, which the caller steps along instead of dividing each time).  A
+// choice of pointer, so that the load itself is unconditional.
+__device__ __forceinline__ const int32_t* corpus_ptr(const ProposeArgs& a, const int32_t* text,
+                                                     long long snap_start, long long snap_n,
+                                                     long long q, int slot) {
+  const long long s = q - snap_start;
+  return (s >= 0 && s < snap_n) ? text + s : a.ring + slot;
 }
 
 __device__ __forceinline__ int ring_next(int r, int cap) { return r + 1 == cap ? 0 : r + 1; }
@@ -386,10 +386,10 @@ __device__ __forceinline__ void delta_scan_wave(const ProposeArgs& a, long long 
 template <int KMAX>
 __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[KMAX], int c0,
                                          int cap, int cmin, int* hk, int* hc, int lane, int* out,
-                                         int* n_out, long long* snum_out) {
+                                         int* n_out, int* snum_out) {
   bool al0 = lane < c0, al1 = lane + 64 < c0;
   int nout = 0;
-  long long snum = 0;
+  int snum = 0;  // at most k * M, so every product below fits 32 bits
   bool done = false;
   int tokv = -1;  // lane i collects the i-th voted token
   bool site0 = true;  // site 0 (lane 0, first half) is still on the voted path
@@ -1178,24 +1178,27 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       bool live0 = s0 < c0, live1 = s1 < c0;
       const int rcap = (int)a.ring_cap;
       int r0 = (int)(q0 % a.ring_cap), r1 = (int)(q1 % a.ring_cap);
+      // every window token is loaded at once (each address is a live snapshot position or a
+      // ring slot, so always in bounds); a site's window then ends at its first separator
 #pragma unroll
       for (int d = 0; d < KMAX; ++d) {
-        int x0 = -1, x1 = -1;
-        if (live0 && d < cap) x0 = corpus_at(a, text, ss, sn, q0 + d, r0);
-        if (live1 && d < cap) x1 = corpus_at(a, text, ss, sn, q1 + d, r1);
+        w0[d] = *corpus_ptr(a, text, ss, sn, q0 + d, r0);
+        w1[d] = *corpus_ptr(a, text, ss, sn, q1 + d, r1);
         r0 = ring_next(r0, rcap);
         r1 = ring_next(r1, rcap);
-        live0 = live0 && x0 >= 0;
-        live1 = live1 && x1 >= 0;
-        w0[d] = x0;
-        w1[d] = x1;
+      }
+#pragma unroll
+      for (int d = 0; d < KMAX; ++d) {
+        live0 = live0 && d < cap && w0[d] >= 0;
+        live1 = live1 && d < cap && w1[d] >= 0;
+        w0[d] = live0 ? w0[d] : -1;
+        w1[d] = live1 ? w1[d] : -1;
       }
     }
   }
   __syncthreads();  // the context and the hit lists are dead from here on: vote tables
   if (voter) {
-    int nout = 0;
-    long long snum = 0;
+    int nout = 0, snum = 0;
     int* hk = reinterpret_cast<int*>(dyn) + wid * (2 * kVoteSlots);
     vote_run<KMAX>(w0, w1, c0, cap, a.min_count[c0], hk, hk + kVoteSlots, lane,
                    sm.cand_out[wid], &nout, &snum);
@@ -1211,7 +1214,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   if (wid != 0) return;
   const bool cv = lane < 2 * nb && sm.cand_valid[lane];
   const int csrc = cv ? sm.cand_src[lane] : 0;
-  const long long csn = cv ? sm.cand_snum[csrc] : 0;
+  const int csn = cv ? sm.cand_snum[csrc] : 0;
   const int cc0 = cv ? sm.cand_c0[lane] : 1;
   const int clen = cv ? sm.cand_len[lane] : 0;
   const int cn = cv ? sm.cand_n[csrc] : 0;
@@ -1223,15 +1226,13 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     if (lv && (!gv || l0 >= g0)) win = 0;
     else if (gv) win = nb;
   } else {
-    long long bsn = 0;
-    int bc0 = 1;
+    // scores snum / c0 compared by cross products (snum <= k * M = 4096, c0 <= M = 128)
+    int bsn = 0, bc0 = 1;
     for (int i = 0; i < 2 * nb; ++i) {
       if (!((vmask >> i) & 1)) continue;
-      const long long sn = (long long)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
-                                            (int)((uint64_t)csn >> 32), i) << 32) |
-                                       (uint32_t)__builtin_amdgcn_readlane((int)csn, i));
+      const int sn = __builtin_amdgcn_readlane(csn, i);
       const int c0i = __builtin_amdgcn_readlane(cc0, i);
-      if (win < 0 || sn * (long long)bc0 > bsn * (long long)c0i) {
+      if (win < 0 || sn * bc0 > bsn * c0i) {
         win = i;
         bsn = sn;
         bc0 = c0i;
