@@ -179,7 +179,7 @@ struct Smem {
 // Shape of one request and the corpus state it sees.  Every thread derives it from the same
 // uniform loads, so no thread waits for another before the staging starts.
 struct Req {
-  int n, t, L, J, Lcap, C;
+  int n, t, L, J, Lcap;
   int act;
   bool has, fast;
   long long snap_start, snap_n, tail_w, delta_lo, delta_hi;
@@ -601,8 +601,8 @@ constexpr int kVoteBytes = NW * 2 * kVoteSlots * 4;
 // context ints, then 64 spare slots that absorb the staging stores of lanes past the row end
 __host__ __device__ inline int ctx_ints(int S, int T) { return ((S + T + 4 + 3) & ~3) + 64; }
 __host__ __device__ inline int ctx_spare(int S, int T) { return ctx_ints(S, T) - 64; }
-// Hit-list entries: wavefront w owns [w*C, w*C + C) with C = ceil(J / waves) rounded up to 64,
-// J <= S + T - 1, so S + T + 64 * NW entries always suffice.
+// Hit-list entries: wavefront w owns the entries of its end positions [cbeg, cend), from entry
+// cbeg on; J <= S + T - 1, so S + T + 64 * NW entries always suffice.
 __host__ __device__ inline int hit_cap(int S, int T) { return (S + T + 64 * NW + 63) & ~63; }
 __host__ __device__ inline size_t hpos_offset(bool staged, int S, int T) {
   return staged ? (size_t)4 * ctx_ints(S, T) : 0;
@@ -628,6 +628,25 @@ __host__ __device__ inline size_t dyn_bytes(bool staged, int S, int T, bool corp
 }
 
 constexpr int kScreenLoads = 32;  // 64-position words per screening group (2048 positions)
+
+// Share of the end positions per wavefront age rank on a SIMD (oldest first), and the total share
+// of wavefronts 0 .. w-1.
+constexpr int kAgeWeight[4] = {22, 18, 14, 12};
+__host__ __device__ constexpr int age_prefix(int w) {
+  int p = 0;
+  for (int r = 0; r < 4; ++r) {
+    const int in_rank = w > 4 * r ? (w - 4 * r < 4 ? w - 4 * r : 4) : 0;
+    p += kAgeWeight[r] * in_rank;
+  }
+  return p;
+}
+// First 64-position run of wavefront w out of nch runs shared by NWW workers (the division is by
+// a compile-time total).
+template <int NWW>
+__device__ __forceinline__ int first_run(int nch, int w) {
+  constexpr int pt = age_prefix(NWW);
+  return nch * age_prefix(w) / pt;
+}
 constexpr uint32_t kBufferWord3 = 0x00020000;  // raw buffer resource, gfx9 format bits
 
 __device__ __forceinline__ int lanes_before(uint64_t bal) {
@@ -857,10 +876,8 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       delta = r.delta_hi - r.delta_lo > 1;
       r.fast = r.act >= 0 && r.snap_n > 0 && !delta && r.Lcap >= 2;
     }
-    const int nww = r.fast ? NW - 1 : NW;
-    r.C = ((r.J + nww - 1) / nww + 63) / 64 * 64;
   }
-  const int n = r.n, t = r.t, L = r.L, Lcap = r.Lcap, J = r.J, C = r.C;
+  const int n = r.n, t = r.t, L = r.L, Lcap = r.Lcap, J = r.J;
   int32_t* drow = a.draft + (int64_t)b * a.k;
   if (t == 0) {
     for (int i = tid; i < a.k; i += NT) drow[i] = -1;
@@ -880,21 +897,31 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   if (STAGED && tid < t) ctxs[n + tid] = smp[tid];
 
   // ---------------------------------------------------------------- 1. local match
-  // Wavefront w < NWW owns end positions [w*C, w*C + C): it stages them (STAGED) and marks the
-  // ones whose token equals the last context token.  In the fast path the corpus wavefront
-  // probes the corpus and derives its ladder and sites meanwhile, through every local phase
-  // (the workers synchronise among themselves only).
+  // Wavefront w < NWW owns end positions [cbeg, cend): it stages them (STAGED) and marks the
+  // ones whose token equals the last context token.  The ranges are runs of 64 positions in
+  // wavefront order, sized by the wavefront's age on its SIMD (wavefront w is the (w / 4)-th
+  // on SIMD w % 4): a SIMD issues for its oldest ready wavefront first, so its younger ones
+  // get fewer positions and every worker reaches the barriers at about the same time.  In the
+  // fast path the corpus wavefront probes the corpus and derives its ladder and sites
+  // meanwhile, through every local phase (the workers synchronise among themselves only).
   const int NWW = fast ? NW - 1 : NW;
   const bool worker = wid < NWW;
-  const int cbeg = worker ? (wid * C < J ? wid * C : J) : J;
-  const int cend = worker ? (cbeg + C < J ? cbeg + C : J) : J;
+  int cbeg = J, cend = J;
+  if (worker) {
+    const int nch = (J + 63) >> 6;
+    cbeg = 64 * (fast ? first_run<NW - 1>(nch, wid) : first_run<NW>(nch, wid));
+    cend = wid + 1 == NWW ? J
+                          : 64 * (fast ? first_run<NW - 1>(nch, wid + 1) : first_run<NW>(nch, wid + 1));
+    cbeg = cbeg < J ? cbeg : J;
+    cend = cend < J ? cend : J;
+  }
   if (fast && wid == GW) {
     corpus_wave_probe(a, r, sm, row, smp, lane);
     corpus_wave_sites(a, r, sm, lane);
   } else {
-    uint16_t* hpos = hpos_all + wid * C;
-    uint8_t* hmb = hmb_all + wid * C;
-    uint64_t* b1w = bits_all + wid * (C >> 6);
+    uint16_t* hpos = hpos_all + cbeg;
+    uint8_t* hmb = hmb_all + cbeg;
+    uint64_t* b1w = bits_all + (cbeg >> 6);
     uint64_t s1 = 0;
     const int sbase = cbeg > n ? cbeg : n;
     const int nw = stage_screen<STAGED>(ctxs, ctx_spare(a.S, a.T), b1w, row, smp, n, cbeg, cend,
