@@ -81,6 +81,18 @@ def copy_calibration(torch, dev, mib, reps):
     del src, dst
 
 
+def copy_bandwidth_gbs(torch, dev, stream, mib=512, reps=10):
+    """Achievable HBM bandwidth on this machine: a plain device-to-device copy of `mib` MiB (read
+    plus write counted), HIP events on `stream`, outside the timed region."""
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ms = event_ms(torch, stream, lambda: dst.copy_(src), reps)
+    del src, dst
+    return 2 * mib * (1 << 20) / (ms * 1e-3) / 1e9
+
+
 def event_ms(torch, stream, fn, reps):
     """Mean milliseconds of fn() over reps back-to-back calls, HIP events on `stream`."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -188,12 +200,14 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
         d.propose(dn, dt, ds, draft, nv, stream)
 
     ing_ms, ing_tok, p_delta, p_during, p_live, reb_ms, step_ms = [], 0, [], [], [], [], []
+    delta_tok = []  # tokens in the delta when the delta proposes run (documents plus separators)
     sync_ms = []
     for st in range(warm_steps, warm_steps + steps):
         rows, lens, itok, ntok = batches[st]
         ts = time.time()
         ing_ms.append(timed(lambda: d.harvest_finished(rows, lens, itok, stream), 1))
         ing_tok += ntok
+        delta_tok.append(ntok + int(rows.numel()))
         p_delta.append(timed(prop, calls))
         tr = time.time()
         d.rebuild_async(stream)
@@ -240,6 +254,11 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
                                                       stream=stream), 1))
     d2.close()
     d.close()
+    # the delta scan's work: every request compares its last token with every delta position;
+    # its rate against the chip's vector compare rate (256 CUs x 64 lanes x 2.4 GHz)
+    scan_s = (float(np.mean(p_delta)) - float(np.mean(p_live))) * 1e-3
+    compares = w.B * float(np.mean(delta_tok))
+    valu_peak = 256 * 64 * 2.4e9
     out = {
         "workload": f"ingest-B{w.B}-S{w.S}-ring{w.ring_capacity}",
         "steps": steps, "warm_steps": warm_steps,
@@ -248,6 +267,10 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
         "propose_us_with_delta": round(float(np.mean(p_delta)) * 1e3, 1),
         "propose_us_during_rebuild": round(float(np.mean(p_during)) * 1e3, 1),
         "propose_us_no_delta": round(float(np.mean(p_live)) * 1e3, 1),
+        "delta_tokens": int(np.mean(delta_tok)),
+        "delta_scan_compares_per_s": round(compares / scan_s, 1) if scan_s > 0 else None,
+        "delta_scan_frac_of_valu_compare_rate":
+            round(compares / scan_s / valu_peak, 4) if scan_s > 0 else None,
         "rebuild_ms": round(float(np.median(sync_ms)), 2),
         "rebuild_tokens_per_s": round(w.ring_capacity / (float(np.median(sync_ms)) * 1e-3), 1),
         "async_rebuild_with_proposes_ms": round(float(np.mean(reb_ms)), 2),
@@ -375,6 +398,7 @@ def main():
     single = 1e3 / event_ms(torch, stream, lambda: d.propose(bufs[0][0], bufs[0][1], bufs[0][2],
                                                              draft, nv, stream), 500)
     others = other_workloads(torch, sfx, W, dev)
+    copy_gbs = copy_bandwidth_gbs(torch, dev, stream)
     log(f"[bench] graph-captured {graph_cps:.0f} calls/s; one resident buffer {single:.0f} "
         f"calls/s; {others}")
     load = None if args.no_ingest_load else ingest_under_load(torch, sfx, W, dev)
@@ -446,6 +470,8 @@ def main():
                   "index_rebuild_ms": None if rebuild_s is None else round(rebuild_s * 1e3, 2),
                   "index_rebuild_tokens_per_s":
                       None if not rebuild_s else round(corpus_n / rebuild_s, 1),
+                  "measured_copy_GBps": round(copy_gbs, 1),
+                  "frac_of_measured_copy": round(achieved / copy_gbs, 4),
                   "graph_captured_calls_per_s": round(graph_cps, 1),
                   "single_buffer_calls_per_s": round(single, 1),
                   "workloads_calls_per_s": others,
