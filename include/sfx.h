@@ -295,6 +295,16 @@ int sfx_load(sfx_ctx* ctx, const char* path, void* stream);
  * created with SFX_FLAG_CHECK_INPUTS; otherwise it reads 0.  Synchronises `stream`. */
 int sfx_debug_errors(sfx_ctx* ctx, uint32_t* bits_out, void* stream);
 
+/* Test hook for the failure path of the rebuild (suffix-gpu page, How it works step 4: the
+ * index is rebuilt on a side stream and double-buffered, so a rebuild that does not finish must
+ * leave the live one in place).  The next rebuild of ctx -- sfx_rebuild, or the worker started
+ * by sfx_rebuild_async -- fails with SFX_EHIP after building into the inactive buffer and
+ * before the swap: sfx_rebuild returns the error; sfx_poll then reports it with *swapped = 0 and
+ * sfx_wait_rebuild returns it.  The live index, the corpus and its delta are unchanged, so
+ * proposes keep their results, and the rebuild after that works as usual.  SFX_ESTATE without a
+ * corpus. */
+int sfx_debug_fail_next_rebuild(sfx_ctx* ctx);
+
 /* Suffix array (suffix-gpu page, Highlights and References: Manber & Myers prefix doubling):
  * sa[r] = start of the r-th smallest suffix of text[0:n], tokens compared as signed int32, a
  * proper prefix before the longer suffix.  text and sa are device arrays; workspace is a

@@ -30,6 +30,7 @@ EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_pr
            "sfx_rebuild", "sfx_rebuild_async", "sfx_poll", "sfx_wait_rebuild",
            "sfx_accept_estimate", "sfx_accept_feedback", "sfx_accept_reset", "sfx_accept_counts",
            "sfx_corpus_snapshot", "sfx_save", "sfx_load", "sfx_debug_errors",
+           "sfx_debug_fail_next_rebuild",
            "sfx_suffix_array_workspace_bytes", "sfx_build_suffix_array")
 
 
@@ -130,6 +131,7 @@ def load(path: str = LIB_PATH):
         "sfx_save": (ctypes.c_int, [_V, ctypes.c_char_p, _V]),
         "sfx_load": (ctypes.c_int, [_V, ctypes.c_char_p, _V]),
         "sfx_debug_errors": (ctypes.c_int, [_V, ctypes.POINTER(ctypes.c_uint32), _V]),
+        "sfx_debug_fail_next_rebuild": (ctypes.c_int, [_V]),
         "sfx_suffix_array_workspace_bytes": (ctypes.c_size_t, [_I64]),
         "sfx_build_suffix_array": (ctypes.c_int, [_V, _I64, _V, _V, ctypes.c_size_t, _V]),
     }
@@ -335,6 +337,10 @@ class Drafter:
     def load(self, path, stream=None):
         """Replace the corpus with the one saved in `path` (same corpus_capacity)."""
         _check(load().sfx_load(self._h, os.fsencode(path), _stream(stream)))
+
+    def debug_fail_next_rebuild(self):
+        """Test hook: the next rebuild fails with EHIP before its swap (the live index stays)."""
+        _check(load().sfx_debug_fail_next_rebuild(self._h))
 
     def debug_errors(self, stream=None) -> int:
         """Read and clear the sticky ERR_* bits raised since the last read (synchronises)."""

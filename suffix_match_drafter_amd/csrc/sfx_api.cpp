@@ -89,6 +89,7 @@ struct sfx_ctx {
   // asynchronous rebuild
   std::thread worker;
   std::atomic<int> async_state{0};  // 0 idle, 1 running, 2 finished
+  std::atomic<int> fail_next{0};    // test hook: the next rebuild fails before its swap
   int async_buf = -1;
   uint32_t async_mask = 0;
   int async_err = SFX_OK;
@@ -659,6 +660,7 @@ int sfx_rebuild(sfx_ctx* c, void* stream) {
                 "snapshot launch");
   uint32_t mask = 0;
   if ((rc = build_index(c, buf, st, &mask)) != SFX_OK) return rc;
+  if (c->fail_next.exchange(0)) return fail(SFX_EHIP, "injected rebuild failure");
   HIP_OR_RETURN(launch_swap(c->ctl, buf, mask, st), "swap launch");
   c->active_host = buf;
   return SFX_OK;
@@ -688,6 +690,7 @@ int sfx_rebuild_async(sfx_ctx* c, void* stream) {
       r = fail(SFX_EHIP, "rebuild event");
     if (r == SFX_OK && hipStreamSynchronize(c->side) != hipSuccess)
       r = fail(SFX_EHIP, "rebuild wait");
+    if (r == SFX_OK && c->fail_next.exchange(0)) r = fail(SFX_EHIP, "injected rebuild failure");
     c->async_mask = mask;
     c->async_err = r;
     if (r != SFX_OK) c->async_msg = g_err;
@@ -956,6 +959,14 @@ int sfx_debug_errors(sfx_ctx* c, uint32_t* bits_out, void* stream) {
   HIP_OR_RETURN(launch_clear_word(c->err, st), "error word clear");
   HIP_OR_RETURN(hipStreamSynchronize(st), "error word sync");
   *bits_out = v;
+  return SFX_OK;
+}
+
+int sfx_debug_fail_next_rebuild(sfx_ctx* c) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!c->ctl) return fail(SFX_ESTATE, "context has no corpus (corpus_capacity == 0)");
+  c->fail_next.store(1);
   return SFX_OK;
 }
 

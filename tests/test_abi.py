@@ -82,6 +82,7 @@ def test_null_arguments_rejected(sfx):
     assert L.sfx_accept_counts(None, None, None) == sfx.EINVAL
     assert L.sfx_load(None, b"/nonexistent", None) == sfx.EINVAL
     assert L.sfx_debug_errors(None, None, None) == sfx.EINVAL
+    assert L.sfx_debug_fail_next_rebuild(None) == sfx.EINVAL
     # an empty update is a no-op that touches nothing
     assert L.sfx_update_state(0, 4, 1, None, None, None, None, None) == sfx.OK
 
