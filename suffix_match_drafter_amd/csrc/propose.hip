@@ -892,9 +892,11 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   if (!fast && tid < 2 * kMaxNB) sm.cand_valid[tid] = 0;
   if (tid == 0) sm.wbar = 0;
   __syncthreads();
-  // the tail (read from the extension on) and the sampled ids of the staged context
-  if (tid < Lcap) sm.tail[tid] = ctx_at(row, smp, n, L - 1 - tid);
-  if (STAGED && tid < t) ctxs[n + tid] = smp[tid];
+  // the tail (read from the extension on) and the sampled ids of the staged context: loaded now,
+  // stored to LDS once wavefront 0 has screened its positions, so that the round trip overlaps
+  // its screen
+  const int tailv = tid < Lcap ? ctx_at(row, smp, n, L - 1 - tid) : 0;
+  const int sampv = (STAGED && tid < t) ? smp[tid] : 0;
 
   // ---------------------------------------------------------------- 1. local match
   // Wavefront w < NWW owns end positions [cbeg, cend): it stages them (STAGED) and marks the
@@ -926,6 +928,8 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     const int sbase = cbeg > n ? cbeg : n;
     const int nw = stage_screen<STAGED>(ctxs, ctx_spare(a.S, a.T), b1w, row, smp, n, cbeg, cend,
                                         smp[t - 1], lane, &s1);
+    if (tid < Lcap) sm.tail[tid] = tailv;
+    if (STAGED && tid < t) ctxs[n + tid] = sampv;
     if (fast) worker_barrier(&sm.wbar, NWW, lane);
     else __syncthreads();
 
