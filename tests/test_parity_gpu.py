@@ -162,6 +162,32 @@ def test_tree_depth_cap(S, mode, flags):
 
 
 @pytest.mark.parametrize("flags", FLAGS)
+def test_max_sampled_width(S, flags):
+    """T = 16, the largest sampled width: contexts extend the row prefix by up to 16 sampled ids
+    (n up to S, so a context can be 16 tokens longer than the row), with padding at random
+    points, k = 32 and D = 64, with a corpus."""
+    rng = np.random.default_rng(404)
+    B, Sq, T, V = 16, 300, 16, 3
+    tok = rng.integers(0, V, size=(B, Sq)).astype(np.int32)
+    n = np.concatenate([np.full(4, Sq), rng.integers(0, Sq + 1, size=B - 4)]).astype(np.int32)
+    samp = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    lead = rng.integers(0, T + 1, size=B)
+    lead[:3] = T
+    for b in range(B):
+        samp[b, lead[b]:] = -1
+    docs = [rng.integers(0, V, size=int(rng.integers(0, 80))).astype(np.int32) for _ in range(50)]
+    lc = O.LiveCorpus(10**7)
+    lc.ingest(docs)
+    for mode, nb in ((0, 1), (1, 8)):
+        kn = dict(k=32, max_tree_depth=64, num_backoff=nb, max_occurrences=128, mode=mode,
+                  spec_factor_ppm=4_000_000, min_token_prob_ppm=50_000)
+        exp = O.propose(O.params_from(kn), n, tok, samp, corpus=lc.text())
+        got = run_gpu(S, kn, n, tok, samp, corpus_docs=docs, capacity=1 << 14, flags=flags)
+        assert_same(got[:2], exp, f"T=16 mode={mode} flags={flags}")
+        got[2].close()
+
+
+@pytest.mark.parametrize("flags", FLAGS)
 def test_degenerate_rows(S, flags):
     """Empty rows, rows with no sampled token, a single repeated token (every position
     matches), n above S, S not a multiple of 4, T=0."""
