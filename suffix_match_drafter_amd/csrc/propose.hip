@@ -735,20 +735,23 @@ __device__ __forceinline__ int stage_screen(int* ctxs, int spare, uint64_t* b1w,
 
 // Positions of the set bits of nw words (word i based at base0 + 64 i) followed by one extra
 // word `extra` based at xbase, in order, into out[]; returns their number.  Every lane of the
-// wavefront takes part.
+// wavefront takes part, on a 16-bit quarter of a word each, so that a lane walks at most 16 bits.
 __device__ __forceinline__ int bits_to_list(const uint64_t* w, int nw, uint64_t extra, int xbase,
                                             int base0, uint16_t* out, int lane) {
   int cnt = 0;
-  for (int w0 = 0; w0 <= nw; w0 += 64) {
-    const int wi = w0 + lane;
-    uint64_t wd = wi < nw ? w[wi] : (wi == nw ? extra : 0ull);
-    const int base = wi < nw ? base0 + 64 * wi : xbase;
-    const int c = __popcll(wd);
+  const int nq = 4 * (nw + 1);
+  for (int q0 = 0; q0 < nq; q0 += 64) {
+    const int q = q0 + lane;
+    const int wi = q >> 2, part = q & 3;
+    const uint64_t wd = wi < nw ? w[wi] : (wi == nw ? extra : 0ull);
+    uint32_t piece = (uint32_t)(wd >> (16 * part)) & 0xFFFFu;
+    const int base = (wi < nw ? base0 + 64 * wi : xbase) + 16 * part;
+    const int c = __popc(piece);
     const int incl = wave_incl_add(c);
     int at = cnt + incl - c;
-    while (wd) {
-      out[at++] = (uint16_t)(base + __builtin_ctzll(wd));
-      wd &= wd - 1;
+    while (piece) {
+      out[at++] = (uint16_t)(base + __builtin_ctz(piece));
+      piece &= piece - 1;
     }
     cnt += __builtin_amdgcn_readlane(incl, 63);
   }
