@@ -627,7 +627,7 @@ __host__ __device__ inline size_t dyn_bytes(bool staged, int S, int T, bool corp
   return b;
 }
 
-constexpr int kScreenLoads = 32;  // 64-position words per screening group (2048 positions)
+constexpr int kScreenLoads = 16;  // 64-position words per screening group (1024 positions)
 
 // Share of the end positions per wavefront age rank on a SIMD (oldest first), and the total share
 // of wavefronts 0 .. w-1.
