@@ -361,6 +361,7 @@ def test_config_corpus(S, cid, flags):
     assert np.array_equal(snap, text)
     exp = O.propose(O.params_from(w.knobs()), n, tok, samp, corpus=text, num_threads=NTHREADS)
     assert_same((got_d, got_n), exp, f"config {cid}")
+    assert (got_d != W.POISON).all()
     # a second call on the same context is identical (no state leaks between calls)
     d2, n2 = d.propose(dev(n), dev(tok), dev(samp))
     torch.cuda.synchronize()
