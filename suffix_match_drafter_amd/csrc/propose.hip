@@ -383,110 +383,126 @@ __device__ __forceinline__ void delta_scan_wave(const ProposeArgs& a, long long 
 // continuation windows are w0 / w1 (-1 past the end of a continuation).  Writes the tokens to
 // out[] and returns the count and the sum of per-depth counts.  cmin is the smallest
 // count the stop rule keeps (0 when there is no stop rule).
+// State of one candidate's depth-wise vote, kept by its wavefront.
+struct VoteState {
+  bool al0, al1;  // this lane's two sites still on the voted path
+  bool done;
+  bool site0;     // site 0 (lane 0, first half) is still on the voted path
+  int nout;       // tokens voted so far
+  int snum;       // their counts summed: at most k * M, so every product below fits 32 bits
+  int tokv;       // lane i collects the i-th voted token
+};
+
+// One depth of the vote: x0 and x1 are this lane's two sites' tokens at this depth.
+__device__ __forceinline__ void vote_depth(VoteState& v, int x0, int x1, int cmin, int* hk, int* hc,
+                                           int lane) {
+  bool& al0 = v.al0;
+  bool& al1 = v.al1;
+  bool& done = v.done;
+  bool& site0 = v.site0;
+  int& nout = v.nout;
+  int& snum = v.snum;
+  int& tokv = v.tokv;
+  const int tk0 = al0 ? x0 : -1, tk1 = al1 ? x1 : -1;
+  const uint64_t v0 = __ballot(tk0 >= 0), v1 = __ballot(tk1 >= 0);
+  // site 0's token at this depth does not depend on the votes so far
+  const int s0tok = __builtin_amdgcn_readfirstlane(x0);
+  int c = 0, w = -1;
+  if ((v0 | v1) == 0) {
+    done = true;
+  } else {
+    // the reference is an alive site's token: site 0's while it stays on the voted path,
+    // else the first alive site's; when every alive site agrees with it the token wins
+    // with all their votes
+    int first;
+    if (site0 && s0tok >= 0) {
+      first = s0tok;
+    } else {
+      const int fl = v0 ? __builtin_ctzll(v0) : __builtin_ctzll(v1);
+      first = v0 ? __builtin_amdgcn_readlane(tk0, fl) : __builtin_amdgcn_readlane(tk1, fl);
+    }
+    const uint64_t f0 = __ballot(tk0 == first), f1 = __ballot(tk1 == first);
+    const int nalive = __popcll(v0) + __popcll(v1);
+    const int cf = __popcll(f0) + __popcll(f1);
+    if (cf == nalive) {
+      c = nalive;
+      w = first;
+    } else if (2 * cf > nalive) {
+      // a strict majority: no other token can reach its count
+      c = cf;
+      w = first;
+    } else if (nalive <= kSmallVote) {
+      // few alive sites: one ballot pair per distinct token, until the best count exceeds
+      // every vote not yet counted
+      uint64_t key = ((uint64_t)cf << 32) | (uint32_t)(0x7FFFFFFF - first);
+      uint64_t r0 = v0 & ~f0, rr1 = v1 & ~f1;
+      int rest = nalive - cf;
+      while ((r0 | rr1) && (int)(key >> 32) <= rest) {
+        const int tok = r0 ? __builtin_amdgcn_readlane(tk0, __builtin_ctzll(r0))
+                           : __builtin_amdgcn_readlane(tk1, __builtin_ctzll(rr1));
+        const uint64_t e0 = __ballot(tk0 == tok), e1 = __ballot(tk1 == tok);
+        const uint64_t k = ((uint64_t)(__popcll(e0) + __popcll(e1)) << 32) |
+                           (uint32_t)(0x7FFFFFFF - tok);
+        key = k > key ? k : key;
+        r0 &= ~e0;
+        rr1 &= ~e1;
+        rest -= __popcll(e0) + __popcll(e1);
+      }
+      c = (int)(key >> 32);
+      w = 0x7FFFFFFF - (int)(uint32_t)(key & 0xFFFFFFFFu);
+    } else {
+      // many alive sites: counts in an LDS hash, then max count and smallest token
+      for (int x = lane; x < kVoteSlots; x += 64) {
+        hk[x] = -1;
+        hc[x] = 0;
+      }
+      wave_sync();
+      int sl0 = -1, sl1 = -1;
+      if (tk0 >= 0) sl0 = vote_insert(hk, hc, tk0);
+      if (tk1 >= 0) sl1 = vote_insert(hk, hc, tk1);
+      wave_sync();
+      const int cnt0 = sl0 >= 0 ? hc[sl0] : 0, cnt1 = sl1 >= 0 ? hc[sl1] : 0;
+      if (__ballot(tk0 >= (1 << 24) || tk1 >= (1 << 24)) == 0) {
+        // tokens below 2^24: count and token packed in one key, one reduction
+        const uint32_t k0 = sl0 >= 0 ? ((uint32_t)cnt0 << 24) | (uint32_t)(0xFFFFFF - tk0) : 0u;
+        const uint32_t k1 = sl1 >= 0 ? ((uint32_t)cnt1 << 24) | (uint32_t)(0xFFFFFF - tk1) : 0u;
+        const uint32_t key = wave_max_u32(k0 > k1 ? k0 : k1);
+        c = (int)(key >> 24);
+        w = 0xFFFFFF - (int)(key & 0xFFFFFFu);
+      } else {
+        c = wave_max(cnt0 > cnt1 ? cnt0 : cnt1);
+        int tmin = 0x7FFFFFFF;
+        if (sl0 >= 0 && cnt0 == c) tmin = tk0;
+        if (sl1 >= 0 && cnt1 == c && tk1 < tmin) tmin = tk1;
+        w = wave_min(tmin);
+      }
+      wave_sync();
+    }
+    if (c < cmin) {
+      done = true;
+    } else {
+      tokv = lane == nout ? w : tokv;
+      ++nout;
+      snum += c;
+      site0 = site0 && s0tok == w;
+      al0 = tk0 == w;
+      al1 = tk1 == w;
+    }
+  }
+}
+
 template <int KMAX>
 __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[KMAX], int c0,
                                          int cap, int cmin, int* hk, int* hc, int lane, int* out,
                                          int* n_out, int* snum_out) {
-  bool al0 = lane < c0, al1 = lane + 64 < c0;
-  int nout = 0;
-  int snum = 0;  // at most k * M, so every product below fits 32 bits
-  bool done = false;
-  int tokv = -1;  // lane i collects the i-th voted token
-  bool site0 = true;  // site 0 (lane 0, first half) is still on the voted path
+  VoteState v{lane < c0, lane + 64 < c0, false, true, 0, 0, -1};
 #pragma unroll
   for (int d = 0; d < KMAX; ++d) {
-    if (!done && d < cap) {
-      const int tk0 = al0 ? w0[d] : -1, tk1 = al1 ? w1[d] : -1;
-      const uint64_t v0 = __ballot(tk0 >= 0), v1 = __ballot(tk1 >= 0);
-      // site 0's token at this depth does not depend on the votes so far
-      const int s0tok = __builtin_amdgcn_readfirstlane(w0[d]);
-      int c = 0, w = -1;
-      if ((v0 | v1) == 0) {
-        done = true;
-      } else {
-        // the reference is an alive site's token: site 0's while it stays on the voted path,
-        // else the first alive site's; when every alive site agrees with it the token wins
-        // with all their votes
-        int first;
-        if (site0 && s0tok >= 0) {
-          first = s0tok;
-        } else {
-          const int fl = v0 ? __builtin_ctzll(v0) : __builtin_ctzll(v1);
-          first = v0 ? __builtin_amdgcn_readlane(tk0, fl) : __builtin_amdgcn_readlane(tk1, fl);
-        }
-        const uint64_t f0 = __ballot(tk0 == first), f1 = __ballot(tk1 == first);
-        const int nalive = __popcll(v0) + __popcll(v1);
-        const int cf = __popcll(f0) + __popcll(f1);
-        if (cf == nalive) {
-          c = nalive;
-          w = first;
-        } else if (2 * cf > nalive) {
-          // a strict majority: no other token can reach its count
-          c = cf;
-          w = first;
-        } else if (nalive <= kSmallVote) {
-          // few alive sites: one ballot pair per distinct token, until the best count exceeds
-          // every vote not yet counted
-          uint64_t key = ((uint64_t)cf << 32) | (uint32_t)(0x7FFFFFFF - first);
-          uint64_t r0 = v0 & ~f0, rr1 = v1 & ~f1;
-          int rest = nalive - cf;
-          while ((r0 | rr1) && (int)(key >> 32) <= rest) {
-            const int tok = r0 ? __builtin_amdgcn_readlane(tk0, __builtin_ctzll(r0))
-                               : __builtin_amdgcn_readlane(tk1, __builtin_ctzll(rr1));
-            const uint64_t e0 = __ballot(tk0 == tok), e1 = __ballot(tk1 == tok);
-            const uint64_t k = ((uint64_t)(__popcll(e0) + __popcll(e1)) << 32) |
-                               (uint32_t)(0x7FFFFFFF - tok);
-            key = k > key ? k : key;
-            r0 &= ~e0;
-            rr1 &= ~e1;
-            rest -= __popcll(e0) + __popcll(e1);
-          }
-          c = (int)(key >> 32);
-          w = 0x7FFFFFFF - (int)(uint32_t)(key & 0xFFFFFFFFu);
-        } else {
-          // many alive sites: counts in an LDS hash, then max count and smallest token
-          for (int x = lane; x < kVoteSlots; x += 64) {
-            hk[x] = -1;
-            hc[x] = 0;
-          }
-          wave_sync();
-          int sl0 = -1, sl1 = -1;
-          if (tk0 >= 0) sl0 = vote_insert(hk, hc, tk0);
-          if (tk1 >= 0) sl1 = vote_insert(hk, hc, tk1);
-          wave_sync();
-          const int cnt0 = sl0 >= 0 ? hc[sl0] : 0, cnt1 = sl1 >= 0 ? hc[sl1] : 0;
-          if (__ballot(tk0 >= (1 << 24) || tk1 >= (1 << 24)) == 0) {
-            // tokens below 2^24: count and token packed in one key, one reduction
-            const uint32_t k0 = sl0 >= 0 ? ((uint32_t)cnt0 << 24) | (uint32_t)(0xFFFFFF - tk0) : 0u;
-            const uint32_t k1 = sl1 >= 0 ? ((uint32_t)cnt1 << 24) | (uint32_t)(0xFFFFFF - tk1) : 0u;
-            const uint32_t key = wave_max_u32(k0 > k1 ? k0 : k1);
-            c = (int)(key >> 24);
-            w = 0xFFFFFF - (int)(key & 0xFFFFFFu);
-          } else {
-            c = wave_max(cnt0 > cnt1 ? cnt0 : cnt1);
-            int tmin = 0x7FFFFFFF;
-            if (sl0 >= 0 && cnt0 == c) tmin = tk0;
-            if (sl1 >= 0 && cnt1 == c && tk1 < tmin) tmin = tk1;
-            w = wave_min(tmin);
-          }
-          wave_sync();
-        }
-        if (c < cmin) {
-          done = true;
-        } else {
-          tokv = lane == nout ? w : tokv;
-          ++nout;
-          snum += c;
-          site0 = site0 && s0tok == w;
-          al0 = tk0 == w;
-          al1 = tk1 == w;
-        }
-      }
-    }
+    if (!v.done && d < cap) vote_depth(v, w0[d], w1[d], cmin, hk, hc, lane);
   }
-  if (lane < nout) out[lane] = tokv;
-  *n_out = nout;
-  *snum_out = snum;
+  if (lane < v.nout) out[lane] = v.tokv;
+  *n_out = v.nout;
+  *snum_out = v.snum;
 }
 
 
