@@ -1,0 +1,54 @@
+// delta_index.h -- per-call index of the delta's two-token occurrences (internal to libsfx).
+//
+// The delta (documents appended since the live snapshot) has no suffix array, so its
+// occurrences of a request's tail are found by position (suffix-gpu page, How it works step 2
+// and Highlights: the unindexed documents are scanned directly).  Scanning the whole delta in
+// every request costs B * |delta| compares.  Before a step that may see a delta, four passes
+// sort the delta's end positions by the two tokens that end there, for only those pairs that
+// end some request's context:
+//   1. one workgroup hashes the batch's distinct tail pairs to dense group numbers;
+//   2. every wavefront column counts, per group, the occurrences in its slice of the delta;
+//   3. an exclusive scan over (group, column) gives every slice its place in the list;
+//   4. the slices write their occurrences' offsets (from the delta start), in position order.
+// A request then extends only its own group's occurrences, which are exactly those the scan
+// would find, in the same order.
+#pragma once
+
+#include "sfx_internal.h"
+
+namespace sfx {
+
+constexpr int kPairMaxBatch = 1024;     // batches above this scan the delta instead
+constexpr int kPairCols = 1024;         // wavefront slices of the delta
+constexpr int kPairColsPerBlock = 4;    // 256-thread workgroups of four slices
+
+// Hash-table slots for a batch of up to max_batch requests: a power of two, at least twice
+// the batch.
+inline uint32_t pair_slots(int max_batch) {
+  uint32_t s = 64;
+  while (s < 2u * (uint32_t)max_batch) s <<= 1;
+  return s;
+}
+
+struct PairIndexArgs {
+  int32_t B, S, T, D;
+  const int32_t* ntns;
+  const int32_t* tok;
+  const int32_t* samp;
+  const Ctl* ctl;
+  const int32_t* ring;
+  int64_t ring_cap;
+  unsigned long long* keys;  // [slots] the distinct pairs (empty slots all ones)
+  int32_t* gid;              // [slots] their dense group numbers
+  uint32_t slots;
+  int32_t* group;            // [B] out: the request's group, or -1 when it takes no delta scan
+  int32_t* off;              // [(B + 1) * kPairCols] counts, then list offsets in place
+  int32_t* scan_tmp;         // [ceil((B + 1) * kPairCols / 4096)]
+  uint32_t* list;            // [ring_cap] occurrence offsets from the delta start
+};
+
+// Ints of scan scratch for a batch of B.
+size_t pair_scan_tmp_ints(int B);
+hipError_t launch_pair_index(const PairIndexArgs& a, hipStream_t st);
+
+}  // namespace sfx

@@ -1,0 +1,261 @@
+// delta_index.hip -- per-call index of the delta's occurrences of the batch's tail pairs.
+//
+// suffix-gpu page, How it works step 2 and Highlights: documents appended since the live
+// snapshot are not in the suffix array and are matched by position.  A request's corpus
+// candidates there start from the positions x whose token is its last context token and whose
+// previous token (still inside the delta) is its second-to-last, with a real token after x.
+// The drafter step used to find them by scanning the whole delta in every request.  These
+// passes find them once per call for every request at the same time: positions are grouped by
+// the pair (token before, token at x), for the pairs that end some request's context, and each
+// group keeps position order, which is the logical order the step's site rule needs.
+#include "delta_index.h"
+
+#include "sa_build.h"
+
+namespace sfx {
+
+namespace {
+
+constexpr unsigned long long kNoPair = ~0ull;  // a pair whose first token is -1: never a key
+
+__device__ __forceinline__ unsigned long long pair_key(int first, int second) {
+  return ((unsigned long long)(uint32_t)first << 32) | (uint32_t)second;
+}
+
+__device__ __forceinline__ uint32_t pair_hash(unsigned long long k) {
+  k ^= k >> 33;
+  k *= 0xff51afd7ed558ccdull;
+  k ^= k >> 33;
+  k *= 0xc4ceb9fe1a85ec53ull;
+  k ^= k >> 33;
+  return (uint32_t)k;
+}
+
+// The delta's logical range [lo, hi) under the control block, by the drafter step's rule: it
+// starts at the live snapshot's end (or at the oldest live document, if later).  Returns
+// whether it holds a candidate end position (at least two tokens).
+__device__ __forceinline__ bool delta_range(const Ctl* ctl, long long* lo, long long* hi) {
+  const Ctl c = *ctl;
+  long long l = c.tail;
+  if (c.active >= 0) {
+    const long long se = c.active == 0 ? c.snap_end[0] : c.snap_end[1];
+    l = se > l ? se : l;
+  }
+  *lo = l;
+  *hi = c.head;
+  return c.head - l > 1;
+}
+
+// Pass 1 (one workgroup of 1024 threads, one request per thread): the tail pair of each
+// request whose step scans the delta -- a non-empty sampled prefix, a two-token tail within
+// max_tree_depth and a non-negative second-to-last token -- inserted into an open-addressing
+// table; the occupied slots are numbered densely in slot order.
+__global__ __launch_bounds__(1024) void pair_table_kernel(PairIndexArgs a) {
+  __shared__ unsigned long long hk[2 * kPairMaxBatch];
+  __shared__ int hg[2 * kPairMaxBatch];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const uint32_t mask = a.slots - 1;
+  for (uint32_t i = tid; i < a.slots; i += 1024) hk[i] = kNoPair;
+  __syncthreads();
+  unsigned long long key = kNoPair;
+  if (tid < a.B) {
+    int n = a.ntns[tid];
+    n = n < 0 ? 0 : (n > a.S ? a.S : n);
+    const int32_t* smp = a.samp + (int64_t)tid * a.T;
+    const int32_t* row = a.tok + (int64_t)tid * a.S;
+    int t = 0;
+    while (t < a.T && smp[t] >= 0) ++t;
+    const int L = n + t;
+    const int lcap = a.D < L ? a.D : L;
+    if (t > 0 && lcap >= 2) {
+      const int last = smp[t - 1];
+      const int before = L - 2 >= n ? smp[L - 2 - n] : row[L - 2];
+      if (before >= 0) key = pair_key(before, last);
+    }
+  }
+  if (key != kNoPair) {
+    uint32_t h = pair_hash(key) & mask;
+    for (;;) {
+      const unsigned long long prev = atomicCAS(&hk[h], kNoPair, key);
+      if (prev == kNoPair || prev == key) break;
+      h = (h + 1) & mask;
+    }
+  }
+  __syncthreads();
+  // thread i numbers slots 2i and 2i + 1 (slots <= 2048)
+  const uint32_t s0 = 2 * tid, s1 = 2 * tid + 1;
+  const int o0 = s0 < a.slots && hk[s0] != kNoPair, o1 = s1 < a.slots && hk[s1] != kNoPair;
+  int incl = o0 + o1;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wid; ++w) before += wsum[w];
+  const int excl = before + incl - o0 - o1;
+  if (s0 < a.slots) {
+    hg[s0] = o0 ? excl : -1;
+    a.keys[s0] = hk[s0];
+    a.gid[s0] = hg[s0];
+  }
+  if (s1 < a.slots) {
+    hg[s1] = o1 ? excl + o0 : -1;
+    a.keys[s1] = hk[s1];
+    a.gid[s1] = hg[s1];
+  }
+  __syncthreads();
+  if (tid < a.B) {
+    int g = -1;
+    if (key != kNoPair) {
+      uint32_t h = pair_hash(key) & mask;
+      while (hk[h] != key) h = (h + 1) & mask;
+      g = hg[h];
+    }
+    a.group[tid] = g;
+  }
+}
+
+constexpr int kSliceRuns = 4;  // 64-position runs whose loads a wavefront issues together
+
+// Passes 2 and 4 (workgroups of four wavefronts, one delta slice each).  The delta's end
+// positions lo + 1 .. hi - 2 are cut into kPairCols slices of whole 64-position runs, and
+// wavefront column c takes slice c.  A position belongs to group g when (token before, token
+// at it) is group g's pair and a real token follows it.  COUNT: the slice's count per group
+// goes to off[g * kPairCols + c] (zeros too, so the scan sees every entry).  Otherwise off
+// holds the exclusive scan of those counts, and the slice writes its positions' offsets from
+// lo to list[] from there, in position order within each group.
+template <bool COUNT>
+__global__ __launch_bounds__(256) void pair_slices_kernel(PairIndexArgs a) {
+  __shared__ unsigned long long hk[2 * kPairMaxBatch];
+  __shared__ int hg[2 * kPairMaxBatch];
+  __shared__ int cur[kPairColsPerBlock][kPairMaxBatch + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = blockIdx.x * kPairColsPerBlock + w;
+  const int ng = a.B + 1;
+  long long lo, hi;
+  const bool any = delta_range(a.ctl, &lo, &hi);
+  if (!COUNT && !any) return;  // uniform over the grid: the step reads no list
+  {
+    // the table (at most 2048 slots) and this column's counters, loads issued together
+    constexpr int kTab = 2 * kPairMaxBatch / 256, kCur = (kPairMaxBatch + 1 + 63) / 64;
+    unsigned long long tk[kTab];
+    int tg[kTab], tc[kCur];
+#pragma unroll
+    for (int j = 0; j < kTab; ++j) {
+      const uint32_t i = tid + 256 * j;
+      tk[j] = i < a.slots ? a.keys[i] : kNoPair;
+      tg[j] = i < a.slots ? a.gid[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kCur; ++j) {
+      const int g = lane + 64 * j;
+      tc[j] = (!COUNT && g < ng) ? a.off[(int64_t)g * kPairCols + col] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kTab; ++j) {
+      const uint32_t i = tid + 256 * j;
+      if (i < a.slots) {
+        hk[i] = tk[j];
+        hg[i] = tg[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kCur; ++j)
+      if (lane + 64 * j < ng) cur[w][lane + 64 * j] = tc[j];
+  }
+  __syncthreads();
+  const long long nd = any ? hi - lo - 2 : 0;
+  if (nd > 0) {
+    const long long seg = ((nd + kPairCols - 1) / kPairCols + 63) / 64 * 64;
+    const long long xb = lo + 1 + (long long)col * seg;
+    const long long xe = xb + seg < hi - 1 ? xb + seg : hi - 1;
+    const uint32_t mask = a.slots - 1;
+    const int cap = (int)a.ring_cap;
+    int s = xb < xe ? (int)((xb + lane) % a.ring_cap) : 0;  // slot of this lane's position
+    for (long long x0 = xb; x0 < xe; x0 += 64 * kSliceRuns) {
+      int p[kSliceRuns], c[kSliceRuns], nx[kSliceRuns];
+#pragma unroll
+      for (int u = 0; u < kSliceRuns; ++u) {
+        const bool in = x0 + 64 * u + lane < xe;
+        const int sp = s == 0 ? cap - 1 : s - 1;
+        const int sn = s + 1 == cap ? 0 : s + 1;
+        p[u] = in ? a.ring[sp] : -1;
+        c[u] = in ? a.ring[s] : -1;
+        nx[u] = in ? a.ring[sn] : -1;
+        s += 64;
+        while (s >= cap) s -= cap;
+      }
+#pragma unroll
+      for (int u = 0; u < kSliceRuns; ++u) {
+        const long long x = x0 + 64 * u + lane;
+        int g = -1;
+        if (p[u] >= 0 && nx[u] >= 0) {
+          const unsigned long long key = pair_key(p[u], c[u]);
+          uint32_t h = pair_hash(key) & mask;
+          for (;;) {
+            const unsigned long long k = hk[h];
+            if (k == key) {
+              g = hg[h];
+              break;
+            }
+            if (k == kNoPair) break;
+            h = (h + 1) & mask;
+          }
+        }
+        if (COUNT) {
+          if (g >= 0) atomicAdd(&cur[w][g], 1);
+        } else {
+          // one group at a time: the lanes of group gg take consecutive list entries
+          uint64_t pend = __ballot(g >= 0);
+          while (pend) {
+            const int gg = __builtin_amdgcn_readlane(g, __builtin_ctzll(pend));
+            const uint64_t same = __ballot(g == gg);
+            const int base = cur[w][gg];
+            if (g == gg) a.list[base + __popcll(same & ((1ull << lane) - 1))] = (uint32_t)(x - lo);
+            __builtin_amdgcn_wave_barrier();
+            if (lane == 0) cur[w][gg] = base + __popcll(same);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            pend &= ~same;
+          }
+        }
+      }
+    }
+  }
+  if (COUNT) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int g = lane; g < ng; g += 64) a.off[(int64_t)g * kPairCols + col] = cur[w][g];
+  }
+}
+
+}  // namespace
+
+size_t pair_scan_tmp_ints(int B) {
+  const int64_t m = (int64_t)(B + 1) * kPairCols;
+  return (size_t)((m + 4095) / 4096);
+}
+
+hipError_t launch_pair_index(const PairIndexArgs& a, hipStream_t st) {
+  if (a.B <= 0) return hipSuccess;
+  if (a.B > kPairMaxBatch || a.slots < 2u * (uint32_t)a.B || a.slots > 2u * kPairMaxBatch ||
+      (a.slots & (a.slots - 1)) != 0)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pair_table_kernel, dim3(1), dim3(1024), 0, st, a);
+  const dim3 grid(kPairCols / kPairColsPerBlock);
+  hipLaunchKernelGGL((pair_slices_kernel<true>), grid, dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = scan_sum_exclusive(a.off, a.off, (int64_t)(a.B + 1) * kPairCols, a.scan_tmp, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((pair_slices_kernel<false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sfx

@@ -23,6 +23,11 @@ struct ProposeArgs {
   int64_t ring_cap;    // ring slots: slot = position % ring_cap
   int32_t stream_ctx;  // read the context from HBM instead of staging it in LDS
   int32_t* pick;       // [B] out: the winner as num_valid << 16 | source << 8 | length, or -1
+  // per-call index of the delta's tail-pair occurrences (delta_index.h), or nullptr, in which
+  // case a request scans the whole delta
+  const int32_t* pair_group;
+  const int32_t* pair_off;
+  const uint32_t* pair_list;
 };
 
 constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one gfx950 workgroup

@@ -21,6 +21,7 @@
 //      integer cross-multiplication; selection and the [k] output row follow.
 #include <type_traits>
 
+#include "delta_index.h"
 #include "propose.h"
 
 namespace sfx {
@@ -312,8 +313,9 @@ __device__ __forceinline__ uint64_t pick_mask(const uint64_t (&h)[U], int u) {
 // position is an occurrence of the tail's last two tokens when its own token is tail[0] and the
 // one before it (not before dlo) is tail[1]: two compares per chunk, whose ballots are combined
 // with a one-bit shift, select them.  Only those lanes extend backwards, and an occurrence
-// followed by a separator is dropped.  For every chunk that holds a candidate, f(x, m) gets each
-// lane's position and match length (0 where none); f returns false to stop the scan.
+// followed by a separator is dropped.  For every chunk that holds a candidate, f(x, x, m) gets
+// each lane's position (twice: as the record coordinate and as the position) and match length
+// (0 where none); f returns false to stop the scan.
 template <typename F>
 __device__ __forceinline__ void delta_scan_wave(const ProposeArgs& a, long long dlo, long long x0,
                                                 long long x1, int Lcap, const int* tail,
@@ -371,11 +373,69 @@ __device__ __forceinline__ void delta_scan_wave(const ProposeArgs& a, long long 
             }
           }
         }
-        if (!f(xp, m)) return;
+        if (!f(xp, xp, m)) return;
       }
     }
     x += len;
     r = 0;  // a run ends at x1 or at the last slot
+  }
+}
+
+constexpr int kListRound = 4;  // tokens compared per round trip when extending listed entries
+
+// The same occurrences from the per-call pair index: entries [i0, i1) of the request's group
+// list hold, in position order, the offsets from dlo of the delta positions that end with the
+// tail's last two tokens and are followed by a real token.  All 64 lanes extend an entry each:
+// one token, then kListRound tokens per round trip, so a batch waits for about one round trip
+// per kListRound tokens of its longest match.  f(i, x, m) gets each lane's entry index, position
+// and match length (0 past i1).
+template <typename F>
+__device__ __forceinline__ void delta_list_wave(const ProposeArgs& a, long long dlo, long long i0,
+                                                long long i1, int Lcap, const int* tail,
+                                                int lane, F&& f) {
+  const int cap = (int)a.ring_cap;
+  const int dslot = (int)(dlo % a.ring_cap);
+  for (long long e = i0; e < i1; e += 64) {
+    const long long i = e + lane;
+    long long x = 0;
+    int m = 0;
+    if (i < i1) {
+      const uint32_t o = a.pair_list[i];
+      x = dlo + (long long)o;
+      int s = dslot + (int)o;
+      if (s >= cap) s -= cap;
+      // length m extends while m < Lcap and position x - m is still in the delta.  Most
+      // occurrences of a frequent pair end at the next token, which is read alone; the lanes
+      // that match it go on in rounds.
+      const int lim = (long long)Lcap <= x - dlo ? Lcap : (int)(x - dlo) + 1;
+      m = 2;
+      if (m < lim) {
+        int q = s - 2;
+        if (q < 0) q += cap;
+        const int c = a.ring[q];
+        if (c >= 0 && c == tail[2]) m = 3;
+      }
+      while (m > 2 && m < lim) {
+        int v[kListRound];
+#pragma unroll
+        for (int j = 0; j < kListRound; ++j) {
+          int q = s - m - j;  // m + j < lim <= the delta's length <= cap: one wrap at most
+          if (q < 0) q += cap;
+          v[j] = m + j < lim ? a.ring[q] : -2;
+        }
+        int run = 0;
+        bool stop = false;
+#pragma unroll
+        for (int j = 0; j < kListRound; ++j) {
+          const int tj = m + j < kMaxD ? m + j : kMaxD - 1;
+          stop = stop || v[j] < 0 || v[j] != tail[tj];
+          run += stop ? 0 : 1;
+        }
+        m += run;
+        if (stop) break;
+      }
+    }
+    if (!f(i, x, m)) return;
   }
 }
 
@@ -1062,32 +1122,46 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
         if (m >= 5) atomicAdd(&sm.ghist[m], 1);
       }
     }
-    // delta: documents appended since the live snapshot, scanned by brute force.  Wavefront w
-    // owns the end positions [sb, se) and keeps its occurrences of length >= 2 in LDS, in
-    // position order (offset from sb << 6 | length - 2; the context hit lists are dead by now),
-    // at most H of them, plus a length histogram.
+    // delta: documents appended since the live snapshot.  With the per-call pair index,
+    // wavefront w owns entries [sb, se) of the request's group list; without it, the end
+    // positions [sb, se), scanned by brute force.  It keeps its occurrences of length >= 2 in
+    // LDS, in position order (coordinate offset from sb << 6 | length - 2; the context hit
+    // lists are dead by now), at most H of them, plus a length histogram.
     const long long dlo = r.delta_lo, dhi = r.delta_hi;
     const bool has_delta = dhi - dlo > 1;
-    const long long dseg = has_delta ? ((dhi - 1 - dlo + NW - 1) / NW + 63) / 64 * 64 : 0;
-    const long long sb = dlo + (long long)wid * dseg;
-    const long long se = has_delta ? (sb + dseg < dhi - 1 ? sb + dseg : dhi - 1) : sb;
+    const bool listed = has_delta && a.pair_group != nullptr;
+    long long sb, se;
+    if (listed) {
+      const int g = a.pair_group[b];
+      const long long i0 = g >= 0 ? a.pair_off[(int64_t)g * kPairCols] : 0;
+      const long long i1 = g >= 0 ? a.pair_off[(int64_t)(g + 1) * kPairCols] : 0;
+      const long long per = ((i1 - i0 + NW - 1) / NW + 63) / 64 * 64;
+      sb = i0 + (long long)wid * per < i1 ? i0 + (long long)wid * per : i1;
+      se = sb + per < i1 ? sb + per : i1;
+    } else {
+      const long long dseg = has_delta ? ((dhi - 1 - dlo + NW - 1) / NW + 63) / 64 * 64 : 0;
+      sb = dlo + (long long)wid * dseg;
+      se = has_delta ? (sb + dseg < dhi - 1 ? sb + dseg : dhi - 1) : sb;
+    }
     const size_t dbase = hpos_offset(STAGED, a.S, a.T);
     const int H = (int)((dyn_bytes(STAGED, a.S, a.T, true) - dbase) / (4 * NW));
     uint32_t* recs = reinterpret_cast<uint32_t*>(dyn + dbase) + wid * H;
     int nrec = 0;
     if (has_delta) {
       int* wh = sm.whist[wid];
-      delta_scan_wave(a, dlo, sb, se, Lcap, sm.tail, lane, [&](long long x, int m) {
+      auto keep = [&](long long u, long long, int m) {
         const bool q = m >= 2;
         const uint64_t bal = __ballot(q);
         if (bal) {
           const int rk = nrec + lanes_before(bal);
-          if (q && rk < H) recs[rk] = ((uint32_t)(x - sb) << 6) | (uint32_t)(m - 2);
+          if (q && rk < H) recs[rk] = ((uint32_t)(u - sb) << 6) | (uint32_t)(m - 2);
           if (q) atomicAdd(&wh[m], 1);
           nrec += __popcll(bal);
         }
         return true;
-      });
+      };
+      if (listed) delta_list_wave(a, dlo, sb, se, Lcap, sm.tail, lane, keep);
+      else delta_scan_wave(a, dlo, sb, se, Lcap, sm.tail, lane, keep);
       wave_sync();
       // this wavefront's suffix sums: wsuf[w][v] = its occurrences of length >= v, v = lane + 1
       const int h = lane + 1 <= Lcap ? wh[lane + 1] : 0;
@@ -1175,19 +1249,24 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
           const bool q = e < kept && (int)(rc & 63u) + 2 >= l;
           const uint64_t bal = __ballot(q);
           const int rk = off + lanes_before(bal);
-          if (q && rk < M) gs[rk] = sb + (long long)(rc >> 6) + 1;
+          if (q && rk < M) {
+            const long long u = sb + (long long)(rc >> 6);
+            gs[rk] = (listed ? dlo + (long long)a.pair_list[u] : u) + 1;
+          }
           off += __popcll(bal);
         }
         if (nrec > H && off < M) {
           const long long from = sb + (long long)(recs[H - 1] >> 6) + 1;
-          delta_scan_wave(a, dlo, from, se, Lcap, sm.tail, lane, [&](long long x, int m) {
+          auto site = [&](long long, long long x, int m) {
             const bool q = m >= l;
             const uint64_t bal = __ballot(q);
             const int rk = off + lanes_before(bal);
             if (q && rk < M) gs[rk] = x + 1;
             off += __popcll(bal);
             return off < M;
-          });
+          };
+          if (listed) delta_list_wave(a, dlo, from, se, Lcap, sm.tail, lane, site);
+          else delta_scan_wave(a, dlo, from, se, Lcap, sm.tail, lane, site);
         }
       }
       __syncthreads();

@@ -19,6 +19,7 @@
 #include "corpus.h"
 #include "call_forms.h"
 #include "checks.h"
+#include "delta_index.h"
 #include "propose.h"
 #include "sa_build.h"
 
@@ -86,6 +87,20 @@ struct sfx_ctx {
   hipEvent_t ev_snap = nullptr;
   hipEvent_t ev_done = nullptr;
   int active_host = -1;  // host mirror of the live buffer
+  // per-call pair index of the delta (delta_index.h); absent above kPairMaxBatch rows
+  unsigned long long* pair_keys = nullptr;
+  int32_t* pair_gid = nullptr;
+  int32_t* pair_group = nullptr;
+  int32_t* pair_off = nullptr;
+  int32_t* pair_tmp = nullptr;
+  uint32_t* pair_list = nullptr;
+  uint32_t pair_slots = 0;
+  // Ingest calls so far, and how many of them the live index covers (that of the snapshot
+  // being built, for an asynchronous rebuild).  While they differ the corpus may hold a delta,
+  // and the step builds the pair index first.
+  uint64_t ingest_epoch = 0;
+  uint64_t live_epoch = 0;
+  uint64_t snap_epoch = 0;
   // asynchronous rebuild
   std::thread worker;
   std::atomic<int> async_state{0};  // 0 idle, 1 running, 2 finished
@@ -163,6 +178,12 @@ void free_ctx(sfx_ctx* c) {
     }
   }
   f(c->sa_ws);
+  f(c->pair_keys);
+  f(c->pair_gid);
+  f(c->pair_group);
+  f(c->pair_off);
+  f(c->pair_tmp);
+  f(c->pair_list);
   if (c->side) (void)hipStreamDestroy(c->side);
   if (c->ev_snap) (void)hipEventDestroy(c->ev_snap);
   if (c->ev_done) (void)hipEventDestroy(c->ev_done);
@@ -293,6 +314,7 @@ int swap_in(sfx_ctx* c, hipStream_t st) {
   HIP_OR_RETURN(hipStreamWaitEvent(st, c->ev_done, 0), "wait for rebuild");
   HIP_OR_RETURN(launch_swap(c->ctl, c->async_buf, c->async_mask, st), "swap launch");
   c->active_host = c->async_buf;
+  c->live_epoch = c->snap_epoch;
   c->async_state.store(0);
   return SFX_OK;
 }
@@ -370,6 +392,16 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
     }
     c->sa_ws_bytes = sa_workspace_bytes(c->cap);
     ok = ok && al(&c->sa_ws, c->sa_ws_bytes);
+    if (ok && cfg->max_batch >= 1 && cfg->max_batch <= kPairMaxBatch) {
+      const int mb = cfg->max_batch;
+      c->pair_slots = pair_slots(mb);
+      ok = al((void**)&c->pair_keys, 8 * (size_t)c->pair_slots) &&
+           al((void**)&c->pair_gid, 4 * (size_t)c->pair_slots) &&
+           al((void**)&c->pair_group, 4 * (size_t)mb) &&
+           al((void**)&c->pair_off, 4 * (size_t)(mb + 1) * kPairCols) &&
+           al((void**)&c->pair_tmp, 4 * pair_scan_tmp_ints(mb)) &&
+           al((void**)&c->pair_list, 4 * (size_t)c->cap);
+    }
     if (!ok) {
       free_ctx(c);
       return fail(SFX_ENOMEM, "device allocation failed for a corpus of %lld tokens",
@@ -466,6 +498,30 @@ static int propose_k(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
   a.ring_cap = c->cap > 0 ? c->cap : 1;
   a.stream_ctx = (g.flags & SFX_FLAG_STREAM_CONTEXT) != 0;
   a.pick = c->pick;
+  if (c->pair_list && B <= kPairMaxBatch && c->ingest_epoch != c->live_epoch) {
+    PairIndexArgs p{};
+    p.B = B;
+    p.S = S;
+    p.T = T;
+    p.D = g.max_tree_depth;
+    p.ntns = ntns;
+    p.tok = tok;
+    p.samp = samp;
+    p.ctl = c->ctl;
+    p.ring = c->ring;
+    p.ring_cap = c->cap;
+    p.keys = c->pair_keys;
+    p.gid = c->pair_gid;
+    p.slots = c->pair_slots;
+    p.group = c->pair_group;
+    p.off = c->pair_off;
+    p.scan_tmp = c->pair_tmp;
+    p.list = c->pair_list;
+    HIP_OR_RETURN(launch_pair_index(p, (hipStream_t)stream), "pair index launch");
+    a.pair_group = c->pair_group;
+    a.pair_off = c->pair_off;
+    a.pair_list = c->pair_list;
+  }
   HIP_OR_RETURN(launch_propose(a, (hipStream_t)stream), "propose launch");
   return SFX_OK;
 }
@@ -550,6 +606,7 @@ static int ingest_common(sfx_ctx* c, IngestArgs a, int hint, hipStream_t st) {
   a.doc_off = c->doc_off;
   a.doc_idx = c->doc_idx;
   const int R = a.R;
+  ++c->ingest_epoch;
   for (int r0 = 0; r0 < R; r0 += kIngestChunk) {
     IngestArgs ch = a;
     ch.R = R - r0 < kIngestChunk ? R - r0 : kIngestChunk;
@@ -656,6 +713,7 @@ int sfx_rebuild(sfx_ctx* c, void* stream) {
   if (c->async_state.load() != 0) return fail(SFX_ESTATE, "an asynchronous rebuild is in flight");
   hipStream_t st = (hipStream_t)stream;
   const int buf = pick_buffer(c);
+  const uint64_t epoch = c->ingest_epoch;
   HIP_OR_RETURN(launch_snapshot(c->ctl, c->ring, c->cap, c->idx[buf].text, buf, c->range_dev, st),
                 "snapshot launch");
   uint32_t mask = 0;
@@ -663,6 +721,7 @@ int sfx_rebuild(sfx_ctx* c, void* stream) {
   if (c->fail_next.exchange(0)) return fail(SFX_EHIP, "injected rebuild failure");
   HIP_OR_RETURN(launch_swap(c->ctl, buf, mask, st), "swap launch");
   c->active_host = buf;
+  c->live_epoch = epoch;
   return SFX_OK;
 }
 
@@ -678,6 +737,7 @@ int sfx_rebuild_async(sfx_ctx* c, void* stream) {
                 "snapshot launch");
   HIP_OR_RETURN(hipEventRecord(c->ev_snap, st), "snapshot event");
   c->async_buf = buf;
+  c->snap_epoch = c->ingest_epoch;
   c->async_err = SFX_OK;
   c->async_state.store(1);
   c->worker = std::thread([c, buf]() {
@@ -929,6 +989,7 @@ int sfx_load(sfx_ctx* c, const char* path, void* stream) {
   HIP_OR_RETURN(hipMemcpyAsync(c->ctl, &k, sizeof k, hipMemcpyHostToDevice, st), "control write");
   HIP_OR_RETURN(hipStreamSynchronize(st), "load wait");
   c->active_host = k.active;
+  ++c->ingest_epoch;  // the file's documents past its snapshot form a delta
   return SFX_OK;
 }
 

@@ -264,13 +264,75 @@ def test_full_depth_match(S, flags):
             d.close()
 
 
+# Above this many rows a context keeps no pair index of the delta, and every request scans the
+# delta itself: the tests below run both ways.
+NO_INDEX_BATCH = 1100
+
+
 @pytest.mark.parametrize("flags", FLAGS)
+@pytest.mark.parametrize("index", [True, False])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_fuzz_with_delta(S, mode, index, flags):
+    """Documents ingested after the last rebuild (the delta) from small vocabularies, so that
+    many requests share a tail pair, many pairs collide, and a pair occurs thousands of times;
+    rows without sampled tokens, with a negative token before the sampled one, shorter than two
+    tokens; rings that wrap and evict.  Drafts equal the oracle's on the live corpus, with the
+    per-call pair index and with the scan of the whole delta."""
+    import torch
+
+    rng = np.random.default_rng(500 + 2 * mode + index)
+    for it in range(12):
+        V = int(rng.choice([2, 3, 5, 12, 40]))
+        B = int(rng.integers(1, 160))
+        Sq = int(rng.integers(2, 300))
+        T = int(rng.integers(1, 4))
+        nb = 1 if mode == 0 else int(rng.integers(1, 9))
+        D = int(rng.choice([2, 3, 5, 9, 24]))
+        kn = dict(k=int(rng.integers(1, 17)), max_tree_depth=D, num_backoff=nb,
+                  max_occurrences=int(rng.choice([1, 5, 128])), mode=mode,
+                  spec_factor_ppm=int(rng.choice([1_000_000, 2_000_000])),
+                  min_token_prob_ppm=int(rng.choice([0, 100_000, 400_000])),
+                  min_corpus_match=int(rng.integers(2, D + 1)))
+        cap = int(rng.choice([3000, 1 << 14]))
+        seed = [rng.integers(0, V, size=int(rng.integers(0, 80))).astype(np.int32)
+                for _ in range(int(rng.integers(0, 30)))]
+        delta = [rng.integers(0, V, size=int(rng.integers(0, 400))).astype(np.int32)
+                 for _ in range(int(rng.integers(1, 40)))]
+        tok = rng.integers(0, V, size=(B, Sq)).astype(np.int32)
+        n = rng.integers(0, Sq + 1, size=B).astype(np.int32)
+        samp = rng.integers(0, V, size=(B, T)).astype(np.int32)
+        samp[rng.random((B, T)) < 0.15] = -1           # some rows stop early or draft nothing
+        neg = rng.random(B) < 0.05                     # a negative token before the sampled one
+        for b in np.nonzero(neg)[0]:
+            if n[b] > 0:
+                tok[b, n[b] - 1] = -3
+        cfg = S.Config(max_batch=NO_INDEX_BATCH if not index else max(B, 1), max_seq=Sq,
+                       max_sampled=T, corpus_capacity=cap, **kn)
+        d = S.Drafter(cfg)
+        lc = O.LiveCorpus(cap)
+        if seed:
+            d.ingest_docs(seed)
+            lc.ingest(seed)
+        d.rebuild()
+        d.ingest_docs(delta)
+        lc.ingest(delta)
+        exp = O.propose(O.params_from(kn), n, tok, samp, corpus=lc.text())
+        dd, dn = d.propose(dev(n), dev(tok), dev(samp))
+        torch.cuda.synchronize()
+        assert_same((dd.cpu().numpy(), dn.cpu().numpy()), exp,
+                    f"delta fuzz it={it} V={V} B={B} cap={cap} kn={kn}")
+        d.close()
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+@pytest.mark.parametrize("index", [True, False])
 @pytest.mark.parametrize("wrap", [False, True])
-def test_delta_many_short_matches(S, flags, wrap):
+def test_delta_many_short_matches(S, flags, wrap, index):
     """A delta with 20000 occurrences of exactly the last two context tokens, then three of the
-    last 24: far more short occurrences than any wavefront of the scan keeps, so the long
-    candidate's sites lie past every kept record and must be found again.  With wrap the delta
-    runs across the end of the ring and the oldest documents are evicted."""
+    last 24: far more short occurrences than any wavefront keeps, so the long candidate's sites
+    lie past every kept record and must be found again.  With wrap the delta runs across the end
+    of the ring and the oldest documents are evicted.  Run with the per-call pair index and with
+    the scan of the whole delta."""
     import torch
 
     rng = np.random.default_rng(77)
@@ -289,8 +351,8 @@ def test_delta_many_short_matches(S, flags, wrap):
     for mode, nb in ((0, 1), (1, 4)):
         kn = dict(k=8, max_tree_depth=24, num_backoff=nb, max_occurrences=128, mode=mode,
                   spec_factor_ppm=2_000_000, min_token_prob_ppm=100_000)
-        cfg = S.Config(max_batch=2, max_seq=n, max_sampled=1, corpus_capacity=cap,
-                       flags=flags, **kn)
+        cfg = S.Config(max_batch=2 if index else NO_INDEX_BATCH, max_seq=n, max_sampled=1,
+                       corpus_capacity=cap, flags=flags, **kn)
         d = S.Drafter(cfg)
         lc = O.LiveCorpus(cap)
         d.ingest_docs(seed)
