@@ -111,7 +111,8 @@ typedef struct sfx_config {
 typedef struct sfx_ctx sfx_ctx;
 
 /* Validates *cfg and allocates every device buffer the context will ever use (rows scratch,
- * corpus ring, double-buffered corpus index, control block) on the current HIP device.
+ * corpus ring, double-buffered corpus index, control block and, for max_batch <= 1024, the
+ * per-call pair index of the delta) on the current HIP device.
  * Returns SFX_EINVAL for a configuration outside the ranges above, SFX_ENOMEM when device
  * memory runs out.  *out receives the context. */
 int sfx_create(const sfx_config* cfg, sfx_ctx** out);
@@ -131,7 +132,11 @@ const char* sfx_last_error(void);
  *                            (LONGEST_FILL) or -1 (SCORED); all -1 when a row has no sampled id
  *   num_valid          [B]   out: number of proposed ids
  * Token ids must be >= 0.  Requires B <= max_batch, S <= max_seq, T <= max_sampled
- * (else SFX_ECAPACITY).  Reads the corpus index that is live when the kernel runs. */
+ * (else SFX_ECAPACITY).  Reads the corpus index that is live when the kernel runs.  While some
+ * ingest since the context's last swapped-in rebuild is pending (and B <= 1024), the call first
+ * groups the delta's positions by the batch's tail pairs (four small passes on `stream`,
+ * no allocation); otherwise, or in a graph captured without them, each request scans the
+ * delta itself.  Both give the same result. */
 int sfx_propose(sfx_ctx* ctx, int32_t B, int32_t S, int32_t T, const int32_t* num_tokens_no_spec,
                 const int32_t* token_ids, const int32_t* sampled, int32_t* draft,
                 int32_t* num_valid, void* stream);
@@ -171,7 +176,7 @@ int sfx_update_state(int32_t B, int32_t S, int32_t T, int32_t* token_ids,
  * in r order and followed by one -1 separator; afterwards the oldest documents are evicted
  * while the live total exceeds corpus_capacity.  token_ids is [num_rows, S]; a row index
  * outside [0, num_rows) makes an empty document.  New documents become visible to
- * sfx_propose at once (through the delta scan until the next rebuild is swapped in).
+ * sfx_propose at once (matched in the delta until the next rebuild is swapped in).
  * SFX_ESTATE when the context has no corpus. */
 int sfx_harvest_finished(sfx_ctx* ctx, int32_t R, const int32_t* row_indices,
                          const int32_t* lengths, const int32_t* token_ids, int32_t num_rows,
