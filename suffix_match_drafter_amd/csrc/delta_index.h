@@ -19,14 +19,15 @@
 namespace sfx {
 
 constexpr int kPairMaxBatch = 1024;     // batches above this scan the delta instead
-constexpr int kPairCols = 1024;         // wavefront slices of the delta
+constexpr int kPairCols = 2048;         // wavefront slices of the delta
 constexpr int kPairColsPerBlock = 4;    // 256-thread workgroups of four slices
 
-// Hash-table slots for a batch of up to max_batch requests: a power of two, at least twice
-// the batch.
+// Hash-table slots for a batch of up to max_batch requests: a power of two, at least four
+// times the batch up to 2048 slots (so at least twice any batch), which keeps the probe runs
+// of the many positions whose pair is no request's short.
 inline uint32_t pair_slots(int max_batch) {
   uint32_t s = 64;
-  while (s < 2u * (uint32_t)max_batch) s <<= 1;
+  while (s < 4u * (uint32_t)max_batch && s < 2u * kPairMaxBatch) s <<= 1;
   return s;
 }
 
