@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 KERNEL_SOURCES = ("suffix_match_drafter_amd/csrc/propose.hip",
                   "suffix_match_drafter_amd/csrc/propose.h",
+                  "suffix_match_drafter_amd/csrc/delta_index.h",
                   "suffix_match_drafter_amd/csrc/sfx_internal.h")
 
 

@@ -3,9 +3,11 @@ decode graphs; suffix-gpu page, Highlights: static shapes, no host synchronisati
 without moving buffers).
 
 sfx_propose is captured once and replayed while the program's own eager work runs between the
-replays: new documents are harvested (so the next replay must see them through the delta scan),
-rebuilds are swapped in, and the input rows are rewritten in place.  Every replay must equal an
-eager call and the oracle on the live corpus."""
+replays: new documents are harvested (so the next replay must find them in the delta), rebuilds
+are swapped in, and the input rows are rewritten in place.  Every replay must equal an eager call
+and the oracle on the live corpus.  A step captured while an ingest is pending records the passes
+that index the delta by tail pair, and its replays run them; one captured with nothing pending
+records none, and its replays scan the delta instead."""
 import numpy as np
 import pytest
 
@@ -15,7 +17,8 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-def test_captured_propose_follows_corpus_and_inputs():
+@pytest.mark.parametrize("pending", [False, True])
+def test_captured_propose_follows_corpus_and_inputs(pending):
     import torch
 
     assert torch.cuda.is_available(), "GPU tests need a HIP device"
@@ -31,6 +34,9 @@ def test_captured_propose_follows_corpus_and_inputs():
     d.ingest_docs(docs[:100])
     lc.ingest(docs[:100])
     d.rebuild()
+    if pending:  # documents past the live index at capture time
+        d.ingest_docs(docs[400:420])
+        lc.ingest(docs[400:420])
     p = O.params_from(knobs)
 
     n0, tok0, samp0 = W.make_batch(2, set_index=0, B=B)
