@@ -381,61 +381,73 @@ __device__ __forceinline__ void delta_scan_wave(const ProposeArgs& a, long long 
   }
 }
 
-constexpr int kListRound = 4;  // tokens compared per round trip when extending listed entries
+constexpr int kListRound = 4;    // tokens compared per round trip when extending listed entries
+constexpr int kListBatches = 4;  // 64-entry batches whose first loads are issued together
 
 // The same occurrences from the per-call pair index: entries [i0, i1) of the request's group
 // list hold, in position order, the offsets from dlo of the delta positions that end with the
 // tail's last two tokens and are followed by a real token.  All 64 lanes extend an entry each:
-// one token, then kListRound tokens per round trip, so a batch waits for about one round trip
-// per kListRound tokens of its longest match.  f(i, x, m) gets each lane's entry index, position
-// and match length (0 past i1).
+// the next token (where most occurrences of a frequent pair end), then kListRound tokens per
+// round trip.  The list entries and next tokens of kListBatches batches are loaded together,
+// so a wavefront waits for two round trips per kListBatches batches plus the rounds of its
+// longest matches.  f(i, x, m) gets, batch by batch in order, each lane's entry index,
+// position and match length (0 past i1).
 template <typename F>
 __device__ __forceinline__ void delta_list_wave(const ProposeArgs& a, long long dlo, long long i0,
                                                 long long i1, int Lcap, const int* tail,
                                                 int lane, F&& f) {
   const int cap = (int)a.ring_cap;
   const int dslot = (int)(dlo % a.ring_cap);
-  for (long long e = i0; e < i1; e += 64) {
-    const long long i = e + lane;
-    long long x = 0;
-    int m = 0;
-    if (i < i1) {
-      const uint32_t o = a.pair_list[i];
-      x = dlo + (long long)o;
-      int s = dslot + (int)o;
-      if (s >= cap) s -= cap;
-      // length m extends while m < Lcap and position x - m is still in the delta.  Most
-      // occurrences of a frequent pair end at the next token, which is read alone; the lanes
-      // that match it go on in rounds.
-      const int lim = (long long)Lcap <= x - dlo ? Lcap : (int)(x - dlo) + 1;
-      m = 2;
-      if (m < lim) {
-        int q = s - 2;
-        if (q < 0) q += cap;
-        const int c = a.ring[q];
-        if (c >= 0 && c == tail[2]) m = 3;
-      }
-      while (m > 2 && m < lim) {
-        int v[kListRound];
+  for (long long e0 = i0; e0 < i1; e0 += 64 * kListBatches) {
+    uint32_t o[kListBatches];
 #pragma unroll
-        for (int j = 0; j < kListRound; ++j) {
-          int q = s - m - j;  // m + j < lim <= the delta's length <= cap: one wrap at most
-          if (q < 0) q += cap;
-          v[j] = m + j < lim ? a.ring[q] : -2;
-        }
-        int run = 0;
-        bool stop = false;
-#pragma unroll
-        for (int j = 0; j < kListRound; ++j) {
-          const int tj = m + j < kMaxD ? m + j : kMaxD - 1;
-          stop = stop || v[j] < 0 || v[j] != tail[tj];
-          run += stop ? 0 : 1;
-        }
-        m += run;
-        if (stop) break;
-      }
+    for (int u = 0; u < kListBatches; ++u) {
+      const long long i = e0 + 64 * u + lane;
+      o[u] = i < i1 ? a.pair_list[i] : 0u;
     }
-    if (!f(i, x, m)) return;
+    int sl[kListBatches], lim[kListBatches], nxt[kListBatches];
+#pragma unroll
+    for (int u = 0; u < kListBatches; ++u) {
+      const long long i = e0 + 64 * u + lane;
+      const long long x = dlo + (long long)o[u];
+      int sx = dslot + (int)o[u];
+      if (sx >= cap) sx -= cap;
+      sl[u] = sx;
+      // length m extends while m < Lcap and position x - m is still in the delta
+      lim[u] = i >= i1 ? 0 : ((long long)Lcap <= x - dlo ? Lcap : (int)(x - dlo) + 1);
+      int q = sx - 2;
+      if (q < 0) q += cap;
+      nxt[u] = 2 < lim[u] ? a.ring[q] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kListBatches; ++u) {
+      if (e0 + 64 * u >= i1) return;  // uniform: no entry left
+      const long long i = e0 + 64 * u + lane;
+      int m = 0;
+      if (i < i1) {
+        m = nxt[u] >= 0 && nxt[u] == tail[2] ? 3 : 2;
+        while (m > 2 && m < lim[u]) {
+          int v[kListRound];
+#pragma unroll
+          for (int j = 0; j < kListRound; ++j) {
+            int q = sl[u] - m - j;  // m + j < lim <= the delta's length <= cap: one wrap at most
+            if (q < 0) q += cap;
+            v[j] = m + j < lim[u] ? a.ring[q] : -2;
+          }
+          int run = 0;
+          bool stop = false;
+#pragma unroll
+          for (int j = 0; j < kListRound; ++j) {
+            const int tj = m + j < kMaxD ? m + j : kMaxD - 1;
+            stop = stop || v[j] < 0 || v[j] != tail[tj];
+            run += stop ? 0 : 1;
+          }
+          m += run;
+          if (stop) break;
+        }
+      }
+      if (!f(i, dlo + (long long)o[u], m)) return;
+    }
   }
 }
 
@@ -1155,7 +1167,11 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
         if (bal) {
           const int rk = nrec + lanes_before(bal);
           if (q && rk < H) recs[rk] = ((uint32_t)(u - sb) << 6) | (uint32_t)(m - 2);
-          if (q) atomicAdd(&wh[m], 1);
+          // length 2 (most occurrences of a frequent pair) counted from one ballot, not with
+          // one conflicting LDS atomic per lane
+          const uint64_t two = __ballot(m == 2);
+          if (m > 2) atomicAdd(&wh[m], 1);
+          if (lane == 0 && two) atomicAdd(&wh[2], __popcll(two));
           nrec += __popcll(bal);
         }
         return true;
