@@ -11,10 +11,11 @@
 //   2. global match (step 2; vLLM docs, Model Runner V2: probe by the last 2 and last 4 tokens,
 //      extend to the longest match): 2-, 3- and 4-gram probes into hash tables over the
 //      suffix-array groups of the live snapshot and backward extension of the 4-gram
-//      occurrences.  Without a delta, a dedicated wavefront does all of it -- probes, ladder and
-//      sites -- while the other fifteen work through the local match, which synchronise among
-//      themselves only.  With a delta (documents appended since the snapshot) the whole
-//      workgroup scans the delta by brute force and merges;
+//      occurrences.  With a live snapshot, a dedicated wavefront does it while the other
+//      fifteen work through the local match, which synchronise among themselves only; without
+//      a delta it also derives the corpus ladder and sites.  With a delta (documents appended
+//      since the snapshot) the whole workgroup then finds the delta's occurrences -- from the
+//      per-call pair index, or by a brute-force scan -- and merges;
 //   3. expansion (step 3): one wavefront per candidate votes depth by depth over its sites
 //      (one ballot pair when every alive site agrees or one token holds a majority, ballots
 //      per token when few sites are alive, an LDS hash otherwise); stop rule and score use
@@ -182,7 +183,7 @@ struct Smem {
 struct Req {
   int n, t, L, J, Lcap;
   int act;
-  bool has, fast;
+  bool has, fast, delta;
   long long snap_start, snap_n, tail_w, delta_lo, delta_hi;
   uint32_t ht_mask;
 };
@@ -947,6 +948,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     r.has = a.ctl != nullptr;
     r.act = -1;
     r.fast = false;
+    r.delta = false;
     r.snap_start = r.snap_n = r.tail_w = r.delta_lo = r.delta_hi = 0;
     r.ht_mask = 0;
     bool delta = false;
@@ -965,7 +967,8 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
         r.delta_lo = r.tail_w;
       }
       delta = r.delta_hi - r.delta_lo > 1;
-      r.fast = r.act >= 0 && r.snap_n > 0 && !delta && r.Lcap >= 2;
+      r.delta = delta;
+      r.fast = r.act >= 0 && r.snap_n > 0 && r.Lcap >= 2;
     }
   }
   const int n = r.n, t = r.t, L = r.L, Lcap = r.Lcap, J = r.J;
@@ -1010,7 +1013,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   }
   if (fast && wid == GW) {
     corpus_wave_probe(a, r, sm, row, smp, lane);
-    corpus_wave_sites(a, r, sm, lane);
+    if (!r.delta) corpus_wave_sites(a, r, sm, lane);
   } else {
     uint16_t* hpos = hpos_all + cbeg;
     uint8_t* hmb = hmb_all + cbeg;
@@ -1101,9 +1104,12 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   }
 
   // ---------------------------------------------------------------- 2. global (general path)
-  if (r.has && !fast && Lcap >= 2) {
+  if (r.has && (!fast || r.delta) && Lcap >= 2) {
+    // With a live snapshot and a delta, the corpus wavefront has probed the snapshot beside the
+    // local phase (its results stand); the workers may use their histograms until here.
+    if (fast) __syncthreads();
     if (tid <= kMaxD) {
-      sm.ghist[tid] = 0;
+      if (!fast) sm.ghist[tid] = 0;
       sm.dhist[tid] = 0;
     }
     for (int i = tid; i < NW * (kMaxD + 1); i += NT) (&sm.whist[0][0])[i] = 0;
@@ -1117,7 +1123,9 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       sm.plp[1] = ib.pl1;
       sm.plp[2] = ib.pl2;
     }
-    if (act >= 0 && r.snap_n > 0) {
+    if (fast) {
+      // probed already
+    } else if (act >= 0 && r.snap_n > 0) {
       if (tid == 0) probe_ngram<0>(ib, sm.tail, Lcap, dead_below, &sm.g_off[0], &sm.g_live[0]);
       if (tid == 1) probe_ngram<1>(ib, sm.tail, Lcap, dead_below, &sm.g_off[1], &sm.g_live[1]);
       if (tid == 2) probe_ngram<2>(ib, sm.tail, Lcap, dead_below, &sm.g_off[2], &sm.g_live[2]);
@@ -1127,7 +1135,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     }
     __syncthreads();
     const int live4 = sm.g_live[2];
-    if (act >= 0 && Lcap >= 5 && live4 > 0) {
+    if (!fast && act >= 0 && Lcap >= 5 && live4 > 0) {
       const int32_t* pl4 = ib.pl2 + sm.g_off[2];
       for (int x = tid; x < live4; x += NT) {
         const int m = extend4(ib.text, sm.tail, pl4[x], Lcap);
