@@ -20,7 +20,7 @@ namespace sfx {
 
 constexpr int kPairMaxBatch = 1024;     // batches above this scan the delta instead
 constexpr int kPairCols = 2048;         // wavefront slices of the delta
-constexpr int kPairColsPerBlock = 4;    // 256-thread workgroups of four slices
+constexpr int kPairColsPerBlock = 8;    // 512-thread workgroups of eight slices
 
 // Hash-table slots for a batch of up to max_batch requests: a power of two, at least four
 // times the batch up to 2048 slots (so at least twice any batch), which keeps the probe runs

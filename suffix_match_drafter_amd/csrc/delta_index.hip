@@ -120,15 +120,19 @@ __global__ __launch_bounds__(1024) void pair_table_kernel(PairIndexArgs a) {
 
 constexpr int kSliceRuns = 4;  // 64-position runs whose loads a wavefront issues together
 
-// Passes 2 and 4 (workgroups of four wavefronts, one delta slice each).  The delta's end
+// Passes 2 and 4 (workgroups of kPairColsPerBlock wavefronts, one delta slice each).  The delta's end
 // positions lo + 1 .. hi - 2 are cut into kPairCols slices of whole 64-position runs, and
 // wavefront column c takes slice c.  A position belongs to group g when (token before, token
 // at it) is group g's pair and a real token follows it.  COUNT: the slice's count per group
 // goes to off[g * kPairCols + c] (zeros too, so the scan sees every entry).  Otherwise off
 // holds the exclusive scan of those counts, and the slice writes its positions' offsets from
-// lo to list[] from there, in position order within each group.
+// lo to list[] from there, in position order within each group.  The workgroup moves its
+// block of columns to and from off[] together, so that each group's kPairColsPerBlock
+// consecutive entries are one access.
+constexpr int kSliceThreads = 64 * kPairColsPerBlock;
+
 template <bool COUNT>
-__global__ __launch_bounds__(256) void pair_slices_kernel(PairIndexArgs a) {
+__global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArgs a) {
   __shared__ unsigned long long hk[2 * kPairMaxBatch];
   __shared__ int hg[2 * kPairMaxBatch];
   __shared__ int cur[kPairColsPerBlock][kPairMaxBatch + 1];
@@ -140,32 +144,39 @@ __global__ __launch_bounds__(256) void pair_slices_kernel(PairIndexArgs a) {
   const bool any = delta_range(a.ctl, &lo, &hi);
   if (!COUNT && !any) return;  // uniform over the grid: the step reads no list
   {
-    // the table (at most 2048 slots) and this column's counters, loads issued together
-    constexpr int kTab = 2 * kPairMaxBatch / 256, kCur = (kPairMaxBatch + 1 + 63) / 64;
+    // the table (at most 2048 slots) and the block's counters, loads issued together; entry
+    // e of the block is group e / kPairColsPerBlock of column e % kPairColsPerBlock
+    constexpr int kTab = 2 * kPairMaxBatch / kSliceThreads;
+    constexpr int kCur = (kPairColsPerBlock * (kPairMaxBatch + 1) + kSliceThreads - 1) / kSliceThreads;
+    const int col0 = blockIdx.x * kPairColsPerBlock;
     unsigned long long tk[kTab];
     int tg[kTab], tc[kCur];
 #pragma unroll
     for (int j = 0; j < kTab; ++j) {
-      const uint32_t i = tid + 256 * j;
+      const uint32_t i = tid + kSliceThreads * j;
       tk[j] = i < a.slots ? a.keys[i] : kNoPair;
       tg[j] = i < a.slots ? a.gid[i] : -1;
     }
 #pragma unroll
     for (int j = 0; j < kCur; ++j) {
-      const int g = lane + 64 * j;
-      tc[j] = (!COUNT && g < ng) ? a.off[(int64_t)g * kPairCols + col] : 0;
+      const int e = tid + kSliceThreads * j;
+      const int g = e / kPairColsPerBlock, c = e % kPairColsPerBlock;
+      tc[j] = (!COUNT && g < ng) ? a.off[(int64_t)g * kPairCols + col0 + c] : 0;
     }
 #pragma unroll
     for (int j = 0; j < kTab; ++j) {
-      const uint32_t i = tid + 256 * j;
+      const uint32_t i = tid + kSliceThreads * j;
       if (i < a.slots) {
         hk[i] = tk[j];
         hg[i] = tg[j];
       }
     }
 #pragma unroll
-    for (int j = 0; j < kCur; ++j)
-      if (lane + 64 * j < ng) cur[w][lane + 64 * j] = tc[j];
+    for (int j = 0; j < kCur; ++j) {
+      const int e = tid + kSliceThreads * j;
+      const int g = e / kPairColsPerBlock, c = e % kPairColsPerBlock;
+      if (g < ng) cur[c][g] = tc[j];
+    }
   }
   __syncthreads();
   const long long nd = any ? hi - lo - 2 : 0;
@@ -228,10 +239,12 @@ __global__ __launch_bounds__(256) void pair_slices_kernel(PairIndexArgs a) {
     }
   }
   if (COUNT) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int g = lane; g < ng; g += 64) a.off[(int64_t)g * kPairCols + col] = cur[w][g];
+    __syncthreads();
+    const int col0 = blockIdx.x * kPairColsPerBlock;
+    for (int e = tid; e < kPairColsPerBlock * ng; e += kSliceThreads) {
+      const int g = e / kPairColsPerBlock, c = e % kPairColsPerBlock;
+      a.off[(int64_t)g * kPairCols + col0 + c] = cur[c][g];
+    }
   }
 }
 
@@ -249,12 +262,12 @@ hipError_t launch_pair_index(const PairIndexArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(pair_table_kernel, dim3(1), dim3(1024), 0, st, a);
   const dim3 grid(kPairCols / kPairColsPerBlock);
-  hipLaunchKernelGGL((pair_slices_kernel<true>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((pair_slices_kernel<true>), grid, dim3(kSliceThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = scan_sum_exclusive(a.off, a.off, (int64_t)(a.B + 1) * kPairCols, a.scan_tmp, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((pair_slices_kernel<false>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((pair_slices_kernel<false>), grid, dim3(kSliceThreads), 0, st, a);
   return hipGetLastError();
 }
 
