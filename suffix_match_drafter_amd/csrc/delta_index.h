@@ -8,8 +8,9 @@
 // end some request's context:
 //   1. one workgroup hashes the batch's distinct tail pairs to dense group numbers;
 //   2. every wavefront column counts, per group, the occurrences in its slice of the delta;
-//   3. an exclusive scan over (group, column) gives every slice its place in the list;
-//   4. the slices write their occurrences' offsets (from the delta start), in position order.
+//   3. one workgroup per group scans that group's counts over the columns and totals them;
+//   4. every slice workgroup turns the totals into group starts, and the slices write their
+//      occurrences' offsets (from the delta start), in position order.
 // A request then extends only its own group's occurrences, which are exactly those the scan
 // would find, in the same order.
 #pragma once
@@ -43,13 +44,12 @@ struct PairIndexArgs {
   int32_t* gid;              // [slots] their dense group numbers
   uint32_t slots;
   int32_t* group;            // [B] out: the request's group, or -1 when it takes no delta scan
-  int32_t* off;              // [(B + 1) * kPairCols] counts, then list offsets in place
-  int32_t* scan_tmp;         // [ceil((B + 1) * kPairCols / 4096)]
+  int32_t* off;              // [(B + 1) * kPairCols] counts, then their prefix within a group
+  int32_t* tot;              // [B + 1] out: occurrences of each group
+  int32_t* base;             // [B + 1] out: start of each group's entries in list
   uint32_t* list;            // [ring_cap] occurrence offsets from the delta start
 };
 
-// Ints of scan scratch for a batch of B.
-size_t pair_scan_tmp_ints(int B);
 hipError_t launch_pair_index(const PairIndexArgs& a, hipStream_t st);
 
 }  // namespace sfx

@@ -10,8 +10,6 @@
 // group keeps position order, which is the logical order the step's site rule needs.
 #include "delta_index.h"
 
-#include "sa_build.h"
-
 namespace sfx {
 
 namespace {
@@ -125,8 +123,10 @@ constexpr int kSliceRuns = 4;  // 64-position runs whose loads a wavefront issue
 // wavefront column c takes slice c.  A position belongs to group g when (token before, token
 // at it) is group g's pair and a real token follows it.  COUNT: the slice's count per group
 // goes to off[g * kPairCols + c] (zeros too, so the scan sees every entry).  Otherwise off
-// holds the exclusive scan of those counts, and the slice writes its positions' offsets from
-// lo to list[] from there, in position order within each group.  The workgroup moves its
+// holds those counts' exclusive prefix within each group and tot the group totals; the
+// workgroup derives the group starts (and workgroup 0 stores them), and the slice writes its
+// positions' offsets from lo to list[] from base[g] + off[g * kPairCols + c] on, in position
+// order within each group.  The workgroup moves its
 // block of columns to and from off[] together, so that each group's kPairColsPerBlock
 // consecutive entries are one access.
 constexpr int kSliceThreads = 64 * kPairColsPerBlock;
@@ -136,6 +136,8 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
   __shared__ unsigned long long hk[2 * kPairMaxBatch];
   __shared__ int hg[2 * kPairMaxBatch];
   __shared__ int cur[kPairColsPerBlock][kPairMaxBatch + 1];
+  __shared__ int gbase[kPairMaxBatch + 1];
+  __shared__ int wsum[kPairColsPerBlock];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = blockIdx.x * kPairColsPerBlock + w;
@@ -149,8 +151,9 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
     constexpr int kTab = 2 * kPairMaxBatch / kSliceThreads;
     constexpr int kCur = (kPairColsPerBlock * (kPairMaxBatch + 1) + kSliceThreads - 1) / kSliceThreads;
     const int col0 = blockIdx.x * kPairColsPerBlock;
+    constexpr int kTot = (kPairMaxBatch + 1 + kSliceThreads - 1) / kSliceThreads;
     unsigned long long tk[kTab];
-    int tg[kTab], tc[kCur];
+    int tg[kTab], tc[kCur], tt[kTot];
 #pragma unroll
     for (int j = 0; j < kTab; ++j) {
       const uint32_t i = tid + kSliceThreads * j;
@@ -163,6 +166,12 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
       const int g = e / kPairColsPerBlock, c = e % kPairColsPerBlock;
       tc[j] = (!COUNT && g < ng) ? a.off[(int64_t)g * kPairCols + col0 + c] : 0;
     }
+    // thread t holds the totals of groups kTot * t .. kTot * t + kTot - 1
+#pragma unroll
+    for (int j = 0; j < kTot; ++j) {
+      const int g = kTot * tid + j;
+      tt[j] = (!COUNT && g < ng) ? a.tot[g] : 0;
+    }
 #pragma unroll
     for (int j = 0; j < kTab; ++j) {
       const uint32_t i = tid + kSliceThreads * j;
@@ -171,11 +180,36 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
         hg[i] = tg[j];
       }
     }
+    if (!COUNT) {
+      // group starts: exclusive prefix of the totals over the workgroup
+      int sum = 0;
+#pragma unroll
+      for (int j = 0; j < kTot; ++j) sum += tt[j];
+      int incl = sum;
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+      }
+      if (lane == 63) wsum[w] = incl;
+      __syncthreads();
+      int run = incl - sum;
+      for (int v = 0; v < w; ++v) run += wsum[v];
+#pragma unroll
+      for (int j = 0; j < kTot; ++j) {
+        const int g = kTot * tid + j;
+        if (g < ng) {
+          gbase[g] = run;
+          if (blockIdx.x == 0) a.base[g] = run;
+        }
+        run += tt[j];
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int j = 0; j < kCur; ++j) {
       const int e = tid + kSliceThreads * j;
       const int g = e / kPairColsPerBlock, c = e % kPairColsPerBlock;
-      if (g < ng) cur[c][g] = tc[j];
+      if (g < ng) cur[c][g] = COUNT ? tc[j] : tc[j] + gbase[g];
     }
   }
   __syncthreads();
@@ -248,12 +282,45 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
   }
 }
 
-}  // namespace
+// Pass 3 (one 256-thread workgroup per group g <= B): the exclusive prefix of the group's
+// per-slice counts over the slices, in place, and its total.
+constexpr int kRowThreads = 256;
+constexpr int kRowItems = kPairCols / kRowThreads;
 
-size_t pair_scan_tmp_ints(int B) {
-  const int64_t m = (int64_t)(B + 1) * kPairCols;
-  return (size_t)((m + 4095) / 4096);
+__global__ __launch_bounds__(kRowThreads) void pair_rowscan_kernel(PairIndexArgs a) {
+  __shared__ int wsum[kRowThreads / 64];
+  long long lo, hi;
+  if (!delta_range(a.ctl, &lo, &hi)) return;  // uniform over the grid: the step reads no list
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int32_t* row = a.off + (int64_t)blockIdx.x * kPairCols + kRowItems * tid;
+  int v[kRowItems];
+#pragma unroll
+  for (int j = 0; j < kRowItems; ++j) v[j] = row[j];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < kRowItems; ++j) sum += v[j];
+  int incl = sum;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int run = incl - sum, total = 0;
+  for (int u = 0; u < kRowThreads / 64; ++u) {
+    if (u < w) run += wsum[u];
+    total += wsum[u];
+  }
+#pragma unroll
+  for (int j = 0; j < kRowItems; ++j) {
+    const int x = v[j];
+    row[j] = run;
+    run += x;
+  }
+  if (tid == 0) a.tot[blockIdx.x] = total;
 }
+
+}  // namespace
 
 hipError_t launch_pair_index(const PairIndexArgs& a, hipStream_t st) {
   if (a.B <= 0) return hipSuccess;
@@ -263,10 +330,7 @@ hipError_t launch_pair_index(const PairIndexArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(pair_table_kernel, dim3(1), dim3(1024), 0, st, a);
   const dim3 grid(kPairCols / kPairColsPerBlock);
   hipLaunchKernelGGL((pair_slices_kernel<true>), grid, dim3(kSliceThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = scan_sum_exclusive(a.off, a.off, (int64_t)(a.B + 1) * kPairCols, a.scan_tmp, st);
-  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pair_rowscan_kernel, dim3(a.B + 1), dim3(kRowThreads), 0, st, a);
   hipLaunchKernelGGL((pair_slices_kernel<false>), grid, dim3(kSliceThreads), 0, st, a);
   return hipGetLastError();
 }

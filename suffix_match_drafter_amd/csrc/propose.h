@@ -26,7 +26,8 @@ struct ProposeArgs {
   // per-call index of the delta's tail-pair occurrences (delta_index.h), or nullptr, in which
   // case a request scans the whole delta
   const int32_t* pair_group;
-  const int32_t* pair_off;
+  const int32_t* pair_base;  // [B + 1] start of each group's entries in pair_list
+  const int32_t* pair_tot;   // [B + 1] their number
   const uint32_t* pair_list;
 };
 

@@ -1153,8 +1153,8 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     long long sb, se;
     if (listed) {
       const int g = a.pair_group[b];
-      const long long i0 = g >= 0 ? a.pair_off[(int64_t)g * kPairCols] : 0;
-      const long long i1 = g >= 0 ? a.pair_off[(int64_t)(g + 1) * kPairCols] : 0;
+      const long long i0 = g >= 0 ? a.pair_base[g] : 0;
+      const long long i1 = g >= 0 ? i0 + a.pair_tot[g] : 0;
       const long long per = ((i1 - i0 + NW - 1) / NW + 63) / 64 * 64;
       sb = i0 + (long long)wid * per < i1 ? i0 + (long long)wid * per : i1;
       se = sb + per < i1 ? sb + per : i1;

@@ -24,11 +24,6 @@ struct SaWork {
 size_t sa_workspace_bytes(int64_t n);
 SaWork sa_carve(void* ws, int64_t n);
 
-// Exclusive prefix sums of in[0..m) into out (which may be in), with scratch tmp of
-// ceil(m / 4096) ints.
-hipError_t scan_sum_exclusive(const int32_t* in, int32_t* out, int64_t m, int32_t* tmp,
-                              hipStream_t st);
-
 // Builds sa[0..n) of text[0..n) on `st`.  The host waits for `st` once per doubling round to
 // read the number of distinct ranks.  *rounds_out (optional) receives the rounds run.
 hipError_t sa_build(const int32_t* text, int64_t n, int32_t* sa, const SaWork& w, hipStream_t st,

@@ -350,11 +350,6 @@ inline int bits_for(uint64_t maxv) {
 }  // namespace
 
 // ------------------------------------------------------------------ workspace
-hipError_t scan_sum_exclusive(const int32_t* in, int32_t* out, int64_t m, int32_t* tmp,
-                              hipStream_t st) {
-  return scan_i32<0, 0>(in, out, m, tmp, st);
-}
-
 size_t sa_workspace_bytes(int64_t n) {
   const int64_t nn = n < 1 ? 1 : n;
   const int64_t nt = cdiv(nn, RS_TILE);

@@ -92,7 +92,8 @@ struct sfx_ctx {
   int32_t* pair_gid = nullptr;
   int32_t* pair_group = nullptr;
   int32_t* pair_off = nullptr;
-  int32_t* pair_tmp = nullptr;
+  int32_t* pair_tot = nullptr;
+  int32_t* pair_base = nullptr;
   uint32_t* pair_list = nullptr;
   uint32_t pair_slots = 0;
   // Ingest calls so far, and how many of them the live index covers (that of the snapshot
@@ -182,7 +183,8 @@ void free_ctx(sfx_ctx* c) {
   f(c->pair_gid);
   f(c->pair_group);
   f(c->pair_off);
-  f(c->pair_tmp);
+  f(c->pair_tot);
+  f(c->pair_base);
   f(c->pair_list);
   if (c->side) (void)hipStreamDestroy(c->side);
   if (c->ev_snap) (void)hipEventDestroy(c->ev_snap);
@@ -399,7 +401,8 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
            al((void**)&c->pair_gid, 4 * (size_t)c->pair_slots) &&
            al((void**)&c->pair_group, 4 * (size_t)mb) &&
            al((void**)&c->pair_off, 4 * (size_t)(mb + 1) * kPairCols) &&
-           al((void**)&c->pair_tmp, 4 * pair_scan_tmp_ints(mb)) &&
+           al((void**)&c->pair_tot, 4 * (size_t)(mb + 1)) &&
+           al((void**)&c->pair_base, 4 * (size_t)(mb + 1)) &&
            al((void**)&c->pair_list, 4 * (size_t)c->cap);
     }
     if (!ok) {
@@ -515,11 +518,13 @@ static int propose_k(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
     p.slots = c->pair_slots;
     p.group = c->pair_group;
     p.off = c->pair_off;
-    p.scan_tmp = c->pair_tmp;
+    p.tot = c->pair_tot;
+    p.base = c->pair_base;
     p.list = c->pair_list;
     HIP_OR_RETURN(launch_pair_index(p, (hipStream_t)stream), "pair index launch");
     a.pair_group = c->pair_group;
-    a.pair_off = c->pair_off;
+    a.pair_base = c->pair_base;
+    a.pair_tot = c->pair_tot;
     a.pair_list = c->pair_list;
   }
   HIP_OR_RETURN(launch_propose(a, (hipStream_t)stream), "propose launch");
