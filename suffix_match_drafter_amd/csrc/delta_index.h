@@ -3,13 +3,14 @@
 // The delta (documents appended since the live snapshot) has no suffix array, so its
 // occurrences of a request's tail are found by position (suffix-gpu page, How it works step 2
 // and Highlights: the unindexed documents are scanned directly).  Scanning the whole delta in
-// every request costs B * |delta| compares.  Before a step that may see a delta, four passes
+// every request costs B * |delta| compares.  Before a step that may see a delta, three passes
 // sort the delta's end positions by the two tokens that end there, for only those pairs that
 // end some request's context:
-//   1. one workgroup hashes the batch's distinct tail pairs to dense group numbers;
-//   2. every wavefront column counts, per group, the occurrences in its slice of the delta;
-//   3. one workgroup per group scans that group's counts over the columns and totals them;
-//   4. every slice workgroup turns the totals into group starts, and the slices write their
+//   1. every wavefront column of the delta hashes the batch's tail pairs into a table (a
+//      pair's group is named by its first request) and counts, per group, the occurrences in
+//      its slice of the delta;
+//   2. one workgroup per group scans that group's counts over the columns and totals them;
+//   3. every slice workgroup turns the totals into group starts, and the slices write their
 //      occurrences' offsets (from the delta start), in position order.
 // A request then extends only its own group's occurrences, which are exactly those the scan
 // would find, in the same order.
@@ -41,7 +42,7 @@ struct PairIndexArgs {
   const int32_t* ring;
   int64_t ring_cap;
   unsigned long long* keys;  // [slots] the distinct pairs (empty slots all ones)
-  int32_t* gid;              // [slots] their dense group numbers
+  int32_t* gid;              // [slots] their groups: the first request with the pair
   uint32_t slots;
   int32_t* group;            // [B] out: the request's group, or -1 when it takes no delta scan
   int32_t* off;              // [(B + 1) * kPairCols] counts, then their prefix within a group

@@ -44,81 +44,30 @@ __device__ __forceinline__ bool delta_range(const Ctl* ctl, long long* lo, long 
   return c.head - l > 1;
 }
 
-// Pass 1 (one workgroup of 1024 threads, one request per thread): the tail pair of each
-// request whose step scans the delta -- a non-empty sampled prefix, a two-token tail within
-// max_tree_depth and a non-negative second-to-last token -- inserted into an open-addressing
-// table; the occupied slots are numbered densely in slot order.
-__global__ __launch_bounds__(1024) void pair_table_kernel(PairIndexArgs a) {
-  __shared__ unsigned long long hk[2 * kPairMaxBatch];
-  __shared__ int hg[2 * kPairMaxBatch];
-  __shared__ int wsum[16];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const uint32_t mask = a.slots - 1;
-  for (uint32_t i = tid; i < a.slots; i += 1024) hk[i] = kNoPair;
-  __syncthreads();
-  unsigned long long key = kNoPair;
-  if (tid < a.B) {
-    int n = a.ntns[tid];
-    n = n < 0 ? 0 : (n > a.S ? a.S : n);
-    const int32_t* smp = a.samp + (int64_t)tid * a.T;
-    const int32_t* row = a.tok + (int64_t)tid * a.S;
-    int t = 0;
-    while (t < a.T && smp[t] >= 0) ++t;
-    const int L = n + t;
-    const int lcap = a.D < L ? a.D : L;
-    if (t > 0 && lcap >= 2) {
-      const int last = smp[t - 1];
-      const int before = L - 2 >= n ? smp[L - 2 - n] : row[L - 2];
-      if (before >= 0) key = pair_key(before, last);
-    }
-  }
-  if (key != kNoPair) {
-    uint32_t h = pair_hash(key) & mask;
-    for (;;) {
-      const unsigned long long prev = atomicCAS(&hk[h], kNoPair, key);
-      if (prev == kNoPair || prev == key) break;
-      h = (h + 1) & mask;
-    }
-  }
-  __syncthreads();
-  // thread i numbers slots 2i and 2i + 1 (slots <= 2048)
-  const uint32_t s0 = 2 * tid, s1 = 2 * tid + 1;
-  const int o0 = s0 < a.slots && hk[s0] != kNoPair, o1 = s1 < a.slots && hk[s1] != kNoPair;
-  int incl = o0 + o1;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += y;
-  }
-  if (lane == 63) wsum[wid] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wid; ++w) before += wsum[w];
-  const int excl = before + incl - o0 - o1;
-  if (s0 < a.slots) {
-    hg[s0] = o0 ? excl : -1;
-    a.keys[s0] = hk[s0];
-    a.gid[s0] = hg[s0];
-  }
-  if (s1 < a.slots) {
-    hg[s1] = o1 ? excl + o0 : -1;
-    a.keys[s1] = hk[s1];
-    a.gid[s1] = hg[s1];
-  }
-  __syncthreads();
-  if (tid < a.B) {
-    int g = -1;
-    if (key != kNoPair) {
-      uint32_t h = pair_hash(key) & mask;
-      while (hk[h] != key) h = (h + 1) & mask;
-      g = hg[h];
-    }
-    a.group[tid] = g;
-  }
+// The tail pair of request b when its step reads the delta -- a non-empty sampled prefix, a
+// two-token tail within max_tree_depth and a non-negative second-to-last token -- else kNoPair.
+__device__ __forceinline__ unsigned long long tail_pair(const PairIndexArgs& a, int b) {
+  int n = a.ntns[b];
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  const int32_t* smp = a.samp + (int64_t)b * a.T;
+  const int32_t* row = a.tok + (int64_t)b * a.S;
+  int t = 0;
+  while (t < a.T && smp[t] >= 0) ++t;
+  const int L = n + t;
+  const int lcap = a.D < L ? a.D : L;
+  if (t == 0 || lcap < 2) return kNoPair;
+  const int last = smp[t - 1];
+  const int before = L - 2 >= n ? smp[L - 2 - n] : row[L - 2];
+  return before >= 0 ? pair_key(before, last) : kNoPair;
 }
 
 constexpr int kSliceRuns = 4;  // 64-position runs whose loads a wavefront issues together
 
-// Passes 2 and 4 (workgroups of kPairColsPerBlock wavefronts, one delta slice each).  The delta's end
+// Pass 1 (count) and pass 3 (scatter), workgroups of kPairColsPerBlock wavefronts, one delta
+// slice each.  The count pass first builds the table of the batch's tail pairs in LDS: a group
+// is named by its first request (the smallest b with that pair), the same in every workgroup
+// whatever the order of insertion; workgroup 0 also stores the table and every request's
+// group for the scatter pass and the step.  The delta's end
 // positions lo + 1 .. hi - 2 are cut into kPairCols slices of whole 64-position runs, and
 // wavefront column c takes slice c.  A position belongs to group g when (token before, token
 // at it) is group g's pair and a real token follows it.  COUNT: the slice's count per group
@@ -137,6 +86,7 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
   __shared__ int hg[2 * kPairMaxBatch];
   __shared__ int cur[kPairColsPerBlock][kPairMaxBatch + 1];
   __shared__ int gbase[kPairMaxBatch + 1];
+  const uint32_t mask = a.slots - 1;
   __shared__ int wsum[kPairColsPerBlock];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -152,13 +102,19 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
     constexpr int kCur = (kPairColsPerBlock * (kPairMaxBatch + 1) + kSliceThreads - 1) / kSliceThreads;
     const int col0 = blockIdx.x * kPairColsPerBlock;
     constexpr int kTot = (kPairMaxBatch + 1 + kSliceThreads - 1) / kSliceThreads;
-    unsigned long long tk[kTab];
+    constexpr int kReq = kPairMaxBatch / kSliceThreads;
+    unsigned long long tk[kTab], rk[kReq];
     int tg[kTab], tc[kCur], tt[kTot];
 #pragma unroll
     for (int j = 0; j < kTab; ++j) {
       const uint32_t i = tid + kSliceThreads * j;
-      tk[j] = i < a.slots ? a.keys[i] : kNoPair;
-      tg[j] = i < a.slots ? a.gid[i] : -1;
+      tk[j] = (!COUNT && i < a.slots) ? a.keys[i] : kNoPair;
+      tg[j] = (!COUNT && i < a.slots) ? a.gid[i] : INT32_MAX;
+    }
+#pragma unroll
+    for (int j = 0; j < kReq; ++j) {
+      const int b = tid + kSliceThreads * j;
+      rk[j] = (COUNT && b < a.B) ? tail_pair(a, b) : kNoPair;
     }
 #pragma unroll
     for (int j = 0; j < kCur; ++j) {
@@ -180,7 +136,39 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
         hg[i] = tg[j];
       }
     }
-    if (!COUNT) {
+    if (COUNT) {
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kReq; ++j) {
+        if (rk[j] == kNoPair) continue;
+        uint32_t h = pair_hash(rk[j]) & mask;
+        for (;;) {
+          const unsigned long long prev = atomicCAS(&hk[h], kNoPair, rk[j]);
+          if (prev == kNoPair || prev == rk[j]) break;
+          h = (h + 1) & mask;
+        }
+        atomicMin(&hg[h], tid + kSliceThreads * j);
+      }
+      __syncthreads();
+      if (blockIdx.x == 0) {
+        for (uint32_t i = tid; i < a.slots; i += kSliceThreads) {
+          a.keys[i] = hk[i];
+          a.gid[i] = hk[i] == kNoPair ? -1 : hg[i];
+        }
+#pragma unroll
+        for (int j = 0; j < kReq; ++j) {
+          const int b = tid + kSliceThreads * j;
+          if (b >= a.B) continue;
+          int g = -1;
+          if (rk[j] != kNoPair) {
+            uint32_t h = pair_hash(rk[j]) & mask;
+            while (hk[h] != rk[j]) h = (h + 1) & mask;
+            g = hg[h];
+          }
+          a.group[b] = g;
+        }
+      }
+    } else {
       // group starts: exclusive prefix of the totals over the workgroup
       int sum = 0;
 #pragma unroll
@@ -218,7 +206,6 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
     const long long seg = ((nd + kPairCols - 1) / kPairCols + 63) / 64 * 64;
     const long long xb = lo + 1 + (long long)col * seg;
     const long long xe = xb + seg < hi - 1 ? xb + seg : hi - 1;
-    const uint32_t mask = a.slots - 1;
     const int cap = (int)a.ring_cap;
     int s = xb < xe ? (int)((xb + lane) % a.ring_cap) : 0;  // slot of this lane's position
     for (long long x0 = xb; x0 < xe; x0 += 64 * kSliceRuns) {
@@ -282,7 +269,7 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
   }
 }
 
-// Pass 3 (one 256-thread workgroup per group g <= B): the exclusive prefix of the group's
+// Pass 2 (one 256-thread workgroup per group g <= B): the exclusive prefix of the group's
 // per-slice counts over the slices, in place, and its total.
 constexpr int kRowThreads = 256;
 constexpr int kRowItems = kPairCols / kRowThreads;
@@ -327,7 +314,6 @@ hipError_t launch_pair_index(const PairIndexArgs& a, hipStream_t st) {
   if (a.B > kPairMaxBatch || a.slots < 2u * (uint32_t)a.B || a.slots > 2u * kPairMaxBatch ||
       (a.slots & (a.slots - 1)) != 0)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(pair_table_kernel, dim3(1), dim3(1024), 0, st, a);
   const dim3 grid(kPairCols / kPairColsPerBlock);
   hipLaunchKernelGGL((pair_slices_kernel<true>), grid, dim3(kSliceThreads), 0, st, a);
   hipLaunchKernelGGL(pair_rowscan_kernel, dim3(a.B + 1), dim3(kRowThreads), 0, st, a);
