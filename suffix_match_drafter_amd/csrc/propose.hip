@@ -1199,31 +1199,35 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       sm.dhist[lane + 1] = sum;  // delta occurrences of length >= lane + 1
       wave_sync();
     }
-    if (tid == 0) {
-      int gcum = 0, ti = 0;
-      for (int l = Lcap; l >= 2 && ti < nb; --l) {
-        const int dcum = sm.dhist[l];
-        gcum += sm.ghist[l];
-        int snap = l <= 4 ? sm.g_live[l - 2] : gcum;
-        if (act < 0) snap = 0;
-        const int cnt = snap + dcum;
-        while (ti < nb && cnt >= ti + 1) {
-          sm.cand_len[nb + ti] = l;
-          sm.cand_sup[nb + ti] = cnt;
-          ++ti;
-        }
-      }
-      for (; ti < nb; ++ti) {
-        sm.cand_len[nb + ti] = 0;
-        sm.cand_sup[nb + ti] = 0;
-      }
+    if (wid == 0) {
+      // the corpus ladder on one wavefront: lane v - 1 holds the support of length v, the live
+      // snapshot's (the v-gram group for v <= 4, else the 4-gram occurrences extending to v)
+      // plus the delta's; it does not grow with v, so candidate ti takes the largest length
+      // whose support is at least ti + 1
+      const int v = lane + 1;
+      const int gh = (v >= 5 && v <= Lcap) ? sm.ghist[v] : 0;
+      const int gin = wave_incl_add(gh);
+      const int gsuf = __builtin_amdgcn_readlane(gin, 63) - gin + gh;
+      int snap = v >= 2 && v <= 4 ? sm.g_live[v - 2] : gsuf;
+      if (act < 0) snap = 0;
+      const int cnt = snap + (v <= Lcap ? sm.dhist[v] : 0);
       const int minc = a.min_corpus > 2 ? a.min_corpus : 2;
-      for (int i = 0; i < nb; ++i) {
-        const int ci = nb + i;
-        sm.cand_valid[ci] = sm.cand_len[ci] >= minc;
-        sm.cand_c0[ci] = sm.cand_sup[ci] < M ? sm.cand_sup[ci] : M;
-        sm.cand_src[ci] =
-            (i > 0 && sm.cand_len[ci] == sm.cand_len[ci - 1]) ? sm.cand_src[ci - 1] : ci;
+      int prev_l = -1, prev_src = -1;
+      for (int ti = 0; ti < nb; ++ti) {
+        const uint64_t ok = __ballot(v >= 2 && v <= Lcap && cnt >= ti + 1);
+        const int l = ok ? 64 - __builtin_clzll(ok) : 0;
+        const int sup = l ? __builtin_amdgcn_readlane(cnt, l - 1) : 0;
+        const int ci = nb + ti;
+        const int src = (ti > 0 && l == prev_l) ? prev_src : ci;
+        prev_l = l;
+        prev_src = src;
+        if (lane == 0) {
+          sm.cand_len[ci] = l;
+          sm.cand_sup[ci] = sup;
+          sm.cand_valid[ci] = l >= minc;
+          sm.cand_c0[ci] = sup < M ? sup : M;
+          sm.cand_src[ci] = src;
+        }
       }
     }
     __syncthreads();
