@@ -41,14 +41,14 @@ struct PairIndexArgs {
   const Ctl* ctl;
   const int32_t* ring;
   int64_t ring_cap;
-  unsigned long long* keys;  // [slots] the distinct pairs (empty slots all ones)
-  int32_t* gid;              // [slots] their groups: the first request with the pair
-  uint32_t slots;
+  uint32_t slots;            // LDS hash-table slots for the batch's tail pairs
   int32_t* group;            // [B] out: the request's group, or -1 when it takes no delta scan
   int32_t* off;              // [(B + 1) * kPairCols] counts, then their prefix within a group
   int32_t* tot;              // [B + 1] out: occurrences of each group
   int32_t* base;             // [B + 1] out: start of each group's entries in list
   uint32_t* list;            // [ring_cap] occurrence offsets from the delta start
+  uint16_t* pos_group;       // [ring_cap] group of delta end position lo + 1 + i (count pass),
+                             // 0xFFFF for none
 };
 
 hipError_t launch_pair_index(const PairIndexArgs& a, hipStream_t st);

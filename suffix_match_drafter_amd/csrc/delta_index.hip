@@ -66,12 +66,12 @@ constexpr int kSliceRuns = 4;  // 64-position runs whose loads a wavefront issue
 // Pass 1 (count) and pass 3 (scatter), workgroups of kPairColsPerBlock wavefronts, one delta
 // slice each.  The count pass first builds the table of the batch's tail pairs in LDS: a group
 // is named by its first request (the smallest b with that pair), the same in every workgroup
-// whatever the order of insertion; workgroup 0 also stores the table and every request's
-// group for the scatter pass and the step.  The delta's end
-// positions lo + 1 .. hi - 2 are cut into kPairCols slices of whole 64-position runs, and
-// wavefront column c takes slice c.  A position belongs to group g when (token before, token
-// at it) is group g's pair and a real token follows it.  COUNT: the slice's count per group
-// goes to off[g * kPairCols + c] (zeros too, so the scan sees every entry).  Otherwise off
+// whatever the order of insertion; workgroup 0 also stores every request's group for the
+// step.  The delta's end positions lo + 1 .. hi - 2 are cut into kPairCols slices of whole
+// 64-position runs, and wavefront column c takes slice c.  A position belongs to group g when
+// (token before, token at it) is group g's pair and a real token follows it.  COUNT: each
+// position's group goes to pos_group (for the scatter pass), and the slice's count per group
+// to off[g * kPairCols + c] (zeros too, so the scan sees every entry).  Otherwise off
 // holds those counts' exclusive prefix within each group and tot the group totals; the
 // workgroup derives the group starts (and workgroup 0 stores them), and the slice writes its
 // positions' offsets from lo to list[] from base[g] + off[g * kPairCols + c] on, in position
@@ -103,14 +103,8 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
     const int col0 = blockIdx.x * kPairColsPerBlock;
     constexpr int kTot = (kPairMaxBatch + 1 + kSliceThreads - 1) / kSliceThreads;
     constexpr int kReq = kPairMaxBatch / kSliceThreads;
-    unsigned long long tk[kTab], rk[kReq];
-    int tg[kTab], tc[kCur], tt[kTot];
-#pragma unroll
-    for (int j = 0; j < kTab; ++j) {
-      const uint32_t i = tid + kSliceThreads * j;
-      tk[j] = (!COUNT && i < a.slots) ? a.keys[i] : kNoPair;
-      tg[j] = (!COUNT && i < a.slots) ? a.gid[i] : INT32_MAX;
-    }
+    unsigned long long rk[kReq];
+    int tc[kCur], tt[kTot];
 #pragma unroll
     for (int j = 0; j < kReq; ++j) {
       const int b = tid + kSliceThreads * j;
@@ -128,15 +122,15 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
       const int g = kTot * tid + j;
       tt[j] = (!COUNT && g < ng) ? a.tot[g] : 0;
     }
-#pragma unroll
-    for (int j = 0; j < kTab; ++j) {
-      const uint32_t i = tid + kSliceThreads * j;
-      if (i < a.slots) {
-        hk[i] = tk[j];
-        hg[i] = tg[j];
-      }
-    }
     if (COUNT) {
+#pragma unroll
+      for (int j = 0; j < kTab; ++j) {
+        const uint32_t i = tid + kSliceThreads * j;
+        if (i < a.slots) {
+          hk[i] = kNoPair;
+          hg[i] = INT32_MAX;
+        }
+      }
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < kReq; ++j) {
@@ -151,10 +145,6 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
       }
       __syncthreads();
       if (blockIdx.x == 0) {
-        for (uint32_t i = tid; i < a.slots; i += kSliceThreads) {
-          a.keys[i] = hk[i];
-          a.gid[i] = hk[i] == kNoPair ? -1 : hg[i];
-        }
 #pragma unroll
         for (int j = 0; j < kReq; ++j) {
           const int b = tid + kSliceThreads * j;
@@ -209,23 +199,31 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
     const int cap = (int)a.ring_cap;
     int s = xb < xe ? (int)((xb + lane) % a.ring_cap) : 0;  // slot of this lane's position
     for (long long x0 = xb; x0 < xe; x0 += 64 * kSliceRuns) {
+      // COUNT: the tokens around each position; otherwise the group the count pass stored
       int p[kSliceRuns], c[kSliceRuns], nx[kSliceRuns];
 #pragma unroll
       for (int u = 0; u < kSliceRuns; ++u) {
-        const bool in = x0 + 64 * u + lane < xe;
-        const int sp = s == 0 ? cap - 1 : s - 1;
-        const int sn = s + 1 == cap ? 0 : s + 1;
-        p[u] = in ? a.ring[sp] : -1;
-        c[u] = in ? a.ring[s] : -1;
-        nx[u] = in ? a.ring[sn] : -1;
-        s += 64;
-        while (s >= cap) s -= cap;
+        const long long x = x0 + 64 * u + lane;
+        const bool in = x < xe;
+        if (COUNT) {
+          const int sp = s == 0 ? cap - 1 : s - 1;
+          const int sn = s + 1 == cap ? 0 : s + 1;
+          p[u] = in ? a.ring[sp] : -1;
+          c[u] = in ? a.ring[s] : -1;
+          nx[u] = in ? a.ring[sn] : -1;
+          s += 64;
+          while (s >= cap) s -= cap;
+        } else {
+          p[u] = in ? (int)(int16_t)a.pos_group[x - lo - 1] : -1;
+        }
       }
 #pragma unroll
       for (int u = 0; u < kSliceRuns; ++u) {
         const long long x = x0 + 64 * u + lane;
         int g = -1;
-        if (p[u] >= 0 && nx[u] >= 0) {
+        if (!COUNT) {
+          g = p[u];
+        } else if (p[u] >= 0 && nx[u] >= 0) {
           const unsigned long long key = pair_key(p[u], c[u]);
           uint32_t h = pair_hash(key) & mask;
           for (;;) {
@@ -239,6 +237,7 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
           }
         }
         if (COUNT) {
+          if (x < xe) a.pos_group[x - lo - 1] = (uint16_t)g;
           if (g >= 0) atomicAdd(&cur[w][g], 1);
         } else {
           // one group at a time: the lanes of group gg take consecutive list entries
