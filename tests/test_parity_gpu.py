@@ -276,7 +276,8 @@ def test_fuzz_with_delta(S, mode, index, flags):
     """Documents ingested after the last rebuild (the delta) from small vocabularies, so that
     many requests share a tail pair, many pairs collide, and a pair occurs thousands of times;
     rows without sampled tokens, with a negative token before the sampled one, shorter than two
-    tokens; rings that wrap and evict.  Drafts equal the oracle's on the live corpus, with the
+    tokens; rings that wrap and evict, down to a ring shorter than two 64-position runs.  Drafts
+    equal the oracle's on the live corpus, with the
     per-call pair index and with the scan of the whole delta."""
     import torch
 
@@ -293,7 +294,7 @@ def test_fuzz_with_delta(S, mode, index, flags):
                   spec_factor_ppm=int(rng.choice([1_000_000, 2_000_000])),
                   min_token_prob_ppm=int(rng.choice([0, 100_000, 400_000])),
                   min_corpus_match=int(rng.integers(2, D + 1)))
-        cap = int(rng.choice([3000, 1 << 14]))
+        cap = int(rng.choice([70, 3000, 1 << 14]))  # 70: ring slots wrap inside one 64-run
         seed = [rng.integers(0, V, size=int(rng.integers(0, 80))).astype(np.int32)
                 for _ in range(int(rng.integers(0, 30)))]
         delta = [rng.integers(0, V, size=int(rng.integers(0, 400))).astype(np.int32)
