@@ -1297,7 +1297,8 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
           else delta_scan_wave(a, dlo, from, se, Lcap, sm.tail, lane, site);
         }
       }
-      __syncthreads();
+      // no barrier per candidate: each writes only its own site array, and the workgroup scan
+      // of the next one ends with its own barriers
     }
   }
   __syncthreads();
