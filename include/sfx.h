@@ -85,7 +85,10 @@ enum {
                                     counts outside [0, T]) or a decreasing document offset */
   SFX_ERR_NEGATIVE_TOKEN = 2,    /* a negative id inside a row prefix or a document */
   SFX_ERR_SAMPLED_AFTER_PAD = 4, /* a non-negative sampled id after a negative one (ignored) */
-  SFX_ERR_ROW_INDEX = 8          /* an ingest row index outside the rows (ignored) */
+  SFX_ERR_ROW_INDEX = 8,         /* an ingest row index outside the rows (ignored) */
+  SFX_ERR_SYNC_TIMEOUT = 16      /* a propose workgroup's bounded wait for its other wavefronts
+                                    ran out (raised with or without SFX_FLAG_CHECK_INPUTS; the
+                                    drafts of that call are unreliable) */
 };
 
 typedef struct sfx_config {

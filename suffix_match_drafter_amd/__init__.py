@@ -40,6 +40,7 @@ FLAG_TREE_DEPTH_CAP = 4  # match length plus draft length at most max_tree_depth
 
 # bits of the sticky error word (include/sfx.h)
 ERR_LENGTH, ERR_NEGATIVE_TOKEN, ERR_SAMPLED_AFTER_PAD, ERR_ROW_INDEX = 1, 2, 4, 8
+ERR_SYNC_TIMEOUT = 16    # a propose workgroup's bounded internal wait ran out
 
 
 class SfxError(RuntimeError):

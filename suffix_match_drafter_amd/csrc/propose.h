@@ -29,17 +29,29 @@ struct ProposeArgs {
   const int32_t* pair_base;  // [B + 1] start of each group's entries in pair_list
   const int32_t* pair_tot;   // [B + 1] their number
   const uint32_t* pair_list;
+  // the context's sticky error word (kErrSyncTimeout is raised here)
+  uint32_t* err;
+  // per-wavefront phase timestamps (shader clock), written only by builds with
+  // SFX_PHASE_TRACE=1; nullptr otherwise
+  uint64_t* trace;
 };
+
+// Error-word bit raised when a workgroup's bounded internal wait runs out (SFX_ERR_SYNC_TIMEOUT
+// of include/sfx.h).
+constexpr uint32_t kErrSyncTimeout = 16;
+
+// Timestamps per wavefront in a phase trace: [B][16 wavefronts][kTracePhases].
+constexpr int kTracePhases = 16;
 
 constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one gfx950 workgroup
 // Dynamic LDS of one request: the staged context (when staged), the hit lists and, with a
 // corpus, the delta scan's occurrence records.
-size_t propose_dynamic_lds(bool staged, int S, int T, bool corpus);
+size_t propose_dynamic_lds(bool staged, int S, int T, bool corpus, int nb);
 // Static LDS of the propose kernel (the per-request bookkeeping).
 size_t propose_static_lds();
 // Whether a call with row capacity S stages the context in LDS: it does unless asked not to or
 // the staged layout does not fit one workgroup's LDS.
-bool propose_staged(int S, int T, bool stream_ctx, bool corpus);
+bool propose_staged(int S, int T, bool stream_ctx, bool corpus, int nb);
 // Allows the largest dynamic LDS on every propose kernel instantiation.
 hipError_t propose_prepare();
 hipError_t launch_propose(const ProposeArgs& a, hipStream_t st);

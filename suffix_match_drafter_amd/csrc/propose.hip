@@ -1,29 +1,36 @@
 // propose.hip -- the drafter step on gfx950: one workgroup (16 wavefronts) per request.
 //
 // Steps, in the order of the suffix-gpu page, How it works:
-//   1. local match (step 1): each worker wavefront owns a contiguous chunk of end positions; it
-//      streams the chunk with coalesced bounds-checked loads (staging it in LDS when the row
-//      fits there) and keeps one ballot word per 64 positions marking the positions whose
-//      token is the last context token.  The marked positions are listed in order and their
-//      backward match lengths against the tail computed, into a per-wavefront histogram.  The
-//      histograms give the ladder (t-th largest length) and, per wavefront, the offsets of its
-//      earliest continuation sites, so one ordered pass writes the sites of every level;
+//   1. local match (step 1): each worker wavefront owns a contiguous chunk of end positions.  It
+//      streams the chunk with coalesced bounds-checked loads (staging it, plus the 64 positions
+//      before it, in LDS when the row fits there) and keeps one ballot word per 64 positions:
+//      the end positions whose token is the last context token.  Without waiting for the other
+//      wavefronts it then narrows those words to the positions whose previous token is the
+//      second-to-last context token, computes their backward match lengths against the tail and
+//      publishes per-length counts.  After one barrier among the workers, wavefront t derives
+//      the t-th rung of the ladder (the t-th largest match length), gathers its earliest
+//      continuation sites from the published lists and votes;
 //   2. global match (step 2; vLLM docs, Model Runner V2: probe by the last 2 and last 4 tokens,
 //      extend to the longest match): 2-, 3- and 4-gram probes into hash tables over the
 //      suffix-array groups of the live snapshot and backward extension of the 4-gram
-//      occurrences.  With a live snapshot, a dedicated wavefront does it while the other
-//      fifteen work through the local match, which synchronise among themselves only; without
-//      a delta it also derives the corpus ladder and sites.  With a delta (documents appended
-//      since the snapshot) the whole workgroup then finds the delta's occurrences -- from the
-//      per-call pair index, or by a brute-force scan -- and merges;
-//   3. expansion (step 3): one wavefront per candidate votes depth by depth over its sites
-//      (one ballot pair when every alive site agrees or one token holds a majority, ballots
-//      per token when few sites are alive, an LDS hash otherwise); stop rule and score use
-//      integer cross-multiplication; selection and the [k] output row follow.
+//      occurrences.  With a live snapshot and no delta a dedicated wavefront does all of it --
+//      probes, ladder, earliest sites and the votes of the corpus candidates -- while the others
+//      work through the local match.  With a delta (documents appended since the snapshot) the
+//      whole workgroup then finds the delta's occurrences -- from the per-call pair index, or by
+//      a brute-force scan -- and merges;
+//   3. expansion (step 3): one wavefront per candidate votes depth by depth over its sites, with
+//      the alive sites as wavefront masks (one ballot pair settles a depth whose alive sites
+//      agree or hold a strict majority; ballots per token when few sites are alive, an LDS hash
+//      otherwise); stop rule and score use integer cross-multiplication; selection and the [k]
+//      output row follow.
 #include <type_traits>
 
 #include "delta_index.h"
 #include "propose.h"
+
+#ifndef SFX_PHASE_TRACE
+#define SFX_PHASE_TRACE 0
+#endif
 
 namespace sfx {
 
@@ -32,8 +39,18 @@ namespace {
 constexpr int NT = 1024;
 constexpr int NW = NT / 64;
 constexpr int GW = NW - 1;          // the corpus wavefront of the fast path
-constexpr int kVoteSlots = 256;
+constexpr int kVoteSlots = 256;     // LDS hash slots of one voter (keys and counts)
 constexpr int kSmallVote = 24;      // alive sites at or below this vote with ballots
+
+// f(integral_constant<int, I>) for I = I0 .. N-1, unrolled at compile time (so that lane and
+// register indices are immediates).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -99,6 +116,11 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+__device__ __forceinline__ int lanes_before(uint64_t bal) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
 // Exclusive prefix sum of one int per thread over the workgroup; *total gets the sum.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -127,16 +149,42 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
 }
 
 // Barrier over the worker wavefronts only, so that the corpus wavefront of the fast path keeps
-// working through the local phases: an LDS arrival count.  Every worker wavefront passes each
-// such barrier exactly once, so the count reaches k * (workers) at the k-th one; the spin is
-// bounded as a guard.
-__device__ __forceinline__ void worker_barrier(int* ctr, int target, int lane) {
+// working through the local phase: an LDS arrival count.  Every worker wavefront passes it
+// exactly once, so the count reaches the number of workers.  The wait is bounded so that every
+// wavefront ends even if the count never arrives; running out of the bound raises
+// kErrSyncTimeout in the context's error word (the call's results are then unreliable).
+constexpr int kSpinBound = 1 << 24;
+__device__ __forceinline__ void worker_barrier(int* ctr, int target, int lane, uint32_t* err) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  for (int spin = 0; spin < (1 << 24); ++spin) {
-    if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+  bool ok = false;
+  for (int spin = 0; spin < kSpinBound; ++spin) {
+    if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) {
+      ok = true;
+      break;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
+  if (!ok && lane == 0 && err)
+    __hip_atomic_fetch_or(err, (uint32_t)kErrSyncTimeout, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Bounded wait for an LDS flag set by another wavefront of the workgroup (same timeout
+// convention as worker_barrier).
+__device__ __forceinline__ void wait_flag(int* flag, int lane, uint32_t* err) {
+  bool ok = false;
+  for (int spin = 0; spin < kSpinBound; ++spin) {
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) {
+      ok = true;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (!ok && lane == 0 && err)
+    __hip_atomic_fetch_or(err, (uint32_t)kErrSyncTimeout, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
@@ -160,8 +208,11 @@ __device__ __forceinline__ int vote_insert(int* hk, int* hc, int tok) {
 struct Smem {
   int tail[kMaxD];
   int gtail[kMaxD];
-  int whist[NW][kMaxD + 1];
+  // per worker wavefront w: wsuf[w][v] = its end positions with match length >= v (v >= 1);
+  // while they are computed, wsuf[w][m] counts its lengths m >= 3 (converted in place)
   int wsuf[NW][kMaxD + 2];
+  int wbeg[NW];          // first end position of each worker wavefront (its list base)
+  int vex[kMaxNB][NW];   // per local voter: exclusive prefix of the scanned lists
   int ghist[kMaxD + 1];
   int dhist[kMaxD + 1];
   int g_off[kNG], g_live[kNG];
@@ -170,18 +221,25 @@ struct Smem {
   int cand_snum[2 * kMaxNB];  // at most k * M = 4096
   int cand_out[2 * kMaxNB][kMaxK];
   int lsites[kMaxNB][kMaxM];
-  long long gsites[kMaxNB][kMaxM];
+  int gsites[kMaxNB][kMaxM];  // logical corpus positions minus the oldest live one (Ctl tail)
   int gpl[kNG][kMaxM];  // heads of the live 2-, 3- and 4-gram groups
   int gm4[kMaxM];       // extension lengths of the first 4-gram occurrences
   const int32_t* plp[kNG];
   int wsum[NW + 1];
-  int wbar;  // arrivals at the worker-only barriers
+  int wbar;    // arrivals at the worker-only barrier
+  int gready;  // the corpus wavefront has published its candidates and sites (fast path)
+  uint8_t cap_tab[kMaxD + 1];  // the per-call draft cap and stop-count tables, staged
+  uint8_t min_tab[kMaxM + 1];
+#if SFX_PHASE_TRACE
+  unsigned long long ts[NW][kTracePhases];
+#endif
 };
 
 // Shape of one request and the corpus state it sees.  Every thread derives it from the same
 // uniform loads, so no thread waits for another before the staging starts.
 struct Req {
   int n, t, L, J, Lcap;
+  int t0;  // the last context token (the last sampled id)
   int act;
   bool has, fast, delta;
   long long snap_start, snap_n, tail_w, delta_lo, delta_hi;
@@ -261,26 +319,27 @@ __device__ void probe_ngram(const View ib, const int* tail, int Lcap, long long 
 }
 
 // Backward extension of a 4-gram occurrence starting at snapshot position i: the match length
-// (>= 4) against the tail, at most `cap`.  The preceding tokens are fetched eight at a time, all
-// eight loads in flight, so a match of length l costs about (l - 4) / 8 + 1 round trips.
-__device__ __forceinline__ int extend4(const int32_t* text, const int* tail, int i, int cap) {
+// (>= 4) against the tail, at most `cap`.  The preceding tokens are fetched kExtRound at a time,
+// all of them in flight together, so a match of up to kExtRound + 4 tokens costs one round trip.
+constexpr int kExtRound = 20;
+__device__ __noinline__ int extend4(const int32_t* text, const int* tail, int i, int cap) {
   int m = 4;
-  for (int base = 0; base < cap - 4; base += 8) {
-    int c[8];
+  for (int base = 0; base < cap - 4; base += kExtRound) {
+    int c[kExtRound];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kExtRound; ++q) {
       const int o = base + q;
       c[q] = (o < cap - 4 && i - 1 - o >= 0) ? text[i - 1 - o] : -2;
     }
     bool stop = false;
+    int run = 0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      if (!stop) {
-        const int ti = 4 + base + q < kMaxD ? 4 + base + q : kMaxD - 1;
-        if (c[q] >= 0 && c[q] == tail[ti]) ++m;
-        else stop = true;
-      }
+    for (int q = 0; q < kExtRound; ++q) {
+      const int ti = 4 + base + q < kMaxD ? 4 + base + q : kMaxD - 1;
+      stop = stop || c[q] < 0 || c[q] != tail[ti];
+      run += stop ? 0 : 1;
     }
+    m += run;
     if (stop) break;
   }
   return m;
@@ -452,137 +511,293 @@ __device__ __forceinline__ void delta_list_wave(const ProposeArgs& a, long long 
   }
 }
 
-// Depth-wise vote of one candidate held by one wavefront: lane l owns sites l and l+64, whose
-// continuation windows are w0 / w1 (-1 past the end of a continuation).  Writes the tokens to
-// out[] and returns the count and the sum of per-depth counts.  cmin is the smallest
-// count the stop rule keeps (0 when there is no stop rule).
-// State of one candidate's depth-wise vote, kept by its wavefront.
-struct VoteState {
-  bool al0, al1;  // this lane's two sites still on the voted path
-  bool done;
-  bool site0;     // site 0 (lane 0, first half) is still on the voted path
-  int nout;       // tokens voted so far
-  int snum;       // their counts summed: at most k * M, so every product below fits 32 bits
-  int tokv;       // lane i collects the i-th voted token
-};
-
-// One depth of the vote: x0 and x1 are this lane's two sites' tokens at this depth.
-__device__ __forceinline__ void vote_depth(VoteState& v, int x0, int x1, int cmin, int* hk, int* hc,
-                                           int lane) {
-  bool& al0 = v.al0;
-  bool& al1 = v.al1;
-  bool& done = v.done;
-  bool& site0 = v.site0;
-  int& nout = v.nout;
-  int& snum = v.snum;
-  int& tokv = v.tokv;
-  const int tk0 = al0 ? x0 : -1, tk1 = al1 ? x1 : -1;
-  const uint64_t v0 = __ballot(tk0 >= 0), v1 = __ballot(tk1 >= 0);
-  // site 0's token at this depth does not depend on the votes so far
-  const int s0tok = __builtin_amdgcn_readfirstlane(x0);
-  int c = 0, w = -1;
-  if ((v0 | v1) == 0) {
-    done = true;
-  } else {
-    // the reference is an alive site's token: site 0's while it stays on the voted path,
-    // else the first alive site's; when every alive site agrees with it the token wins
-    // with all their votes
-    int first;
-    if (site0 && s0tok >= 0) {
-      first = s0tok;
-    } else {
-      const int fl = v0 ? __builtin_ctzll(v0) : __builtin_ctzll(v1);
-      first = v0 ? __builtin_amdgcn_readlane(tk0, fl) : __builtin_amdgcn_readlane(tk1, fl);
+// The vote at one depth when the reference token (the first voting site's) holds no strict
+// majority among the na voting sites (alive and with a token at this depth): the count of every
+// token, then the largest count and the smallest token among the largest.  x0 / x1 are this
+// lane's two sites' tokens, V0 / V1 the voting sites, E0 / E1 those voting for ref.  Returns
+// count << 32 | token (a function of its own: this path is rare and its code is long).
+__device__ __noinline__ uint64_t vote_split(int x0, int x1, uint64_t V0, uint64_t V1, int ref,
+                                            uint64_t E0, uint64_t E1, int na, int* hk, int* hc,
+                                            int lane) {
+  const int ce = __popcll(E0) + __popcll(E1);
+  if (na <= kSmallVote) {
+    // one ballot pair per distinct token, until the best count exceeds every vote not yet
+    // counted (a tie with a smaller token still has to be looked at)
+    uint64_t key = ((uint64_t)ce << 32) | (uint32_t)(0x7FFFFFFF - ref);
+    uint64_t r0 = V0 & ~E0, r1 = V1 & ~E1;
+    int rest = na - ce;
+    while ((r0 | r1) && (int)(key >> 32) <= rest) {
+      const int tok = r0 ? __builtin_amdgcn_readlane(x0, __builtin_ctzll(r0))
+                         : __builtin_amdgcn_readlane(x1, __builtin_ctzll(r1));
+      const uint64_t e0 = __ballot(x0 == tok) & r0, e1 = __ballot(x1 == tok) & r1;
+      const int ct = __popcll(e0) + __popcll(e1);
+      const uint64_t k = ((uint64_t)ct << 32) | (uint32_t)(0x7FFFFFFF - tok);
+      key = k > key ? k : key;
+      r0 &= ~e0;
+      r1 &= ~e1;
+      rest -= ct;
     }
-    const uint64_t f0 = __ballot(tk0 == first), f1 = __ballot(tk1 == first);
-    const int nalive = __popcll(v0) + __popcll(v1);
-    const int cf = __popcll(f0) + __popcll(f1);
-    if (cf == nalive) {
-      c = nalive;
-      w = first;
-    } else if (2 * cf > nalive) {
-      // a strict majority: no other token can reach its count
-      c = cf;
-      w = first;
-    } else if (nalive <= kSmallVote) {
-      // few alive sites: one ballot pair per distinct token, until the best count exceeds
-      // every vote not yet counted
-      uint64_t key = ((uint64_t)cf << 32) | (uint32_t)(0x7FFFFFFF - first);
-      uint64_t r0 = v0 & ~f0, rr1 = v1 & ~f1;
-      int rest = nalive - cf;
-      while ((r0 | rr1) && (int)(key >> 32) <= rest) {
-        const int tok = r0 ? __builtin_amdgcn_readlane(tk0, __builtin_ctzll(r0))
-                           : __builtin_amdgcn_readlane(tk1, __builtin_ctzll(rr1));
-        const uint64_t e0 = __ballot(tk0 == tok), e1 = __ballot(tk1 == tok);
-        const uint64_t k = ((uint64_t)(__popcll(e0) + __popcll(e1)) << 32) |
-                           (uint32_t)(0x7FFFFFFF - tok);
-        key = k > key ? k : key;
-        r0 &= ~e0;
-        rr1 &= ~e1;
-        rest -= __popcll(e0) + __popcll(e1);
-      }
-      c = (int)(key >> 32);
-      w = 0x7FFFFFFF - (int)(uint32_t)(key & 0xFFFFFFFFu);
+    return (key >> 32) << 32 | (uint32_t)(0x7FFFFFFF - (int)(uint32_t)(key & 0xFFFFFFFFu));
+  }
+  // many voting sites: counts in an LDS hash, then max count and smallest token
+  const bool v0 = (V0 >> lane) & 1, v1 = (V1 >> lane) & 1;
+  for (int x = lane; x < kVoteSlots; x += 64) {
+    hk[x] = -1;
+    hc[x] = 0;
+  }
+  wave_sync();
+  int sl0 = -1, sl1 = -1;
+  if (v0) sl0 = vote_insert(hk, hc, x0);
+  if (v1) sl1 = vote_insert(hk, hc, x1);
+  wave_sync();
+  const int cnt0 = sl0 >= 0 ? hc[sl0] : 0, cnt1 = sl1 >= 0 ? hc[sl1] : 0;
+  uint64_t res;
+  if (__ballot((v0 && x0 >= (1 << 24)) || (v1 && x1 >= (1 << 24))) == 0) {
+    // tokens below 2^24: count and token packed in one key, one reduction
+    const uint32_t k0 = sl0 >= 0 ? ((uint32_t)cnt0 << 24) | (uint32_t)(0xFFFFFF - x0) : 0u;
+    const uint32_t k1 = sl1 >= 0 ? ((uint32_t)cnt1 << 24) | (uint32_t)(0xFFFFFF - x1) : 0u;
+    const uint32_t key = wave_max_u32(k0 > k1 ? k0 : k1);
+    res = (uint64_t)(key >> 24) << 32 | (uint32_t)(0xFFFFFF - (int)(key & 0xFFFFFFu));
+  } else {
+    const int c = wave_max(cnt0 > cnt1 ? cnt0 : cnt1);
+    int tmin = 0x7FFFFFFF;
+    if (sl0 >= 0 && cnt0 == c) tmin = x0;
+    if (sl1 >= 0 && cnt1 == c && x1 < tmin) tmin = x1;
+    res = (uint64_t)(uint32_t)c << 32 | (uint32_t)wave_min(tmin);
+  }
+  wave_sync();
+  return res;
+}
+
+// Index of the lowest set bit of m, or KMAX when none is set below KMAX.
+template <int KMAX>
+__device__ __forceinline__ int first_set(uint32_t m) {
+  const int f = m ? __builtin_ctz(m) : 32;
+  return f < KMAX ? f : KMAX;
+}
+
+// One depth of the vote, decided from scratch: x0 / x1 are this lane's two sites' tokens, A0 / A1
+// the alive sites.  On return *w / *c hold the winner and its count, or *c = 0 when no alive
+// site has a token here.
+__device__ __forceinline__ void vote_depth(int x0, int x1, uint64_t A0, uint64_t A1, int cmin,
+                                           int* hk, int* hc, int lane, int* w, int* c) {
+  const uint64_t V0 = __ballot(x0 >= 0) & A0, V1 = __ballot(x1 >= 0) & A1;
+  *c = 0;
+  *w = -1;
+  if ((V0 | V1) == 0) return;
+  // the reference is the first voting site's token; when every voting site agrees with it, or a
+  // strict majority does, it wins with their votes
+  const int ref = V0 ? __builtin_amdgcn_readlane(x0, __builtin_ctzll(V0))
+                     : __builtin_amdgcn_readlane(x1, __builtin_ctzll(V1));
+  const uint64_t E0 = __ballot(x0 == ref) & A0, E1 = __ballot(x1 == ref) & A1;
+  const int na = __popcll(V0) + __popcll(V1);
+  const int ce = __popcll(E0) + __popcll(E1);
+  if (2 * ce > na) {
+    *w = ref;
+    *c = ce;
+  } else if (na < cmin) {
+    *c = na;  // no token reaches the stop count: any count below cmin stops the vote
+  } else {
+    const uint64_t res = vote_split(x0, x1, V0, V1, ref, E0, E1, na, hk, hc, lane);
+    *c = (int)(res >> 32);
+    *w = (int)(uint32_t)res;
+  }
+}
+
+// Depth-wise vote, depth by depth from depth d, with the alive sites as wavefront masks A0 / A1:
+// lane l owns sites l and l + 64, whose windows are w0 / w1 (-1 past a window's end).  A depth
+// whose voting sites all carry the first voting site's token is settled by one ballot pair;
+// otherwise vote_depth decides it.  TWO: whether slot 1 holds sites (more than 64).
+template <int KMAX, bool TWO>
+__device__ __forceinline__ void vote_seq(const int (&w0)[KMAX], const int (&w1)[KMAX],
+                                         uint64_t A0, uint64_t A1, int d, int dmax, int cmin,
+                                         int* hk, int* hc, int lane, int* nout_io, int* snum_io,
+                                         int* tokv_io) {
+  int nout = *nout_io, snum = *snum_io, tokv = *tokv_io;
+  bool done = false;
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    if (done || i < d || i >= dmax) continue;
+    // the depth's tokens pass through an empty asm, so that its compares are issued in depth
+    // order: hoisted, the 64-bit masks of every depth would not fit the scalar registers
+    int x0 = w0[i], x1 = TWO ? w1[i] : -1;
+    asm volatile("" : "+v"(x0), "+v"(x1));
+    const uint64_t V0 = __ballot(x0 >= 0) & A0;
+    const uint64_t V1 = TWO ? __ballot(x1 >= 0) & A1 : 0ull;
+    if ((V0 | V1) == 0) {
+      done = true;
+      continue;
+    }
+    const int ref = V0 ? __builtin_amdgcn_readlane(x0, __builtin_ctzll(V0))
+                       : __builtin_amdgcn_readlane(x1, __builtin_ctzll(V1));
+    const uint64_t E0 = __ballot(x0 == ref) & V0;
+    const uint64_t E1 = TWO ? __ballot(x1 == ref) & V1 : 0ull;
+    int w = ref, c;
+    if (E0 == V0 && E1 == V1) {
+      c = __popcll(V0) + (TWO ? __popcll(V1) : 0);
     } else {
-      // many alive sites: counts in an LDS hash, then max count and smallest token
-      for (int x = lane; x < kVoteSlots; x += 64) {
-        hk[x] = -1;
-        hc[x] = 0;
-      }
-      wave_sync();
-      int sl0 = -1, sl1 = -1;
-      if (tk0 >= 0) sl0 = vote_insert(hk, hc, tk0);
-      if (tk1 >= 0) sl1 = vote_insert(hk, hc, tk1);
-      wave_sync();
-      const int cnt0 = sl0 >= 0 ? hc[sl0] : 0, cnt1 = sl1 >= 0 ? hc[sl1] : 0;
-      if (__ballot(tk0 >= (1 << 24) || tk1 >= (1 << 24)) == 0) {
-        // tokens below 2^24: count and token packed in one key, one reduction
-        const uint32_t k0 = sl0 >= 0 ? ((uint32_t)cnt0 << 24) | (uint32_t)(0xFFFFFF - tk0) : 0u;
-        const uint32_t k1 = sl1 >= 0 ? ((uint32_t)cnt1 << 24) | (uint32_t)(0xFFFFFF - tk1) : 0u;
-        const uint32_t key = wave_max_u32(k0 > k1 ? k0 : k1);
-        c = (int)(key >> 24);
-        w = 0xFFFFFF - (int)(key & 0xFFFFFFu);
-      } else {
-        c = wave_max(cnt0 > cnt1 ? cnt0 : cnt1);
-        int tmin = 0x7FFFFFFF;
-        if (sl0 >= 0 && cnt0 == c) tmin = tk0;
-        if (sl1 >= 0 && cnt1 == c && tk1 < tmin) tmin = tk1;
-        w = wave_min(tmin);
-      }
-      wave_sync();
+      vote_depth(x0, x1, V0, V1, cmin, hk, hc, lane, &w, &c);
     }
     if (c < cmin) {
       done = true;
-    } else {
-      tokv = lane == nout ? w : tokv;
-      ++nout;
+      continue;
+    }
+    A0 = __ballot(x0 == w) & V0;
+    if (TWO) A1 = __ballot(x1 == w) & V1;
+    tokv = lane == i ? w : tokv;
+    snum += c;
+    nout = i + 1;
+  }
+  *nout_io = nout;
+  *snum_io = snum;
+  *tokv_io = tokv;
+}
+
+// Depth-wise vote of one candidate held by one wavefront: lane l owns sites l and l+64, whose
+// continuation windows are w0 / w1 (-1 past the end of a continuation and from depth cap on;
+// len0 / len1 leading tokens, windows end for good).  tok_at(e) reloads slot 0's token at depth
+// e from its source (used only at a depth a pass cannot settle).  Writes the voted tokens to
+// out[] and returns their number and the sum of their counts.  cmin is the smallest count the
+// stop rule keeps (0 without a stop rule).  hk / hc: this voter's LDS table.
+//
+// With at most 64 sites, depths are first settled in passes against a representative site r.
+// The sites that agree with r through depth d form r's group at d; when it is larger than all
+// other sites voting at d together, r's token wins with the group's count (no other token can
+// match it).  One pass takes each alive site's first disagreement with r, histograms those
+// depths (LDS atomics), and by one suffix scan and one ballot finds the first depth that r's
+// group does not settle or where the vote stops; every depth before it is settled at once.
+// That depth is voted from scratch, the winner's first site becomes the representative, and
+// the next pass starts after it.  Short votes, votes of more than 64 sites and what the passes
+// leave go depth by depth.
+constexpr int kPathMinDepths = 4;
+constexpr int kPathPasses = 3;
+template <int KMAX, typename TokAt>
+__device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[KMAX], int len0,
+                                         int c0, int cap, int cmin, int* hk, int* hc, int lane,
+                                         TokAt&& tok_at, int* out, int* n_out, int* snum_out) {
+  uint64_t A0 = __ballot(lane < c0), A1 = __ballot(lane + 64 < c0);
+  int nout = 0, snum = 0, tokv = -1;
+  const int dmax = cap < KMAX ? cap : KMAX;
+  int d = 0;  // next depth to vote
+  bool done = dmax <= 0;
+  if (!done && c0 <= 64 && dmax >= kPathMinDepths) {
+    int r = 0;
+    for (int pass = 0; pass < kPathPasses; ++pass) {
+      // each site's first depth of disagreement with r (r's end counts as one); lane i picks up
+      // r's token at depth i
+      uint32_t mm = 0;
+      int rtl = -1;
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {
+        int x = __builtin_amdgcn_readlane(w0[i], r);
+        rtl = lane == i ? x : rtl;
+        x = x < 0 ? (int)0x80000000 : x;
+        mm |= (w0[i] != x ? 1u : 0u) << i;
+      }
+      const int lcp = first_set<KMAX>(mm);
+      const int al = (int)((A0 >> lane) & 1);
+      // histograms over depth bins: hk[m] = alive sites whose first disagreement is m,
+      // hc[m] = those of them that still have a token at m
+      if (lane <= KMAX) {
+        hk[lane] = 0;
+        hc[lane] = 0;
+      }
+      atomicAdd(&hk[lcp], al);
+      atomicAdd(&hc[lcp], al & (len0 > lcp ? 1 : 0));
+      wave_sync();
+      // lane i: g = r's group at depth i (sites agreeing through i), o = other sites voting there
+      const int h = lane <= KMAX ? hk[lane] : 0;
+      const int o = lane < KMAX ? hc[lane] : 0;
+      const int incl = wave_incl_add(h);
+      const int g = __builtin_amdgcn_readlane(incl, 63) - incl;
+      const bool in = lane >= d && lane < dmax;
+      const bool stop = g + o == 0 || (g > o && g < cmin);
+      const uint64_t ev = __ballot(in && (stop || g <= o));
+      const int e = ev ? (int)__builtin_ctzll(ev) : dmax;
+      // depths d .. e-1 are settled: tokens r's, counts g
+      const bool acc = lane >= d && lane < e;
+      tokv = acc ? rtl : tokv;
+      const int gs = wave_incl_add(acc ? g : 0);
+      snum += __builtin_amdgcn_readlane(gs, 63);
+      nout = e > d ? e : nout;
+      wave_sync();
+      if (e >= dmax || (__ballot(stop) >> e) & 1) {
+        done = true;
+        break;
+      }
+      // depth e from scratch, over the sites still on r's path
+      const uint64_t B0 = __ballot(al && lcp >= e);
+      const int x0 = ((B0 >> lane) & 1) && len0 > e ? tok_at(e) : -1;
+      int w, c;
+      vote_depth(x0, -1, B0, 0ull, cmin, hk, hc, lane, &w, &c);
+      if (c == 0 || c < cmin) {
+        done = true;
+        break;
+      }
+      tokv = lane == e ? w : tokv;
       snum += c;
-      site0 = site0 && s0tok == w;
-      al0 = tk0 == w;
-      al1 = tk1 == w;
+      nout = e + 1;
+      A0 = __ballot(x0 == w) & B0;
+      d = e + 1;
+      if (d >= dmax) {
+        done = true;
+        break;
+      }
+      r = (int)__builtin_ctzll(A0);
     }
   }
+  if (!done) {
+    if (c0 > 64) vote_seq<KMAX, true>(w0, w1, A0, A1, d, dmax, cmin, hk, hc, lane, &nout, &snum,
+                                      &tokv);
+    else vote_seq<KMAX, false>(w0, w1, A0, 0ull, d, dmax, cmin, hk, hc, lane, &nout, &snum,
+                               &tokv);
+  }
+  if (lane < nout) out[lane] = tokv;
+  *n_out = nout;
+  *snum_out = snum;
 }
 
+// Windows of a corpus candidate: c0 sites (logical corpus positions, relative to the oldest live
+// one, in gs), continuation tokens loaded all at once (each address is a live snapshot position
+// or a ring slot, so always in bounds) and cut at each site's first separator.
 template <int KMAX>
-__device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[KMAX], int c0,
-                                         int cap, int cmin, int* hk, int* hc, int lane, int* out,
-                                         int* n_out, int* snum_out) {
-  VoteState v{lane < c0, lane + 64 < c0, false, true, 0, 0, -1};
+__device__ __forceinline__ void corpus_windows(const ProposeArgs& a, const Req& r, const int* gs,
+                                               int c0, int cap, int lane, int (&w0)[KMAX],
+                                               int (&w1)[KMAX], long long* q0_out,
+                                               long long* q1_out, int* len0_out) {
+  const int act = r.act;
+  const int32_t* text = act == 0 ? a.idx[0].text : (act == 1 ? a.idx[1].text : nullptr);
+  const long long ss = r.snap_start, sn = r.snap_n;
+  const int s0 = lane, s1 = lane + 64;
+  const long long q0 = r.tail_w + (s0 < c0 ? gs[s0] : 0), q1 = r.tail_w + (s1 < c0 ? gs[s1] : 0);
+  *q0_out = q0;
+  *q1_out = q1;
+  bool live0 = s0 < c0, live1 = s1 < c0;
+  const int rcap = (int)a.ring_cap;
+  int r0 = (int)(q0 % a.ring_cap), r1 = (int)(q1 % a.ring_cap);
 #pragma unroll
   for (int d = 0; d < KMAX; ++d) {
-    if (!v.done && d < cap) vote_depth(v, w0[d], w1[d], cmin, hk, hc, lane);
+    w0[d] = *corpus_ptr(a, text, ss, sn, q0 + d, r0);
+    w1[d] = *corpus_ptr(a, text, ss, sn, q1 + d, r1);
+    r0 = ring_next(r0, rcap);
+    r1 = ring_next(r1, rcap);
   }
-  if (lane < v.nout) out[lane] = v.tokv;
-  *n_out = v.nout;
-  *snum_out = v.snum;
+  int len0 = 0;
+#pragma unroll
+  for (int d = 0; d < KMAX; ++d) {
+    live0 = live0 && d < cap && w0[d] >= 0;
+    live1 = live1 && d < cap && w1[d] >= 0;
+    w0[d] = live0 ? w0[d] : -1;
+    w1[d] = live1 ? w1[d] : -1;
+    len0 += live0 ? 1 : 0;
+  }
+  *len0_out = len0;
 }
 
-
-// The corpus wavefront of the fast path (live snapshot, no delta), first part, run while the
-// other wavefronts stage the context: tail from global memory, the three n-gram probes, the
-// heads of the three position-ordered groups into LDS, and the backward extension of the live
-// 4-gram occurrences into a length histogram (lengths of the first kMaxM kept in LDS).
+// The corpus wavefront of the fast path, first part, run while the other wavefronts stage the
+// context: tail from global memory, the three n-gram probes, the heads of the three
+// position-ordered groups into LDS, and the backward extension of the live 4-gram occurrences
+// into a length histogram (lengths of the first kMaxM kept in LDS).
 __device__ __forceinline__ void corpus_wave_probe(const ProposeArgs& a, const Req& r, Smem& sm,
                                                   const int32_t* row, const int32_t* smp,
                                                   int lane) {
@@ -617,12 +832,12 @@ __device__ __forceinline__ void corpus_wave_probe(const ProposeArgs& a, const Re
   }
 }
 
-// Second part, run while the other wavefronts compute the match lengths of the context: the
-// corpus ladder (lane l - 1 holds the support of length l) and the earliest sites of each level.
+// Second part: the corpus ladder (lane l - 1 holds the support of length l) and the earliest
+// sites of each level.
 __device__ __forceinline__ void corpus_wave_sites(const ProposeArgs& a, const Req& r, Smem& sm,
                                                   int lane) {
   const int Lcap = r.Lcap, nb = a.nb, M = a.M;
-  const long long snap_start = r.snap_start;
+  const int sbase = (int)(r.snap_start - r.tail_w);  // snapshot index -> site coordinate
   wave_sync();
   // support of length v = lane + 1 (lengths up to 64 on 64 lanes): the live v-gram group for
   // v <= 4, else the extensions reaching v
@@ -649,11 +864,11 @@ __device__ __forceinline__ void corpus_wave_sites(const ProposeArgs& a, const Re
       sm.cand_src[ci] = src;
     }
     if (l < minc || src != ci) continue;
-    long long* gs = sm.gsites[ti];
+    int* gs = sm.gsites[ti];
     if (l <= 4) {
       const int g = l - 2;
       const int ns = sup < M ? sup : M;
-      for (int x = lane; x < ns; x += 64) gs[x] = (long long)sm.gpl[g][x] + l + snap_start;
+      for (int x = lane; x < ns; x += 64) gs[x] = sm.gpl[g][x] + l + sbase;
     } else {
       // the first M live 4-gram occurrences (position order) whose extension reaches l
       const int live4 = sm.g_live[2];
@@ -676,44 +891,55 @@ __device__ __forceinline__ void corpus_wave_sites(const ProposeArgs& a, const Re
         }
         const uint64_t bal = __ballot(q);
         const int rk = run + __popcll(bal & below);
-        if (q && rk < M) gs[rk] = (long long)i + 4 + snap_start;
+        if (q && rk < M) gs[rk] = i + 4 + sbase;
         run += __popcll(bal);
       }
+      // the vote reads exactly the sites written
+      if (lane == 0 && run < (sup < M ? sup : M)) sm.cand_c0[ci] = run;
     }
   }
+  wave_sync();
 }
 
-// Dynamic LDS of one request.  Staged: [context ints | hit positions (u16) | hit lengths (u8) |
-// hit bit words]; streaming (the context stays in HBM): the same without the context.  The vote
-// tables of the expansion alias the start of the region once those are dead.
-constexpr int kVoteBytes = NW * 2 * kVoteSlots * 4;
+// Dynamic LDS of one request:
+//   staged:    [context ints | hit bit words | two-token bit words | hit positions (u16) |
+//               hit lengths (u8) | vote tables]
+//   streaming: the same without the context.
+// With a corpus, the region from the hit positions on also holds the delta scan's occurrence
+// records (after the local sites are gathered), at least kDeltaMinRecs per wavefront.
+constexpr int kVoteBytes = 2 * kVoteSlots * 4;  // one voter's keys and counts
 // context ints, then 64 spare slots that absorb the staging stores of lanes past the row end
 __host__ __device__ inline int ctx_ints(int S, int T) { return ((S + T + 4 + 3) & ~3) + 64; }
 __host__ __device__ inline int ctx_spare(int S, int T) { return ctx_ints(S, T) - 64; }
+// one bit word per 64 end positions (J <= S + T - 1), plus one
+__host__ __device__ inline int bit_words(int S, int T) { return (S + T + 63) / 64 + 1; }
 // Hit-list entries: wavefront w owns the entries of its end positions [cbeg, cend), from entry
-// cbeg on; J <= S + T - 1, so S + T + 64 * NW entries always suffice.
-__host__ __device__ inline int hit_cap(int S, int T) { return (S + T + 64 * NW + 63) & ~63; }
-__host__ __device__ inline size_t hpos_offset(bool staged, int S, int T) {
+// cbeg on (a list never holds more entries than its chunk has positions); J <= S + T - 1.
+__host__ __device__ inline int hit_cap(int S, int T) { return (S + T + 63) & ~63; }
+__host__ __device__ inline size_t bits_offset(bool staged, int S, int T) {
   return staged ? (size_t)4 * ctx_ints(S, T) : 0;
+}
+__host__ __device__ inline size_t bits2_offset(bool staged, int S, int T) {
+  return bits_offset(staged, S, T) + (size_t)8 * bit_words(S, T);
+}
+__host__ __device__ inline size_t hpos_offset(bool staged, int S, int T) {
+  return bits2_offset(staged, S, T) + (size_t)8 * bit_words(S, T);
 }
 __host__ __device__ inline size_t hmb_offset(bool staged, int S, int T) {
   return hpos_offset(staged, S, T) + (size_t)2 * hit_cap(S, T);
 }
-// one 64-bit word of hit bits per 64 end positions
-__host__ __device__ inline size_t bits_offset(bool staged, int S, int T) {
-  return (hmb_offset(staged, S, T) + hit_cap(S, T) + 15) & ~(size_t)15;
-}
-// With a corpus, the region from hpos_offset on also holds the delta scan's occurrence records
-// (after the local phase), at least kDeltaMinRecs per wavefront.
 constexpr int kDeltaMinRecs = 256;
-__host__ __device__ inline size_t dyn_bytes(bool staged, int S, int T, bool corpus) {
-  size_t b = bits_offset(staged, S, T) + (size_t)8 * (hit_cap(S, T) / 64);
-  if (b < (size_t)kVoteBytes) b = kVoteBytes;
+__host__ __device__ inline size_t vote_offset(bool staged, int S, int T, bool corpus) {
+  size_t b = hmb_offset(staged, S, T) + (size_t)hit_cap(S, T);
   if (corpus) {
     const size_t need = hpos_offset(staged, S, T) + (size_t)4 * NW * kDeltaMinRecs;
     if (b < need) b = need;
   }
-  return b;
+  return (b + 15) & ~(size_t)15;
+}
+// one vote table per voter: wavefronts 0 .. 2 nb - 1
+__host__ __device__ inline size_t dyn_bytes(bool staged, int S, int T, bool corpus, int nb) {
+  return vote_offset(staged, S, T, corpus) + (size_t)kVoteBytes * 2 * nb;
 }
 
 constexpr int kScreenLoads = 16;  // 64-position words per screening group (1024 positions)
@@ -738,11 +964,6 @@ __device__ __forceinline__ int first_run(int nch, int w) {
 }
 constexpr uint32_t kBufferWord3 = 0x00020000;  // raw buffer resource, gfx9 format bits
 
-__device__ __forceinline__ int lanes_before(uint64_t bal) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-}
-
 // Lanes L and L+1 of acc := the low and high halves of a 64-bit ballot; L is an immediate.
 // The ballot is an SGPR pair written by a VALU compare just before, and the compiler does not
 // look inside inline assembly for hazards, so five wait states come first.
@@ -754,35 +975,33 @@ __device__ __forceinline__ uint32_t put_ballot(uint32_t acc, uint64_t v) {
   return acc;
 }
 
-// f(integral_constant<int, I>) for I = I0 .. N-1, unrolled at compile time (so that lane and
-// register indices are immediates).
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
+// DPP controls of whole-wavefront lane moves (GFX9): lane i takes lane i - 1 (lane 0 keeps the
+// old value), and lane i takes lane i - 1 mod 64.
+constexpr int kDppWaveShr1 = 0x138;
+constexpr int kDppWaveRor1 = 0x13C;
 
-// Local step 1 for one wavefront's chunk [cbeg, cend) of end positions.  The row part is read
-// with bounds-checked buffer loads (every load of a lane in flight; lanes on consecutive
+// Local step 1 for one wavefront's chunk [cbeg, cend) of end positions, row part.  The row part
+// is read with bounds-checked buffer loads (every load of a lane in flight; lanes on consecutive
 // positions, so each load instruction is one coalesced 256-byte run) and staged in LDS when
-// STAGED.  For every 64 positions one ballot is kept as a bit word: the end positions whose
-// token is the last context token t0 (match length >= 1).  Word i covers positions
-// cbeg + 64 i ...; the end positions among the sampled ids (at most T - 1, after every row
-// position) go to *s1, based at max(cbeg, n).  Returns the number of row words.
+// STAGED.  For every 64 positions two ballots are kept as bit words: the end positions whose
+// token is the last context token t0 (match length >= 1), and of those the ones whose previous
+// token is the second-to-last context token t1 (length >= 2; the previous token is the next
+// lower lane's, lane 0 taking the previous word's lane 63 or, for the first word, prev0 =
+// ctx[cbeg - 1]).  Word i covers positions cbeg + 64 i ...  Returns the number of row words;
+// *nbits gets the number of set bits of the first kind.
 template <bool STAGED>
-__device__ __forceinline__ int stage_screen(int* ctxs, int spare, uint64_t* b1w,
-                                            const int32_t* row, const int32_t* smp, int n,
-                                            int cbeg, int cend, int t0, int lane, uint64_t* s1) {
+__device__ __forceinline__ int stage_screen(int* ctxs, int spare, uint64_t* b1w, uint64_t* b2w,
+                                            const int32_t* row, int n, int cbeg, int cend, int t0,
+                                            int t1, int prev0, int lane, int* nbits) {
   const int rend = __builtin_amdgcn_readfirstlane(cend < n ? cend : n);
   // t0 arrives by a scalar load, which shares a counter with the LDS stores below: settle it
   // once here so that no store in the loop has to drain that counter
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  int nw = 0;
+  int nw = 0, cnt = 0;
   if (rend > cbeg) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, rend * 4, kBufferWord3);
+    int carry = prev0;  // the token before the group's first position
     for (int g0 = cbeg; g0 < rend; g0 += 64 * kScreenLoads) {
       int v[kScreenLoads];
       const int vo = (g0 + lane) * 4;
@@ -791,11 +1010,16 @@ __device__ __forceinline__ int stage_screen(int* ctxs, int spare, uint64_t* b1w,
         v[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo + 256 * i, 0, 0);
       const int ne = (rend - g0 + 63) >> 6 < kScreenLoads ? (rend - g0 + 63) >> 6 : kScreenLoads;
       const int nfull = (rend - g0) >> 6;  // elements whose 64 positions all lie below rend
-      uint32_t a1 = 0;
+      uint32_t a1 = 0, a2 = 0;
       static_for<0, kScreenLoads>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         if (i < ne) {
           const int x = g0 + 64 * i + lane;
+          // previous token: the lower lane's, lane 0 the previous element's lane 63
+          const int old = i == 0 ? carry
+                                 : __builtin_amdgcn_update_dpp(0, v[i > 0 ? i - 1 : 0],
+                                                               kDppWaveRor1, 0xF, 0xF, false);
+          const int prv = __builtin_amdgcn_update_dpp(old, v[i], kDppWaveShr1, 0xF, 0xF, false);
           uint64_t w1;
           if (i < nfull) {
             if (STAGED) ctxs[x] = v[i];
@@ -805,36 +1029,37 @@ __device__ __forceinline__ int stage_screen(int* ctxs, int spare, uint64_t* b1w,
             if (STAGED) ctxs[x < rend ? x : spare + lane] = v[i];
             w1 = __ballot(v[i] == t0) & ((1ull << rem) - 1ull);
           }
+          const uint64_t w2 = w1 & __ballot(prv == t1);
+          cnt += __popcll(w1);
           a1 = put_ballot<(2 * i) & 62>(a1, w1);
+          a2 = put_ballot<(2 * i) & 62>(a2, w2);
         }
       });
-      if (lane < 2 * ne) reinterpret_cast<uint32_t*>(b1w + nw)[lane] = a1;
+      carry = __builtin_amdgcn_readlane(v[kScreenLoads - 1], 63);
+      if (lane < 2 * ne) {
+        reinterpret_cast<uint32_t*>(b1w + nw)[lane] = a1;
+        reinterpret_cast<uint32_t*>(b2w + nw)[lane] = a2;
+      }
       nw += ne;
     }
   }
-  *s1 = 0;
-  if (cend > n) {
-    const int x = (cbeg > n ? cbeg : n) + lane;
-    const bool in = x < cend;
-    const int v = in ? smp[x - n] : -1;
-    *s1 = __ballot(in && v == t0);
-  }
+  *nbits = cnt;
   return nw;
 }
 
-// Positions of the set bits of nw words (word i based at base0 + 64 i) followed by one extra
-// word `extra` based at xbase, in order, into out[]; returns their number.  Every lane of the
-// wavefront takes part, on a 16-bit quarter of a word each, so that a lane walks at most 16 bits.
-__device__ __forceinline__ int bits_to_list(const uint64_t* w, int nw, uint64_t extra, int xbase,
-                                            int base0, uint16_t* out, int lane) {
+// Positions of the set bits of nw words (word i based at base0 + 64 i), in order, into out[];
+// returns their number.  Every lane of the wavefront takes part, on a 16-bit quarter of a word
+// each, so that a lane walks at most 16 bits.
+__device__ __forceinline__ int bits_to_list(const uint64_t* w, int nw, int base0, uint16_t* out,
+                                            int lane) {
   int cnt = 0;
-  const int nq = 4 * (nw + 1);
+  const int nq = 4 * nw;
   for (int q0 = 0; q0 < nq; q0 += 64) {
     const int q = q0 + lane;
     const int wi = q >> 2, part = q & 3;
-    const uint64_t wd = wi < nw ? w[wi] : (wi == nw ? extra : 0ull);
+    const uint64_t wd = wi < nw ? w[wi] : 0ull;
     uint32_t piece = (uint32_t)(wd >> (16 * part)) & 0xFFFFu;
-    const int base = (wi < nw ? base0 + 64 * wi : xbase) + 16 * part;
+    const int base = base0 + 64 * wi + 16 * part;
     const int c = __popc(piece);
     const int incl = wave_incl_add(c);
     int at = cnt + incl - c;
@@ -847,63 +1072,57 @@ __device__ __forceinline__ int bits_to_list(const uint64_t* w, int nw, uint64_t 
   return cnt;
 }
 
-// Local step 2: the backward match length of every listed hit (its last token already matches,
-// so the length is at least 1), one hit per lane: the previous token decides whether the match
-// goes on; if it does, the tail is compared four offsets per round.  Lengths go to hmb[] and
-// the wavefront's histogram.
-constexpr int kTailRegs = 24;  // tail offsets 2 .. 25 held in registers during the extension
+// Local step 2 for one wavefront's chunk, run as soon as its own screen is done: the two-token
+// hits listed in order and their backward match lengths against the tail.
+// Offsets 2 .. kTailRegs + 1 of every listed hit are read at once and compared with tail values
+// in scalar registers; longer matches (D > kTailRegs + 2) go on four offsets per round.  Lengths
+// go to hmb[] and the wavefront's histogram; returns the number of two-token hits.
+constexpr int kTailRegs = 24;
 template <bool STAGED>
-__device__ __forceinline__ void extend_hits(const int* ctxs, const uint16_t* hpos, uint8_t* hmb,
-                                            int nhit, const int* tail, int D, int* whist,
-                                            const int32_t* row, const int32_t* smp, int n,
-                                            int lane) {
-  const int t1 = D >= 2 ? tail[1] : -1;
-  const bool short_d = D <= 2 + kTailRegs;
+__device__ __forceinline__ int list_extend(const int* ctxs, const uint64_t* b2w, int nwt,
+                                           int cbeg, uint16_t* hpos, uint8_t* hmb, int tailv,
+                                           const int* tail, int D, int* whist, const int32_t* row,
+                                           const int32_t* smp, int n, int lane) {
+  const int nhit = bits_to_list(b2w, nwt, cbeg, hpos, lane);
+  wave_sync();
   int tq[kTailRegs];
 #pragma unroll
-  for (int x = 0; x < kTailRegs; ++x) tq[x] = (short_d && 2 + x < D) ? tail[2 + x] : -1;
+  for (int x = 0; x < kTailRegs; ++x) tq[x] = __builtin_amdgcn_readlane(tailv, 2 + x);
+  const bool short_d = D <= 2 + kTailRegs;
   for (int e0 = 0; e0 < nhit; e0 += 64) {
     const int e = e0 + lane;
     const bool ok = e < nhit;
     const int j = ok ? hpos[e] : 0;
     const int lim = D < j + 1 ? D : j + 1;
-    int m = 1;
-    if (ok && lim >= 2) {
-      const int c1 = STAGED ? ctxs[j - 1] : ctx_at(row, smp, n, j - 1);
-      if (c1 == t1 && short_d) {
-        // offsets 2 .. 25 in six rounds of four, compared with tail values held in registers
-        m = 2;
-        bool go = true;
+    int m = 2;
+    if (ok && lim > 2) {
+      int c[kTailRegs];
 #pragma unroll
-        for (int r = 0; r < kTailRegs / 4; ++r) {
-          if (go && 2 + 4 * r < lim) {
-            int c[4];
+      for (int q = 0; q < kTailRegs; ++q) {
+        const int o = 2 + q;
+        const int at = o < lim ? j - o : 0;
+        c[q] = STAGED ? ctxs[at] : ctx_at(row, smp, n, at);
+      }
+      bool go = true;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int o = 2 + 4 * r + q;
-              c[q] = STAGED ? ctxs[o < lim ? j - o : 0] : ctx_at(row, smp, n, o < lim ? j - o : 0);
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              go = go && 2 + 4 * r + q < lim && c[q] == tq[4 * r + q];
-              m += go ? 1 : 0;
-            }
-          }
-        }
-      } else if (c1 == t1) {
-        m = 2;
-        for (int o0 = 2; o0 < lim; o0 += 4) {
-          int c[4];
+      for (int q = 0; q < kTailRegs; ++q) {
+        go = go && 2 + q < lim && c[q] == tq[q];
+        m += go ? 1 : 0;
+      }
+      if (go && !short_d) {
+        // match lengths above kTailRegs + 2 (max_tree_depth up to 64)
+        for (int o0 = 2 + kTailRegs; o0 < lim; o0 += 4) {
+          int cc[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int at = o0 + q < lim ? j - o0 - q : 0;
-            c[q] = STAGED ? ctxs[at] : ctx_at(row, smp, n, at);
+            cc[q] = STAGED ? ctxs[at] : ctx_at(row, smp, n, at);
           }
           bool stop = false;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             if (!stop) {
-              if (o0 + q < lim && c[q] == tail[o0 + q]) ++m;
+              if (o0 + q < lim && cc[q] == tail[o0 + q]) ++m;
               else stop = true;
             }
           }
@@ -912,20 +1131,156 @@ __device__ __forceinline__ void extend_hits(const int* ctxs, const uint16_t* hpo
       }
     }
     if (ok) hmb[e] = (uint8_t)m;
-    const uint64_t one = __ballot(ok && m == 1);
-    if (ok && m > 1) atomicAdd(&whist[m], 1);
-    if (lane == 0 && one) atomicAdd(&whist[1], __popcll(one));
+    if (ok && m > 2) atomicAdd(&whist[m], 1);
+  }
+  return nhit;
+}
+
+// Local ladder rung t and, when it is the first rung of its length, its earliest continuation
+// sites (run by wavefront t once every worker has published its counts, bit words and two-token
+// lists).  Lane v - 1 of cg holds the end positions of length >= v.
+__device__ __forceinline__ void local_candidate(const ProposeArgs& a, Smem& sm, int NWW, int maxl,
+                                                int J, const uint64_t* bits,
+                                                const uint16_t* hpos_all, const uint8_t* hmb_all,
+                                                int t, int lane) {
+  const int M = a.M;
+  const int mins = a.min_self > 1 ? a.min_self : 1;
+  int cg = 0;
+  for (int w = 0; w < NWW; ++w) cg += sm.wsuf[w][lane + 1];
+  int l = 0, sup = 0, src = 0, prev_l = -1, prev_src = -1;
+  for (int ti = 0; ti <= t; ++ti) {
+    const uint64_t ok = __ballot(lane + 1 <= maxl && cg >= ti + 1);
+    l = ok ? 64 - __builtin_clzll(ok) : 0;
+    sup = l ? __builtin_amdgcn_readlane(cg, l - 1) : 0;
+    src = (ti > 0 && l == prev_l) ? prev_src : ti;
+    prev_l = l;
+    prev_src = src;
+  }
+  const int c0 = sup < M ? sup : M;
+  if (lane == 0) {
+    sm.cand_len[t] = l;
+    sm.cand_sup[t] = sup;
+    sm.cand_valid[t] = l >= mins;
+    sm.cand_c0[t] = c0;
+    sm.cand_src[t] = src;
+  }
+  if (l < mins || src != t) return;
+  int* ls = sm.lsites[t];
+  if (l == 1) {
+    // every end position whose token is the last context token: the set bits of the bit words
+    const int nwords = (J + 63) >> 6;
+    int found = 0;
+    for (int q0 = 0; found < c0 && q0 < 4 * nwords; q0 += 64) {
+      const int q = q0 + lane;
+      const int wi = q >> 2, part = q & 3;
+      const uint64_t wd = wi < nwords ? bits[wi] : 0ull;
+      uint32_t piece = (uint32_t)(wd >> (16 * part)) & 0xFFFFu;
+      const int c = __popc(piece);
+      const int incl = wave_incl_add(c);
+      int at = found + incl - c;
+      while (piece && at < c0) {
+        ls[at++] = 64 * wi + 16 * part + __builtin_ctz(piece) + 1;
+        piece &= piece - 1;
+      }
+      found += __builtin_amdgcn_readlane(incl, 63);
+    }
+    // the vote reads exactly the sites written: a count that disagreed with the bit words
+    // could otherwise leave site slots unwritten
+    if (lane == 0 && found < c0) sm.cand_c0[t] = found;
+    return;
+  }
+  // the two-token lists of the workers that hold an end position of length >= l, concatenated
+  // in wavefront (so position) order, filtered by length
+  const int q = lane < NWW ? sm.wsuf[lane][l] : 0;
+  const int c2 = lane < NWW ? sm.wsuf[lane][2] : 0;
+  const int sc = q > 0 ? c2 : 0;
+  const int inc = wave_incl_add(sc);
+  const int total = __builtin_amdgcn_readlane(inc, 63);
+  if (lane < NW) sm.vex[t][lane] = inc - sc;
+  wave_sync();
+  const uint64_t below = lanes_below(lane);
+  int found = 0;
+  for (int base = 0; base < total && found < c0; base += 64) {
+    const int e = base + lane;
+    int ex = 0, bs = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int xw = sm.vex[t][w];
+      if (w < NWW && e >= xw) {
+        ex = xw;
+        bs = sm.wbeg[w];
+      }
+    }
+    const bool in = e < total;
+    const int x = bs + e - ex;
+    const int j = in ? hpos_all[x] : 0;
+    const int m = in ? hmb_all[x] : 0;
+    const bool qq = in && m >= l;
+    const uint64_t bal = __ballot(qq);
+    const int rk = found + __popcll(bal & below);
+    if (qq && rk < c0) ls[rk] = j + 1;
+    found += __popcll(bal);
+  }
+  if (lane == 0 && found < c0) sm.cand_c0[t] = found;  // as above
+}
+
+// Windows of local candidate t, from the staged or streamed context.
+template <int KMAX, bool STAGED>
+__device__ __forceinline__ void local_windows(const Smem& sm, const int* ctxs, const int32_t* row,
+                                              const int32_t* smp, int n, int L, int t, int c0,
+                                              int cap, int lane, int (&w0)[KMAX],
+                                              int (&w1)[KMAX], int* p0_out, int* p1_out,
+                                              int* len0_out) {
+  const int* ls = sm.lsites[t];
+  const int s0 = lane, s1 = lane + 64;
+  const int p0 = s0 < c0 ? ls[s0] : 0, p1 = s1 < c0 ? ls[s1] : 0;
+  *p0_out = p0;
+  *p1_out = p1;
+  // a window holds min(cap, L - p) tokens
+  const int room0 = L - p0, cap0 = cap < KMAX ? cap : KMAX;
+  *len0_out = s0 < c0 ? (room0 < cap0 ? room0 : cap0) : 0;
+#pragma unroll
+  for (int d = 0; d < KMAX; ++d) {
+    const bool q0 = s0 < c0 && d < cap && p0 + d < L, q1 = s1 < c0 && d < cap && p1 + d < L;
+    if (STAGED) {
+      w0[d] = q0 ? ctxs[p0 + d] : -1;
+      w1[d] = q1 ? ctxs[p1 + d] : -1;
+    } else {
+      w0[d] = q0 ? ctx_at(row, smp, n, p0 + d) : -1;
+      w1[d] = q1 ? ctx_at(row, smp, n, p1 + d) : -1;
+    }
   }
 }
+
+#if SFX_PHASE_TRACE
+#define PHASE(p)                                                                 \
+  do {                                                                           \
+    if (a.trace && lane == 0) sm.ts[wid][p] = __builtin_amdgcn_s_memtime();      \
+  } while (0)
+#define PHASE_FLUSH()                                                            \
+  do {                                                                           \
+    if (a.trace && lane < kTracePhases)                                          \
+      a.trace[((size_t)b * NW + wid) * kTracePhases + lane] = sm.ts[wid][lane];  \
+  } while (0)
+#else
+#define PHASE(p) \
+  do {           \
+  } while (0)
+#define PHASE_FLUSH() \
+  do {                \
+  } while (0)
+#endif
 
 template <int KMAX, bool STAGED>
 __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   extern __shared__ int4 dyn4[];
   unsigned char* dyn = reinterpret_cast<unsigned char*>(dyn4);
   int* ctxs = reinterpret_cast<int*>(dyn);  // the context (STAGED only)
+  uint64_t* bits_all = reinterpret_cast<uint64_t*>(dyn + bits_offset(STAGED, a.S, a.T));
+  uint64_t* bits2_all = reinterpret_cast<uint64_t*>(dyn + bits2_offset(STAGED, a.S, a.T));
   uint16_t* hpos_all = reinterpret_cast<uint16_t*>(dyn + hpos_offset(STAGED, a.S, a.T));
   uint8_t* hmb_all = dyn + hmb_offset(STAGED, a.S, a.T);
-  uint64_t* bits_all = reinterpret_cast<uint64_t*>(dyn + bits_offset(STAGED, a.S, a.T));
+  int* vote_all = reinterpret_cast<int*>(dyn + vote_offset(STAGED, a.S, a.T, a.ctl != nullptr));
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform (SGPR)
@@ -933,15 +1288,30 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   const int32_t* row = a.tok + (int64_t)b * a.S;
   const int32_t* smp = a.samp + (int64_t)b * a.T;
   const int D = a.D, nb = a.nb, M = a.M;
+#if SFX_PHASE_TRACE
+  if (lane < kTracePhases) sm.ts[wid][lane] = 0;
+#endif
+  PHASE(0);
 
   Req r;
   {
     int n = a.ntns[b];
     n = n < 0 ? 0 : (n > a.S ? a.S : n);
+    int sv[kMaxT];
+#pragma unroll
+    for (int i = 0; i < kMaxT; ++i) sv[i] = i < a.T ? smp[i] : -1;
     int t = 0;
-    while (t < a.T && smp[t] >= 0) ++t;
+    bool on = true;
+#pragma unroll
+    for (int i = 0; i < kMaxT; ++i) {
+      on = on && sv[i] >= 0;
+      t += on ? 1 : 0;
+    }
     r.n = n;
     r.t = t;
+    r.t0 = -1;
+#pragma unroll
+    for (int i = 0; i < kMaxT; ++i) r.t0 = i == t - 1 ? sv[i] : r.t0;
     r.L = n + t;
     r.J = r.L > 0 ? r.L - 1 : 0;
     r.Lcap = D < r.L ? D : r.L;
@@ -951,7 +1321,6 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     r.delta = false;
     r.snap_start = r.snap_n = r.tail_w = r.delta_lo = r.delta_hi = 0;
     r.ht_mask = 0;
-    bool delta = false;
     if (r.has) {
       const Ctl c = *a.ctl;  // one round of loads for the whole control block
       r.act = c.active;
@@ -966,8 +1335,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       } else {
         r.delta_lo = r.tail_w;
       }
-      delta = r.delta_hi - r.delta_lo > 1;
-      r.delta = delta;
+      r.delta = r.delta_hi - r.delta_lo > 1;
       r.fast = r.act >= 0 && r.snap_n > 0 && r.Lcap >= 2;
     }
   }
@@ -982,141 +1350,145 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     return;
   }
   const bool fast = r.fast;
-  for (int i = tid; i < NW * (kMaxD + 1); i += NT) (&sm.whist[0][0])[i] = 0;
-  if (!fast && tid < 2 * kMaxNB) sm.cand_valid[tid] = 0;
-  if (tid == 0) sm.wbar = 0;
+  PHASE(1);
+  for (int i = tid; i < NW * (kMaxD + 2); i += NT) (&sm.wsuf[0][0])[i] = 0;
+  if (tid < 2 * kMaxNB) sm.cand_valid[tid] = 0;
+  if (tid == 0) {
+    sm.wbar = 0;
+    sm.gready = 0;
+  }
+  if (tid <= kMaxD) sm.cap_tab[tid] = a.cap_of_len[tid];
+  if (tid <= kMaxM) sm.min_tab[tid] = a.min_count[tid];
+  // every site slot holds a valid position before any is written (a site read past a list's
+  // end can then only name a real context or corpus position)
+  static_assert(kMaxNB * kMaxM <= NT, "one site slot per thread");
+  (&sm.lsites[0][0])[tid] = 1;
+  (&sm.gsites[0][0])[tid] = 0;
   __syncthreads();
-  // the tail (read from the extension on) and the sampled ids of the staged context: loaded now,
-  // stored to LDS once wavefront 0 has screened its positions, so that the round trip overlaps
-  // its screen
-  const int tailv = tid < Lcap ? ctx_at(row, smp, n, L - 1 - tid) : 0;
-  const int sampv = (STAGED && tid < t) ? smp[tid] : 0;
 
   // ---------------------------------------------------------------- 1. local match
   // Wavefront w < NWW owns end positions [cbeg, cend): it stages them (STAGED) and marks the
   // ones whose token equals the last context token.  The ranges are runs of 64 positions in
   // wavefront order, sized by the wavefront's age on its SIMD (wavefront w is the (w / 4)-th
   // on SIMD w % 4): a SIMD issues for its oldest ready wavefront first, so its younger ones
-  // get fewer positions and every worker reaches the barriers at about the same time.  In the
-  // fast path the corpus wavefront probes the corpus and derives its ladder and sites
-  // meanwhile, through every local phase (the workers synchronise among themselves only).
+  // get fewer positions and every worker reaches the barrier at about the same time.
   const int NWW = fast ? NW - 1 : NW;
-  const bool worker = wid < NWW;
-  int cbeg = J, cend = J;
-  if (worker) {
-    const int nch = (J + 63) >> 6;
-    cbeg = 64 * (fast ? first_run<NW - 1>(nch, wid) : first_run<NW>(nch, wid));
-    cend = wid + 1 == NWW ? J
-                          : 64 * (fast ? first_run<NW - 1>(nch, wid + 1) : first_run<NW>(nch, wid + 1));
-    cbeg = cbeg < J ? cbeg : J;
-    cend = cend < J ? cend : J;
-  }
   if (fast && wid == GW) {
     corpus_wave_probe(a, r, sm, row, smp, lane);
-    if (!r.delta) corpus_wave_sites(a, r, sm, lane);
+    PHASE(2);
+    if (!r.delta) {
+      corpus_wave_sites(a, r, sm, lane);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) __hip_atomic_store(&sm.gready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      PHASE(3);
+    }
   } else {
-    uint16_t* hpos = hpos_all + cbeg;
-    uint8_t* hmb = hmb_all + cbeg;
+    const int nch = (J + 63) >> 6;
+    int cbeg = 64 * (fast ? first_run<NW - 1>(nch, wid) : first_run<NW>(nch, wid));
+    int cend = wid + 1 == NWW
+                   ? J
+                   : 64 * (fast ? first_run<NW - 1>(nch, wid + 1) : first_run<NW>(nch, wid + 1));
+    cbeg = cbeg < J ? cbeg : J;
+    cend = cend < J ? cend : J;
+    // the tail (lane x holds ctx[L-1-x]), the 64 positions before the chunk (the extension of
+    // hits near its start reads them) and the sampled ids: loaded now, in flight during the
+    // screen, and staged after it by every worker that needs them (same values, same addresses)
+    const int tailv = lane < Lcap ? ctx_at(row, smp, n, L - 1 - lane) : -1;
+    const int hx = cbeg - 64 + lane;
+    const bool hon = STAGED && cbeg < cend && hx >= 0;
+    // (the last worker stages the sampled ids in any case: windows reach the last context token)
+    const bool son = STAGED && lane < t && (wid == NWW - 1 || (cbeg < cend && cend > n));
+    const int halo = hon ? ctx_at(row, smp, n, hx) : 0;
+    const int sampv = son ? smp[lane] : 0;
     uint64_t* b1w = bits_all + (cbeg >> 6);
-    uint64_t s1 = 0;
-    const int sbase = cbeg > n ? cbeg : n;
-    const int nw = stage_screen<STAGED>(ctxs, ctx_spare(a.S, a.T), b1w, row, smp, n, cbeg, cend,
-                                        smp[t - 1], lane, &s1);
-    if (tid < Lcap) sm.tail[tid] = tailv;
-    if (STAGED && tid < t) ctxs[n + tid] = sampv;
-    if (fast) worker_barrier(&sm.wbar, NWW, lane);
-    else __syncthreads();
-
-    // match lengths of the hits, listed in order
-    const int nhit = bits_to_list(b1w, nw, s1, sbase, cbeg, hpos, lane);
+    uint64_t* b2w = bits2_all + (cbeg >> 6);
+    // the second-to-last context token (compared as it is, like every context token) and the
+    // token before the chunk
+    const bool has_t1 = D >= 2 && L >= 2;
+    const int t1 = has_t1 ? ctx_at(row, smp, n, L - 2) : -1;
+    const int prev0 = cbeg > 0 && cbeg < cend ? ctx_at(row, smp, n, cbeg - 1) : -1;
+    int c1 = 0;
+    const int nwr = stage_screen<STAGED>(ctxs, ctx_spare(a.S, a.T), b1w, b2w, row, n, cbeg, cend,
+                                         r.t0, t1, prev0, lane, &c1);
+    if (hon) ctxs[hx] = halo;
+    if (son) ctxs[n + lane] = sampv;
+    int nwt = nwr;
+    if (cend > n && cend > cbeg) {
+      // end positions among the sampled ids (at most T - 1, after every row position): their
+      // bits join the words of the row (positions sb ..).  A wavefront with an empty chunk
+      // (cbeg == cend, short rows) owns no word and writes none.
+      const int sb = cbeg > n ? cbeg : n;
+      const int x = sb + lane;
+      const bool in = x < cend;
+      const uint64_t s1 = __ballot(in && smp[in ? x - n : 0] == r.t0);
+      const int pvx = in && x >= 1 ? ctx_at(row, smp, n, x - 1) : -1;
+      const uint64_t s2 = s1 & __ballot(pvx == t1);
+      c1 += __popcll(s1);
+      const int sw = (sb >> 6) - (cbeg >> 6), sh = sb & 63;
+      if (lane == 0) {
+        const uint64_t lo = s1 << sh, hi = sh ? s1 >> (64 - sh) : 0ull;
+        const uint64_t lo2 = s2 << sh, hi2 = sh ? s2 >> (64 - sh) : 0ull;
+        b1w[sw] = (sw < nwr ? b1w[sw] : 0ull) | lo;
+        b2w[sw] = (sw < nwr ? b2w[sw] : 0ull) | lo2;
+        if (sh && ((cend - 1) >> 6) > (sb >> 6)) {
+          b1w[sw + 1] = hi;
+          b2w[sw + 1] = hi2;
+        }
+      }
+      nwt = ((cend + 63) >> 6) - (cbeg >> 6);
+    }
     wave_sync();
-    extend_hits<STAGED>(ctxs, hpos, hmb, nhit, sm.tail, D, sm.whist[wid], row, smp, n, lane);
+    PHASE(2);
+    // every worker writes the same tail values (its longest matches read them back)
+    if (lane < Lcap) sm.tail[lane] = tailv;
+    if (lane == 0) sm.wbeg[wid] = cbeg;
+    // two-token hits and their match lengths
+    int c2 = 0;
+    if (has_t1 && nwt > 0) {
+      c2 = list_extend<STAGED>(ctxs, b2w, nwt, cbeg, hpos_all + cbeg, hmb_all + cbeg, tailv,
+                               sm.tail, D, sm.wsuf[wid], row, smp, n, lane);
+    }
+    PHASE(10);
     wave_sync();
     {
-      // this wavefront's suffix sums: wsuf[w][v] = its positions with length >= v, for
-      // v = lane + 1 (lengths 1 .. 64 on 64 lanes)
-      const int h = lane + 1 <= D ? sm.whist[wid][lane + 1] : 0;
+      // this wavefront's suffix counts, in place over its histogram: wsuf[w][v] = its end
+      // positions with length >= v, for v = lane + 1 (lengths 1 .. 64 on 64 lanes)
+      const int v = lane + 1;
+      const int h = (v >= 3 && v <= D) ? sm.wsuf[wid][v] : 0;
       const int incl = wave_incl_add(h);
-      sm.wsuf[wid][lane + 1] = __builtin_amdgcn_readlane(incl, 63) - incl + h;
+      int s = __builtin_amdgcn_readlane(incl, 63) - incl + h;
+      s = v == 1 ? c1 : (v == 2 ? c2 : s);
+      sm.wsuf[wid][v] = s;
     }
-    if (fast) worker_barrier(&sm.wbar, 2 * NWW, lane);
+    PHASE(3);
+    if (fast) worker_barrier(&sm.wbar, NWW, lane, a.err);
     else __syncthreads();
-
-    // ladder and this wavefront's site offsets: every worker wavefront derives them from the
-    // per-wavefront suffix sums (lane v - 1 of cg = positions with length >= v); wavefront 0 also
-    // records the candidates.  Then the earliest sites of every distinct local level, in one
-    // ordered pass over the hit list.
-    int cg = 0;
-    for (int w = 0; w < NWW; ++w) cg += sm.wsuf[w][lane + 1];
-    const int maxl = D < J ? D : J;
-    const int mins = a.min_self > 1 ? a.min_self : 1;
-    int lv[kMaxNB], pre[kMaxNB], run[kMaxNB];
-    bool act[kMaxNB];
-    bool any = false;
-    int prev_l = -1, prev_src = -1;
-#pragma unroll
-    for (int ti = 0; ti < kMaxNB; ++ti) {
-      act[ti] = false;
-      lv[ti] = 0;
-      pre[ti] = 0;
-      run[ti] = 0;
-      if (ti < nb) {
-        const uint64_t ok = __ballot(lane + 1 <= maxl && cg >= ti + 1);
-        const int l = ok ? 64 - __builtin_clzll(ok) : 0;
-        const int sup = l ? __builtin_amdgcn_readlane(cg, l - 1) : 0;
-        const int src = (ti > 0 && l == prev_l) ? prev_src : ti;
-        prev_l = l;
-        prev_src = src;
-        if (wid == 0 && lane == 0) {
-          sm.cand_len[ti] = l;
-          sm.cand_sup[ti] = sup;
-          sm.cand_valid[ti] = l >= mins;
-          sm.cand_c0[ti] = sup < M ? sup : M;
-          sm.cand_src[ti] = src;
-        }
-        const int c = (l >= 1 && lane < NWW) ? sm.wsuf[lane][l] : 0;
-        const int x = wave_incl_add(c);
-        const int mypre = __builtin_amdgcn_readlane(x - c, wid);
-        act[ti] = l >= mins && src == ti && mypre < M;
-        lv[ti] = l;
-        pre[ti] = mypre;
-        any = any || act[ti];
-      }
-    }
-    for (int e0 = 0; any && e0 < nhit; e0 += 64) {
-      const int e = e0 + lane;
-      const int j = e < nhit ? hpos[e] : 0;
-      const int m = e < nhit ? hmb[e] : 0;
-      any = false;
-#pragma unroll
-      for (int ti = 0; ti < kMaxNB; ++ti) {
-        if (act[ti]) {
-          const bool q = m >= lv[ti];
-          const uint64_t bal = __ballot(q);
-          const int rk = pre[ti] + run[ti] + lanes_before(bal);
-          if (q && rk < M) sm.lsites[ti][rk] = j + 1;
-          run[ti] += __popcll(bal);
-          act[ti] = pre[ti] + run[ti] < M;
-          any = any || act[ti];
-        }
-      }
+    PHASE(4);
+    // ladder rung, sites, windows and vote of local candidate wid
+    if (wid < nb) {
+      const int maxl = D < J ? D : J;
+      local_candidate(a, sm, NWW, maxl, J, bits_all, hpos_all, hmb_all, wid, lane);
+      wave_sync();
+      PHASE(5);
     }
   }
 
   // ---------------------------------------------------------------- 2. global (general path)
   if (r.has && (!fast || r.delta) && Lcap >= 2) {
-    // With a live snapshot and a delta, the corpus wavefront has probed the snapshot beside the
-    // local phase (its results stand); the workers may use their histograms until here.
-    if (fast) __syncthreads();
+    // The local sites are gathered and the hit lists are dead.  With a live snapshot and a
+    // delta, the corpus wavefront has probed the snapshot beside the local phase (its results
+    // stand).
+    __syncthreads();
     if (tid <= kMaxD) {
       if (!fast) sm.ghist[tid] = 0;
       sm.dhist[tid] = 0;
     }
-    for (int i = tid; i < NW * (kMaxD + 1); i += NT) (&sm.whist[0][0])[i] = 0;
+    for (int i = tid; i < NW * (kMaxD + 2); i += NT) (&sm.wsuf[0][0])[i] = 0;
     __syncthreads();
     const int act = r.act;
     const long long snap_start = r.snap_start;
     const long long dead_below = r.tail_w - snap_start;
+    const int sbase = (int)(snap_start - r.tail_w);  // snapshot index -> site coordinate
     const View ib = view_of(a, act >= 0 ? act : 0, r.ht_mask);
     if (tid == 0) {
       sm.plp[0] = ib.pl0;
@@ -1164,11 +1536,11 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       se = has_delta ? (sb + dseg < dhi - 1 ? sb + dseg : dhi - 1) : sb;
     }
     const size_t dbase = hpos_offset(STAGED, a.S, a.T);
-    const int H = (int)((dyn_bytes(STAGED, a.S, a.T, true) - dbase) / (4 * NW));
+    const int H = (int)((vote_offset(STAGED, a.S, a.T, true) - dbase) / (4 * NW));
     uint32_t* recs = reinterpret_cast<uint32_t*>(dyn + dbase) + wid * H;
     int nrec = 0;
     if (has_delta) {
-      int* wh = sm.whist[wid];
+      int* wh = sm.wsuf[wid];  // this wavefront's length histogram, then (in place) suffix sums
       auto keep = [&](long long u, long long, int m) {
         const bool q = m >= 2;
         const uint64_t bal = __ballot(q);
@@ -1189,6 +1561,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       wave_sync();
       // this wavefront's suffix sums: wsuf[w][v] = its occurrences of length >= v, v = lane + 1
       const int h = lane + 1 <= Lcap ? wh[lane + 1] : 0;
+      wave_sync();
       const int incl = wave_incl_add(h);
       sm.wsuf[wid][lane + 1] = __builtin_amdgcn_readlane(incl, 63) - incl + h;
     }
@@ -1236,7 +1609,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       const int ci = nb + ti;
       if (!sm.cand_valid[ci] || sm.cand_src[ci] != ci) continue;  // uniform
       const int l = sm.cand_len[ci];
-      long long* gs = sm.gsites[ti];
+      int* gs = sm.gsites[ti];
       int nsnap = 0;
       if (act >= 0) {
         if (l <= 4) {
@@ -1244,7 +1617,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
           const int live = sm.g_live[g];
           const int32_t* pl = sm.plp[g] + sm.g_off[g];
           nsnap = live < M ? live : M;
-          for (int x = tid; x < nsnap; x += NT) gs[x] = (long long)pl[x] + l + snap_start;
+          for (int x = tid; x < nsnap; x += NT) gs[x] = pl[x] + l + sbase;
         } else {
           const int32_t* pl4 = ib.pl2 + sm.g_off[2];
           const int seg = (live4 + NT - 1) / NT;
@@ -1257,7 +1630,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
           if (c && rk < M) {
             for (int x = lo; x < hi && rk < M; ++x) {
               const int i = pl4[x];
-              if (extend4(ib.text, sm.tail, i, l) >= l) gs[rk++] = (long long)i + 4 + snap_start;
+              if (extend4(ib.text, sm.tail, i, l) >= l) gs[rk++] = i + 4 + sbase;
             }
           }
           nsnap = total < M ? total : M;
@@ -1279,7 +1652,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
           const int rk = off + lanes_before(bal);
           if (q && rk < M) {
             const long long u = sb + (long long)(rc >> 6);
-            gs[rk] = (listed ? dlo + (long long)a.pair_list[u] : u) + 1;
+            gs[rk] = (int)((listed ? dlo + (long long)a.pair_list[u] : u) + 1 - r.tail_w);
           }
           off += __popcll(bal);
         }
@@ -1289,7 +1662,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
             const bool q = m >= l;
             const uint64_t bal = __ballot(q);
             const int rk = off + lanes_before(bal);
-            if (q && rk < M) gs[rk] = x + 1;
+            if (q && rk < M) gs[rk] = (int)(x + 1 - r.tail_w);
             off += __popcll(bal);
             return off < M;
           };
@@ -1300,76 +1673,60 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       // no barrier per candidate: each writes only its own site array, and the workgroup scan
       // of the next one ends with its own barriers
     }
+    __syncthreads();
   }
-  __syncthreads();
 
-  // ---------------------------------------------------------------- 3. expansion and vote
-  const bool voter = wid < 2 * nb && sm.cand_valid[wid] && sm.cand_src[wid] == wid;
-  int w0[KMAX], w1[KMAX];
-  int c0 = 0, cap = 0;
-  if (voter) {
+  // ---------------------------------------------------------------- 3. votes
+  // One call site for every vote: wavefront ci votes candidate ci.  Without the general path,
+  // local candidate t is voted right after its sites, and corpus candidate nb + t as soon as the
+  // corpus wavefront has published its sites (while other wavefronts still work).
+  if (wid < 2 * nb) {
     const int ci = wid;
-    const int src = sm.cand_src[ci];
-    c0 = sm.cand_c0[ci];
-    cap = a.cap_of_len[sm.cand_len[ci]];
-    const int s0 = lane, s1 = lane + 64;
-    if (ci < nb) {
-      const int* ls = sm.lsites[src];
-      const int p0 = s0 < c0 ? ls[s0] : 0, p1 = s1 < c0 ? ls[s1] : 0;
-#pragma unroll
-      for (int d = 0; d < KMAX; ++d) {
-        const bool q0 = s0 < c0 && d < cap && p0 + d < L, q1 = s1 < c0 && d < cap && p1 + d < L;
-        if (STAGED) {
-          w0[d] = q0 ? ctxs[p0 + d] : -1;
-          w1[d] = q1 ? ctxs[p1 + d] : -1;
-        } else {
-          w0[d] = q0 ? ctx_at(row, smp, n, p0 + d) : -1;
-          w1[d] = q1 ? ctx_at(row, smp, n, p1 + d) : -1;
+    const bool general = r.has && (!fast || r.delta) && Lcap >= 2;
+    if (fast && !general && ci >= nb && wid != GW) wait_flag(&sm.gready, lane, a.err);
+    if (sm.cand_valid[ci] && sm.cand_src[ci] == ci) {
+      int* hk = vote_all + wid * (2 * kVoteSlots);
+      const int c0 = sm.cand_c0[ci];
+      const int cap = sm.cap_tab[sm.cand_len[ci]];
+      int w0[KMAX], w1[KMAX];
+      int p0 = 0, p1 = 0, len0 = 0;
+      long long q0 = 0, q1 = 0;
+      const bool loc = ci < nb;
+      if (loc)
+        local_windows<KMAX, STAGED>(sm, ctxs, row, smp, n, L, ci, c0, cap, lane, w0, w1, &p0, &p1,
+                                    &len0);
+      else
+        corpus_windows<KMAX>(a, r, sm.gsites[ci - nb], c0, cap, lane, w0, w1, &q0, &q1, &len0);
+      PHASE(6);
+      // site slot 0's token at depth e, from its source (only for depths inside its window)
+      auto tok_at = [&](int e) -> int {
+        if (loc) {
+          const int x = p0 + e;
+          return STAGED ? ctxs[x] : ctx_at(row, smp, n, x);
         }
-      }
-    } else {
-      const long long* gs = sm.gsites[src - nb];
-      const int act = r.act;
-      const int32_t* text = act == 0 ? a.idx[0].text : (act == 1 ? a.idx[1].text : nullptr);
-      const long long ss = r.snap_start, sn = r.snap_n;
-      const long long q0 = s0 < c0 ? gs[s0] : 0, q1 = s1 < c0 ? gs[s1] : 0;
-      bool live0 = s0 < c0, live1 = s1 < c0;
-      const int rcap = (int)a.ring_cap;
-      int r0 = (int)(q0 % a.ring_cap), r1 = (int)(q1 % a.ring_cap);
-      // every window token is loaded at once (each address is a live snapshot position or a
-      // ring slot, so always in bounds); a site's window then ends at its first separator
-#pragma unroll
-      for (int d = 0; d < KMAX; ++d) {
-        w0[d] = *corpus_ptr(a, text, ss, sn, q0 + d, r0);
-        w1[d] = *corpus_ptr(a, text, ss, sn, q1 + d, r1);
-        r0 = ring_next(r0, rcap);
-        r1 = ring_next(r1, rcap);
-      }
-#pragma unroll
-      for (int d = 0; d < KMAX; ++d) {
-        live0 = live0 && d < cap && w0[d] >= 0;
-        live1 = live1 && d < cap && w1[d] >= 0;
-        w0[d] = live0 ? w0[d] : -1;
-        w1[d] = live1 ? w1[d] : -1;
+        const int32_t* text = r.act == 0 ? a.idx[0].text : a.idx[1].text;
+        const long long q = q0 + e;
+        return *corpus_ptr(a, text, r.snap_start, r.snap_n, q, (int)(q % a.ring_cap));
+      };
+      int nout = 0, snum = 0;
+      vote_run<KMAX>(w0, w1, len0, c0, cap, sm.min_tab[c0], hk, hk + kVoteSlots, lane, tok_at,
+                     sm.cand_out[ci], &nout, &snum);
+      if (lane == 0) {
+        sm.cand_n[ci] = nout;
+        sm.cand_snum[ci] = snum;
       }
     }
   }
-  __syncthreads();  // the context and the hit lists are dead from here on: vote tables
-  if (voter) {
-    int nout = 0, snum = 0;
-    int* hk = reinterpret_cast<int*>(dyn) + wid * (2 * kVoteSlots);
-    vote_run<KMAX>(w0, w1, c0, cap, a.min_count[c0], hk, hk + kVoteSlots, lane,
-                   sm.cand_out[wid], &nout, &snum);
-    if (lane == 0) {
-      sm.cand_n[wid] = nout;
-      sm.cand_snum[wid] = snum;
-    }
-  }
+  PHASE(7);
   __syncthreads();
+  PHASE(8);
 
-  // selection and output row, by wavefront 0 from registers (a candidate with the same length
-  // as an earlier one of its source shares that one's sites and vote)
-  if (wid != 0) return;
+  // selection and output row, by wavefront 0 (a candidate with the same length as an earlier
+  // one of its source shares that one's sites and vote)
+  if (wid != 0) {
+    PHASE_FLUSH();
+    return;
+  }
   const bool cv = lane < 2 * nb && sm.cand_valid[lane];
   const int csrc = cv ? sm.cand_src[lane] : 0;
   const int csn = cv ? sm.cand_snum[csrc] : 0;
@@ -1399,13 +1756,15 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   }
   const int ws = win >= 0 ? __builtin_amdgcn_readlane(csrc, win) : -1;
   const int nv = win >= 0 ? __builtin_amdgcn_readlane(cn, win) : 0;
-  const int fill = a.mode == 0 ? sm.tail[0] : -1;
+  const int fill = a.mode == 0 ? r.t0 : -1;
   const int wlen = win >= 0 ? __builtin_amdgcn_readlane(clen, win) : 0;
   for (int i = lane; i < a.k; i += 64) drow[i] = i < nv ? sm.cand_out[ws][i] : fill;
   if (lane == 0) {
     a.nvalid[b] = nv;
     a.pick[b] = win >= 0 ? (nv << 16) | ((win >= nb ? 1 : 0) << 8) | wlen : -1;
   }
+  PHASE(9);
+  PHASE_FLUSH();
 }
 
 __global__ void update_state_kernel(int B, int S, int T, int32_t* tok, const int32_t* ntns,
@@ -1433,8 +1792,8 @@ hipError_t launch_k(const ProposeArgs& a, bool staged, size_t dyn, hipStream_t s
 
 }  // namespace
 
-size_t propose_dynamic_lds(bool staged, int S, int T, bool corpus) {
-  return dyn_bytes(staged, S, T, corpus);
+size_t propose_dynamic_lds(bool staged, int S, int T, bool corpus, int nb) {
+  return dyn_bytes(staged, S, T, corpus, nb);
 }
 
 namespace {
@@ -1443,8 +1802,8 @@ size_t g_static_lds = 0;  // largest static LDS over the propose instantiations 
 
 size_t propose_static_lds() { return g_static_lds ? g_static_lds : sizeof(Smem); }
 
-bool propose_staged(int S, int T, bool stream_ctx, bool corpus) {
-  return !stream_ctx && dyn_bytes(true, S, T, corpus) + propose_static_lds() <= kLdsBytes;
+bool propose_staged(int S, int T, bool stream_ctx, bool corpus, int nb) {
+  return !stream_ctx && dyn_bytes(true, S, T, corpus, nb) + propose_static_lds() <= kLdsBytes;
 }
 
 hipError_t propose_prepare() {
@@ -1472,8 +1831,8 @@ hipError_t propose_prepare() {
 hipError_t launch_propose(const ProposeArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const bool corpus = a.ctl != nullptr;
-  const bool staged = propose_staged(a.S, a.T, a.stream_ctx != 0, corpus);
-  const size_t dyn = dyn_bytes(staged, a.S, a.T, corpus);
+  const bool staged = propose_staged(a.S, a.T, a.stream_ctx != 0, corpus, a.nb);
+  const size_t dyn = dyn_bytes(staged, a.S, a.T, corpus, a.nb);
   if (dyn + propose_static_lds() > kLdsBytes) return hipErrorInvalidValue;
   if (a.k <= 8) return launch_k<8>(a, staged, dyn, st);
   if (a.k <= 16) return launch_k<16>(a, staged, dyn, st);

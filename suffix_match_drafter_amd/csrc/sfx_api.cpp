@@ -344,8 +344,10 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
   {
     const bool corpus = cfg->corpus_capacity > 0;
     const bool staged = propose_staged(cfg->max_seq, cfg->max_sampled,
-                                       (cfg->flags & SFX_FLAG_STREAM_CONTEXT) != 0, corpus);
-    const size_t lds = propose_dynamic_lds(staged, cfg->max_seq, cfg->max_sampled, corpus);
+                                       (cfg->flags & SFX_FLAG_STREAM_CONTEXT) != 0, corpus,
+                                       cfg->num_backoff);
+    const size_t lds =
+        propose_dynamic_lds(staged, cfg->max_seq, cfg->max_sampled, corpus, cfg->num_backoff);
     if (lds + propose_static_lds() > kLdsBytes) {
       delete c;
       return fail(SFX_EINVAL, "max_seq=%d with max_sampled=%d needs %zu bytes of LDS per request, "
@@ -462,6 +464,16 @@ static void fill_tables(const sfx_config& g, int32_t k, ProposeArgs* a) {
         scored ? (uint8_t)((g.min_token_prob_ppm * c0 + 999999) / 1000000) : (uint8_t)0;
 }
 
+#ifndef SFX_PHASE_TRACE
+#define SFX_PHASE_TRACE 0
+#endif
+#if SFX_PHASE_TRACE
+// Phase-trace builds only: the device buffer that every propose launch stamps its wavefronts'
+// phase times into ([B][16][kTracePhases] uint64), or nullptr.
+static uint64_t* g_phase_trace = nullptr;
+extern "C" void sfx_debug_phase_trace(void* buf) { g_phase_trace = (uint64_t*)buf; }
+#endif
+
 // The drafter step with draft width k (at most the configured one), after argument checks.
 static int propose_k(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
                      const int32_t* ntns, const int32_t* tok, const int32_t* samp,
@@ -498,6 +510,10 @@ static int propose_k(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
   a.ring_cap = c->cap > 0 ? c->cap : 1;
   a.stream_ctx = (g.flags & SFX_FLAG_STREAM_CONTEXT) != 0;
   a.pick = c->pick;
+  a.err = c->err;
+#if SFX_PHASE_TRACE
+  a.trace = g_phase_trace;
+#endif
   if (c->pair_list && B <= kPairMaxBatch && c->ingest_epoch != c->live_epoch) {
     PairIndexArgs p{};
     p.B = B;
