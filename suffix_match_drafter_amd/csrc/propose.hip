@@ -219,6 +219,9 @@ struct Smem {
   int cand_len[2 * kMaxNB], cand_sup[2 * kMaxNB], cand_c0[2 * kMaxNB], cand_valid[2 * kMaxNB];
   int cand_src[2 * kMaxNB], cand_n[2 * kMaxNB];
   int cand_snum[2 * kMaxNB];  // at most k * M = 4096
+  // 1 once candidate i's vote is final (its cand_n / cand_snum written before): the scored mode
+  // drops a vote as soon as a final score beats every score it could still reach
+  int cand_done[2 * kMaxNB];
   int cand_out[2 * kMaxNB][kMaxK];
   int lsites[kMaxNB][kMaxM];
   int gsites[kMaxNB][kMaxM];  // logical corpus positions minus the oldest live one (Ctl tail)
@@ -228,6 +231,7 @@ struct Smem {
   int wsum[NW + 1];
   int wbar;    // arrivals at the worker-only barrier
   int gready;  // the corpus wavefront has published its candidates and sites (fast path)
+  int lready;  // local candidate 0's length and validity are written (fast path)
   uint8_t cap_tab[kMaxD + 1];  // the per-call draft cap and stop-count tables, staged
   uint8_t min_tab[kMaxM + 1];
 #if SFX_PHASE_TRACE
@@ -604,6 +608,37 @@ __device__ __forceinline__ void vote_depth(int x0, int x1, uint64_t A0, uint64_t
   }
 }
 
+// Scored selection: whether a candidate other than ci whose vote is final beats every score ci
+// can still reach, bnum / bden (a higher score, or the same one earlier in candidate order), so
+// that ci cannot be selected.  Scores compare by cross products (snum <= 4096, c0 <= 128).
+__device__ __forceinline__ bool outscored(Smem& sm, int ci, int nb, int bnum, int bden,
+                                          int lane) {
+  const bool on = lane < 2 * nb && lane != ci;
+  const int dn = on ? __hip_atomic_load(&sm.cand_done[lane], __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_WORKGROUP)
+                    : 0;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const int sj = dn ? sm.cand_snum[lane] : 0, cj = dn ? sm.cand_c0[lane] : 1;
+  const int lhs = sj * bden, rhs = bnum * cj;
+  return __ballot(dn != 0 && (lhs > rhs || (lhs == rhs && lane < ci))) != 0;
+}
+
+// w[e] for a wavefront-uniform e < KMAX (a power of two), by a tree of selects on e's bits:
+// registers cannot be indexed at run time.
+template <int KMAX>
+__device__ __forceinline__ int pick_depth(const int (&w)[KMAX], int e) {
+  int x[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) x[i] = w[i];
+#pragma unroll
+  for (int h = KMAX / 2; h >= 1; h /= 2) {
+    const bool hi = (e & h) != 0;
+#pragma unroll
+    for (int i = 0; i < h; ++i) x[i] = hi ? x[i + h] : x[i];
+  }
+  return x[0];
+}
+
 // Depth-wise vote, depth by depth from depth d, with the alive sites as wavefront masks A0 / A1:
 // lane l owns sites l and l + 64, whose windows are w0 / w1 (-1 past a window's end).  A depth
 // whose voting sites all carry the first voting site's token is settled by one ballot pair;
@@ -655,9 +690,8 @@ __device__ __forceinline__ void vote_seq(const int (&w0)[KMAX], const int (&w1)[
 
 // Depth-wise vote of one candidate held by one wavefront: lane l owns sites l and l+64, whose
 // continuation windows are w0 / w1 (-1 past the end of a continuation and from depth cap on;
-// len0 / len1 leading tokens, windows end for good).  tok_at(e) reloads slot 0's token at depth
-// e from its source (used only at a depth a pass cannot settle).  Writes the voted tokens to
-// out[] and returns their number and the sum of their counts.  cmin is the smallest count the
+// len0 / len1 leading tokens, windows end for good).  Writes the voted tokens to out[] and
+// returns their number and the sum of their counts.  cmin is the smallest count the
 // stop rule keeps (0 without a stop rule).  hk / hc: this voter's LDS table.
 //
 // With at most 64 sites, depths are first settled in passes against a representative site r.
@@ -668,21 +702,45 @@ __device__ __forceinline__ void vote_seq(const int (&w0)[KMAX], const int (&w1)[
 // group does not settle or where the vote stops; every depth before it is settled at once.
 // That depth is voted from scratch, the winner's first site becomes the representative, and
 // the next pass starts after it.  Short votes, votes of more than 64 sites and what the passes
-// leave go depth by depth.
+// leave go depth by depth.  Returns false when the vote was dropped because beaten(bound)
+// reported that another candidate's final score beats the best this one can still reach (the
+// sum bound / c0); n_out and snum_out are then 0.
 constexpr int kPathMinDepths = 4;
 constexpr int kPathPasses = 3;
-template <int KMAX, typename TokAt>
-__device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[KMAX], int len0,
+template <int KMAX, typename Beaten>
+__device__ __forceinline__ bool vote_run(const int (&w0)[KMAX], const int (&w1)[KMAX], int len0,
                                          int c0, int cap, int cmin, int* hk, int* hc, int lane,
-                                         TokAt&& tok_at, int* out, int* n_out, int* snum_out) {
+                                         Beaten&& beaten, int* out, int* n_out, int* snum_out,
+                                         unsigned long long* vts) {
+#if SFX_PHASE_TRACE
+#define VSTAMP(i)                                                \
+  do {                                                           \
+    if (vts && lane == 0) vts[i] = __builtin_amdgcn_s_memtime(); \
+  } while (0)
+  if (vts) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the windows have landed
+  VSTAMP(11);
+#else
+#define VSTAMP(i) \
+  do {            \
+  } while (0)
+  (void)vts;
+#endif
   uint64_t A0 = __ballot(lane < c0), A1 = __ballot(lane + 64 < c0);
   int nout = 0, snum = 0, tokv = -1;
   const int dmax = cap < KMAX ? cap : KMAX;
   int d = 0;  // next depth to vote
   bool done = dmax <= 0;
+  // counts never grow with depth (the sites voting at a depth are the previous winner's), so
+  // snum + clast * (dmax - nout) bounds the final sum; clast: the last count taken
+  int clast = c0;
+  bool cut = false;  // dropped: another candidate's final score beats every reachable one
   if (!done && c0 <= 64 && dmax >= kPathMinDepths) {
     int r = 0;
     for (int pass = 0; pass < kPathPasses; ++pass) {
+      if (pass > 0 && beaten(snum + clast * (dmax - nout))) {
+        cut = true;
+        break;
+      }
       // each site's first depth of disagreement with r (r's end counts as one); lane i picks up
       // r's token at depth i
       uint32_t mm = 0;
@@ -714,11 +772,13 @@ __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[
       const bool stop = g + o == 0 || (g > o && g < cmin);
       const uint64_t ev = __ballot(in && (stop || g <= o));
       const int e = ev ? (int)__builtin_ctzll(ev) : dmax;
+      if (pass == 0) VSTAMP(12);
       // depths d .. e-1 are settled: tokens r's, counts g
       const bool acc = lane >= d && lane < e;
       tokv = acc ? rtl : tokv;
       const int gs = wave_incl_add(acc ? g : 0);
       snum += __builtin_amdgcn_readlane(gs, 63);
+      clast = e > d ? __builtin_amdgcn_readlane(g, e - 1) : clast;
       nout = e > d ? e : nout;
       wave_sync();
       if (e >= dmax || (__ballot(stop) >> e) & 1) {
@@ -727,15 +787,18 @@ __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[
       }
       // depth e from scratch, over the sites still on r's path
       const uint64_t B0 = __ballot(al && lcp >= e);
-      const int x0 = ((B0 >> lane) & 1) && len0 > e ? tok_at(e) : -1;
+      const int xe = pick_depth<KMAX>(w0, e);
+      const int x0 = ((B0 >> lane) & 1) && len0 > e ? xe : -1;
       int w, c;
       vote_depth(x0, -1, B0, 0ull, cmin, hk, hc, lane, &w, &c);
+      if (pass == 0) VSTAMP(13);
       if (c == 0 || c < cmin) {
         done = true;
         break;
       }
       tokv = lane == e ? w : tokv;
       snum += c;
+      clast = c;
       nout = e + 1;
       A0 = __ballot(x0 == w) & B0;
       d = e + 1;
@@ -746,15 +809,25 @@ __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[
       r = (int)__builtin_ctzll(A0);
     }
   }
-  if (!done) {
+  VSTAMP(14);
+  if (!done && !cut && beaten(snum + clast * (dmax - nout))) cut = true;
+  if (!done && !cut) {
     if (c0 > 64) vote_seq<KMAX, true>(w0, w1, A0, A1, d, dmax, cmin, hk, hc, lane, &nout, &snum,
                                       &tokv);
     else vote_seq<KMAX, false>(w0, w1, A0, 0ull, d, dmax, cmin, hk, hc, lane, &nout, &snum,
                                &tokv);
   }
+  VSTAMP(15);
+#undef VSTAMP
+  if (cut) {
+    *n_out = 0;
+    *snum_out = 0;
+    return false;
+  }
   if (lane < nout) out[lane] = tokv;
   *n_out = nout;
   *snum_out = snum;
+  return true;
 }
 
 // Windows of a corpus candidate: c0 sites (logical corpus positions, relative to the oldest live
@@ -763,26 +836,41 @@ __device__ __forceinline__ void vote_run(const int (&w0)[KMAX], const int (&w1)[
 template <int KMAX>
 __device__ __forceinline__ void corpus_windows(const ProposeArgs& a, const Req& r, const int* gs,
                                                int c0, int cap, int lane, int (&w0)[KMAX],
-                                               int (&w1)[KMAX], long long* q0_out,
-                                               long long* q1_out, int* len0_out) {
+                                               int (&w1)[KMAX], int* len0_out, int* len1_out) {
   const int act = r.act;
   const int32_t* text = act == 0 ? a.idx[0].text : (act == 1 ? a.idx[1].text : nullptr);
   const long long ss = r.snap_start, sn = r.snap_n;
   const int s0 = lane, s1 = lane + 64;
   const long long q0 = r.tail_w + (s0 < c0 ? gs[s0] : 0), q1 = r.tail_w + (s1 < c0 ? gs[s1] : 0);
-  *q0_out = q0;
-  *q1_out = q1;
   bool live0 = s0 < c0, live1 = s1 < c0;
-  const int rcap = (int)a.ring_cap;
-  int r0 = (int)(q0 % a.ring_cap), r1 = (int)(q1 % a.ring_cap);
+  // offsets into the snapshot text (an unused slot reads its first token)
+  const long long o0 = live0 ? q0 - ss : 0, o1 = live1 ? q1 - ss : 0;
+  const bool in0 = text != nullptr && o0 >= 0 && o0 < sn;
+  const bool in1 = text != nullptr && o1 >= 0 && o1 < sn;
+  if (__ballot(!(in0 && in1)) == 0) {
+    // every site inside the snapshot, whose text ends with a separator: a window runs at most to
+    // it, so positions past the text's end are clamped onto it
+    const int32_t* t0p = text + o0;
+    const int32_t* t1p = text + o1;
+    const long long r0 = sn - 1 - o0, r1 = sn - 1 - o1;
+    const int l0 = r0 < KMAX ? (int)r0 : KMAX, l1 = r1 < KMAX ? (int)r1 : KMAX;
 #pragma unroll
-  for (int d = 0; d < KMAX; ++d) {
-    w0[d] = *corpus_ptr(a, text, ss, sn, q0 + d, r0);
-    w1[d] = *corpus_ptr(a, text, ss, sn, q1 + d, r1);
-    r0 = ring_next(r0, rcap);
-    r1 = ring_next(r1, rcap);
+    for (int d = 0; d < KMAX; ++d) {
+      w0[d] = t0p[d < l0 ? d : l0];
+      w1[d] = t1p[d < l1 ? d : l1];
+    }
+  } else {
+    const int rcap = (int)a.ring_cap;
+    int r0 = (int)(q0 % a.ring_cap), r1 = (int)(q1 % a.ring_cap);
+#pragma unroll
+    for (int d = 0; d < KMAX; ++d) {
+      w0[d] = *corpus_ptr(a, text, ss, sn, q0 + d, r0);
+      w1[d] = *corpus_ptr(a, text, ss, sn, q1 + d, r1);
+      r0 = ring_next(r0, rcap);
+      r1 = ring_next(r1, rcap);
+    }
   }
-  int len0 = 0;
+  int len0 = 0, len1 = 0;
 #pragma unroll
   for (int d = 0; d < KMAX; ++d) {
     live0 = live0 && d < cap && w0[d] >= 0;
@@ -790,19 +878,20 @@ __device__ __forceinline__ void corpus_windows(const ProposeArgs& a, const Req& 
     w0[d] = live0 ? w0[d] : -1;
     w1[d] = live1 ? w1[d] : -1;
     len0 += live0 ? 1 : 0;
+    len1 += live1 ? 1 : 0;
   }
   *len0_out = len0;
+  *len1_out = len1;
 }
 
 // The corpus wavefront of the fast path, first part, run while the other wavefronts stage the
-// context: tail from global memory, the three n-gram probes, the heads of the three
-// position-ordered groups into LDS, and the backward extension of the live 4-gram occurrences
-// into a length histogram (lengths of the first kMaxM kept in LDS).
+// context: the tail (lane x holds ctx[L-1-x]) into LDS, the three n-gram probes, the heads of
+// the three position-ordered groups into LDS, and the backward extension of the live 4-gram
+// occurrences into a length histogram (lengths of the first kMaxM kept in LDS).
 __device__ __forceinline__ void corpus_wave_probe(const ProposeArgs& a, const Req& r, Smem& sm,
-                                                  const int32_t* row, const int32_t* smp,
-                                                  int lane) {
-  const int n = r.n, L = r.L, Lcap = r.Lcap, M = a.M;
-  if (lane < Lcap) sm.gtail[lane] = ctx_at(row, smp, n, L - 1 - lane);
+                                                  int tailv, int lane) {
+  const int Lcap = r.Lcap, M = a.M;
+  if (lane < Lcap) sm.gtail[lane] = tailv;
   for (int i = lane; i <= kMaxD; i += 64) sm.ghist[i] = 0;
   wave_sync();
   const View ib = view_of(a, r.act, r.ht_mask);
@@ -981,66 +1070,84 @@ constexpr int kDppWaveShr1 = 0x138;
 constexpr int kDppWaveRor1 = 0x13C;
 
 // Local step 1 for one wavefront's chunk [cbeg, cend) of end positions, row part.  The row part
-// is read with bounds-checked buffer loads (every load of a lane in flight; lanes on consecutive
-// positions, so each load instruction is one coalesced 256-byte run) and staged in LDS when
-// STAGED.  For every 64 positions two ballots are kept as bit words: the end positions whose
-// token is the last context token t0 (match length >= 1), and of those the ones whose previous
-// token is the second-to-last context token t1 (length >= 2; the previous token is the next
-// lower lane's, lane 0 taking the previous word's lane 63 or, for the first word, prev0 =
-// ctx[cbeg - 1]).  Word i covers positions cbeg + 64 i ...  Returns the number of row words;
-// *nbits gets the number of set bits of the first kind.
+// [cbeg, rend), rend = min(cend, n), is read with bounds-checked buffer loads (every load of a
+// lane in flight; lanes on consecutive positions, so each load instruction is one coalesced
+// 256-byte run) and staged in LDS when STAGED.  For every 64 positions two ballots are kept as
+// bit words: the end positions whose token is the last context token t0 (match length >= 1),
+// and of those the ones whose previous token is the second-to-last context token t1 (length
+// >= 2; the previous token is the next lower lane's, lane 0 taking the previous word's lane 63
+// or, for the first word, prev0 = ctx[cbeg - 1]).  Word i covers positions cbeg + 64 i ...
+// screen_issue loads the first group of positions (issued before the workgroup's set-up
+// barrier, so the barrier waits under their latency); stage_screen consumes it and loads the
+// rest.  Returns the number of row words; *nbits gets the number of set bits of the first kind.
+struct ScreenSrc {
+  __amdgpu_buffer_rsrc_t rs;
+  int rend;
+};
+
+__device__ __forceinline__ ScreenSrc screen_issue(const int32_t* row, int n, int cbeg, int cend,
+                                                  int lane, int (&v)[kScreenLoads]) {
+  ScreenSrc src;
+  src.rend = __builtin_amdgcn_readfirstlane(cend < n ? cend : n);
+  src.rs = __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0,
+                                             (src.rend > 0 ? src.rend : 0) * 4, kBufferWord3);
+  // unconditional: a load at or past rend is out of the buffer's range and returns 0 without
+  // touching memory (every load of an empty chunk is)
+  const int vo = (cbeg + lane) * 4;
+#pragma unroll
+  for (int i = 0; i < kScreenLoads; ++i)
+    v[i] = __builtin_amdgcn_raw_buffer_load_b32(src.rs, vo + 256 * i, 0, 0);
+  return src;
+}
+
 template <bool STAGED>
 __device__ __forceinline__ int stage_screen(int* ctxs, int spare, uint64_t* b1w, uint64_t* b2w,
-                                            const int32_t* row, int n, int cbeg, int cend, int t0,
-                                            int t1, int prev0, int lane, int* nbits) {
-  const int rend = __builtin_amdgcn_readfirstlane(cend < n ? cend : n);
-  // t0 arrives by a scalar load, which shares a counter with the LDS stores below: settle it
-  // once here so that no store in the loop has to drain that counter
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                                            const ScreenSrc& src, int (&v)[kScreenLoads],
+                                            int cbeg, int t0, int t1, int prev0, int lane,
+                                            int* nbits) {
+  const int rend = src.rend;
   int nw = 0, cnt = 0;
-  if (rend > cbeg) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, rend * 4, kBufferWord3);
-    int carry = prev0;  // the token before the group's first position
-    for (int g0 = cbeg; g0 < rend; g0 += 64 * kScreenLoads) {
-      int v[kScreenLoads];
-      const int vo = (g0 + lane) * 4;
+  int carry = prev0;  // the token before the group's first position
+  for (int g0 = cbeg; g0 < rend; g0 += 64 * kScreenLoads) {
+    const int ne = (rend - g0 + 63) >> 6 < kScreenLoads ? (rend - g0 + 63) >> 6 : kScreenLoads;
+    const int nfull = (rend - g0) >> 6;  // elements whose 64 positions all lie below rend
+    uint32_t a1 = 0, a2 = 0;
+    static_for<0, kScreenLoads>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if (i < ne) {
+        const int x = g0 + 64 * i + lane;
+        // previous token: the lower lane's, lane 0 the previous element's lane 63
+        const int old = i == 0 ? carry
+                               : __builtin_amdgcn_update_dpp(0, v[i > 0 ? i - 1 : 0],
+                                                             kDppWaveRor1, 0xF, 0xF, false);
+        const int prv = __builtin_amdgcn_update_dpp(old, v[i], kDppWaveShr1, 0xF, 0xF, false);
+        uint64_t w1;
+        if (i < nfull) {
+          if (STAGED) ctxs[x] = v[i];
+          w1 = __ballot(v[i] == t0);
+        } else {
+          const int rem = rend - g0 - 64 * i;  // 1..63
+          if (STAGED) ctxs[x < rend ? x : spare + lane] = v[i];
+          w1 = __ballot(v[i] == t0) & ((1ull << rem) - 1ull);
+        }
+        const uint64_t w2 = w1 & __ballot(prv == t1);
+        cnt += __popcll(w1);
+        a1 = put_ballot<(2 * i) & 62>(a1, w1);
+        a2 = put_ballot<(2 * i) & 62>(a2, w2);
+      }
+    });
+    carry = __builtin_amdgcn_readlane(v[kScreenLoads - 1], 63);
+    if (lane < 2 * ne) {
+      reinterpret_cast<uint32_t*>(b1w + nw)[lane] = a1;
+      reinterpret_cast<uint32_t*>(b2w + nw)[lane] = a2;
+    }
+    nw += ne;
+    const int g1 = g0 + 64 * kScreenLoads;
+    if (g1 < rend) {
+      const int vo = (g1 + lane) * 4;
 #pragma unroll
       for (int i = 0; i < kScreenLoads; ++i)
-        v[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo + 256 * i, 0, 0);
-      const int ne = (rend - g0 + 63) >> 6 < kScreenLoads ? (rend - g0 + 63) >> 6 : kScreenLoads;
-      const int nfull = (rend - g0) >> 6;  // elements whose 64 positions all lie below rend
-      uint32_t a1 = 0, a2 = 0;
-      static_for<0, kScreenLoads>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        if (i < ne) {
-          const int x = g0 + 64 * i + lane;
-          // previous token: the lower lane's, lane 0 the previous element's lane 63
-          const int old = i == 0 ? carry
-                                 : __builtin_amdgcn_update_dpp(0, v[i > 0 ? i - 1 : 0],
-                                                               kDppWaveRor1, 0xF, 0xF, false);
-          const int prv = __builtin_amdgcn_update_dpp(old, v[i], kDppWaveShr1, 0xF, 0xF, false);
-          uint64_t w1;
-          if (i < nfull) {
-            if (STAGED) ctxs[x] = v[i];
-            w1 = __ballot(v[i] == t0);
-          } else {
-            const int rem = rend - g0 - 64 * i;  // 1..63
-            if (STAGED) ctxs[x < rend ? x : spare + lane] = v[i];
-            w1 = __ballot(v[i] == t0) & ((1ull << rem) - 1ull);
-          }
-          const uint64_t w2 = w1 & __ballot(prv == t1);
-          cnt += __popcll(w1);
-          a1 = put_ballot<(2 * i) & 62>(a1, w1);
-          a2 = put_ballot<(2 * i) & 62>(a2, w2);
-        }
-      });
-      carry = __builtin_amdgcn_readlane(v[kScreenLoads - 1], 63);
-      if (lane < 2 * ne) {
-        reinterpret_cast<uint32_t*>(b1w + nw)[lane] = a1;
-        reinterpret_cast<uint32_t*>(b2w + nw)[lane] = a2;
-      }
-      nw += ne;
+        v[i] = __builtin_amdgcn_raw_buffer_load_b32(src.rs, vo + 256 * i, 0, 0);
     }
   }
   *nbits = cnt;
@@ -1164,6 +1271,11 @@ __device__ __forceinline__ void local_candidate(const ProposeArgs& a, Smem& sm, 
     sm.cand_c0[t] = c0;
     sm.cand_src[t] = src;
   }
+  if (t == 0) {
+    // (the longest-match mode's corpus voter waits for candidate 0's length)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane == 0) __hip_atomic_store(&sm.lready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
   if (l < mins || src != t) return;
   int* ls = sm.lsites[t];
   if (l == 1) {
@@ -1224,32 +1336,47 @@ __device__ __forceinline__ void local_candidate(const ProposeArgs& a, Smem& sm, 
   if (lane == 0 && found < c0) sm.cand_c0[t] = found;  // as above
 }
 
-// Windows of local candidate t, from the staged or streamed context.
+// Windows of local candidate t, from the staged or streamed context.  Every load is issued
+// unconditionally at a position clamped into [0, L) (all of which are staged, or readable from
+// the row and the sampled ids), and what lies outside a window is set to -1 afterwards.  A
+// window holds min(cap, L - p) tokens and ends early at a negative id.
 template <int KMAX, bool STAGED>
 __device__ __forceinline__ void local_windows(const Smem& sm, const int* ctxs, const int32_t* row,
                                               const int32_t* smp, int n, int L, int t, int c0,
                                               int cap, int lane, int (&w0)[KMAX],
-                                              int (&w1)[KMAX], int* p0_out, int* p1_out,
-                                              int* len0_out) {
+                                              int (&w1)[KMAX], int* len0_out, int* len1_out) {
   const int* ls = sm.lsites[t];
   const int s0 = lane, s1 = lane + 64;
   const int p0 = s0 < c0 ? ls[s0] : 0, p1 = s1 < c0 ? ls[s1] : 0;
-  *p0_out = p0;
-  *p1_out = p1;
-  // a window holds min(cap, L - p) tokens
-  const int room0 = L - p0, cap0 = cap < KMAX ? cap : KMAX;
-  *len0_out = s0 < c0 ? (room0 < cap0 ? room0 : cap0) : 0;
+  const int cap0 = cap < KMAX ? cap : KMAX;
+  const int e0 = s0 < c0 ? (L - p0 < cap0 ? L - p0 : cap0) : 0;
+  const int e1 = s1 < c0 ? (L - p1 < cap0 ? L - p1 : cap0) : 0;
 #pragma unroll
   for (int d = 0; d < KMAX; ++d) {
-    const bool q0 = s0 < c0 && d < cap && p0 + d < L, q1 = s1 < c0 && d < cap && p1 + d < L;
+    const int x0 = p0 + d < L ? p0 + d : L - 1, x1 = p1 + d < L ? p1 + d : L - 1;
     if (STAGED) {
-      w0[d] = q0 ? ctxs[p0 + d] : -1;
-      w1[d] = q1 ? ctxs[p1 + d] : -1;
+      w0[d] = ctxs[x0];
+      w1[d] = ctxs[x1];
     } else {
-      w0[d] = q0 ? ctx_at(row, smp, n, p0 + d) : -1;
-      w1[d] = q1 ? ctx_at(row, smp, n, p1 + d) : -1;
+      w0[d] = *(x0 < n ? row + x0 : smp + (x0 - n));
+      w1[d] = *(x1 < n ? row + x1 : smp + (x1 - n));
     }
   }
+  // a site stops voting for good at its first depth without a token (a negative id counts as
+  // none), so its window ends there
+  bool live0 = true, live1 = true;
+  int len0 = 0, len1 = 0;
+#pragma unroll
+  for (int d = 0; d < KMAX; ++d) {
+    live0 = live0 && d < e0 && w0[d] >= 0;
+    live1 = live1 && d < e1 && w1[d] >= 0;
+    w0[d] = live0 ? w0[d] : -1;
+    w1[d] = live1 ? w1[d] : -1;
+    len0 += live0 ? 1 : 0;
+    len1 += live1 ? 1 : 0;
+  }
+  *len0_out = len0;
+  *len1_out = len1;
 }
 
 #if SFX_PHASE_TRACE
@@ -1293,25 +1420,26 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
 #endif
   PHASE(0);
 
+  // Set-up, first round of loads, all issued together: the row length, the sampled ids (lane
+  // i < T holds sampled[i]), the control block (lane i holds its word i) and the two per-call
+  // tables (thread x holds entry x of each).
+  constexpr int kCtlWords = (int)(sizeof(Ctl) / 4);
+  static_assert(kCtlWords <= 64 && sizeof(Ctl) % 8 == 0, "control block in one wavefront");
+  const int nraw = a.ntns[b];
+  const int sl = lane < a.T ? smp[lane] : -1;
+  const int cw = a.ctl != nullptr && lane < kCtlWords
+                     ? reinterpret_cast<const int*>(a.ctl)[lane] : 0;
+  const int capv = tid <= kMaxD ? a.cap_of_len[tid] : 0;
+  const int minv = tid <= kMaxM ? a.min_count[tid] : 0;
+
   Req r;
   {
-    int n = a.ntns[b];
-    n = n < 0 ? 0 : (n > a.S ? a.S : n);
-    int sv[kMaxT];
-#pragma unroll
-    for (int i = 0; i < kMaxT; ++i) sv[i] = i < a.T ? smp[i] : -1;
-    int t = 0;
-    bool on = true;
-#pragma unroll
-    for (int i = 0; i < kMaxT; ++i) {
-      on = on && sv[i] >= 0;
-      t += on ? 1 : 0;
-    }
+    const int n = nraw < 0 ? 0 : (nraw > a.S ? a.S : nraw);
+    // the leading sampled ids that are tokens (lanes from T on hold -1)
+    const int t = __builtin_ctzll(~__ballot(sl >= 0));
     r.n = n;
     r.t = t;
-    r.t0 = -1;
-#pragma unroll
-    for (int i = 0; i < kMaxT; ++i) r.t0 = i == t - 1 ? sv[i] : r.t0;
+    r.t0 = t > 0 ? __builtin_amdgcn_readlane(sl, t - 1) : -1;
     r.L = n + t;
     r.J = r.L > 0 ? r.L - 1 : 0;
     r.Lcap = D < r.L ? D : r.L;
@@ -1322,14 +1450,18 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     r.snap_start = r.snap_n = r.tail_w = r.delta_lo = r.delta_hi = 0;
     r.ht_mask = 0;
     if (r.has) {
-      const Ctl c = *a.ctl;  // one round of loads for the whole control block
-      r.act = c.active;
-      r.tail_w = c.tail;
-      r.delta_hi = c.head;
+      auto w32 = [&](size_t off) { return __builtin_amdgcn_readlane(cw, (int)(off / 4)); };
+      auto w64 = [&](size_t off) {
+        return (long long)(((uint64_t)(uint32_t)w32(off + 4) << 32) | (uint32_t)w32(off));
+      };
+      r.act = w32(offsetof(Ctl, active));
+      r.tail_w = w64(offsetof(Ctl, tail));
+      r.delta_hi = w64(offsetof(Ctl, head));
       if (r.act >= 0) {
-        r.ht_mask = r.act == 0 ? c.ht_mask[0] : c.ht_mask[1];
-        r.snap_start = r.act == 0 ? c.snap_start[0] : c.snap_start[1];
-        const long long se = r.act == 0 ? c.snap_end[0] : c.snap_end[1];
+        const int i = r.act == 0 ? 0 : 1;
+        r.ht_mask = (uint32_t)w32(offsetof(Ctl, ht_mask) + 4 * i);
+        r.snap_start = w64(offsetof(Ctl, snap_start) + 8 * i);
+        const long long se = w64(offsetof(Ctl, snap_end) + 8 * i);
         r.snap_n = se - r.snap_start;
         r.delta_lo = se > r.tail_w ? se : r.tail_w;
       } else {
@@ -1351,30 +1483,58 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   }
   const bool fast = r.fast;
   PHASE(1);
+  // LDS set-up (the tables' loads have landed with the row length's)
   for (int i = tid; i < NW * (kMaxD + 2); i += NT) (&sm.wsuf[0][0])[i] = 0;
-  if (tid < 2 * kMaxNB) sm.cand_valid[tid] = 0;
+  if (tid < 2 * kMaxNB) {
+    sm.cand_valid[tid] = 0;
+    sm.cand_done[tid] = 0;
+  }
   if (tid == 0) {
     sm.wbar = 0;
     sm.gready = 0;
+    sm.lready = 0;
   }
-  if (tid <= kMaxD) sm.cap_tab[tid] = a.cap_of_len[tid];
-  if (tid <= kMaxM) sm.min_tab[tid] = a.min_count[tid];
+  if (tid <= kMaxD) sm.cap_tab[tid] = (uint8_t)capv;
+  if (tid <= kMaxM) sm.min_tab[tid] = (uint8_t)minv;
   // every site slot holds a valid position before any is written (a site read past a list's
   // end can then only name a real context or corpus position)
   static_assert(kMaxNB * kMaxM <= NT, "one site slot per thread");
   (&sm.lsites[0][0])[tid] = 1;
   (&sm.gsites[0][0])[tid] = 0;
-  __syncthreads();
 
-  // ---------------------------------------------------------------- 1. local match
+  // Second round of loads, in flight across the set-up barrier: the tail (lane x holds
+  // ctx[L-1-x]), and for a worker the first group of its chunk, the 64 positions before the
+  // chunk (the extension of hits near its start reads them; lane 63 holds the token before the
+  // chunk) and the sampled ids it stages.
+  //
   // Wavefront w < NWW owns end positions [cbeg, cend): it stages them (STAGED) and marks the
   // ones whose token equals the last context token.  The ranges are runs of 64 positions in
   // wavefront order, sized by the wavefront's age on its SIMD (wavefront w is the (w / 4)-th
   // on SIMD w % 4): a SIMD issues for its oldest ready wavefront first, so its younger ones
   // get fewer positions and every worker reaches the barrier at about the same time.
   const int NWW = fast ? NW - 1 : NW;
-  if (fast && wid == GW) {
-    corpus_wave_probe(a, r, sm, row, smp, lane);
+  const bool cwave = fast && wid == GW;  // the corpus wavefront of the fast path
+  const int tailv = lane < Lcap ? ctx_at(row, smp, n, L - 1 - lane) : -1;
+  int cbeg = 0, cend = 0;
+  if (!cwave) {
+    const int nch = (J + 63) >> 6;
+    cbeg = 64 * (fast ? first_run<NW - 1>(nch, wid) : first_run<NW>(nch, wid));
+    cend = wid + 1 == NWW
+               ? J
+               : 64 * (fast ? first_run<NW - 1>(nch, wid + 1) : first_run<NW>(nch, wid + 1));
+    cbeg = cbeg < J ? cbeg : J;
+    cend = cend < J ? cend : J;
+  }
+  const int hx = cbeg - 64 + lane;
+  const bool hld = !cwave && cbeg < cend && hx >= 0 && (STAGED || lane == 63);
+  const int halo = hld ? ctx_at(row, smp, n, hx) : -1;
+  int sv[kScreenLoads];
+  const ScreenSrc ssrc = screen_issue(row, n, cbeg, cwave ? cbeg : cend, lane, sv);
+  __syncthreads();
+
+  // ---------------------------------------------------------------- 1. local match
+  if (cwave) {
+    corpus_wave_probe(a, r, sm, tailv, lane);
     PHASE(2);
     if (!r.delta) {
       corpus_wave_sites(a, r, sm, lane);
@@ -1383,35 +1543,20 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       PHASE(3);
     }
   } else {
-    const int nch = (J + 63) >> 6;
-    int cbeg = 64 * (fast ? first_run<NW - 1>(nch, wid) : first_run<NW>(nch, wid));
-    int cend = wid + 1 == NWW
-                   ? J
-                   : 64 * (fast ? first_run<NW - 1>(nch, wid + 1) : first_run<NW>(nch, wid + 1));
-    cbeg = cbeg < J ? cbeg : J;
-    cend = cend < J ? cend : J;
-    // the tail (lane x holds ctx[L-1-x]), the 64 positions before the chunk (the extension of
-    // hits near its start reads them) and the sampled ids: loaded now, in flight during the
-    // screen, and staged after it by every worker that needs them (same values, same addresses)
-    const int tailv = lane < Lcap ? ctx_at(row, smp, n, L - 1 - lane) : -1;
-    const int hx = cbeg - 64 + lane;
-    const bool hon = STAGED && cbeg < cend && hx >= 0;
     // (the last worker stages the sampled ids in any case: windows reach the last context token)
     const bool son = STAGED && lane < t && (wid == NWW - 1 || (cbeg < cend && cend > n));
-    const int halo = hon ? ctx_at(row, smp, n, hx) : 0;
-    const int sampv = son ? smp[lane] : 0;
     uint64_t* b1w = bits_all + (cbeg >> 6);
     uint64_t* b2w = bits2_all + (cbeg >> 6);
     // the second-to-last context token (compared as it is, like every context token) and the
     // token before the chunk
-    const bool has_t1 = D >= 2 && L >= 2;
-    const int t1 = has_t1 ? ctx_at(row, smp, n, L - 2) : -1;
-    const int prev0 = cbeg > 0 && cbeg < cend ? ctx_at(row, smp, n, cbeg - 1) : -1;
+    const bool has_t1 = Lcap >= 2;
+    const int t1 = has_t1 ? __builtin_amdgcn_readlane(tailv, 1) : -1;
+    const int prev0 = __builtin_amdgcn_readlane(halo, 63);
     int c1 = 0;
-    const int nwr = stage_screen<STAGED>(ctxs, ctx_spare(a.S, a.T), b1w, b2w, row, n, cbeg, cend,
+    const int nwr = stage_screen<STAGED>(ctxs, ctx_spare(a.S, a.T), b1w, b2w, ssrc, sv, cbeg,
                                          r.t0, t1, prev0, lane, &c1);
-    if (hon) ctxs[hx] = halo;
-    if (son) ctxs[n + lane] = sampv;
+    if (STAGED && hld) ctxs[hx] = halo;
+    if (son) ctxs[n + lane] = sl;
     int nwt = nwr;
     if (cend > n && cend > cbeg) {
       // end positions among the sampled ids (at most T - 1, after every row position): their
@@ -1420,7 +1565,9 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       const int sb = cbeg > n ? cbeg : n;
       const int x = sb + lane;
       const bool in = x < cend;
-      const uint64_t s1 = __ballot(in && smp[in ? x - n : 0] == r.t0);
+      // sampled id x - n (lanes from T on hold -1; x - n < T - 1 for every lane in range)
+      const int sx = __builtin_amdgcn_ds_bpermute(4 * (in ? x - n : 63), sl);
+      const uint64_t s1 = __ballot(in && sx == r.t0);
       const int pvx = in && x >= 1 ? ctx_at(row, smp, n, x - 1) : -1;
       const uint64_t s2 = s1 & __ballot(pvx == t1);
       c1 += __popcll(s1);
@@ -1679,41 +1826,75 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   // ---------------------------------------------------------------- 3. votes
   // One call site for every vote: wavefront ci votes candidate ci.  Without the general path,
   // local candidate t is voted right after its sites, and corpus candidate nb + t as soon as the
-  // corpus wavefront has published its sites (while other wavefronts still work).
+  // corpus wavefront has published its sites (while other wavefronts still work).  A vote that
+  // cannot change the selection is skipped: in the longest-match mode every candidate but the
+  // one the lengths select, in the scored mode one whose best reachable score a final score
+  // already beats (its score is then left at 0, which still loses to that one).
   if (wid < 2 * nb) {
     const int ci = wid;
     const bool general = r.has && (!fast || r.delta) && Lcap >= 2;
-    if (fast && !general && ci >= nb && wid != GW) wait_flag(&sm.gready, lane, a.err);
-    if (sm.cand_valid[ci] && sm.cand_src[ci] == ci) {
-      int* hk = vote_all + wid * (2 * kVoteSlots);
-      const int c0 = sm.cand_c0[ci];
-      const int cap = sm.cap_tab[sm.cand_len[ci]];
-      int w0[KMAX], w1[KMAX];
-      int p0 = 0, p1 = 0, len0 = 0;
-      long long q0 = 0, q1 = 0;
-      const bool loc = ci < nb;
-      if (loc)
-        local_windows<KMAX, STAGED>(sm, ctxs, row, smp, n, L, ci, c0, cap, lane, w0, w1, &p0, &p1,
-                                    &len0);
-      else
-        corpus_windows<KMAX>(a, r, sm.gsites[ci - nb], c0, cap, lane, w0, w1, &q0, &q1, &len0);
-      PHASE(6);
-      // site slot 0's token at depth e, from its source (only for depths inside its window)
-      auto tok_at = [&](int e) -> int {
-        if (loc) {
-          const int x = p0 + e;
-          return STAGED ? ctxs[x] : ctx_at(row, smp, n, x);
+    const bool gwait = fast && !general;  // corpus candidates arrive by flag
+    if (gwait && ci >= nb && wid != GW) wait_flag(&sm.gready, lane, a.err);
+    bool need = sm.cand_valid[ci] && sm.cand_src[ci] == ci;
+    const int c0 = sm.cand_c0[ci];
+    const int cap = sm.cap_tab[sm.cand_len[ci]];
+    const int dmax = cap < KMAX ? cap : KMAX;
+    if (need && a.mode == 0) {
+      if (ci != 0 && ci != nb) {
+        need = false;
+      } else {
+        bool known = true;  // both lengths written
+        if (gwait) {
+          if (ci == nb) {
+            wait_flag(&sm.lready, lane, a.err);
+          } else {
+            known = __hip_atomic_load(&sm.gready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+          }
         }
-        const int32_t* text = r.act == 0 ? a.idx[0].text : a.idx[1].text;
-        const long long q = q0 + e;
-        return *corpus_ptr(a, text, r.snap_start, r.snap_n, q, (int)(q % a.ring_cap));
-      };
+        if (known) {
+          const bool lv = sm.cand_valid[0], gv = sm.cand_valid[nb];
+          const bool local_wins = lv && (!gv || sm.cand_len[0] >= sm.cand_len[nb]);
+          need = (ci == 0) == local_wins;
+        }
+      }
+    } else if (need && outscored(sm, ci, nb, dmax, 1, lane)) {
+      need = false;
+    }
+    if (!need) {
+      if (lane == 0) {
+        sm.cand_n[ci] = 0;
+        sm.cand_snum[ci] = 0;
+      }
+    } else {
+      int* hk = vote_all + wid * (2 * kVoteSlots);
+      int w0[KMAX], w1[KMAX];
+      int len0 = 0, len1 = 0;
+      if (ci < nb)
+        local_windows<KMAX, STAGED>(sm, ctxs, row, smp, n, L, ci, c0, cap, lane, w0, w1, &len0,
+                                    &len1);
+      else
+        corpus_windows<KMAX>(a, r, sm.gsites[ci - nb], c0, cap, lane, w0, w1, &len0, &len1);
+      PHASE(6);
       int nout = 0, snum = 0;
-      vote_run<KMAX>(w0, w1, len0, c0, cap, sm.min_tab[c0], hk, hk + kVoteSlots, lane, tok_at,
-                     sm.cand_out[ci], &nout, &snum);
+#if SFX_PHASE_TRACE
+      unsigned long long* vts = a.trace ? sm.ts[wid] : nullptr;
+#else
+      unsigned long long* vts = nullptr;
+#endif
+      // (scored mode) whether a final score beats every score this vote can still reach
+      auto beaten = [&](int bnum) { return a.mode == 1 && outscored(sm, ci, nb, bnum, c0, lane); };
+      const int cmin = sm.min_tab[c0];
+      const bool fin = vote_run<KMAX>(w0, w1, len0, c0, cap, cmin, hk, hk + kVoteSlots, lane,
+                                      beaten, sm.cand_out[ci], &nout, &snum, vts);
       if (lane == 0) {
         sm.cand_n[ci] = nout;
         sm.cand_snum[ci] = snum;
+      }
+      if (fin) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (lane == 0)
+          __hip_atomic_store(&sm.cand_done[ci], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
   }
@@ -1741,18 +1922,22 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     if (lv && (!gv || l0 >= g0)) win = 0;
     else if (gv) win = nb;
   } else {
-    // scores snum / c0 compared by cross products (snum <= k * M = 4096, c0 <= M = 128)
-    int bsn = 0, bc0 = 1;
-    for (int i = 0; i < 2 * nb; ++i) {
-      if (!((vmask >> i) & 1)) continue;
-      const int sn = __builtin_amdgcn_readlane(csn, i);
-      const int c0i = __builtin_amdgcn_readlane(cc0, i);
-      if (win < 0 || sn * bc0 > bsn * c0i) {
-        win = i;
-        bsn = sn;
-        bc0 = c0i;
+    // scores snum / c0 compared by cross products (snum <= k * M = 4096, c0 <= M = 128); lane i
+    // holds candidate i, which wins when no valid candidate beats it: a higher score, or the
+    // same score earlier in candidate order.  The comparisons of all lanes run side by side.
+    // (bitwise, not short-circuit, operators, so that the compares do not branch)
+    int beaten = cv ? 0 : 1;
+#pragma unroll
+    for (int j = 0; j < 2 * kMaxNB; ++j) {
+      if (j < 2 * nb) {
+        const int sj = __builtin_amdgcn_readlane(csn, j), cj = __builtin_amdgcn_readlane(cc0, j);
+        const int lhs = sj * cc0, rhs = csn * cj;
+        const int vj = (int)((vmask >> j) & 1);
+        beaten |= vj & ((lhs > rhs) | ((lhs == rhs) & (j < lane)));
       }
     }
+    const uint64_t wm = __ballot(beaten == 0);
+    win = wm ? __builtin_ctzll(wm) : -1;
   }
   const int ws = win >= 0 ? __builtin_amdgcn_readlane(csrc, win) : -1;
   const int nv = win >= 0 ? __builtin_amdgcn_readlane(cn, win) : 0;
