@@ -41,6 +41,7 @@ constexpr int NW = NT / 64;
 constexpr int GW = NW - 1;          // the corpus wavefront of the fast path
 constexpr int kVoteSlots = 256;     // LDS hash slots of one voter (keys and counts)
 constexpr int kSmallVote = 24;      // alive sites at or below this vote with ballots
+constexpr int kColSites = 8;        // candidates with at most this many sites vote by columns
 
 // f(integral_constant<int, I>) for I = I0 .. N-1, unrolled at compile time (so that lane and
 // register indices are immediates).
@@ -523,6 +524,17 @@ __device__ __forceinline__ void delta_list_wave(const ProposeArgs& a, long long 
 __device__ __noinline__ uint64_t vote_split(int x0, int x1, uint64_t V0, uint64_t V1, int ref,
                                             uint64_t E0, uint64_t E1, int na, int* hk, int* hc,
                                             int lane) {
+  // wavefront-uniform arguments arrive in vector registers: make them scalar again
+  auto u64 = [](uint64_t v) {
+    return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v) |
+           ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)) << 32);
+  };
+  V0 = u64(V0);
+  V1 = u64(V1);
+  E0 = u64(E0);
+  E1 = u64(E1);
+  ref = __builtin_amdgcn_readfirstlane(ref);
+  na = __builtin_amdgcn_readfirstlane(na);
   const int ce = __popcll(E0) + __popcll(E1);
   if (na <= kSmallVote) {
     // one ballot pair per distinct token, until the best count exceeds every vote not yet
@@ -602,9 +614,11 @@ __device__ __forceinline__ void vote_depth(int x0, int x1, uint64_t A0, uint64_t
   } else if (na < cmin) {
     *c = na;  // no token reaches the stop count: any count below cmin stops the vote
   } else {
+    // (the call returns in vector registers: readfirstlane tells the compiler that the winner
+    // and its count are wavefront-uniform, or every loop around this becomes a divergent one)
     const uint64_t res = vote_split(x0, x1, V0, V1, ref, E0, E1, na, hk, hc, lane);
-    *c = (int)(res >> 32);
-    *w = (int)(uint32_t)res;
+    *c = __builtin_amdgcn_readfirstlane((int)(res >> 32));
+    *w = __builtin_amdgcn_readfirstlane((int)(uint32_t)res);
   }
 }
 
@@ -830,6 +844,118 @@ __device__ __forceinline__ bool vote_run(const int (&w0)[KMAX], const int (&w1)[
   return true;
 }
 
+// Depth-wise vote of a candidate with at most CS sites, in columns: lane i holds depth i, and
+// T[s] is site s's column (its continuation token at each depth, -1 from its first depth
+// without one on; len[s] leading tokens; every column ends by dmax <= 64).  Same result and
+// outputs as vote_run.
+//
+// A pass takes the alive site with the longest column as the reference r.  Site s's first
+// disagreement with r from depth d on, fd_s, is one ballot.  At depth i the alive sites that
+// followed r through i - 1 and still have a token vote: g_i of them with r's token (fd_s > i),
+// o_i with another (fd_s == i).  Where g_i > o_i, r's token wins with count g_i whatever the
+// others vote; the first depth where it does not (g_i <= o_i), or where the stop rule ends
+// the chain, is found by one ballot over the depth lanes.  That depth is voted from scratch
+// (the sites' tokens moved to lanes 0 .. CS - 1), the alive sites become the winner's, and the
+// next pass starts after it.
+template <int CS, typename Beaten>
+__device__ __forceinline__ bool vote_columns(const int (&T)[CS], const int (&len)[CS], int c0,
+                                             int dmax, int cmin, int* hk, int* hc, int lane,
+                                             Beaten&& beaten, int* out, int* n_out,
+                                             int* snum_out) {
+  uint32_t AS = c0 >= 32 ? ~0u : ((1u << c0) - 1u);  // alive sites
+  int nout = 0, snum = 0, tokv = -1, clast = c0;
+  const int cstop = cmin > 1 ? cmin : 1;  // a depth with fewer votes than this ends the chain
+  bool cut = false;
+  int d = 0;
+  for (int pass = 0; d < dmax && AS != 0; ++pass) {
+    if (pass > 0 && beaten(snum + clast * (dmax - nout))) {
+      cut = true;
+      break;
+    }
+    // the reference: the first alive site of the longest column
+    int rs = 0, rl = -1;
+#pragma unroll
+    for (int s = 0; s < CS; ++s) {
+      const bool better = ((AS >> s) & 1) && len[s] > rl;
+      rl = better ? len[s] : rl;
+      rs = better ? s : rs;
+    }
+    int tref = T[0];
+#pragma unroll
+    for (int s = 1; s < CS; ++s) tref = rs == s ? T[s] : tref;
+    const uint64_t from = ~0ull << d;  // depths d ..
+    int g = 0, o = 0;
+    int fd[CS];
+#pragma unroll
+    for (int s = 0; s < CS; ++s) {
+      const uint64_t D = __ballot(T[s] >= 0 && T[s] != tref) & from;
+      fd[s] = D ? (int)__builtin_ctzll(D) : 64;
+      const int m = fd[s] < len[s] ? fd[s] : len[s];
+      const bool al = (AS >> s) & 1;
+      g += al && lane < m ? 1 : 0;
+      o += al && lane == fd[s] ? 1 : 0;
+    }
+    const bool in = lane >= d && lane < dmax;
+    const int na = g + o;
+    const bool stop = in && (na < cstop || (g > o && g < cmin));
+    const bool cont = in && !stop && g <= o;
+    const uint64_t sb = __ballot(stop);
+    const uint64_t ev = sb | __ballot(cont);
+    const int e = ev ? (int)__builtin_ctzll(ev) : dmax;
+    if (e > d) {
+      const bool acc = lane >= d && lane < e;
+      tokv = acc ? tref : tokv;
+      snum += __builtin_amdgcn_readlane(wave_incl_add(acc ? g : 0), 63);
+      clast = __builtin_amdgcn_readlane(g, e - 1);
+      nout = e;
+    }
+    if (e >= dmax || ((sb >> e) & 1)) break;
+    // depth e from scratch: lane s votes site s's token when s followed r through e - 1
+    int x = -1;
+#pragma unroll
+    for (int s = 0; s < CS; ++s) {
+      const int xs = __builtin_amdgcn_readlane(T[s], e);
+      const bool vs = ((AS >> s) & 1) && fd[s] >= e;
+      x = lane == s && vs ? xs : x;
+    }
+    const uint64_t X = __ballot(x >= 0);
+    int w, c;
+    vote_depth(x, -1, X, 0ull, cmin, hk, hc, lane, &w, &c);
+    if (c == 0 || c < cmin) break;
+    tokv = lane == e ? w : tokv;
+    snum += c;
+    clast = c;
+    nout = e + 1;
+    AS = (uint32_t)__ballot(x == w);
+    d = e + 1;
+  }
+  if (cut) {
+    *n_out = 0;
+    *snum_out = 0;
+    return false;
+  }
+  if (lane < nout) out[lane] = tokv;
+  *n_out = nout;
+  *snum_out = snum;
+  return true;
+}
+
+// Columns of a candidate's sites for vote_columns: lane i of T[s] gets the token at depth i of
+// site s (s < c0), from its first depth without a token on -1; len[s] its leading tokens.  at(s,
+// i) gives the token (or -1) at depth i < dmax of site s.
+template <int CS, typename At>
+__device__ __forceinline__ void columns_cut(int (&T)[CS], int (&len)[CS], int c0, int dmax,
+                                            int lane, At&& at) {
+#pragma unroll
+  for (int s = 0; s < CS; ++s) T[s] = s < c0 && lane < dmax ? at(s, lane) : -1;
+#pragma unroll
+  for (int s = 0; s < CS; ++s) {
+    const uint64_t ok = __ballot(T[s] >= 0);
+    len[s] = (int)__builtin_ctzll(~ok);
+    T[s] = lane < len[s] ? T[s] : -1;
+  }
+}
+
 // Windows of a corpus candidate: c0 sites (logical corpus positions, relative to the oldest live
 // one, in gs), continuation tokens loaded all at once (each address is a live snapshot position
 // or a ring slot, so always in bounds) and cut at each site's first separator.
@@ -1031,7 +1157,12 @@ __host__ __device__ inline size_t dyn_bytes(bool staged, int S, int T, bool corp
   return vote_offset(staged, S, T, corpus) + (size_t)kVoteBytes * 2 * nb;
 }
 
-constexpr int kScreenLoads = 16;  // 64-position words per screening group (1024 positions)
+// 64-position words per screening group: 1536 positions (1024 with 32-token windows, whose
+// vote needs the registers)
+template <int KMAX>
+constexpr int screen_loads() {
+  return KMAX >= 32 ? 16 : 24;
+}
 
 // Share of the end positions per wavefront age rank on a SIMD (oldest first), and the total share
 // of wavefronts 0 .. w-1.
@@ -1085,8 +1216,9 @@ struct ScreenSrc {
   int rend;
 };
 
+template <int G>
 __device__ __forceinline__ ScreenSrc screen_issue(const int32_t* row, int n, int cbeg, int cend,
-                                                  int lane, int (&v)[kScreenLoads]) {
+                                                  int lane, int (&v)[G]) {
   ScreenSrc src;
   src.rend = __builtin_amdgcn_readfirstlane(cend < n ? cend : n);
   src.rs = __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0,
@@ -1095,24 +1227,24 @@ __device__ __forceinline__ ScreenSrc screen_issue(const int32_t* row, int n, int
   // touching memory (every load of an empty chunk is)
   const int vo = (cbeg + lane) * 4;
 #pragma unroll
-  for (int i = 0; i < kScreenLoads; ++i)
+  for (int i = 0; i < G; ++i)
     v[i] = __builtin_amdgcn_raw_buffer_load_b32(src.rs, vo + 256 * i, 0, 0);
   return src;
 }
 
-template <bool STAGED>
+template <bool STAGED, int G>
 __device__ __forceinline__ int stage_screen(int* ctxs, int spare, uint64_t* b1w, uint64_t* b2w,
-                                            const ScreenSrc& src, int (&v)[kScreenLoads],
+                                            const ScreenSrc& src, int (&v)[G],
                                             int cbeg, int t0, int t1, int prev0, int lane,
                                             int* nbits) {
   const int rend = src.rend;
   int nw = 0, cnt = 0;
   int carry = prev0;  // the token before the group's first position
-  for (int g0 = cbeg; g0 < rend; g0 += 64 * kScreenLoads) {
-    const int ne = (rend - g0 + 63) >> 6 < kScreenLoads ? (rend - g0 + 63) >> 6 : kScreenLoads;
+  for (int g0 = cbeg; g0 < rend; g0 += 64 * G) {
+    const int ne = (rend - g0 + 63) >> 6 < G ? (rend - g0 + 63) >> 6 : G;
     const int nfull = (rend - g0) >> 6;  // elements whose 64 positions all lie below rend
     uint32_t a1 = 0, a2 = 0;
-    static_for<0, kScreenLoads>([&](auto ic) {
+    static_for<0, G>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       if (i < ne) {
         const int x = g0 + 64 * i + lane;
@@ -1136,17 +1268,17 @@ __device__ __forceinline__ int stage_screen(int* ctxs, int spare, uint64_t* b1w,
         a2 = put_ballot<(2 * i) & 62>(a2, w2);
       }
     });
-    carry = __builtin_amdgcn_readlane(v[kScreenLoads - 1], 63);
+    carry = __builtin_amdgcn_readlane(v[G - 1], 63);
     if (lane < 2 * ne) {
       reinterpret_cast<uint32_t*>(b1w + nw)[lane] = a1;
       reinterpret_cast<uint32_t*>(b2w + nw)[lane] = a2;
     }
     nw += ne;
-    const int g1 = g0 + 64 * kScreenLoads;
+    const int g1 = g0 + 64 * G;
     if (g1 < rend) {
       const int vo = (g1 + lane) * 4;
 #pragma unroll
-      for (int i = 0; i < kScreenLoads; ++i)
+      for (int i = 0; i < G; ++i)
         v[i] = __builtin_amdgcn_raw_buffer_load_b32(src.rs, vo + 256 * i, 0, 0);
     }
   }
@@ -1528,8 +1660,9 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   const int hx = cbeg - 64 + lane;
   const bool hld = !cwave && cbeg < cend && hx >= 0 && (STAGED || lane == 63);
   const int halo = hld ? ctx_at(row, smp, n, hx) : -1;
-  int sv[kScreenLoads];
-  const ScreenSrc ssrc = screen_issue(row, n, cbeg, cwave ? cbeg : cend, lane, sv);
+  constexpr int G = screen_loads<KMAX>();
+  int sv[G];
+  const ScreenSrc ssrc = screen_issue<G>(row, n, cbeg, cwave ? cbeg : cend, lane, sv);
   __syncthreads();
 
   // ---------------------------------------------------------------- 1. local match
@@ -1553,7 +1686,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     const int t1 = has_t1 ? __builtin_amdgcn_readlane(tailv, 1) : -1;
     const int prev0 = __builtin_amdgcn_readlane(halo, 63);
     int c1 = 0;
-    const int nwr = stage_screen<STAGED>(ctxs, ctx_spare(a.S, a.T), b1w, b2w, ssrc, sv, cbeg,
+    const int nwr = stage_screen<STAGED, G>(ctxs, ctx_spare(a.S, a.T), b1w, b2w, ssrc, sv, cbeg,
                                          r.t0, t1, prev0, lane, &c1);
     if (STAGED && hld) ctxs[hx] = halo;
     if (son) ctxs[n + lane] = sl;
@@ -1835,28 +1968,41 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     const bool general = r.has && (!fast || r.delta) && Lcap >= 2;
     const bool gwait = fast && !general;  // corpus candidates arrive by flag
     if (gwait && ci >= nb && wid != GW) wait_flag(&sm.gready, lane, a.err);
-    bool need = sm.cand_valid[ci] && sm.cand_src[ci] == ci;
-    const int c0 = sm.cand_c0[ci];
-    const int cap = sm.cap_tab[sm.cand_len[ci]];
+    // the longest-match mode compares candidate 0 with candidate nb: wait for, or look at,
+    // the flag of the one this wavefront does not produce
+    bool known = true;
+    if (a.mode == 0 && gwait) {
+      if (ci == nb) {
+        wait_flag(&sm.lready, lane, a.err);
+      } else if (ci == 0) {
+        known = __hip_atomic_load(&sm.gready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      }
+    }
+    // two rounds of LDS reads: lane j < 2 nb takes candidate j's fields, every lane its site
+    // slot of candidate ci (slots past c0 hold harmless initial positions), then the cap and
+    // the stop count of lane j's candidate
+    const bool cl = lane < 2 * nb;
+    const int fv = cl ? sm.cand_valid[lane] : 0;
+    const int fs = cl ? sm.cand_src[lane] : -1;
+    const int fc = cl ? sm.cand_c0[lane] : 0;
+    const int fl = cl ? sm.cand_len[lane] : 0;
+    const int sv_all = ci < nb ? sm.lsites[ci][lane] : sm.gsites[ci - nb][lane];
+    const int fcap = sm.cap_tab[fl];
+    const int fmin = sm.min_tab[fc];
+    bool need = __builtin_amdgcn_readlane(fv, ci) && __builtin_amdgcn_readlane(fs, ci) == ci;
+    const int c0 = __builtin_amdgcn_readlane(fc, ci);
+    const int cap = __builtin_amdgcn_readlane(fcap, ci);
+    const int cmin = __builtin_amdgcn_readlane(fmin, ci);
     const int dmax = cap < KMAX ? cap : KMAX;
     if (need && a.mode == 0) {
       if (ci != 0 && ci != nb) {
         need = false;
-      } else {
-        bool known = true;  // both lengths written
-        if (gwait) {
-          if (ci == nb) {
-            wait_flag(&sm.lready, lane, a.err);
-          } else {
-            known = __hip_atomic_load(&sm.gready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-          }
-        }
-        if (known) {
-          const bool lv = sm.cand_valid[0], gv = sm.cand_valid[nb];
-          const bool local_wins = lv && (!gv || sm.cand_len[0] >= sm.cand_len[nb]);
-          need = (ci == 0) == local_wins;
-        }
+      } else if (known) {
+        const bool lv = __builtin_amdgcn_readlane(fv, 0), gv = __builtin_amdgcn_readlane(fv, nb);
+        const bool local_wins = lv && (!gv || __builtin_amdgcn_readlane(fl, 0) >=
+                                                  __builtin_amdgcn_readlane(fl, nb));
+        need = (ci == 0) == local_wins;
       }
     } else if (need && outscored(sm, ci, nb, dmax, 1, lane)) {
       need = false;
@@ -1868,14 +2014,6 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       }
     } else {
       int* hk = vote_all + wid * (2 * kVoteSlots);
-      int w0[KMAX], w1[KMAX];
-      int len0 = 0, len1 = 0;
-      if (ci < nb)
-        local_windows<KMAX, STAGED>(sm, ctxs, row, smp, n, L, ci, c0, cap, lane, w0, w1, &len0,
-                                    &len1);
-      else
-        corpus_windows<KMAX>(a, r, sm.gsites[ci - nb], c0, cap, lane, w0, w1, &len0, &len1);
-      PHASE(6);
       int nout = 0, snum = 0;
 #if SFX_PHASE_TRACE
       unsigned long long* vts = a.trace ? sm.ts[wid] : nullptr;
@@ -1884,9 +2022,67 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
 #endif
       // (scored mode) whether a final score beats every score this vote can still reach
       auto beaten = [&](int bnum) { return a.mode == 1 && outscored(sm, ci, nb, bnum, c0, lane); };
-      const int cmin = sm.min_tab[c0];
-      const bool fin = vote_run<KMAX>(w0, w1, len0, c0, cap, cmin, hk, hk + kVoteSlots, lane,
-                                      beaten, sm.cand_out[ci], &nout, &snum, vts);
+      const bool loc = ci < nb;
+      // few sites (and, for a corpus candidate, all of them in the snapshot text): columns
+      const int32_t* text = r.act == 0 ? a.idx[0].text : (r.act == 1 ? a.idx[1].text : nullptr);
+      const int sv = lane < c0 ? sv_all : 0;
+      bool cols = c0 <= kColSites;
+      if (cols && !loc) {
+        const long long o = r.tail_w + sv - r.snap_start;
+        cols = text != nullptr && __ballot(lane < c0 && (o < 0 || o >= r.snap_n)) == 0;
+      }
+      bool fin;
+      if (cols) {
+        // lane s: site s's first position (local) or text offset (corpus, < 2^30), and the
+        // depths it can reach before the context or the text ends (the text's last token is a
+        // separator: depths past it read that one)
+        int lim;
+        if (loc) {
+          lim = L - sv;
+        } else {
+          const int o = (int)(r.tail_w + sv - r.snap_start);
+          lim = lane < c0 ? (int)r.snap_n - 1 - o : 0;
+        }
+        const int so = loc ? sv : (int)(r.tail_w + sv - r.snap_start);
+        auto at = [&](int si, int i) {
+          const int p = __builtin_amdgcn_readlane(so, si);
+          const int lm = __builtin_amdgcn_readlane(lim, si);
+          if (!loc) return text[p + (i < lm ? i : lm)];
+          int v;
+          if (STAGED) {
+            v = ctxs[p + i];  // p + i < L + 64: inside the stage
+          } else {
+            const int xc = i < lm ? p + i : L - 1;
+            v = *(xc < n ? row + xc : smp + (xc - n));
+          }
+          return i < lm ? v : -1;
+        };
+        // the site loops are unrolled: instantiated for 1, 2, 4 and 8 sites
+        auto run = [&](auto csc) {
+          constexpr int CS = decltype(csc)::value;
+          int T[CS], len[CS];
+          columns_cut<CS>(T, len, c0, dmax, lane, at);
+          PHASE(6);
+          return vote_columns<CS>(T, len, c0, dmax, cmin, hk, hk + kVoteSlots, lane, beaten,
+                                  sm.cand_out[ci], &nout, &snum);
+        };
+        static_assert(kColSites == 8, "column instantiations");
+        if (c0 <= 1) fin = run(std::integral_constant<int, 1>{});
+        else if (c0 <= 2) fin = run(std::integral_constant<int, 2>{});
+        else if (c0 <= 4) fin = run(std::integral_constant<int, 4>{});
+        else fin = run(std::integral_constant<int, 8>{});
+      } else {
+        int w0[KMAX], w1[KMAX];
+        int len0 = 0, len1 = 0;
+        if (loc)
+          local_windows<KMAX, STAGED>(sm, ctxs, row, smp, n, L, ci, c0, cap, lane, w0, w1, &len0,
+                                      &len1);
+        else
+          corpus_windows<KMAX>(a, r, sm.gsites[ci - nb], c0, cap, lane, w0, w1, &len0, &len1);
+        PHASE(6);
+        fin = vote_run<KMAX>(w0, w1, len0, c0, cap, cmin, hk, hk + kVoteSlots, lane, beaten,
+                             sm.cand_out[ci], &nout, &snum, vts);
+      }
       if (lane == 0) {
         sm.cand_n[ci] = nout;
         sm.cand_snum[ci] = snum;
