@@ -316,8 +316,10 @@ int sfx_debug_fail_next_rebuild(sfx_ctx* ctx);
 /* Suffix array (suffix-gpu page, Highlights and References: Manber & Myers prefix doubling):
  * sa[r] = start of the r-th smallest suffix of text[0:n], tokens compared as signed int32, a
  * proper prefix before the longer suffix.  text and sa are device arrays; workspace is a
- * device buffer of at least sfx_suffix_array_workspace_bytes(n) bytes.  The host waits for
- * `stream` once per doubling round.  n at most 2^30. */
+ * device buffer of at least sfx_suffix_array_workspace_bytes(n) bytes.  The doubling rounds
+ * count the suffixes left to sort on the device; the host reads those counts two rounds late
+ * through pinned memory, with no wait per round, and stops enqueueing once one is 0.  Returns
+ * after `stream` has finished the build.  n at most 2^30. */
 size_t sfx_suffix_array_workspace_bytes(int64_t n);
 int sfx_build_suffix_array(const int32_t* text, int64_t n, int32_t* sa, void* workspace,
                            size_t workspace_bytes, void* stream);

@@ -25,12 +25,22 @@ namespace {
 
 constexpr int RS_T = 256;              // threads per radix tile
 constexpr int RS_I = 16;               // items per thread
-constexpr int RS_TILE = RS_T * RS_I;   // 4096 keys per tile
+static_assert(RS_T * RS_I == kSaRadixTile, "radix tile");
 constexpr int SC_T = 1024;             // scan block
 constexpr int SC_I = 4;
-constexpr int SC_TILE = SC_T * SC_I;
+static_assert(SC_T * SC_I == kSaScanTile, "scan tile");
+constexpr int RS_TILE = kSaRadixTile;  // 4096 keys per tile
+constexpr int SC_TILE = kSaScanTile;
 
-inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+constexpr int64_t cdiv(int64_t a, int64_t b) { return sa_cdiv(a, b); }
+
+// Element count of a launch: the static bound m, or, when the count lives on the device (mp),
+// the smaller of the two.  Grids are sized for the bound; threads past the count do nothing.
+__device__ __forceinline__ int64_t dyn_count(int64_t m, const int32_t* mp) {
+  if (!mp) return m;
+  const int64_t d = *mp;
+  return d < m ? d : m;
+}
 
 // ------------------------------------------------------------------ generic int32 scans
 // Three phases: per-tile reduction, scan of tile totals, per-tile apply.  Op: 0 sum, 1 max.
@@ -65,8 +75,9 @@ __device__ int block_scan_incl(int v, int* wbuf) {
 
 template <int OP>
 __global__ __launch_bounds__(SC_T) void scan_reduce_kernel(const int32_t* in, int64_t m,
-                                                           int32_t* tile_tot) {
+                                                           const int32_t* mp, int32_t* tile_tot) {
   __shared__ int wbuf[SC_T / 64];
+  m = dyn_count(m, mp);
   const int64_t base = (int64_t)blockIdx.x * SC_TILE + (int64_t)threadIdx.x * SC_I;
   int acc = OP == 0 ? 0 : INT32_MIN;
   for (int u = 0; u < SC_I; ++u)
@@ -102,10 +113,12 @@ __global__ __launch_bounds__(SC_T) void scan_tiles_kernel(int32_t* tile_tot, int
 // Inclusive (INCL=1) or exclusive scan of `in` into `out` with the tile prefixes.
 template <int OP, int INCL>
 __global__ __launch_bounds__(SC_T) void scan_apply_kernel(const int32_t* in, int32_t* out,
-                                                          int64_t m, const int32_t* tile_pre) {
+                                                          int64_t m, const int32_t* mp,
+                                                          const int32_t* tile_pre) {
   __shared__ int wbuf[SC_T / 64];
   __shared__ int incl_buf[SC_T];
   constexpr int ID = OP == 0 ? 0 : INT32_MIN;
+  m = dyn_count(m, mp);
   const int64_t base = (int64_t)blockIdx.x * SC_TILE + (int64_t)threadIdx.x * SC_I;
   int v[SC_I];
   int acc = ID;
@@ -127,21 +140,26 @@ __global__ __launch_bounds__(SC_T) void scan_apply_kernel(const int32_t* in, int
   }
 }
 
+// Scan of in[0, m) into out; with mp, of in[0, min(m, *mp)) (m the bound the grids are sized
+// for).
 template <int OP, int INCL>
-hipError_t scan_i32(const int32_t* in, int32_t* out, int64_t m, int32_t* tmp, hipStream_t st) {
+hipError_t scan_i32(const int32_t* in, int32_t* out, int64_t m, int32_t* tmp, hipStream_t st,
+                    const int32_t* mp = nullptr) {
   if (m <= 0) return hipSuccess;
   const int64_t nt = cdiv(m, SC_TILE);
-  hipLaunchKernelGGL((scan_reduce_kernel<OP>), dim3(nt), dim3(SC_T), 0, st, in, m, tmp);
+  hipLaunchKernelGGL((scan_reduce_kernel<OP>), dim3(nt), dim3(SC_T), 0, st, in, m, mp, tmp);
   hipLaunchKernelGGL((scan_tiles_kernel<OP>), dim3(1), dim3(SC_T), 0, st, tmp, nt);
-  hipLaunchKernelGGL((scan_apply_kernel<OP, INCL>), dim3(nt), dim3(SC_T), 0, st, in, out, m, tmp);
+  hipLaunchKernelGGL((scan_apply_kernel<OP, INCL>), dim3(nt), dim3(SC_T), 0, st, in, out, m, mp,
+                     tmp);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ stable LSD radix sort
 template <typename K>
-__global__ __launch_bounds__(RS_T) void rs_hist_kernel(const K* keys, int64_t n, int shift,
-                                                       int32_t* hist, int64_t ntiles) {
+__global__ __launch_bounds__(RS_T) void rs_hist_kernel(const K* keys, int64_t n, const int32_t* mp,
+                                                       int shift, int32_t* hist, int64_t ntiles) {
   __shared__ int h[256];
+  n = dyn_count(n, mp);
   h[threadIdx.x] = 0;
   __syncthreads();
   const int64_t base = (int64_t)blockIdx.x * RS_TILE;
@@ -157,9 +175,11 @@ __global__ __launch_bounds__(RS_T) void rs_hist_kernel(const K* keys, int64_t n,
 template <typename K>
 __global__ __launch_bounds__(RS_T) void rs_scatter_kernel(const K* kin, const int32_t* vin,
                                                           K* kout, int32_t* vout, int64_t n,
-                                                          int shift, const int32_t* offs,
-                                                          int64_t ntiles) {
+                                                          const int32_t* mp, int shift,
+                                                          const int32_t* offs, int64_t ntiles) {
   __shared__ int run[256];
+  n = dyn_count(n, mp);
+  if ((int64_t)blockIdx.x * RS_TILE >= n) return;  // (the whole block: every key past the count)
   __shared__ int gbase[256];
   __shared__ int wcnt[RS_T / 64][256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -210,23 +230,27 @@ __global__ __launch_bounds__(RS_T) void rs_scatter_kernel(const K* kin, const in
 }
 
 // Sorts (k[0..n), v[0..n)) by the key bits [0, bits) stably; the result ends in buffer
-// `*which` (0: k0/v0, 1: k1/v1).
+// `*which` (0: k0/v0, 1: k1/v1).  With mp the count is min(n, *mp), read on the device (n
+// sizes the grids; the passes run whatever the count, so *which does not depend on it).
 template <typename K>
 hipError_t radix_sort(K* k0, int32_t* v0, K* k1, int32_t* v1, int64_t n, int bits,
-                      int32_t* hist, int32_t* tmp, int* which, hipStream_t st) {
+                      int32_t* hist, int32_t* tmp, int* which, hipStream_t st,
+                      const int32_t* mp = nullptr) {
   *which = 0;
-  if (n <= 1) return hipSuccess;
+  if (n <= 1 && !mp) return hipSuccess;
+  if (n <= 0) return hipSuccess;
   const int64_t nt = cdiv(n, RS_TILE);
   K* ka = k0;
   int32_t* va = v0;
   K* kb = k1;
   int32_t* vb = v1;
   for (int shift = 0; shift < bits; shift += 8) {
-    hipLaunchKernelGGL((rs_hist_kernel<K>), dim3(nt), dim3(RS_T), 0, st, ka, n, shift, hist, nt);
+    hipLaunchKernelGGL((rs_hist_kernel<K>), dim3(nt), dim3(RS_T), 0, st, ka, n, mp, shift, hist,
+                       nt);
     hipError_t e = scan_i32<0, 0>(hist, hist, 256 * nt, tmp, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((rs_scatter_kernel<K>), dim3(nt), dim3(RS_T), 0, st, ka, va, kb, vb, n,
-                       shift, hist, nt);
+                       mp, shift, hist, nt);
     std::swap(ka, kb);
     std::swap(va, vb);
     *which ^= 1;
@@ -266,12 +290,23 @@ __global__ __launch_bounds__(256) void minmax_kernel(const int32_t* text, int64_
   }
 }
 
-__global__ void init_keys_kernel(const int32_t* text, int64_t n, int32_t tmin, uint64_t* k,
+// First keys: the tokens minus the smallest one (mm[0], found on the device), as 32-bit keys.
+__global__ void init_keys_kernel(const int32_t* text, int64_t n, const int32_t* mm, uint64_t* k,
                                  int32_t* v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  k[i] = (uint64_t)(uint32_t)((int64_t)text[i] - tmin);
+  k[i] = (uint64_t)(uint32_t)((int64_t)text[i] - mm[0]);
   v[i] = (int32_t)i;
+}
+
+// mm[0], mm[1]: the token range to find; gate: open (a round runs) until a round finds no
+// suffix left to sort.
+__global__ void minmax_init_kernel(int32_t* mm, int32_t* gate) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    mm[0] = INT32_MAX;
+    mm[1] = INT32_MIN;
+    *gate = INT32_MAX;
+  }
 }
 
 // head[j] = j+1 if key[j] differs from key[j-1] (or j == 0), else 0; any equal neighbour
@@ -293,21 +328,29 @@ __global__ void rank_kernel(const int32_t* v, const int32_t* headmax, int64_t n,
 }
 
 // cnt[j] = 1 when position j's group has two or more members (heads: nonzero at group starts).
-__global__ void active_flags_kernel(const int32_t* head, int64_t n, int32_t* cnt) {
+// Nothing once the gate is shut.
+__global__ void active_flags_kernel(const int32_t* head, int64_t n, const int32_t* gate,
+                                    int32_t* cnt) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= n) return;
+  if (j >= dyn_count(n, gate)) return;
   const bool single = head[j] != 0 && (j + 1 == n || head[j + 1] != 0);
   cnt[j] = single ? 0 : 1;
 }
 
 // incl[j]: active positions in [0, j].  The t-th active position gets its suffix i, the key
-// (rank[i] << bits) | rank[i + h] (0 past the end), and its position.
+// (rank[i] << bits) | rank[i + h] (0 past the end), and its position.  The number of active
+// positions goes to *m (the round's sort size, read by the round's other kernels), and the
+// gate shuts when it is 0.  Nothing once the gate is shut (*m is 0 by then).
 __global__ void gather_active_kernel(const int32_t* incl, const int32_t* sa, const int32_t* rank,
                                      int64_t n, int64_t h, int bits, int32_t* act, uint64_t* k,
-                                     int32_t* v) {
+                                     int32_t* v, int32_t* m, int32_t* gate) {
   const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= n) return;
+  if (j >= n || *gate == 0) return;
   const int c = incl[j];
+  if (j == n - 1) {
+    *m = c;
+    if (c == 0) *gate = 0;
+  }
   if (c == (j ? incl[j - 1] : 0)) return;  // not active
   const int t = c - 1;
   const int64_t i = sa[j];
@@ -321,9 +364,10 @@ __global__ void gather_active_kernel(const int32_t* incl, const int32_t* sa, con
 // The sorted active suffixes back into their positions; a new group starts wherever the key
 // changes, and hv[t] = position + 1 at a start (else 0) for the max scan that ranks them.
 __global__ void scatter_back_kernel(const int32_t* act, const uint64_t* k, const int32_t* v,
-                                    int64_t m, int32_t* sa, int32_t* head, int32_t* hv) {
+                                    int64_t m, const int32_t* mp, int32_t* sa, int32_t* head,
+                                    int32_t* hv) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= m) return;
+  if (t >= dyn_count(m, mp)) return;
   const int32_t p = act[t];
   sa[p] = v[t];
   const bool start = t == 0 || k[t] != k[t - 1];
@@ -331,9 +375,10 @@ __global__ void scatter_back_kernel(const int32_t* act, const uint64_t* k, const
   hv[t] = start ? p + 1 : 0;
 }
 
-__global__ void rerank_kernel(const int32_t* v, const int32_t* hmax, int64_t m, int32_t* rank) {
+__global__ void rerank_kernel(const int32_t* v, const int32_t* hmax, int64_t m, const int32_t* mp,
+                              int32_t* rank) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < m) rank[v[t]] = hmax[t];
+  if (t < dyn_count(m, mp)) rank[v[t]] = hmax[t];
 }
 
 __global__ void copy_i32_kernel(const int32_t* a, int32_t* b, int64_t n) {
@@ -350,19 +395,7 @@ inline int bits_for(uint64_t maxv) {
 }  // namespace
 
 // ------------------------------------------------------------------ workspace
-size_t sa_workspace_bytes(int64_t n) {
-  const int64_t nn = n < 1 ? 1 : n;
-  const int64_t nt = cdiv(nn, RS_TILE);
-  size_t b = 0;
-  b += 2 * sizeof(uint64_t) * (size_t)nn;        // k0, k1
-  b += 2 * sizeof(int32_t) * (size_t)nn;         // v0, v1
-  b += 4 * sizeof(int32_t) * (size_t)nn;         // rank, head, aux, act
-  b += sizeof(int32_t) * (size_t)(256 * nt + 64);  // hist
-  b += sizeof(int32_t) * (size_t)(cdiv(256 * nt + nn, SC_TILE) + 64);  // scan tiles
-  b += 256;                                      // counters
-  b += 16 * 256;                                 // alignment slack
-  return b;
-}
+size_t sa_workspace_bytes(int64_t n) { return sa_ws_bytes(n); }
 
 SaWork sa_carve(void* ws, int64_t n) {
   const int64_t nn = n < 1 ? 1 : n;
@@ -390,26 +423,21 @@ SaWork sa_carve(void* ws, int64_t n) {
 }
 
 hipError_t sa_build(const int32_t* text, int64_t n, int32_t* sa, const SaWork& w, hipStream_t st,
-                    int* rounds_out) {
+                    const SaPoll* poll, int* rounds_out) {
   if (rounds_out) *rounds_out = 0;
   if (n <= 0) return hipSuccess;
   const int TB = 256;
   const int64_t gb = cdiv(n, TB);
-  // token range -> bits of the first sort
-  int32_t mm_init[2] = {INT32_MAX, INT32_MIN};
-  hipError_t e = hipMemcpyAsync(w.counters, mm_init, sizeof(mm_init), hipMemcpyHostToDevice, st);
-  if (e != hipSuccess) return e;
+  int32_t* mm = (int32_t*)w.counters;       // token range
+  int32_t* mdev = (int32_t*)w.counters + 4;  // the current round's sort size
+  int32_t* gate = (int32_t*)w.counters + 5;  // INT32_MAX while rounds run, then 0
+  // first sort: by token, on 32-bit keys relative to the smallest token (found on the device)
+  hipLaunchKernelGGL(minmax_init_kernel, dim3(1), dim3(64), 0, st, mm, gate);
   hipLaunchKernelGGL(minmax_kernel, dim3((unsigned)std::min<int64_t>(gb, 256)), dim3(TB), 0, st,
-                     text, n, (int32_t*)w.counters);
-  int32_t mm[2];
-  if ((e = hipMemcpyAsync(mm, w.counters, sizeof(mm), hipMemcpyDeviceToHost, st)) != hipSuccess)
-    return e;
-  if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(init_keys_kernel, dim3(gb), dim3(TB), 0, st, text, n, mm[0], w.k0, w.v0);
+                     text, n, mm);
+  hipLaunchKernelGGL(init_keys_kernel, dim3(gb), dim3(TB), 0, st, text, n, mm, w.k0, w.v0);
   int which = 0;
-  e = radix_sort<uint64_t>(w.k0, w.v0, w.k1, w.v1, n,
-                           bits_for((uint64_t)((int64_t)mm[1] - mm[0])), w.hist, w.tiles, &which,
-                           st);
+  hipError_t e = radix_sort<uint64_t>(w.k0, w.v0, w.k1, w.v1, n, 32, w.hist, w.tiles, &which, st);
   if (e != hipSuccess) return e;
   uint64_t* kc = which ? w.k1 : w.k0;
   int32_t* vc = which ? w.v1 : w.v0;
@@ -418,32 +446,48 @@ hipError_t sa_build(const int32_t* text, int64_t n, int32_t* sa, const SaWork& w
   hipLaunchKernelGGL(heads_kernel, dim3(gb), dim3(TB), 0, st, kc, n, w.head, w.counters + 8);
   if ((e = scan_i32<1, 1>(w.head, w.aux, n, w.tiles, st)) != hipSuccess) return e;
   hipLaunchKernelGGL(rank_kernel, dim3(gb), dim3(TB), 0, st, vc, w.aux, n, w.rank);
+  // Doubling rounds h = 1, 2, 4, ... < n.  Each sorts the suffixes still sharing a rank; how
+  // many there are is counted on the device and read there by the round's kernels, so a round
+  // after convergence does nothing.  Without a poll every round is enqueued; with one, the
+  // host reads each round's count through pinned memory kPollLag rounds late (the device is
+  // still busy with the rounds in between) and stops enqueueing once a count is 0.
   const int rbits = bits_for((uint64_t)n);
-  int rounds = 1;
-  for (int64_t h = 1;; h *= 2) {
-    // the suffixes still sharing a rank, and how many
-    hipLaunchKernelGGL(active_flags_kernel, dim3(gb), dim3(TB), 0, st, w.head, n, w.aux);
-    if ((e = scan_i32<0, 1>(w.aux, w.aux, n, w.tiles, st)) != hipSuccess) return e;
-    int32_t m = 0;
-    if ((e = hipMemcpyAsync(&m, w.aux + (n - 1), sizeof(m), hipMemcpyDeviceToHost, st)) !=
-        hipSuccess)
-      return e;
-    if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
-    if (m == 0 || h >= n) break;
+  int rounds = 1, r = 0;
+  bool known_done = false;
+  for (int64_t h = 1; h < n && !known_done; h *= 2, ++r) {
+    hipLaunchKernelGGL(active_flags_kernel, dim3(gb), dim3(TB), 0, st, w.head, n, gate, w.aux);
+    if ((e = scan_i32<0, 1>(w.aux, w.aux, n, w.tiles, st, gate)) != hipSuccess) return e;
     hipLaunchKernelGGL(gather_active_kernel, dim3(gb), dim3(TB), 0, st, w.aux, sa, w.rank, n, h,
-                       rbits, w.act, w.k0, w.v0);
-    e = radix_sort<uint64_t>(w.k0, w.v0, w.k1, w.v1, m, 2 * rbits, w.hist, w.tiles, &which, st);
+                       rbits, w.act, w.k0, w.v0, mdev, gate);
+    e = radix_sort<uint64_t>(w.k0, w.v0, w.k1, w.v1, n, 2 * rbits, w.hist, w.tiles, &which, st,
+                             mdev);
     if (e != hipSuccess) return e;
     const uint64_t* ks = which ? w.k1 : w.k0;
     const int32_t* vs = which ? w.v1 : w.v0;
-    const int64_t gm = cdiv(m, TB);
-    hipLaunchKernelGGL(scatter_back_kernel, dim3(gm), dim3(TB), 0, st, w.act, ks, vs, m, sa,
+    hipLaunchKernelGGL(scatter_back_kernel, dim3(gb), dim3(TB), 0, st, w.act, ks, vs, n, mdev, sa,
                        w.head, w.aux);
-    if ((e = scan_i32<1, 1>(w.aux, w.aux, m, w.tiles, st)) != hipSuccess) return e;
-    hipLaunchKernelGGL(rerank_kernel, dim3(gm), dim3(TB), 0, st, vs, w.aux, m, w.rank);
-    ++rounds;
+    if ((e = scan_i32<1, 1>(w.aux, w.aux, n, w.tiles, st, mdev)) != hipSuccess) return e;
+    hipLaunchKernelGGL(rerank_kernel, dim3(gb), dim3(TB), 0, st, vs, w.aux, n, mdev, w.rank);
+    if (poll && r < kPollRounds) {
+      if ((e = hipMemcpyAsync(poll->counts + r, mdev, sizeof(int32_t), hipMemcpyDeviceToHost,
+                              st)) != hipSuccess)
+        return e;
+      if ((e = hipEventRecord(poll->ev[r], st)) != hipSuccess) return e;
+      if (r >= kPollLag) {
+        if ((e = hipEventSynchronize(poll->ev[r - kPollLag])) != hipSuccess) return e;
+        known_done = poll->counts[r - kPollLag] == 0;
+      }
+    }
   }
-  if (rounds_out) *rounds_out = rounds;
+  if (rounds_out) {
+    // the rounds that sorted something, plus the first sort (one more wait, at the end)
+    if (poll) {
+      const int last = r < kPollRounds ? r : kPollRounds;
+      if (last > 0 && (e = hipEventSynchronize(poll->ev[last - 1])) != hipSuccess) return e;
+      for (int i = 0; i < last && poll->counts[i] > 0; ++i) ++rounds;
+    }
+    *rounds_out = rounds;
+  }
   return hipGetLastError();
 }
 

@@ -83,6 +83,7 @@ struct sfx_ctx {
   void* sa_ws = nullptr;
   size_t sa_ws_bytes = 0;
   SaWork saw{};
+  SaPoll poll{};  // pinned round counts and events of the rebuild's suffix-array rounds
   hipStream_t side = nullptr;
   hipEvent_t ev_snap = nullptr;
   hipEvent_t ev_done = nullptr;
@@ -153,6 +154,29 @@ int validate(const sfx_config* c) {
   return SFX_OK;
 }
 
+// Host side of the suffix-array round counts: pinned counts and events.
+bool alloc_poll(SaPoll* p) {
+  *p = SaPoll{};
+  if (hipHostMalloc((void**)&p->counts, sizeof(int32_t) * kPollRounds, hipHostMallocDefault) !=
+      hipSuccess) {
+    p->counts = nullptr;
+    return false;
+  }
+  for (int i = 0; i < kPollRounds; ++i)
+    if (hipEventCreateWithFlags(&p->ev[i], hipEventDisableTiming) != hipSuccess) {
+      p->ev[i] = nullptr;
+      return false;
+    }
+  return true;
+}
+
+void free_poll(SaPoll* p) {
+  for (int i = 0; i < kPollRounds; ++i)
+    if (p->ev[i]) (void)hipEventDestroy(p->ev[i]);
+  if (p->counts) (void)hipHostFree(p->counts);
+  *p = SaPoll{};
+}
+
 void free_ctx(sfx_ctx* c) {
   auto f = [](void* p) {
     if (p) (void)hipFree(p);
@@ -184,6 +208,7 @@ void free_ctx(sfx_ctx* c) {
   f(c->pair_base);
   f(c->pair_list);
   f(c->pair_pos);
+  free_poll(&c->poll);
   if (c->side) (void)hipStreamDestroy(c->side);
   if (c->ev_snap) (void)hipEventDestroy(c->ev_snap);
   if (c->ev_done) (void)hipEventDestroy(c->ev_done);
@@ -205,7 +230,7 @@ int build_index(sfx_ctx* c, int buf, hipStream_t st, uint32_t* mask_out) {
   const int64_t n = range[1] - range[0];
   if (n < 0 || n > c->cap) return fail(SFX_EHIP, "corrupt snapshot range");
   IndexBuf& b = c->idx[buf];
-  HIP_OR_RETURN(sa_build(b.text, n, b.sa, c->saw, st, nullptr), "suffix array build");
+  HIP_OR_RETURN(sa_build(b.text, n, b.sa, c->saw, st, &c->poll, nullptr), "suffix array build");
   const uint32_t slots = slots_for(c, n);
   HIP_OR_RETURN(ngram_tables_build(b.text, b.sa, n, b.pl, b.ht, slots, c->saw, st),
                 "probe table build");
@@ -410,7 +435,8 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
                   (long long)cfg->corpus_capacity);
     }
     c->saw = sa_carve(c->sa_ws, c->cap);
-    if (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
+    if (!alloc_poll(&c->poll) ||
+        hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
         hipEventCreateWithFlags(&c->ev_snap, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&c->ev_done, hipEventDisableTiming) != hipSuccess) {
       free_ctx(c);
@@ -1022,7 +1048,17 @@ int sfx_build_suffix_array(const int32_t* text, int64_t n, int32_t* sa, void* ws
     return fail(SFX_ECAPACITY, "workspace of %zu bytes, %zu needed", ws_bytes,
                 sa_workspace_bytes(n));
   SaWork w = sa_carve(ws, n);
-  HIP_OR_RETURN(sa_build(text, n, sa, w, (hipStream_t)stream, nullptr), "suffix array build");
+  SaPoll poll{};
+  if (!alloc_poll(&poll)) {
+    free_poll(&poll);
+    return fail(SFX_ENOMEM, "pinned round-count buffer");
+  }
+  const hipError_t e = sa_build(text, n, sa, w, (hipStream_t)stream, &poll, nullptr);
+  // the events and the pinned counts are freed only after the last enqueued round has read
+  // them: wait for the stream first
+  const hipError_t e2 = e == hipSuccess ? hipStreamSynchronize((hipStream_t)stream) : e;
+  free_poll(&poll);
+  HIP_OR_RETURN(e2, "suffix array build");
   return SFX_OK;
 }
 
