@@ -324,6 +324,17 @@ size_t sfx_suffix_array_workspace_bytes(int64_t n);
 int sfx_build_suffix_array(const int32_t* text, int64_t n, int32_t* sa, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate (code under graph capture, tight serving loops, harnesses
+ * that forbid allocation): sfx_build_suffix_array without a workspace argument and without
+ * any allocation.  Same result in sa.  Its workspace is a device array held by the library on
+ * each device it runs on, until the process ends: n is at most 2^20 (SFX_ECAPACITY above
+ * that), for about 40 MiB per device.  It calls no allocator, creates no event, uses no host
+ * memory and does not wait: every doubling round is enqueued on `stream` (the rounds after
+ * convergence do nothing) and the call returns; sa is ready once `stream` reaches that point.
+ * Every call on one device shares that array, so calls that overlap on one device (on
+ * different streams, or from several threads) race: order them, for example on one stream. */
+int sfx_build_suffix_array_noalloc(const int32_t* text, int64_t n, int32_t* sa, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,8 @@ EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_pr
            "sfx_accept_estimate", "sfx_accept_feedback", "sfx_accept_reset", "sfx_accept_counts",
            "sfx_corpus_snapshot", "sfx_save", "sfx_load", "sfx_debug_errors",
            "sfx_debug_fail_next_rebuild",
-           "sfx_suffix_array_workspace_bytes", "sfx_build_suffix_array")
+           "sfx_suffix_array_workspace_bytes", "sfx_build_suffix_array",
+           "sfx_build_suffix_array_noalloc")
 
 
 FLAG_STREAM_CONTEXT = 1  # read contexts from device memory instead of staging them in LDS
@@ -135,6 +136,7 @@ def load(path: str = LIB_PATH):
         "sfx_debug_fail_next_rebuild": (ctypes.c_int, [_V]),
         "sfx_suffix_array_workspace_bytes": (ctypes.c_size_t, [_I64]),
         "sfx_build_suffix_array": (ctypes.c_int, [_V, _I64, _V, _V, ctypes.c_size_t, _V]),
+        "sfx_build_suffix_array_noalloc": (ctypes.c_int, [_V, _I64, _V, _V]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -368,6 +370,19 @@ def update_state(token_ids, num_tokens, sampled, num_tokens_out=None, stream=Non
     _check(load().sfx_update_state(B, S, samp.shape[1], _ptr(tok), _ptr(nt), _ptr(samp),
                                    _ptr(num_tokens_out), _stream(stream)))
     return num_tokens_out
+
+
+NOALLOC_MAX_TOKENS = 1 << 20  # largest text of build_suffix_array_noalloc
+
+
+def build_suffix_array_noalloc(text: torch.Tensor, sa: torch.Tensor, stream=None) -> None:
+    """sfx_build_suffix_array_noalloc: the suffix array of text into the caller's sa (same
+    length), with no allocation; sa is ready once `stream` reaches the call."""
+    t = _i32(text, "text", 1)
+    out = _i32(sa, "sa", 1)
+    if out.shape[0] != t.shape[0]:
+        raise ValueError("sa must have text's length")
+    _check(load().sfx_build_suffix_array_noalloc(_ptr(t), t.shape[0], _ptr(out), _stream(stream)))
 
 
 def build_suffix_array(text: torch.Tensor, stream=None) -> torch.Tensor:

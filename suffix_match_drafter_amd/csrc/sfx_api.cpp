@@ -20,6 +20,7 @@
 #include "call_forms.h"
 #include "checks.h"
 #include "delta_index.h"
+#include "noalloc.h"
 #include "propose.h"
 #include "sa_build.h"
 
@@ -1059,6 +1060,23 @@ int sfx_build_suffix_array(const int32_t* text, int64_t n, int32_t* sa, void* ws
   const hipError_t e2 = e == hipSuccess ? hipStreamSynchronize((hipStream_t)stream) : e;
   free_poll(&poll);
   HIP_OR_RETURN(e2, "suffix array build");
+  return SFX_OK;
+}
+
+int sfx_build_suffix_array_noalloc(const int32_t* text, int64_t n, int32_t* sa, void* stream) {
+  if (n < 0 || n > kNoAllocMaxTokens)
+    return fail(SFX_ECAPACITY, "n=%lld outside [0, %lld], the allocation-free maximum",
+                (long long)n, (long long)kNoAllocMaxTokens);
+  if (n == 0) return SFX_OK;
+  if (!text || !sa) return fail(SFX_EINVAL, "NULL array argument");
+  void* ws = nullptr;
+  size_t bytes = 0;
+  HIP_OR_RETURN(noalloc_workspace(&ws, &bytes), "workspace lookup");
+  if (bytes < sa_workspace_bytes(n)) return fail(SFX_ECAPACITY, "workspace too small");
+  // no poll: every doubling round is enqueued (rounds after convergence do nothing), with no
+  // host memory, event or wait
+  HIP_OR_RETURN(sa_build(text, n, sa, sa_carve(ws, n), (hipStream_t)stream, nullptr, nullptr),
+                "suffix array build");
   return SFX_OK;
 }
 
