@@ -303,6 +303,16 @@ int sfx_load(sfx_ctx* ctx, const char* path, void* stream);
  * created with SFX_FLAG_CHECK_INPUTS; otherwise it reads 0.  Synchronises `stream`. */
 int sfx_debug_errors(sfx_ctx* ctx, uint32_t* bits_out, void* stream);
 
+/* Debug export of the live corpus index (suffix-gpu page, How it works step 4: the snapshot
+ * text and its suffix array, rebuilt on a side stream and swapped in): copies the live buffer's
+ * snapshot text into text_out and its suffix array into sa_out (device, capacity `cap` ints
+ * each) and the snapshot length into *n_out (host; 0, with nothing copied, before the first
+ * rebuild).  The snapshot is the live corpus of the rebuild that produced the index; documents
+ * evicted since then stay in it (proposes skip them).  Synchronises `stream`.  SFX_ECAPACITY if
+ * cap is too small, SFX_ESTATE without a corpus. */
+int sfx_debug_index(sfx_ctx* ctx, int32_t* text_out, int32_t* sa_out, int64_t cap,
+                    int64_t* n_out, void* stream);
+
 /* Test hook for the failure path of the rebuild (suffix-gpu page, How it works step 4: the
  * index is rebuilt on a side stream and double-buffered, so a rebuild that does not finish must
  * leave the live one in place).  The next rebuild of ctx -- sfx_rebuild, or the worker started

@@ -30,7 +30,7 @@ EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_pr
            "sfx_rebuild", "sfx_rebuild_async", "sfx_poll", "sfx_wait_rebuild",
            "sfx_accept_estimate", "sfx_accept_feedback", "sfx_accept_reset", "sfx_accept_counts",
            "sfx_corpus_snapshot", "sfx_save", "sfx_load", "sfx_debug_errors",
-           "sfx_debug_fail_next_rebuild",
+           "sfx_debug_fail_next_rebuild", "sfx_debug_index",
            "sfx_suffix_array_workspace_bytes", "sfx_build_suffix_array",
            "sfx_build_suffix_array_noalloc")
 
@@ -134,6 +134,7 @@ def load(path: str = LIB_PATH):
         "sfx_load": (ctypes.c_int, [_V, ctypes.c_char_p, _V]),
         "sfx_debug_errors": (ctypes.c_int, [_V, ctypes.POINTER(ctypes.c_uint32), _V]),
         "sfx_debug_fail_next_rebuild": (ctypes.c_int, [_V]),
+        "sfx_debug_index": (ctypes.c_int, [_V, _V, _V, _I64, ctypes.POINTER(_I64), _V]),
         "sfx_suffix_array_workspace_bytes": (ctypes.c_size_t, [_I64]),
         "sfx_build_suffix_array": (ctypes.c_int, [_V, _I64, _V, _V, ctypes.c_size_t, _V]),
         "sfx_build_suffix_array_noalloc": (ctypes.c_int, [_V, _I64, _V, _V]),
@@ -358,6 +359,16 @@ class Drafter:
         _check(load().sfx_corpus_snapshot(self._h, _ptr(out), cap, ctypes.byref(n),
                                           _stream(stream)))
         return out[: n.value]
+
+    def debug_index(self, stream=None):
+        """sfx_debug_index: (snapshot text, suffix array) of the live corpus index."""
+        cap = max(int(self.cfg.corpus_capacity), 1)
+        text = torch.empty(cap, dtype=torch.int32, device="cuda")
+        sa = torch.empty(cap, dtype=torch.int32, device="cuda")
+        n = _I64(0)
+        _check(load().sfx_debug_index(self._h, _ptr(text), _ptr(sa), cap, ctypes.byref(n),
+                                      _stream(stream)))
+        return text[: n.value], sa[: n.value]
 
 
 def update_state(token_ids, num_tokens, sampled, num_tokens_out=None, stream=None):

@@ -853,6 +853,32 @@ int sfx_corpus_snapshot(sfx_ctx* c, int32_t* text_out, int64_t cap, int64_t* n_o
   return SFX_OK;
 }
 
+int sfx_debug_index(sfx_ctx* c, int32_t* text_out, int32_t* sa_out, int64_t cap, int64_t* n_out,
+                    void* stream) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!n_out) return fail(SFX_EINVAL, "n_out is NULL");
+  *n_out = 0;
+  if (!c->ctl) return fail(SFX_ESTATE, "context has no corpus (corpus_capacity == 0)");
+  hipStream_t st = (hipStream_t)stream;
+  Ctl h;
+  HIP_OR_RETURN(hipMemcpyAsync(&h, c->ctl, sizeof h, hipMemcpyDeviceToHost, st), "control read");
+  HIP_OR_RETURN(hipStreamSynchronize(st), "control wait");
+  if (h.active < 0) return SFX_OK;  // no live index
+  const int64_t n = h.snap_end[h.active] - h.snap_start[h.active];
+  *n_out = n;
+  if (n > cap) return fail(SFX_ECAPACITY, "live index has %lld tokens, buffers %lld",
+                           (long long)n, (long long)cap);
+  if (n > 0 && (!text_out || !sa_out)) return fail(SFX_EINVAL, "NULL array argument");
+  const IndexBuf& b = c->idx[h.active];
+  HIP_OR_RETURN(hipMemcpyAsync(text_out, b.text, 4 * (size_t)n, hipMemcpyDeviceToDevice, st),
+                "text copy");
+  HIP_OR_RETURN(hipMemcpyAsync(sa_out, b.sa, 4 * (size_t)n, hipMemcpyDeviceToDevice, st),
+                "suffix array copy");
+  HIP_OR_RETURN(hipStreamSynchronize(st), "copy wait");
+  return SFX_OK;
+}
+
 int sfx_accept_estimate(sfx_ctx* c, int32_t B, int32_t* est_ppm, void* stream) {
   int rc = check_ctx(c);
   if (rc) return rc;

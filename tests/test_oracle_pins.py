@@ -87,6 +87,18 @@ def test_golden_global(orc, case):
     assert nv[0] == case["longest_fill_k4"]["num_valid"]
 
 
+@pytest.mark.parametrize("case", GOLD["selection"], ids=lambda c: c["name"])
+def test_golden_selection(orc, case):
+    lc = orc.LiveCorpus(10**6)
+    lc.ingest([np.array(x, np.int32) for x in case["docs"]])
+    C = lc.text()
+    p = orc.make_params(**case["knobs"])
+    d, nv = orc.propose(p, np.array([case["n"]]), np.array([case["row"]], np.int32),
+                        np.array([case["sampled"]], np.int32), corpus=C if len(C) else None)
+    assert d[0].tolist() == case["expect"]["draft"]
+    assert nv[0] == case["expect"]["num_valid"]
+
+
 @pytest.mark.parametrize("case", GOLD["suffix_array"], ids=lambda c: str(c["text"]))
 def test_golden_suffix_array(orc, case):
     assert orc.suffix_array(case["text"]).tolist() == case["sa"]

@@ -69,6 +69,24 @@ def knobs_of(w):
 FLAGS = [0, 1]
 
 
+# ------------------------------------------------------------------ hand-worked selection cases
+GOLD = __import__("json").load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                                 "worked_examples.json")))
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+@pytest.mark.parametrize("case", GOLD["selection"], ids=lambda c: c["name"])
+def test_golden_selection_gpu(S, case, flags):
+    n = np.array([case["n"]], np.int32)
+    tok = np.array([case["row"]], np.int32)
+    samp = np.array([case["sampled"]], np.int32)
+    docs = [np.array(x, np.int32) for x in case["docs"]]
+    got = run_gpu(S, case["knobs"], n, tok, samp, corpus_docs=docs if docs else None,
+                  capacity=1024 if docs else 0, flags=flags)
+    assert got[0][0].tolist() == case["expect"]["draft"], case["name"]
+    assert got[1][0] == case["expect"]["num_valid"], case["name"]
+
+
 # ------------------------------------------------------------------ fuzz and edge cases
 @pytest.mark.parametrize("flags", FLAGS)
 @pytest.mark.parametrize("mode", [0, 1])
@@ -422,6 +440,10 @@ def test_config_corpus(S, cid, flags):
                               flags=flags)
     snap = d.corpus_snapshot().cpu().numpy()
     assert np.array_equal(snap, text)
+    # the live index: its snapshot text and suffix array
+    itext, isa = (x.cpu().numpy() for x in d.debug_index())
+    assert np.array_equal(itext, text)
+    assert np.array_equal(isa, O.suffix_array(itext))
     exp = O.propose(O.params_from(w.knobs()), n, tok, samp, corpus=text, num_threads=NTHREADS)
     assert_same((got_d, got_n), exp, f"config {cid}")
     assert (got_d != W.POISON).all()
@@ -471,8 +493,67 @@ def test_config_ingest_under_load(S):
     snap = d.corpus_snapshot().cpu().numpy()
     assert np.array_equal(snap, lc.text())
     assert lc.evicted() > 0, "the ring should have started evicting"
+    # after the wrap and the eviction: a rebuild of the live corpus, and its suffix array at the
+    # ring's size against the oracle's
+    d.rebuild()
+    itext, isa = (x.cpu().numpy() for x in d.debug_index())
+    assert np.array_equal(itext, lc.text())
+    assert itext.shape[0] > (3 * w.ring_capacity) // 4
+    assert np.array_equal(isa, O.suffix_array(itext))
     d.close()
     assert checks == 3
+
+
+# ------------------------------------------------------------------ large token ids
+# Ids at and above 2^24 and next to INT32_MAX: the vote's hash path then takes the count and the
+# token from two reductions (they no longer pack into one word), the first suffix-array sort
+# uses all 32 key bits, and the n-gram hash sees full-width keys.  A few frequent symbols give
+# candidates with many more than 24 alive sites and split votes.
+BIG_IDS = np.array([(1 << 24) + 7919 * i for i in range(24)] +
+                   [(1 << 30) + 104729 * i for i in range(8)] +
+                   [2**31 - 1 - i for i in range(8)], np.int64).astype(np.int32)
+
+
+def _big_rows(rng, B, Sq, nsym):
+    p = 1.0 / np.arange(1, nsym + 1) ** 0.8
+    p /= p.sum()
+    sym = rng.choice(nsym, size=(B, Sq), p=p)
+    return BIG_IDS[sym]
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+@pytest.mark.parametrize("mode", [0, 1])
+def test_large_token_ids(S, mode, flags):
+    rng = np.random.default_rng(900 + mode)
+    B, Sq = 8, 3000
+    tok = _big_rows(rng, B, Sq, 40)
+    n = rng.integers(Sq // 2, Sq, size=B).astype(np.int32)
+    samp = BIG_IDS[rng.integers(0, 40, size=(B, 1))]
+    docs = [_big_rows(rng, 1, int(rng.integers(50, 200)), 40)[0] for _ in range(300)]
+    kn = dict(k=16, max_tree_depth=24, num_backoff=1 if mode == 0 else 4, max_occurrences=128,
+              mode=mode, spec_factor_ppm=2_000_000, min_token_prob_ppm=0)
+    lc = O.LiveCorpus(10**7)
+    lc.ingest(docs)
+    exp = O.propose(O.params_from(kn), n, tok, samp, corpus=lc.text(), num_threads=NTHREADS)
+    got = run_gpu(S, kn, n, tok, samp, corpus_docs=docs, capacity=1 << 17, flags=flags)[:2]
+    assert_same(got, exp, f"large ids mode={mode} flags={flags}")
+    # without the corpus as well (local candidates only)
+    exp = O.propose(O.params_from(kn), n, tok, samp, num_threads=NTHREADS)
+    got = run_gpu(S, kn, n, tok, samp, flags=flags)[:2]
+    assert_same(got, exp, f"large ids, no corpus, mode={mode} flags={flags}")
+
+
+def test_large_token_ids_suffix_array(S):
+    rng = np.random.default_rng(77)
+    docs = [_big_rows(rng, 1, int(rng.integers(20, 400)), 40)[0] for _ in range(400)]
+    text = W.join_docs(docs)
+    sa = S.build_suffix_array(dev(text)).cpu().numpy()
+    assert np.array_equal(sa, O.suffix_array(text))
+    # the full signed range: INT32_MIN .. INT32_MAX in one text
+    wide = np.concatenate([BIG_IDS, -BIG_IDS, [np.iinfo(np.int32).min, -1, 0]]).astype(np.int32)
+    wide = rng.choice(wide, size=50000)
+    sa = S.build_suffix_array(dev(wide)).cpu().numpy()
+    assert np.array_equal(sa, O.suffix_array(wide))
 
 
 # ------------------------------------------------------------------ suffix arrays
