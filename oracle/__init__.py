@@ -1,9 +1,10 @@
 """Plain CPU oracle of the suffix-match drafter (ctypes wrapper over ``liboracle.so``).
 
-TEST INFRASTRUCTURE ONLY.  The tests, the package smoke check and the benchmark's CPU-baseline
-leg are its only users; the GPU product path never imports it.  The arithmetic lives in
-``oracle.c`` (plain C loops written from the pages' definitions) and in ``corpus.py`` (the
-live-document bookkeeping of the shared corpus).
+TEST INFRASTRUCTURE ONLY.  The tests, the package smoke check, the benchmark's CPU-baseline
+leg and ``alg_bytes.py`` (which writes the stored algorithmic bytes the benchmark reads) are its
+only users; the GPU product path never imports it.  The arithmetic lives in ``oracle.c`` (plain
+C loops written from the pages' definitions), ``alg_bytes.c`` (the instrumented word count of a
+call) and ``corpus.py`` (the live-document bookkeeping of the shared corpus).
 """
 from __future__ import annotations
 
@@ -31,7 +32,8 @@ def build(force: bool = True) -> str:
     """Compile liboracle.so with gcc (plain -O2, OpenMP only to spread rows over threads)."""
     if force or not os.path.exists(_SO):
         cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fopenmp", "-shared", "-fPIC",
-               "-o", _SO + ".tmp", os.path.join(_HERE, "oracle.c")]
+               "-o", _SO + ".tmp", os.path.join(_HERE, "oracle.c"),
+               os.path.join(_HERE, "alg_bytes.c")]
         subprocess.check_call(cmd)
         os.replace(_SO + ".tmp", _SO)
     return _SO
@@ -111,6 +113,10 @@ def lib():
                                        _I32P, _I32P, _I32P]
         L.orc_suffix_array.restype = ctypes.c_int
         L.orc_suffix_array.argtypes = [_I32P, ctypes.c_int64, _I32P]
+        L.orc_alg_words.restype = ctypes.c_int
+        L.orc_alg_words.argtypes = [ctypes.POINTER(Params), ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, _I32P, _I32P, _I32P, _I32P, ctypes.c_int64,
+                                    _I32P, _I64P, ctypes.c_int32]
         _lib = L
     return _lib
 
@@ -277,6 +283,32 @@ def update_state(token_ids, num_tokens, sampled):
     out = np.empty(B, np.int32)
     lib().orc_update_state(B, S, T, _p(tok), _p(nt), _p(samp), _p(out))
     return tok, out
+
+
+ALG_CATEGORIES = ("context", "io", "sa_probes", "interval_scans", "voted_tokens")
+
+
+def alg_words(params: Params, num_tokens, token_ids, sampled, corpus=None, sa=None,
+              num_threads=1):
+    """Words one call must touch, by category (alg_bytes.c); sa: the corpus's suffix array
+    (computed here when not given)."""
+    tok = _i32(token_ids)
+    samp = _i32(sampled)
+    nt = _i32(num_tokens)
+    B, S = tok.shape
+    T = samp.shape[1]
+    out = np.zeros(5, np.int64)
+    if corpus is not None and len(corpus):
+        C = _i32(corpus)
+        SA = _i32(sa) if sa is not None else suffix_array(C)
+        cp, N, sp = _p(C), len(C), _p(SA)
+    else:
+        cp, N, sp = None, 0, None
+    rc = lib().orc_alg_words(ctypes.byref(params), B, S, T, _p(nt), _p(tok), _p(samp), cp, N, sp,
+                             out.ctypes.data_as(_I64P), num_threads)
+    if rc != 0:
+        raise ValueError("bad arguments")
+    return dict(zip(ALG_CATEGORIES, (int(x) for x in out)))
 
 
 def suffix_array(text):

@@ -75,6 +75,14 @@ void orc_update_state(int32_t B, int32_t S, int32_t T, int32_t* token_ids,
 /* suffix array of text[0,n): starts sorted by suffix, signed compare, proper prefix first */
 int orc_suffix_array(const int32_t* text, int64_t n, int32_t* sa);
 
+/* alg_bytes.c: the words one call must touch, by category (context, per-request I/O,
+ * suffix-array probes, interval scans, voted continuation tokens); sa is the corpus's suffix
+ * array (ignored without a corpus). */
+int orc_alg_words(const orc_params* p, int32_t B, int32_t S, int32_t T,
+                  const int32_t* num_tokens_no_spec, const int32_t* token_ids,
+                  const int32_t* sampled, const int32_t* C, int64_t N, const int32_t* sa,
+                  int64_t* words_out, int32_t num_threads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -543,3 +543,83 @@ def test_tree_depth_cap(orc):
                     assert capd[0][b][:keep].tolist() == free[0][b][:keep].tolist()
                     if fill is not None:
                         assert (capd[0][b][keep:] == samp[b, 0]).all()
+
+
+# ------------------------------------------------------------------ algorithmic-byte counter
+def test_alg_words_context_and_io(orc):
+    # categories 0 and 1 in closed form; no corpus: no probe or interval words
+    rng = np.random.default_rng(41)
+    B, S, T, k = 5, 60, 2, 6
+    tok = rng.integers(0, 4, size=(B, S)).astype(np.int32)
+    n = np.array([0, 7, 60, 33, 12], np.int32)
+    samp = np.array([[1, 2], [3, -1], [-1, 5], [0, 0], [2, -1]], np.int32)
+    w = orc.alg_words(orc.make_params(k), n, tok, samp)
+    t = np.array([2, 1, 0, 2, 1])
+    assert w["context"] == int((n + t)[t > 0].sum())
+    assert w["io"] == B * (2 + T + k + 1)
+    assert w["sa_probes"] == 0 and w["interval_scans"] == 0
+
+
+def test_alg_words_single_site_votes(orc):
+    # the worked example "single earlier occurrence of the tail": one site, the continuation
+    # 1 2 4 1 2 3 has no negative id, so a k=4 longest-match vote reads one word per depth
+    case = GOLD["local"][0]
+    w = orc.alg_words(orc.make_params(4, max_tree_depth=case["D"]), np.array([case["n"]]),
+                      np.array([case["row"]], np.int32), np.array([case["sampled"]], np.int32))
+    assert w["voted_tokens"] == 4
+
+
+def test_alg_words_probe_closed_form(orc):
+    # every corpus token is smaller than the tail's tokens, and the corpus holds 2^5 - 1 tokens:
+    # each lower-bound search halves [0, N) five times, always to the right, reading one
+    # suffix-array word and one token per step; the upper bound then starts at N (no step)
+    N = 31
+    C = np.array([i % 3 for i in range(N - 1)] + [-1], np.int32)
+    row = np.array([[7, 8, 9, 7, 8, 9]], np.int32)
+    for D, L_tail in ((24, 7), (4, 4), (2, 2)):
+        w = orc.alg_words(orc.make_params(3, max_tree_depth=D), np.array([6]), row,
+                          np.array([[9]], np.int32), corpus=C)
+        lengths = len(range(2, min(D, 7) + 1))
+        assert w["sa_probes"] == lengths * 5 * 2, (D, w)
+        assert w["interval_scans"] == 0
+
+
+def test_alg_words_interval_is_occurrence_count(orc):
+    # the interval scanned for the corpus candidate holds every occurrence of its g-gram (the
+    # suffixes starting with it), counted here by direct substring comparison
+    rng = np.random.default_rng(43)
+    for it in range(60):
+        V = int(rng.choice([2, 3]))
+        C = _rand_corpus(rng, V, int(rng.integers(1, 8)), 0, 25)
+        if len(C) == 0:
+            continue
+        row = rng.integers(0, V, size=(1, 20)).astype(np.int32)
+        samp = rng.integers(0, V, size=(1, 1)).astype(np.int32)
+        p = orc.make_params(4, max_tree_depth=6)
+        w = orc.alg_words(p, np.array([20]), row, samp, corpus=C)
+        ctx, _ = orc.context(row[0], 20, samp[0])
+        m = orc.corpus_match(C, ctx, 6)
+        g = orc.kth_largest(m, 1)
+        if g < 2:
+            assert w["interval_scans"] == 0
+            continue
+        pat = ctx[len(ctx) - g:].tolist()
+        occ = sum(1 for i in range(len(C)) if C[i:i + g].tolist() == pat)
+        assert w["interval_scans"] == occ, (it, g)
+
+
+def test_alg_bytes_file_is_current(orc):
+    # the stored algorithmic bytes the benchmark reads were written by oracle/alg_bytes.py from
+    # the current oracle and generators: recompute two of its workloads' sets
+    import workloads as W
+
+    stored = json.load(open(os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle",
+                                         "alg_bytes.json")))["workloads"]
+    for cid, set_index in ((1, 0), (1, 3), (3, 0)):
+        w = W.WORKLOADS[cid]
+        C = W.join_docs(W.corpus_docs(cid)) if w.corpus else None
+        n, tok, samp = W.make_batch(cid, set_index=set_index)
+        words = orc.alg_words(orc.params_from(w.knobs()), n, tok, samp, corpus=C, num_threads=8)
+        exp = [s for s in stored[w.name]["sets"] if s["set_index"] == set_index][0]["bytes"]
+        assert {k: 4 * v for k, v in words.items()} == {k: v for k, v in exp.items()
+                                                         if k != "total"}
