@@ -31,6 +31,9 @@ KERNEL_SOURCES = ("suffix_match_drafter_amd/csrc/propose.hip",
                   "suffix_match_drafter_amd/csrc/sfx_internal.h")
 
 
+REBUILD_BYTES_PER_TOKEN_ROUND = 8 + 4 * 32 + 16
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -236,6 +239,7 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
         step_ms.append((time.time() - ts) * 1e3)
         p_live.append(timed(prop, calls))
     # the rebuild alone: synchronous, nothing else on the GPU, after one more harvest each
+    reb_rounds, reb_tokens = [], []
     for st in range(sync_reps):
         rows, lens, itok, _ = batches[warm_steps + steps + st]
         d.harvest_finished(rows, lens, itok, stream)
@@ -244,6 +248,9 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
         d.rebuild(stream)
         torch.cuda.synchronize()
         sync_ms.append((time.time() - tr) * 1e3)
+        r, ntok = d.rebuild_stats()
+        reb_rounds.append(r)
+        reb_tokens.append(ntok)
     # save and restore of the whole corpus (host file; a fresh context of the same capacity)
     import tempfile
 
@@ -287,6 +294,17 @@ def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
         "delta_extra_us": round(extra_us, 1),
         "rebuild_ms": round(float(np.median(sync_ms)), 2),
         "rebuild_tokens_per_s": round(w.ring_capacity / (float(np.median(sync_ms)) * 1e-3), 1),
+        "rebuild_snapshot_tokens": int(np.median(reb_tokens)),
+        "rebuild_rounds": int(np.median(reb_rounds)),
+        # prefix doubling's bytes per token and round: key build 8, four radix passes of key and
+        # value read and written plus their histogram 4 x 32, re-rank 16
+        "rebuild_bytes_per_round": int(np.median(reb_tokens)) * REBUILD_BYTES_PER_TOKEN_ROUND,
+        "rebuild_GBps": round(np.median(reb_rounds) * np.median(reb_tokens) *
+                              REBUILD_BYTES_PER_TOKEN_ROUND / (np.median(sync_ms) * 1e-3) / 1e9,
+                              1),
+        "rebuild_roofline_frac": round(np.median(reb_rounds) * np.median(reb_tokens) *
+                                       REBUILD_BYTES_PER_TOKEN_ROUND /
+                                       (np.median(sync_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "async_rebuild_with_proposes_ms": round(float(np.mean(reb_ms)), 2),
         "step_ms": round(float(np.mean(step_ms)), 2),
         "save_ms": round(save_ms, 1),
@@ -347,6 +365,7 @@ def main():
                      corpus_capacity=(1 << 20) if w.corpus else 0, **w.knobs())
     d = sfx.Drafter(cfg)
     rebuild_s = None
+    rebuild_rounds = None
     corpus_n = 0
     if w.corpus:
         d.ingest_docs(docs)
@@ -356,7 +375,9 @@ def main():
         torch.cuda.synchronize()
         rebuild_s = time.time() - t1
         corpus_n = int(d.corpus_snapshot().numel())
-        log(f"[bench] corpus {corpus_n} tokens indexed in {rebuild_s * 1e3:.1f} ms")
+        rebuild_rounds = d.rebuild_stats()[0]
+        log(f"[bench] corpus {corpus_n} tokens indexed in {rebuild_s * 1e3:.1f} ms, "
+            f"{rebuild_rounds} doubling rounds")
     bufs = []
     for c in range(args.copies):
         for (n, tok, samp) in sets:
@@ -491,6 +512,7 @@ def main():
                       None if not alg_exact else {k: int(v) for k, v in alg_exact.items()},
                   "algorithmic_bytes_floor": int(alg_floor),
                   "index_rebuild_ms": None if rebuild_s is None else round(rebuild_s * 1e3, 2),
+                  "index_rebuild_rounds": rebuild_rounds,
                   "index_rebuild_tokens_per_s":
                       None if not rebuild_s else round(corpus_n / rebuild_s, 1),
                   "measured_copy_GBps": round(copy_gbs, 1),

@@ -303,6 +303,13 @@ int sfx_load(sfx_ctx* ctx, const char* path, void* stream);
  * created with SFX_FLAG_CHECK_INPUTS; otherwise it reads 0.  Synchronises `stream`. */
 int sfx_debug_errors(sfx_ctx* ctx, uint32_t* bits_out, void* stream);
 
+/* Statistics of the last index build (sfx_rebuild, or an asynchronous rebuild that has
+ * finished): *rounds_out = prefix-doubling rounds of its suffix array (the first sort plus
+ * every doubling round that had suffixes left to sort), *tokens_out = its snapshot tokens.
+ * Host values; waits for the build's last round if it is still running.  SFX_ESTATE while an
+ * asynchronous rebuild is in flight or without a corpus. */
+int sfx_rebuild_stats(sfx_ctx* ctx, int32_t* rounds_out, int64_t* tokens_out);
+
 /* Debug export of the live corpus index (suffix-gpu page, How it works step 4: the snapshot
  * text and its suffix array, rebuilt on a side stream and swapped in): copies the live buffer's
  * snapshot text into text_out and its suffix array into sa_out (device, capacity `cap` ints

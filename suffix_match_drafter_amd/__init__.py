@@ -30,7 +30,7 @@ EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_pr
            "sfx_rebuild", "sfx_rebuild_async", "sfx_poll", "sfx_wait_rebuild",
            "sfx_accept_estimate", "sfx_accept_feedback", "sfx_accept_reset", "sfx_accept_counts",
            "sfx_corpus_snapshot", "sfx_save", "sfx_load", "sfx_debug_errors",
-           "sfx_debug_fail_next_rebuild", "sfx_debug_index",
+           "sfx_debug_fail_next_rebuild", "sfx_debug_index", "sfx_rebuild_stats",
            "sfx_suffix_array_workspace_bytes", "sfx_build_suffix_array",
            "sfx_build_suffix_array_noalloc")
 
@@ -135,6 +135,7 @@ def load(path: str = LIB_PATH):
         "sfx_debug_errors": (ctypes.c_int, [_V, ctypes.POINTER(ctypes.c_uint32), _V]),
         "sfx_debug_fail_next_rebuild": (ctypes.c_int, [_V]),
         "sfx_debug_index": (ctypes.c_int, [_V, _V, _V, _I64, ctypes.POINTER(_I64), _V]),
+        "sfx_rebuild_stats": (ctypes.c_int, [_V, ctypes.POINTER(_I32), ctypes.POINTER(_I64)]),
         "sfx_suffix_array_workspace_bytes": (ctypes.c_size_t, [_I64]),
         "sfx_build_suffix_array": (ctypes.c_int, [_V, _I64, _V, _V, ctypes.c_size_t, _V]),
         "sfx_build_suffix_array_noalloc": (ctypes.c_int, [_V, _I64, _V, _V]),
@@ -359,6 +360,12 @@ class Drafter:
         _check(load().sfx_corpus_snapshot(self._h, _ptr(out), cap, ctypes.byref(n),
                                           _stream(stream)))
         return out[: n.value]
+
+    def rebuild_stats(self):
+        """sfx_rebuild_stats: (doubling rounds, snapshot tokens) of the last index build."""
+        r, n = _I32(0), _I64(0)
+        _check(load().sfx_rebuild_stats(self._h, ctypes.byref(r), ctypes.byref(n)))
+        return r.value, n.value
 
     def debug_index(self, stream=None):
         """sfx_debug_index: (snapshot text, suffix array) of the live corpus index."""

@@ -47,6 +47,7 @@ constexpr int kPollLag = 2;      // rounds between a count's enqueue and its rea
 struct SaPoll {
   int32_t* counts;  // pinned host memory, kPollRounds entries
   hipEvent_t ev[kPollRounds];
+  int enqueued = 0;  // rounds of the last build whose count was enqueued (set by sa_build)
 };
 
 // Builds sa[0..n) of text[0..n) on `st`, with no host wait per round: every kernel reads the

@@ -479,6 +479,7 @@ hipError_t sa_build(const int32_t* text, int64_t n, int32_t* sa, const SaWork& w
       }
     }
   }
+  if (poll) const_cast<SaPoll*>(poll)->enqueued = r < kPollRounds ? r : kPollRounds;
   if (rounds_out) {
     // the rounds that sorted something, plus the first sort (one more wait, at the end)
     if (poll) {

@@ -85,6 +85,7 @@ struct sfx_ctx {
   size_t sa_ws_bytes = 0;
   SaWork saw{};
   SaPoll poll{};  // pinned round counts and events of the rebuild's suffix-array rounds
+  int64_t last_index_tokens = 0;  // snapshot tokens of the last index build
   hipStream_t side = nullptr;
   hipEvent_t ev_snap = nullptr;
   hipEvent_t ev_done = nullptr;
@@ -231,6 +232,7 @@ int build_index(sfx_ctx* c, int buf, hipStream_t st, uint32_t* mask_out) {
   const int64_t n = range[1] - range[0];
   if (n < 0 || n > c->cap) return fail(SFX_EHIP, "corrupt snapshot range");
   IndexBuf& b = c->idx[buf];
+  c->last_index_tokens = n;
   HIP_OR_RETURN(sa_build(b.text, n, b.sa, c->saw, st, &c->poll, nullptr), "suffix array build");
   const uint32_t slots = slots_for(c, n);
   HIP_OR_RETURN(ngram_tables_build(b.text, b.sa, n, b.pl, b.ht, slots, c->saw, st),
@@ -850,6 +852,21 @@ int sfx_corpus_snapshot(sfx_ctx* c, int32_t* text_out, int64_t cap, int64_t* n_o
   if (n > 0 && !text_out) return fail(SFX_EINVAL, "text_out is NULL");
   HIP_OR_RETURN(launch_ring_copy(c->ctl, c->ring, c->cap, text_out, cap, st), "copy launch");
   HIP_OR_RETURN(hipStreamSynchronize(st), "copy wait");
+  return SFX_OK;
+}
+
+int sfx_rebuild_stats(sfx_ctx* c, int32_t* rounds_out, int64_t* tokens_out) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!rounds_out || !tokens_out) return fail(SFX_EINVAL, "NULL output argument");
+  if (!c->ctl) return fail(SFX_ESTATE, "context has no corpus (corpus_capacity == 0)");
+  if (c->async_state.load() == 1) return fail(SFX_ESTATE, "an asynchronous rebuild is in flight");
+  const int e = c->poll.enqueued;
+  if (e > 0) HIP_OR_RETURN(hipEventSynchronize(c->poll.ev[e - 1]), "last round wait");
+  int rounds = c->last_index_tokens > 0 ? 1 : 0;
+  for (int i = 0; i < e && c->poll.counts[i] > 0; ++i) ++rounds;
+  *rounds_out = rounds;
+  *tokens_out = c->last_index_tokens;
   return SFX_OK;
 }
 

@@ -440,10 +440,17 @@ def test_config_corpus(S, cid, flags):
                               flags=flags)
     snap = d.corpus_snapshot().cpu().numpy()
     assert np.array_equal(snap, text)
-    # the live index: its snapshot text and suffix array
+    # the live index: its snapshot text and suffix array, and its doubling rounds: the first
+    # sort by one token plus one round per h = 1, 2, 4, ... up to the longest common prefix of
+    # two suffixes (lam), i.e. floor(log2(lam)) + 2
     itext, isa = (x.cpu().numpy() for x in d.debug_index())
     assert np.array_equal(itext, text)
-    assert np.array_equal(isa, O.suffix_array(itext))
+    osa = O.suffix_array(itext)
+    assert np.array_equal(isa, osa)
+    lam = _max_adjacent_lcp(itext, osa)
+    rounds, ntok = d.rebuild_stats()
+    assert ntok == len(itext)
+    assert rounds == (int(np.floor(np.log2(lam))) + 2 if lam >= 1 else 1), (rounds, lam)
     exp = O.propose(O.params_from(w.knobs()), n, tok, samp, corpus=text, num_threads=NTHREADS)
     assert_same((got_d, got_n), exp, f"config {cid}")
     assert (got_d != W.POISON).all()
@@ -452,6 +459,27 @@ def test_config_corpus(S, cid, flags):
     torch.cuda.synchronize()
     assert np.array_equal(d2.cpu().numpy(), got_d) and np.array_equal(n2.cpu().numpy(), got_n)
     d.close()
+
+
+def _max_adjacent_lcp(text, sa):
+    # longest common prefix of suffixes adjacent in suffix-array order (the longest of any two)
+    best = 0
+    t = text.astype(np.int64)
+    n = len(t)
+    a, b = sa[:-1].astype(np.int64), sa[1:].astype(np.int64)
+    lcp = np.zeros(len(a), np.int64)
+    alive = np.ones(len(a), bool)
+    k = 0
+    while alive.any():
+        ia, ib = a + k, b + k
+        ok = alive & (ia < n) & (ib < n)
+        eq = np.zeros(len(a), bool)
+        eq[ok] = t[ia[ok]] == t[ib[ok]]
+        lcp += eq
+        alive = eq
+        k += 1
+    best = int(lcp.max()) if len(lcp) else 0
+    return best
 
 
 def test_config_ingest_under_load(S):
