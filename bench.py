@@ -150,6 +150,31 @@ def graph_calls_per_s(torch, d, bufs, draft, nv, per_graph=32, replays=60):
     return per_graph / (ms * 1e-3)
 
 
+def bucketed_graph_calls_per_s(torch, d, bufs, draft, nv, B, buckets, calls=600):
+    """The library's batch-bucketed graphs (sfx_graphs_create at warm-up, sfx_graphs_propose
+    per call), one graph set per rotating buffer, over copies of the lengths and sampled ids
+    (a padded bucket empties its rows past B): calls/s at batch B, with how many calls replayed
+    a graph."""
+    stream = torch.cuda.current_stream()
+    sets = []
+    for b in bufs:
+        nt, sm = b[0].clone(), b[2].clone()
+        sets.append((d.graphs(buckets, nt, b[1], sm, draft, nv, stream=stream), nt, sm))
+    torch.cuda.synchronize()
+    k = [0]
+
+    def one():
+        sets[k[0] % len(sets)][0].propose(B, stream)
+        k[0] += 1
+
+    event_ms(torch, stream, one, 2 * len(sets))
+    ms = event_ms(torch, stream, one, calls)
+    replayed = sum(s[0].stats()["replays"] for s in sets)
+    for s in sets:
+        s[0].close()
+    return 1e3 / ms, replayed / k[0]
+
+
 def other_workloads(torch, sfx, W, dev, calls=200):
     """Workloads 1-3 (self match, self match + template corpus) in calls/s, one resident input
     set each."""
@@ -434,6 +459,13 @@ def main():
             e1.synchronize()
             lst.append(e0.elapsed_time(e1))
     graph_cps = graph_calls_per_s(torch, d, bufs, draft, nv)
+    buckets = [w.B // 4, w.B // 2, 3 * w.B // 4, w.B]
+    bucket_cps, bucket_replayed = bucketed_graph_calls_per_s(torch, d, bufs, draft, nv, w.B,
+                                                             buckets)
+    pad_b = w.B - 6
+    bucket_pad_cps, _ = bucketed_graph_calls_per_s(torch, d, bufs, draft, nv, pad_b, buckets)
+    log(f"[bench] bucketed graphs {buckets}: B={w.B} {bucket_cps:.0f} calls/s "
+        f"(replayed {bucket_replayed:.2f}), B={pad_b} padded to {w.B} {bucket_pad_cps:.0f}")
     single = 1e3 / event_ms(torch, stream, lambda: d.propose(bufs[0][0], bufs[0][1], bufs[0][2],
                                                              draft, nv, stream), 500)
     others = other_workloads(torch, sfx, W, dev)
@@ -518,6 +550,10 @@ def main():
                   "measured_copy_GBps": round(copy_gbs, 1),
                   "frac_of_measured_copy": round(achieved / copy_gbs, 4),
                   "graph_captured_calls_per_s": round(graph_cps, 1),
+                  "bucketed_graph": {"buckets": buckets, "calls_per_s": round(bucket_cps, 1),
+                                     "replayed_fraction": round(bucket_replayed, 3),
+                                     "padded_B": pad_b,
+                                     "padded_calls_per_s": round(bucket_pad_cps, 1)},
                   "single_buffer_calls_per_s": round(single, 1),
                   "workloads_calls_per_s": others,
                   "accept_estimate_us": round(float(np.mean(est_ms)) * 1e3, 2),

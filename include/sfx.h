@@ -261,6 +261,60 @@ int sfx_accept_feedback(sfx_ctx* ctx, int32_t B, const int32_t* num_accepted, vo
 int sfx_accept_reset(sfx_ctx* ctx, void* stream);
 int sfx_accept_counts(sfx_ctx* ctx, uint64_t* counts, void* stream);
 
+/* Batch-bucketed graphs of the drafter step (RFC page "[RFC]: Suffix decoding on GPU
+ * (suffix_gpu)", Design, Proposer bullet: the draft chain is captured per batch-size bucket at
+ * engine warm-up, so no serving step pays for a capture, and runs eagerly when capture fails or
+ * graphs are disabled).
+ *
+ * sfx_graphs_create captures, for every bucket size Bp of `buckets` (nbuckets entries, host
+ * array, strictly ascending, 1 <= Bp <= max_batch, at most 64 buckets), the step over the first
+ * Bp rows of the caller's persistent device buffers:
+ *   num_tokens   [max bucket]     row prefix lengths (rows past B are overwritten, see below)
+ *   token_ids    [max bucket, S]  resident rows (written only with SFX_GRAPHS_UPDATE_STATE)
+ *   sampled      [max bucket, T]  sampled ids, -1 padded (rows past B are overwritten)
+ *   draft        [max bucket, k]  out, as for sfx_propose
+ *   num_valid    [max bucket]     out, as for sfx_propose
+ *   num_tokens_out [max bucket]   out, new lengths (SFX_GRAPHS_UPDATE_STATE only, else NULL;
+ *                                 may be num_tokens itself)
+ * The chain of a bucket is sfx_propose(Bp rows), then with SFX_GRAPHS_UPDATE_STATE
+ * sfx_update_state(Bp rows).  Each bucket gets two graphs: one for B == Bp, and one that first
+ * empties rows B .. Bp-1 (num_tokens 0, sampled -1: such a row reads nothing, proposes nothing,
+ * gets draft -1 and num_valid 0, and with the update keeps its token_ids row).  Capture happens
+ * on a stream of the library's own, so `stream` is only used to upload the graphs; no kernel
+ * runs during creation.  A bucket whose capture or instantiation fails is run eagerly
+ * instead (sfx_graphs_stats reports which).  The buffers must stay allocated, and the context
+ * alive, until sfx_graphs_destroy.  The graphs read the corpus index and delta that are live
+ * when they run (swaps keep every buffer in place).
+ *
+ * sfx_graphs_propose(g, B, stream) runs the step for the first B rows: the graph of the
+ * smallest bucket >= B, replayed on `stream` (B == 0 does nothing).  With B above the largest
+ * bucket, with a bucket that was not captured, or with SFX_GRAPHS_EAGER, the same chain runs
+ * eagerly for exactly B rows (sfx_propose's errors apply).  Replays neither allocate nor wait.
+ * Not thread-safe for one object: calls on one object must be serialised by the caller. */
+enum {
+  SFX_GRAPHS_EAGER = 1,         /* capture nothing: every call runs eagerly */
+  SFX_GRAPHS_UPDATE_STATE = 2,  /* the chain ends with sfx_update_state */
+  SFX_GRAPHS_DELTA_INDEX = 4,   /* every chain groups the delta by tail pair first (as
+                                   sfx_propose does while an ingest is pending), for engines that
+                                   ingest every step; without it the replays scan the delta */
+  SFX_GRAPHS_DEBUG_BREAK_ODD = 8 /* test hook: a call that is not allowed under capture is made
+                                   inside the capture of every odd-indexed bucket, so those
+                                   captures fail and those buckets run eagerly */
+};
+typedef struct sfx_graphs sfx_graphs;
+int sfx_graphs_create(sfx_ctx* ctx, int32_t nbuckets, const int32_t* buckets, int32_t S,
+                      int32_t T, int32_t* num_tokens, int32_t* token_ids, int32_t* sampled,
+                      int32_t* draft, int32_t* num_valid, int32_t* num_tokens_out,
+                      int32_t flags, void* stream, sfx_graphs** out);
+int sfx_graphs_propose(sfx_graphs* g, int32_t B, void* stream);
+/* Bit i of *exact_mask / *padded_mask: bucket i's graph for B == Bp / B < Bp was captured.
+ * *replays and *eager_calls count the calls of sfx_graphs_propose so far.  NULL outputs are
+ * skipped. */
+int sfx_graphs_stats(sfx_graphs* g, int32_t* nbuckets, uint64_t* exact_mask,
+                     uint64_t* padded_mask, int64_t* replays, int64_t* eager_calls);
+/* Frees the graphs (not the buffers).  Work already launched may still be running. */
+void sfx_graphs_destroy(sfx_graphs* g);
+
 /* Persist the corpus (suffix-gpu page, TODO: the cross-request global memory -- corpus ring,
  * suffix array and delta -- is saved to disk and restored across sessions, so the accumulated
  * statistics survive a restart instead of being rebuilt).  Writes the host file `path`: the

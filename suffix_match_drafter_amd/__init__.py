@@ -32,12 +32,19 @@ EXPORTS = ("sfx_create", "sfx_destroy", "sfx_last_error", "sfx_propose", "sfx_pr
            "sfx_corpus_snapshot", "sfx_save", "sfx_load", "sfx_debug_errors",
            "sfx_debug_fail_next_rebuild", "sfx_debug_index", "sfx_rebuild_stats",
            "sfx_suffix_array_workspace_bytes", "sfx_build_suffix_array",
-           "sfx_build_suffix_array_noalloc")
+           "sfx_build_suffix_array_noalloc", "sfx_graphs_create", "sfx_graphs_propose",
+           "sfx_graphs_stats", "sfx_graphs_destroy")
 
 
 FLAG_STREAM_CONTEXT = 1  # read contexts from device memory instead of staging them in LDS
 FLAG_CHECK_INPUTS = 2    # check device-resident inputs into the sticky error word
 FLAG_TREE_DEPTH_CAP = 4  # match length plus draft length at most max_tree_depth
+
+# flags of a batch-bucketed graph set (include/sfx.h)
+GRAPHS_EAGER = 1             # capture nothing: every call runs eagerly
+GRAPHS_UPDATE_STATE = 2      # the chain ends with the state update
+GRAPHS_DELTA_INDEX = 4       # every chain groups the delta by tail pair first
+GRAPHS_DEBUG_BREAK_ODD = 8   # test hook: captures of odd-indexed buckets fail
 
 # bits of the sticky error word (include/sfx.h)
 ERR_LENGTH, ERR_NEGATIVE_TOKEN, ERR_SAMPLED_AFTER_PAD, ERR_ROW_INDEX = 1, 2, 4, 8
@@ -139,6 +146,14 @@ def load(path: str = LIB_PATH):
         "sfx_suffix_array_workspace_bytes": (ctypes.c_size_t, [_I64]),
         "sfx_build_suffix_array": (ctypes.c_int, [_V, _I64, _V, _V, ctypes.c_size_t, _V]),
         "sfx_build_suffix_array_noalloc": (ctypes.c_int, [_V, _I64, _V, _V]),
+        "sfx_graphs_create": (ctypes.c_int, [_V, _I32, ctypes.POINTER(_I32), _I32, _I32, _V, _V,
+                                             _V, _V, _V, _V, _I32, _V, ctypes.POINTER(_V)]),
+        "sfx_graphs_propose": (ctypes.c_int, [_V, _I32, _V]),
+        "sfx_graphs_stats": (ctypes.c_int, [_V, ctypes.POINTER(_I32),
+                                            ctypes.POINTER(ctypes.c_uint64),
+                                            ctypes.POINTER(ctypes.c_uint64),
+                                            ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+        "sfx_graphs_destroy": (None, [_V]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -246,6 +261,12 @@ class Drafter:
                                          _ptr(tok), _ptr(samp), _ptr(cnt), _ptr(draft),
                                          _ptr(num_valid), _stream(stream)))
         return draft, num_valid
+
+    def graphs(self, buckets, num_tokens, token_ids, sampled, draft, num_valid,
+               num_tokens_out=None, flags=0, stream=None) -> "GraphSet":
+        """Pre-capture the step for each batch bucket over these persistent buffers."""
+        return GraphSet(self, buckets, num_tokens, token_ids, sampled, draft, num_valid,
+                        num_tokens_out, flags, stream)
 
     def propose_with_update(self, num_tokens, token_ids, sampled, stream=None):
         draft, nv = self.propose(num_tokens, token_ids, sampled, stream=stream)
@@ -376,6 +397,60 @@ class Drafter:
         _check(load().sfx_debug_index(self._h, _ptr(text), _ptr(sa), cap, ctypes.byref(n),
                                       _stream(stream)))
         return text[: n.value], sa[: n.value]
+
+
+class GraphSet:
+    """Graphs of the drafter step captured per batch-size bucket over persistent buffers
+    (sfx_graphs_create); propose(B) replays the smallest bucket >= B with rows B.. emptied, or
+    runs eagerly where no graph was captured."""
+
+    def __init__(self, drafter, buckets, num_tokens, token_ids, sampled, draft, num_valid,
+                 num_tokens_out=None, flags=0, stream=None):
+        buckets = [int(x) for x in buckets]
+        nt = _i32(num_tokens, "num_tokens", 1)
+        tok = _i32(token_ids, "token_ids", 2)
+        smp = _i32(sampled, "sampled", 2)
+        dr = _i32(draft, "draft", 2)
+        nv = _i32(num_valid, "num_valid", 1)
+        nout = None if num_tokens_out is None else _i32(num_tokens_out, "num_tokens_out", 1)
+        rows = max(buckets) if buckets else 0
+        for name, t in (("num_tokens", nt), ("token_ids", tok), ("sampled", smp),
+                        ("draft", dr), ("num_valid", nv), ("num_tokens_out", nout)):
+            if t is not None and t.shape[0] < rows:
+                raise ValueError(f"{name} has {t.shape[0]} rows, the largest bucket {rows}")
+        if dr.shape[1] != drafter.cfg.k:
+            raise ValueError(f"draft must have k={drafter.cfg.k} columns")
+        # the buffers stay referenced while the graphs exist
+        self._keep = (drafter, nt, tok, smp, dr, nv, nout)
+        arr = (_I32 * max(len(buckets), 1))(*buckets)
+        h = _V()
+        _check(load().sfx_graphs_create(drafter._h, len(buckets), arr, tok.shape[1],
+                                        smp.shape[1], _ptr(nt), _ptr(tok), _ptr(smp), _ptr(dr),
+                                        _ptr(nv), _ptr(nout), int(flags), _stream(stream),
+                                        ctypes.byref(h)))
+        self._h = h
+
+    def propose(self, B, stream=None):
+        _check(load().sfx_graphs_propose(self._h, int(B), _stream(stream)))
+
+    def stats(self):
+        nb, em, pm = _I32(), ctypes.c_uint64(), ctypes.c_uint64()
+        rep, eag = _I64(), _I64()
+        _check(load().sfx_graphs_stats(self._h, ctypes.byref(nb), ctypes.byref(em),
+                                       ctypes.byref(pm), ctypes.byref(rep), ctypes.byref(eag)))
+        return {"buckets": nb.value, "exact_mask": em.value, "padded_mask": pm.value,
+                "replays": rep.value, "eager_calls": eag.value}
+
+    def close(self):
+        if getattr(self, "_h", None):
+            load().sfx_graphs_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def update_state(token_ids, num_tokens, sampled, num_tokens_out=None, stream=None):

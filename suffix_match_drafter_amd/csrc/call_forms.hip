@@ -41,7 +41,53 @@ __global__ void counts_prep_kernel(int B, int T, const int32_t* sampled, const i
   s_out[i] = x < c ? sampled[i] : -1;
 }
 
+// Padding of a batch bucket (RFC page, Design, Proposer: the draft chain is captured per batch
+// size bucket).  Rows [from, to) become empty rows, no prefix and no sampled id, so a step
+// captured for `to` rows reads nothing of them and proposes nothing for them.  One thread per
+// row entry: entry 0 is the length, entries 1 .. T the sampled ids.  The grid covers `to` rows,
+// the most any `from` >= 0 leaves, so only the arguments change between calls.
+__global__ void pad_rows_kernel(int32_t* ntns, int32_t* samp, int T, int from, int to) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int w = T + 1;
+  if (from < 0 || i >= (int64_t)(to - from) * w) return;
+  const int64_t r = from + i / w;
+  const int c = (int)(i % w);
+  if (c == 0)
+    ntns[r] = 0;
+  else
+    samp[r * T + c - 1] = -1;
+}
+
+constexpr int kPadThreads = 256;
+
+hipKernelNodeParams pad_params(void** args, int T, int to) {
+  hipKernelNodeParams p{};
+  const int64_t n = (int64_t)to * (T + 1);
+  p.func = reinterpret_cast<void*>(pad_rows_kernel);
+  p.gridDim = dim3((unsigned)((n + kPadThreads - 1) / kPadThreads > 0
+                                  ? (n + kPadThreads - 1) / kPadThreads : 1));
+  p.blockDim = dim3(kPadThreads);
+  p.sharedMemBytes = 0;
+  p.kernelParams = args;
+  p.extra = nullptr;
+  return p;
+}
+
 }  // namespace
+
+hipError_t launch_pad_rows(int32_t* ntns, int32_t* samp, int T, int from, int to,
+                          hipStream_t st) {
+  void* args[] = {&ntns, &samp, &T, &from, &to};
+  const hipKernelNodeParams p = pad_params(args, T, to);
+  return hipLaunchKernel(p.func, p.gridDim, p.blockDim, args, 0, st);
+}
+
+hipError_t set_pad_rows(hipGraphExec_t exec, hipGraphNode_t node, int32_t* ntns, int32_t* samp,
+                        int T, int from, int to) {
+  void* args[] = {&ntns, &samp, &T, &from, &to};
+  const hipKernelNodeParams p = pad_params(args, T, to);
+  return hipGraphExecKernelNodeSetParams(exec, node, &p);
+}
 
 hipError_t launch_counts_prep(int B, int T, const int32_t* sampled, const int32_t* counts,
                               int32_t* s_out, hipStream_t st) {

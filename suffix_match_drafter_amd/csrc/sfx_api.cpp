@@ -504,9 +504,11 @@ extern "C" void sfx_debug_phase_trace(void* buf) { g_phase_trace = (uint64_t*)bu
 #endif
 
 // The drafter step with draft width k (at most the configured one), after argument checks.
+// With force_pairs the delta grouping passes run even when no ingest is pending (a captured
+// chain meant for engines that ingest every step).
 static int propose_k(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
                      const int32_t* ntns, const int32_t* tok, const int32_t* samp,
-                     int32_t* draft, int32_t* nvalid, void* stream) {
+                     int32_t* draft, int32_t* nvalid, void* stream, bool force_pairs = false) {
   const sfx_config& g = c->cfg;
   if (B < 0 || S < 0 || T < 0) return fail(SFX_EINVAL, "negative shape B=%d S=%d T=%d", B, S, T);
   if (B > g.max_batch || S > g.max_seq || T > g.max_sampled)
@@ -543,7 +545,7 @@ static int propose_k(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
 #if SFX_PHASE_TRACE
   a.trace = g_phase_trace;
 #endif
-  if (c->pair_list && B <= kPairMaxBatch && c->ingest_epoch != c->live_epoch) {
+  if (c->pair_list && B <= kPairMaxBatch && (force_pairs || c->ingest_epoch != c->live_epoch)) {
     PairIndexArgs p{};
     p.B = B;
     p.S = S;
@@ -1135,6 +1137,225 @@ int sfx_debug_errors(sfx_ctx* c, uint32_t* bits_out, void* stream) {
   HIP_OR_RETURN(hipStreamSynchronize(st), "error word sync");
   *bits_out = v;
   return SFX_OK;
+}
+
+// ------------------------------------------------------------------ batch-bucketed graphs
+// RFC page "[RFC]: Suffix decoding on GPU (suffix_gpu)", Design, Proposer bullet: the draft
+// chain is captured per batch-size bucket at warm-up, with an eager fallback.  Each bucket keeps
+// an exact graph (B == Bp) and a padded one whose first node empties rows B .. Bp-1; only that
+// node's arguments change between replays.  Both are captured from the stream (a node added to
+// a captured graph by hand measured slower to launch).
+constexpr int kMaxGraphBuckets = 64;
+
+}  // extern "C"
+
+struct sfx_graphs {
+  sfx_ctx* ctx = nullptr;
+  int32_t S = 0, T = 0, flags = 0;
+  int32_t* ntns = nullptr;
+  int32_t* tok = nullptr;
+  int32_t* samp = nullptr;
+  int32_t* draft = nullptr;
+  int32_t* nvalid = nullptr;
+  int32_t* nout = nullptr;
+  int nb = 0;
+  int32_t bucket[kMaxGraphBuckets]{};
+  hipGraph_t graph[kMaxGraphBuckets]{};  // the padded graph (its padding node lives there)
+  hipGraphExec_t exact[kMaxGraphBuckets]{};
+  hipGraphExec_t padded[kMaxGraphBuckets]{};
+  hipGraphNode_t pad[kMaxGraphBuckets]{};
+  int32_t pad_from[kMaxGraphBuckets]{};
+  int64_t replays = 0, eager = 0;
+};
+
+namespace {
+
+// The chain of one step over B rows of the graph set's buffers.
+int graph_chain(sfx_graphs* g, int32_t B, hipStream_t st) {
+  int rc = check_ctx(g->ctx);
+  if (rc) return rc;
+  rc = propose_k(g->ctx, g->ctx->cfg.k, B, g->S, g->T, g->ntns, g->tok, g->samp, g->draft,
+                 g->nvalid, st, (g->flags & SFX_GRAPHS_DELTA_INDEX) != 0);
+  if (rc) return rc;
+  if (checking(g->ctx))
+    HIP_OR_RETURN(launch_check_propose(B, g->S, g->T, g->ntns, g->tok, g->samp, nullptr,
+                                       g->ctx->err, st), "input check launch");
+  if (g->flags & SFX_GRAPHS_UPDATE_STATE)
+    return sfx_update_state(B, g->S, g->T, g->tok, g->ntns, g->samp, g->nout, st);
+  return SFX_OK;
+}
+
+// Captures bucket i's chain on a stream of its own (thread-local mode: the context's rebuild
+// worker may use the runtime meanwhile), once as it is and once behind the padding node (found
+// as the capture's only dependency right after it is launched).  Any failure ends the capture,
+// drops what was captured, discards that stream and clears the runtime's last error; a graph
+// that is missing runs eagerly.
+hipGraphExec_t capture_chain(sfx_graphs* g, int i, bool padded, hipGraphNode_t* pad_node,
+                             hipGraph_t* graph_out) {
+  const int bp = g->bucket[i];
+  hipStream_t cap = nullptr;
+  if (hipStreamCreateWithFlags(&cap, hipStreamNonBlocking) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    (void)hipStreamDestroy(cap);
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  int rc = SFX_OK;
+  if (padded) {
+    hipStreamCaptureStatus cs;
+    const hipGraphNode_t* deps = nullptr;
+    size_t ndeps = 0;
+    if (launch_pad_rows(g->ntns, g->samp, g->T, bp, bp, cap) != hipSuccess ||
+        hipStreamGetCaptureInfo_v2(cap, &cs, nullptr, nullptr, &deps, &ndeps) != hipSuccess ||
+        ndeps != 1)
+      rc = SFX_EHIP;
+    else
+      *pad_node = deps[0];
+  }
+  if (rc == SFX_OK) rc = graph_chain(g, bp, cap);
+  if (rc == SFX_OK && (g->flags & SFX_GRAPHS_DEBUG_BREAK_ODD) && (i & 1))
+    rc = hipStreamSynchronize(cap) == hipSuccess ? SFX_OK : SFX_EHIP;  // not allowed here
+  hipGraph_t gr = nullptr;
+  const hipError_t e = hipStreamEndCapture(cap, &gr);
+  (void)hipStreamDestroy(cap);
+  hipGraphExec_t ex = nullptr;
+  if (rc != SFX_OK || e != hipSuccess || !gr ||
+      hipGraphInstantiate(&ex, gr, nullptr, nullptr, 0) != hipSuccess) {
+    ex = nullptr;
+    if (gr) (void)hipGraphDestroy(gr);
+    gr = nullptr;
+  }
+  (void)hipGetLastError();
+  if (padded)
+    *graph_out = gr;  // the node handle stays valid while its graph lives
+  else if (gr)
+    (void)hipGraphDestroy(gr);
+  return ex;
+}
+
+void capture_bucket(sfx_graphs* g, int i, hipStream_t upload) {
+  g->exact[i] = capture_chain(g, i, false, nullptr, nullptr);
+  if (g->exact[i]) (void)hipGraphUpload(g->exact[i], upload);
+  if (g->bucket[i] > 1) {
+    g->padded[i] = capture_chain(g, i, true, &g->pad[i], &g->graph[i]);
+    g->pad_from[i] = g->bucket[i];
+    if (g->padded[i]) (void)hipGraphUpload(g->padded[i], upload);
+  }
+  (void)hipGetLastError();
+}
+
+void free_graphs(sfx_graphs* g) {
+  for (int i = 0; i < g->nb; ++i) {
+    if (g->exact[i]) (void)hipGraphExecDestroy(g->exact[i]);
+    if (g->padded[i]) (void)hipGraphExecDestroy(g->padded[i]);
+    if (g->graph[i]) (void)hipGraphDestroy(g->graph[i]);
+  }
+  delete g;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sfx_graphs_create(sfx_ctx* c, int32_t nbuckets, const int32_t* buckets, int32_t S,
+                      int32_t T, int32_t* ntns, int32_t* tok, int32_t* samp, int32_t* draft,
+                      int32_t* nvalid, int32_t* nout, int32_t flags, void* stream,
+                      sfx_graphs** out) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!out) return fail(SFX_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (nbuckets < 1 || nbuckets > kMaxGraphBuckets || !buckets)
+    return fail(SFX_EINVAL, "nbuckets=%d outside [1,%d] (or buckets NULL)", nbuckets,
+                kMaxGraphBuckets);
+  if (flags & ~(SFX_GRAPHS_EAGER | SFX_GRAPHS_UPDATE_STATE | SFX_GRAPHS_DELTA_INDEX |
+                SFX_GRAPHS_DEBUG_BREAK_ODD))
+    return fail(SFX_EINVAL, "unknown graph flags 0x%x", flags);
+  for (int i = 0; i < nbuckets; ++i) {
+    if (buckets[i] < 1 || (i > 0 && buckets[i] <= buckets[i - 1]))
+      return fail(SFX_EINVAL, "buckets must be >= 1 and strictly ascending (bucket %d = %d)", i,
+                  buckets[i]);
+  }
+  if (buckets[nbuckets - 1] > c->cfg.max_batch)
+    return fail(SFX_ECAPACITY, "bucket %d above max_batch=%d", buckets[nbuckets - 1],
+                c->cfg.max_batch);
+  if (S < 0 || T < 0) return fail(SFX_EINVAL, "negative shape S=%d T=%d", S, T);
+  if (S > c->cfg.max_seq || T > c->cfg.max_sampled)
+    return fail(SFX_ECAPACITY, "S=%d T=%d above max_seq=%d max_sampled=%d", S, T,
+                c->cfg.max_seq, c->cfg.max_sampled);
+  const bool update = (flags & SFX_GRAPHS_UPDATE_STATE) != 0;
+  if (!ntns || !draft || !nvalid || (S > 0 && !tok) || (T > 0 && !samp) || (update && !nout))
+    return fail(SFX_EINVAL, "NULL buffer argument");
+  if (!update && nout) return fail(SFX_EINVAL, "num_tokens_out given without the update flag");
+  sfx_graphs* g = new sfx_graphs;
+  g->ctx = c;
+  g->S = S;
+  g->T = T;
+  g->flags = flags;
+  g->ntns = ntns;
+  g->tok = tok;
+  g->samp = samp;
+  g->draft = draft;
+  g->nvalid = nvalid;
+  g->nout = nout;
+  g->nb = nbuckets;
+  for (int i = 0; i < nbuckets; ++i) g->bucket[i] = buckets[i];
+  if (!(flags & SFX_GRAPHS_EAGER))
+    for (int i = 0; i < nbuckets; ++i) capture_bucket(g, i, (hipStream_t)stream);
+  *out = g;
+  return SFX_OK;
+}
+
+int sfx_graphs_propose(sfx_graphs* g, int32_t B, void* stream) {
+  if (!g) return fail(SFX_EINVAL, "graph set is NULL");
+  if (B < 0) return fail(SFX_EINVAL, "negative B=%d", B);
+  if (B == 0) return SFX_OK;
+  hipStream_t st = (hipStream_t)stream;
+  int i = 0;
+  while (i < g->nb && g->bucket[i] < B) ++i;
+  if (i < g->nb) {
+    if (B == g->bucket[i] && g->exact[i]) {
+      HIP_OR_RETURN(hipGraphLaunch(g->exact[i], st), "graph launch");
+      ++g->replays;
+      return SFX_OK;
+    }
+    if (B < g->bucket[i] && g->padded[i]) {
+      if (g->pad_from[i] != B) {
+        HIP_OR_RETURN(set_pad_rows(g->padded[i], g->pad[i], g->ntns, g->samp, g->T, B,
+                                   g->bucket[i]), "pad node update");
+        g->pad_from[i] = B;
+      }
+      HIP_OR_RETURN(hipGraphLaunch(g->padded[i], st), "graph launch");
+      ++g->replays;
+      return SFX_OK;
+    }
+  }
+  const int rc = graph_chain(g, B, st);
+  if (rc == SFX_OK) ++g->eager;
+  return rc;
+}
+
+int sfx_graphs_stats(sfx_graphs* g, int32_t* nbuckets, uint64_t* exact_mask,
+                     uint64_t* padded_mask, int64_t* replays, int64_t* eager_calls) {
+  if (!g) return fail(SFX_EINVAL, "graph set is NULL");
+  uint64_t em = 0, pm = 0;
+  for (int i = 0; i < g->nb; ++i) {
+    if (g->exact[i]) em |= 1ull << i;
+    if (g->padded[i]) pm |= 1ull << i;
+  }
+  if (nbuckets) *nbuckets = g->nb;
+  if (exact_mask) *exact_mask = em;
+  if (padded_mask) *padded_mask = pm;
+  if (replays) *replays = g->replays;
+  if (eager_calls) *eager_calls = g->eager;
+  return SFX_OK;
+}
+
+void sfx_graphs_destroy(sfx_graphs* g) {
+  if (g) free_graphs(g);
 }
 
 int sfx_debug_fail_next_rebuild(sfx_ctx* c) {
