@@ -20,7 +20,7 @@ HIPCC_FLAGS = [
 
 def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip"))) + \
-        [os.path.join(HERE, "csrc", "sfx_api.cpp")]
+        [os.path.join(HERE, "csrc", "sfx_api.cpp"), os.path.join(HERE, "csrc", "corpus_file.cpp")]
 
 
 def build(force: bool = True, verbose: bool = False) -> str:

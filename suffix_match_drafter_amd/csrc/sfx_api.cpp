@@ -17,6 +17,7 @@
 #include "../../include/sfx.h"
 #include "accept.h"
 #include "corpus.h"
+#include "corpus_file.h"
 #include "call_forms.h"
 #include "checks.h"
 #include "delta_index.h"
@@ -257,27 +258,6 @@ void finish_async(sfx_ctx* c) {
 }
 
 // ------------------------------------------------------------------ corpus files
-// Layout and checksum as declared with sfx_save in sfx.h.
-constexpr char kCorpusMagic[8] = {'S', 'F', 'X', 'C', 'O', 'R', 'P', '1'};
-struct CorpusHeader {
-  char magic[8];
-  int64_t capacity, head, tail, doc_head, doc_tail, snap_start, snap_end;
-  uint64_t checksum;
-};
-static_assert(sizeof(CorpusHeader) == 72, "corpus file header is 72 bytes");
-
-struct Fnv32Words {
-  uint64_t h = 14695981039346656037ull;
-  void add(const void* p, size_t bytes) {  // bytes is a multiple of 4
-    const unsigned char* b = static_cast<const unsigned char*>(p);
-    for (size_t i = 0; i + 4 <= bytes; i += 4) {
-      uint32_t w;
-      std::memcpy(&w, b + i, 4);
-      h = (h ^ w) * 1099511628211ull;
-    }
-  }
-};
-
 // Copies n elements of a device ring of `size` elements starting at logical index `from`
 // (slot from % size) into host memory, in at most two pieces.
 template <typename T>
@@ -302,40 +282,6 @@ hipError_t host_to_ring(T* ring, int64_t size, int64_t from, const T* src, int64
   if (e == hipSuccess && n > first)
     e = hipMemcpyAsync(ring, src + first, sizeof(T) * (n - first), hipMemcpyHostToDevice, st);
   return e;
-}
-
-// Consistency of a corpus file's contents against the context it is loaded into: everything a
-// kernel would later index with (document starts, the suffix array) is range-checked here.
-int check_corpus(const CorpusHeader& h, const std::vector<int32_t>& live,
-                 const std::vector<int64_t>& starts, const std::vector<int32_t>& text,
-                 const std::vector<int32_t>& sa) {
-  const int64_t nl = h.head - h.tail, nd = h.doc_head - h.doc_tail, ni = h.snap_end - h.snap_start;
-  if (nl > 0 && live[nl - 1] != -1) return fail(SFX_EIO, "corpus file: last document unterminated");
-  if ((nd == 0) != (nl == 0)) return fail(SFX_EIO, "corpus file: documents and tokens disagree");
-  for (int64_t j = 0; j < nd; ++j) {
-    // the first document starts at tail; every later one after the previous start, before
-    // head, and right after a separator (range first, so the lookup stays inside `live`)
-    const int64_t st = starts[j];
-    const bool good = j == 0 ? st == h.tail
-                             : st > starts[j - 1] && st < h.head && live[st - h.tail - 1] == -1;
-    if (!good)
-      return fail(SFX_EIO, "corpus file: document %lld starts at %lld, not after a separator",
-                  (long long)j, (long long)st);
-  }
-  // the indexed text agrees with the live corpus where both exist
-  const int64_t lo = h.snap_start > h.tail ? h.snap_start : h.tail;
-  for (int64_t q = lo; q < h.snap_end; ++q)
-    if (text[q - h.snap_start] != live[q - h.tail])
-      return fail(SFX_EIO, "corpus file: index text differs from the corpus at %lld",
-                  (long long)q);
-  std::vector<unsigned char> seen(ni, 0);
-  for (int64_t r = 0; r < ni; ++r) {
-    const int32_t v = sa[r];
-    if (v < 0 || v >= ni || seen[v])
-      return fail(SFX_EIO, "corpus file: suffix array is not a permutation");
-    seen[v] = 1;
-  }
-  return SFX_OK;
 }
 
 int swap_in(sfx_ctx* c, hipStream_t st) {
@@ -952,8 +898,8 @@ int sfx_save(sfx_ctx* c, const char* path, void* stream) {
   Ctl k{};
   HIP_OR_RETURN(hipMemcpyAsync(&k, c->ctl, sizeof k, hipMemcpyDeviceToHost, st), "control read");
   HIP_OR_RETURN(hipStreamSynchronize(st), "control wait");
-  CorpusHeader h{};
-  std::memcpy(h.magic, kCorpusMagic, 8);
+  CorpusImage m;
+  CorpusHeader& h = m.h;
   h.capacity = c->cap;
   h.head = k.head;
   h.tail = k.tail;
@@ -965,38 +911,22 @@ int sfx_save(sfx_ctx* c, const char* path, void* stream) {
   const int64_t nl = h.head - h.tail, nd = h.doc_head - h.doc_tail, ni = h.snap_end - h.snap_start;
   if (nl < 0 || nl > c->cap || nd < 0 || nd >= c->dcap || ni < 0 || ni > c->cap)
     return fail(SFX_EHIP, "corrupt control block");
-  std::vector<int32_t> live(nl), text(ni), sa(ni);
-  std::vector<int64_t> starts(nd);
-  HIP_OR_RETURN(ring_to_host(live.data(), c->ring, c->cap, h.tail, nl, st), "ring read");
-  HIP_OR_RETURN(ring_to_host(starts.data(), c->doc_start, c->dcap, h.doc_tail, nd, st),
+  m.live.resize(nl);
+  m.starts.resize(nd);
+  m.text.resize(ni);
+  m.sa.resize(ni);
+  HIP_OR_RETURN(ring_to_host(m.live.data(), c->ring, c->cap, h.tail, nl, st), "ring read");
+  HIP_OR_RETURN(ring_to_host(m.starts.data(), c->doc_start, c->dcap, h.doc_tail, nd, st),
                 "document read");
   if (ni > 0) {
-    HIP_OR_RETURN(hipMemcpyAsync(text.data(), c->idx[a].text, 4 * ni, hipMemcpyDeviceToHost, st),
+    HIP_OR_RETURN(hipMemcpyAsync(m.text.data(), c->idx[a].text, 4 * ni, hipMemcpyDeviceToHost, st),
                   "index text read");
-    HIP_OR_RETURN(hipMemcpyAsync(sa.data(), c->idx[a].sa, 4 * ni, hipMemcpyDeviceToHost, st),
+    HIP_OR_RETURN(hipMemcpyAsync(m.sa.data(), c->idx[a].sa, 4 * ni, hipMemcpyDeviceToHost, st),
                   "suffix array read");
   }
   HIP_OR_RETURN(hipStreamSynchronize(st), "read wait");
-  Fnv32Words f;
-  f.add(live.data(), 4 * nl);
-  f.add(starts.data(), 8 * nd);
-  f.add(text.data(), 4 * ni);
-  f.add(sa.data(), 4 * ni);
-  h.checksum = f.h;
-  // written beside the target and renamed over it, so a failed save leaves no partial file
-  const std::string tmp = std::string(path) + ".partial";
-  FILE* fp = std::fopen(tmp.c_str(), "wb");
-  if (!fp) return fail(SFX_EIO, "cannot open %s for writing", tmp.c_str());
-  bool ok = std::fwrite(&h, sizeof h, 1, fp) == 1;
-  ok = ok && (nl == 0 || std::fwrite(live.data(), 4, nl, fp) == (size_t)nl);
-  ok = ok && (nd == 0 || std::fwrite(starts.data(), 8, nd, fp) == (size_t)nd);
-  ok = ok && (ni == 0 || std::fwrite(text.data(), 4, ni, fp) == (size_t)ni);
-  ok = ok && (ni == 0 || std::fwrite(sa.data(), 4, ni, fp) == (size_t)ni);
-  ok = (std::fclose(fp) == 0) && ok;
-  if (!ok || std::rename(tmp.c_str(), path) != 0) {
-    std::remove(tmp.c_str());
-    return fail(SFX_EIO, "writing %s failed", path);
-  }
+  std::string why;
+  if ((rc = write_corpus_file(path, &m, &why)) != SFX_OK) return fail(rc, "%s", why.c_str());
   return SFX_OK;
 }
 
@@ -1006,58 +936,21 @@ int sfx_load(sfx_ctx* c, const char* path, void* stream) {
   if (!path) return fail(SFX_EINVAL, "path is NULL");
   if (!c->ctl) return fail(SFX_ESTATE, "context has no corpus (corpus_capacity == 0)");
   if (c->async_state.load() != 0) return fail(SFX_ESTATE, "an asynchronous rebuild is in flight");
-  FILE* fp = std::fopen(path, "rb");
-  if (!fp) return fail(SFX_EIO, "cannot open %s", path);
-  CorpusHeader h{};
-  std::vector<int32_t> live, text, sa;
-  std::vector<int64_t> starts;
-  auto bad = [&](int code, const char* what) {
-    std::fclose(fp);
-    return fail(code, "corpus file %s: %s", path, what);
-  };
-  if (std::fread(&h, sizeof h, 1, fp) != 1) return bad(SFX_EIO, "truncated header");
-  if (std::memcmp(h.magic, kCorpusMagic, 8) != 0) return bad(SFX_EIO, "not a corpus file");
-  if (h.capacity != c->cap) {
-    std::fclose(fp);
-    return fail(SFX_EINVAL, "corpus file %s has capacity %lld, the context %lld", path,
-                (long long)h.capacity, (long long)c->cap);
-  }
-  const int64_t kMaxPos = int64_t(1) << 62;
-  if (h.tail < 0 || h.head < h.tail || h.head > kMaxPos || h.head - h.tail > c->cap ||
-      h.doc_tail < 0 || h.doc_head < h.doc_tail || h.doc_head > kMaxPos ||
-      h.doc_head - h.doc_tail > h.head - h.tail || h.snap_start < 0 ||
-      h.snap_end < h.snap_start || h.snap_end > h.head || h.snap_end - h.snap_start > c->cap)
-    return bad(SFX_EIO, "inconsistent counters");
+  CorpusImage m;
+  std::string why;
+  if ((rc = read_corpus_file(path, c->cap, &m, &why)) != SFX_OK) return fail(rc, "%s", why.c_str());
+  const CorpusHeader& h = m.h;
   const int64_t nl = h.head - h.tail, nd = h.doc_head - h.doc_tail, ni = h.snap_end - h.snap_start;
-  live.resize(nl);
-  starts.resize(nd);
-  text.resize(ni);
-  sa.resize(ni);
-  bool ok = nl == 0 || std::fread(live.data(), 4, nl, fp) == (size_t)nl;
-  ok = ok && (nd == 0 || std::fread(starts.data(), 8, nd, fp) == (size_t)nd);
-  ok = ok && (ni == 0 || std::fread(text.data(), 4, ni, fp) == (size_t)ni);
-  ok = ok && (ni == 0 || std::fread(sa.data(), 4, ni, fp) == (size_t)ni);
-  if (!ok) return bad(SFX_EIO, "truncated payload");
-  if (std::fgetc(fp) != EOF) return bad(SFX_EIO, "trailing bytes");
-  std::fclose(fp);
-  Fnv32Words f;
-  f.add(live.data(), 4 * nl);
-  f.add(starts.data(), 8 * nd);
-  f.add(text.data(), 4 * ni);
-  f.add(sa.data(), 4 * ni);
-  if (f.h != h.checksum) return fail(SFX_EIO, "corpus file %s: checksum mismatch", path);
-  if ((rc = check_corpus(h, live, starts, text, sa)) != SFX_OK) return rc;
-
   hipStream_t st = (hipStream_t)stream;
-  HIP_OR_RETURN(host_to_ring(c->ring, c->cap, h.tail, live.data(), nl, st), "ring write");
-  HIP_OR_RETURN(host_to_ring(c->doc_start, c->dcap, h.doc_tail, starts.data(), nd, st),
+  HIP_OR_RETURN(host_to_ring(c->ring, c->cap, h.tail, m.live.data(), nl, st), "ring write");
+  HIP_OR_RETURN(host_to_ring(c->doc_start, c->dcap, h.doc_tail, m.starts.data(), nd, st),
                 "document write");
   uint32_t mask = 0;
   IndexBuf& b = c->idx[0];
   if (ni > 0) {
-    HIP_OR_RETURN(hipMemcpyAsync(b.text, text.data(), 4 * ni, hipMemcpyHostToDevice, st),
+    HIP_OR_RETURN(hipMemcpyAsync(b.text, m.text.data(), 4 * ni, hipMemcpyHostToDevice, st),
                   "index text write");
-    HIP_OR_RETURN(hipMemcpyAsync(b.sa, sa.data(), 4 * ni, hipMemcpyHostToDevice, st),
+    HIP_OR_RETURN(hipMemcpyAsync(b.sa, m.sa.data(), 4 * ni, hipMemcpyHostToDevice, st),
                   "suffix array write");
     const uint32_t slots = slots_for(c, ni);
     HIP_OR_RETURN(ngram_tables_build(b.text, b.sa, ni, b.pl, b.ht, slots, c->saw, st),
