@@ -228,6 +228,11 @@ struct Smem {
   int gsites[kMaxNB][kMaxM];  // logical corpus positions minus the oldest live one (Ctl tail)
   int gpl[kNG][kMaxM];  // heads of the live 2-, 3- and 4-gram groups
   int gm4[kMaxM];       // extension lengths of the first 4-gram occurrences
+  // hot 4-gram groups: per length l >= 5, the support and the first suffix-array index of the
+  // suffixes that start with the length-l tail pattern and continue with a real token
+  int hsup[kMaxD + 1], hlo[kMaxD + 1];
+  int ghot;  // 1 when the snapshot part of lengths >= 5 comes from them
+  int hn;    // snapshot sites found by the general path's hot site pass
   const int32_t* plp[kNG];
   int wsum[NW + 1];
   int wbar;    // arrivals at the worker-only barrier
@@ -255,6 +260,7 @@ struct Req {
 // selects keep the kernel arguments out of scratch memory.
 struct View {
   const int32_t* text;
+  const int32_t* sa;
   const int32_t* pl0;
   const int32_t* pl1;
   const int32_t* pl2;
@@ -268,6 +274,7 @@ __device__ __forceinline__ View view_of(const ProposeArgs& a, int act, uint32_t 
   View v;
   v.mask = mask;
   v.text = z ? a.idx[0].text : a.idx[1].text;
+  v.sa = z ? a.idx[0].sa : a.idx[1].sa;
   v.pl0 = z ? a.idx[0].pl[0] : a.idx[1].pl[0];
   v.pl1 = z ? a.idx[0].pl[1] : a.idx[1].pl[1];
   v.pl2 = z ? a.idx[0].pl[2] : a.idx[1].pl[2];
@@ -348,6 +355,157 @@ __device__ __noinline__ int extend4(const int32_t* text, const int* tail, int i,
     if (stop) break;
   }
   return m;
+}
+
+// Hot 4-gram groups (suffix-gpu page, How it works step 2: a fixed-iteration binary search of the
+// suffix array for every pattern length).  Extending each live occurrence of the tail's 4-gram
+// costs one round trip per 64 occurrences, so above kHotGroup of them the snapshot part of
+// lengths >= 5 comes from the suffix array instead.  The suffixes that start with the length-l
+// tail pattern P_l and continue with a real token form one range of it, inside the group of
+// the 4-gram that starts P_l (whose range the probe table holds): two bound searches per length,
+// all lengths at once, give every support.  A candidate's earliest sites are then the smallest
+// positions of its range (selected from the range itself when it holds at most kHotSelect
+// entries, else found by the position-ordered scan of the 4-gram group, which stops after M of
+// them: about M * group / support occurrences).  This needs every snapshot position live, so it
+// is not used while documents evicted since the snapshot still lie in it.
+constexpr int kHotGroup = 1024;
+constexpr int kHotSelect = 2048;
+constexpr int kHotCmp = 8;  // suffix tokens compared per round trip
+
+// Bounds of lengths l = 5 .. Lcap: lane pair (2 (l - 5), 2 (l - 5) + 1) finds the first index of
+// the range whose suffix is >= P_l followed by token 0 (lower bound), and the first whose suffix
+// is above every suffix with prefix P_l (upper bound).  tl[x] is the context token x places
+// before the last one.  Writes sup[l] and lo[l] for 5 <= l <= Lcap.
+__device__ __noinline__ void hot_bounds(const View ib, const int* tl, int Lcap, int snap_n,
+                                        int lane, int* sup, int* lo_out) {
+  for (int pass = 0; pass < 2; ++pass) {
+    const int idx = lane + 64 * pass;
+    const int l = 5 + (idx >> 1), side = idx & 1;
+    int lo = 0;
+    if (l <= Lcap) {
+      // the group of Q_l = P_l[0..3] = tl[l-1], tl[l-2], tl[l-3], tl[l-4]
+      int key[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) key[x] = tl[l - 1 - x];
+      uint32_t h = ngram_hash4(key, 4) & ib.mask;
+      int beg = 0, cnt = 0;
+      for (;;) {
+        const NgramSlot s = ib.ht2[h];
+        if (s.owner == 0) break;
+        if (s.key[0] == key[0] && s.key[1] == key[1] && s.key[2] == key[2] &&
+            s.key[3] == key[3]) {
+          beg = s.sa_lo;
+          cnt = s.cnt;
+          break;
+        }
+        h = (h + 1) & ib.mask;
+      }
+      lo = beg;
+      int hi = beg + cnt;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const int pos = ib.sa[mid];
+        // compare the suffix at pos from offset 4 on with P_l (then, for the lower bound, with
+        // token 0 at offset l); every suffix of the group matches offsets 0..3
+        int cmp = 0;  // -1 suffix below, +1 above, 0 equal so far
+        for (int o0 = 4; o0 <= l && cmp == 0; o0 += kHotCmp) {
+          int c[kHotCmp];
+#pragma unroll
+          for (int q = 0; q < kHotCmp; ++q) {
+            // the text ends with a separator, which decides before any clamped read matters
+            const int at = pos + o0 + q < snap_n ? pos + o0 + q : snap_n - 1;
+            c[q] = ib.text[at];
+          }
+#pragma unroll
+          for (int q = 0; q < kHotCmp; ++q) {
+            const int o = o0 + q;
+            if (cmp == 0 && o <= l) {
+              if (o < l) {
+                const int p = tl[l - 1 - o];
+                cmp = c[q] < p ? -1 : (c[q] > p ? 1 : 0);
+              } else if (side == 0) {
+                cmp = c[q] < 0 ? -1 : 1;  // continues with a separator: below P_l, 0
+              }
+            }
+          }
+        }
+        const bool right = side == 0 ? cmp < 0 : cmp <= 0;
+        if (right) lo = mid + 1;
+        else hi = mid;
+      }
+    }
+    const int up = __builtin_amdgcn_ds_bpermute(4 * ((lane + 1) & 63), lo);
+    if (l <= Lcap && side == 0) {
+      sup[l] = up - lo;
+      lo_out[l] = lo;
+    }
+  }
+}
+
+// Earliest sites of a hot candidate of length l whose range [lo, lo + sup) has at most
+// kHotSelect entries: the m = min(M, sup) smallest suffix positions, found by a search for the
+// m-th smallest value, then put in order by rank; gs[r] = position + l + sbase.  Returns m.
+__device__ __noinline__ int hot_select(const View ib, int lo, int sup, int l, int M, int snap_n,
+                                       int sbase, int* gs, int lane) {
+  constexpr int Q = kHotSelect / 64;
+  const int m = sup < M ? sup : M;
+  int v[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int e = lane + 64 * q;
+    v[q] = e < sup ? ib.sa[lo + e] : 0x7fffffff;
+  }
+  int a = 0, b = snap_n - 1;  // the m-th smallest lies in [a, b]
+  while (a < b) {
+    const int mid = a + ((b - a) >> 1);
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) c += __popcll(__ballot(v[q] <= mid));
+    if (c >= m) b = mid;
+    else a = mid + 1;
+  }
+  // the m values <= a (positions are distinct), gathered in any order, then ranked
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const bool s = v[q] <= a;
+    const uint64_t bal = __ballot(s);
+    if (s) gs[n + lanes_before(bal)] = v[q];
+    n += __popcll(bal);
+  }
+  wave_sync();
+  const int e0 = lane < m ? gs[lane] : 0x7fffffff;
+  const int e1 = lane + 64 < m ? gs[lane + 64] : 0x7fffffff;
+  int r0 = 0, r1 = 0;
+  for (int j = 0; j < m; ++j) {
+    const int x = gs[j];
+    r0 += x < e0 ? 1 : 0;
+    r1 += x < e1 ? 1 : 0;
+  }
+  wave_sync();
+  if (lane < m) gs[r0] = e0 + l + sbase;
+  if (lane + 64 < m) gs[r1] = e1 + l + sbase;
+  wave_sync();
+  return m;
+}
+
+// Earliest sites of a hot candidate of length l with a larger range: the live 4-gram
+// occurrences in position order whose extension reaches l, until M are found.  Returns how many.
+__device__ __forceinline__ int hot_scan(const View ib, const int32_t* pl4, int live4,
+                                        const int* tl, int l, int M, int sbase, int* gs,
+                                        int lane) {
+  const uint64_t below = lanes_below(lane);
+  int run = 0;
+  for (int base = 0; base < live4 && run < M; base += 64) {
+    const int x = base + lane;
+    const int i = x < live4 ? pl4[x] : 0;
+    const bool q = x < live4 && extend4(ib.text, tl, i, l) >= l;
+    const uint64_t bal = __ballot(q);
+    const int rk = run + __popcll(bal & below);
+    if (q && rk < M) gs[rk] = i + 4 + sbase;
+    run += __popcll(bal);
+  }
+  return run < M ? run : M;
 }
 
 // Address of the corpus token at logical position q: snapshot text below snap_end, else ring slot
@@ -1033,7 +1191,11 @@ __device__ __forceinline__ void corpus_wave_probe(const ProposeArgs& a, const Re
     for (int x = lane; x < ns; x += 64) sm.gpl[g][x] = pl[x];
   }
   const int live4 = sm.g_live[2];
-  if (Lcap >= 5 && live4 > 0) {
+  const bool hot = Lcap >= 5 && live4 > kHotGroup && dead_below <= 0;
+  if (lane == 0) sm.ghot = hot;
+  if (hot) {
+    hot_bounds(ib, sm.gtail, Lcap, (int)r.snap_n, lane, sm.hsup, sm.hlo);
+  } else if (Lcap >= 5 && live4 > 0) {
     const int32_t* pl4 = ib.pl2 + sm.g_off[2];
     for (int x = lane; x < live4; x += 64) {
       const int i = pl4[x];
@@ -1057,10 +1219,12 @@ __device__ __forceinline__ void corpus_wave_sites(const ProposeArgs& a, const Re
   // support of length v = lane + 1 (lengths up to 64 on 64 lanes): the live v-gram group for
   // v <= 4, else the extensions reaching v
   const int v = lane + 1;
+  const bool hot = sm.ghot;
   const int gh = (v >= 5 && v <= Lcap) ? sm.ghist[v] : 0;
   const int gin = wave_incl_add(gh);
   const int gsuf = __builtin_amdgcn_readlane(gin, 63) - gin + gh;
-  const int sup_l = v >= 2 && v <= 4 ? sm.g_live[v - 2] : gsuf;
+  const int hsup = (v >= 5 && v <= Lcap) ? sm.hsup[v] : 0;
+  const int sup_l = v >= 2 && v <= 4 ? sm.g_live[v - 2] : (hot ? hsup : gsuf);
   const int minc = a.min_corpus > 2 ? a.min_corpus : 2;
   int prev_l = -1, prev_src = -1;
   for (int ti = 0; ti < nb; ++ti) {
@@ -1084,6 +1248,13 @@ __device__ __forceinline__ void corpus_wave_sites(const ProposeArgs& a, const Re
       const int g = l - 2;
       const int ns = sup < M ? sup : M;
       for (int x = lane; x < ns; x += 64) gs[x] = sm.gpl[g][x] + l + sbase;
+    } else if (hot) {
+      const View ib = view_of(a, r.act, r.ht_mask);
+      const int got = sup <= kHotSelect
+                          ? hot_select(ib, sm.hlo[l], sup, l, M, (int)r.snap_n, sbase, gs, lane)
+                          : hot_scan(ib, ib.pl2 + sm.g_off[2], sm.g_live[2], sm.gtail, l, M,
+                                     sbase, gs, lane);
+      if (lane == 0 && got < (sup < M ? sup : M)) sm.cand_c0[ci] = got;
     } else {
       // the first M live 4-gram occurrences (position order) whose extension reaches l
       const int live4 = sm.g_live[2];
@@ -1787,7 +1958,11 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     }
     __syncthreads();
     const int live4 = sm.g_live[2];
-    if (!fast && act >= 0 && Lcap >= 5 && live4 > 0) {
+    // the same choice as the corpus wavefront's (the same inputs), which stands on the fast path
+    const bool hot = act >= 0 && Lcap >= 5 && live4 > kHotGroup && dead_below <= 0;
+    if (!fast && hot) {
+      if (wid == 0) hot_bounds(ib, sm.tail, Lcap, (int)r.snap_n, lane, sm.hsup, sm.hlo);
+    } else if (!fast && act >= 0 && Lcap >= 5 && live4 > 0) {
       const int32_t* pl4 = ib.pl2 + sm.g_off[2];
       for (int x = tid; x < live4; x += NT) {
         const int m = extend4(ib.text, sm.tail, pl4[x], Lcap);
@@ -1861,7 +2036,8 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       const int gh = (v >= 5 && v <= Lcap) ? sm.ghist[v] : 0;
       const int gin = wave_incl_add(gh);
       const int gsuf = __builtin_amdgcn_readlane(gin, 63) - gin + gh;
-      int snap = v >= 2 && v <= 4 ? sm.g_live[v - 2] : gsuf;
+      const int hsup = (v >= 5 && v <= Lcap) ? sm.hsup[v] : 0;
+      int snap = v >= 2 && v <= 4 ? sm.g_live[v - 2] : (hot ? hsup : gsuf);
       if (act < 0) snap = 0;
       const int cnt = snap + (v <= Lcap ? sm.dhist[v] : 0);
       const int minc = a.min_corpus > 2 ? a.min_corpus : 2;
@@ -1898,6 +2074,18 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
           const int32_t* pl = sm.plp[g] + sm.g_off[g];
           nsnap = live < M ? live : M;
           for (int x = tid; x < nsnap; x += NT) gs[x] = pl[x] + l + sbase;
+        } else if (hot) {
+          if (wid == 0) {
+            const int sup = sm.hsup[l];
+            const int got = sup <= kHotSelect
+                                ? hot_select(ib, sm.hlo[l], sup, l, M, (int)r.snap_n, sbase, gs,
+                                             lane)
+                                : hot_scan(ib, ib.pl2 + sm.g_off[2], live4, sm.tail, l, M, sbase,
+                                           gs, lane);
+            if (lane == 0) sm.hn = got;
+          }
+          __syncthreads();
+          nsnap = sm.hn;
         } else {
           const int32_t* pl4 = ib.pl2 + sm.g_off[2];
           const int seg = (live4 + NT - 1) / NT;

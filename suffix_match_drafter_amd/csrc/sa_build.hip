@@ -574,6 +574,7 @@ __global__ void ng_groups_kernel(const int32_t* text, const int32_t* sa, int64_t
   for (int x = 0; x < 4; ++x) ht[h].key[x] = key[x];
   ht[h].off = goff[g];
   ht[h].cnt = goff[g + 1] - goff[g];
+  ht[h].sa_lo = (int32_t)j;
 }
 
 __global__ void iota_kernel(int32_t* p, int64_t n) {

@@ -19,13 +19,16 @@ constexpr int kNG = 3;       // probe tables for 2-, 3- and 4-grams
 constexpr int kEmptyTok = -1;
 
 // One open-addressing slot of an n-gram table: the n tokens (unused ones -1), the offset of
-// the n-gram's group in the position list and the group size.  owner == 0 marks an empty slot.
+// the n-gram's group in the position list, the group size, and the suffix-array index of the
+// group's first entry.  A group, the occurrences of the n-gram followed by a real token, is one
+// contiguous range of the suffix array (a separator sorts below every token), so it is
+// [sa_lo, sa_lo + cnt) there.  owner == 0 marks an empty slot.
 struct alignas(32) NgramSlot {
   int32_t key[4];
   int32_t off;
   int32_t cnt;
   int32_t owner;
-  int32_t pad;
+  int32_t sa_lo;
 };
 
 // One of the two corpus index buffers.  text holds the snapshot (live documents, each followed

@@ -9,7 +9,12 @@ agentic traces, which are not available here; these generators stand in for them
   fresh tokens are drawn Zipf(s=1.1) over the vocabulary;
 * the corpus imitates cross-request reuse: 2000 documents of U[200,800] tokens stitched from a
   pool of 500 shared template spans of U[16,128] tokens, with 20% of tokens replaced by fresh
-  Zipf noise.
+  Zipf noise;
+* the hot-4-gram variant imitates boilerplate-heavy traces (tool calls, agentic loops): rows and
+  documents are made of short segments, each U[0,2] Zipf noise tokens, then one of 400 shared
+  prefixes of U[2,8] tokens (drawn Zipf(s=1.1) over the pool), then one fixed 4-gram H; every
+  request's context ends with a prefix and H.  The 1M-token corpus then holds H over 10^5
+  times.
 
 All ranges are inclusive.  Randomness is numpy PCG64 seeded by SeedSequence(1000 + config id),
 spawned into independent streams (lengths, rows, templates, documents, ingest).
@@ -80,6 +85,10 @@ WORKLOADS = {
                 num_backoff=4, max_occurrences=128, mode=1, spec_factor_ppm=2_000_000,
                 spec_offset_ppm=0, min_token_prob_ppm=100_000, ring_capacity=1 << 22,
                 ingest_rows=256, ingest_len_lo=512, ingest_len_hi=2048, ingest_S=2048),
+    6: Workload(6, "hot4gram-B256-S16384-V151936-corpus1M", B=256, S=16384, T=1, n_lo=4096,
+                n_hi=16384, V=151936, p_copy=0.6, corpus=True, k=16, max_tree_depth=24,
+                num_backoff=4, max_occurrences=128, mode=1, spec_factor_ppm=2_000_000,
+                spec_offset_ppm=0, min_token_prob_ppm=100_000),
 }
 
 N_TEMPLATES = 500
@@ -131,6 +140,49 @@ def _streams(cid: int, n: int = 5):
     return [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(n)]
 
 
+HOT_PREFIXES = 400
+HOT_PREFIX_LO, HOT_PREFIX_HI = 2, 8
+HOT_NOISE_HI = 2
+HOT_DOCS = 2000
+
+
+def hot_gram(V: int) -> np.ndarray:
+    """The fixed boilerplate 4-gram of the hot-4-gram workload (four distinct mid-range ids)."""
+    return np.array([V // 7 + 11, V // 5 + 13, V // 3 + 17, V // 2 + 19], np.int32)
+
+
+@lru_cache(maxsize=2)
+def hot_prefixes(V: int):
+    r = _streams(6)[2]
+    return [zipf(r, V, int(r.integers(HOT_PREFIX_LO, HOT_PREFIX_HI + 1)))
+            for _ in range(HOT_PREFIXES)]
+
+
+def hot_row(rng: np.random.Generator, length: int, V: int, p_copy: float) -> np.ndarray:
+    """A row of boilerplate segments (noise, a shared prefix, the hot 4-gram), with spans copied
+    from earlier in the row as gen_row does, ending with a prefix and the 4-gram."""
+    H, pre = hot_gram(V), hot_prefixes(V)
+    parts, n = [], 0
+    while n < length:
+        if n >= 8 and rng.random() < p_copy:
+            m = int(rng.integers(8, 65))
+            if n >= m:
+                row = np.concatenate(parts)
+                s = int(rng.integers(0, n - m + 1))
+                parts = [row, row[s:s + m].copy()]
+                n += m
+                continue
+        seg = [zipf(rng, V, int(rng.integers(0, HOT_NOISE_HI + 1))),
+               pre[int(zipf(rng, HOT_PREFIXES, 1)[0])], H]
+        parts.extend(seg)
+        n += sum(len(x) for x in seg)
+    row = np.concatenate(parts)[:length].copy()
+    tail = np.concatenate([pre[int(zipf(rng, HOT_PREFIXES, 1)[0])], H])
+    m = min(len(tail), length)
+    row[length - m:] = tail[len(tail) - m:]
+    return row
+
+
 def make_batch(cid: int, set_index: int = 0, B: int | None = None):
     """Propose inputs for workload cid: (num_tokens [B], token_ids [B,S], sampled [B,T]).
 
@@ -142,8 +194,9 @@ def make_batch(cid: int, set_index: int = 0, B: int | None = None):
     n = r_len.integers(w.n_lo, w.n_hi + 1, size=B).astype(np.int32)
     tok = np.full((B, w.S), POISON, np.int32)
     samp = np.full((B, w.T), -1, np.int32)
+    gen = hot_row if cid == 6 else gen_row
     for b in range(B):
-        row = gen_row(r_row, int(n[b]) + w.T, w.V, w.p_copy)
+        row = gen(r_row, int(n[b]) + w.T, w.V, w.p_copy)
         tok[b, : n[b]] = row[: n[b]]
         samp[b, :] = row[n[b]: n[b] + w.T]
     return n, tok, samp
@@ -169,6 +222,24 @@ def template_docs(V: int, cid: int = 4):
     return docs
 
 
+def hot_docs(V: int):
+    """The hot-4-gram corpus: HOT_DOCS documents of U[200,800] tokens made of boilerplate
+    segments (without separators)."""
+    r = _streams(6)[3]
+    H, pre = hot_gram(V), hot_prefixes(V)
+    docs = []
+    for _ in range(HOT_DOCS):
+        target = int(r.integers(DOC_LO, DOC_HI + 1))
+        parts, got = [], 0
+        while got < target:
+            seg = [zipf(r, V, int(r.integers(0, HOT_NOISE_HI + 1))),
+                   pre[int(zipf(r, HOT_PREFIXES, 1)[0])], H]
+            parts.extend(seg)
+            got += sum(len(x) for x in seg)
+        docs.append(np.concatenate(parts)[:target].astype(np.int32))
+    return docs
+
+
 def join_docs(docs) -> np.ndarray:
     parts = []
     for d in docs:
@@ -182,6 +253,8 @@ def corpus_docs(cid: int):
     w = WORKLOADS[cid]
     if not w.corpus:
         return []
+    if cid == 6:
+        return hot_docs(w.V)
     return template_docs(w.V, cid=3 if cid == 3 else 4)
 
 
