@@ -231,7 +231,9 @@ struct Smem {
   // hot 4-gram groups: per length l >= 5, the support and the first suffix-array index of the
   // suffixes that start with the length-l tail pattern and continue with a real token
   int hsup[kMaxD + 1], hlo[kMaxD + 1];
+  int hoff[kMaxD + 1], hcnt[kMaxD + 1];  // position-list group of P_l's first 4-gram
   int ghot;  // 1 when the snapshot part of lengths >= 5 comes from them
+  int hrad[256];  // digit histogram of the hot site selection
   int hn;    // snapshot sites found by the general path's hot site pass
   const int32_t* plp[kNG];
   int wsum[NW + 1];
@@ -364,20 +366,21 @@ __device__ __noinline__ int extend4(const int32_t* text, const int* tail, int i,
 // tail pattern P_l and continue with a real token form one range of it, inside the group of
 // the 4-gram that starts P_l (whose range the probe table holds): two bound searches per length,
 // all lengths at once, give every support.  A candidate's earliest sites are then the smallest
-// positions of its range (selected from the range itself when it holds at most kHotSelect
-// entries, else found by the position-ordered scan of the 4-gram group, which stops after M of
-// them: about M * group / support occurrences).  This needs every snapshot position live, so it
+// positions of its range, selected from the range itself, or found by a position-ordered scan of
+// a 4-gram group that stops after M of them (about M * group / support entries), whichever
+// costs fewer round trips.  This needs every snapshot position live, so it
 // is not used while documents evicted since the snapshot still lie in it.
 constexpr int kHotGroup = 1024;
-constexpr int kHotSelect = 2048;
-constexpr int kHotCmp = 8;  // suffix tokens compared per round trip
+constexpr int kHotSelect = 2048;  // range entries read per selection chunk
+constexpr int kHotCmp = 16;  // suffix tokens compared per round trip
 
 // Bounds of lengths l = 5 .. Lcap: lane pair (2 (l - 5), 2 (l - 5) + 1) finds the first index of
 // the range whose suffix is >= P_l followed by token 0 (lower bound), and the first whose suffix
 // is above every suffix with prefix P_l (upper bound).  tl[x] is the context token x places
-// before the last one.  Writes sup[l] and lo[l] for 5 <= l <= Lcap.
+// before the last one.  Writes sup[l] and lo[l] for 5 <= l <= Lcap, and the 4-gram group's
+// position-list offset and size in goff[l], gcnt[l].
 __device__ __noinline__ void hot_bounds(const View ib, const int* tl, int Lcap, int snap_n,
-                                        int lane, int* sup, int* lo_out) {
+                                        int lane, int* sup, int* lo_out, int* goff, int* gcnt) {
   for (int pass = 0; pass < 2; ++pass) {
     const int idx = lane + 64 * pass;
     const int l = 5 + (idx >> 1), side = idx & 1;
@@ -388,7 +391,7 @@ __device__ __noinline__ void hot_bounds(const View ib, const int* tl, int Lcap, 
 #pragma unroll
       for (int x = 0; x < 4; ++x) key[x] = tl[l - 1 - x];
       uint32_t h = ngram_hash4(key, 4) & ib.mask;
-      int beg = 0, cnt = 0;
+      int beg = 0, cnt = 0, off = 0;
       for (;;) {
         const NgramSlot s = ib.ht2[h];
         if (s.owner == 0) break;
@@ -396,9 +399,14 @@ __device__ __noinline__ void hot_bounds(const View ib, const int* tl, int Lcap, 
             s.key[3] == key[3]) {
           beg = s.sa_lo;
           cnt = s.cnt;
+          off = s.off;
           break;
         }
         h = (h + 1) & ib.mask;
+      }
+      if (side == 0) {
+        goff[l] = off;
+        gcnt[l] = cnt;
       }
       lo = beg;
       int hi = beg + cnt;
@@ -442,51 +450,135 @@ __device__ __noinline__ void hot_bounds(const View ib, const int* tl, int Lcap, 
   }
 }
 
-// Earliest sites of a hot candidate of length l whose range [lo, lo + sup) has at most
-// kHotSelect entries: the m = min(M, sup) smallest suffix positions, found by a search for the
-// m-th smallest value, then put in order by rank; gs[r] = position + l + sbase.  Returns m.
-__device__ __noinline__ int hot_select(const View ib, int lo, int sup, int l, int M, int snap_n,
-                                       int sbase, int* gs, int lane) {
+// Earliest sites of a hot candidate of length l from its range [lo, lo + sup): the m =
+// min(M, sup) smallest suffix positions, put in order by rank; gs[r] = position + l + sbase.
+// The range is read kHotSelect entries at a time; the m smallest of a chunk and of the best so
+// far (two per lane) are those up to the m-th smallest, found digit by digit (8 bits at a time)
+// from a histogram in LDS (positions are distinct).  Returns m.
+__device__ __noinline__ int hot_select(const View ib, int* hist, int lo, int sup, int l, int M,
+                                       int snap_n, int sbase, int* gs, int lane) {
   constexpr int Q = kHotSelect / 64;
-  const int m = sup < M ? sup : M;
-  int v[Q];
+  constexpr int kNone = 0x7fffffff;
+  const int top = 32 - __builtin_clz((unsigned)(snap_n > 1 ? snap_n - 1 : 1));
+  const int shift0 = ((top + 7) / 8 - 1) * 8;  // lowest bit of the highest digit
+  int b0 = kNone, b1 = kNone, nb = 0;
+  for (int c0 = 0; c0 < sup; c0 += kHotSelect) {
+    int v[Q + 2];
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int e = lane + 64 * q;
-    v[q] = e < sup ? ib.sa[lo + e] : 0x7fffffff;
-  }
-  int a = 0, b = snap_n - 1;  // the m-th smallest lies in [a, b]
-  while (a < b) {
-    const int mid = a + ((b - a) >> 1);
-    int c = 0;
+    for (int q = 0; q < Q; ++q) {
+      const int e = c0 + lane + 64 * q;
+      v[q] = e < sup ? ib.sa[lo + e] : kNone;
+    }
+    v[Q] = b0;
+    v[Q + 1] = b1;
+    const int cn = sup - c0 < kHotSelect ? sup - c0 : kHotSelect;
+    const int m = nb + cn < M ? nb + cn : M;
+    // the m-th smallest of the chunk and the best so far
+    int prefix = 0, need = m;
+    for (int sh = shift0; sh >= 0; sh -= 8) {
 #pragma unroll
-    for (int q = 0; q < Q; ++q) c += __popcll(__ballot(v[q] <= mid));
-    if (c >= m) b = mid;
-    else a = mid + 1;
-  }
-  // the m values <= a (positions are distinct), gathered in any order, then ranked
-  int n = 0;
+      for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0;
+      wave_sync();
+      const unsigned hi_mask = sh + 8 >= 32 ? 0u : ~((1u << (sh + 8)) - 1u);
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const bool s = v[q] <= a;
-    const uint64_t bal = __ballot(s);
-    if (s) gs[n + lanes_before(bal)] = v[q];
-    n += __popcll(bal);
+      for (int q = 0; q < Q + 2; ++q) {
+        const unsigned x = (unsigned)v[q];
+        if (v[q] != kNone && (x & hi_mask) == (unsigned)prefix)
+          atomicAdd(&hist[(x >> sh) & 255u], 1);
+      }
+      wave_sync();
+      const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
+                h3 = hist[4 * lane + 3];
+      const int tot = h0 + h1 + h2 + h3;
+      const int incl = wave_incl_add(tot);
+      const int excl = incl - tot;
+      // the lane whose four digits hold the need-th value, then the digit inside it
+      const uint64_t past = __ballot(incl >= need);
+      const int owner = __builtin_ctzll(past);
+      int d = 4 * lane, below = excl;
+      if (below + h0 < need) {
+        below += h0;
+        d += 1;
+        if (below + h1 < need) {
+          below += h1;
+          d += 1;
+          if (below + h2 < need) {
+            below += h2;
+            d += 1;
+          }
+        }
+      }
+      const int dd = __builtin_amdgcn_readlane(d, owner);
+      const int bb = __builtin_amdgcn_readlane(below, owner);
+      prefix |= dd << sh;
+      need -= bb;
+      wave_sync();
+    }
+    // keep the m values <= prefix, in any order
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < Q + 2; ++q) {
+      const bool k = v[q] != kNone && v[q] <= prefix;
+      const uint64_t bal = __ballot(k);
+      if (k) gs[n + lanes_before(bal)] = v[q];
+      n += __popcll(bal);
+    }
+    wave_sync();
+    b0 = lane < m ? gs[lane] : kNone;
+    b1 = lane + 64 < m ? gs[lane + 64] : kNone;
+    nb = m;
+    wave_sync();
   }
-  wave_sync();
-  const int e0 = lane < m ? gs[lane] : 0x7fffffff;
-  const int e1 = lane + 64 < m ? gs[lane + 64] : 0x7fffffff;
+  const int m = nb;
   int r0 = 0, r1 = 0;
   for (int j = 0; j < m; ++j) {
     const int x = gs[j];
-    r0 += x < e0 ? 1 : 0;
-    r1 += x < e1 ? 1 : 0;
+    r0 += x < b0 ? 1 : 0;
+    r1 += x < b1 ? 1 : 0;
   }
   wave_sync();
-  if (lane < m) gs[r0] = e0 + l + sbase;
-  if (lane + 64 < m) gs[r1] = e1 + l + sbase;
+  if (lane < m) gs[r0] = b0 + l + sbase;
+  if (lane + 64 < m) gs[r1] = b1 + l + sbase;
   wave_sync();
   return m;
+}
+
+// Earliest sites of a hot candidate of length l with a larger range, from the position list of
+// the 4-gram that starts P_l (pl, cnt entries, each the start of a continuing occurrence of it):
+// in position order, the entries whose suffix goes on with the rest of P_l and then a real token,
+// until M are found.  Returns how many.
+__device__ __noinline__ int hot_scan_head(const View ib, const int32_t* pl, int cnt,
+                                          const int* tl, int l, int M, int snap_n, int sbase,
+                                          int* gs, int lane) {
+  const uint64_t below = lanes_below(lane);
+  int run = 0;
+  for (int base = 0; base < cnt && run < M; base += 64) {
+    const int x = base + lane;
+    const int pos = x < cnt ? pl[x] : 0;
+    bool live = x < cnt, ok = live;
+    for (int o0 = 4; o0 <= l && __ballot(live); o0 += kHotCmp) {
+      int c[kHotCmp];
+#pragma unroll
+      for (int q = 0; q < kHotCmp; ++q) {
+        const int at = pos + o0 + q < snap_n ? pos + o0 + q : snap_n - 1;
+        c[q] = ib.text[at];
+      }
+#pragma unroll
+      for (int q = 0; q < kHotCmp; ++q) {
+        const int o = o0 + q;
+        if (live && o <= l) {
+          const bool eq = o < l ? c[q] == tl[l - 1 - o] : c[q] >= 0;
+          ok = ok && eq;
+          live = eq && o < l;
+        }
+      }
+    }
+    const uint64_t bal = __ballot(ok);
+    const int rk = run + __popcll(bal & below);
+    if (ok && rk < M) gs[rk] = pos + l + sbase;
+    run += __popcll(bal);
+  }
+  return run < M ? run : M;
 }
 
 // Earliest sites of a hot candidate of length l with a larger range: the live 4-gram
@@ -506,6 +598,25 @@ __device__ __forceinline__ int hot_scan(const View ib, const int32_t* pl4, int l
     run += __popcll(bal);
   }
   return run < M ? run : M;
+}
+
+// Earliest sites of hot candidate length l: selection from its range when it is small, else the
+// position-ordered scan of whichever 4-gram group is smaller (the one that starts P_l, or the
+// tail's).  Returns how many were written to gs.
+__device__ __forceinline__ int hot_sites(const View ib, Smem& sm, const int* tl, int l, int M,
+                                         int snap_n, int sbase, const int32_t* pl4, int live4,
+                                         int* gs, int lane) {
+  const int sup = sm.hsup[l];
+  const int hcnt = sm.hcnt[l];
+  // costs in round trips: a selection chunk is one plus about as much arithmetic; a scan takes
+  // about two and a half per 64 entries, and reaches M sites after about M * group / sup of them
+  const long long sel = 2ll * ((sup + kHotSelect - 1) / kHotSelect);
+  const bool head = hcnt <= live4;
+  const long long grp = head ? hcnt : live4;
+  const long long scan = 5ll * ((long long)M * grp / sup / 64 + 1) / 2;
+  if (sel <= scan) return hot_select(ib, sm.hrad, sm.hlo[l], sup, l, M, snap_n, sbase, gs, lane);
+  if (head) return hot_scan_head(ib, ib.pl2 + sm.hoff[l], hcnt, tl, l, M, snap_n, sbase, gs, lane);
+  return hot_scan(ib, pl4, live4, tl, l, M, sbase, gs, lane);
 }
 
 // Address of the corpus token at logical position q: snapshot text below snap_end, else ring slot
@@ -1194,7 +1305,7 @@ __device__ __forceinline__ void corpus_wave_probe(const ProposeArgs& a, const Re
   const bool hot = Lcap >= 5 && live4 > kHotGroup && dead_below <= 0;
   if (lane == 0) sm.ghot = hot;
   if (hot) {
-    hot_bounds(ib, sm.gtail, Lcap, (int)r.snap_n, lane, sm.hsup, sm.hlo);
+    hot_bounds(ib, sm.gtail, Lcap, (int)r.snap_n, lane, sm.hsup, sm.hlo, sm.hoff, sm.hcnt);
   } else if (Lcap >= 5 && live4 > 0) {
     const int32_t* pl4 = ib.pl2 + sm.g_off[2];
     for (int x = lane; x < live4; x += 64) {
@@ -1250,10 +1361,8 @@ __device__ __forceinline__ void corpus_wave_sites(const ProposeArgs& a, const Re
       for (int x = lane; x < ns; x += 64) gs[x] = sm.gpl[g][x] + l + sbase;
     } else if (hot) {
       const View ib = view_of(a, r.act, r.ht_mask);
-      const int got = sup <= kHotSelect
-                          ? hot_select(ib, sm.hlo[l], sup, l, M, (int)r.snap_n, sbase, gs, lane)
-                          : hot_scan(ib, ib.pl2 + sm.g_off[2], sm.g_live[2], sm.gtail, l, M,
-                                     sbase, gs, lane);
+      const int got = hot_sites(ib, sm, sm.gtail, l, M, (int)r.snap_n, sbase,
+                                ib.pl2 + sm.g_off[2], sm.g_live[2], gs, lane);
       if (lane == 0 && got < (sup < M ? sup : M)) sm.cand_c0[ci] = got;
     } else {
       // the first M live 4-gram occurrences (position order) whose extension reaches l
@@ -1961,7 +2070,8 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     // the same choice as the corpus wavefront's (the same inputs), which stands on the fast path
     const bool hot = act >= 0 && Lcap >= 5 && live4 > kHotGroup && dead_below <= 0;
     if (!fast && hot) {
-      if (wid == 0) hot_bounds(ib, sm.tail, Lcap, (int)r.snap_n, lane, sm.hsup, sm.hlo);
+      if (wid == 0)
+        hot_bounds(ib, sm.tail, Lcap, (int)r.snap_n, lane, sm.hsup, sm.hlo, sm.hoff, sm.hcnt);
     } else if (!fast && act >= 0 && Lcap >= 5 && live4 > 0) {
       const int32_t* pl4 = ib.pl2 + sm.g_off[2];
       for (int x = tid; x < live4; x += NT) {
@@ -2076,12 +2186,8 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
           for (int x = tid; x < nsnap; x += NT) gs[x] = pl[x] + l + sbase;
         } else if (hot) {
           if (wid == 0) {
-            const int sup = sm.hsup[l];
-            const int got = sup <= kHotSelect
-                                ? hot_select(ib, sm.hlo[l], sup, l, M, (int)r.snap_n, sbase, gs,
-                                             lane)
-                                : hot_scan(ib, ib.pl2 + sm.g_off[2], live4, sm.tail, l, M, sbase,
-                                           gs, lane);
+            const int got = hot_sites(ib, sm, sm.tail, l, M, (int)r.snap_n, sbase,
+                                      ib.pl2 + sm.g_off[2], live4, gs, lane);
             if (lane == 0) sm.hn = got;
           }
           __syncthreads();
