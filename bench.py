@@ -198,6 +198,42 @@ def other_workloads(torch, sfx, W, dev, calls=200):
     return out
 
 
+def hot_gram_workload(torch, sfx, W, dev, sets=4, copies=2, calls=100):
+    """The boilerplate workload: the workload-4 shape over a 1M-token corpus in which every
+    request's last 4-gram occurs over 10^5 times; calls/s over rotating input buffers."""
+    w = W.WORKLOADS[6]
+    docs = W.corpus_docs(6)
+    d = sfx.Drafter(sfx.Config(max_batch=w.B, max_seq=w.S, max_sampled=w.T,
+                               corpus_capacity=1 << 21, **w.knobs()))
+    d.ingest_docs(docs)
+    d.rebuild()
+    bufs = []
+    for s in range(sets):
+        arrs = W.make_batch(6, set_index=s)
+        for _ in range(copies):
+            bufs.append(tuple(torch.from_numpy(x).to(dev) for x in arrs))
+    draft = torch.empty((w.B, w.k), dtype=torch.int32, device=dev)
+    nv = torch.empty((w.B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    k = [0]
+
+    def one():
+        b = bufs[k[0] % len(bufs)]
+        d.propose(b[0], b[1], b[2], draft, nv, stream)
+        k[0] += 1
+
+    event_ms(torch, stream, one, len(bufs))
+    ms = event_ms(torch, stream, one, calls)
+    d.close()
+    c = W.join_docs(docs)
+    H = W.hot_gram(w.V)
+    occ = int(((c[:-4] == H[0]) & (c[1:-3] == H[1]) & (c[2:-2] == H[2]) & (c[3:-1] == H[3]) &
+               (c[4:] >= 0)).sum())
+    return {"workload": w.name, "us_per_call": round(ms * 1e3, 1),
+            "calls_per_s": round(1e3 / ms, 1), "tail_4gram_occurrences": occ,
+            "rotating_buffers": len(bufs)}
+
+
 def ingest_under_load(torch, sfx, W, dev, warm_steps=16, steps=6, calls=10):
     """The ingest-and-rebuild workload: a ring of 2^22 tokens seeded with the template corpus;
     every step harvests 256 finished rows of U[512,2048] tokens; propose runs at B=512, S=32768,
@@ -469,6 +505,9 @@ def main():
     single = 1e3 / event_ms(torch, stream, lambda: d.propose(bufs[0][0], bufs[0][1], bufs[0][2],
                                                              draft, nv, stream), 500)
     others = other_workloads(torch, sfx, W, dev)
+    hot = hot_gram_workload(torch, sfx, W, dev)
+    log(f"[bench] hot 4-gram workload: {hot['us_per_call']} us/call "
+        f"({hot['tail_4gram_occurrences']} occurrences of the tail 4-gram)")
     copy_gbs = copy_bandwidth_gbs(torch, dev, stream)
     log(f"[bench] graph-captured {graph_cps:.0f} calls/s; one resident buffer {single:.0f} "
         f"calls/s; {others}")
@@ -556,6 +595,7 @@ def main():
                                      "padded_calls_per_s": round(bucket_pad_cps, 1)},
                   "single_buffer_calls_per_s": round(single, 1),
                   "workloads_calls_per_s": others,
+                  "hot_4gram": hot,
                   "accept_estimate_us": round(float(np.mean(est_ms)) * 1e3, 2),
                   "accept_feedback_us": round(float(np.mean(fb_ms)) * 1e3, 2),
                   "ingest_under_load": load,

@@ -286,28 +286,28 @@ __device__ __forceinline__ View view_of(const ProposeArgs& a, int act, uint32_t 
   return v;
 }
 
-// Probe of the (G+2)-gram that ends the context: its group in the position list, minus the
-// prefix of occurrences in documents evicted since the snapshot.
-template <int G>
-__device__ void probe_ngram(const View ib, const int* tail, int Lcap, long long dead_below,
-                            int* off_out, int* live_out) {
-  constexpr int ng = G + 2;
+// Probe of the (g+2)-gram that ends the context: its group in the position list, minus the
+// prefix of occurrences in documents evicted since the snapshot.  The n-gram is chosen at run
+// time (g = lane), so that the three probes of one wavefront run side by side, not one branch
+// after another.
+__device__ __forceinline__ void probe_lane(const View ib, const int* tail, int Lcap,
+                                           long long dead_below, int g, int* off_out,
+                                           int* live_out) {
+  const int ng = g + 2;
   int off = 0, live = 0;
   if (ng <= Lcap) {
     int key[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) key[x] = x < ng ? tail[ng - 1 - x] : -1;
-    const NgramSlot* ht = G == 0 ? ib.ht0 : (G == 1 ? ib.ht1 : ib.ht2);
-    const int32_t* plist = G == 0 ? ib.pl0 : (G == 1 ? ib.pl1 : ib.pl2);
+    for (int x = 0; x < 4; ++x) key[x] = x < ng ? tail[x < ng ? ng - 1 - x : 0] : -1;
+    const NgramSlot* ht = g == 0 ? ib.ht0 : (g == 1 ? ib.ht1 : ib.ht2);
+    const int32_t* plist = g == 0 ? ib.pl0 : (g == 1 ? ib.pl1 : ib.pl2);
     uint32_t h = ngram_hash4(key, ng) & ib.mask;
     int cnt = 0;
     for (;;) {
       const NgramSlot s = ht[h];
       if (s.owner == 0) break;
-      bool eq = true;
-#pragma unroll
-      for (int x = 0; x < ng; ++x) eq = eq && s.key[x] == key[x];
-      if (eq) {
+      if (s.key[0] == key[0] && s.key[1] == key[1] && s.key[2] == key[2] &&
+          s.key[3] == key[3]) {
         off = s.off;
         cnt = s.cnt;
         break;
@@ -333,12 +333,14 @@ __device__ void probe_ngram(const View ib, const int* tail, int Lcap, long long 
 }
 
 // Backward extension of a 4-gram occurrence starting at snapshot position i: the match length
-// (>= 4) against the tail, at most `cap`.  The preceding tokens are fetched kExtRound at a time,
-// all of them in flight together, so a match of up to kExtRound + 4 tokens costs one round trip.
+// (>= 4) against the tail, at most `cap`, given that the `start` tokens before it match already.
+// The preceding tokens are fetched kExtRound at a time, all of them in flight together, so a
+// match of up to kExtRound + 4 tokens costs one round trip.
 constexpr int kExtRound = 20;
-__device__ __noinline__ int extend4(const int32_t* text, const int* tail, int i, int cap) {
-  int m = 4;
-  for (int base = 0; base < cap - 4; base += kExtRound) {
+__device__ __noinline__ int extend4(const int32_t* text, const int* tail, int i, int cap,
+                                    int start = 0) {
+  int m = 4 + start;
+  for (int base = start; base < cap - 4; base += kExtRound) {
     int c[kExtRound];
 #pragma unroll
     for (int q = 0; q < kExtRound; ++q) {
@@ -617,6 +619,35 @@ __device__ __forceinline__ int hot_sites(const View ib, Smem& sm, const int* tl,
   if (sel <= scan) return hot_select(ib, sm.hrad, sm.hlo[l], sup, l, M, snap_n, sbase, gs, lane);
   if (head) return hot_scan_head(ib, ib.pl2 + sm.hoff[l], hcnt, tl, l, M, snap_n, sbase, gs, lane);
   return hot_scan(ib, pl4, live4, tl, l, M, sbase, gs, lane);
+}
+
+// Backward extension of two 4-gram occurrences at once (q0, q1: whether each exists): the four
+// tokens before each are fetched together (unconditionally, at clamped positions), and only a
+// match that runs through all four goes on with extend4.
+__device__ __forceinline__ void extend4_pair(const int32_t* text, const int* tail, int i0,
+                                             bool q0, int i1, bool q1, int cap, int* m0,
+                                             int* m1) {
+  int c[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    c[q] = text[i0 - 1 - q >= 0 ? i0 - 1 - q : 0];
+    c[4 + q] = text[i1 - 1 - q >= 0 ? i1 - 1 - q : 0];
+  }
+  bool s0 = !q0, s1 = !q1;
+  int r0 = 0, r1 = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int t = tail[4 + q];
+    const bool in = q < cap - 4;
+    s0 = s0 | !in | (i0 - 1 - q < 0) | (c[q] < 0) | (c[q] != t);
+    s1 = s1 | !in | (i1 - 1 - q < 0) | (c[4 + q] < 0) | (c[4 + q] != t);
+    r0 += s0 ? 0 : 1;
+    r1 += s1 ? 0 : 1;
+  }
+  *m0 = 4 + r0;
+  *m1 = 4 + r1;
+  if (!s0 && cap > 8) *m0 = extend4(text, tail, i0, cap, 4);
+  if (!s1 && cap > 8) *m1 = extend4(text, tail, i1, cap, 4);
 }
 
 // Address of the corpus token at logical position q: snapshot text below snap_end, else ring slot
@@ -1291,31 +1322,48 @@ __device__ __forceinline__ void corpus_wave_probe(const ProposeArgs& a, const Re
   wave_sync();
   const View ib = view_of(a, r.act, r.ht_mask);
   const long long dead_below = r.tail_w - r.snap_start;
-  if (lane == 0) probe_ngram<0>(ib, sm.gtail, Lcap, dead_below, &sm.g_off[0], &sm.g_live[0]);
-  if (lane == 1) probe_ngram<1>(ib, sm.gtail, Lcap, dead_below, &sm.g_off[1], &sm.g_live[1]);
-  if (lane == 2) probe_ngram<2>(ib, sm.gtail, Lcap, dead_below, &sm.g_off[2], &sm.g_live[2]);
+  if (lane < kNG)
+    probe_lane(ib, sm.gtail, Lcap, dead_below, lane, &sm.g_off[lane], &sm.g_live[lane]);
   wave_sync();
+  // the first M entries of all three groups in one round trip, two per lane
+  int ns[kNG], hv[kNG][2];
 #pragma unroll
   for (int g = 0; g < kNG; ++g) {
     const int32_t* pl = (g == 0 ? ib.pl0 : (g == 1 ? ib.pl1 : ib.pl2)) + sm.g_off[g];
-    const int ns = sm.g_live[g] < M ? sm.g_live[g] : M;
-    for (int x = lane; x < ns; x += 64) sm.gpl[g][x] = pl[x];
+    ns[g] = sm.g_live[g] < M ? sm.g_live[g] : M;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) hv[g][h] = lane + 64 * h < ns[g] ? pl[lane + 64 * h] : 0;
   }
+#pragma unroll
+  for (int g = 0; g < kNG; ++g)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (lane + 64 * h < ns[g]) sm.gpl[g][lane + 64 * h] = hv[g][h];
   const int live4 = sm.g_live[2];
   const bool hot = Lcap >= 5 && live4 > kHotGroup && dead_below <= 0;
   if (lane == 0) sm.ghot = hot;
   if (hot) {
     hot_bounds(ib, sm.gtail, Lcap, (int)r.snap_n, lane, sm.hsup, sm.hlo, sm.hoff, sm.hcnt);
   } else if (Lcap >= 5 && live4 > 0) {
+    // two occurrences per lane per round (the first round's positions are loaded already)
     const int32_t* pl4 = ib.pl2 + sm.g_off[2];
-    for (int x = lane; x < live4; x += 64) {
-      const int i = pl4[x];
-      const int m = extend4(ib.text, sm.gtail, i, Lcap);
-      if (x < kMaxM) {
-        sm.gm4[x] = m;
-        sm.gpl[2][x] = i;
+    for (int base = 0; base < live4; base += 128) {
+      const int x0 = base + lane, x1 = x0 + 64;
+      const bool q0 = x0 < live4, q1 = x1 < live4;
+      const int i0 = x0 < ns[2] ? hv[2][0] : (q0 ? pl4[x0] : 0);
+      const int i1 = x1 < ns[2] ? hv[2][1] : (q1 ? pl4[x1] : 0);
+      int m0, m1;
+      extend4_pair(ib.text, sm.gtail, i0, q0, i1, q1, Lcap, &m0, &m1);
+      if (q0 && x0 < kMaxM) {
+        sm.gm4[x0] = m0;
+        sm.gpl[2][x0] = i0;
       }
-      if (m >= 5) atomicAdd(&sm.ghist[m], 1);
+      if (q1 && x1 < kMaxM) {
+        sm.gm4[x1] = m1;
+        sm.gpl[2][x1] = i1;
+      }
+      if (q0 && m0 >= 5) atomicAdd(&sm.ghist[m0], 1);
+      if (q1 && m1 >= 5) atomicAdd(&sm.ghist[m1], 1);
     }
   }
 }
@@ -2058,9 +2106,8 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     if (fast) {
       // probed already
     } else if (act >= 0 && r.snap_n > 0) {
-      if (tid == 0) probe_ngram<0>(ib, sm.tail, Lcap, dead_below, &sm.g_off[0], &sm.g_live[0]);
-      if (tid == 1) probe_ngram<1>(ib, sm.tail, Lcap, dead_below, &sm.g_off[1], &sm.g_live[1]);
-      if (tid == 2) probe_ngram<2>(ib, sm.tail, Lcap, dead_below, &sm.g_off[2], &sm.g_live[2]);
+      if (tid < kNG)
+        probe_lane(ib, sm.tail, Lcap, dead_below, tid, &sm.g_off[tid], &sm.g_live[tid]);
     } else if (tid < kNG) {
       sm.g_off[tid] = 0;
       sm.g_live[tid] = 0;
