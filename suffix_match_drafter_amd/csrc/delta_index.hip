@@ -4,10 +4,11 @@
 // snapshot are not in the suffix array and are matched by position.  A request's corpus
 // candidates there start from the positions x whose token is its last context token and whose
 // previous token (still inside the delta) is its second-to-last, with a real token after x.
-// The drafter step used to find them by scanning the whole delta in every request.  These
-// passes find them once per call for every request at the same time: positions are grouped by
-// the pair (token before, token at x), for the pairs that end some request's context, and each
-// group keeps position order, which is the logical order the step's site rule needs.
+// The drafter step used to find them by scanning the whole delta in every request.  One pass
+// finds them once per call for every request at the same time: positions are grouped by the
+// pair (token before, token at x), for the pairs that end some request's context, slice by
+// slice, and each group keeps position order inside a slice, which with the slices in order is
+// the logical order the step's site rule needs.
 #include "delta_index.h"
 
 namespace sfx {
@@ -62,193 +63,122 @@ __device__ __forceinline__ unsigned long long tail_pair(const PairIndexArgs& a, 
 }
 
 constexpr int kSliceRuns = 4;  // 64-position runs whose loads a wavefront issues together
+constexpr int kSliceThreads = 64 * kPairWaves;
 
-// Pass 1 (count) and pass 3 (scatter), workgroups of kPairColsPerBlock wavefronts, one delta
-// slice each.  The count pass first builds the table of the batch's tail pairs in LDS: a group
-// is named by its first request (the smallest b with that pair), the same in every workgroup
-// whatever the order of insertion; workgroup 0 also stores every request's group for the
-// step.  The delta's end positions lo + 1 .. hi - 2 are cut into kPairCols slices of whole
-// 64-position runs, and wavefront column c takes slice c.  A position belongs to group g when
-// (token before, token at it) is group g's pair and a real token follows it.  COUNT: each
-// position's group goes to pos_group (for the scatter pass), and the slice's count per group
-// to off[g * kPairCols + c] (zeros too, so the scan sees every entry).  Otherwise off
-// holds those counts' exclusive prefix within each group and tot the group totals; the
-// workgroup derives the group starts (and workgroup 0 stores them), and the slice writes its
-// positions' offsets from lo to list[] from base[g] + off[g * kPairCols + c] on, in position
-// order within each group.  The workgroup moves its
-// block of columns to and from off[] together, so that each group's kPairColsPerBlock
-// consecutive entries are one access.
-constexpr int kSliceThreads = 64 * kPairColsPerBlock;
+// The group of end position x (ring slot sl): (token before, token at x) is the group's pair and
+// a real token follows; -1 otherwise.
+__device__ __forceinline__ int group_at(const unsigned long long* hk, const int* hg,
+                                        uint32_t mask, int p, int c, int nx) {
+  if (p < 0 || nx < 0) return -1;
+  const unsigned long long key = pair_key(p, c);
+  uint32_t h = pair_hash(key) & mask;
+  for (;;) {
+    const unsigned long long k = hk[h];
+    if (k == key) return hg[h];
+    if (k == kNoPair) return -1;
+    h = (h + 1) & mask;
+  }
+}
 
-template <bool COUNT>
-__global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArgs a) {
+// One workgroup per delta slice (see delta_index.h).  Wavefront w of slice s walks its own
+// run of the slice twice, first counting per group, then writing; cw[w][g] holds its counts,
+// then its next list entry of group g.
+__global__ __launch_bounds__(kSliceThreads) void pair_index_kernel(PairIndexArgs a) {
   __shared__ unsigned long long hk[2 * kPairMaxBatch];
   __shared__ int hg[2 * kPairMaxBatch];
-  __shared__ int cur[kPairColsPerBlock][kPairMaxBatch + 1];
-  __shared__ int gbase[kPairMaxBatch + 1];
+  __shared__ int cw[kPairWaves][kPairMaxBatch + 1];
+  __shared__ int wsum[kPairWaves];
   const uint32_t mask = a.slots - 1;
-  __shared__ int wsum[kPairColsPerBlock];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = blockIdx.x * kPairColsPerBlock + w;
+  const int sidx = blockIdx.x;
   const int ng = a.B + 1;
   long long lo, hi;
   const bool any = delta_range(a.ctl, &lo, &hi);
-  if (!COUNT && !any) return;  // uniform over the grid: the step reads no list
-  {
-    // the table (at most 2048 slots) and the block's counters, loads issued together; entry
-    // e of the block is group e / kPairColsPerBlock of column e % kPairColsPerBlock
-    constexpr int kTab = 2 * kPairMaxBatch / kSliceThreads;
-    constexpr int kCur = (kPairColsPerBlock * (kPairMaxBatch + 1) + kSliceThreads - 1) / kSliceThreads;
-    const int col0 = blockIdx.x * kPairColsPerBlock;
-    constexpr int kTot = (kPairMaxBatch + 1 + kSliceThreads - 1) / kSliceThreads;
-    constexpr int kReq = kPairMaxBatch / kSliceThreads;
-    unsigned long long rk[kReq];
-    int tc[kCur], tt[kTot];
+  // the table of the batch's tail pairs, and zero counters
+  constexpr int kReq = kPairMaxBatch / kSliceThreads;
+  unsigned long long rk[kReq];
+#pragma unroll
+  for (int j = 0; j < kReq; ++j) {
+    const int b = tid + kSliceThreads * j;
+    rk[j] = b < a.B ? tail_pair(a, b) : kNoPair;
+  }
+  for (uint32_t i = tid; i < a.slots; i += kSliceThreads) {
+    hk[i] = kNoPair;
+    hg[i] = INT32_MAX;
+  }
+  for (int e = tid; e < kPairWaves * (kPairMaxBatch + 1); e += kSliceThreads)
+    (&cw[0][0])[e] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kReq; ++j) {
+    if (rk[j] == kNoPair) continue;
+    uint32_t h = pair_hash(rk[j]) & mask;
+    for (;;) {
+      const unsigned long long prev = atomicCAS(&hk[h], kNoPair, rk[j]);
+      if (prev == kNoPair || prev == rk[j]) break;
+      h = (h + 1) & mask;
+    }
+    atomicMin(&hg[h], tid + kSliceThreads * j);
+  }
+  __syncthreads();
+  if (sidx == 0) {
 #pragma unroll
     for (int j = 0; j < kReq; ++j) {
       const int b = tid + kSliceThreads * j;
-      rk[j] = (COUNT && b < a.B) ? tail_pair(a, b) : kNoPair;
-    }
-#pragma unroll
-    for (int j = 0; j < kCur; ++j) {
-      const int e = tid + kSliceThreads * j;
-      const int g = e / kPairColsPerBlock, c = e % kPairColsPerBlock;
-      tc[j] = (!COUNT && g < ng) ? a.off[(int64_t)g * kPairCols + col0 + c] : 0;
-    }
-    // thread t holds the totals of groups kTot * t .. kTot * t + kTot - 1
-#pragma unroll
-    for (int j = 0; j < kTot; ++j) {
-      const int g = kTot * tid + j;
-      tt[j] = (!COUNT && g < ng) ? a.tot[g] : 0;
-    }
-    if (COUNT) {
-#pragma unroll
-      for (int j = 0; j < kTab; ++j) {
-        const uint32_t i = tid + kSliceThreads * j;
-        if (i < a.slots) {
-          hk[i] = kNoPair;
-          hg[i] = INT32_MAX;
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kReq; ++j) {
-        if (rk[j] == kNoPair) continue;
+      if (b >= a.B) continue;
+      int g = -1;
+      if (rk[j] != kNoPair) {
         uint32_t h = pair_hash(rk[j]) & mask;
-        for (;;) {
-          const unsigned long long prev = atomicCAS(&hk[h], kNoPair, rk[j]);
-          if (prev == kNoPair || prev == rk[j]) break;
-          h = (h + 1) & mask;
-        }
-        atomicMin(&hg[h], tid + kSliceThreads * j);
+        while (hk[h] != rk[j]) h = (h + 1) & mask;
+        g = hg[h];
       }
-      __syncthreads();
-      if (blockIdx.x == 0) {
-#pragma unroll
-        for (int j = 0; j < kReq; ++j) {
-          const int b = tid + kSliceThreads * j;
-          if (b >= a.B) continue;
-          int g = -1;
-          if (rk[j] != kNoPair) {
-            uint32_t h = pair_hash(rk[j]) & mask;
-            while (hk[h] != rk[j]) h = (h + 1) & mask;
-            g = hg[h];
-          }
-          a.group[b] = g;
-        }
-      }
-    } else {
-      // group starts: exclusive prefix of the totals over the workgroup
-      int sum = 0;
-#pragma unroll
-      for (int j = 0; j < kTot; ++j) sum += tt[j];
-      int incl = sum;
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += y;
-      }
-      if (lane == 63) wsum[w] = incl;
-      __syncthreads();
-      int run = incl - sum;
-      for (int v = 0; v < w; ++v) run += wsum[v];
-#pragma unroll
-      for (int j = 0; j < kTot; ++j) {
-        const int g = kTot * tid + j;
-        if (g < ng) {
-          gbase[g] = run;
-          if (blockIdx.x == 0) a.base[g] = run;
-        }
-        run += tt[j];
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int j = 0; j < kCur; ++j) {
-      const int e = tid + kSliceThreads * j;
-      const int g = e / kPairColsPerBlock, c = e % kPairColsPerBlock;
-      if (g < ng) cur[c][g] = COUNT ? tc[j] : tc[j] + gbase[g];
+      a.group[b] = g;
     }
   }
-  __syncthreads();
-  const long long nd = any ? hi - lo - 2 : 0;
-  if (nd > 0) {
-    const long long seg = ((nd + kPairCols - 1) / kPairCols + 63) / 64 * 64;
-    const long long xb = lo + 1 + (long long)col * seg;
-    const long long xe = xb + seg < hi - 1 ? xb + seg : hi - 1;
-    const int cap = (int)a.ring_cap;
-    int s = xb < xe ? (int)((xb + lane) % a.ring_cap) : 0;  // slot of this lane's position
-    for (long long x0 = xb; x0 < xe; x0 += 64 * kSliceRuns) {
-      // COUNT: the tokens around each position; otherwise the group the count pass stored
+  if (!any) return;  // uniform over the grid: the step reads no list
+  // this slice's end positions [xb, xe) and this wavefront's run [wb, we) of them
+  const long long nd = hi - lo - 2;
+  const long long sg = pair_seg(nd);
+  const long long xb = lo + 1 + (long long)sidx * sg;
+  const long long xe = xb + sg < hi - 1 ? xb + sg : hi - 1;
+  const long long wn = ((sg + kPairWaves - 1) / kPairWaves + 63) / 64 * 64;
+  const long long wb = xb + (long long)w * wn;
+  const long long we = wb + wn < xe ? wb + wn : xe;
+  const int cap = (int)a.ring_cap;
+  const int s0 = wb < we ? (int)((wb + lane) % a.ring_cap) : 0;  // slot of the lane's position
+  uint32_t* part = a.list + (size_t)sidx * (size_t)sg;
+  for (int pass = 0; pass < 2; ++pass) {
+    int s = s0;
+    for (long long x0 = wb; x0 < we; x0 += 64 * kSliceRuns) {
       int p[kSliceRuns], c[kSliceRuns], nx[kSliceRuns];
 #pragma unroll
       for (int u = 0; u < kSliceRuns; ++u) {
-        const long long x = x0 + 64 * u + lane;
-        const bool in = x < xe;
-        if (COUNT) {
-          const int sp = s == 0 ? cap - 1 : s - 1;
-          const int sn = s + 1 == cap ? 0 : s + 1;
-          p[u] = in ? a.ring[sp] : -1;
-          c[u] = in ? a.ring[s] : -1;
-          nx[u] = in ? a.ring[sn] : -1;
-          s += 64;
-          while (s >= cap) s -= cap;
-        } else {
-          p[u] = in ? (int)(int16_t)a.pos_group[x - lo - 1] : -1;
-        }
+        const bool in = x0 + 64 * u + lane < we;
+        const int sp = s == 0 ? cap - 1 : s - 1;
+        const int sn = s + 1 == cap ? 0 : s + 1;
+        p[u] = in ? a.ring[sp] : -1;
+        c[u] = in ? a.ring[s] : -1;
+        nx[u] = in ? a.ring[sn] : -1;
+        s += 64;
+        while (s >= cap) s -= cap;
       }
 #pragma unroll
       for (int u = 0; u < kSliceRuns; ++u) {
         const long long x = x0 + 64 * u + lane;
-        int g = -1;
-        if (!COUNT) {
-          g = p[u];
-        } else if (p[u] >= 0 && nx[u] >= 0) {
-          const unsigned long long key = pair_key(p[u], c[u]);
-          uint32_t h = pair_hash(key) & mask;
-          for (;;) {
-            const unsigned long long k = hk[h];
-            if (k == key) {
-              g = hg[h];
-              break;
-            }
-            if (k == kNoPair) break;
-            h = (h + 1) & mask;
-          }
-        }
-        if (COUNT) {
-          if (x < xe) a.pos_group[x - lo - 1] = (uint16_t)g;
-          if (g >= 0) atomicAdd(&cur[w][g], 1);
+        const int g = group_at(hk, hg, mask, p[u], c[u], nx[u]);
+        if (pass == 0) {
+          if (g >= 0) atomicAdd(&cw[w][g], 1);
         } else {
           // one group at a time: the lanes of group gg take consecutive list entries
           uint64_t pend = __ballot(g >= 0);
           while (pend) {
             const int gg = __builtin_amdgcn_readlane(g, __builtin_ctzll(pend));
             const uint64_t same = __ballot(g == gg);
-            const int base = cur[w][gg];
-            if (g == gg) a.list[base + __popcll(same & ((1ull << lane) - 1))] = (uint32_t)(x - lo);
+            const int base = cw[w][gg];
+            if (g == gg) part[base + __popcll(same & ((1ull << lane) - 1))] = (uint32_t)(x - lo);
             __builtin_amdgcn_wave_barrier();
-            if (lane == 0) cur[w][gg] = base + __popcll(same);
+            if (lane == 0) cw[w][gg] = base + __popcll(same);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -257,53 +187,48 @@ __global__ __launch_bounds__(kSliceThreads) void pair_slices_kernel(PairIndexArg
         }
       }
     }
-  }
-  if (COUNT) {
+    if (pass == 1) break;
     __syncthreads();
-    const int col0 = blockIdx.x * kPairColsPerBlock;
-    for (int e = tid; e < kPairColsPerBlock * ng; e += kSliceThreads) {
-      const int g = e / kPairColsPerBlock, c = e % kPairColsPerBlock;
-      a.off[(int64_t)g * kPairCols + col0 + c] = cur[c][g];
+    // per group: its count in the slice, its offset (the counts of the groups before it), and
+    // each wavefront's first entry (after the wavefronts before it); thread t takes groups
+    // kPer * t .. kPer * t + kPer - 1
+    constexpr int kPer = (kPairMaxBatch + 1 + kSliceThreads - 1) / kSliceThreads;
+    int cnt[kPer], sum = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int g = kPer * tid + k;
+      cnt[k] = 0;
+      if (g < ng)
+#pragma unroll
+        for (int v = 0; v < kPairWaves; ++v) cnt[k] += cw[v][g];
+      sum += cnt[k];
     }
-  }
-}
-
-// Pass 2 (one 256-thread workgroup per group g <= B): the exclusive prefix of the group's
-// per-slice counts over the slices, in place, and its total.
-constexpr int kRowThreads = 256;
-constexpr int kRowItems = kPairCols / kRowThreads;
-
-__global__ __launch_bounds__(kRowThreads) void pair_rowscan_kernel(PairIndexArgs a) {
-  __shared__ int wsum[kRowThreads / 64];
-  long long lo, hi;
-  if (!delta_range(a.ctl, &lo, &hi)) return;  // uniform over the grid: the step reads no list
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int32_t* row = a.off + (int64_t)blockIdx.x * kPairCols + kRowItems * tid;
-  int v[kRowItems];
+    int incl = sum;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += y;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int v = 0; v < w; ++v) run += wsum[v];
 #pragma unroll
-  for (int j = 0; j < kRowItems; ++j) v[j] = row[j];
-  int sum = 0;
+    for (int k = 0; k < kPer; ++k) {
+      const int g = kPer * tid + k;
+      if (g < ng) {
+        a.seg[(size_t)sidx * ng + g] = PairSeg{run, cnt[k]};
+        int b = run;
 #pragma unroll
-  for (int j = 0; j < kRowItems; ++j) sum += v[j];
-  int incl = sum;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += y;
+        for (int v = 0; v < kPairWaves; ++v) {
+          const int t = cw[v][g];
+          cw[v][g] = b;
+          b += t;
+        }
+      }
+      run += cnt[k];
+    }
+    __syncthreads();
   }
-  if (lane == 63) wsum[w] = incl;
-  __syncthreads();
-  int run = incl - sum, total = 0;
-  for (int u = 0; u < kRowThreads / 64; ++u) {
-    if (u < w) run += wsum[u];
-    total += wsum[u];
-  }
-#pragma unroll
-  for (int j = 0; j < kRowItems; ++j) {
-    const int x = v[j];
-    row[j] = run;
-    run += x;
-  }
-  if (tid == 0) a.tot[blockIdx.x] = total;
 }
 
 }  // namespace
@@ -313,10 +238,7 @@ hipError_t launch_pair_index(const PairIndexArgs& a, hipStream_t st) {
   if (a.B > kPairMaxBatch || a.slots < 2u * (uint32_t)a.B || a.slots > 2u * kPairMaxBatch ||
       (a.slots & (a.slots - 1)) != 0)
     return hipErrorInvalidValue;
-  const dim3 grid(kPairCols / kPairColsPerBlock);
-  hipLaunchKernelGGL((pair_slices_kernel<true>), grid, dim3(kSliceThreads), 0, st, a);
-  hipLaunchKernelGGL(pair_rowscan_kernel, dim3(a.B + 1), dim3(kRowThreads), 0, st, a);
-  hipLaunchKernelGGL((pair_slices_kernel<false>), grid, dim3(kSliceThreads), 0, st, a);
+  hipLaunchKernelGGL(pair_index_kernel, dim3(kPairSlices), dim3(kSliceThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // propose.h -- launch interface of the drafter-step kernels (internal to libsfx).
 #pragma once
 
+#include "delta_index.h"
 #include "sfx_internal.h"
 
 namespace sfx {
@@ -26,8 +27,7 @@ struct ProposeArgs {
   // per-call index of the delta's tail-pair occurrences (delta_index.h), or nullptr, in which
   // case a request scans the whole delta
   const int32_t* pair_group;
-  const int32_t* pair_base;  // [B + 1] start of each group's entries in pair_list
-  const int32_t* pair_tot;   // [B + 1] their number
+  const PairSeg* pair_seg;   // [kPairSlices * (B + 1)] each slice's entries of each group
   const uint32_t* pair_list;
   // the context's sticky error word (kErrSyncTimeout is raised here)
   uint32_t* err;

@@ -746,6 +746,19 @@ __device__ __forceinline__ void delta_scan_wave(const ProposeArgs& a, long long 
   }
 }
 
+// Listed delta entries: wavefront w of a request walks the request's group in slices
+// w * kListSlices .. (w + 1) * kListSlices - 1, one running entry number v over them.  Lane j <
+// kListSlices holds slice j's first entry number (non-decreasing in j) in `first` and the
+// difference between its list index and its entry number in `shift`; entry v is in the last
+// slice whose first entry number is at most v.  Every lane of the wavefront must take part.
+constexpr int kListSlices = kPairSlices / NW;
+__device__ __forceinline__ int list_index(int v, int first, int shift) {
+  int j = 0;
+#pragma unroll
+  for (int q = 1; q < kListSlices; ++q) j += v >= __builtin_amdgcn_readlane(first, q) ? 1 : 0;
+  return v + __builtin_amdgcn_ds_bpermute(4 * j, shift);
+}
+
 constexpr int kListRound = 4;    // tokens compared per round trip when extending listed entries
 constexpr int kListBatches = 4;  // 64-entry batches whose first loads are issued together
 
@@ -760,15 +773,18 @@ constexpr int kListBatches = 4;  // 64-entry batches whose first loads are issue
 template <typename F>
 __device__ __forceinline__ void delta_list_wave(const ProposeArgs& a, long long dlo, long long i0,
                                                 long long i1, int Lcap, const int* tail,
-                                                int lane, F&& f) {
+                                                int lane, int lfirst, int lshift, F&& f) {
   const int cap = (int)a.ring_cap;
   const int dslot = (int)(dlo % a.ring_cap);
   for (long long e0 = i0; e0 < i1; e0 += 64 * kListBatches) {
     uint32_t o[kListBatches];
+    int li[kListBatches];
+#pragma unroll
+    for (int u = 0; u < kListBatches; ++u) li[u] = list_index((int)(e0 + 64 * u + lane), lfirst, lshift);
 #pragma unroll
     for (int u = 0; u < kListBatches; ++u) {
       const long long i = e0 + 64 * u + lane;
-      o[u] = i < i1 ? a.pair_list[i] : 0u;
+      o[u] = i < i1 ? a.pair_list[li[u]] : 0u;
     }
     int sl[kListBatches], lim[kListBatches], nxt[kListBatches];
 #pragma unroll
@@ -1886,6 +1902,8 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   constexpr int kCtlWords = (int)(sizeof(Ctl) / 4);
   static_assert(kCtlWords <= 64 && sizeof(Ctl) % 8 == 0, "control block in one wavefront");
   const int nraw = a.ntns[b];
+  // the request's delta group, read now so that it has landed when the delta walk needs it
+  const int pgroup = a.pair_group != nullptr ? a.pair_group[b] : -1;
   const int sl = lane < a.T ? smp[lane] : -1;
   const int cw = a.ctl != nullptr && lane < kCtlWords
                      ? reinterpret_cast<const int*>(a.ctl)[lane] : 0;
@@ -2083,6 +2101,15 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
 
   // ---------------------------------------------------------------- 2. global (general path)
   if (r.has && (!fast || r.delta) && Lcap >= 2) {
+    // this wavefront's slices of the request's delta group (read before the barrier, so that
+    // they land while the local candidates finish)
+    const long long dlo = r.delta_lo, dhi = r.delta_hi;
+    const bool has_delta = dhi - dlo > 1;
+    const bool listed = has_delta && a.pair_group != nullptr;
+    const int sj = wid * kListSlices + lane;
+    const PairSeg pseg = (listed && pgroup >= 0 && lane < kListSlices)
+                             ? a.pair_seg[(size_t)sj * (size_t)(a.B + 1) + pgroup]
+                             : PairSeg{0, 0};
     // The local sites are gathered and the hit lists are dead.  With a live snapshot and a
     // delta, the corpus wavefront has probed the snapshot beside the local phase (its results
     // stand).
@@ -2127,26 +2154,27 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       }
     }
     // delta: documents appended since the live snapshot.  With the per-call pair index,
-    // wavefront w owns entries [sb, se) of the request's group list; without it, the end
-    // positions [sb, se), scanned by brute force.  It keeps its occurrences of length >= 2 in
+    // wavefront w owns the request's group entries in its slices (numbered [sb, se)); without
+    // it, the end positions [sb, se), scanned by brute force.  It keeps its occurrences of length >= 2 in
     // LDS, in position order (coordinate offset from sb << 6 | length - 2; the context hit
     // lists are dead by now), at most H of them, plus a length histogram.
-    const long long dlo = r.delta_lo, dhi = r.delta_hi;
-    const bool has_delta = dhi - dlo > 1;
-    const bool listed = has_delta && a.pair_group != nullptr;
     long long sb, se;
+    int lfirst = 0, lshift = 0;  // slice table of the listed walk (list_index)
     if (listed) {
-      const int g = a.pair_group[b];
-      const long long i0 = g >= 0 ? a.pair_base[g] : 0;
-      const long long i1 = g >= 0 ? i0 + a.pair_tot[g] : 0;
-      const long long per = ((i1 - i0 + NW - 1) / NW + 63) / 64 * 64;
-      sb = i0 + (long long)wid * per < i1 ? i0 + (long long)wid * per : i1;
-      se = sb + per < i1 ? sb + per : i1;
+      // this wavefront's slices of the request's group: entries numbered 0 .. se - 1
+      const long long sg = pair_seg(dhi - dlo - 2);
+      const PairSeg e = pseg;
+      const int incl = wave_incl_add(e.cnt);
+      lfirst = incl - e.cnt;
+      lshift = (int)((long long)sj * sg + e.off - lfirst);
+      sb = 0;
+      se = __builtin_amdgcn_readlane(incl, 63);
     } else {
       const long long dseg = has_delta ? ((dhi - 1 - dlo + NW - 1) / NW + 63) / 64 * 64 : 0;
       sb = dlo + (long long)wid * dseg;
       se = has_delta ? (sb + dseg < dhi - 1 ? sb + dseg : dhi - 1) : sb;
     }
+    PHASE(11);  // (slots 11-15 of the voters are the vote's own; wavefronts from 2 nb on keep these)
     const size_t dbase = hpos_offset(STAGED, a.S, a.T);
     const int H = (int)((vote_offset(STAGED, a.S, a.T, true) - dbase) / (4 * NW));
     uint32_t* recs = reinterpret_cast<uint32_t*>(dyn + dbase) + wid * H;
@@ -2168,7 +2196,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
         }
         return true;
       };
-      if (listed) delta_list_wave(a, dlo, sb, se, Lcap, sm.tail, lane, keep);
+      if (listed) delta_list_wave(a, dlo, sb, se, Lcap, sm.tail, lane, lfirst, lshift, keep);
       else delta_scan_wave(a, dlo, sb, se, Lcap, sm.tail, lane, keep);
       wave_sync();
       // this wavefront's suffix sums: wsuf[w][v] = its occurrences of length >= v, v = lane + 1
@@ -2178,6 +2206,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       sm.wsuf[wid][lane + 1] = __builtin_amdgcn_readlane(incl, 63) - incl + h;
     }
     __syncthreads();
+    PHASE(12);
     if (has_delta && wid == 0) {
       int sum = 0;
       for (int w = 0; w < NW; ++w) sum += sm.wsuf[w][lane + 1];
@@ -2217,6 +2246,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       }
     }
     __syncthreads();
+    PHASE(13);
     // earliest sites: live snapshot occurrences in position order, then delta occurrences
     for (int ti = 0; ti < nb; ++ti) {
       const int ci = nb + ti;
@@ -2236,6 +2266,35 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
             const int got = hot_sites(ib, sm, sm.tail, l, M, (int)r.snap_n, sbase,
                                       ib.pl2 + sm.g_off[2], live4, gs, lane);
             if (lane == 0) sm.hn = got;
+          }
+          __syncthreads();
+          nsnap = sm.hn;
+        } else if (fast) {
+          // the corpus wavefront has the first kMaxM occurrences' extension lengths: one
+          // wavefront walks the occurrences in position order, extending only past those
+          if (wid == 0) {
+            const int32_t* pl4 = ib.pl2 + sm.g_off[2];
+            const uint64_t below = lanes_below(lane);
+            int run = 0;
+            for (int base = 0; base < live4 && run < M; base += 64) {
+              const int x = base + lane;
+              bool q = false;
+              int i = 0;
+              if (x < live4) {
+                if (x < kMaxM) {
+                  i = sm.gpl[2][x];
+                  q = sm.gm4[x] >= l;
+                } else {
+                  i = pl4[x];
+                  q = extend4(ib.text, sm.tail, i, l) >= l;
+                }
+              }
+              const uint64_t bal = __ballot(q);
+              const int rk = run + __popcll(bal & below);
+              if (q && rk < M) gs[rk] = i + 4 + sbase;
+              run += __popcll(bal);
+            }
+            if (lane == 0) sm.hn = run < M ? run : M;
           }
           __syncthreads();
           nsnap = sm.hn;
@@ -2271,10 +2330,10 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
           const bool q = e < kept && (int)(rc & 63u) + 2 >= l;
           const uint64_t bal = __ballot(q);
           const int rk = off + lanes_before(bal);
-          if (q && rk < M) {
-            const long long u = sb + (long long)(rc >> 6);
-            gs[rk] = (int)((listed ? dlo + (long long)a.pair_list[u] : u) + 1 - r.tail_w);
-          }
+          const long long u = sb + (long long)(rc >> 6);
+          const int li = listed ? list_index((int)u, lfirst, lshift) : 0;  // (every lane)
+          if (q && rk < M)
+            gs[rk] = (int)((listed ? dlo + (long long)a.pair_list[li] : u) + 1 - r.tail_w);
           off += __popcll(bal);
         }
         if (nrec > H && off < M) {
@@ -2287,7 +2346,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
             off += __popcll(bal);
             return off < M;
           };
-          if (listed) delta_list_wave(a, dlo, from, se, Lcap, sm.tail, lane, site);
+          if (listed) delta_list_wave(a, dlo, from, se, Lcap, sm.tail, lane, lfirst, lshift, site);
           else delta_scan_wave(a, dlo, from, se, Lcap, sm.tail, lane, site);
         }
       }
@@ -2297,6 +2356,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     __syncthreads();
   }
 
+  PHASE(14);
   // ---------------------------------------------------------------- 3. votes
   // One call site for every vote: wavefront ci votes candidate ci.  Without the general path,
   // local candidate t is voted right after its sites, and corpus candidate nb + t as soon as the
@@ -2408,6 +2468,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
                                   sm.cand_out[ci], &nout, &snum);
         };
         static_assert(kColSites == 8, "column instantiations");
+        static_assert(kPairSlices % NW == 0 && kListSlices <= 64, "listed slices per wavefront");
         if (c0 <= 1) fin = run(std::integral_constant<int, 1>{});
         else if (c0 <= 2) fin = run(std::integral_constant<int, 2>{});
         else if (c0 <= 4) fin = run(std::integral_constant<int, 4>{});

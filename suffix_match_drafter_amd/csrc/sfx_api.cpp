@@ -93,11 +93,8 @@ struct sfx_ctx {
   int active_host = -1;  // host mirror of the live buffer
   // per-call pair index of the delta (delta_index.h); absent above kPairMaxBatch rows
   int32_t* pair_group = nullptr;
-  int32_t* pair_off = nullptr;
-  int32_t* pair_tot = nullptr;
-  int32_t* pair_base = nullptr;
+  PairSeg* pair_seg = nullptr;
   uint32_t* pair_list = nullptr;
-  uint16_t* pair_pos = nullptr;
   uint32_t pair_slots = 0;
   // Ingest calls so far, and how many of them the live index covers (that of the snapshot
   // being built, for an asynchronous rebuild).  While they differ the corpus may hold a delta,
@@ -206,11 +203,8 @@ void free_ctx(sfx_ctx* c) {
   }
   f(c->sa_ws);
   f(c->pair_group);
-  f(c->pair_off);
-  f(c->pair_tot);
-  f(c->pair_base);
+  f(c->pair_seg);
   f(c->pair_list);
-  f(c->pair_pos);
   free_poll(&c->poll);
   if (c->side) (void)hipStreamDestroy(c->side);
   if (c->ev_snap) (void)hipEventDestroy(c->ev_snap);
@@ -372,11 +366,8 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
       const int mb = cfg->max_batch;
       c->pair_slots = pair_slots(mb);
       ok = al((void**)&c->pair_group, 4 * (size_t)mb) &&
-           al((void**)&c->pair_off, 4 * (size_t)(mb + 1) * kPairCols) &&
-           al((void**)&c->pair_tot, 4 * (size_t)(mb + 1)) &&
-           al((void**)&c->pair_base, 4 * (size_t)(mb + 1)) &&
-           al((void**)&c->pair_list, 4 * (size_t)c->cap) &&
-           al((void**)&c->pair_pos, 2 * (size_t)c->cap);
+           al((void**)&c->pair_seg, sizeof(PairSeg) * (size_t)(mb + 1) * kPairSlices) &&
+           al((void**)&c->pair_list, 4 * pair_list_entries(c->cap));
     }
     if (!ok) {
       free_ctx(c);
@@ -505,15 +496,11 @@ static int propose_k(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
     p.ring_cap = c->cap;
     p.slots = c->pair_slots;
     p.group = c->pair_group;
-    p.off = c->pair_off;
-    p.tot = c->pair_tot;
-    p.base = c->pair_base;
+    p.seg = c->pair_seg;
     p.list = c->pair_list;
-    p.pos_group = c->pair_pos;
     HIP_OR_RETURN(launch_pair_index(p, (hipStream_t)stream), "pair index launch");
     a.pair_group = c->pair_group;
-    a.pair_base = c->pair_base;
-    a.pair_tot = c->pair_tot;
+    a.pair_seg = c->pair_seg;
     a.pair_list = c->pair_list;
   }
   HIP_OR_RETURN(launch_propose(a, (hipStream_t)stream), "propose launch");
