@@ -381,7 +381,7 @@ constexpr int kHotCmp = 16;  // suffix tokens compared per round trip
 // is above every suffix with prefix P_l (upper bound).  tl[x] is the context token x places
 // before the last one.  Writes sup[l] and lo[l] for 5 <= l <= Lcap, and the 4-gram group's
 // position-list offset and size in goff[l], gcnt[l].
-__device__ __noinline__ void hot_bounds(const View ib, const int* tl, int Lcap, int snap_n,
+__device__ __forceinline__ void hot_bounds(const View ib, const int* tl, int Lcap, int snap_n,
                                         int lane, int* sup, int* lo_out, int* goff, int* gcnt) {
   for (int pass = 0; pass < 2; ++pass) {
     const int idx = lane + 64 * pass;
@@ -457,7 +457,7 @@ __device__ __noinline__ void hot_bounds(const View ib, const int* tl, int Lcap, 
 // The range is read kHotSelect entries at a time; the m smallest of a chunk and of the best so
 // far (two per lane) are those up to the m-th smallest, found digit by digit (8 bits at a time)
 // from a histogram in LDS (positions are distinct).  Returns m.
-__device__ __noinline__ int hot_select(const View ib, int* hist, int lo, int sup, int l, int M,
+__device__ __forceinline__ int hot_select(const View ib, int* hist, int lo, int sup, int l, int M,
                                        int snap_n, int sbase, int* gs, int lane) {
   constexpr int Q = kHotSelect / 64;
   constexpr int kNone = 0x7fffffff;
@@ -549,7 +549,7 @@ __device__ __noinline__ int hot_select(const View ib, int* hist, int lo, int sup
 // the 4-gram that starts P_l (pl, cnt entries, each the start of a continuing occurrence of it):
 // in position order, the entries whose suffix goes on with the rest of P_l and then a real token,
 // until M are found.  Returns how many.
-__device__ __noinline__ int hot_scan_head(const View ib, const int32_t* pl, int cnt,
+__device__ __forceinline__ int hot_scan_head(const View ib, const int32_t* pl, int cnt,
                                           const int* tl, int l, int M, int snap_n, int sbase,
                                           int* gs, int lane) {
   const uint64_t below = lanes_below(lane);
