@@ -1,9 +1,10 @@
 // sfx_api.cpp -- host side of libsfx: the C-ABI declared in include/sfx.h.
 //
 // Host code only validates, allocates at creation, and enqueues kernels.  The propose and ingest
-// paths never read device memory from the host.  The index rebuild is driven by the host
-// (one stream wait per doubling round), either inline on the caller's stream (sfx_rebuild) or
-// on a library-owned worker thread and side stream (sfx_rebuild_async + sfx_poll).
+// paths never read device memory from the host.  The index rebuild is enqueued by the host,
+// which follows the device's count of suffixes left to sort two doubling rounds late through
+// pinned memory (no wait per round), either inline on the caller's stream (sfx_rebuild) or on
+// a library-owned worker thread and side stream (sfx_rebuild_async + sfx_poll).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
