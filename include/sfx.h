@@ -236,9 +236,9 @@ int sfx_corpus_snapshot(sfx_ctx* ctx, int32_t* text_out, int64_t cap, int64_t* n
                         void* stream);
 
 /* Per-slot acceptance estimate (vLLM docs "Suffix Decoding", Use adaptive verification at
- * higher concurrency: the speculator reports a per-slot acceptance estimate learned online by
- * draft source, match length and position, and the scheduler verifies only the slots worth
- * their cost).  Every sfx_propose records, per row b < B, its winning candidate: source (0 the
+ * higher concurrency: a running estimate of each draft position's chance of acceptance, keyed
+ * by the draft's source, its match length and the position, lets the scheduler skip verifying
+ * positions that are unlikely to pay off).  Every sfx_propose records, per row b < B, its winning candidate: source (0 the
  * request's own context, 1 the corpus), match length, and num_valid (no winner: nothing).
  * The context keeps a table of counts per (source, length 0..64, slot 0..31): proposed and
  * accepted.

@@ -1,7 +1,8 @@
 """Per-slot acceptance estimate, learned online (oracle side; test infrastructure only).
 
-vLLM docs "Suffix Decoding", Use adaptive verification at higher concurrency: the speculator
-reports a per-slot acceptance estimate learned online by draft source, match length and position.
+vLLM docs "Suffix Decoding", Use adaptive verification at higher concurrency: a running
+estimate of each draft position's chance of acceptance, keyed by the draft's source, its match
+length and the position.
 
 Readings taken:
   * a draft's source is its winning candidate's: 0 for the request's own context, 1 for the

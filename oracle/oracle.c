@@ -19,8 +19,9 @@
 
 /* Context of one request.
  * SuffixGPU page, Quickstart: the resident state is token_ids[B,S], num_tokens_no_spec[B] and the
- * last verifier output sampled_token_ids[B,T], -1 padded.  The RFC page (Summary, Design) says
- * drafts come from the previous step's device sampled ids.  Reading: the context is the row
+ * last verifier output sampled_token_ids[B,T], -1 padded.  The RFC page (Summary, Design) has
+ * the draft built from the sampled ids of the step before, as they sit on the device.
+ * Reading: the context is the row
  * prefix of length n (clamped to [0,S]) followed by the leading non-negative sampled ids. */
 int32_t orc_context(int32_t S, int32_t T, int32_t n_raw, const int32_t* row, const int32_t* samp,
                     int32_t* ctx, int32_t* t_out) {
@@ -48,9 +49,10 @@ void orc_match_back(const int32_t* ctx, int32_t L, int32_t D, int32_t* mb) {
   }
 }
 
-/* Corpus match lengths.  vLLM docs "Suffix Decoding", Model Runner V2: each request looks up
- * corpus positions by its last 2 and last 4 tokens and extends them to the longest suffix
- * match; SuffixGPU page, How it works step 2: the same tail is searched in the shared corpus.
+/* Corpus match lengths.  vLLM docs "Suffix Decoding", Model Runner V2: the corpus positions
+ * that share the request's final two and final four tokens are found first and then grown
+ * backwards as far as the match goes; SuffixGPU page, How it works step 2: the same tail is
+ * searched in the shared corpus.
  * Reading: the corpus is the live documents in ingest order, each followed by one -1; a match
  * never covers a -1 and must be followed by a real token (C[e+1] >= 0), so it has a
  * continuation.  m[e] (e = 0..N-1) = that backward match length at end e, capped at

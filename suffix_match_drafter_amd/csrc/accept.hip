@@ -1,8 +1,9 @@
 // accept.hip -- per-slot acceptance estimate of the drafts, learned online.
 //
-// vLLM docs "Suffix Decoding", Use adaptive verification at higher concurrency: the speculator
-// reports a per-slot acceptance estimate learned online by draft source, match length and
-// position, so that the scheduler verifies only the slots worth their cost.
+// vLLM docs "Suffix Decoding", Use adaptive verification at higher concurrency: the drafter
+// keeps, for each draft position, a running estimate of how likely it is to be accepted,
+// keyed by where the draft came from and how long its match was; the scheduler uses it to
+// skip verifying positions that are unlikely to pay off.
 //
 // sfx_propose records each request's winner (source: local or corpus; its match length; the
 // number of drafted tokens).  Verifier feedback then adds, for every drafted slot d, one

@@ -1,6 +1,6 @@
 """Per-slot acceptance estimate (vLLM docs "Suffix Decoding", Use adaptive verification at
-higher concurrency: an estimate per draft slot, learned online by draft source, match length and
-position).
+higher concurrency: a running estimate per draft position, keyed by the draft's source, its match
+length and the position).
 
 Each step proposes on the GPU and in the oracle (whose row information names the winning
 candidate), then compares the estimates with the oracle's acceptance model, feeds the same
