@@ -95,6 +95,31 @@ __global__ __launch_bounds__(kSliceThreads) void pair_index_kernel(PairIndexArgs
   const int ng = a.B + 1;
   long long lo, hi;
   const bool any = delta_range(a.ctl, &lo, &hi);
+  // this slice's end positions [xb, xe) and this wavefront's run [wb, we) of them
+  const long long nd = any ? hi - lo - 2 : 0;
+  const long long sg = pair_seg(nd);
+  const long long xb = lo + 1 + (long long)sidx * sg;
+  const long long xe = xb + sg < hi - 1 ? xb + sg : hi - 1;
+  const long long wn = ((sg + kPairWaves - 1) / kPairWaves + 63) / 64 * 64;
+  const long long wb = xb + (long long)w * wn;
+  const long long we = wb + wn < xe ? wb + wn : xe;
+  const int cap = (int)a.ring_cap;
+  const int s0 = any && wb < we ? (int)((wb + lane) % a.ring_cap) : 0;  // the lane's first slot
+  // the first kSliceRuns runs' tokens, loaded before the table is built so that both wait
+  // together; their groups are kept for the writing walk
+  int p1[kSliceRuns], c1[kSliceRuns], n1[kSliceRuns], g1[kSliceRuns];
+  int s1 = s0;
+#pragma unroll
+  for (int u = 0; u < kSliceRuns; ++u) {
+    const bool in = wb + 64 * u + lane < we;
+    const int sp = s1 == 0 ? cap - 1 : s1 - 1;
+    const int sn = s1 + 1 == cap ? 0 : s1 + 1;
+    p1[u] = in ? a.ring[sp] : -1;
+    c1[u] = in ? a.ring[s1] : -1;
+    n1[u] = in ? a.ring[sn] : -1;
+    s1 += 64;
+    while (s1 >= cap) s1 -= cap;
+  }
   // the table of the batch's tail pairs, and zero counters
   constexpr int kReq = kPairMaxBatch / kSliceThreads;
   unsigned long long rk[kReq];
@@ -137,36 +162,35 @@ __global__ __launch_bounds__(kSliceThreads) void pair_index_kernel(PairIndexArgs
     }
   }
   if (!any) return;  // uniform over the grid: the step reads no list
-  // this slice's end positions [xb, xe) and this wavefront's run [wb, we) of them
-  const long long nd = hi - lo - 2;
-  const long long sg = pair_seg(nd);
-  const long long xb = lo + 1 + (long long)sidx * sg;
-  const long long xe = xb + sg < hi - 1 ? xb + sg : hi - 1;
-  const long long wn = ((sg + kPairWaves - 1) / kPairWaves + 63) / 64 * 64;
-  const long long wb = xb + (long long)w * wn;
-  const long long we = wb + wn < xe ? wb + wn : xe;
-  const int cap = (int)a.ring_cap;
-  const int s0 = wb < we ? (int)((wb + lane) % a.ring_cap) : 0;  // slot of the lane's position
   uint32_t* part = a.list + (size_t)sidx * (size_t)sg;
   for (int pass = 0; pass < 2; ++pass) {
-    int s = s0;
+    int s = s1;  // slot past the first runs
     for (long long x0 = wb; x0 < we; x0 += 64 * kSliceRuns) {
+      const bool first = x0 == wb;
       int p[kSliceRuns], c[kSliceRuns], nx[kSliceRuns];
+      if (!first) {
 #pragma unroll
-      for (int u = 0; u < kSliceRuns; ++u) {
-        const bool in = x0 + 64 * u + lane < we;
-        const int sp = s == 0 ? cap - 1 : s - 1;
-        const int sn = s + 1 == cap ? 0 : s + 1;
-        p[u] = in ? a.ring[sp] : -1;
-        c[u] = in ? a.ring[s] : -1;
-        nx[u] = in ? a.ring[sn] : -1;
-        s += 64;
-        while (s >= cap) s -= cap;
+        for (int u = 0; u < kSliceRuns; ++u) {
+          const bool in = x0 + 64 * u + lane < we;
+          const int sp = s == 0 ? cap - 1 : s - 1;
+          const int sn = s + 1 == cap ? 0 : s + 1;
+          p[u] = in ? a.ring[sp] : -1;
+          c[u] = in ? a.ring[s] : -1;
+          nx[u] = in ? a.ring[sn] : -1;
+          s += 64;
+          while (s >= cap) s -= cap;
+        }
       }
 #pragma unroll
       for (int u = 0; u < kSliceRuns; ++u) {
         const long long x = x0 + 64 * u + lane;
-        const int g = group_at(hk, hg, mask, p[u], c[u], nx[u]);
+        int g;
+        if (first) {
+          if (pass == 0) g1[u] = group_at(hk, hg, mask, p1[u], c1[u], n1[u]);
+          g = g1[u];
+        } else {
+          g = group_at(hk, hg, mask, p[u], c[u], nx[u]);
+        }
         if (pass == 0) {
           if (g >= 0) atomicAdd(&cw[w][g], 1);
         } else {
