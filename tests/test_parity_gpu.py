@@ -746,3 +746,30 @@ def test_counted_form(S, flags):
             d.propose_counts(13, dev(n), dev(tok), dev(samp), dev(counts))
         assert ei.value.code == S.ECAPACITY
         d.close()
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+def test_delta_walk_with_and_without_early_region(S, flags):
+    """Long staged rows leave no LDS for the early delta walk's own region (the delta is walked
+    after the local sites, in the hit lists' space); streamed rows leave room (the wavefronts
+    that vote no local candidate walk it beside them).  Both against the oracle, with the pair
+    index, on a corpus with a delta of template documents."""
+    import torch
+
+    knobs = dict(k=16, max_tree_depth=24, num_backoff=4, max_occurrences=128, mode=1,
+                 spec_factor_ppm=2_000_000, min_token_prob_ppm=100_000)
+    B, Sq, cap = 16, 16384, 1 << 18
+    n, tok, samp = W.make_batch(4, set_index=3, B=B)
+    docs = W.corpus_docs(4)
+    d = S.Drafter(S.Config(max_batch=B, max_seq=Sq, max_sampled=1, corpus_capacity=cap,
+                           flags=flags, **knobs))
+    lc = O.LiveCorpus(cap)
+    d.ingest_docs(docs[:300])
+    lc.ingest(docs[:300])
+    d.rebuild()
+    d.ingest_docs(docs[300:420])
+    lc.ingest(docs[300:420])
+    dd, dn = d.propose(dev(n), dev(tok), dev(samp))
+    torch.cuda.synchronize()
+    exp = O.propose(O.params_from(knobs), n, tok, samp, corpus=lc.text(), num_threads=NTHREADS)
+    assert_same((dd.cpu().numpy(), dn.cpu().numpy()), exp, f"flags={flags}")
