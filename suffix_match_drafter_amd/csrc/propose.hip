@@ -193,16 +193,47 @@ __device__ __forceinline__ int ctx_at(const int32_t* row, const int32_t* smp, in
   return x < n ? row[x] : smp[x - n];
 }
 
-// Count one vote for `tok` in a wavefront's LDS table; returns the slot used.
-__device__ __forceinline__ int vote_insert(int* hk, int* hc, int tok) {
-  uint32_t h = ((uint32_t)tok * 0x9E3779B1u) >> 24;
-  for (;;) {
-    int prev = atomicCAS(&hk[h], -1, tok);
-    if (prev == -1 || prev == tok) {
-      atomicAdd(&hc[h], 1);
-      return (int)h;
+// An int in LDS, typed as such: a function that is not inlined sees a generic pointer
+// otherwise, and reaches LDS through flat instructions (slower, and every one waits on the
+// vector memory counter too).
+typedef __attribute__((address_space(3))) int lds_int;
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+
+// Count this lane's votes for t0 (when p0) and t1 (when p1) in a wavefront's LDS table, by
+// open addressing; *s0 / *s1 get the slots used (-1 for no vote).  The two inserts of a lane
+// run side by side, so that their exchanges share one LDS round trip.
+__device__ __forceinline__ void vote_insert2(lds_int* hk, lds_int* hc, bool p0, int t0, bool p1,
+                                             int t1, int* s0, int* s1) {
+  uint32_t h0 = ((uint32_t)t0 * 0x9E3779B1u) >> 24, h1 = ((uint32_t)t1 * 0x9E3779B1u) >> 24;
+  *s0 = -1;
+  *s1 = -1;
+  while (p0 || p1) {
+    int q0 = -1, q1 = -1;  // on return: the slot's key before the exchange
+    if (p0)
+      __hip_atomic_compare_exchange_strong(&hk[h0], &q0, t0, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (p1)
+      __hip_atomic_compare_exchange_strong(&hk[h1], &q1, t1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (p0) {
+      if (q0 == -1 || q0 == t0) {
+        __hip_atomic_fetch_add(&hc[h0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        *s0 = (int)h0;
+        p0 = false;
+      } else {
+        h0 = (h0 + 1) & (kVoteSlots - 1);
+      }
     }
-    h = (h + 1) & (kVoteSlots - 1);
+    if (p1) {
+      if (q1 == -1 || q1 == t1) {
+        __hip_atomic_fetch_add(&hc[h1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        *s1 = (int)h1;
+        p1 = false;
+      } else {
+        h1 = (h1 + 1) & (kVoteSlots - 1);
+      }
+    }
   }
 }
 
@@ -836,10 +867,12 @@ __device__ __forceinline__ void delta_list_wave(const ProposeArgs& a, long long 
 // majority among the na voting sites (alive and with a token at this depth): the count of every
 // token, then the largest count and the smallest token among the largest.  x0 / x1 are this
 // lane's two sites' tokens, V0 / V1 the voting sites, E0 / E1 those voting for ref.  Returns
-// count << 32 | token (a function of its own: this path is rare and its code is long).
+// count << 32 | token (a function of its own: this path is rare and its code is long).  With
+// few voters it may return as soon as no token can reach cmin; the count is then below cmin
+// (the vote stops there, whatever the token).
 __device__ __noinline__ uint64_t vote_split(int x0, int x1, uint64_t V0, uint64_t V1, int ref,
-                                            uint64_t E0, uint64_t E1, int na, int* hk, int* hc,
-                                            int lane) {
+                                            uint64_t E0, uint64_t E1, int na, int cmin,
+                                            lds_int* hk, lds_int* hc, int lane) {
   // wavefront-uniform arguments arrive in vector registers: make them scalar again
   auto u64 = [](uint64_t v) {
     return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v) |
@@ -851,14 +884,16 @@ __device__ __noinline__ uint64_t vote_split(int x0, int x1, uint64_t V0, uint64_
   E1 = u64(E1);
   ref = __builtin_amdgcn_readfirstlane(ref);
   na = __builtin_amdgcn_readfirstlane(na);
+  cmin = __builtin_amdgcn_readfirstlane(cmin);
   const int ce = __popcll(E0) + __popcll(E1);
   if (na <= kSmallVote) {
     // one ballot pair per distinct token, until the best count exceeds every vote not yet
-    // counted (a tie with a smaller token still has to be looked at)
+    // counted (a tie with a smaller token still has to be looked at), or until neither the best
+    // count nor the votes left reach cmin
     uint64_t key = ((uint64_t)ce << 32) | (uint32_t)(0x7FFFFFFF - ref);
     uint64_t r0 = V0 & ~E0, r1 = V1 & ~E1;
     int rest = na - ce;
-    while ((r0 | r1) && (int)(key >> 32) <= rest) {
+    while ((r0 | r1) && (int)(key >> 32) <= rest && (rest >= cmin || (int)(key >> 32) >= cmin)) {
       const int tok = r0 ? __builtin_amdgcn_readlane(x0, __builtin_ctzll(r0))
                          : __builtin_amdgcn_readlane(x1, __builtin_ctzll(r1));
       const uint64_t e0 = __ballot(x0 == tok) & r0, e1 = __ballot(x1 == tok) & r1;
@@ -871,31 +906,36 @@ __device__ __noinline__ uint64_t vote_split(int x0, int x1, uint64_t V0, uint64_
     }
     return (key >> 32) << 32 | (uint32_t)(0x7FFFFFFF - (int)(uint32_t)(key & 0xFFFFFFFFu));
   }
-  // many voting sites: counts in an LDS hash, then max count and smallest token
-  const bool v0 = (V0 >> lane) & 1, v1 = (V1 >> lane) & 1;
-  for (int x = lane; x < kVoteSlots; x += 64) {
-    hk[x] = -1;
-    hc[x] = 0;
-  }
+  // many voting sites: the reference's count is ce; the other voters' tokens are counted in an
+  // LDS hash (at most 127 distinct in 256 slots), then the largest count and smallest token
+  // over both
+  static_assert(kVoteSlots == 4 * 64, "one 16-byte store per lane clears a table");
+  const bool v0 = ((V0 & ~E0) >> lane) & 1, v1 = ((V1 & ~E1) >> lane) & 1;
+  reinterpret_cast<lds_v4i*>(hk)[lane] = v4i{-1, -1, -1, -1};
+  reinterpret_cast<lds_v4i*>(hc)[lane] = v4i{0, 0, 0, 0};
   wave_sync();
-  int sl0 = -1, sl1 = -1;
-  if (v0) sl0 = vote_insert(hk, hc, x0);
-  if (v1) sl1 = vote_insert(hk, hc, x1);
+  int sl0, sl1;
+  vote_insert2(hk, hc, v0, x0, v1, x1, &sl0, &sl1);
   wave_sync();
   const int cnt0 = sl0 >= 0 ? hc[sl0] : 0, cnt1 = sl1 >= 0 ? hc[sl1] : 0;
   uint64_t res;
-  if (__ballot((v0 && x0 >= (1 << 24)) || (v1 && x1 >= (1 << 24))) == 0) {
+  if (ref < (1 << 24) && __ballot((v0 && x0 >= (1 << 24)) || (v1 && x1 >= (1 << 24))) == 0) {
     // tokens below 2^24: count and token packed in one key, one reduction
     const uint32_t k0 = sl0 >= 0 ? ((uint32_t)cnt0 << 24) | (uint32_t)(0xFFFFFF - x0) : 0u;
     const uint32_t k1 = sl1 >= 0 ? ((uint32_t)cnt1 << 24) | (uint32_t)(0xFFFFFF - x1) : 0u;
-    const uint32_t key = wave_max_u32(k0 > k1 ? k0 : k1);
+    const uint32_t kr = ((uint32_t)ce << 24) | (uint32_t)(0xFFFFFF - ref);
+    uint32_t key = wave_max_u32(k0 > k1 ? k0 : k1);
+    key = key > kr ? key : kr;
     res = (uint64_t)(key >> 24) << 32 | (uint32_t)(0xFFFFFF - (int)(key & 0xFFFFFFu));
   } else {
-    const int c = wave_max(cnt0 > cnt1 ? cnt0 : cnt1);
+    int c = wave_max(cnt0 > cnt1 ? cnt0 : cnt1);
+    c = c > ce ? c : ce;
     int tmin = 0x7FFFFFFF;
     if (sl0 >= 0 && cnt0 == c) tmin = x0;
     if (sl1 >= 0 && cnt1 == c && x1 < tmin) tmin = x1;
-    res = (uint64_t)(uint32_t)c << 32 | (uint32_t)wave_min(tmin);
+    tmin = wave_min(tmin);
+    if (ce == c && ref < tmin) tmin = ref;
+    res = (uint64_t)(uint32_t)c << 32 | (uint32_t)tmin;
   }
   wave_sync();
   return res;
@@ -932,7 +972,8 @@ __device__ __forceinline__ void vote_depth(int x0, int x1, uint64_t A0, uint64_t
   } else {
     // (the call returns in vector registers: readfirstlane tells the compiler that the winner
     // and its count are wavefront-uniform, or every loop around this becomes a divergent one)
-    const uint64_t res = vote_split(x0, x1, V0, V1, ref, E0, E1, na, hk, hc, lane);
+    const uint64_t res = vote_split(x0, x1, V0, V1, ref, E0, E1, na, cmin, (lds_int*)hk,
+                                    (lds_int*)hc, lane);
     *c = __builtin_amdgcn_readfirstlane((int)(res >> 32));
     *w = __builtin_amdgcn_readfirstlane((int)(uint32_t)res);
   }
@@ -1035,7 +1076,9 @@ __device__ __forceinline__ void vote_seq(const int (&w0)[KMAX], const int (&w1)[
 // leave go depth by depth.  Returns false when the vote was dropped because beaten(bound)
 // reported that another candidate's final score beats the best this one can still reach (the
 // sum bound / c0); n_out and snum_out are then 0.
-constexpr int kPathMinDepths = 4;
+// (a pass costs as much as several depths voted one by one: votes of up to 10 depths go depth
+// by depth, which measured faster than passes from 4, 5, 7 or 9 depths on)
+constexpr int kPathMinDepths = 11;
 constexpr int kPathPasses = 3;
 template <int KMAX, typename Beaten>
 __device__ __forceinline__ bool vote_run(const int (&w0)[KMAX], const int (&w1)[KMAX], int len0,
@@ -2414,7 +2457,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
         sm.cand_snum[ci] = 0;
       }
     } else {
-      int* hk = vote_all + wid * (2 * kVoteSlots);
+      int* hk = vote_all + ci * (2 * kVoteSlots);
       int nout = 0, snum = 0;
 #if SFX_PHASE_TRACE
       unsigned long long* vts = a.trace ? sm.ts[wid] : nullptr;
