@@ -103,6 +103,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(a0, a1), max(a2, a3));
 }
 
+// Maximum over lanes 0 .. 15 (every lane takes part; the others hold their own row's).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppQuadXor2, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppHalfMirror, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, kDppMirror, 0xF, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+}
+
 __device__ __forceinline__ int wave_min(int v) {
   v = min(v, __builtin_amdgcn_mov_dpp(v, kDppQuadXor1, 0xF, 0xF, false));
   v = min(v, __builtin_amdgcn_mov_dpp(v, kDppQuadXor2, 0xF, 0xF, false));
@@ -2543,18 +2552,22 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   __syncthreads();
   PHASE(8);
 
-  // selection and output row, by wavefront 0 (a candidate with the same length as an earlier
-  // one of its source shares that one's sites and vote)
+  // selection and output row, by wavefront 0.  Only a candidate that is the first of its length
+  // in its source takes part: a later one shares that one's sites and vote, so it has the same
+  // score and loses the tie to the earlier one.
   if (wid != 0) {
     PHASE_FLUSH();
     return;
   }
-  const bool cv = lane < 2 * nb && sm.cand_valid[lane];
-  const int csrc = cv ? sm.cand_src[lane] : 0;
-  const int csn = cv ? sm.cand_snum[csrc] : 0;
-  const int cc0 = cv ? sm.cand_c0[lane] : 1;
-  const int clen = cv ? sm.cand_len[lane] : 0;
-  const int cn = cv ? sm.cand_n[csrc] : 0;
+  const bool cl = lane < 2 * nb;
+  const int fvalid = cl ? sm.cand_valid[lane] : 0;
+  const int fsrc = cl ? sm.cand_src[lane] : -1;
+  const int csn = cl ? sm.cand_snum[lane] : 0;
+  const int cc0 = cl ? sm.cand_c0[lane] : 1;
+  const int clen = cl ? sm.cand_len[lane] : 0;
+  const int fn = cl ? sm.cand_n[lane] : 0;
+  const bool cv = fvalid && fsrc == lane;
+  const int cn = cv ? fn : 0;
   const uint64_t vmask = __ballot(cv);
   int win = -1;
   if (a.mode == 0) {
@@ -2563,24 +2576,18 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     if (lv && (!gv || l0 >= g0)) win = 0;
     else if (gv) win = nb;
   } else {
-    // scores snum / c0 compared by cross products (snum <= k * M = 4096, c0 <= M = 128); lane i
-    // holds candidate i, which wins when no valid candidate beats it: a higher score, or the
-    // same score earlier in candidate order.  The comparisons of all lanes run side by side.
-    // (bitwise, not short-circuit, operators, so that the compares do not branch)
-    int beaten = cv ? 0 : 1;
-#pragma unroll
-    for (int j = 0; j < 2 * kMaxNB; ++j) {
-      if (j < 2 * nb) {
-        const int sj = __builtin_amdgcn_readlane(csn, j), cj = __builtin_amdgcn_readlane(cc0, j);
-        const int lhs = sj * cc0, rhs = csn * cj;
-        const int vj = (int)((vmask >> j) & 1);
-        beaten |= vj & ((lhs > rhs) | ((lhs == rhs) & (j < lane)));
-      }
-    }
-    const uint64_t wm = __ballot(beaten == 0);
-    win = wm ? __builtin_ctzll(wm) : -1;
+    // the highest score snum / c0, the first candidate among equal ones.  Scores become exact
+    // integer keys: with snum <= 64 * 128 = 2^13 and 1 <= c0 <= 128, two different fractions
+    // differ by at least 1 / 128^2 = 2^-14, so floor(snum * 2^14 / c0) keeps their order and
+    // gives equal fractions equal keys.  The low four bits prefer the earlier candidate (lane i
+    // holds candidate i < 16), and one maximum over the 16 lanes picks the winner.
+    static_assert(2 * kMaxNB <= 16, "candidates in one row of 16 lanes");
+    const uint32_t q = ((uint32_t)csn << 14) / (uint32_t)(cc0 > 0 ? cc0 : 1);
+    const uint32_t key = cv ? ((q << 4) | (uint32_t)(15 - lane)) + 1u : 0u;
+    const uint32_t best = row16_max_u32(key);
+    win = best ? 15 - (int)((best - 1u) & 15u) : -1;
   }
-  const int ws = win >= 0 ? __builtin_amdgcn_readlane(csrc, win) : -1;
+  const int ws = win;
   const int nv = win >= 0 ? __builtin_amdgcn_readlane(cn, win) : 0;
   const int fill = a.mode == 0 ? r.t0 : -1;
   const int wlen = win >= 0 ? __builtin_amdgcn_readlane(clen, win) : 0;
