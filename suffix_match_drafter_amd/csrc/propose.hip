@@ -1348,10 +1348,18 @@ __device__ __forceinline__ void corpus_windows(const ProposeArgs& a, const Req& 
     const int32_t* t1p = text + o1;
     const long long r0 = sn - 1 - o0, r1 = sn - 1 - o1;
     const int l0 = r0 < KMAX ? (int)r0 : KMAX, l1 = r1 < KMAX ? (int)r1 : KMAX;
+    if (c0 > 64) {  // (wavefront-uniform) a second site per lane
 #pragma unroll
-    for (int d = 0; d < KMAX; ++d) {
-      w0[d] = t0p[d < l0 ? d : l0];
-      w1[d] = t1p[d < l1 ? d : l1];
+      for (int d = 0; d < KMAX; ++d) {
+        w0[d] = t0p[d < l0 ? d : l0];
+        w1[d] = t1p[d < l1 ? d : l1];
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < KMAX; ++d) {
+        w0[d] = t0p[d < l0 ? d : l0];
+        w1[d] = -1;
+      }
     }
   } else {
     const int rcap = (int)a.ring_cap;
@@ -1879,15 +1887,18 @@ __device__ __forceinline__ void local_windows(const Smem& sm, const int* ctxs, c
   const int cap0 = cap < KMAX ? cap : KMAX;
   const int e0 = s0 < c0 ? (L - p0 < cap0 ? L - p0 : cap0) : 0;
   const int e1 = s1 < c0 ? (L - p1 < cap0 ? L - p1 : cap0) : 0;
+  auto at = [&](int x) { return STAGED ? ctxs[x] : *(x < n ? row + x : smp + (x - n)); };
+  if (c0 > 64) {  // (wavefront-uniform) a second site per lane
 #pragma unroll
-  for (int d = 0; d < KMAX; ++d) {
-    const int x0 = p0 + d < L ? p0 + d : L - 1, x1 = p1 + d < L ? p1 + d : L - 1;
-    if (STAGED) {
-      w0[d] = ctxs[x0];
-      w1[d] = ctxs[x1];
-    } else {
-      w0[d] = *(x0 < n ? row + x0 : smp + (x0 - n));
-      w1[d] = *(x1 < n ? row + x1 : smp + (x1 - n));
+    for (int d = 0; d < KMAX; ++d) {
+      w0[d] = at(p0 + d < L ? p0 + d : L - 1);
+      w1[d] = at(p1 + d < L ? p1 + d : L - 1);
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < KMAX; ++d) {
+      w0[d] = at(p0 + d < L ? p0 + d : L - 1);
+      w1[d] = -1;
     }
   }
   // a site stops voting for good at its first depth without a token (a negative id counts as
@@ -2412,10 +2423,11 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   // ---------------------------------------------------------------- 3. votes
   // One call site for every vote: wavefront ci votes candidate ci.  Without the general path,
   // local candidate t is voted right after its sites, and corpus candidate nb + t as soon as the
-  // corpus wavefront has published its sites (while other wavefronts still work).  A vote that
-  // cannot change the selection is skipped: in the longest-match mode every candidate but the
-  // one the lengths select, in the scored mode one whose best reachable score a final score
-  // already beats (its score is then left at 0, which still loses to that one).
+  // corpus wavefront has published its sites (while other wavefronts still work).  In the
+  // longest-match mode only the candidate that the lengths select is voted.  In the scored mode
+  // a vote is dropped between its passes once another candidate's final score beats every score
+  // it can still reach (its score is then left at 0, which still loses to that one); it is not
+  // checked before the vote starts, when the other votes have rarely ended.
   if (wid < 2 * nb) {
     const int ci = wid;
     const bool general = r.has && (!fast || r.delta) && Lcap >= 2;
@@ -2457,8 +2469,6 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
                                                   __builtin_amdgcn_readlane(fl, nb));
         need = (ci == 0) == local_wins;
       }
-    } else if (need && outscored(sm, ci, nb, dmax, 1, lane)) {
-      need = false;
     }
     if (!need) {
       if (lane == 0) {
