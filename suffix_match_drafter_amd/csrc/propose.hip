@@ -957,20 +957,13 @@ __device__ __forceinline__ int first_set(uint32_t m) {
   return f < KMAX ? f : KMAX;
 }
 
-// One depth of the vote, decided from scratch: x0 / x1 are this lane's two sites' tokens, A0 / A1
-// the alive sites.  On return *w / *c hold the winner and its count, or *c = 0 when no alive
-// site has a token here.
-__device__ __forceinline__ void vote_depth(int x0, int x1, uint64_t A0, uint64_t A1, int cmin,
-                                           int* hk, int* hc, int lane, int* w, int* c) {
-  const uint64_t V0 = __ballot(x0 >= 0) & A0, V1 = __ballot(x1 >= 0) & A1;
+// The second half of vote_depth, for a caller that has the voting sites V0 / V1 (not both
+// empty), the reference token ref (the first voting site's) and its voters E0 / E1 already.
+__device__ __forceinline__ void vote_decide(int x0, int x1, uint64_t V0, uint64_t V1, int ref,
+                                            uint64_t E0, uint64_t E1, int cmin, int* hk, int* hc,
+                                            int lane, int* w, int* c) {
   *c = 0;
   *w = -1;
-  if ((V0 | V1) == 0) return;
-  // the reference is the first voting site's token; when every voting site agrees with it, or a
-  // strict majority does, it wins with their votes
-  const int ref = V0 ? __builtin_amdgcn_readlane(x0, __builtin_ctzll(V0))
-                     : __builtin_amdgcn_readlane(x1, __builtin_ctzll(V1));
-  const uint64_t E0 = __ballot(x0 == ref) & A0, E1 = __ballot(x1 == ref) & A1;
   const int na = __popcll(V0) + __popcll(V1);
   const int ce = __popcll(E0) + __popcll(E1);
   if (2 * ce > na) {
@@ -986,6 +979,23 @@ __device__ __forceinline__ void vote_depth(int x0, int x1, uint64_t A0, uint64_t
     *c = __builtin_amdgcn_readfirstlane((int)(res >> 32));
     *w = __builtin_amdgcn_readfirstlane((int)(uint32_t)res);
   }
+}
+
+// One depth of the vote, decided from scratch: x0 / x1 are this lane's two sites' tokens, A0 / A1
+// the alive sites.  On return *w / *c hold the winner and its count, or *c = 0 when no alive
+// site has a token here.
+__device__ __forceinline__ void vote_depth(int x0, int x1, uint64_t A0, uint64_t A1, int cmin,
+                                           int* hk, int* hc, int lane, int* w, int* c) {
+  const uint64_t V0 = __ballot(x0 >= 0) & A0, V1 = __ballot(x1 >= 0) & A1;
+  *c = 0;
+  *w = -1;
+  if ((V0 | V1) == 0) return;
+  // the reference is the first voting site's token; when every voting site agrees with it, or a
+  // strict majority does, it wins with their votes
+  const int ref = V0 ? __builtin_amdgcn_readlane(x0, __builtin_ctzll(V0))
+                     : __builtin_amdgcn_readlane(x1, __builtin_ctzll(V1));
+  const uint64_t E0 = __ballot(x0 == ref) & V0, E1 = __ballot(x1 == ref) & V1;
+  vote_decide(x0, x1, V0, V1, ref, E0, E1, cmin, hk, hc, lane, w, c);
 }
 
 // Scored selection: whether a candidate other than ci whose vote is final beats every score ci
@@ -1051,7 +1061,7 @@ __device__ __forceinline__ void vote_seq(const int (&w0)[KMAX], const int (&w1)[
     if (E0 == V0 && E1 == V1) {
       c = __popcll(V0) + (TWO ? __popcll(V1) : 0);
     } else {
-      vote_depth(x0, x1, V0, V1, cmin, hk, hc, lane, &w, &c);
+      vote_decide(x0, x1, V0, V1, ref, E0, E1, cmin, hk, hc, lane, &w, &c);
     }
     if (c < cmin) {
       done = true;
