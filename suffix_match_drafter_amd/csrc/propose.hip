@@ -873,15 +873,39 @@ __device__ __forceinline__ void delta_list_wave(const ProposeArgs& a, long long 
 }
 
 // The vote at one depth when the reference token (the first voting site's) holds no strict
-// majority among the na voting sites (alive and with a token at this depth): the count of every
-// token, then the largest count and the smallest token among the largest.  x0 / x1 are this
-// lane's two sites' tokens, V0 / V1 the voting sites, E0 / E1 those voting for ref.  Returns
-// count << 32 | token (a function of its own: this path is rare and its code is long).  With
-// few voters it may return as soon as no token can reach cmin; the count is then below cmin
-// (the vote stops there, whatever the token).
+// majority among the na voting sites (alive and with a token at this depth), for at most
+// kSmallVote voters: the count of every token, then the largest count and the smallest token
+// among the largest.  x0 / x1 are this lane's two sites' tokens, V0 / V1 the voting sites, E0 /
+// E1 those voting for ref (all wavefront-uniform but x0 / x1).  Returns count << 32 | token.
+// One ballot pair per distinct token, until the best count exceeds every vote not yet counted
+// (a tie with a smaller token still has to be looked at), or until neither the best count nor
+// the votes left reach cmin: the count is then below cmin (the vote stops there, whatever the
+// token).
+__device__ __forceinline__ uint64_t vote_small(int x0, int x1, uint64_t V0, uint64_t V1, int ref,
+                                               uint64_t E0, uint64_t E1, int na, int cmin) {
+  const int ce = __popcll(E0) + __popcll(E1);
+  uint64_t key = ((uint64_t)ce << 32) | (uint32_t)(0x7FFFFFFF - ref);
+  uint64_t r0 = V0 & ~E0, r1 = V1 & ~E1;
+  int rest = na - ce;
+  while ((r0 | r1) && (int)(key >> 32) <= rest && (rest >= cmin || (int)(key >> 32) >= cmin)) {
+    const int tok = r0 ? __builtin_amdgcn_readlane(x0, __builtin_ctzll(r0))
+                       : __builtin_amdgcn_readlane(x1, __builtin_ctzll(r1));
+    const uint64_t e0 = __ballot(x0 == tok) & r0, e1 = __ballot(x1 == tok) & r1;
+    const int ct = __popcll(e0) + __popcll(e1);
+    const uint64_t k = ((uint64_t)ct << 32) | (uint32_t)(0x7FFFFFFF - tok);
+    key = k > key ? k : key;
+    r0 &= ~e0;
+    r1 &= ~e1;
+    rest -= ct;
+  }
+  return (key >> 32) << 32 | (uint32_t)(0x7FFFFFFF - (int)(uint32_t)(key & 0xFFFFFFFFu));
+}
+
+// The same vote for more than kSmallVote voters, by counting in an LDS hash (a function of its
+// own: this path is rare and its code is long).
 __device__ __noinline__ uint64_t vote_split(int x0, int x1, uint64_t V0, uint64_t V1, int ref,
-                                            uint64_t E0, uint64_t E1, int na, int cmin,
-                                            lds_int* hk, lds_int* hc, int lane) {
+                                            uint64_t E0, uint64_t E1, lds_int* hk, lds_int* hc,
+                                            int lane) {
   // wavefront-uniform arguments arrive in vector registers: make them scalar again
   auto u64 = [](uint64_t v) {
     return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v) |
@@ -892,29 +916,7 @@ __device__ __noinline__ uint64_t vote_split(int x0, int x1, uint64_t V0, uint64_
   E0 = u64(E0);
   E1 = u64(E1);
   ref = __builtin_amdgcn_readfirstlane(ref);
-  na = __builtin_amdgcn_readfirstlane(na);
-  cmin = __builtin_amdgcn_readfirstlane(cmin);
   const int ce = __popcll(E0) + __popcll(E1);
-  if (na <= kSmallVote) {
-    // one ballot pair per distinct token, until the best count exceeds every vote not yet
-    // counted (a tie with a smaller token still has to be looked at), or until neither the best
-    // count nor the votes left reach cmin
-    uint64_t key = ((uint64_t)ce << 32) | (uint32_t)(0x7FFFFFFF - ref);
-    uint64_t r0 = V0 & ~E0, r1 = V1 & ~E1;
-    int rest = na - ce;
-    while ((r0 | r1) && (int)(key >> 32) <= rest && (rest >= cmin || (int)(key >> 32) >= cmin)) {
-      const int tok = r0 ? __builtin_amdgcn_readlane(x0, __builtin_ctzll(r0))
-                         : __builtin_amdgcn_readlane(x1, __builtin_ctzll(r1));
-      const uint64_t e0 = __ballot(x0 == tok) & r0, e1 = __ballot(x1 == tok) & r1;
-      const int ct = __popcll(e0) + __popcll(e1);
-      const uint64_t k = ((uint64_t)ct << 32) | (uint32_t)(0x7FFFFFFF - tok);
-      key = k > key ? k : key;
-      r0 &= ~e0;
-      r1 &= ~e1;
-      rest -= ct;
-    }
-    return (key >> 32) << 32 | (uint32_t)(0x7FFFFFFF - (int)(uint32_t)(key & 0xFFFFFFFFu));
-  }
   // many voting sites: the reference's count is ce; the other voters' tokens are counted in an
   // LDS hash (at most 127 distinct in 256 slots), then the largest count and smallest token
   // over both
@@ -971,11 +973,14 @@ __device__ __forceinline__ void vote_decide(int x0, int x1, uint64_t V0, uint64_
     *c = ce;
   } else if (na < cmin) {
     *c = na;  // no token reaches the stop count: any count below cmin stops the vote
+  } else if (na <= kSmallVote) {
+    const uint64_t res = vote_small(x0, x1, V0, V1, ref, E0, E1, na, cmin);
+    *c = (int)(res >> 32);
+    *w = (int)(uint32_t)res;
   } else {
     // (the call returns in vector registers: readfirstlane tells the compiler that the winner
     // and its count are wavefront-uniform, or every loop around this becomes a divergent one)
-    const uint64_t res = vote_split(x0, x1, V0, V1, ref, E0, E1, na, cmin, (lds_int*)hk,
-                                    (lds_int*)hc, lane);
+    const uint64_t res = vote_split(x0, x1, V0, V1, ref, E0, E1, (lds_int*)hk, (lds_int*)hc, lane);
     *c = __builtin_amdgcn_readfirstlane((int)(res >> 32));
     *w = __builtin_amdgcn_readfirstlane((int)(uint32_t)res);
   }
