@@ -54,7 +54,10 @@ size_t propose_static_lds();
 bool propose_staged(int S, int T, bool stream_ctx, bool corpus, int nb);
 // Allows the largest dynamic LDS on every propose kernel instantiation.
 hipError_t propose_prepare();
-hipError_t launch_propose(const ProposeArgs& a, hipStream_t st);
+// general: launch the kernel with the general path (a delta, or no live snapshot).  Without it
+// the kernel ignores the delta, which is right only when no document was ingested since the
+// live snapshot was taken (the call then sees no delta).
+hipError_t launch_propose(const ProposeArgs& a, bool general, hipStream_t st);
 hipError_t launch_update_state(int B, int S, int T, int32_t* tok, const int32_t* ntns,
                                const int32_t* samp, int32_t* nout, hipStream_t st);
 

@@ -1952,7 +1952,12 @@ __device__ __forceinline__ void local_windows(const Smem& sm, const int* ctxs, c
   } while (0)
 #endif
 
-template <int KMAX, bool STAGED>
+// GENERAL: whether the general path (section 2) is compiled in.  Without it the kernel is for
+// calls that the host knows see no delta: no document ingested since the live snapshot was
+// taken.  Then the general path would only run without a live snapshot, and it finds no corpus
+// candidate there, so leaving it out changes no result; its code (about a quarter of the
+// kernel's) is then out of the instruction cache and the register allocation.
+template <int KMAX, bool STAGED, bool GENERAL>
 __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   extern __shared__ int4 dyn4[];
   unsigned char* dyn = reinterpret_cast<unsigned char*>(dyn4);
@@ -1981,7 +1986,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   static_assert(kCtlWords <= 64 && sizeof(Ctl) % 8 == 0, "control block in one wavefront");
   const int nraw = a.ntns[b];
   // the request's delta group, read now so that it has landed when the delta walk needs it
-  const int pgroup = a.pair_group != nullptr ? a.pair_group[b] : -1;
+  const int pgroup = GENERAL && a.pair_group != nullptr ? a.pair_group[b] : -1;
   const int sl = lane < a.T ? smp[lane] : -1;
   const int cw = a.ctl != nullptr && lane < kCtlWords
                      ? reinterpret_cast<const int*>(a.ctl)[lane] : 0;
@@ -2178,7 +2183,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   }
 
   // ---------------------------------------------------------------- 2. global (general path)
-  if (r.has && (!fast || r.delta) && Lcap >= 2) {
+  if (GENERAL && r.has && (!fast || r.delta) && Lcap >= 2) {
     // this wavefront's slices of the request's delta group (read before the barrier, so that
     // they land while the local candidates finish)
     const long long dlo = r.delta_lo, dhi = r.delta_hi;
@@ -2445,7 +2450,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
   // checked before the vote starts, when the other votes have rarely ended.
   if (wid < 2 * nb) {
     const int ci = wid;
-    const bool general = r.has && (!fast || r.delta) && Lcap >= 2;
+    const bool general = GENERAL && r.has && (!fast || r.delta) && Lcap >= 2;
     const bool gwait = fast && !general;  // corpus candidates arrive by flag
     if (gwait && ci >= nb && wid != GW) wait_flag(&sm.gready, lane, a.err);
     // the longest-match mode compares candidate 0 with candidate nb: wait for, or look at,
@@ -2640,11 +2645,15 @@ __global__ void update_state_kernel(int B, int S, int T, int32_t* tok, const int
 }
 
 template <int KMAX>
-hipError_t launch_k(const ProposeArgs& a, bool staged, size_t dyn, hipStream_t st) {
-  if (staged)
-    hipLaunchKernelGGL((propose_kernel<KMAX, true>), dim3(a.B), dim3(NT), dyn, st, a);
+hipError_t launch_k(const ProposeArgs& a, bool staged, bool general, size_t dyn, hipStream_t st) {
+  if (staged && general)
+    hipLaunchKernelGGL((propose_kernel<KMAX, true, true>), dim3(a.B), dim3(NT), dyn, st, a);
+  else if (staged)
+    hipLaunchKernelGGL((propose_kernel<KMAX, true, false>), dim3(a.B), dim3(NT), dyn, st, a);
+  else if (general)
+    hipLaunchKernelGGL((propose_kernel<KMAX, false, true>), dim3(a.B), dim3(NT), dyn, st, a);
   else
-    hipLaunchKernelGGL((propose_kernel<KMAX, false>), dim3(a.B), dim3(NT), dyn, st, a);
+    hipLaunchKernelGGL((propose_kernel<KMAX, false, false>), dim3(a.B), dim3(NT), dyn, st, a);
   return hipGetLastError();
 }
 
@@ -2666,9 +2675,12 @@ bool propose_staged(int S, int T, bool stream_ctx, bool corpus, int nb) {
 
 hipError_t propose_prepare() {
   const void* fns[] = {
-      (const void*)propose_kernel<8, true>,  (const void*)propose_kernel<8, false>,
-      (const void*)propose_kernel<16, true>, (const void*)propose_kernel<16, false>,
-      (const void*)propose_kernel<32, true>, (const void*)propose_kernel<32, false>};
+      (const void*)propose_kernel<8, true, true>,   (const void*)propose_kernel<8, false, true>,
+      (const void*)propose_kernel<16, true, true>,  (const void*)propose_kernel<16, false, true>,
+      (const void*)propose_kernel<32, true, true>,  (const void*)propose_kernel<32, false, true>,
+      (const void*)propose_kernel<8, true, false>,  (const void*)propose_kernel<8, false, false>,
+      (const void*)propose_kernel<16, true, false>, (const void*)propose_kernel<16, false, false>,
+      (const void*)propose_kernel<32, true, false>, (const void*)propose_kernel<32, false, false>};
   size_t st = sizeof(Smem);
   for (const void* f : fns) {
     hipFuncAttributes fa;
@@ -2686,15 +2698,15 @@ hipError_t propose_prepare() {
   return hipSuccess;
 }
 
-hipError_t launch_propose(const ProposeArgs& a, hipStream_t st) {
+hipError_t launch_propose(const ProposeArgs& a, bool general, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const bool corpus = a.ctl != nullptr;
   const bool staged = propose_staged(a.S, a.T, a.stream_ctx != 0, corpus, a.nb);
   const size_t dyn = dyn_bytes(staged, a.S, a.T, corpus, a.nb);
   if (dyn + propose_static_lds() > kLdsBytes) return hipErrorInvalidValue;
-  if (a.k <= 8) return launch_k<8>(a, staged, dyn, st);
-  if (a.k <= 16) return launch_k<16>(a, staged, dyn, st);
-  return launch_k<32>(a, staged, dyn, st);
+  if (a.k <= 8) return launch_k<8>(a, staged, general, dyn, st);
+  if (a.k <= 16) return launch_k<16>(a, staged, general, dyn, st);
+  return launch_k<32>(a, staged, general, dyn, st);
 }
 
 hipError_t launch_update_state(int B, int S, int T, int32_t* tok, const int32_t* ntns,

@@ -443,10 +443,15 @@ extern "C" void sfx_debug_phase_trace(void* buf) { g_phase_trace = (uint64_t*)bu
 
 // The drafter step with draft width k (at most the configured one), after argument checks.
 // With force_pairs the delta grouping passes run even when no ingest is pending (a captured
-// chain meant for engines that ingest every step).
+// chain meant for engines that ingest every step).  A call with no ingest pending (nothing
+// ingested since the live snapshot was taken, so no delta) launches the kernel without the
+// general path; a replayable one (a chain captured into a graph, here or by the caller on a
+// capturing stream, run later against whatever corpus is then live) always takes the one
+// with it.
 static int propose_k(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
                      const int32_t* ntns, const int32_t* tok, const int32_t* samp,
-                     int32_t* draft, int32_t* nvalid, void* stream, bool force_pairs = false) {
+                     int32_t* draft, int32_t* nvalid, void* stream, bool force_pairs = false,
+                     bool replayable = false) {
   const sfx_config& g = c->cfg;
   if (B < 0 || S < 0 || T < 0) return fail(SFX_EINVAL, "negative shape B=%d S=%d T=%d", B, S, T);
   if (B > g.max_batch || S > g.max_seq || T > g.max_sampled)
@@ -504,7 +509,14 @@ static int propose_k(sfx_ctx* c, int32_t k, int32_t B, int32_t S, int32_t T,
     a.pair_seg = c->pair_seg;
     a.pair_list = c->pair_list;
   }
-  HIP_OR_RETURN(launch_propose(a, (hipStream_t)stream), "propose launch");
+  bool general = replayable || force_pairs || c->ingest_epoch != c->live_epoch;
+  if (!general) {
+    // a launch captured into a graph (by the caller) is replayed later, whatever the corpus is
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    HIP_OR_RETURN(hipStreamIsCapturing((hipStream_t)stream, &cs), "capture status");
+    general = cs != hipStreamCaptureStatusNone;
+  }
+  HIP_OR_RETURN(launch_propose(a, general, (hipStream_t)stream), "propose launch");
   return SFX_OK;
 }
 
@@ -1056,7 +1068,7 @@ int graph_chain(sfx_graphs* g, int32_t B, hipStream_t st) {
   int rc = check_ctx(g->ctx);
   if (rc) return rc;
   rc = propose_k(g->ctx, g->ctx->cfg.k, B, g->S, g->T, g->ntns, g->tok, g->samp, g->draft,
-                 g->nvalid, st, (g->flags & SFX_GRAPHS_DELTA_INDEX) != 0);
+                 g->nvalid, st, (g->flags & SFX_GRAPHS_DELTA_INDEX) != 0, true);
   if (rc) return rc;
   if (checking(g->ctx))
     HIP_OR_RETURN(launch_check_propose(B, g->S, g->T, g->ntns, g->tok, g->samp, nullptr,
