@@ -421,8 +421,17 @@ constexpr int kHotCmp = 16;  // suffix tokens compared per round trip
 // is above every suffix with prefix P_l (upper bound).  tl[x] is the context token x places
 // before the last one.  Writes sup[l] and lo[l] for 5 <= l <= Lcap, and the 4-gram group's
 // position-list offset and size in goff[l], gcnt[l].
-__device__ __forceinline__ void hot_bounds(const View ib, const int* tl, int Lcap, int snap_n,
-                                        int lane, int* sup, int* lo_out, int* goff, int* gcnt) {
+//
+// A function of its own (so is hot_sites): only a hot group runs it, and inlined its code sits
+// in every request's path and instruction cache.  Its arrays are in LDS, typed as such inside,
+// so that it reaches them with ds instructions rather than flat ones.
+__device__ __noinline__ void hot_bounds(const View ib, const int* tl_g, int Lcap, int snap_n,
+                                        int lane, int* sup_g, int* lo_g, int* goff_g, int* gcnt_g) {
+  const lds_int* tl = (const lds_int*)tl_g;
+  lds_int* sup = (lds_int*)sup_g;
+  lds_int* lo_out = (lds_int*)lo_g;
+  lds_int* goff = (lds_int*)goff_g;
+  lds_int* gcnt = (lds_int*)gcnt_g;
   for (int pass = 0; pass < 2; ++pass) {
     const int idx = lane + 64 * pass;
     const int l = 5 + (idx >> 1), side = idx & 1;
@@ -645,9 +654,14 @@ __device__ __forceinline__ int hot_scan(const View ib, const int32_t* pl4, int l
 // Earliest sites of hot candidate length l: selection from its range when it is small, else the
 // position-ordered scan of whichever 4-gram group is smaller (the one that starts P_l, or the
 // tail's).  Returns how many were written to gs.
-__device__ __forceinline__ int hot_sites(const View ib, Smem& sm, const int* tl, int l, int M,
-                                         int snap_n, int sbase, const int32_t* pl4, int live4,
-                                         int* gs, int lane) {
+__device__ __noinline__ int hot_sites(const View ib, Smem& sm_g, const int* tl_g, int l, int M,
+                                      int snap_n, int sbase, const int32_t* pl4, int live4,
+                                      int* gs_g, int lane) {
+  // (sm, the tail and the sites are in LDS: cast through LDS pointers, the inlined helpers reach
+  // them with ds instructions)
+  Smem& sm = *(Smem*)(lds_int*)(int*)&sm_g;
+  const int* tl = (const int*)(const lds_int*)tl_g;
+  int* gs = (int*)(lds_int*)gs_g;
   const int sup = sm.hsup[l];
   const int hcnt = sm.hcnt[l];
   // costs in round trips: a selection chunk is one plus about as much arithmetic; a scan takes
