@@ -1845,19 +1845,19 @@ __device__ __forceinline__ void local_candidate(const ProposeArgs& a, Smem& sm, 
   int* ls = sm.lsites[t];
   if (l == 1) {
     // every end position whose token is the last context token: the set bits of the bit words
+    // (a whole word per lane: the earliest c0 often lie far apart, and a round per 64 words
+    // instead of per 16 makes up for the longer walk of a dense word, which stops at c0)
     const int nwords = (J + 63) >> 6;
     int found = 0;
-    for (int q0 = 0; found < c0 && q0 < 4 * nwords; q0 += 64) {
-      const int q = q0 + lane;
-      const int wi = q >> 2, part = q & 3;
-      const uint64_t wd = wi < nwords ? bits[wi] : 0ull;
-      uint32_t piece = (uint32_t)(wd >> (16 * part)) & 0xFFFFu;
-      const int c = __popc(piece);
+    for (int w0 = 0; found < c0 && w0 < nwords; w0 += 64) {
+      const int wi = w0 + lane;
+      uint64_t wd = wi < nwords ? bits[wi] : 0ull;
+      const int c = __popcll(wd);
       const int incl = wave_incl_add(c);
       int at = found + incl - c;
-      while (piece && at < c0) {
-        ls[at++] = 64 * wi + 16 * part + __builtin_ctz(piece) + 1;
-        piece &= piece - 1;
+      while (wd && at < c0) {
+        ls[at++] = 64 * wi + __builtin_ctzll(wd) + 1;
+        wd &= wd - 1;
       }
       found += __builtin_amdgcn_readlane(incl, 63);
     }
