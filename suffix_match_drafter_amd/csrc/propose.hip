@@ -42,6 +42,7 @@ constexpr int GW = NW - 1;          // the corpus wavefront of the fast path
 constexpr int kVoteSlots = 256;     // LDS hash slots of one voter (keys and counts)
 constexpr int kSmallVote = 24;      // alive sites at or below this vote with ballots
 constexpr int kColSites = 8;        // candidates with at most this many sites vote by columns
+constexpr int kPrefetchTokens = 2048;  // row tokens fetched during the set-up round trip
 
 // f(integral_constant<int, I>) for I = I0 .. N-1, unrolled at compile time (so that lane and
 // register indices are immediates).
@@ -273,6 +274,7 @@ struct Smem {
   int hsup[kMaxD + 1], hlo[kMaxD + 1];
   int hoff[kMaxD + 1], hcnt[kMaxD + 1];  // position-list group of P_l's first 4-gram
   int ghot;  // 1 when the snapshot part of lengths >= 5 comes from them
+  int sink[NW];   // the set-up prefetch's values (kept only so that the loads are made)
   int hrad[256];  // digit histogram of the hot site selection
   int hn;    // snapshot sites found by the general path's hot site pass
   const int32_t* plp[kNG];
@@ -2006,6 +2008,15 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
                      ? reinterpret_cast<const int*>(a.ctl)[lane] : 0;
   const int capv = tid <= kMaxD ? a.cap_of_len[tid] : 0;
   const int minv = tid <= kMaxM ? a.min_count[tid] : 0;
+  // The first kPrefetchTokens of the row, one 128-byte line per thread, start their way from
+  // HBM now, while the set-up round trip runs and HBM is otherwise idle; the screen reads them
+  // again from L2.  (Past the row's capacity a load reads nothing; a row shorter than this
+  // fetches at most 8 KB it does not use.)  The value is kept in LDS at the end, so the load
+  // stays.
+  const int pf_ints = a.S < kPrefetchTokens ? a.S : kPrefetchTokens;
+  const __amdgpu_buffer_rsrc_t pf_rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)row, (short)0, pf_ints * 4, kBufferWord3);
+  const int pf = __builtin_amdgcn_raw_buffer_load_b32(pf_rs, tid * 128, 0, 0);
 
   Req r;
   {
@@ -2592,6 +2603,7 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
       }
     }
   }
+  if (lane == 0) sm.sink[wid] = pf;
   PHASE(7);
   __syncthreads();
   PHASE(8);
