@@ -71,6 +71,10 @@ constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside a row of 16
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside a half row of 8
 constexpr int kDppRowBcast15 = 0x142; // lane 15 of each row to the next row
 constexpr int kDppRowBcast31 = 0x143; // lane 31 to rows 2 and 3
+// whole-wavefront lane moves: lane i takes lane i - 1 (lane 0 keeps the old value), and lane i
+// takes lane i - 1 mod 64
+constexpr int kDppWaveShr1 = 0x138;
+constexpr int kDppWaveRor1 = 0x13C;
 
 // Inclusive prefix sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ int wave_incl_add(int v) {
@@ -1243,24 +1247,53 @@ __device__ __forceinline__ bool vote_run(const int (&w0)[KMAX], const int (&w1)[
   return true;
 }
 
-// Depth-wise vote of a candidate with at most CS sites, in columns: lane i holds depth i, and
-// T[s] is site s's column (its continuation token at each depth, -1 from its first depth
+// Inclusive AND over lanes 0 .. lane (lanes take all-ones where a move has no source lane).
+__device__ __forceinline__ uint32_t wave_incl_and(uint32_t v) {
+  v &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, kDppRowShr1, 0xF, 0xF, false);
+  v &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, kDppRowShr2, 0xF, 0xF, false);
+  v &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, kDppRowShr4, 0xF, 0xF, false);
+  v &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, kDppRowShr8, 0xF, 0xF, false);
+  v &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, kDppRowBcast15, 0xA, 0xF, false);
+  v &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, kDppRowBcast31, 0xC, 0xF, false);
+  return v;
+}
+
+// v of a wavefront-uniform site s < CS (a tree of selects: registers cannot be indexed at run
+// time).
+template <int CS, typename V>
+__device__ __forceinline__ V pick_site(const V (&v)[CS], int s) {
+  V x = v[0];
+#pragma unroll
+  for (int q = 1; q < CS; ++q) x = s == q ? v[q] : x;
+  return x;
+}
+
+// Depth-wise vote of a candidate with at most CS <= 8 sites, in columns: lane i holds depth i,
+// and T[s] is site s's column (its continuation token at each depth, -1 from its first depth
 // without one on; len[s] leading tokens; every column ends by dmax <= 64).  Same result and
 // outputs as vote_run.
 //
-// A pass takes the alive site with the longest column as the reference r.  Site s's first
-// disagreement with r from depth d on, fd_s, is one ballot.  At depth i the alive sites that
-// followed r through i - 1 and still have a token vote: g_i of them with r's token (fd_s > i),
-// o_i with another (fd_s == i).  Where g_i > o_i, r's token wins with count g_i whatever the
-// others vote; the first depth where it does not (g_i <= o_i), or where the stop rule ends
-// the chain, is found by one ballot over the depth lanes.  That depth is voted from scratch
-// (the sites' tokens moved to lanes 0 .. CS - 1), the alive sites become the winner's, and the
-// next pass starts after it.
+// Sites are bits of 8-bit masks.  A pass takes the alive site with the longest column as the
+// reference r, and each depth lane builds the mask of the sites whose token there equals r's
+// (none where r has none): the sites alive at depth i are those alive at d that agree with r at
+// every depth d .. i - 1 (an AND scan of that mask over the depth lanes).  At depth i the alive sites with a token vote: g_i of them with r's token, o_i with
+// another.  Where g_i > o_i, r's token wins with count g_i whatever the others vote; the first
+// depth where it does not (g_i <= o_i), or where the stop rule ends the chain, is found by one
+// ballot over the depth lanes.  That depth is voted from scratch on the masks (one count per
+// distinct token, stopping when the best count beats every vote not yet counted), the alive
+// sites become the winner's, and the next pass starts after it.
 template <int CS, typename Beaten>
 __device__ __forceinline__ bool vote_columns(const int (&T)[CS], const int (&len)[CS], int c0,
                                              int dmax, int cmin, int* hk, int* hc, int lane,
                                              Beaten&& beaten, int* out, int* n_out,
                                              int* snum_out) {
+  static_assert(CS <= 8, "sites as bits of an 8-bit mask");
+  (void)hk;
+  (void)hc;
+  // per depth lane: the sites with a token there
+  uint32_t vm = 0;
+#pragma unroll
+  for (int q = 0; q < CS; ++q) vm |= T[q] >= 0 ? (1u << q) : 0u;
   uint32_t AS = c0 >= 32 ? ~0u : ((1u << c0) - 1u);  // alive sites
   int nout = 0, snum = 0, tokv = -1, clast = c0;
   const int cstop = cmin > 1 ? cmin : 1;  // a depth with fewer votes than this ends the chain
@@ -1274,28 +1307,29 @@ __device__ __forceinline__ bool vote_columns(const int (&T)[CS], const int (&len
     // the reference: the first alive site of the longest column
     int rs = 0, rl = -1;
 #pragma unroll
-    for (int s = 0; s < CS; ++s) {
-      const bool better = ((AS >> s) & 1) && len[s] > rl;
-      rl = better ? len[s] : rl;
-      rs = better ? s : rs;
+    for (int q = 0; q < CS; ++q) {
+      const bool better = ((AS >> q) & 1) && len[q] > rl;
+      rl = better ? len[q] : rl;
+      rs = better ? q : rs;
     }
-    int tref = T[0];
+    const int tref = pick_site<CS>(T, rs);
+    uint32_t gr = 0;  // the sites with r's token at this depth
 #pragma unroll
-    for (int s = 1; s < CS; ++s) tref = rs == s ? T[s] : tref;
-    const uint64_t from = ~0ull << d;  // depths d ..
-    int g = 0, o = 0;
-    int fd[CS];
-#pragma unroll
-    for (int s = 0; s < CS; ++s) {
-      const uint64_t D = __ballot(T[s] >= 0 && T[s] != tref) & from;
-      fd[s] = D ? (int)__builtin_ctzll(D) : 64;
-      const int m = fd[s] < len[s] ? fd[s] : len[s];
-      const bool al = (AS >> s) & 1;
-      g += al && lane < m ? 1 : 0;
-      o += al && lane == fd[s] ? 1 : 0;
+    for (int q = 0; q < CS; ++q) gr |= T[q] == tref ? (1u << q) : 0u;
+    gr = tref >= 0 ? gr : 0u;
+    // alive entering depth i >= d: AS and agreement with r at every depth d .. i - 1 (no scan
+    // when every alive site with a token agrees with r at every depth)
+    uint32_t alive = AS;
+    if (__ballot(lane >= d && lane < dmax && (AS & vm & ~gr) != 0) != 0) {
+      const uint32_t incl = wave_incl_and(lane >= d ? gr : ~0u);
+      const uint32_t before = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)incl, kDppWaveShr1,
+                                                                    0xF, 0xF, false);
+      alive = AS & (lane > d ? before : ~0u);
     }
+    const uint32_t V = alive & vm;
+    const int g = __popc(V & gr), na = __popc(V);
+    const int o = na - g;
     const bool in = lane >= d && lane < dmax;
-    const int na = g + o;
     const bool stop = in && (na < cstop || (g > o && g < cmin));
     const bool cont = in && !stop && g <= o;
     const uint64_t sb = __ballot(stop);
@@ -1309,23 +1343,38 @@ __device__ __forceinline__ bool vote_columns(const int (&T)[CS], const int (&len
       nout = e;
     }
     if (e >= dmax || ((sb >> e) & 1)) break;
-    // depth e from scratch: lane s votes site s's token when s followed r through e - 1
-    int x = -1;
+    // depth e from scratch, in scalar registers: the voters and their tokens, then one count per
+    // distinct token (the highest count, then the smallest token)
+    const uint32_t Ve = (uint32_t)__builtin_amdgcn_readlane((int)V, e);
+    int xe[CS];
 #pragma unroll
-    for (int s = 0; s < CS; ++s) {
-      const int xs = __builtin_amdgcn_readlane(T[s], e);
-      const bool vs = ((AS >> s) & 1) && fd[s] >= e;
-      x = lane == s && vs ? xs : x;
+    for (int q = 0; q < CS; ++q) xe[q] = __builtin_amdgcn_readlane(T[q], e);
+    uint32_t R = Ve, bgrp = 0;
+    int best = -1, btok = 0, rest = __popc(Ve);
+    while (R && best <= rest) {
+      const int q = __builtin_ctz(R);
+      int tok = xe[0];
+#pragma unroll
+      for (int u = 1; u < CS; ++u) tok = q == u ? xe[u] : tok;
+      uint32_t grp = 0;
+#pragma unroll
+      for (int u = 0; u < CS; ++u) grp |= xe[u] == tok ? (1u << u) : 0u;
+      grp &= Ve;
+      const int cnt = __popc(grp);
+      if (cnt > best || (cnt == best && tok < btok)) {
+        best = cnt;
+        btok = tok;
+        bgrp = grp;
+      }
+      R &= ~grp;
+      rest -= cnt;
     }
-    const uint64_t X = __ballot(x >= 0);
-    int w, c;
-    vote_depth(x, -1, X, 0ull, cmin, hk, hc, lane, &w, &c);
-    if (c == 0 || c < cmin) break;
-    tokv = lane == e ? w : tokv;
-    snum += c;
-    clast = c;
+    if (best <= 0 || best < cmin) break;
+    tokv = lane == e ? btok : tokv;
+    snum += best;
+    clast = best;
     nout = e + 1;
-    AS = (uint32_t)__ballot(x == w);
+    AS = bgrp;
     d = e + 1;
   }
   if (cut) {
@@ -1630,10 +1679,6 @@ __device__ __forceinline__ uint32_t put_ballot(uint32_t acc, uint64_t v) {
   return acc;
 }
 
-// DPP controls of whole-wavefront lane moves (GFX9): lane i takes lane i - 1 (lane 0 keeps the
-// old value), and lane i takes lane i - 1 mod 64.
-constexpr int kDppWaveShr1 = 0x138;
-constexpr int kDppWaveRor1 = 0x13C;
 
 // Local step 1 for one wavefront's chunk [cbeg, cend) of end positions, row part.  The row part
 // [cbeg, rend), rend = min(cend, n), is read with bounds-checked buffer loads (every load of a
