@@ -1815,18 +1815,35 @@ __device__ __forceinline__ int list_extend(const int* ctxs, const uint64_t* b2w,
     const int lim = D < j + 1 ? D : j + 1;
     int m = 2;
     if (ok && lim > 2) {
+      // offsets 2 .. 5 first (most hits end there), the other kTailRegs - 4 only when some lane
+      // of the wavefront still matches
       int c[kTailRegs];
 #pragma unroll
-      for (int q = 0; q < kTailRegs; ++q) {
+      for (int q = 0; q < 4; ++q) {
         const int o = 2 + q;
         const int at = o < lim ? j - o : 0;
         c[q] = STAGED ? ctxs[at] : ctx_at(row, smp, n, at);
       }
       bool go = true;
 #pragma unroll
-      for (int q = 0; q < kTailRegs; ++q) {
+      for (int q = 0; q < 4; ++q) {
         go = go && 2 + q < lim && c[q] == tq[q];
         m += go ? 1 : 0;
+      }
+      if (__ballot(go && lim > 6) != 0) {
+#pragma unroll
+        for (int q = 4; q < kTailRegs; ++q) {
+          const int o = 2 + q;
+          const int at = o < lim ? j - o : 0;
+          c[q] = STAGED ? ctxs[at] : ctx_at(row, smp, n, at);
+        }
+#pragma unroll
+        for (int q = 4; q < kTailRegs; ++q) {
+          go = go && 2 + q < lim && c[q] == tq[q];
+          m += go ? 1 : 0;
+        }
+      } else {
+        go = false;
       }
       if (go && !short_d) {
         // match lengths above kTailRegs + 2 (max_tree_depth up to 64)
