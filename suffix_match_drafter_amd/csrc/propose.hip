@@ -1258,13 +1258,18 @@ __device__ __forceinline__ uint32_t wave_incl_and(uint32_t v) {
   return v;
 }
 
-// v of a wavefront-uniform site s < CS (a tree of selects: registers cannot be indexed at run
-// time).
+// v of a wavefront-uniform site s < CS (a chain of selects: registers cannot be indexed at run
+// time).  Each step passes through an empty asm: the compiler would otherwise fold the chain into
+// an indexed load and move the array to scratch memory, a memory round trip per use.
 template <int CS, typename V>
 __device__ __forceinline__ V pick_site(const V (&v)[CS], int s) {
+  static_assert(sizeof(V) == 4, "one register per lane");
   V x = v[0];
 #pragma unroll
-  for (int q = 1; q < CS; ++q) x = s == q ? v[q] : x;
+  for (int q = 1; q < CS; ++q) {
+    x = s == q ? v[q] : x;
+    asm volatile("" : "+v"(x));
+  }
   return x;
 }
 
@@ -2677,14 +2682,17 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
     PHASE_FLUSH();
     return;
   }
+  // (every lane reads, lanes from 2 nb on candidate 0's fields, so that the six reads are
+  // issued together; only lanes below 2 nb are used)
   const bool cl = lane < 2 * nb;
-  const int fvalid = cl ? sm.cand_valid[lane] : 0;
-  const int fsrc = cl ? sm.cand_src[lane] : -1;
-  const int csn = cl ? sm.cand_snum[lane] : 0;
-  const int cc0 = cl ? sm.cand_c0[lane] : 1;
-  const int clen = cl ? sm.cand_len[lane] : 0;
-  const int fn = cl ? sm.cand_n[lane] : 0;
-  const bool cv = fvalid && fsrc == lane;
+  const int li = cl ? lane : 0;
+  const int fvalid = sm.cand_valid[li];
+  const int fsrc = sm.cand_src[li];
+  const int csn = sm.cand_snum[li];
+  const int cc0 = sm.cand_c0[li];
+  const int clen = sm.cand_len[li];
+  const int fn = sm.cand_n[li];
+  const bool cv = cl && (fvalid != 0) & (fsrc == lane);
   const int cn = cv ? fn : 0;
   const uint64_t vmask = __ballot(cv);
   int win = -1;
