@@ -1395,12 +1395,16 @@ __device__ __forceinline__ bool vote_columns(const int (&T)[CS], const int (&len
 
 // Columns of a candidate's sites for vote_columns: lane i of T[s] gets the token at depth i of
 // site s (s < c0), from its first depth without a token on -1; len[s] its leading tokens.  at(s,
-// i) gives the token (or -1) at depth i < dmax of site s.
+// i) gives the token (or -1) at depth i < dmax of site s; it must read in bounds for every s < CS
+// and lane i (its value is dropped where s >= c0 or i >= dmax), so that every site's read is
+// issued before any is used.
 template <int CS, typename At>
 __device__ __forceinline__ void columns_cut(int (&T)[CS], int (&len)[CS], int c0, int dmax,
                                             int lane, At&& at) {
 #pragma unroll
-  for (int s = 0; s < CS; ++s) T[s] = s < c0 && lane < dmax ? at(s, lane) : -1;
+  for (int s = 0; s < CS; ++s) T[s] = at(s, lane);
+#pragma unroll
+  for (int s = 0; s < CS; ++s) T[s] = s < c0 && lane < dmax ? T[s] : -1;
 #pragma unroll
   for (int s = 0; s < CS; ++s) {
     const uint64_t ok = __ballot(T[s] >= 0);
@@ -1420,7 +1424,9 @@ __device__ __forceinline__ void corpus_windows(const ProposeArgs& a, const Req& 
   const int32_t* text = act == 0 ? a.idx[0].text : (act == 1 ? a.idx[1].text : nullptr);
   const long long ss = r.snap_start, sn = r.snap_n;
   const int s0 = lane, s1 = lane + 64;
-  const long long q0 = r.tail_w + (s0 < c0 ? gs[s0] : 0), q1 = r.tail_w + (s1 < c0 ? gs[s1] : 0);
+  // (both slots are read, together: a candidate's list holds kMaxM = 128 of them)
+  const int g0 = gs[s0], g1 = gs[s1];
+  const long long q0 = r.tail_w + (s0 < c0 ? g0 : 0), q1 = r.tail_w + (s1 < c0 ? g1 : 0);
   bool live0 = s0 < c0, live1 = s1 < c0;
   // offsets into the snapshot text (an unused slot reads its first token)
   const long long o0 = live0 ? q0 - ss : 0, o1 = live1 ? q1 - ss : 0;
@@ -1428,21 +1434,21 @@ __device__ __forceinline__ void corpus_windows(const ProposeArgs& a, const Req& 
   const bool in1 = text != nullptr && o1 >= 0 && o1 < sn;
   if (__ballot(!(in0 && in1)) == 0) {
     // every site inside the snapshot, whose text ends with a separator: a window runs at most to
-    // it, so positions past the text's end are clamped onto it
+    // it, and reads on past the text's end unclamped (the buffer holds kTextSlack >= KMAX more
+    // positions), so that its loads share one address
+    static_assert(KMAX <= kTextSlack, "windows inside the text buffer");
     const int32_t* t0p = text + o0;
     const int32_t* t1p = text + o1;
-    const long long r0 = sn - 1 - o0, r1 = sn - 1 - o1;
-    const int l0 = r0 < KMAX ? (int)r0 : KMAX, l1 = r1 < KMAX ? (int)r1 : KMAX;
     if (c0 > 64) {  // (wavefront-uniform) a second site per lane
 #pragma unroll
       for (int d = 0; d < KMAX; ++d) {
-        w0[d] = t0p[d < l0 ? d : l0];
-        w1[d] = t1p[d < l1 ? d : l1];
+        w0[d] = t0p[d];
+        w1[d] = t1p[d];
       }
     } else {
 #pragma unroll
       for (int d = 0; d < KMAX; ++d) {
-        w0[d] = t0p[d < l0 ? d : l0];
+        w0[d] = t0p[d];
         w1[d] = -1;
       }
     }
@@ -1981,21 +1987,28 @@ __device__ __forceinline__ void local_windows(const Smem& sm, const int* ctxs, c
                                               int (&w1)[KMAX], int* len0_out, int* len1_out) {
   const int* ls = sm.lsites[t];
   const int s0 = lane, s1 = lane + 64;
-  const int p0 = s0 < c0 ? ls[s0] : 0, p1 = s1 < c0 ? ls[s1] : 0;
+  const int l0 = ls[s0], l1 = ls[s1];  // (read together: the list holds kMaxM = 128 slots)
+  const int p0 = s0 < c0 ? l0 : 0, p1 = s1 < c0 ? l1 : 0;
   const int cap0 = cap < KMAX ? cap : KMAX;
   const int e0 = s0 < c0 ? (L - p0 < cap0 ? L - p0 : cap0) : 0;
   const int e1 = s1 < c0 ? (L - p1 < cap0 ? L - p1 : cap0) : 0;
-  auto at = [&](int x) { return STAGED ? ctxs[x] : *(x < n ? row + x : smp + (x - n)); };
+  // staged, a window reads on past L (the stage holds L + 64 positions; what lies past L is cut
+  // below), so that its reads share one address; from HBM it stops at the last context token
+  auto at = [&](int p, int d) {
+    if (STAGED) return ctxs[p + d];
+    const int x = p + d < L ? p + d : L - 1;
+    return *(x < n ? row + x : smp + (x - n));
+  };
   if (c0 > 64) {  // (wavefront-uniform) a second site per lane
 #pragma unroll
     for (int d = 0; d < KMAX; ++d) {
-      w0[d] = at(p0 + d < L ? p0 + d : L - 1);
-      w1[d] = at(p1 + d < L ? p1 + d : L - 1);
+      w0[d] = at(p0, d);
+      w1[d] = at(p1, d);
     }
   } else {
 #pragma unroll
     for (int d = 0; d < KMAX; ++d) {
-      w0[d] = at(p0 + d < L ? p0 + d : L - 1);
+      w0[d] = at(p0, d);
       w1[d] = -1;
     }
   }
@@ -2619,10 +2632,16 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
           lim = lane < c0 ? (int)r.snap_n - 1 - o : 0;
         }
         const int so = loc ? sv : (int)(r.tail_w + sv - r.snap_start);
-        auto at = [&](int si, int i) {
-          const int p = __builtin_amdgcn_readlane(so, si);
+        // (a site from c0 on reads at position 0 with limit 0 (corpus: the text buffer holds the
+        // ring's capacity) or L (local): in bounds)
+        auto at_corpus = [&](int si, int i) {
+          const int p = si < c0 ? __builtin_amdgcn_readlane(so, si) : 0;
           const int lm = __builtin_amdgcn_readlane(lim, si);
-          if (!loc) return text[p + (i < lm ? i : lm)];
+          return text[p + (i < lm ? i : lm)];
+        };
+        auto at_local = [&](int si, int i) {
+          const int p = si < c0 ? __builtin_amdgcn_readlane(so, si) : 0;
+          const int lm = __builtin_amdgcn_readlane(lim, si);
           int v;
           if (STAGED) {
             v = ctxs[p + i];  // p + i < L + 64: inside the stage
@@ -2636,7 +2655,8 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
         auto run = [&](auto csc) {
           constexpr int CS = decltype(csc)::value;
           int T[CS], len[CS];
-          columns_cut<CS>(T, len, c0, dmax, lane, at);
+          if (loc) columns_cut<CS>(T, len, c0, dmax, lane, at_local);
+          else columns_cut<CS>(T, len, c0, dmax, lane, at_corpus);
           PHASE(6);
           return vote_columns<CS>(T, len, c0, dmax, cmin, hk, hk + kVoteSlots, lane, beaten,
                                   sm.cand_out[ci], &nout, &snum);

@@ -356,7 +356,7 @@ int sfx_create(const sfx_config* cfg, sfx_ctx** out) {
               al((void**)&c->range_dev, 32);
     for (int bi = 0; bi < 2 && ok; ++bi) {
       IndexBuf& b = c->idx[bi];
-      ok = al((void**)&b.text, 4 * c->cap) && al((void**)&b.sa, 4 * c->cap);
+      ok = al((void**)&b.text, 4 * (c->cap + kTextSlack)) && al((void**)&b.sa, 4 * c->cap);
       for (int g = 0; g < kNG && ok; ++g)
         ok = al((void**)&b.pl[g], 4 * c->cap) &&
              al((void**)&b.ht[g], sizeof(NgramSlot) * (size_t)c->ht_slots);

@@ -10,6 +10,10 @@
 namespace sfx {
 
 constexpr int kMaxK = 32;    // draft width limit (register windows in the vote)
+// Positions allocated past a snapshot text's capacity: the propose kernel reads a corpus window
+// of up to kMaxK tokens without clamping it to the text's end (the text ends with a separator,
+// which ends every window, so what lies past it is never used).
+constexpr int kTextSlack = 64;
 constexpr int kMaxD = 64;    // max_tree_depth limit (tail staged in LDS, lengths fit a byte)
 constexpr int kMaxNB = 8;    // num_backoff limit
 constexpr int kMaxM = 128;   // max_occurrences limit (two sites per lane of one wavefront)
