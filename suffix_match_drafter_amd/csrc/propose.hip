@@ -900,14 +900,23 @@ __device__ __forceinline__ void delta_list_wave(const ProposeArgs& a, long long 
 // One ballot pair per distinct token, until the best count exceeds every vote not yet counted
 // (a tie with a smaller token still has to be looked at), or until neither the best count nor
 // the votes left reach cmin: the count is then below cmin (the vote stops there, whatever the
-// token).
+// token).  After kSmallRounds tokens without an end it gives up (*fin false): the hash count
+// then takes the vote.
+constexpr int kSmallRounds = 12;
 __device__ __forceinline__ uint64_t vote_small(int x0, int x1, uint64_t V0, uint64_t V1, int ref,
-                                               uint64_t E0, uint64_t E1, int na, int cmin) {
+                                               uint64_t E0, uint64_t E1, int na, int cmin,
+                                               bool* fin) {
   const int ce = __popcll(E0) + __popcll(E1);
   uint64_t key = ((uint64_t)ce << 32) | (uint32_t)(0x7FFFFFFF - ref);
   uint64_t r0 = V0 & ~E0, r1 = V1 & ~E1;
   int rest = na - ce;
-  while ((r0 | r1) && (int)(key >> 32) <= rest && (rest >= cmin || (int)(key >> 32) >= cmin)) {
+  *fin = false;
+#pragma nounroll
+  for (int it = 0; it < kSmallRounds; ++it) {
+    if (!((r0 | r1) && (int)(key >> 32) <= rest && (rest >= cmin || (int)(key >> 32) >= cmin))) {
+      *fin = true;
+      break;
+    }
     const int tok = r0 ? __builtin_amdgcn_readlane(x0, __builtin_ctzll(r0))
                        : __builtin_amdgcn_readlane(x1, __builtin_ctzll(r1));
     const uint64_t e0 = __ballot(x0 == tok) & r0, e1 = __ballot(x1 == tok) & r1;
@@ -921,8 +930,8 @@ __device__ __forceinline__ uint64_t vote_small(int x0, int x1, uint64_t V0, uint
   return (key >> 32) << 32 | (uint32_t)(0x7FFFFFFF - (int)(uint32_t)(key & 0xFFFFFFFFu));
 }
 
-// The same vote for more than kSmallVote voters, by counting in an LDS hash (a function of its
-// own: this path is rare and its code is long).
+// The same vote for more than kSmallVote voters, or many distinct tokens, by counting in an LDS
+// hash (a function of its own: this path is rare and its code is long).
 __device__ __noinline__ uint64_t vote_split(int x0, int x1, uint64_t V0, uint64_t V1, int ref,
                                             uint64_t E0, uint64_t E1, lds_int* hk, lds_int* hc,
                                             int lane) {
@@ -993,11 +1002,15 @@ __device__ __forceinline__ void vote_decide(int x0, int x1, uint64_t V0, uint64_
     *c = ce;
   } else if (na < cmin) {
     *c = na;  // no token reaches the stop count: any count below cmin stops the vote
-  } else if (na <= kSmallVote) {
-    const uint64_t res = vote_small(x0, x1, V0, V1, ref, E0, E1, na, cmin);
-    *c = (int)(res >> 32);
-    *w = (int)(uint32_t)res;
   } else {
+    bool fin = false;
+    uint64_t rs = 0;
+    if (na <= kSmallVote) rs = vote_small(x0, x1, V0, V1, ref, E0, E1, na, cmin, &fin);
+    if (fin) {
+      *c = (int)(rs >> 32);
+      *w = (int)(uint32_t)rs;
+      return;
+    }
     // (the call returns in vector registers: readfirstlane tells the compiler that the winner
     // and its count are wavefront-uniform, or every loop around this becomes a divergent one)
     const uint64_t res = vote_split(x0, x1, V0, V1, ref, E0, E1, (lds_int*)hk, (lds_int*)hc, lane);
