@@ -267,7 +267,7 @@ struct Smem {
   int cand_snum[2 * kMaxNB];  // at most k * M = 4096
   // 1 once candidate i's vote is final (its cand_n / cand_snum written before): the scored mode
   // drops a vote as soon as a final score beats every score it could still reach
-  int cand_done[2 * kMaxNB];
+  int cand_done[2 * kMaxNB];  // 0, or a final vote's 1 << 30 | snum << 8 | c0
   int cand_out[2 * kMaxNB][kMaxK];
   int lsites[kMaxNB][kMaxM];
   int gsites[kMaxNB][kMaxM];  // logical corpus positions minus the oldest live one (Ctl tail)
@@ -1042,11 +1042,11 @@ __device__ __forceinline__ void vote_depth(int x0, int x1, uint64_t A0, uint64_t
 __device__ __forceinline__ bool outscored(Smem& sm, int ci, int nb, int bnum, int bden,
                                           int lane) {
   const bool on = lane < 2 * nb && lane != ci;
+  // a final vote's word carries its score: 1 << 30 | snum << 8 | c0 (one read, no fence)
   const int dn = on ? __hip_atomic_load(&sm.cand_done[lane], __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_WORKGROUP)
                     : 0;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  const int sj = dn ? sm.cand_snum[lane] : 0, cj = dn ? sm.cand_c0[lane] : 1;
+  const int sj = (dn & 0x3FFFFFFF) >> 8, cj = dn & 0xFF;
   const int lhs = sj * bden, rhs = bnum * cj;
   return __ballot(dn != 0 && (lhs > rhs || (lhs == rhs && lane < ci))) != 0;
 }
@@ -2696,11 +2696,12 @@ __global__ __launch_bounds__(NT) void propose_kernel(ProposeArgs a) {
         sm.cand_n[ci] = nout;
         sm.cand_snum[ci] = snum;
       }
-      if (fin) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        if (lane == 0)
-          __hip_atomic_store(&sm.cand_done[ci], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
+      // a final vote publishes its score in its done word (snum <= 4096 < 2^22 and
+      // c0 <= 128 < 2^8 fit beside the flag bit); the selection reads the fields after a barrier
+      static_assert(kMaxK * kMaxM < (1 << 22) && kMaxM < 256, "score packed in the done word");
+      if (fin && lane == 0)
+        __hip_atomic_store(&sm.cand_done[ci], (1 << 30) | (snum << 8) | c0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }
   if (lane == 0) sm.sink[wid] = pf;
